@@ -1,0 +1,173 @@
+"""fp64 CPU oracle for Kimi Delta Attention (KDA) -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The KDA library (the HIP path) never
+imports, links or calls it, and the two share no code.
+
+The oracle is the plain definition of the KDA recurrence, evaluated token by
+token in fp64 (``kda_oracle.c`` states the recurrence and the passages of the
+Kimi K3 pages it follows).  This module compiles that C file with gcc on first
+use and wraps it with ctypes.
+
+Pins (tests/test_oracle_pins.py): a brute-force unrolled product form on short
+sequences, closed forms (frozen state, cumulative linear attention with
+orthogonal keys, first-order small-beta limit, exact key overwrite, geometric
+sum of decay and erase, decay-only product), invariants (continuation,
+linearity, column independence, varlen = independent calls, decode = prefill,
+norm bound), a hand-computed worked example under tests/golden/, and an fp64
+chunked mirror of the chunkwise (UT/WY) algebra.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile libkda_oracle.so with gcc (plain -O2: no fast-math, fp64 as written)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_long
+            lib.kda_oracle_forward.argtypes = [vp] * 5 + [i32, vp, vp, vp, i32, i64, i32, i32, i32, i32]
+            lib.kda_oracle_forward.restype = i32
+            lib.kda_oracle_forward_units.argtypes = [vp] * 5 + [i32, vp, vp, vp, i32, i64, i32, i32, i32, vp, i32, i32]
+            lib.kda_oracle_forward_units.restype = i32
+            lib.kda_oracle_forward_varlen.argtypes = [vp] * 5 + [i32, vp, i32, vp, vp, vp, i32, i32, i32, i32]
+            lib.kda_oracle_forward_varlen.restype = i32
+            lib.kda_oracle_decode_step.argtypes = [vp] * 5 + [i32, vp, vp, i32, i32, i32, i32, i32]
+            lib.kda_oracle_decode_step.restype = i32
+            _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _dtype_code(*arrs) -> int:
+    dts = {a.dtype for a in arrs}
+    if dts == {np.dtype(np.float32)}:
+        return 0
+    if dts == {np.dtype(np.uint16)}:
+        return 1
+    raise TypeError("oracle inputs must all be float32 or all bf16 bit patterns (uint16), got %s" % dts)
+
+
+def _c(a):
+    return None if a is None else np.ascontiguousarray(a)
+
+
+def _state64(h0):
+    """Initial state as contiguous fp64 (fp32 converts exactly), or None."""
+    if h0 is None:
+        return None
+    h0 = np.asarray(h0)
+    assert h0.dtype in (np.float32, np.float64), h0.dtype
+    return np.ascontiguousarray(h0, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def forward(q, k, v, g, beta, h0=None, want_o=True, want_hT=True, nthreads=None):
+    """Batched forward.  q, k, g: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H];
+    h0: [B,H,dk,dv] float32/float64 or None.  Returns (o [B,T,H,dv] fp64 or None,
+    hT [B,H,dk,dv] fp64 or None)."""
+    q, k, v, g, beta = map(_c, (q, k, v, g, beta))
+    h0 = _state64(h0)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and g.shape == q.shape and v.shape == (B, T, H, dv) and beta.shape == (B, T, H)
+    dt = _dtype_code(q, k, v, g, beta)
+    if h0 is not None:
+        assert h0.shape == (B, H, dk, dv)
+    o = np.empty((B, T, H, dv), np.float64) if want_o else None
+    hT = np.empty((B, H, dk, dv), np.float64) if want_hT else None
+    rc = _load().kda_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), dt, _ptr(h0), _ptr(o), _ptr(hT),
+                                    B, T, H, dk, dv, nthreads or default_threads())
+    if rc:
+        raise RuntimeError("kda_oracle_forward: invalid arguments")
+    return o, hT
+
+
+def forward_units(q, k, v, g, beta, h0, unit_ids, want_o=True, want_hT=True, nthreads=None):
+    """Forward on a subset of (b, h) units (unit id = b * H + h), for sampled checks.
+    Returns (o [n, T, dv] fp64 or None, hT [n, dk, dv] fp64 or None)."""
+    q, k, v, g, beta = map(_c, (q, k, v, g, beta))
+    h0 = _state64(h0)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q, k, v, g, beta)
+    if h0 is not None:
+        assert h0.shape == (B, H, dk, dv)
+    ids = np.ascontiguousarray(np.asarray(unit_ids, dtype=np.int32))
+    n = ids.size
+    o = np.empty((n, T, dv), np.float64) if want_o else None
+    hT = np.empty((n, dk, dv), np.float64) if want_hT else None
+    rc = _load().kda_oracle_forward_units(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), dt, _ptr(h0), _ptr(o),
+                                          _ptr(hT), B, T, H, dk, dv, ids.ctypes.data, n,
+                                          nthreads or default_threads())
+    if rc:
+        raise RuntimeError("kda_oracle_forward_units: invalid arguments")
+    return o, hT
+
+
+def forward_varlen(q, k, v, g, beta, cu_seqlens, h0=None, want_o=True, want_hT=True, nthreads=None):
+    """Packed varlen forward.  q, k, g: [T_total,H,dk] (or [1,T_total,H,dk]); v: [..,T_total,H,dv];
+    beta: [..,T_total,H]; cu_seqlens: int32 [N+1]; h0: [N,H,dk,dv] float32/float64 or None.
+    Returns (o [T_total,H,dv] fp64, hT [N,H,dk,dv] fp64)."""
+    q, k, v, g, beta = map(_c, (q, k, v, g, beta))
+    h0 = _state64(h0)
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    N = cu.size - 1
+    dk, dv, H = q.shape[-1], v.shape[-1], q.shape[-2]
+    Tt = int(cu[-1])
+    assert q.size == Tt * H * dk and v.size == Tt * H * dv and beta.size == Tt * H
+    dt = _dtype_code(q, k, v, g, beta)
+    if h0 is not None:
+        assert h0.shape == (N, H, dk, dv)
+    o = np.empty((Tt, H, dv), np.float64) if want_o else None
+    hT = np.empty((N, H, dk, dv), np.float64) if want_hT else None
+    rc = _load().kda_oracle_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), dt, cu.ctypes.data, N,
+                                           _ptr(h0), _ptr(o), _ptr(hT), H, dk, dv, nthreads or default_threads())
+    if rc:
+        raise RuntimeError("kda_oracle_forward_varlen: invalid arguments")
+    return o, hT
+
+
+def decode_step(q, k, v, g, beta, state, nthreads=None):
+    """One decode step, in place on the fp64 state [B,H,dk,dv].  q, k, g: [B,H,dk];
+    v: [B,H,dv]; beta: [B,H].  Returns o [B,H,dv] fp64."""
+    q, k, v, g, beta = map(_c, (q, k, v, g, beta))
+    assert state.dtype == np.float64 and state.flags["C_CONTIGUOUS"]
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q, k, v, g, beta)
+    o = np.empty((B, H, dv), np.float64)
+    rc = _load().kda_oracle_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), dt, state.ctypes.data,
+                                        o.ctypes.data, B, H, dk, dv, nthreads or default_threads())
+    if rc:
+        raise RuntimeError("kda_oracle_decode_step: invalid arguments")
+    return o

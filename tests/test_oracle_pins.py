@@ -1,0 +1,356 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test fixes a property the KDA recurrence must have (a hand-worked example,
+a brute-force product form, closed forms of special cases, invariants), chosen
+so that a plausible slip in the oracle -- a dropped term, a wrong sign, the
+gate on the wrong axis, the read-out before the update, a transposed operand --
+fails at least one of them.  The recurrence pinned here:
+
+    S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t
+
+(gated delta rule with a channel-wise forget gate: Kimi K3 technical-report
+page, "Architecture at a glance" and FAQ; architecture blog, "Kimi Delta
+Attention: the linear core").
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = datagen.DT_F32
+
+
+def rel_err(x, y):
+    """max |x - y| / max |y| (0/0 = 0)."""
+    x, y = np.asarray(x, np.float64), np.asarray(y, np.float64)
+    den = np.abs(y).max() if y.size else 0.0
+    num = np.abs(x - y).max() if y.size else 0.0
+    return 0.0 if num == 0 else num / (den if den > 0 else 1.0)
+
+
+def f64(a):
+    return datagen.to_f64(a)
+
+
+def inputs(seed, B, T, H, dk, dv, h0_std=0.02):
+    return datagen.prefill_inputs(seed, B, T, H, dk, dv, F32, h0_std)
+
+
+def run(d, h0="same", **kw):
+    return oracle.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"] if h0 == "same" else h0, **kw)
+
+
+# --------------------------------------------------------------------------------------------
+# Worked example by hand (tests/golden/worked_example_3tok.json)
+
+
+def test_golden_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example_3tok.json")))
+    f = lambda key, shape: np.asarray(ex[key], np.float32).reshape(shape)
+    q, k, v, g = f("q", (1, 3, 1, 2)), f("k", (1, 3, 1, 2)), f("v", (1, 3, 1, 2)), f("g", (1, 3, 1, 2))
+    beta = f("beta", (1, 3, 1))
+    h0 = f("h0", (1, 1, 2, 2))
+    o, hT = oracle.forward(q, k, v, g, beta, h0)
+    tol = ex["tolerance"]
+    assert np.abs(o[0, :, 0, :] - np.asarray(ex["expected_o"])).max() < tol
+    assert np.abs(hT[0, 0] - np.asarray(ex["expected_hT"])).max() < tol
+
+
+# --------------------------------------------------------------------------------------------
+# P1: brute-force unrolled product form, T <= 16
+
+
+def brute_force(q, k, v, g, beta, h0):
+    """S_t = Phi(t,0) S_0 + sum_{j<=t} Phi(t,j) beta_j k_j v_j^T with
+    Phi(t,j) = M_t ... M_{j+1}, M_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)); o_t = S_t^T q_t.
+    One (sequence, head): q, k, g [T, dk]; v [T, dv]; beta [T]; h0 [dk, dv]."""
+    T, dk = q.shape
+    I = np.eye(dk)
+    M = [(I - beta[t] * np.outer(k[t], k[t])) @ np.diag(np.exp(g[t])) for t in range(T)]
+
+    def phi(t, j):  # product M_t ... M_{j+1}
+        P = I.copy()
+        for s in range(j + 1, t + 1):
+            P = M[s] @ P
+        return P
+
+    o = np.zeros((T, v.shape[1]))
+    S = None
+    for t in range(T):
+        S = phi(t, -1) @ h0
+        for j in range(t + 1):
+            S = S + phi(t, j) @ (beta[j] * np.outer(k[j], v[j]))
+        o[t] = S.T @ q[t]
+    return o, S
+
+
+@pytest.mark.parametrize("T,dk,dv", [(1, 4, 3), (7, 8, 5), (16, 16, 16), (12, 5, 9)])
+def test_p1_brute_force_product_form(T, dk, dv):
+    d = inputs(11 + T, 2, T, 2, dk, dv)
+    o, hT = run(d)
+    for b in range(2):
+        for h in range(2):
+            ob, Sb = brute_force(f64(d["q"][b, :, h]), f64(d["k"][b, :, h]), f64(d["v"][b, :, h]),
+                                 f64(d["g"][b, :, h]), f64(d["beta"][b, :, h]), f64(d["h0"][b, h]))
+            assert rel_err(o[b, :, h], ob) < 1e-12
+            assert rel_err(hT[b, h], Sb) < 1e-12
+
+
+# --------------------------------------------------------------------------------------------
+# P2: beta = 0, g = 0 -> nothing is written and nothing decays: S_t = h0, o_t = h0^T q_t
+
+
+def test_p2_frozen_state():
+    d = inputs(21, 1, 40, 3, 16, 12)
+    d["beta"][:] = 0
+    d["g"][:] = 0
+    o, hT = run(d)
+    h0 = f64(d["h0"])
+    assert np.array_equal(hT, h0)
+    exp = np.einsum("bhcj,bthc->bthj", h0, f64(d["q"]))
+    assert rel_err(o, exp) < 1e-14
+
+
+# --------------------------------------------------------------------------------------------
+# P3: orthonormal keys, g = 0, h0 = 0 -> beta-weighted cumulative linear attention, exactly
+
+
+def hadamard(n):
+    H = np.array([[1.0]])
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def test_p3_orthogonal_keys_linear_attention():
+    dk, dv, T = 16, 10, 16
+    rng = np.random.default_rng(3)
+    Hd = hadamard(dk) / 4.0  # rows orthonormal, entries +-1/4 (exact in fp32)
+    keys = (Hd[rng.permutation(dk)] * rng.choice([-1.0, 1.0], size=(dk, 1)))[:T]
+    d = inputs(31, 1, T, 1, dk, dv, h0_std=None)
+    d["k"][0, :, 0] = keys.astype(np.float32)
+    d["g"][:] = 0
+    o, hT = run(d)
+    q, k, v, be = f64(d["q"][0, :, 0]), f64(d["k"][0, :, 0]), f64(d["v"][0, :, 0]), f64(d["beta"][0, :, 0])
+    exp = np.array([sum(be[j] * (q[t] @ k[j]) * v[j] for j in range(t + 1)) for t in range(T)])
+    assert rel_err(o[0, :, 0], exp) < 1e-14
+    assert rel_err(hT[0, 0], sum(be[j] * np.outer(k[j], v[j]) for j in range(T))) < 1e-14
+
+
+# --------------------------------------------------------------------------------------------
+# P4: beta = eps * b, g = 0, h0 = 0 -> o / eps tends to sum_{j<=t} b_j (q_t . k_j) v_j, error O(eps)
+
+
+def test_p4_small_beta_limit():
+    dk, dv, T = 16, 8, 24
+    d = inputs(41, 1, T, 1, dk, dv, h0_std=None)
+    d["g"][:] = 0
+    b = f64(d["beta"][0, :, 0])
+    q, k, v = f64(d["q"][0, :, 0]), f64(d["k"][0, :, 0]), f64(d["v"][0, :, 0])
+    lin = np.array([sum(b[j] * (q[t] @ k[j]) * v[j] for j in range(t + 1)) for t in range(T)])
+    errs = []
+    for eps in (1e-3, 1e-4, 1e-5):
+        d2 = dict(d)
+        d2["beta"] = (d["beta"].astype(np.float64) * eps).astype(np.float32)
+        beps = f64(d2["beta"][0, :, 0])
+        lin_eps = np.array([sum(beps[j] * (q[t] @ k[j]) * v[j] for j in range(t + 1)) for t in range(T)])
+        o, _ = run(d2)
+        errs.append(rel_err(o[0, :, 0], lin_eps))
+    assert errs[0] < 1e-1 and errs[2] < 1e-4
+    # first order: the error shrinks in proportion to eps
+    assert 5 < errs[0] / errs[1] < 20 and 5 < errs[1] / errs[2] < 20
+    assert rel_err(lin, lin) == 0
+
+
+# --------------------------------------------------------------------------------------------
+# P5: g = 0, beta = 1, one-hot keys (with repeats), q = k -> exact key overwrite
+
+
+def test_p5_exact_key_overwrite():
+    dk, dv, T = 8, 6, 30
+    rng = np.random.default_rng(5)
+    d = inputs(51, 1, T, 1, dk, dv)
+    keys = rng.integers(0, dk - 2, size=T)  # the last two rows are never written
+    d["k"][:] = 0
+    d["k"][0, np.arange(T), 0, keys] = 1
+    d["q"][:] = d["k"]
+    d["g"][:] = 0
+    d["beta"][:] = 1
+    o, hT = run(d)
+    v = f64(d["v"][0, :, 0])
+    assert np.array_equal(o[0, :, 0], v)
+    exp = f64(d["h0"][0, 0]).copy()
+    for t in range(T):
+        exp[keys[t]] = v[t]
+    assert np.array_equal(hT[0, 0], exp)
+
+
+# --------------------------------------------------------------------------------------------
+# P6: fixed one-hot key e_c, constant gate, beta and v -> geometric sum on row c
+#     x_t = r x_{t-1} + beta v, r = alpha_c (1 - beta); other rows decay as alpha^t
+
+
+def test_p6_geometric_sum():
+    dk, dv, T, c = 8, 5, 50, 3
+    d = inputs(61, 1, T, 1, dk, dv)
+    g_row = d["g"][0, 0, 0].copy()
+    d["g"][:] = g_row
+    d["k"][:] = 0
+    d["k"][0, :, 0, c] = 1
+    d["beta"][:] = d["beta"][0, 0, 0]
+    d["v"][:] = d["v"][0, 0, 0]
+    o, hT = run(d)
+    alpha = np.exp(f64(g_row))
+    be, v, S0 = float(f64(d["beta"][0, 0, 0])), f64(d["v"][0, 0, 0]), f64(d["h0"][0, 0])
+    r = alpha[c] * (1 - be)
+    q = f64(d["q"][0, :, 0])
+    for t in range(1, T + 1):
+        S = alpha[:, None] ** t * S0
+        S[c] = r ** t * S0[c] + be * v * (1 - r ** t) / (1 - r)
+        assert rel_err(o[0, t - 1, 0], S.T @ q[t - 1]) < 1e-13
+    assert rel_err(hT[0, 0], S) < 1e-13
+
+
+# --------------------------------------------------------------------------------------------
+# P7: beta = 0 -> decay only: S_t = Diag(exp(G_t)) h0, G_t = sum_{s<=t} g_s; o_t = h0^T (exp(G_t) * q_t)
+
+
+def test_p7_decay_only_product():
+    d = inputs(71, 2, 64, 2, 16, 8)
+    d["beta"][:] = 0
+    o, hT = run(d)
+    G = np.cumsum(f64(d["g"]), axis=1)
+    h0 = f64(d["h0"])
+    exp_o = np.einsum("bhcj,bthc->bthj", h0, np.exp(G) * f64(d["q"]))
+    assert rel_err(o, exp_o) < 1e-13
+    assert rel_err(hT, np.exp(G[:, -1])[..., None] * h0) < 1e-13
+
+
+# --------------------------------------------------------------------------------------------
+# P9: continuation -- two calls with hT -> h0 equal one call (exact in fp64)
+
+
+def test_p9_continuation():
+    d = inputs(91, 2, 96, 2, 16, 8)
+    o, hT = run(d)
+    first = {key: d[key][:, :40] for key in ("q", "k", "v", "g", "beta")}
+    second = {key: d[key][:, 40:] for key in ("q", "k", "v", "g", "beta")}
+    o1, h1 = oracle.forward(**first, h0=d["h0"])
+    o2, h2 = oracle.forward(**second, h0=h1)
+    assert np.array_equal(np.concatenate([o1, o2], axis=1), o)
+    assert np.array_equal(h2, hT)
+
+
+# --------------------------------------------------------------------------------------------
+# P10: the map (h0, V) -> (o, hT) is linear: out(h0, V) = out(h0, 0) + out(0, V)
+
+
+def test_p10_linearity():
+    d = inputs(101, 1, 80, 2, 16, 8)
+    o, hT = run(d)
+    dz = dict(d)
+    dz["v"] = np.zeros_like(d["v"])
+    oa, ha = run(dz)
+    ob, hb = run(d, h0=None)
+    assert rel_err(oa + ob, o) < 1e-13
+    assert rel_err(ha + hb, hT) < 1e-13
+
+
+# --------------------------------------------------------------------------------------------
+# P11: value columns evolve independently: permuting columns of v and h0 permutes o and hT
+
+
+def test_p11_column_independence():
+    d = inputs(111, 1, 50, 2, 16, 12)
+    o, hT = run(d)
+    perm = np.random.default_rng(11).permutation(12)
+    dp = dict(d)
+    dp["v"] = np.ascontiguousarray(d["v"][..., perm])
+    dp["h0"] = np.ascontiguousarray(d["h0"][..., perm])
+    op, hp = run(dp)
+    assert np.array_equal(op, o[..., perm])
+    assert np.array_equal(hp, hT[..., perm])
+    # and a slice of columns alone gives the same columns
+    ds = dict(d)
+    ds["v"] = np.ascontiguousarray(d["v"][..., 4:8])
+    ds["h0"] = np.ascontiguousarray(d["h0"][..., 4:8])
+    os_, hs = run(ds)
+    assert np.array_equal(os_, o[..., 4:8]) and np.array_equal(hs, hT[..., 4:8])
+
+
+# --------------------------------------------------------------------------------------------
+# P12: T single-token decode steps equal one prefill of T tokens
+
+
+def test_p12_decode_equals_prefill():
+    B, T, H, dk, dv = 2, 20, 3, 16, 8
+    d = inputs(121, B, T, H, dk, dv)
+    o, hT = run(d)
+    state = f64(d["h0"]).copy()
+    for t in range(T):
+        ot = oracle.decode_step(d["q"][:, t], d["k"][:, t], d["v"][:, t], d["g"][:, t], d["beta"][:, t], state)
+        assert np.array_equal(ot, o[:, t])
+    assert np.array_equal(state, hT)
+
+
+# --------------------------------------------------------------------------------------------
+# P13: packed varlen equals independent per-sequence calls; nothing crosses a boundary
+
+
+def test_p13_varlen_independent_sequences():
+    lens = [5, 0, 17, 64, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    Tt, H, dk, dv = int(cu[-1]), 2, 16, 8
+    d = inputs(131, 1, Tt, H, dk, dv, h0_std=None)
+    h0 = datagen.fill(131, datagen.TID_H0, 0, 0, 0.02, F32, (len(lens), H, dk, dv), dv)
+    o, hT = oracle.forward_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, h0)
+    for n in range(len(lens)):
+        s, e = cu[n], cu[n + 1]
+        on, hn = oracle.forward(*(d[key][:, s:e] for key in ("q", "k", "v", "g", "beta")), h0=h0[n:n + 1])
+        assert np.array_equal(o[s:e], on[0])
+        assert np.array_equal(hT[n], hn[0])
+    assert np.array_equal(hT[1], f64(h0[1]))  # empty sequence: hT = h0
+
+
+# --------------------------------------------------------------------------------------------
+# P14: contraction -- ||S_t||_F <= ||S_{t-1}||_F + beta_t ||v_t|| when ||k|| = 1, beta in [0,1], alpha <= 1
+
+
+def test_p14_norm_bound():
+    B, T, H, dk, dv = 1, 300, 2, 32, 16
+    d = inputs(141, B, T, H, dk, dv)
+    state = f64(d["h0"]).copy()
+    prev = np.linalg.norm(state, axis=(2, 3))
+    for t in range(T):
+        oracle.decode_step(d["q"][:, t], d["k"][:, t], d["v"][:, t], d["g"][:, t], d["beta"][:, t], state)
+        now = np.linalg.norm(state, axis=(2, 3))
+        bound = prev + f64(d["beta"][:, t]) * np.linalg.norm(f64(d["v"][:, t]), axis=-1)
+        # keys are unit-norm only to fp32 rounding, hence the 1e-6 slack
+        assert np.all(now <= bound * (1 + 1e-6))
+        prev = now
+
+
+# --------------------------------------------------------------------------------------------
+# Edge cases: T = 0 (hT = h0), bf16 inputs decode exactly
+
+
+def test_empty_sequence():
+    d = inputs(151, 2, 0, 2, 8, 4)
+    o, hT = run(d)
+    assert o.shape == (2, 0, 2, 4)
+    assert np.array_equal(hT, f64(d["h0"]))
+    o, hT = run(d, h0=None)
+    assert np.array_equal(hT, np.zeros_like(hT))
+
+
+def test_bf16_inputs_decode_exactly():
+    d32 = datagen.prefill_inputs(161, 1, 20, 2, 16, 8, datagen.DT_BF16, 0.02)
+    dd = {key: (datagen.bf16_bits_to_f32(val) if key != "h0" else val) for key, val in d32.items()}
+    o1, h1 = run(d32)
+    o2, h2 = run(dd)
+    assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
