@@ -1,0 +1,182 @@
+"""Kimi Delta Attention (KDA) on AMD Instinct MI355X -- Python binding of libkda.so.
+
+Thin ctypes marshalling over the C ABI declared in ``include/kda.h``: every
+step of the computation runs in the library's HIP kernels; PyTorch only
+provides device memory and the current stream.  The functions carry the C
+entry points' names:
+
+* ``kda_chunked_forward``        -- chunked prefill, B equal-length sequences
+* ``kda_chunked_forward_varlen`` -- chunked prefill, packed sequences (cu_seqlens)
+* ``kda_decode_step``            -- one token per sequence, state updated in place
+
+Importing this package fails loudly when ``libkda.so`` has not been built
+(``python gated_delta_rule_94_amd/build.py`` or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_HIP"}
+
+# exported symbols of libkda.so (the C ABI)
+EXPORTS = (
+    "kda_status_string", "kda_version", "kda_chunked_forward_workspace_bytes", "kda_chunked_forward",
+    "kda_chunked_forward_varlen", "kda_chunked_forward_varlen_workspace_bytes", "kda_decode_step",
+)
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libkda.so is not built (%s): run `python gated_delta_rule_94_amd/build.py`" % LIB_PATH)
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_lib.kda_status_string.argtypes = [_i32]
+_lib.kda_status_string.restype = ctypes.c_char_p
+_lib.kda_version.argtypes = []
+_lib.kda_version.restype = _i32
+_lib.kda_chunked_forward_workspace_bytes.argtypes = [_i32] * 7
+_lib.kda_chunked_forward_workspace_bytes.restype = _sz
+_lib.kda_chunked_forward_varlen_workspace_bytes.argtypes = [_i32] * 8
+_lib.kda_chunked_forward_varlen_workspace_bytes.restype = _sz
+_lib.kda_chunked_forward.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp, _sz, _vp]
+_lib.kda_chunked_forward.restype = _i32
+_lib.kda_chunked_forward_varlen.argtypes = [_vp] * 8 + [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
+_lib.kda_chunked_forward_varlen.restype = _i32
+_lib.kda_decode_step.argtypes = [_vp] * 7 + [_i32] * 4 + [_i32, _vp]
+_lib.kda_decode_step.restype = _i32
+
+
+class KDAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (%s)" % (fn, STATUS.get(status, status), kda_status_string(status)))
+        self.status = status
+
+
+def kda_status_string(status: int) -> str:
+    return _lib.kda_status_string(int(status)).decode()
+
+
+def kda_version() -> int:
+    return int(_lib.kda_version())
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkda.so (for callers that marshal arguments themselves)."""
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return KDA_F32
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError("KDA inputs must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(name, t, shape, dtype=None, device=None):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (name, dtype, t.dtype))
+    if device is not None and t.device != device:
+        raise ValueError("%s: expected device %s, got %s" % (name, device, t.device))
+
+
+def kda_chunked_forward(q, k, v, g, beta, h0=None, *, chunk: int = 64, o=None, hT=None, want_hT: bool = True,
+                        stream=None):
+    """Chunked prefill.  q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H] (one dtype, float32 or
+    bfloat16); h0 [B,H,dk,dv] float32 or None.  Returns (o [B,T,H,dv], hT [B,H,dk,dv] float32 or None).
+    o / hT may be passed preallocated; hT may be h0 (updated in place)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("g", g, (B, T, H, dk)),
+                         ("v", v, (B, T, H, dv)), ("beta", beta, (B, T, H))):
+        _check(name, t, shp, dt, dev)
+    _check("h0", h0, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check("o", o, (B, T, H, dv), dt, dev)
+    if hT is None and want_hT:
+        hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check("hT", hT, (B, H, dk, dv), torch.float32, dev)
+    ws_bytes = _lib.kda_chunked_forward_workspace_bytes(B, T, H, dk, dv, chunk, _dtype_code(q))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = _lib.kda_chunked_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
+                                  B, T, H, dk, dv, chunk, _dtype_code(q), _ptr(ws), ws_bytes, _stream(stream))
+    if st:
+        raise KDAError("kda_chunked_forward", st)
+    return o, hT
+
+
+def kda_chunked_forward_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen: int, h0=None, *, chunk: int = 64, o=None,
+                               hT=None, want_hT: bool = True, stream=None):
+    """Packed varlen prefill.  q, k, g [1,T_total,H,dk] (or [T_total,H,dk]); v [..,T_total,H,dv];
+    beta [..,T_total,H]; cu_seqlens int32 [N+1] on the device; h0 [N,H,dk,dv] float32 or None.
+    Returns (o shaped like v, hT [N,H,dk,dv] float32 or None)."""
+    Tt, H, dk = q.shape[-3:]
+    dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    dt, dev = q.dtype, q.device
+    lead = tuple(q.shape[:-3])
+    if lead not in ((), (1,)):
+        raise ValueError("varlen inputs are packed along one token axis (batch 1)")
+    for name, t, shp in (("q", q, lead + (Tt, H, dk)), ("k", k, lead + (Tt, H, dk)), ("g", g, lead + (Tt, H, dk)),
+                         ("v", v, lead + (Tt, H, dv)), ("beta", beta, lead + (Tt, H))):
+        _check(name, t, shp, dt, dev)
+    _check("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
+    _check("h0", h0, (N, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty(lead + (Tt, H, dv), dtype=dt, device=dev)
+    _check("o", o, lead + (Tt, H, dv), dt, dev)
+    if hT is None and want_hT:
+        hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _check("hT", hT, (N, H, dk, dv), torch.float32, dev)
+    ws_bytes = _lib.kda_chunked_forward_varlen_workspace_bytes(N, Tt, max_seqlen, H, dk, dv, chunk, _dtype_code(q))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = _lib.kda_chunked_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
+                                         _ptr(cu_seqlens), N, Tt, int(max_seqlen), H, dk, dv, chunk, _dtype_code(q),
+                                         _ptr(ws), ws_bytes, _stream(stream))
+    if st:
+        raise KDAError("kda_chunked_forward_varlen", st)
+    return o, hT
+
+
+def kda_decode_step(q, k, v, g, beta, state, *, o=None, stream=None):
+    """One decode step.  q, k, g [B,H,dk]; v [B,H,dv]; beta [B,H]; state [B,H,dk,dv] float32,
+    updated in place.  Returns o [B,H,dv]."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, shp in (("q", q, (B, H, dk)), ("k", k, (B, H, dk)), ("g", g, (B, H, dk)), ("v", v, (B, H, dv)),
+                         ("beta", beta, (B, H))):
+        _check(name, t, shp, dt, dev)
+    _check("state", state, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+    _check("o", o, (B, H, dv), dt, dev)
+    st = _lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), B, H, dk, dv,
+                              _dtype_code(q), _stream(stream))
+    if st:
+        raise KDAError("kda_decode_step", st)
+    return o

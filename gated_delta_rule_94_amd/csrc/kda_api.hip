@@ -1,0 +1,124 @@
+// C ABI of libkda.so: argument validation, then launches on the caller's stream.
+// Declarations and the contract of every entry point are in include/kda.h.
+#include <stdint.h>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dim_ok(int d) { return d == 64 || d == 128; }
+bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
+
+// Shared checks of the two prefill entry points (everything except the batch geometry).
+kda_status check_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta, const float* h0,
+                         const void* o, const float* hT, int tokens, int H, int d_k, int d_v, int chunk,
+                         kda_dtype dt) {
+  if (H <= 0 || d_k <= 0 || d_v <= 0 || chunk <= 0 || tokens < 0) return KDA_ERR_INVALID_ARG;
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
+  if (tokens > 0) {
+    if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) || !aligned16(o))
+      return KDA_ERR_INVALID_ARG;
+  }
+  if ((h0 && !aligned16(h0)) || (hT && !aligned16(hT))) return KDA_ERR_INVALID_ARG;
+  if (!dim_ok(d_k) || !dim_ok(d_v) || !chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+  if (!kda::chunked_forward_supported(dt == KDA_F32, d_k, d_v, chunk)) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID_ARG: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case KDA_ERR_WORKSPACE: return "workspace too small";
+    case KDA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int kda_version(void) { return 100; }
+
+size_t kda_chunked_forward_workspace_bytes(int, int, int, int, int, int, kda_dtype) { return 0; }
+
+size_t kda_chunked_forward_varlen_workspace_bytes(int, int, int, int, int, int, int, kda_dtype) { return 0; }
+
+kda_status kda_chunked_forward(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                               const float* h0, void* o, float* hT, int B, int T, int H, int d_k, int d_v, int chunk,
+                               kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
+  const kda_status st = check_prefill(q, k, v, g, beta, h0, o, hT, B * T, H, d_k, d_v, chunk, dt);
+  if (st != KDA_OK) return st;
+  if (B == 0) return KDA_OK;
+  if (T == 0 && !hT) return KDA_OK;
+  kda::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.h0 = h0; a.o = o; a.hT = hT;
+  a.cu_seqlens = nullptr;
+  a.num_seqs = B;
+  a.T = T;
+  a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk;
+  a.f32 = dt == KDA_F32;
+  a.stream = hip_stream;
+  return kda::launch_chunked_forward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_chunked_forward_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                      const float* h0, void* o, float* hT, const int32_t* cu_seqlens, int num_seqs,
+                                      int T_total, int max_seqlen, int H, int d_k, int d_v, int chunk, kda_dtype dt,
+                                      void* workspace, size_t workspace_bytes, void* hip_stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (num_seqs < 0 || T_total < 0 || max_seqlen < 0) return KDA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!cu_seqlens || max_seqlen > T_total)) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)num_seqs * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
+  const kda_status st = check_prefill(q, k, v, g, beta, h0, o, hT, T_total, H, d_k, d_v, chunk, dt);
+  if (st != KDA_OK) return st;
+  if (num_seqs == 0) return KDA_OK;
+  kda::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.h0 = h0; a.o = o; a.hT = hT;
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.T = T_total;
+  a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk;
+  a.f32 = dt == KDA_F32;
+  a.stream = hip_stream;
+  return kda::launch_chunked_forward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta, float* state,
+                           void* o, int B, int H, int d_k, int d_v, kda_dtype dt, void* hip_stream) {
+  if (B < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARG;
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)B * H > INT32_MAX / 2) return KDA_ERR_UNSUPPORTED;
+  if (B > 0) {
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) || !aligned16(state) ||
+        !aligned16(o))
+      return KDA_ERR_INVALID_ARG;
+  }
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+  if (B == 0) return KDA_OK;
+  kda::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.state = state;
+  a.o = o;
+  a.units = B * H;
+  a.dk = d_k;
+  a.dv = d_v;
+  a.f32 = dt == KDA_F32;
+  a.stream = hip_stream;
+  return kda::launch_decode_step(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+/*
+ * kda.h -- C ABI of libkda.so, Kimi Delta Attention (KDA) on AMD Instinct MI355X (gfx950).
+ *
+ * KDA is the gated delta-rule linear attention of Kimi K3 (technical-report
+ * page, "Quick answer", "Architecture at a glance" and FAQ "What is Kimi Delta
+ * Attention?"; architecture blog, "Kimi Delta Attention: the linear core").
+ * Per (sequence, head) it carries a fixed-size state S (d_k x d_v, fp32) and,
+ * for every token t,
+ *
+ *   S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T,     o_t = S_t^T q_t
+ *
+ * with g_t the per-key-channel log-decay (the channel-wise forget gate; the
+ * pages bound it below through a scaled sigmoid, so the library expects
+ * -5 <= g <= 0 and takes g as given), beta_t a per-(token, head) write
+ * strength in [0, 1], and no query scaling.  o_t is read after the update.
+ * The prefill entry points evaluate this in its chunkwise form (the pages'
+ * "chunkwise algorithm" on specialised diagonal-plus-low-rank transitions);
+ * the result equals the token-by-token recurrence up to rounding and does not
+ * depend on the chunk size beyond rounding.
+ *
+ * Conventions common to every entry point
+ *  - Every pointer is device memory owned by the caller.  The library never
+ *    allocates or frees device memory and keeps no state between calls.
+ *  - All work is enqueued on `hip_stream` (a hipStream_t; NULL = the null
+ *    stream).  No call synchronises the host, copies between host and device,
+ *    or allocates.  Results are visible once the caller synchronises.
+ *  - Arguments are validated before anything is enqueued: an invalid call
+ *    returns a nonzero status and has no side effects.  A failed launch
+ *    returns KDA_ERR_HIP.  Faults during execution surface at the caller's
+ *    synchronisation.
+ *  - Layouts are row-major and contiguous:
+ *      q, k, g   [B, T, H, d_k]      v, o   [B, T, H, d_v]      beta [B, T, H]
+ *      h0, hT, state   [B, H, d_k, d_v] fp32
+ *    q, k, v, g, beta and o share one dtype (kda_dtype); states are fp32.
+ *  - Supported: d_k, d_v in {64, 128}; chunk in {16, 32, 64}; any T >= 0;
+ *    pointers 16-byte aligned.  fp32 inputs with d_k = 128 need chunk <= 32.
+ *    Anything else returns KDA_ERR_UNSUPPORTED.
+ *  - Deterministic: no atomics; repeated calls give bitwise-identical results.
+ *  - Thread-safe: calls share no mutable state.
+ *  - Inputs are expected in the documented envelope (-5 <= g <= 0,
+ *    0 <= beta <= 1, |q|, |k| of order 1).  Outside it the result is
+ *    unspecified; NaN or Inf in an input propagates to o and hT.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype of q, k, v, g, beta and o (states are always fp32) */
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1, /* null pointer, negative size, misaligned pointer, bad cu_seqlens bound */
+  KDA_ERR_UNSUPPORTED = 2, /* valid but outside the supported shapes */
+  KDA_ERR_WORKSPACE = 3,   /* workspace smaller than the size query returned */
+  KDA_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} kda_status;
+
+/* Static description of a status code (never NULL). */
+const char* kda_status_string(kda_status s);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int kda_version(void);
+
+/*
+ * Bytes of device workspace kda_chunked_forward needs for this shape
+ * (0 = none; the workspace arguments may then be NULL / 0).
+ */
+size_t kda_chunked_forward_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt);
+
+/*
+ * Chunked prefill over B sequences of T tokens each.
+ *   q, k, g [B,T,H,d_k], v [B,T,H,d_v], beta [B,T,H]   (dtype dt)   in
+ *   h0 [B,H,d_k,d_v] fp32                               in, or NULL for a zero initial state
+ *   o  [B,T,H,d_v]   (dtype dt)                          out
+ *   hT [B,H,d_k,d_v] fp32                               out, or NULL if not wanted
+ * hT may be the same pointer as h0 (the state is read before it is
+ * overwritten); any other overlap between outputs and inputs is undefined.
+ * T = 0 writes hT = h0 (or zeros) and nothing else.
+ * chunk: tokens per chunk of the chunkwise form (a performance knob).
+ */
+kda_status kda_chunked_forward(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                               const float* h0, void* o, float* hT, int B, int T, int H, int d_k, int d_v, int chunk,
+                               kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Packed variable-length prefill: num_seqs sequences concatenated along the
+ * token axis (tensors as above with B = 1 and T = T_total); sequence n covers
+ * tokens [cu_seqlens[n], cu_seqlens[n+1]).  cu_seqlens is an int32 device
+ * array of num_seqs + 1 non-decreasing offsets with cu_seqlens[0] = 0 and
+ * cu_seqlens[num_seqs] = T_total; it is read on the device only (no host
+ * synchronisation).  max_seqlen must bound every sequence length; it sizes
+ * nothing on the host and may be an over-estimate.  Chunks restart at every
+ * sequence start and no state crosses a sequence boundary.
+ *   h0, hT [num_seqs, H, d_k, d_v] fp32 (either may be NULL; hT may equal h0).
+ * Offsets that violate the contract above give unspecified results for the
+ * affected sequences but never access memory outside [0, T_total).
+ */
+kda_status kda_chunked_forward_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                      const float* h0, void* o, float* hT, const int32_t* cu_seqlens, int num_seqs,
+                                      int T_total, int max_seqlen, int H, int d_k, int d_v, int chunk, kda_dtype dt,
+                                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes kda_chunked_forward_varlen needs (0 = none). */
+size_t kda_chunked_forward_varlen_workspace_bytes(int num_seqs, int T_total, int max_seqlen, int H, int d_k, int d_v,
+                                                  int chunk, kda_dtype dt);
+
+/*
+ * One decode step for B sequences (one token each), updating the fp32 state
+ * in place (the fixed-size state that replaces a growing KV cache: architecture
+ * blog, "Why the attention stack is the story"; how-K3-works page, "KDA: a
+ * fixed memory instead of a growing bill").
+ *   q, k, g [B,H,d_k], v [B,H,d_v], beta [B,H]   (dtype dt)   in
+ *   state [B,H,d_k,d_v] fp32                      in/out
+ *   o [B,H,d_v] (dtype dt)                        out
+ * The state is read and written once; o needs no second pass over it.
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta, float* state,
+                           void* o, int B, int H, int d_k, int d_v, kda_dtype dt, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,92 @@
+"""The C ABI without a GPU: libkda.so loads, exports every entry point include/kda.h declares,
+and rejects invalid calls synchronously (before anything would be launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+kda = pytest.importorskip("gated_delta_rule_94_amd", reason="libkda.so not built")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 7
+    lib = ctypes.CDLL(kda.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(kda.EXPORTS)
+
+
+def test_status_strings_and_version():
+    assert kda.kda_status_string(0) == "ok"
+    assert "invalid" in kda.kda_status_string(1)
+    assert "unsupported" in kda.kda_status_string(2)
+    assert kda.kda_status_string(99) == "unknown status"
+    assert kda.kda_version() >= 100
+
+
+def test_workspace_queries():
+    lib = kda.lib()
+    assert lib.kda_chunked_forward_workspace_bytes(4, 4096, 16, 128, 128, 64, 1) == 0
+    assert lib.kda_chunked_forward_varlen_workspace_bytes(16, 1 << 20, 131072, 8, 128, 128, 64, 1) == 0
+
+
+FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced because validation fails first
+
+
+def fwd(B=1, T=64, H=2, dk=64, dv=64, chunk=64, dt=1, ptr=FAKE, h0=None, hT=None):
+    return kda.lib().kda_chunked_forward(ptr, ptr, ptr, ptr, ptr, h0, ptr, hT, B, T, H, dk, dv, chunk, dt, None, 0,
+                                         None)
+
+
+def test_prefill_validation():
+    assert fwd(ptr=None) == INVALID
+    assert fwd(ptr=FAKE + 4) == INVALID  # misaligned
+    assert fwd(B=-1) == INVALID
+    assert fwd(T=-1) == INVALID
+    assert fwd(H=0) == INVALID
+    assert fwd(dt=7) == INVALID
+    assert fwd(dk=96) == UNSUPPORTED
+    assert fwd(dv=32) == UNSUPPORTED
+    assert fwd(chunk=48) == UNSUPPORTED
+    assert fwd(chunk=128) == UNSUPPORTED
+    assert fwd(dt=0, dk=128, chunk=64) == UNSUPPORTED  # fp32 with d_k = 128 needs chunk <= 32
+    assert fwd(h0=FAKE + 8) == INVALID
+    # empty batch: nothing to do, null tensors allowed
+    assert fwd(B=0, ptr=None) == OK
+
+
+def test_varlen_validation():
+    lib = kda.lib()
+    call = lambda cu, N, Tt, ms, ptr=FAKE: lib.kda_chunked_forward_varlen(ptr, ptr, ptr, ptr, ptr, None, ptr, None,
+                                                                         cu, N, Tt, ms, 2, 64, 64, 64, 1, None, 0,
+                                                                         None)
+    assert call(None, 2, 100, 60) == INVALID       # missing cu_seqlens
+    assert call(FAKE, -1, 100, 60) == INVALID
+    assert call(FAKE, 2, 100, 101) == INVALID      # max_seqlen beyond T_total
+    assert call(FAKE, 2, 100, 60, ptr=None) == INVALID
+    assert call(None, 0, 0, 0, ptr=None) == OK     # nothing to do
+
+
+def test_decode_validation():
+    lib = kda.lib()
+    call = lambda B=2, H=2, dk=64, dv=64, dt=1, ptr=FAKE: lib.kda_decode_step(ptr, ptr, ptr, ptr, ptr, ptr, ptr, B, H,
+                                                                             dk, dv, dt, None)
+    assert call(ptr=None) == INVALID
+    assert call(ptr=FAKE + 2) == INVALID
+    assert call(H=0) == INVALID
+    assert call(dk=32) == UNSUPPORTED
+    assert call(dt=3) == INVALID
+    assert call(B=0, ptr=None) == OK
