@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""KDA benchmark on one MI355X: chunked prefill throughput (headline) plus decode bandwidth.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one kda_chunked_forward call over the 4-sequence x 16-head x
+4096-token bf16 workload (fp32 state, random h0, chunk 64): the gate cumsum,
+the intra-chunk UT/WY transform and the inter-chunk state chain, all in one
+kernel.  Inputs are resident in HBM before the timed region; before every
+timed step a 512 MiB buffer is written so the 256 MB Infinity Cache holds
+none of the step's inputs.  Each launch is bracketed by HIP events on the
+stream it runs on; ms_per_step is their mean.
+
+The JSON line carries:
+  roofline      -- the prefill kernel against HBM (its binding roof: 110
+                   algorithmic flop per byte is below the bf16 ridge of ~315);
+                   achieved = algorithmic bytes per launch / mean launch time
+  roofline_mfma -- the same kernel's algorithmic flops against dense bf16 MFMA
+  decode        -- 1000 sequential kda_decode_step calls on the 256-sequence x
+                   32-head state (512 MiB fp32), bytes and fraction of HBM
+  cpu_baseline  -- the fp64 oracle on this host's cores over the same
+                   prefill workload (a baseline, not a target)
+Algorithmic work per token and head (d_k = d_v = d, chunk C):
+  flops 6 d^2 + (C-1) d + 2 (C+1) d + 2 (C+1) d + C^2/3 ; bytes (3 d_k + d_v) s_in + s_beta + d_v s_out,
+  plus 2 * 4 d_k d_v per (sequence, head) for h0 and hT.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2516.6  # MI355X dense bf16 MFMA
+PREFILL_SRC = os.path.join(ROOT, "gated_delta_rule_94_amd", "csrc", "kda_prefill.hip")
+DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_94_amd", "csrc", "kda_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def prefill_flops_per_token_head(dk, dv, C):
+    return 6 * dk * dv + (C - 1) * dk + 2 * (C + 1) * dk + 2 * (C + 1) * dv + C * C / 3.0
+
+
+def prefill_bytes(B, T, H, dk, dv, s_in, s_out, with_h0=True, with_hT=True):
+    per_th = (3 * dk + dv) * s_in + s_in + dv * s_out
+    return B * T * H * per_th + B * H * 4 * dk * dv * (int(with_h0) + int(with_hT))
+
+
+def decode_bytes(B, H, dk, dv, s_in):
+    return B * H * (2 * 4 * dk * dv + (3 * dk + dv) * s_in + s_in + dv * s_in)
+
+
+def sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel_key, src):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if taken on this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha256") != sha256(src):
+        return None
+    return t["bytes_per_launch"]
+
+
+def world_size():
+    return int(os.environ.get("WORLD_SIZE", "1"))
+
+
+def copy_calibration():
+    """One plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = 1 << 28  # 1 GiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n}))
+
+
+def time_launches(fn, steps, flush=None):
+    """Mean duration of `fn` over `steps` launches, each bracketed by events on the current stream."""
+    import torch
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(steps):
+        if flush is not None:
+            flush()
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return sum(ms) / len(ms), wall
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict the Infinity Cache between steps")
+    ap.add_argument("--copy-calibration", action="store_true", help="run one 1 GiB copy (counter scaling) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or world_size() != 1:
+        print("bench.py runs on one GPU only: the KDA path here is the single-GPU kernel "
+              "(multi-GPU sharding is a design note, not built); got --gpus %d, WORLD_SIZE=%d"
+              % (args.gpus, world_size()), file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import datagen
+    import gated_delta_rule_94_amd as kda
+
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---------------- prefill (headline)
+    w = datagen.WORKLOADS["cfg1_bf16_b4_h16_t4096_d128"]
+    d = datagen.prefill_inputs(w.seed, w.B, w.T, w.H, w.dk, w.dv, w.dtype, w.h0_std)
+    g = {key: to_dev(val) for key, val in d.items()}
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    scratch = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def step(_i):
+        kda.kda_chunked_forward(g["q"], g["k"], g["v"], g["g"], g["beta"], g["h0"], chunk=w.chunk, o=o, hT=hT)
+
+    def flush():
+        scratch.fill_(1)
+
+    for _ in range(args.warmup):
+        step(0)
+    torch.cuda.synchronize()
+    ms, wall = time_launches(step, args.steps, None if args.no_flush else flush)
+    s_in = 2
+    tokens = w.B * w.T
+    alg_bytes = prefill_bytes(w.B, w.T, w.H, w.dk, w.dv, s_in, s_in)
+    alg_flops = w.B * w.T * w.H * prefill_flops_per_token_head(w.dk, w.dv, w.chunk)
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    tfs = alg_flops / (ms * 1e-3) / 1e12
+    traffic = measured_traffic("prefill", PREFILL_SRC)
+
+    out = {
+        "metric": "KDA prefill tokens/s (% bf16 MFMA peak); decode GB/s (% HBM peak)",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded SplitMix64/Box-Muller inputs with the workload's distributions",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d_k": w.dk, "d_v": w.dv, "chunk": w.chunk,
+                   "state": "fp32", "h0": "N(0, 0.02)", "tokens_per_step": tokens,
+                   "cache_flushed_between_steps": not args.no_flush},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "chunked_forward_kernel<bf16, d_k 128, chunk 64>",
+                     "alg_bytes_per_launch": alg_bytes},
+        "roofline_mfma": {"achieved": tfs, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                          "frac": tfs / MFMA_BF16_PEAK_TFS, "alg_flops_per_launch": alg_flops},
+        "wall_s_timed_region": wall,
+    }
+
+    # ---------------- decode
+    if not args.no_decode:
+        wd = datagen.WORKLOADS["cfg3_decode_b256_h32_d128"]
+        state = to_dev(datagen.decode_state0(wd.seed, wd.B, wd.H, wd.dk, wd.dv))
+        pool = []
+        for s in range(8):  # distinct inputs, used round-robin (decode time does not depend on values)
+            dd = datagen.decode_inputs(wd.seed, s, wd.B, wd.H, wd.dk, wd.dv, wd.dtype)
+            pool.append([to_dev(dd[key]) for key in ("q", "k", "v", "g", "beta")])
+        od = torch.empty((wd.B, wd.H, wd.dv), dtype=torch.bfloat16, device=dev)
+
+        def dstep(i):
+            kda.kda_decode_step(*pool[i % len(pool)], state, o=od)
+
+        for i in range(3):
+            dstep(i)
+        torch.cuda.synchronize()
+        dms, dwall = time_launches(dstep, args.decode_steps)
+        dbytes = decode_bytes(wd.B, wd.H, wd.dk, wd.dv, 2)
+        dgbs = dbytes / (dms * 1e-3) / 1e9
+        out["decode"] = {
+            "workload": wd.name, "steps": args.decode_steps, "us_per_step": dms * 1e3,
+            "tokens_per_s": wd.B / (dms * 1e-3), "wall_s": dwall,
+            "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dgbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode", DECODE_SRC),
+                         "kernel": "decode_step_kernel<bf16, 128, 128>", "alg_bytes_per_launch": dbytes},
+        }
+        del state, pool
+
+    # ---------------- CPU baseline: the fp64 oracle on this host's cores, same prefill workload
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = max(1, min(16, os.cpu_count() or 1))
+        t0 = time.perf_counter()
+        oracle.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], nthreads=threads)
+        secs = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": tokens / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": "the full prefill workload (4 x 4096 tokens x 16 heads, fp64, token by "
+                                         "token), %.1f s wall on %d threads" % (secs, threads)}
+
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
