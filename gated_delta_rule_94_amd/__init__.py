@@ -89,6 +89,29 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
+def _workspace(ws, nbytes, dev):
+    if ws is not None:
+        if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.device != dev:
+            raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+
+
+def _nbytes(ws):
+    return 0 if ws is None else ws.numel()
+
+
+def workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:
+    """Device workspace kda_chunked_forward needs for this shape."""
+    return int(_lib.kda_chunked_forward_workspace_bytes(B, T, H, dk, dv, chunk, _dtype_code(torch.empty(0, dtype=dtype))))
+
+
+def varlen_workspace_bytes(num_seqs, T_total, max_seqlen, H, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:
+    """Device workspace kda_chunked_forward_varlen needs for this shape."""
+    return int(_lib.kda_chunked_forward_varlen_workspace_bytes(num_seqs, T_total, max_seqlen, H, dk, dv, chunk,
+                                                                _dtype_code(torch.empty(0, dtype=dtype))))
+
+
 def _check(name, t, shape, dtype=None, device=None):
     if t is None:
         return
@@ -103,10 +126,11 @@ def _check(name, t, shape, dtype=None, device=None):
 
 
 def kda_chunked_forward(q, k, v, g, beta, h0=None, *, chunk: int = 64, o=None, hT=None, want_hT: bool = True,
-                        stream=None):
+                        workspace=None, stream=None):
     """Chunked prefill.  q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H] (one dtype, float32 or
     bfloat16); h0 [B,H,dk,dv] float32 or None.  Returns (o [B,T,H,dv], hT [B,H,dk,dv] float32 or None).
-    o / hT may be passed preallocated; hT may be h0 (updated in place)."""
+    o / hT may be passed preallocated; hT may be h0 (updated in place).  workspace: a uint8 device
+    tensor of at least kda_chunked_forward_workspace_bytes(...) bytes, or None to allocate one."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt, dev = q.dtype, q.device
@@ -121,16 +145,16 @@ def kda_chunked_forward(q, k, v, g, beta, h0=None, *, chunk: int = 64, o=None, h
         hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _check("hT", hT, (B, H, dk, dv), torch.float32, dev)
     ws_bytes = _lib.kda_chunked_forward_workspace_bytes(B, T, H, dk, dv, chunk, _dtype_code(q))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    ws = _workspace(workspace, ws_bytes, dev)
     st = _lib.kda_chunked_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
-                                  B, T, H, dk, dv, chunk, _dtype_code(q), _ptr(ws), ws_bytes, _stream(stream))
+                                  B, T, H, dk, dv, chunk, _dtype_code(q), _ptr(ws), _nbytes(ws), _stream(stream))
     if st:
         raise KDAError("kda_chunked_forward", st)
     return o, hT
 
 
 def kda_chunked_forward_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen: int, h0=None, *, chunk: int = 64, o=None,
-                               hT=None, want_hT: bool = True, stream=None):
+                               hT=None, want_hT: bool = True, workspace=None, stream=None):
     """Packed varlen prefill.  q, k, g [1,T_total,H,dk] (or [T_total,H,dk]); v [..,T_total,H,dv];
     beta [..,T_total,H]; cu_seqlens int32 [N+1] on the device; h0 [N,H,dk,dv] float32 or None.
     Returns (o shaped like v, hT [N,H,dk,dv] float32 or None)."""
@@ -153,10 +177,10 @@ def kda_chunked_forward_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen: int, h0
         hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _check("hT", hT, (N, H, dk, dv), torch.float32, dev)
     ws_bytes = _lib.kda_chunked_forward_varlen_workspace_bytes(N, Tt, max_seqlen, H, dk, dv, chunk, _dtype_code(q))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    ws = _workspace(workspace, ws_bytes, dev)
     st = _lib.kda_chunked_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
                                          _ptr(cu_seqlens), N, Tt, int(max_seqlen), H, dk, dv, chunk, _dtype_code(q),
-                                         _ptr(ws), ws_bytes, _stream(stream))
+                                         _ptr(ws), _nbytes(ws), _stream(stream))
     if st:
         raise KDAError("kda_chunked_forward_varlen", st)
     return o, hT

@@ -45,21 +45,38 @@ const char* kda_status_string(kda_status s) {
 
 int kda_version(void) { return 100; }
 
-size_t kda_chunked_forward_workspace_bytes(int, int, int, int, int, int, kda_dtype) { return 0; }
+size_t kda_chunked_forward_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt) {
+  if (B <= 0 || T < 0 || H <= 0 || !chunk_ok(chunk) || (dt != KDA_F32 && dt != KDA_BF16)) return 0;
+  const int64_t max_chunks = (int64_t)B * ((T + chunk - 1) / chunk);
+  return kda::chunked_forward_workspace(dt == KDA_F32, d_k, d_v, chunk, max_chunks, H, B, false);
+}
 
-size_t kda_chunked_forward_varlen_workspace_bytes(int, int, int, int, int, int, int, kda_dtype) { return 0; }
+size_t kda_chunked_forward_varlen_workspace_bytes(int num_seqs, int T_total, int max_seqlen, int H, int d_k, int d_v,
+                                                  int chunk, kda_dtype dt) {
+  (void)max_seqlen;
+  if (num_seqs <= 0 || T_total < 0 || H <= 0 || !chunk_ok(chunk) || (dt != KDA_F32 && dt != KDA_BF16)) return 0;
+  const int64_t max_chunks = (int64_t)T_total / chunk + num_seqs;
+  return kda::chunked_forward_workspace(dt == KDA_F32, d_k, d_v, chunk, max_chunks, H, num_seqs, true);
+}
+
+namespace {
+bool workspace_ok(void* ws, size_t have, size_t need) {
+  if (need == 0) return true;
+  return ws != nullptr && have >= need && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0;
+}
+}  // namespace
 
 kda_status kda_chunked_forward(const void* q, const void* k, const void* v, const void* g, const void* beta,
                                const float* h0, void* o, float* hT, int B, int T, int H, int d_k, int d_v, int chunk,
                                kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
   if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
   const kda_status st = check_prefill(q, k, v, g, beta, h0, o, hT, B * T, H, d_k, d_v, chunk, dt);
   if (st != KDA_OK) return st;
   if (B == 0) return KDA_OK;
   if (T == 0 && !hT) return KDA_OK;
+  if (!workspace_ok(workspace, workspace_bytes, kda_chunked_forward_workspace_bytes(B, T, H, d_k, d_v, chunk, dt)))
+    return KDA_ERR_WORKSPACE;
   kda::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.h0 = h0; a.o = o; a.hT = hT;
@@ -68,6 +85,8 @@ kda_status kda_chunked_forward(const void* q, const void* k, const void* v, cons
   a.T = T;
   a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk;
   a.f32 = dt == KDA_F32;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
   a.stream = hip_stream;
   return kda::launch_chunked_forward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -76,14 +95,15 @@ kda_status kda_chunked_forward_varlen(const void* q, const void* k, const void* 
                                       const float* h0, void* o, float* hT, const int32_t* cu_seqlens, int num_seqs,
                                       int T_total, int max_seqlen, int H, int d_k, int d_v, int chunk, kda_dtype dt,
                                       void* workspace, size_t workspace_bytes, void* hip_stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (num_seqs < 0 || T_total < 0 || max_seqlen < 0) return KDA_ERR_INVALID_ARG;
   if (num_seqs > 0 && (!cu_seqlens || max_seqlen > T_total)) return KDA_ERR_INVALID_ARG;
   if ((int64_t)num_seqs * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
   const kda_status st = check_prefill(q, k, v, g, beta, h0, o, hT, T_total, H, d_k, d_v, chunk, dt);
   if (st != KDA_OK) return st;
   if (num_seqs == 0) return KDA_OK;
+  if (!workspace_ok(workspace, workspace_bytes,
+                    kda_chunked_forward_varlen_workspace_bytes(num_seqs, T_total, max_seqlen, H, d_k, d_v, chunk, dt)))
+    return KDA_ERR_WORKSPACE;
   kda::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.h0 = h0; a.o = o; a.hT = hT;
@@ -92,6 +112,8 @@ kda_status kda_chunked_forward_varlen(const void* q, const void* k, const void* 
   a.T = T_total;
   a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk;
   a.f32 = dt == KDA_F32;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
   a.stream = hip_stream;
   return kda::launch_chunked_forward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

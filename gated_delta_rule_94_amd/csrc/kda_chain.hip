@@ -1,0 +1,328 @@
+// KDA inter-chunk state propagation on gfx950.
+//
+// Sequential over the chunks of one (sequence, head), given each chunk's record (kda_record.h):
+//   U  = U~ - W S            (the delta rule's writes, corrected for what S already stores)
+//   O  = (Q . Gamma) S + P U
+//   S  = Diag(e^{G_last}) S + (K . e^{G_last - G})^T U
+// (Kimi K3 pages: the fixed-size recurrent state, architecture blog "Why the attention stack is
+// the story"; its per-channel decay and delta-rule write, "Kimi Delta Attention: the linear
+// core".)  Value columns of S evolve independently (the gate acts on key rows), so each
+// workgroup owns a WS-column slice of the state and the slices of one head run on different
+// CUs -- exact, and it spreads even one long sequence over several CUs.
+//
+// Workgroup of four waves: WS / 16 chain waves, each owning 16 value columns of the state, and
+// the others copy.
+// The fp32 state lives in MFMA accumulator registers and is fed back as the B operand of the
+// next chunk's products; U likewise.  The copy waves stream records from HBM into double-buffered
+// LDS two chunks ahead (two register staging sets): while the chain waves compute chunk n, the
+// copy waves write chunk n+1 into the other buffer and load chunk n+2.
+#include "kda_device.h"
+#include "kda_internal.h"
+#include "kda_record.h"
+
+namespace kda {
+
+struct ChainParams {
+  const unsigned char* ws;  // records, (chunk, head) order
+  const float* h0;
+  void* o;
+  float* hT;
+  const int32_t* cu;      // packed offsets, or NULL
+  const int32_t* chunk0;  // first chunk per packed sequence, or NULL
+  int units, H, T, nch, dv;
+};
+
+template <bool F32, int DK, int DV, int C, int WS>
+struct ChainCfg {
+  using O = Op<F32>;
+  using E = typename O::E;
+  using R = Rec<F32, DK, DV, C>;
+  static constexpr int NT = C / 16, CP = R::CP;
+  static constexpr int NW = WS / 16;  // chain waves
+  static constexpr int NH = 4 - NW;   // copy waves
+  static constexpr int NTH = 256;
+  static constexpr int NC = 64 * NH;  // copy threads
+  static_assert(NW >= 1 && NH >= 2, "slice of 16 or 32 columns");
+  static constexpr int RS = DK + 8, TS = CP + 8, US = C + 8;  // US: stride of the U~^T slice [WS][C]
+  static constexpr int ES = (int)sizeof(E);
+  static constexpr int EPU = 16 / ES;  // elements per 16-byte copy unit
+  static constexpr int al(int x) { return (x + 15) & ~15; }
+  static constexpr int B_NW = 0;
+  static constexpr int B_QG = al(B_NW + C * RS * ES);
+  static constexpr int B_P = al(B_QG + C * RS * ES);
+  static constexpr int B_KPT = al(B_P + C * TS * ES);
+  static constexpr int B_UT = al(B_KPT + DK * TS * ES);
+  static constexpr int B_GAM = al(B_UT + WS * US * ES);
+  static constexpr int BUF = al(B_GAM + DK * 4);
+  static constexpr int TOTAL = 2 * BUF;
+  static_assert(TOTAL <= 163840, "LDS budget of one gfx950 workgroup");
+  // 16-byte copy units of one record slice: -W, Q.Gamma, P, K'^T, U~ slice, gamma
+  static constexpr int U_NW = C * DK / EPU, U_QG = C * DK / EPU, U_P = C * CP / EPU, U_KPT = DK * CP / EPU;
+  static constexpr int U_UT = WS * C / EPU, U_GAM = DK / 4;
+  static constexpr int UNITS = U_NW + U_QG + U_P + U_KPT + U_UT + U_GAM;
+  static constexpr int UPT = (UNITS + NTH - 1) / NTH;  // units per thread
+};
+
+// One part of a record copied by the NC copy threads in 16-byte units: NU units, UPR units per
+// row.  Units past the end repeat the last one (same bytes to the same place), so the copy has no
+// branches and the compiler counts outstanding loads exactly across the pipeline.
+template <int NC, int NU, int UPR, int GBASE, int GROW, int LBASE, int LROW>
+struct CopyPart {
+  static constexpr int K = (NU + NC - 1) / NC;
+  typedef uint32_t vec_t __attribute__((ext_vector_type(4 * K)));
+  vec_t st;  // K 16-byte slots in one vector so that it stays in registers
+  __device__ static __forceinline__ int unit(int ht, int k) {
+    const int u = ht + NC * k;
+    return u < NU ? u : NU - 1;
+  }
+  __device__ __forceinline__ void load(const unsigned char* rec, int ht) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int u = unit(ht, k);
+      const uint4 x = *reinterpret_cast<const uint4*>(rec + GBASE + (u / UPR) * GROW + 16 * (u % UPR));
+      st[4 * k] = x.x;
+      st[4 * k + 1] = x.y;
+      st[4 * k + 2] = x.z;
+      st[4 * k + 3] = x.w;
+    }
+  }
+  __device__ __forceinline__ void store(unsigned char* buf, int ht) const {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int u = unit(ht, k);
+      *reinterpret_cast<uint4*>(buf + LBASE + (u / UPR) * LROW + 16 * (u % UPR)) =
+          make_uint4(st[4 * k], st[4 * k + 1], st[4 * k + 2], st[4 * k + 3]);
+    }
+  }
+};
+
+template <bool F32, int DK, int DV, int C, int WS>
+__global__ __launch_bounds__(256) void chain_kernel(const ChainParams p) {
+  using Cf = ChainCfg<F32, DK, DV, C, WS>;
+  using O = typename Cf::O;
+  using E = typename Cf::E;
+  using R = typename Cf::R;
+  using Frag = typename O::Frag;
+  constexpr int NT = Cf::NT, CP = Cf::CP, RS = Cf::RS, TS = Cf::TS, US = Cf::US, EPU = Cf::EPU;
+  constexpr int KSD = O::nks(DK), KSC = O::nks(CP);
+  __shared__ __align__(16) unsigned char smem[Cf::TOTAL];
+
+  // ---- (unit, slice); the slices of one unit share an XCD (block id mod 8)
+  const int DVr = p.dv;
+  constexpr int nsl_c = DV / WS;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int unit = (idx / nsl_c) * 8 + xcd;
+  const int slice = idx - (idx / nsl_c) * nsl_c;
+  if (unit >= p.units) return;
+  const int H = p.H;
+  const int n = unit / H, h = unit - n * H;
+  int64_t t_begin, t_end, first;
+  if (p.cu) {
+    int x = p.cu[n], y = p.cu[n + 1];
+    x = x < 0 ? 0 : (x > p.T ? p.T : x);
+    y = y < x ? x : (y > p.T ? p.T : y);
+    t_begin = x;
+    t_end = y;
+    first = p.chunk0[n];
+  } else {
+    t_begin = (int64_t)n * p.T;
+    t_end = t_begin + p.T;
+    first = (int64_t)n * p.nch;
+  }
+  const int nchunks = (int)((t_end - t_begin + C - 1) / C);
+  const int col0 = slice * WS;
+  const int tid = threadIdx.x, lane = tid & 63, lo = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool chain = wave < Cf::NW;
+  const int ccol = col0 + 16 * (chain ? wave : 0) + lo;  // value column of this lane
+  const int64_t sbase = (int64_t)unit * DK * DVr;
+
+  // ---- state S in accumulator layout: Sacc[m][r] = S[16 m + 4 grp + r][ccol]
+  f32x4 Sacc[DK / 16];
+#pragma unroll
+  for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      Sacc[m][r] = (chain && p.h0) ? p.h0[sbase + (int64_t)(16 * m + 4 * grp + r) * DVr + ccol] : 0.f;
+
+  // ---- record streaming: 16-byte units, global -> registers -> LDS.  Two register staging sets
+  // alternate, so a record's loads are issued two chunks before it is computed.
+  auto rec_of = [&](int c) -> const unsigned char* { return p.ws + ((first + c) * H + h) * R::BYTES; };
+  constexpr int ES_ = Cf::ES;
+  struct Stage {
+    CopyPart<Cf::NC, Cf::U_NW, DK / EPU, (int)(R::NW * ES_), DK * ES_, Cf::B_NW, RS * ES_> nw;
+    CopyPart<Cf::NC, Cf::U_QG, DK / EPU, (int)(R::QG * ES_), DK * ES_, Cf::B_QG, RS * ES_> qg;
+    CopyPart<Cf::NC, Cf::U_P, CP / EPU, (int)(R::P * ES_), CP * ES_, Cf::B_P, TS * ES_> pp;
+    CopyPart<Cf::NC, Cf::U_KPT, CP / EPU, (int)(R::KPT * ES_), CP * ES_, Cf::B_KPT, TS * ES_> kpt;
+    CopyPart<Cf::NC, Cf::U_UT, C / EPU, (int)(R::UT * ES_), C * ES_, Cf::B_UT, US * ES_> ut;  // record pointer + col0 rows
+    CopyPart<Cf::NC, Cf::U_GAM, Cf::U_GAM, (int)R::GAM_BYTE, 0, Cf::B_GAM, 0> gam;
+    __device__ __forceinline__ void load(const unsigned char* rp, int ht, int col0b) {
+      nw.load(rp, ht); qg.load(rp, ht); pp.load(rp, ht); kpt.load(rp, ht); ut.load(rp + col0b, ht); gam.load(rp, ht);
+    }
+    __device__ __forceinline__ void store(unsigned char* b, int ht) const {
+      nw.store(b, ht); qg.store(b, ht); pp.store(b, ht); kpt.store(b, ht); ut.store(b, ht); gam.store(b, ht);
+    }
+  };
+  const int ht = tid - 64 * Cf::NW;  // copy-thread index (copy waves only)
+  const int ostride = H * DVr;              // output elements between consecutive tokens
+  const int o_lane = 4 * grp * ostride + ccol;  // this lane's output offset within a 16-token tile
+  const int col0b = col0 * C * ES_;  // first U~^T row of the slice
+
+  // one chunk of the chain from LDS buffer `buf`
+  auto chunk_step = [&](int c, int buf) {
+    const unsigned char* b = smem + buf * Cf::BUF;
+    const E* Wn = reinterpret_cast<const E*>(b + Cf::B_NW);
+    const E* QG = reinterpret_cast<const E*>(b + Cf::B_QG);
+    const E* Ps = reinterpret_cast<const E*>(b + Cf::B_P);
+    const E* Kpt = reinterpret_cast<const E*>(b + Cf::B_KPT);
+    const E* Ut = reinterpret_cast<const E*>(b + Cf::B_UT);
+    const float* Gam = reinterpret_cast<const float*>(b + Cf::B_GAM);
+    const int64_t t0 = t_begin + (int64_t)c * C;
+    const int len = (int)((t_end - t0) < C ? (t_end - t0) : C);
+    const int64_t obase = (t0 * H + h) * DVr;  // output element of (token t0, head h, column 0): uniform
+    if (!chain) return;
+    Frag Sf[KSD];
+#pragma unroll
+    for (int sk = 0; sk < KSD; ++sk) Sf[sk] = O::from_acc(Sacc, sk);
+    // all fragments of -W and Q . Gamma up front: their LDS latency overlaps, and four independent
+    // accumulators per product keep the MFMA pipe busy
+    Frag wf[NT][KSD], qf[NT][KSD];
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt)
+#pragma unroll
+      for (int sk = 0; sk < KSD; ++sk) {
+        wf[bt][sk] = O::ld(Wn + (16 * bt + lo) * RS, sk, grp);
+        qf[bt][sk] = O::ld(QG + (16 * bt + lo) * RS, sk, grp);
+      }
+    // U = U~ - W S   (U~^T in LDS: this lane's 4 tokens of its column are contiguous)
+    f32x4 U[NT], Ob[NT];
+    const E* ut = Ut + (16 * wave + lo) * US + 4 * grp;
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt) {
+      if constexpr (F32) {
+        const float4 x = *reinterpret_cast<const float4*>(ut + 16 * bt);
+        U[bt] = f32x4{x.x, x.y, x.z, x.w};
+      } else {
+        const bf16x4 x = *reinterpret_cast<const bf16x4*>(ut + 16 * bt);
+        U[bt] = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+      }
+      Ob[bt] = zero4();
+    }
+#pragma unroll
+    for (int sk = 0; sk < KSD; ++sk)
+#pragma unroll
+      for (int bt = 0; bt < NT; ++bt) U[bt] = O::mma(wf[bt][sk], Sf[sk], U[bt]);
+    // O = (Q . Gamma) S + P U
+#pragma unroll
+    for (int sk = 0; sk < KSD; ++sk)
+#pragma unroll
+      for (int bt = 0; bt < NT; ++bt) Ob[bt] = O::mma(qf[bt][sk], Sf[sk], Ob[bt]);
+    Frag uf[KSC];
+#pragma unroll
+    for (int sk = 0; sk < KSC; ++sk) uf[sk] = O::from_acc(U, sk);
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt) {
+      const E* prow = Ps + (16 * bt + lo) * TS;
+#pragma unroll
+      for (int sk = 0; sk < O::nks(16 * (bt + 1)); ++sk) Ob[bt] = O::mma(O::ld(prow, sk, grp), uf[sk], Ob[bt]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tr = 16 * bt + 4 * grp + r;
+        if (tr < len) stg<F32>(p.o, obase + (o_lane + (16 * bt + r) * ostride), Ob[bt][r]);
+      }
+    }
+    // S = Diag(gamma) S + K'^T U
+    Frag kf[DK / 16][KSC];
+#pragma unroll
+    for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+      for (int sk = 0; sk < KSC; ++sk) kf[m][sk] = O::ld(Kpt + (16 * m + lo) * TS, sk, grp);
+#pragma unroll
+    for (int m = 0; m < DK / 16; ++m) {
+      const float4 gm = *reinterpret_cast<const float4*>(Gam + 16 * m + 4 * grp);
+      f32x4 acc = Sacc[m];
+      acc[0] *= gm.x;
+      acc[1] *= gm.y;
+      acc[2] *= gm.z;
+      acc[3] *= gm.w;
+#pragma unroll
+      for (int sk = 0; sk < KSC; ++sk) acc = O::mma(kf[m][sk], uf[sk], acc);
+      Sacc[m] = acc;
+    }
+  };
+
+  // Chain waves compute; copy waves stream records.  The two roles run separate loops with the same
+  // barriers, so each role's registers are live on its own path only.  Prologue: chunk 0 in buffer
+  // 0, chunk 1 loading into s1.  Chunk indices past the last are clamped to it: those copies repeat
+  // the last record into a buffer nobody reads.
+  // Invariant at chunk c: buffer c&1 holds chunk c, stage (c+1)&1 holds chunk c+1, stage c&1 is
+  // free; the copy waves fill buffer (c+1)&1 while the chain waves read buffer c&1.
+  const int last = nchunks - 1;
+  if (chain) {
+    __syncthreads();
+    for (int c = 0; c < nchunks; c += 2) {
+      chunk_step(c, 0);
+      __syncthreads();
+      if (c + 1 >= nchunks) break;
+      chunk_step(c + 1, 1);
+      __syncthreads();
+    }
+  } else {
+    Stage s0, s1;
+    if (nchunks > 0) {
+      s0.load(rec_of(0), ht, col0b);
+      s0.store(smem, ht);
+      s1.load(rec_of(last < 1 ? last : 1), ht, col0b);
+    }
+    __syncthreads();
+    for (int c = 0; c < nchunks; c += 2) {
+      s0.load(rec_of(c + 2 < last ? c + 2 : last), ht, col0b);
+      s1.store(smem + Cf::BUF, ht);
+      __syncthreads();
+      if (c + 1 >= nchunks) break;
+      s1.load(rec_of(c + 3 < last ? c + 3 : last), ht, col0b);
+      s0.store(smem, ht);
+      __syncthreads();
+    }
+  }
+
+  if (chain && p.hT) {
+#pragma unroll
+    for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p.hT[sbase + (int64_t)(16 * m + 4 * grp + r) * DVr + ccol] = Sacc[m][r];
+  }
+}
+
+template <bool F32, int DK, int DV, int C, int WS>
+static hipError_t launch_chain_impl(const ChainLaunch& L) {
+  ChainParams p;
+  p.ws = L.records; p.h0 = L.h0; p.o = L.o; p.hT = L.hT; p.cu = L.cu; p.chunk0 = L.chunk0;
+  p.units = L.units; p.H = L.H; p.T = L.T; p.nch = L.nch; p.dv = DV;
+  const int grid = ((L.units + 7) / 8) * 8 * (DV / WS);
+  hipLaunchKernelGGL((chain_kernel<F32, DK, DV, C, WS>), dim3(grid), dim3(256), 0, (hipStream_t)L.stream, p);
+  return hipGetLastError();
+}
+
+// Slice width: bf16 picks 32 or 16 value columns per workgroup (16 -- more workgroups -- when there
+// are few (sequence, head) units); fp32 uses 16.
+#define KDA_CHAIN_BF16(X, D, V, CC) X(false, D, V, CC, 32) X(false, D, V, CC, 16)
+#define KDA_CHAIN_INSTANCES(X)                                                                                   \
+  KDA_CHAIN_BF16(X, 64, 64, 16) KDA_CHAIN_BF16(X, 64, 64, 32) KDA_CHAIN_BF16(X, 64, 64, 64)                        \
+  KDA_CHAIN_BF16(X, 64, 128, 16) KDA_CHAIN_BF16(X, 64, 128, 32) KDA_CHAIN_BF16(X, 64, 128, 64)                     \
+  KDA_CHAIN_BF16(X, 128, 64, 16) KDA_CHAIN_BF16(X, 128, 64, 32) KDA_CHAIN_BF16(X, 128, 64, 64)                     \
+  KDA_CHAIN_BF16(X, 128, 128, 16) KDA_CHAIN_BF16(X, 128, 128, 32) KDA_CHAIN_BF16(X, 128, 128, 64)                  \
+  X(true, 64, 64, 16, 16) X(true, 64, 64, 32, 16) X(true, 64, 64, 64, 16)                                         \
+  X(true, 64, 128, 16, 16) X(true, 64, 128, 32, 16) X(true, 64, 128, 64, 16)                                      \
+  X(true, 128, 64, 16, 16) X(true, 128, 64, 32, 16) X(true, 128, 128, 16, 16) X(true, 128, 128, 32, 16)
+
+hipError_t launch_chain(const ChainLaunch& L) {
+#define KDA_LAUNCH(F, D, V, CC, W) \
+  if (L.f32 == F && L.dk == D && L.dv == V && L.chunk == CC && L.ws == W) return launch_chain_impl<F, D, V, CC, W>(L);
+  KDA_CHAIN_INSTANCES(KDA_LAUNCH)
+#undef KDA_LAUNCH
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kda

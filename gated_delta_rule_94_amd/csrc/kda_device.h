@@ -133,4 +133,48 @@ __device__ __forceinline__ f32x4 mma16(const float (&a)[4], const float (&b)[4],
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Packed element stores of operand type E (bf16 or fp32) to LDS or global memory.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+}
+// two adjacent elements (4-byte or 8-byte aligned)
+template <bool F32>
+__device__ __forceinline__ void st2(void* dst, float a, float b) {
+  if constexpr (F32) *reinterpret_cast<float2*>(dst) = make_float2(a, b);
+  else *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(a, b);
+}
+// eight adjacent elements (16-byte aligned)
+template <bool F32>
+__device__ __forceinline__ void st8(void* dst, const float (&x)[8]) {
+  if constexpr (F32) {
+    float4* d = reinterpret_cast<float4*>(dst);
+    d[0] = make_float4(x[0], x[1], x[2], x[3]);
+    d[1] = make_float4(x[4], x[5], x[6], x[7]);
+  } else {
+    *reinterpret_cast<uint4*>(dst) =
+        make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+  }
+}
+
+// Two adjacent channels of one token, loaded from an fp32 or bf16 tensor (zero when !ok).
+template <bool F32>
+struct Raw2;
+template <>
+struct Raw2<false> {
+  uint32_t w;
+  __device__ __forceinline__ float2 f() const { return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)); }
+  __device__ __forceinline__ void load(const void* base, int64_t i, bool ok) {
+    w = ok ? *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + i) : 0u;
+  }
+};
+template <>
+struct Raw2<true> {
+  float2 v;
+  __device__ __forceinline__ float2 f() const { return v; }
+  __device__ __forceinline__ void load(const void* base, int64_t i, bool ok) {
+    v = ok ? *reinterpret_cast<const float2*>(static_cast<const float*>(base) + i) : make_float2(0.f, 0.f);
+  }
+};
+
 }  // namespace kda

@@ -26,13 +26,47 @@ struct PrefillArgs {
   int T;                      // tokens per sequence (cu_seqlens == NULL) or T_total
   int H, dk, dv, chunk;
   bool f32;
+  void* workspace;
+  size_t workspace_bytes;
+  void* stream;
+};
+
+// intra-chunk kernel launch (kda_intra.hip)
+struct IntraLaunch {
+  const void *q, *k, *v, *g, *beta;
+  const int32_t* cu;
+  const int32_t* chunk0;
+  unsigned char* records;
+  int num_seqs, H, T, nch;
+  int dk, dv, chunk;
+  bool f32;
+  int grid;
+  void* stream;
+};
+
+// chain kernel launch (kda_chain.hip)
+struct ChainLaunch {
+  const unsigned char* records;
+  const float* h0;
+  void* o;
+  float* hT;
+  const int32_t* cu;
+  const int32_t* chunk0;
+  int units, H, T, nch;
+  int dk, dv, chunk, ws;
+  bool f32;
   void* stream;
 };
 
 hipError_t launch_decode_step(const DecodeArgs& a);
+hipError_t launch_intra(const IntraLaunch& L);
+hipError_t launch_chain(const ChainLaunch& L);
+hipError_t launch_chunk_map(const int32_t* cu, int num_seqs, int T, int C, int32_t* chunk0, void* stream);
 
-// Returns hipErrorInvalidValue when no kernel instance covers the shape.
-hipError_t launch_chunked_forward(const PrefillArgs& a);
+// Prefill: supported shape?  workspace bytes?  launch (hipErrorInvalidValue: unsupported shape).
 bool chunked_forward_supported(bool f32, int dk, int dv, int chunk);
+size_t chunked_forward_workspace(bool f32, int dk, int dv, int chunk, int64_t max_chunks, int H, int num_seqs,
+                                 bool varlen);
+hipError_t launch_chunked_forward(const PrefillArgs& a);
 
 }  // namespace kda

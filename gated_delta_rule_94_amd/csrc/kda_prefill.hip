@@ -1,560 +1,85 @@
-// KDA chunked prefill on gfx950: gate cumsum, intra-chunk WY/UT transform and
-// inter-chunk state propagation, fused into one kernel.
+// KDA chunked prefill on gfx950: orchestration of the three kernels, all on the caller's stream.
 //
-// Method (Kimi K3 pages: architecture blog, "Kimi Delta Attention: the linear
-// core" -- a chunkwise algorithm on a specialised diagonal-plus-low-rank
-// transition; technical-report page, "Architecture at a glance" -- the
-// scaled-sigmoid lower bound on the log-decay keeps every causal tile a dense
-// matrix product).  For one chunk of C tokens starting from state S0, with G
-// the chunk-local inclusive cumulative sum of the log-decay g and Gamma = e^G:
+//   1. chunk_map_kernel    (packed sequences only) first chunk of every sequence, from the device
+//                          offsets -- no host synchronisation
+//   2. intra_chunk_kernel  gate cumulative sum + UT/WY transform of every (chunk, head), in parallel,
+//                          into per-chunk records in the workspace
+//   3. chain_kernel        the sequential state chain per (sequence, head, value slice)
 //
-//   A  = diag(beta) strictLower(M_kk),   M_kk[r,i] = sum_c k_r[c] k_i[c] e^{G_r[c] - G_i[c]}
-//   T  = (I + A)^{-1} diag(beta)                                   (UT transform)
-//   W  = T (K . Gamma),  U~ = T V,  U = U~ - W S0                   (WY form of the delta rule)
-//   P  = lowerIncl(M_qk),               M_qk[r,i] = sum_c q_r[c] k_i[c] e^{G_r[c] - G_i[c]}
-//   O  = (Q . Gamma) S0 + P U
-//   S  = Diag(Gamma_last) S0 + (K . e^{G_last - G})^T U
-//
-// Exponent safety: over a whole chunk G spans up to 5 C in log space (320 at
-// C = 64, beyond fp32), so M is factorised per 16-row sub-tile b with the
-// reference R_b = G just before the sub-tile: rows scaled by e^{G_r - R_b}
-// (in [e^-80, 1]), columns by e^{R_b - G_i} (in [1, e^80] inside the
-// sub-tile, <= 1 before it).  Every factor is finite; a factor can underflow
-// only where the exact product is itself negligible.  All e^{..} factors come
-// from one exp per element (the per-token decay e^g) and running products
-// inside each 16-row sub-tile.
-//
-// Kernel structure.  One workgroup (4 waves) per (sequence, head, slice of
-// WS value columns); value columns evolve independently, so the d_v split is
-// exact and spreads long single sequences over more CUs.  Per chunk:
-//   1. prep    : cumulative products of e^g per sub-tile; scaled operand
-//                tiles (bf16, or fp32 for fp32 inputs) into LDS
-//   2. intra   : M_kk -> A (fp32), M_qk -> P        (MFMA, one tile pair per wave)
-//   3. T       : 16x16 diagonal blocks of (I + A)^{-1} by forward substitution
-//                in fp32, off-diagonal blocks by the block recurrence
-//                X_ba = -L_bb sum_c A_bc X_ca on 16x16x16 MFMA, registers only
-//   4. W, U~   : MFMA
-//   5. chain   : U, O, S update on MFMA; the fp32 state and U never leave
-//                registers (accumulator tiles are fed back as B operands)
-// The next chunk's inputs are loaded into registers while stages 2-5 run.
-#include "kda_device.h"
+// Workspace: [records: max_chunks * H * record bytes][chunk0: (num_seqs + 1) int32, packed only],
+// where max_chunks bounds the number of chunks: B * ceil(T / C) for equal-length sequences,
+// floor(T_total / C) + num_seqs for packed ones (each sequence adds at most one partial chunk).
 #include "kda_internal.h"
+#include "kda_record.h"
 
 namespace kda {
 
-struct KParams {
-  const void *q, *k, *v, *g, *beta;
-  const float* h0;
-  void* o;
-  float* hT;
-  const int32_t* cu;
-  int units, H, T, dv;
-};
+bool chunked_forward_supported(bool f32, int dk, int dv, int chunk) { return record_bytes(f32, dk, dv, chunk) > 0; }
 
-template <bool F32, int DK, int C, int WS>
-struct Cfg {
-  using O = Op<F32>;
-  using E = typename O::E;
-  static constexpr int NT = C / 16;                     // 16-token sub-tiles per chunk
-  static constexpr int CP = (!F32 && C < 32) ? 32 : C;  // token extent of token-contraction operands
-  static constexpr int RS = DK + 4;                     // stride of [token][channel] tiles
-  static constexpr int TS = CP + 4;                     // stride of [..][token] tiles
-  static constexpr int AS = C + 4;                      // stride of the fp32 A tile
-  static constexpr int NCT = WS / 16;                   // value-column tiles = chain waves
-  static constexpr int ES = (int)sizeof(E);
-  static constexpr int al(int x) { return (x + 15) & ~15; }
-  // R1: scaled operands of the intra products, dead afterwards and reused for T, -W and L
-  static constexpr int OFF_QH = 0;
-  static constexpr int OFF_KH = al(OFF_QH + C * RS * ES);
-  static constexpr int OFF_KC = al(OFF_KH + C * RS * ES);
-  static constexpr int OFF_KT = al(OFF_KC + C * RS * ES);
-  static constexpr int R1_END = al(OFF_KT + C * RS * ES);
-  static constexpr int OFF_T = 0;
-  static constexpr int OFF_W = al(OFF_T + C * TS * ES);
-  static constexpr int OFF_L = al(OFF_W + C * RS * ES);
-  static constexpr int R1_ALIAS_END = OFF_L + NT * 16 * 17 * 4;
-  // operands of the chain and of W / U~
-  static constexpr int OFF_QG = R1_END;                     // Q . Gamma        [C][RS]
-  static constexpr int OFF_KGT = al(OFF_QG + C * RS * ES);  // (K . Gamma)^T    [DK][TS]
-  static constexpr int OFF_KPT = al(OFF_KGT + DK * TS * ES);// (K . e^{G_last - G})^T [DK][TS]
-  static constexpr int OFF_VT = al(OFF_KPT + DK * TS * ES); // V^T slice        [WS][TS]
-  static constexpr int OFF_A = al(OFF_VT + WS * TS * ES);   // A (fp32)         [C][AS]
-  static constexpr int OFF_P = al(OFF_A + C * AS * 4);      // P                [C][TS]
-  static constexpr int OFF_EEND = al(OFF_P + C * TS * ES);  // e^{sub-tile total} [NT][DK]
-  static constexpr int OFF_D = al(OFF_EEND + NT * DK * 4);  // gap factors      [3][DK]
-  static constexpr int OFF_GAM = al(OFF_D + 3 * DK * 4);    // e^{G_last}       [DK]
-  static constexpr int OFF_BETA = al(OFF_GAM + DK * 4);     // beta             [C]
-  static constexpr int TOTAL = al(OFF_BETA + C * 4);
-  static_assert(R1_ALIAS_END <= R1_END, "R1 aliases");
-  static_assert(TOTAL <= 163840, "LDS budget of one gfx950 workgroup");
-  static_assert(C == 16 || C == 32 || C == 64, "chunk");
-  static_assert(WS % 16 == 0 && WS <= 64, "slice");
-};
-
-// index of the gap factor of off-diagonal sub-tile pair (b, a), b >= a + 2 (only at C = 64)
-__device__ __forceinline__ constexpr int gap_index(int b, int a) { return (b == 2) ? 0 : (a == 0 ? 1 : 2); }
-
-template <bool F32>
-struct Raw2;  // two adjacent channels of one token
-template <>
-struct Raw2<false> {
-  uint32_t w;
-  __device__ __forceinline__ float2 f() const { return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)); }
-  __device__ __forceinline__ void load(const void* base, int64_t i, bool ok) {
-    w = ok ? *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + i) : 0u;
-  }
-};
-template <>
-struct Raw2<true> {
-  float2 v;
-  __device__ __forceinline__ float2 f() const { return v; }
-  __device__ __forceinline__ void load(const void* base, int64_t i, bool ok) {
-    v = ok ? *reinterpret_cast<const float2*>(static_cast<const float*>(base) + i) : make_float2(0.f, 0.f);
-  }
-};
-
-template <bool F32>
-struct Raw8;  // eight adjacent value columns of one token
-template <>
-struct Raw8<false> {
-  uint4 w;
-  __device__ __forceinline__ void load(const void* base, int64_t i, bool ok) {
-    w = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + i) : make_uint4(0, 0, 0, 0);
-  }
-  __device__ __forceinline__ float at(int j) const {
-    const uint32_t x = (j < 2) ? w.x : (j < 4) ? w.y : (j < 6) ? w.z : w.w;
-    return (j & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
-  }
-};
-template <>
-struct Raw8<true> {
-  float4 a, b;
-  __device__ __forceinline__ void load(const void* base, int64_t i, bool ok) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
-    a = ok ? p[0] : make_float4(0.f, 0.f, 0.f, 0.f);
-    b = ok ? p[1] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  __device__ __forceinline__ float at(int j) const {
-    const float4& x = (j < 4) ? a : b;
-    const int m = j & 3;
-    return m == 0 ? x.x : m == 1 ? x.y : m == 2 ? x.z : x.w;
-  }
-};
-
-template <bool F32, int DK, int C, int WS>
-__global__ __launch_bounds__(256, 1) void chunked_forward_kernel(const KParams p) {
-  using Cf = Cfg<F32, DK, C, WS>;
-  using O = typename Cf::O;
-  using E = typename Cf::E;
-  using Frag = typename O::Frag;
-  constexpr int NT = Cf::NT, CP = Cf::CP, RS = Cf::RS, TS = Cf::TS, AS = Cf::AS, NCT = Cf::NCT;
-  constexpr int NCP = DK / 2;              // channel pairs
-  constexpr int NPU = NCP * NT;            // prep units (channel pair, sub-tile)
-  static_assert(NPU <= 256, "one prep unit per thread");
-  constexpr int VV = C * WS / 8;           // 8-column vectors of the V slice per chunk
-  constexpr int VPT = (VV + 255) / 256;
-  constexpr int KSD = O::nks(DK);          // k-steps of a contraction over d_k
-  constexpr int KSC = O::nks(CP);          // k-steps of a contraction over the chunk's tokens
-
-  __shared__ __align__(16) unsigned char smem[Cf::TOTAL];
-  E* Qh = reinterpret_cast<E*>(smem + Cf::OFF_QH);
-  E* Kh = reinterpret_cast<E*>(smem + Cf::OFF_KH);
-  E* Kc = reinterpret_cast<E*>(smem + Cf::OFF_KC);
-  E* Kt = reinterpret_cast<E*>(smem + Cf::OFF_KT);
-  E* Ts = reinterpret_cast<E*>(smem + Cf::OFF_T);
-  E* Ws = reinterpret_cast<E*>(smem + Cf::OFF_W);
-  float* Ls = reinterpret_cast<float*>(smem + Cf::OFF_L);
-  E* QG = reinterpret_cast<E*>(smem + Cf::OFF_QG);
-  E* KGt = reinterpret_cast<E*>(smem + Cf::OFF_KGT);
-  E* Kpt = reinterpret_cast<E*>(smem + Cf::OFF_KPT);
-  E* Vt = reinterpret_cast<E*>(smem + Cf::OFF_VT);
-  float* As = reinterpret_cast<float*>(smem + Cf::OFF_A);
-  E* Ps = reinterpret_cast<E*>(smem + Cf::OFF_P);
-  float* Eend = reinterpret_cast<float*>(smem + Cf::OFF_EEND);
-  float* Dg = reinterpret_cast<float*>(smem + Cf::OFF_D);
-  float* Gam = reinterpret_cast<float*>(smem + Cf::OFF_GAM);
-  float* Bet = reinterpret_cast<float*>(smem + Cf::OFF_BETA);
-
-  // ---- which (sequence, head, value slice): slices of one unit share an XCD (block id mod 8)
-  const int DV = p.dv;
-  const int nsl = DV / WS;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, idx = bid >> 3;
-  const int unit = (idx / nsl) * 8 + xcd;
-  const int slice = idx - (idx / nsl) * nsl;
-  if (unit >= p.units) return;
-  const int H = p.H;
-  const int n = unit / H, h = unit - n * H;
-  int64_t t_begin, t_end;
-  if (p.cu) {
-    int s0 = p.cu[n], s1 = p.cu[n + 1];
-    s0 = s0 < 0 ? 0 : (s0 > p.T ? p.T : s0);
-    s1 = s1 < s0 ? s0 : (s1 > p.T ? p.T : s1);
-    t_begin = s0;
-    t_end = s1;
-  } else {
-    t_begin = (int64_t)n * p.T;
-    t_end = t_begin + p.T;
-  }
-  const int col0 = slice * WS;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lo = lane & 15, grp = lane >> 4;
-  const bool chain = wave < NCT;
-  const int ccol = col0 + 16 * wave + lo;  // value column of this lane in the chain stage
-  const int64_t sbase = (int64_t)unit * DK * DV;
-
-  // ---- state S (fp32 master) in accumulator layout: Sacc[m][r] = S[16 m + 4 grp + r][ccol]
-  f32x4 Sacc[DK / 16];
-#pragma unroll
-  for (int m = 0; m < DK / 16; ++m)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      Sacc[m][r] = (chain && p.h0) ? p.h0[sbase + (int64_t)(16 * m + 4 * grp + r) * DV + ccol] : 0.f;
-
-  // ---- register prefetch of one chunk's inputs
-  const int pcp = tid % NCP, psb = tid / NCP;  // prep unit: channel pair, sub-tile
-  const bool pact = psb < NT;
-  const int c0 = 2 * pcp;
-  Raw2<F32> rg[16], rq[16], rk[16];
-  Raw8<F32> rv[VPT];
-  float rb = 0.f;
-  auto prefetch = [&](int64_t t0, int len) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 16 * psb + i;
-      const bool ok = pact && r < len;
-      const int64_t off = ((t0 + r) * H + h) * DK + c0;
-      rg[i].load(p.g, off, ok);
-      rq[i].load(p.q, off, ok);
-      rk[i].load(p.k, off, ok);
-    }
-#pragma unroll
-    for (int it = 0; it < VPT; ++it) {
-      const int vi = tid + 256 * it;
-      const int r = vi / (WS / 8), c8 = vi - r * (WS / 8);
-      const bool ok = vi < VV && r < len;
-      rv[it].load(p.v, ((t0 + r) * H + h) * DV + col0 + 8 * c8, ok);
-    }
-    rb = (tid < len) ? ldg<F32>(p.beta, (t0 + tid) * H + h) : 0.f;
-  };
-
-  if (t_begin < t_end) prefetch(t_begin, (int)((t_end - t_begin) < C ? (t_end - t_begin) : C));
-
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += C) {
-    const int len = (int)((t_end - t0) < C ? (t_end - t0) : C);
-
-    // ================= 1. prep, pass 1: per-sub-tile running products of e^g
-    float E0[16], E1[16], F0[16], F1[16];
-    if (pact) {
-      float a0[16], a1[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float2 gg = rg[i].f();
-        a0[i] = __expf(gg.x);
-        a1[i] = __expf(gg.y);
-      }
-      E0[0] = a0[0];
-      E1[0] = a1[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) {
-        E0[i] = E0[i - 1] * a0[i];
-        E1[i] = E1[i - 1] * a1[i];
-      }
-      F0[15] = 1.f;
-      F1[15] = 1.f;
-#pragma unroll
-      for (int i = 14; i >= 0; --i) {
-        F0[i] = F0[i + 1] * a0[i + 1];
-        F1[i] = F1[i + 1] * a1[i + 1];
-      }
-      Eend[psb * DK + c0] = E0[15];
-      Eend[psb * DK + c0 + 1] = E1[15];
-    }
-    if (tid < C) Bet[tid] = rb;
-#pragma unroll
-    for (int it = 0; it < VPT; ++it) {
-      const int vi = tid + 256 * it;
-      if (vi < VV) {
-        const int r = vi / (WS / 8), c8 = vi - r * (WS / 8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) Vt[(8 * c8 + j) * TS + r] = (E)rv[it].at(j);
-      }
-    }
-    if constexpr (CP > C) {
-      for (int e = tid; e < WS * (CP - C); e += 256) Vt[(e / (CP - C)) * TS + C + e % (CP - C)] = (E)0.f;
-      for (int e = tid; e < DK * (CP - C); e += 256) {
-        KGt[(e / (CP - C)) * TS + C + e % (CP - C)] = (E)0.f;
-        Kpt[(e / (CP - C)) * TS + C + e % (CP - C)] = (E)0.f;
-      }
-    }
-    __syncthreads();
-
-    // ================= 1. prep, pass 2: scaled operand tiles
-    if (pact) {
-      float eP0 = 1.f, eP1 = 1.f, eS0 = 1.f, eS1 = 1.f;
-#pragma unroll
-      for (int x = 0; x < NT; ++x) {
-        const float e0 = Eend[x * DK + c0], e1 = Eend[x * DK + c0 + 1];
-        if (x < psb) { eP0 *= e0; eP1 *= e1; }
-        if (x > psb) { eS0 *= e0; eS1 *= e1; }
-      }
-      const float rT0 = 1.f / E0[15], rT1 = 1.f / E1[15];
-      if (psb == 0) {
-        float g0 = 1.f, g1 = 1.f;
-#pragma unroll
-        for (int x = 0; x < NT; ++x) { g0 *= Eend[x * DK + c0]; g1 *= Eend[x * DK + c0 + 1]; }
-        Gam[c0] = g0;
-        Gam[c0 + 1] = g1;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 16 * psb + i;
-        const float2 qq = rq[i].f(), kk = rk[i].f();
-        E* qh = Qh + r * RS + c0; qh[0] = (E)(qq.x * E0[i]); qh[1] = (E)(qq.y * E1[i]);
-        E* kh = Kh + r * RS + c0; kh[0] = (E)(kk.x * E0[i]); kh[1] = (E)(kk.y * E1[i]);
-        E* kt = Kt + r * RS + c0; kt[0] = (E)(kk.x * F0[i]); kt[1] = (E)(kk.y * F1[i]);
-        E* kc = Kc + r * RS + c0; kc[0] = (E)(kk.x * (F0[i] * rT0)); kc[1] = (E)(kk.y * (F1[i] * rT1));
-        E* qg = QG + r * RS + c0; qg[0] = (E)(qq.x * (E0[i] * eP0)); qg[1] = (E)(qq.y * (E1[i] * eP1));
-        KGt[c0 * TS + r] = (E)(kk.x * (E0[i] * eP0));
-        KGt[(c0 + 1) * TS + r] = (E)(kk.y * (E1[i] * eP1));
-        Kpt[c0 * TS + r] = (E)(kk.x * (F0[i] * eS0));
-        Kpt[(c0 + 1) * TS + r] = (E)(kk.y * (F1[i] * eS1));
-      }
-    }
-    if constexpr (NT == 4) {
-      for (int e = tid; e < 3 * DK; e += 256) {
-        const int d = e / DK, c = e - d * DK;
-        // gap between row sub-tile b and column sub-tile a: product of the sub-tile totals strictly between
-        Dg[e] = (d == 0) ? Eend[1 * DK + c] : (d == 1) ? Eend[1 * DK + c] * Eend[2 * DK + c] : Eend[2 * DK + c];
-      }
-    }
-    // the inputs of this chunk are consumed: fetch the next chunk while the rest runs
-    if (t0 + C < t_end) prefetch(t0 + C, (int)((t_end - t0 - C) < C ? (t_end - t0 - C) : C));
-    __syncthreads();
-
-    // ================= 2. intra-chunk products: M_kk -> A, M_qk -> P (lower-triangular tile pairs)
-    {
-      constexpr int NPAIR = NT * (NT + 1) / 2;
-#pragma unroll
-      for (int pi = 0; pi < 2 * NPAIR; ++pi) {
-        if ((pi & 3) != wave) continue;
-        const bool qk = pi >= NPAIR;
-        int qq = qk ? pi - NPAIR : pi;
-        int b = 0;
-        while (qq > b) { qq -= b + 1; ++b; }
-        const int a = qq;
-        const E* arow = (qk ? Qh : Kh) + (16 * b + lo) * RS;
-        const E* brow = (a == b ? Kc : Kt) + (16 * a + lo) * RS;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int s = 0; s < KSD; ++s) {
-          Frag af = O::ld(arow, s, grp);
-          Frag bf = O::ld(brow, s, grp);
-          if (b >= a + 2) {
-            float f[O::SLOTS];
-#pragma unroll
-            for (int j = 0; j < O::SLOTS; ++j) f[j] = Dg[gap_index(b, a) * DK + O::kidx(s, grp, j)];
-            bf = O::scale(bf, f);
-          }
-          acc = O::mma(af, bf, acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * b + 4 * grp + r, col = 16 * a + lo;
-          if (!qk) As[row * AS + col] = (row > col) ? Bet[row] * acc[r] : 0.f;
-          else Ps[row * TS + col] = (E)((row >= col) ? acc[r] : 0.f);
-        }
-      }
-      // upper tiles of P read by the token contractions are zero
-      for (int e = tid; e < C * CP; e += 256) {
-        const int row = e / CP, col = e - row * CP;
-        if ((col >> 4) > (row >> 4)) Ps[row * TS + col] = (E)0.f;
-      }
-    }
-    __syncthreads();
-
-    // ================= 3a. diagonal 16x16 blocks of (I + A)^{-1} by forward substitution (fp32)
-    if (wave < NT) {
-      const int b = wave, j = lo;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == j) ? 1.f : 0.f;
-#pragma unroll
-        for (int i = 0; i < r; ++i) acc -= As[(16 * b + r) * AS + 16 * b + i] * x[i];
-        x[r] = acc;
-      }
-      if (grp == 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Ls[(b * 16 + r) * 17 + j] = x[r];
-      }
-    }
-    // upper tiles of T read by the token contractions are zero
-    for (int e = tid; e < C * CP; e += 256) {
-      const int row = e / CP, col = e - row * CP;
-      if ((col >> 4) > (row >> 4)) Ts[row * TS + col] = (E)0.f;
-    }
-    __syncthreads();
-
-    // ================= 3b. T = (I + A)^{-1} diag(beta): column block a per wave, X_ba = -L_bb sum_c A_bc X_ca
-#pragma unroll
-    for (int a = 0; a < NT; ++a) {
-      if (wave != a) continue;
-      float Xb[NT][4];  // Xb[c][j] = X_ca[4 grp + j][lo]
-      const float bcol = Bet[16 * a + lo];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) Xb[a][j] = Ls[(a * 16 + 4 * grp + j) * 17 + lo];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Ts[(16 * a + 4 * grp + r) * TS + 16 * a + lo] = (E)(Xb[a][r] * bcol);
-#pragma unroll
-      for (int b = a + 1; b < NT; ++b) {
-        f32x4 z = zero4();
-#pragma unroll
-        for (int c = a; c < b; ++c) {
-          float av[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) av[j] = As[(16 * b + lo) * AS + 16 * c + 4 * grp + j];
-          z = mma16<F32>(av, Xb[c], z);
-        }
-        float lv[4], zb[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          lv[j] = -Ls[(b * 16 + lo) * 17 + 4 * grp + j];
-          zb[j] = z[j];
-        }
-        const f32x4 x = mma16<F32>(lv, zb, zero4());
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Xb[b][j] = x[j];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Ts[(16 * b + 4 * grp + r) * TS + 16 * a + lo] = (E)(x[r] * bcol);
-      }
-    }
-    __syncthreads();
-
-    // ================= 4. -W = -T (K . Gamma) into LDS; U~ = T V kept in the chain waves' registers
-#pragma unroll
-    for (int nt = 0; nt < DK / 16; ++nt) {
-      if ((nt & 3) != wave) continue;
-      const E* krow = KGt + (16 * nt + lo) * TS;
-#pragma unroll
-      for (int b = 0; b < NT; ++b) {
-        const E* trow = Ts + (16 * b + lo) * TS;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int s = 0; s < O::nks(16 * (b + 1)); ++s) acc = O::mma(O::ld(trow, s, grp), O::ld(krow, s, grp), acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Ws[(16 * b + 4 * grp + r) * RS + 16 * nt + lo] = (E)(-acc[r]);
-      }
-    }
-    f32x4 Uacc[NT];
-    if (chain) {
-      const E* vrow = Vt + (16 * wave + lo) * TS;
-#pragma unroll
-      for (int b = 0; b < NT; ++b) {
-        const E* trow = Ts + (16 * b + lo) * TS;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int s = 0; s < O::nks(16 * (b + 1)); ++s) acc = O::mma(O::ld(trow, s, grp), O::ld(vrow, s, grp), acc);
-        Uacc[b] = acc;
-      }
-    }
-    __syncthreads();
-
-    // ================= 5. chain: U = U~ - W S, O = (Q . Gamma) S + P U, S = Diag(gamma) S + K'^T U
-    if (chain) {
-      Frag Sf[KSD];
-#pragma unroll
-      for (int s = 0; s < KSD; ++s) Sf[s] = O::from_acc(Sacc, s);
-      f32x4 U[NT];
-#pragma unroll
-      for (int b = 0; b < NT; ++b) {
-        const E* wrow = Ws + (16 * b + lo) * RS;
-        f32x4 acc = Uacc[b];
-#pragma unroll
-        for (int s = 0; s < KSD; ++s) acc = O::mma(O::ld(wrow, s, grp), Sf[s], acc);
-        U[b] = acc;
-      }
-#pragma unroll
-      for (int b = 0; b < NT; ++b) {
-        const E* qrow = QG + (16 * b + lo) * RS;
-        const E* prow = Ps + (16 * b + lo) * TS;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int s = 0; s < KSD; ++s) acc = O::mma(O::ld(qrow, s, grp), Sf[s], acc);
-#pragma unroll
-        for (int s = 0; s < O::nks(16 * (b + 1)); ++s) acc = O::mma(O::ld(prow, s, grp), O::from_acc(U, s), acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tr = 16 * b + 4 * grp + r;
-          if (tr < len) stg<F32>(p.o, ((t0 + tr) * H + h) * DV + ccol, acc[r]);
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < DK / 16; ++m) {
-        const E* krow = Kpt + (16 * m + lo) * TS;
-        f32x4 acc = Sacc[m];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] *= Gam[16 * m + 4 * grp + r];
-#pragma unroll
-        for (int s = 0; s < KSC; ++s) acc = O::mma(O::ld(krow, s, grp), O::from_acc(U, s), acc);
-        Sacc[m] = acc;
-      }
-    }
-    __syncthreads();
-  }
-
-  if (chain && p.hT) {
-#pragma unroll
-    for (int m = 0; m < DK / 16; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p.hT[sbase + (int64_t)(16 * m + 4 * grp + r) * DV + ccol] = Sacc[m][r];
-  }
+static int64_t max_chunks_of(int T, int chunk, int num_seqs, bool varlen) {
+  return varlen ? (int64_t)T / chunk + num_seqs : (int64_t)num_seqs * ((T + chunk - 1) / chunk);
 }
 
-template <bool F32, int DK, int C, int WS>
-static hipError_t launch(const PrefillArgs& a) {
-  KParams kp;
-  kp.q = a.q; kp.k = a.k; kp.v = a.v; kp.g = a.g; kp.beta = a.beta;
-  kp.h0 = a.h0; kp.o = a.o; kp.hT = a.hT; kp.cu = a.cu_seqlens;
-  kp.units = a.num_seqs * a.H;
-  kp.H = a.H;
-  kp.T = a.T;
-  kp.dv = a.dv;
-  const int nsl = a.dv / WS;
-  const int grid = ((kp.units + 7) / 8) * 8 * nsl;
-  hipLaunchKernelGGL((chunked_forward_kernel<F32, DK, C, WS>), dim3(grid), dim3(256), 0, (hipStream_t)a.stream, kp);
-  return hipGetLastError();
+size_t chunked_forward_workspace(bool f32, int dk, int dv, int chunk, int64_t max_chunks, int H, int num_seqs,
+                                 bool varlen) {
+  const int64_t rb = record_bytes(f32, dk, dv, chunk);
+  if (rb == 0) return 0;
+  size_t bytes = (size_t)(max_chunks * H * rb);
+  if (varlen) bytes += ((size_t)(num_seqs + 1) * 4 + 255) & ~(size_t)255;
+  return bytes;
 }
 
-// Value-slice width per instance: bf16 uses 64 columns (4 chain waves); fp32 uses 16 columns
-// so that its fp32 operand tiles fit the 160 KB of LDS.
-#define KDA_PREFILL_INSTANCES(X) \
-  X(false, 64, 16, 64)           \
-  X(false, 64, 32, 64)           \
-  X(false, 64, 64, 64)           \
-  X(false, 128, 16, 64)          \
-  X(false, 128, 32, 64)          \
-  X(false, 128, 64, 64)          \
-  X(true, 64, 16, 16)            \
-  X(true, 64, 32, 16)            \
-  X(true, 64, 64, 16)            \
-  X(true, 128, 16, 16)           \
-  X(true, 128, 32, 16)
-
-bool chunked_forward_supported(bool f32, int dk, int dv, int chunk) {
-  if (dv != 64 && dv != 128) return false;
-#define KDA_MATCH(F, D, CC, W) \
-  if (f32 == F && dk == D && chunk == CC) return true;
-  KDA_PREFILL_INSTANCES(KDA_MATCH)
-#undef KDA_MATCH
-  return false;
+static int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 hipError_t launch_chunked_forward(const PrefillArgs& a) {
-#define KDA_LAUNCH(F, D, CC, W) \
-  if (a.f32 == F && a.dk == D && a.chunk == CC) return launch<F, D, CC, W>(a);
-  KDA_PREFILL_INSTANCES(KDA_LAUNCH)
-#undef KDA_LAUNCH
-  return hipErrorInvalidValue;
+  const bool varlen = a.cu_seqlens != nullptr;
+  const int C = a.chunk;
+  const int64_t rb = record_bytes(a.f32, a.dk, a.dv, C);
+  if (rb == 0) return hipErrorInvalidValue;
+  const int64_t max_chunks = max_chunks_of(a.T, C, a.num_seqs, varlen);
+  const int nch = varlen ? 0 : (a.T + C - 1) / C;
+  unsigned char* records = static_cast<unsigned char*>(a.workspace);
+  int32_t* chunk0 = nullptr;
+  hipError_t e = hipSuccess;
+  if (varlen) {
+    chunk0 = reinterpret_cast<int32_t*>(records + max_chunks * a.H * rb);
+    e = launch_chunk_map(a.cu_seqlens, a.num_seqs, a.T, C, chunk0, a.stream);
+    if (e != hipSuccess) return e;
+  }
+  const int cus = compute_units();
+  const int64_t items = max_chunks * a.H;
+  if (items > INT32_MAX) return hipErrorInvalidValue;
+  if (items > 0) {
+    IntraLaunch L;
+    L.q = a.q; L.k = a.k; L.v = a.v; L.g = a.g; L.beta = a.beta;
+    L.cu = a.cu_seqlens; L.chunk0 = chunk0; L.records = records;
+    L.num_seqs = a.num_seqs; L.H = a.H; L.T = a.T; L.nch = nch;
+    L.dk = a.dk; L.dv = a.dv; L.chunk = C; L.f32 = a.f32;
+    L.grid = (int)items;  // one 8-wave workgroup per (chunk, head) record (bound; extra ones exit)
+    L.stream = a.stream;
+    e = launch_intra(L);
+    if (e != hipSuccess) return e;
+  }
+  ChainLaunch K;
+  K.records = records; K.h0 = a.h0; K.o = a.o; K.hT = a.hT; K.cu = a.cu_seqlens; K.chunk0 = chunk0;
+  K.units = a.num_seqs * a.H; K.H = a.H; K.T = a.T; K.nch = nch;
+  K.dk = a.dk; K.dv = a.dv; K.chunk = C; K.f32 = a.f32;
+  // value-slice width: 32 columns when that still gives every CU a workgroup, else 16 (fp32: 16)
+  int ws = 16;
+  if (!a.f32 && (int64_t)K.units * (a.dv / 32) >= cus) ws = 32;
+  K.ws = ws;
+  K.stream = a.stream;
+  return launch_chain(K);
 }
 
 }  // namespace kda

@@ -39,15 +39,23 @@ def test_status_strings_and_version():
 
 def test_workspace_queries():
     lib = kda.lib()
-    assert lib.kda_chunked_forward_workspace_bytes(4, 4096, 16, 128, 128, 64, 1) == 0
-    assert lib.kda_chunked_forward_varlen_workspace_bytes(16, 1 << 20, 131072, 8, 128, 128, 64, 1) == 0
+    # one record per (chunk, head): -W, Q.Gamma, K'^T, P, U~ in bf16 plus e^{G_last} in fp32
+    rec = 2 * (3 * 64 * 128 + 64 * 64 + 64 * 128) + 4 * 128
+    rec = (rec + 255) // 256 * 256
+    assert lib.kda_chunked_forward_workspace_bytes(4, 4096, 16, 128, 128, 64, 1) == 4 * 64 * 16 * rec
+    assert lib.kda_chunked_forward_workspace_bytes(1, 100, 2, 128, 128, 64, 1) == 2 * 2 * rec  # ragged tail
+    # packed: at most floor(T_total / C) + N chunks, plus the chunk map
+    n = lib.kda_chunked_forward_varlen_workspace_bytes(16, 1 << 20, 131072, 8, 128, 128, 64, 1)
+    assert n == ((1 << 20) // 64 + 16) * 8 * rec + 256
+    assert lib.kda_chunked_forward_workspace_bytes(0, 10, 2, 64, 64, 64, 1) == 0
+    assert lib.kda_chunked_forward_workspace_bytes(1, 10, 2, 64, 64, 48, 1) == 0  # unsupported chunk
 
 
 FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced because validation fails first
 
 
-def fwd(B=1, T=64, H=2, dk=64, dv=64, chunk=64, dt=1, ptr=FAKE, h0=None, hT=None):
-    return kda.lib().kda_chunked_forward(ptr, ptr, ptr, ptr, ptr, h0, ptr, hT, B, T, H, dk, dv, chunk, dt, None, 0,
+def fwd(B=1, T=64, H=2, dk=64, dv=64, chunk=64, dt=1, ptr=FAKE, h0=None, hT=None, ws=FAKE, ws_bytes=1 << 40):
+    return kda.lib().kda_chunked_forward(ptr, ptr, ptr, ptr, ptr, h0, ptr, hT, B, T, H, dk, dv, chunk, dt, ws, ws_bytes,
                                          None)
 
 
@@ -64,20 +72,27 @@ def test_prefill_validation():
     assert fwd(chunk=128) == UNSUPPORTED
     assert fwd(dt=0, dk=128, chunk=64) == UNSUPPORTED  # fp32 with d_k = 128 needs chunk <= 32
     assert fwd(h0=FAKE + 8) == INVALID
+    # workspace missing, too small or misaligned
+    need = kda.lib().kda_chunked_forward_workspace_bytes(1, 64, 2, 64, 64, 64, 1)
+    assert fwd(ws=None) == 3
+    assert fwd(ws_bytes=need - 1) == 3
+    assert fwd(ws=FAKE + 16, ws_bytes=need) == 3
     # empty batch: nothing to do, null tensors allowed
-    assert fwd(B=0, ptr=None) == OK
+    assert fwd(B=0, ptr=None, ws=None, ws_bytes=0) == OK
 
 
 def test_varlen_validation():
     lib = kda.lib()
     call = lambda cu, N, Tt, ms, ptr=FAKE: lib.kda_chunked_forward_varlen(ptr, ptr, ptr, ptr, ptr, None, ptr, None,
-                                                                         cu, N, Tt, ms, 2, 64, 64, 64, 1, None, 0,
-                                                                         None)
+                                                                         cu, N, Tt, ms, 2, 64, 64, 64, 1, FAKE,
+                                                                         1 << 40, None)
     assert call(None, 2, 100, 60) == INVALID       # missing cu_seqlens
     assert call(FAKE, -1, 100, 60) == INVALID
     assert call(FAKE, 2, 100, 101) == INVALID      # max_seqlen beyond T_total
     assert call(FAKE, 2, 100, 60, ptr=None) == INVALID
     assert call(None, 0, 0, 0, ptr=None) == OK     # nothing to do
+    assert lib.kda_chunked_forward_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 2, 100, 60, 2, 64, 64,
+                                          64, 1, FAKE, 10, None) == 3  # workspace too small
 
 
 def test_decode_validation():

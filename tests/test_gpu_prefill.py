@@ -246,3 +246,24 @@ def test_workload_varlen_16_sequences():
         assert o_err(host64(o[:, s:e]), o_ref) < TOL[w.dtype]
         if n in short:
             assert state_err(host64(hT[n:n + 1]), h_ref) < TOL[w.dtype]
+
+
+def test_short_sequences_precision():
+    """Sequences of 1-4 tokens from a zero state: the output is P U alone, so the intra-chunk products
+    carry the whole result, including slices where q . k nearly cancels."""
+    lens = [1 + (i % 4) for i in range(64)]
+    cu, d = varlen_case(lens, 4, 128, 128, BF16, 50, h0=False)
+    g = {key: dev_tensor(d[key]) for key in KEYS}
+    o, hT = kda.kda_chunked_forward_varlen(g["q"], g["k"], g["v"], g["g"], g["beta"], dev_tensor(cu), max(lens),
+                                           None, chunk=64)
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle.forward_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, None)
+    # per (sequence, head) slice
+    worst = 0.0
+    og = host64(o)[0]
+    for n in range(len(lens)):
+        s, e = cu[n], cu[n + 1]
+        worst = max(worst, slice_err(og[s:e], o_ref[s:e], (1,)))
+    eh = state_err(host64(hT), h_ref)
+    print("short sequences: o %.2e hT %.2e" % (worst, eh))
+    assert worst < TOL[BF16] and eh < TOL[BF16]
