@@ -66,7 +66,11 @@ struct ChainCfg {
 // One part of a record copied by the NC copy threads in 16-byte units: NU units, UPR units per
 // row.  Units past the end repeat the last one (same bytes to the same place), so the copy has no
 // branches and the compiler counts outstanding loads exactly across the pipeline.
-template <int NC, int NU, int UPR, int GBASE, int GROW, int LBASE, int LROW>
+// SW: bf16 tiles read as 8-byte fragment pieces are stored with the two 8-byte halves of every
+// 16-byte unit swapped in rows whose bit 3 is set.  The fragment reads of 16 lanes (rows lo =
+// 0..15, one piece each) then fall on distinct LDS banks; unswizzled, rows lo and lo + 8 share
+// banks at these row strides.  Readers XOR their piece index with (lo >> 3) & 1.
+template <int NC, int NU, int UPR, int GBASE, int GROW, int LBASE, int LROW, bool SW = false>
 struct CopyPart {
   static constexpr int K = (NU + NC - 1) / NC;
   typedef uint32_t vec_t __attribute__((ext_vector_type(4 * K)));
@@ -90,8 +94,19 @@ struct CopyPart {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int u = unit(ht, k);
-      *reinterpret_cast<uint4*>(buf + LBASE + (u / UPR) * LROW + 16 * (u % UPR)) =
-          make_uint4(st[4 * k], st[4 * k + 1], st[4 * k + 2], st[4 * k + 3]);
+      const int row = u / UPR;
+      const uint32_t a0 = st[4 * k], a1 = st[4 * k + 1], a2 = st[4 * k + 2], a3 = st[4 * k + 3];
+      uint4 v;
+      if constexpr (SW) {
+        const bool sw = (row >> 3) & 1;
+        v.x = sw ? a2 : a0;
+        v.y = sw ? a3 : a1;
+        v.z = sw ? a0 : a2;
+        v.w = sw ? a1 : a3;
+      } else {
+        v = make_uint4(a0, a1, a2, a3);
+      }
+      *reinterpret_cast<uint4*>(buf + LBASE + row * LROW + 16 * (u % UPR)) = v;
     }
   }
 };
@@ -134,6 +149,7 @@ __global__ __launch_bounds__(256) void chain_kernel(const ChainParams p) {
   const int col0 = slice * WS;
   const int tid = threadIdx.x, lane = tid & 63, lo = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gsw = F32 ? grp : (grp ^ ((lo >> 3) & 1));  // fragment piece of this lane in swizzled bf16 tiles
   const bool chain = wave < Cf::NW;
   const int ccol = col0 + 16 * (chain ? wave : 0) + lo;  // value column of this lane
   const int64_t sbase = (int64_t)unit * DK * DVr;
@@ -151,11 +167,11 @@ __global__ __launch_bounds__(256) void chain_kernel(const ChainParams p) {
   auto rec_of = [&](int c) -> const unsigned char* { return p.ws + ((first + c) * H + h) * R::BYTES; };
   constexpr int ES_ = Cf::ES;
   struct Stage {
-    CopyPart<Cf::NC, Cf::U_NW, DK / EPU, (int)(R::NW * ES_), DK * ES_, Cf::B_NW, RS * ES_> nw;
-    CopyPart<Cf::NC, Cf::U_QG, DK / EPU, (int)(R::QG * ES_), DK * ES_, Cf::B_QG, RS * ES_> qg;
-    CopyPart<Cf::NC, Cf::U_P, CP / EPU, (int)(R::P * ES_), CP * ES_, Cf::B_P, TS * ES_> pp;
-    CopyPart<Cf::NC, Cf::U_KPT, CP / EPU, (int)(R::KPT * ES_), CP * ES_, Cf::B_KPT, TS * ES_> kpt;
-    CopyPart<Cf::NC, Cf::U_UT, C / EPU, (int)(R::UT * ES_), C * ES_, Cf::B_UT, US * ES_> ut;  // record pointer + col0 rows
+    CopyPart<Cf::NC, Cf::U_NW, DK / EPU, (int)(R::NW * ES_), DK * ES_, Cf::B_NW, RS * ES_, !F32> nw;
+    CopyPart<Cf::NC, Cf::U_QG, DK / EPU, (int)(R::QG * ES_), DK * ES_, Cf::B_QG, RS * ES_, !F32> qg;
+    CopyPart<Cf::NC, Cf::U_P, CP / EPU, (int)(R::P * ES_), CP * ES_, Cf::B_P, TS * ES_, !F32> pp;
+    CopyPart<Cf::NC, Cf::U_KPT, CP / EPU, (int)(R::KPT * ES_), CP * ES_, Cf::B_KPT, TS * ES_, !F32> kpt;
+    CopyPart<Cf::NC, Cf::U_UT, C / EPU, (int)(R::UT * ES_), C * ES_, Cf::B_UT, US * ES_, !F32> ut;  // record pointer + col0 rows
     CopyPart<Cf::NC, Cf::U_GAM, Cf::U_GAM, (int)R::GAM_BYTE, 0, Cf::B_GAM, 0> gam;
     __device__ __forceinline__ void load(const unsigned char* rp, int ht, int col0b) {
       nw.load(rp, ht); qg.load(rp, ht); pp.load(rp, ht); kpt.load(rp, ht); ut.load(rp + col0b, ht); gam.load(rp, ht);
@@ -165,8 +181,8 @@ __global__ __launch_bounds__(256) void chain_kernel(const ChainParams p) {
     }
   };
   const int ht = tid - 64 * Cf::NW;  // copy-thread index (copy waves only)
-  const int ostride = H * DVr;              // output elements between consecutive tokens
-  const int o_lane = 4 * grp * ostride + ccol;  // this lane's output offset within a 16-token tile
+  const int ostride = H * DVr;                              // output elements between consecutive tokens
+  const int ocol = col0 + 16 * (chain ? wave : 0) + 4 * grp;  // first of this lane's 4 output columns
   const int col0b = col0 * C * ES_;  // first U~^T row of the slice
 
   // one chunk of the chain from LDS buffer `buf`
@@ -182,22 +198,23 @@ __global__ __launch_bounds__(256) void chain_kernel(const ChainParams p) {
     const int len = (int)((t_end - t0) < C ? (t_end - t0) : C);
     const int64_t obase = (t0 * H + h) * DVr;  // output element of (token t0, head h, column 0): uniform
     if (!chain) return;
+    // Phases, each issuing the LDS fragment loads of the next so that LDS latency hides behind
+    // MFMAs; the state update (the chunk-to-chunk critical path) comes first:
+    //   1  -W fragments, U~                   2  U = U~ - W S            | K'^T fragments, gamma
+    //   3  S = gamma S + K'^T U               | Q.Gamma fragments
+    //   4  O^T = S_old^T (Q.Gamma)^T          | P fragments           5  O^T += U^T P^T; store
+    // O is formed transposed (the state and U fragments serve as A operands unchanged), so each
+    // lane holds four consecutive value columns of one token: one 8-byte store per 16 tokens.
     Frag Sf[KSD];
 #pragma unroll
     for (int sk = 0; sk < KSD; ++sk) Sf[sk] = O::from_acc(Sacc, sk);
-    // all fragments of -W and Q . Gamma up front: their LDS latency overlaps, and four independent
-    // accumulators per product keep the MFMA pipe busy
-    Frag wf[NT][KSD], qf[NT][KSD];
+    Frag wf[NT][KSD];
 #pragma unroll
-    for (int bt = 0; bt < NT; ++bt)
+    for (int sk = 0; sk < KSD; ++sk)
 #pragma unroll
-      for (int sk = 0; sk < KSD; ++sk) {
-        wf[bt][sk] = O::ld(Wn + (16 * bt + lo) * RS, sk, grp);
-        qf[bt][sk] = O::ld(QG + (16 * bt + lo) * RS, sk, grp);
-      }
-    // U = U~ - W S   (U~^T in LDS: this lane's 4 tokens of its column are contiguous)
-    f32x4 U[NT], Ob[NT];
-    const E* ut = Ut + (16 * wave + lo) * US + 4 * grp;
+      for (int bt = 0; bt < NT; ++bt) wf[bt][sk] = O::ld(Wn + (16 * bt + lo) * RS, sk, gsw);
+    f32x4 U[NT];
+    const E* ut = Ut + (16 * wave + lo) * US + 4 * gsw;  // U~^T: this lane's 4 tokens are contiguous
 #pragma unroll
     for (int bt = 0; bt < NT; ++bt) {
       if constexpr (F32) {
@@ -207,48 +224,73 @@ __global__ __launch_bounds__(256) void chain_kernel(const ChainParams p) {
         const bf16x4 x = *reinterpret_cast<const bf16x4*>(ut + 16 * bt);
         U[bt] = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
       }
-      Ob[bt] = zero4();
     }
+    __builtin_amdgcn_sched_barrier(0);
+
+    Frag kf[DK / 16][KSC];
 #pragma unroll
     for (int sk = 0; sk < KSD; ++sk)
 #pragma unroll
       for (int bt = 0; bt < NT; ++bt) U[bt] = O::mma(wf[bt][sk], Sf[sk], U[bt]);
-    // O = (Q . Gamma) S + P U
-#pragma unroll
-    for (int sk = 0; sk < KSD; ++sk)
-#pragma unroll
-      for (int bt = 0; bt < NT; ++bt) Ob[bt] = O::mma(qf[bt][sk], Sf[sk], Ob[bt]);
-    Frag uf[KSC];
-#pragma unroll
-    for (int sk = 0; sk < KSC; ++sk) uf[sk] = O::from_acc(U, sk);
-#pragma unroll
-    for (int bt = 0; bt < NT; ++bt) {
-      const E* prow = Ps + (16 * bt + lo) * TS;
-#pragma unroll
-      for (int sk = 0; sk < O::nks(16 * (bt + 1)); ++sk) Ob[bt] = O::mma(O::ld(prow, sk, grp), uf[sk], Ob[bt]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tr = 16 * bt + 4 * grp + r;
-        if (tr < len) stg<F32>(p.o, obase + (o_lane + (16 * bt + r) * ostride), Ob[bt][r]);
-      }
-    }
-    // S = Diag(gamma) S + K'^T U
-    Frag kf[DK / 16][KSC];
 #pragma unroll
     for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
-      for (int sk = 0; sk < KSC; ++sk) kf[m][sk] = O::ld(Kpt + (16 * m + lo) * TS, sk, grp);
+      for (int sk = 0; sk < KSC; ++sk) kf[m][sk] = O::ld(Kpt + (16 * m + lo) * TS, sk, gsw);
+    if constexpr (!F32) {
+#pragma unroll
+      for (int i = 0; i < NT * KSD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    Frag uf[KSC];
+#pragma unroll
+    for (int sk = 0; sk < KSC; ++sk) uf[sk] = O::from_acc(U, sk);
+    Frag qf[NT][KSD];
 #pragma unroll
     for (int m = 0; m < DK / 16; ++m) {
       const float4 gm = *reinterpret_cast<const float4*>(Gam + 16 * m + 4 * grp);
-      f32x4 acc = Sacc[m];
-      acc[0] *= gm.x;
-      acc[1] *= gm.y;
-      acc[2] *= gm.z;
-      acc[3] *= gm.w;
+      Sacc[m][0] *= gm.x;
+      Sacc[m][1] *= gm.y;
+      Sacc[m][2] *= gm.z;
+      Sacc[m][3] *= gm.w;
 #pragma unroll
-      for (int sk = 0; sk < KSC; ++sk) acc = O::mma(kf[m][sk], uf[sk], acc);
-      Sacc[m] = acc;
+      for (int sk = 0; sk < KSC; ++sk) Sacc[m] = O::mma(kf[m][sk], uf[sk], Sacc[m]);
+    }
+#pragma unroll
+    for (int sk = 0; sk < KSD; ++sk)
+#pragma unroll
+      for (int bt = 0; bt < NT; ++bt) qf[bt][sk] = O::ld(QG + (16 * bt + lo) * RS, sk, gsw);
+    __builtin_amdgcn_sched_barrier(0);
+
+    f32x4 Ot[NT];
+    Frag pf[NT][KSC];
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt) Ot[bt] = zero4();
+#pragma unroll
+    for (int sk = 0; sk < KSD; ++sk)
+#pragma unroll
+      for (int bt = 0; bt < NT; ++bt) Ot[bt] = O::mma(Sf[sk], qf[bt][sk], Ot[bt]);
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt)
+#pragma unroll
+      for (int sk = 0; sk < O::nks(16 * (bt + 1)); ++sk) pf[bt][sk] = O::ld(Ps + (16 * bt + lo) * TS, sk, gsw);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt) {
+#pragma unroll
+      for (int sk = 0; sk < O::nks(16 * (bt + 1)); ++sk) Ot[bt] = O::mma(uf[sk], pf[bt][sk], Ot[bt]);
+      if (16 * bt + lo < len) {
+        const int64_t oi = obase + (int64_t)(16 * bt + lo) * ostride + ocol;
+        if constexpr (F32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(p.o) + oi) = make_float4(Ot[bt][0], Ot[bt][1], Ot[bt][2], Ot[bt][3]);
+        } else {
+          *reinterpret_cast<uint2*>(static_cast<__bf16*>(p.o) + oi) =
+              make_uint2(pack_bf16x2(Ot[bt][0], Ot[bt][1]), pack_bf16x2(Ot[bt][2], Ot[bt][3]));
+        }
+      }
     }
   };
 

@@ -167,6 +167,12 @@ struct Raw2<false> {
   __device__ __forceinline__ void load(const void* base, int64_t i, bool ok) {
     w = ok ? *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + i) : 0u;
   }
+  // element i (32-bit) of a wave-uniform base: scalar base + vector offset addressing.  The load
+  // is unconditional (i must be in bounds); !ok only zeroes the value, so no branch is needed.
+  __device__ __forceinline__ void load32(const void* base, uint32_t i, bool ok) {
+    const uint32_t x = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(base) + 2u * i);
+    w = ok ? x : 0u;
+  }
 };
 template <>
 struct Raw2<true> {
@@ -174,6 +180,10 @@ struct Raw2<true> {
   __device__ __forceinline__ float2 f() const { return v; }
   __device__ __forceinline__ void load(const void* base, int64_t i, bool ok) {
     v = ok ? *reinterpret_cast<const float2*>(static_cast<const float*>(base) + i) : make_float2(0.f, 0.f);
+  }
+  __device__ __forceinline__ void load32(const void* base, uint32_t i, bool ok) {
+    const float2 x = *reinterpret_cast<const float2*>(static_cast<const char*>(base) + 4u * i);
+    v = ok ? x : make_float2(0.f, 0.f);
   }
 };
 
