@@ -4,22 +4,29 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 A step is one kda_chunked_forward call over the 4-sequence x 16-head x
-4096-token bf16 workload (fp32 state, random h0, chunk 64): the gate cumsum,
-the intra-chunk UT/WY transform and the inter-chunk state chain, all in one
-kernel.  Inputs are resident in HBM before the timed region; before every
-timed step a 512 MiB buffer is written so the 256 MB Infinity Cache holds
-none of the step's inputs.  Each launch is bracketed by HIP events on the
-stream it runs on; ms_per_step is their mean.
+4096-token bf16 workload (fp32 state, random h0, chunk 64).  The call runs two
+kernels on the caller's stream: the intra-chunk kernel (gate cumsum, UT/WY
+transform and the chunk-local products of every (chunk, head), in parallel, to
+a workspace of per-chunk records) and the chain kernel (the sequential state
+recurrence and the outputs).  Inputs are resident in HBM before the timed
+region; before every timed step a 512 MiB buffer is written so the 256 MB
+Infinity Cache holds none of the step's inputs.  Each call is bracketed by HIP
+events on the stream it runs on; ms_per_step is their mean.  A second pass of
+the same steps through kda_chunked_forward_profiled gives each kernel's mean
+duration from events recorded between the kernels.
 
 The JSON line carries:
-  roofline      -- the prefill kernel against HBM (its binding roof: 110
-                   algorithmic flop per byte is below the bf16 ridge of ~315);
-                   achieved = algorithmic bytes per launch / mean launch time
-  roofline_mfma -- the same kernel's algorithmic flops against dense bf16 MFMA
-  decode        -- 1000 sequential kda_decode_step calls on the 256-sequence x
-                   32-head state (512 MiB fp32), bytes and fraction of HBM
-  cpu_baseline  -- the fp64 oracle on this host's cores over the same
-                   prefill workload (a baseline, not a target)
+  roofline       -- the dominant kernel (intra-chunk) against HBM, its binding
+                    roof: achieved = its algorithmic bytes per launch (inputs
+                    read + records written) / its mean duration
+  roofline_chain -- the chain kernel likewise (records read once, h0, hT, o)
+  roofline_mfma  -- the whole call's algorithmic flops against dense bf16 MFMA
+                    (the headline metric's "% of MFMA peak")
+  roofline_call_hbm -- the whole call's algorithmic bytes (inputs, o, h0, hT)
+  decode         -- 1000 sequential kda_decode_step calls on the 256-sequence x
+                    32-head state (512 MiB fp32), bytes and fraction of HBM
+  cpu_baseline   -- the fp64 oracle on this host's cores over one of the four
+                    sequences of the same workload (a baseline, not a target)
 Algorithmic work per token and head (d_k = d_v = d, chunk C):
   flops 6 d^2 + (C-1) d + 2 (C+1) d + 2 (C+1) d + C^2/3 ; bytes (3 d_k + d_v) s_in + s_beta + d_v s_out,
   plus 2 * 4 d_k d_v per (sequence, head) for h0 and hT.
@@ -36,8 +43,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2516.6  # MI355X dense bf16 MFMA
-PREFILL_SRC = os.path.join(ROOT, "gated_delta_rule_94_amd", "csrc", "kda_prefill.hip")
-DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_94_amd", "csrc", "kda_decode.hip")
+CSRC = os.path.join(ROOT, "gated_delta_rule_94_amd", "csrc")
+# the sources each kernel is built from (a counter reading is valid for these exact sources only)
+KERNEL_SOURCES = {
+    "intra": ("kda_intra.hip", "kda_device.h", "kda_record.h"),
+    "chain": ("kda_chain.hip", "kda_device.h", "kda_record.h"),
+    "decode": ("kda_decode.hip", "kda_device.h"),
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -54,19 +66,22 @@ def decode_bytes(B, H, dk, dv, s_in):
     return B * H * (2 * 4 * dk * dv + (3 * dk + dv) * s_in + s_in + dv * s_in)
 
 
-def sha256(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def sources_sha256(kernel_key):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel_key]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def measured_traffic(kernel_key, src):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if taken on this source."""
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if taken on these sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)[kernel_key]
     except (OSError, KeyError, ValueError):
         return None
-    if t.get("source_sha256") != sha256(src):
+    if t.get("source_sha256") != sources_sha256(kernel_key):
         return None
     return t["bytes_per_launch"]
 
@@ -163,13 +178,31 @@ def main():
         step(0)
     torch.cuda.synchronize()
     ms, wall = time_launches(step, args.steps, None if args.no_flush else flush)
+
+    # per-kernel durations: the same steps through the profiling entry point
+    k_ms = [0.0, 0.0]
+    for _ in range(args.steps):
+        if not args.no_flush:
+            flush()
+        a_ms, b_ms = kda.kda_chunked_forward_profiled(g["q"], g["k"], g["v"], g["g"], g["beta"], g["h0"], o, hT,
+                                                      chunk=w.chunk)
+        k_ms[0] += a_ms / args.steps
+        k_ms[1] += b_ms / args.steps
+
     s_in = 2
     tokens = w.B * w.T
+    n_in = w.B * w.T * w.H * ((3 * w.dk + w.dv) * s_in + s_in)  # q, k, g, v, beta
+    n_out = w.B * w.T * w.H * w.dv * s_in
+    n_state = w.B * w.H * w.dk * w.dv * 4
+    rec_bytes = kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.chunk, torch.bfloat16)  # the per-chunk records
+    intra_bytes = n_in + rec_bytes
+    chain_bytes = rec_bytes + 2 * n_state + n_out
     alg_bytes = prefill_bytes(w.B, w.T, w.H, w.dk, w.dv, s_in, s_in)
     alg_flops = w.B * w.T * w.H * prefill_flops_per_token_head(w.dk, w.dv, w.chunk)
+    gbs_intra = intra_bytes / (k_ms[0] * 1e-3) / 1e9
+    gbs_chain = chain_bytes / (k_ms[1] * 1e-3) / 1e9
     gbs = alg_bytes / (ms * 1e-3) / 1e9
     tfs = alg_flops / (ms * 1e-3) / 1e12
-    traffic = measured_traffic("prefill", PREFILL_SRC)
 
     out = {
         "metric": "KDA prefill tokens/s (% bf16 MFMA peak); decode GB/s (% HBM peak)",
@@ -187,12 +220,18 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d_k": w.dk, "d_v": w.dv, "chunk": w.chunk,
                    "state": "fp32", "h0": "N(0, 0.02)", "tokens_per_step": tokens,
                    "cache_flushed_between_steps": not args.no_flush},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "chunked_forward_kernel<bf16, d_k 128, chunk 64>",
-                     "alg_bytes_per_launch": alg_bytes},
+        "roofline": {"bound": "hbm", "achieved": gbs_intra, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs_intra / HBM_PEAK_GBS, "traffic": measured_traffic("intra"),
+                     "kernel": "kda::intra_chunk_kernel<false, 128, 128, 64>", "ms_per_launch": k_ms[0],
+                     "alg_bytes_per_launch": intra_bytes},
+        "roofline_chain": {"bound": "hbm", "achieved": gbs_chain, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": gbs_chain / HBM_PEAK_GBS, "traffic": measured_traffic("chain"),
+                           "kernel": "kda::chain_kernel<false, 128, 128, 64, 32>", "ms_per_launch": k_ms[1],
+                           "alg_bytes_per_launch": chain_bytes},
         "roofline_mfma": {"achieved": tfs, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                          "frac": tfs / MFMA_BF16_PEAK_TFS, "alg_flops_per_launch": alg_flops},
+                          "frac": tfs / MFMA_BF16_PEAK_TFS, "alg_flops_per_launch": alg_flops, "scope": "whole call"},
+        "roofline_call_hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                              "alg_bytes_per_launch": alg_bytes, "scope": "whole call"},
         "wall_s_timed_region": wall,
     }
 
@@ -219,22 +258,23 @@ def main():
             "workload": wd.name, "steps": args.decode_steps, "us_per_step": dms * 1e3,
             "tokens_per_s": wd.B / (dms * 1e-3), "wall_s": dwall,
             "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dgbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode", DECODE_SRC),
+                         "frac": dgbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode"),
                          "kernel": "decode_step_kernel<bf16, 128, 128>", "alg_bytes_per_launch": dbytes},
         }
         del state, pool
 
-    # ---------------- CPU baseline: the fp64 oracle on this host's cores, same prefill workload
+    # ---------------- CPU baseline: the fp64 oracle on this host's cores, one sequence of the workload
     if not args.no_cpu_baseline:
         import oracle
 
         threads = max(1, min(16, os.cpu_count() or 1))
+        one = {key: (val[:1] if val is not None else None) for key, val in d.items()}
         t0 = time.perf_counter()
-        oracle.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], nthreads=threads)
+        oracle.forward(one["q"], one["k"], one["v"], one["g"], one["beta"], one["h0"], nthreads=threads)
         secs = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": tokens / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                               "sample": "the full prefill workload (4 x 4096 tokens x 16 heads, fp64, token by "
-                                         "token), %.1f s wall on %d threads" % (secs, threads)}
+        out["cpu_baseline"] = {"value": w.T / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": "sequence 0 of the prefill workload (%d tokens x %d heads, fp64, token by "
+                                         "token), %.1f s wall on %d threads" % (w.T, w.H, secs, threads)}
 
     print(json.dumps(out))
 

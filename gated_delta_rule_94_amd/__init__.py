@@ -28,7 +28,8 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "K
 # exported symbols of libkda.so (the C ABI)
 EXPORTS = (
     "kda_status_string", "kda_version", "kda_chunked_forward_workspace_bytes", "kda_chunked_forward",
-    "kda_chunked_forward_varlen", "kda_chunked_forward_varlen_workspace_bytes", "kda_decode_step",
+    "kda_chunked_forward_profiled", "kda_chunked_forward_varlen", "kda_chunked_forward_varlen_workspace_bytes",
+    "kda_decode_step",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -46,6 +47,8 @@ _lib.kda_chunked_forward_varlen_workspace_bytes.argtypes = [_i32] * 8
 _lib.kda_chunked_forward_varlen_workspace_bytes.restype = _sz
 _lib.kda_chunked_forward.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp, _sz, _vp]
 _lib.kda_chunked_forward.restype = _i32
+_lib.kda_chunked_forward_profiled.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp, _sz, _vp, _vp]
+_lib.kda_chunked_forward_profiled.restype = _i32
 _lib.kda_chunked_forward_varlen.argtypes = [_vp] * 8 + [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
 _lib.kda_chunked_forward_varlen.restype = _i32
 _lib.kda_decode_step.argtypes = [_vp] * 7 + [_i32] * 4 + [_i32, _vp]
@@ -151,6 +154,28 @@ def kda_chunked_forward(q, k, v, g, beta, h0=None, *, chunk: int = 64, o=None, h
     if st:
         raise KDAError("kda_chunked_forward", st)
     return o, hT
+
+
+def kda_chunked_forward_profiled(q, k, v, g, beta, h0, o, hT, *, chunk: int = 64, workspace=None, stream=None):
+    """kda_chunked_forward into preallocated o / hT (hT may be None), returning the two kernels'
+    durations in ms (intra-chunk, chain) from HIP events on the stream; synchronises the stream."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("g", g, (B, T, H, dk)),
+                         ("v", v, (B, T, H, dv)), ("beta", beta, (B, T, H)), ("o", o, (B, T, H, dv))):
+        _check(name, t, shp, dt, dev)
+    _check("h0", h0, (B, H, dk, dv), torch.float32, dev)
+    _check("hT", hT, (B, H, dk, dv), torch.float32, dev)
+    ws_bytes = _lib.kda_chunked_forward_workspace_bytes(B, T, H, dk, dv, chunk, _dtype_code(q))
+    ws = _workspace(workspace, ws_bytes, dev)
+    ms = (ctypes.c_float * 2)()
+    st = _lib.kda_chunked_forward_profiled(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o),
+                                           _ptr(hT), B, T, H, dk, dv, chunk, _dtype_code(q), _ptr(ws), _nbytes(ws),
+                                           _stream(stream), ctypes.cast(ms, _vp))
+    if st:
+        raise KDAError("kda_chunked_forward_profiled", st)
+    return float(ms[0]), float(ms[1])
 
 
 def kda_chunked_forward_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen: int, h0=None, *, chunk: int = 64, o=None,

@@ -91,6 +91,44 @@ kda_status kda_chunked_forward(const void* q, const void* k, const void* v, cons
   return kda::launch_chunked_forward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_chunked_forward_profiled(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                        const float* h0, void* o, float* hT, int B, int T, int H, int d_k, int d_v,
+                                        int chunk, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                                        void* hip_stream, float* kernel_ms) {
+  if (!kernel_ms) return KDA_ERR_INVALID_ARG;
+  if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
+  const kda_status st = check_prefill(q, k, v, g, beta, h0, o, hT, B * T, H, d_k, d_v, chunk, dt);
+  if (st != KDA_OK) return st;
+  kernel_ms[0] = kernel_ms[1] = 0.f;
+  if (B == 0 || (T == 0 && !hT)) return KDA_OK;
+  if (!workspace_ok(workspace, workspace_bytes, kda_chunked_forward_workspace_bytes(B, T, H, d_k, d_v, chunk, dt)))
+    return KDA_ERR_WORKSPACE;
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  for (int i = 0; i < 3; ++i)
+    if (hipEventCreate(&ev[i]) != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
+      return KDA_ERR_HIP;
+    }
+  kda::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.h0 = h0; a.o = o; a.hT = hT;
+  a.cu_seqlens = nullptr;
+  a.num_seqs = B;
+  a.T = T;
+  a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk;
+  a.f32 = dt == KDA_F32;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  a.stream = hip_stream;
+  a.events = ev;
+  bool ok = kda::launch_chunked_forward(a) == hipSuccess && hipEventSynchronize(ev[2]) == hipSuccess &&
+            hipEventElapsedTime(&kernel_ms[0], ev[0], ev[1]) == hipSuccess &&
+            hipEventElapsedTime(&kernel_ms[1], ev[1], ev[2]) == hipSuccess;
+  for (int i = 0; i < 3; ++i) (void)hipEventDestroy(ev[i]);
+  return ok ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_chunked_forward_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,
                                       const float* h0, void* o, float* hT, const int32_t* cu_seqlens, int num_seqs,
                                       int T_total, int max_seqlen, int H, int d_k, int d_v, int chunk, kda_dtype dt,

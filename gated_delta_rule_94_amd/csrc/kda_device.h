@@ -135,8 +135,12 @@ __device__ __forceinline__ f32x4 mma16(const float (&a)[4], const float (&b)[4],
 
 // ---------------------------------------------------------------------------------------------
 // Packed element stores of operand type E (bf16 or fp32) to LDS or global memory.
+// two fp32 -> bf16 (round to nearest even) in one v_cvt_pk_bf16_f32; a in the low half
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+  const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
 }
 // two adjacent elements (4-byte or 8-byte aligned)
 template <bool F32>

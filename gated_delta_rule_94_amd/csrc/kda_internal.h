@@ -29,6 +29,7 @@ struct PrefillArgs {
   void* workspace;
   size_t workspace_bytes;
   void* stream;
+  hipEvent_t* events = nullptr;  // optional: [3] recorded before the intra kernel, between the kernels, after the chain
 };
 
 // intra-chunk kernel launch (kda_intra.hip)

@@ -51,6 +51,7 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
   unsigned char* records = static_cast<unsigned char*>(a.workspace);
   int32_t* chunk0 = nullptr;
   hipError_t e = hipSuccess;
+  if (a.events && (e = hipEventRecord(a.events[0], (hipStream_t)a.stream)) != hipSuccess) return e;
   if (varlen) {
     chunk0 = reinterpret_cast<int32_t*>(records + max_chunks * a.H * rb);
     e = launch_chunk_map(a.cu_seqlens, a.num_seqs, a.T, C, chunk0, a.stream);
@@ -70,6 +71,7 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
     e = launch_intra(L);
     if (e != hipSuccess) return e;
   }
+  if (a.events && (e = hipEventRecord(a.events[1], (hipStream_t)a.stream)) != hipSuccess) return e;
   ChainLaunch K;
   K.records = records; K.h0 = a.h0; K.o = a.o; K.hT = a.hT; K.cu = a.cu_seqlens; K.chunk0 = chunk0;
   K.units = a.num_seqs * a.H; K.H = a.H; K.T = a.T; K.nch = nch;
@@ -79,7 +81,9 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
   if (!a.f32 && (int64_t)K.units * (a.dv / 32) >= cus) ws = 32;
   K.ws = ws;
   K.stream = a.stream;
-  return launch_chain(K);
+  if ((e = launch_chain(K)) != hipSuccess) return e;
+  if (a.events) e = hipEventRecord(a.events[2], (hipStream_t)a.stream);
+  return e;
 }
 
 }  // namespace kda

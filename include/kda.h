@@ -90,6 +90,22 @@ kda_status kda_chunked_forward(const void* q, const void* k, const void* v, cons
                                kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * Profiling form of kda_chunked_forward: the same arguments, checks and
+ * results, plus kernel_ms[2] (host memory, non-NULL), which receives the
+ * durations in milliseconds of the two kernels of the call -- [0] the
+ * intra-chunk kernel (gate cumulative sums, the UT/WY transform and the
+ * chunk-local products; architecture blog, "Kimi Delta Attention: the linear
+ * core"), [1] the chain kernel (the sequential state recurrence) -- measured
+ * with HIP events recorded on hip_stream around each.  It creates and destroys
+ * its events and synchronises with the stream before returning, so it is for
+ * measurement, not for a launch loop.  kernel_ms is zeroed when nothing runs.
+ */
+kda_status kda_chunked_forward_profiled(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                        const float* h0, void* o, float* hT, int B, int T, int H, int d_k, int d_v,
+                                        int chunk, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                                        void* hip_stream, float* kernel_ms);
+
+/*
  * Packed variable-length prefill: num_seqs sequences concatenated along the
  * token axis (tensors as above with B = 1 and T = T_total); sequence n covers
  * tokens [cu_seqlens[n], cu_seqlens[n+1]).  cu_seqlens is an int32 device

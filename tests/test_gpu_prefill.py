@@ -174,6 +174,20 @@ def test_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+def test_profiled_entry_matches():
+    """kda_chunked_forward_profiled runs the same kernels: bitwise-equal results, positive timings."""
+    d = datagen.prefill_inputs(50, 2, 300, 4, 128, 128, BF16, 0.02)
+    a = gpu_forward(d, 64)
+    g = {key: dev_tensor(d[key]) for key in KEYS}
+    o = torch.empty_like(a[0])
+    hT = torch.empty_like(a[1])
+    ms = kda.kda_chunked_forward_profiled(g["q"], g["k"], g["v"], g["g"], g["beta"], dev_tensor(d["h0"]), o, hT,
+                                          chunk=64)
+    print("kernel ms", ms)
+    assert torch.equal(o, a[0]) and torch.equal(hT, a[1])
+    assert ms[0] > 0 and ms[1] > 0
+
+
 def test_workload_b4_h16_t4096_full():
     """The 4 x 16-head x 4096-token bf16 workload, every output against the oracle."""
     w = datagen.WORKLOADS["cfg1_bf16_b4_h16_t4096_d128"]
