@@ -108,6 +108,16 @@ __device__ __forceinline__ void st2_split(void* hi, void* lo, float a, float b) 
   }
 }
 
+// x of the lane D below within its 16-lane row (DPP row_shr; lanes with no source read 0), or 1
+// where m = 0.  The move must run with every lane enabled -- a DPP read from a lane disabled in
+// EXEC is invalid -- so the choice is arithmetic, fma(y, m, 1 - m) with m in {0, 1} (exact for
+// finite y), never a select the compiler could turn into an EXEC-masked branch around the move.
+template <int D>
+__device__ __forceinline__ float row_shr_or1(float x, float m) {
+  const float y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + D, 0xf, 0xf, true));
+  return __builtin_fmaf(y, m, 1.f - m);
+}
+
 // eight adjacent elements at an 8-byte aligned address
 template <bool F32>
 __device__ __forceinline__ void st8_a8(void* dst, const float (&x)[8]) {
@@ -178,10 +188,9 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   using R = Rec<F32, DK, DV, C>;
   constexpr int NT = Cf::NT, CP = Cf::CP, QS = Cf::QS, TS = Cf::TS, AS = Cf::AS, QW = Cf::QW;
   constexpr bool SPLIT = Cf::SPLIT;
-  constexpr int NPU = DK * NT;          // prep units: (channel pair, sub-tile, half sub-tile)
   constexpr int NVP = DV / 2;           // value-column pairs
   constexpr int NVU = NVP * (CP / 8);   // value units: (column pair, 8-token group)
-  static_assert(NPU <= 512 && NVU <= 512, "one unit per thread");
+  static_assert(128 * NT <= 512 && NVU <= 512, "one unit per thread");
   constexpr int KSQ = O::nks(QW);       // k-steps over one quarter
   constexpr int NPAIR = NT * (NT + 1) / 2;
   constexpr int NSLOT = (2 * NPAIR + 7) / 8;  // tile pairs per wave
@@ -203,13 +212,13 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   const int tid = threadIdx.x, lane = tid & 63, lo = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave work is a scalar branch
   const int H = p.H;
-  // prep unit of this thread: the units of one quarter are whole waves (32 NT threads), lanes
-  // (2 cpl + half) of one sub-tile cover 16 channel pairs x 2 halves
-  const int half = tid & 1, cpl = (tid >> 1) & 15;
-  const int psb = (tid >> 5) % NT, pq = (tid >> 5) / NT;
-  const bool pact = tid < NPU;
-  const int c0 = QW * pq + 2 * cpl;  // first of this thread's two channels
-  const int r0 = 16 * psb + 8 * half;
+  // prep unit of this thread: 2 consecutive rows (a row pair of one 16-row sub-tile) x 2 channels
+  // in every quarter of the key dimension.  The 8 row pairs of a sub-tile are 8 consecutive lanes,
+  // so prefix products over the sub-tile are an 8-lane scan; every quarter's operands are then
+  // built by all threads.
+  const int rp = tid & 7, cpl = (tid >> 3) & 15, psb = tid >> 7;
+  const bool pact = tid < 128 * NT;
+  const int r0 = 16 * psb + 2 * rp;  // rows r0, r0 + 1; channels QW qt + 2 cpl (+1) of quarter qt
   // value unit of this thread
   const int vcp = tid % NVP, vtg = tid / NVP;
   const bool vact = tid < NVU;
@@ -219,7 +228,8 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   const int item = blockIdx.x;
   if (item >= n_items) return;  // the grid covers the bound on the number of chunks
 
-  Raw2<F32> rg[8], rq[8], rk[8], rv[8];
+  constexpr int NQ = Cf::NQ;
+  Raw2<F32> rg[NQ][2], rq[NQ][2], rk[NQ][2], rv[8];
   float rb;
   {
     const int chunk = item / H;
@@ -236,14 +246,19 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
     // loads are unconditional: rows past the chunk's end (len >= 1) and idle threads read a valid
     // element, then take zero
     const int last = cp.len - 1;
-    const uint32_t kc = pact ? (uint32_t)c0 : 0u, vc = vact ? (uint32_t)(2 * vcp) : 0u;
+#pragma unroll
+    for (int qt = 0; qt < NQ; ++qt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bool ok = pact && (r0 + j) <= last;
+        const uint32_t off = (pact ? (uint32_t)(QW * qt + 2 * cpl) : 0u) + (uint32_t)min(r0 + j, last) * kstride;
+        rg[qt][j].load32(gb, off, ok);
+        rq[qt][j].load32(qb, off, ok);
+        rk[qt][j].load32(kb, off, ok);
+      }
+    const uint32_t vc = vact ? (uint32_t)(2 * vcp) : 0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const bool ok = pact && (r0 + i) <= last;
-      const uint32_t off = kc + (uint32_t)min(r0 + i, last) * kstride;
-      rg[i].load32(gb, off, ok);
-      rq[i].load32(qb, off, ok);
-      rk[i].load32(kb, off, ok);
       const bool okv = vact && (8 * vtg + i) <= last;
       rv[i].load32(vb, vc + (uint32_t)min(8 * vtg + i, last) * vstride, okv);
     }
@@ -253,97 +268,28 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   E* rec = reinterpret_cast<E*>(p.ws + (int64_t)item * R::BYTES);
   float* rgam = reinterpret_cast<float*>(p.ws + (int64_t)item * R::BYTES + R::GAM_BYTE);
 
-  // ---------------- prep: E = e^{G_r - R_b} (prefix products), F = e^{G_end - G_r} (suffix
-  // products) of this thread's 8 rows x 2 channels from e^g, the sub-tile halves combined by one
-  // lane exchange (lanes 2 cpl and 2 cpl + 1 hold the two halves).  Recomputed where needed
-  // rather than kept live across the stages.  Every lane of a pair must call it together.
-  auto factors = [&](float (&E0)[8], float (&E1)[8], float (&F0)[8], float (&F1)[8]) {
+  // ---------------- prep: E = e^{G_r - R_b} (prefix products of e^g inside the 16-row sub-tile,
+  // R_b = G before it) for this thread's rows and channels; Tb = the sub-tile's total decay.
+  // Then e^{R_b - G_r} = 1 / E and the suffix product e^{G_end - G_r} = Tb / E.
+  float Ef[NQ][2][2], Tb[NQ][2];  // [quarter][row j][channel]
+  const float m1 = rp >= 1 ? 1.f : 0.f, m2 = rp >= 2 ? 1.f : 0.f, m4 = rp >= 4 ? 1.f : 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {  // e^g, in E
-      const float2 gg = rg[i].f();
-      E0[i] = __expf(gg.x);
-      E1[i] = __expf(gg.y);
-    }
-    F0[7] = 1.f;
-    F1[7] = 1.f;
+  for (int qt = 0; qt < NQ; ++qt) {
+    const float2 g0 = rg[qt][0].f(), g1 = rg[qt][1].f();
 #pragma unroll
-    for (int i = 6; i >= 0; --i) {  // suffix products (exclusive)
-      F0[i] = F0[i + 1] * E0[i + 1];
-      F1[i] = F1[i + 1] * E1[i + 1];
+    for (int ch = 0; ch < 2; ++ch) {
+      const float a0 = __expf(ch ? g0.y : g0.x), a1 = __expf(ch ? g1.y : g1.x);
+      float x = a0 * a1;  // this row pair's product; inclusive scan over the 8 row pairs
+      x *= row_shr_or1<1>(x, m1);
+      x *= row_shr_or1<2>(x, m2);
+      x *= row_shr_or1<4>(x, m4);
+      Ef[qt][0][ch] = row_shr_or1<1>(x, m1) * a0;
+      Ef[qt][1][ch] = x;
+      Tb[qt][ch] = __shfl(x, (tid & 63) | 7);  // row pair 7 of this sub-tile
     }
-#pragma unroll
-    for (int i = 1; i < 8; ++i) {  // prefix products (inclusive), in place
-      E0[i] *= E0[i - 1];
-      E1[i] *= E1[i - 1];
-    }
-    // the second half continues the first half's prefix, the first half the second half's suffix
-    const float o0 = __shfl_xor(E0[7], 1), o1 = __shfl_xor(E1[7], 1);
-    const float pe0 = half ? o0 : 1.f, pe1 = half ? o1 : 1.f;
-    const float pf0 = half ? 1.f : o0, pf1 = half ? 1.f : o1;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      E0[i] *= pe0;
-      E1[i] *= pe1;
-      F0[i] *= pf0;
-      F1[i] *= pf1;
-    }
-  };
-  float E0[8], E1[8], F0[8], F1[8];
-  factors(E0, E1, F0, F1);
-  if (pact && half) {
-    Eend[psb * DK + c0] = E0[7];
-    Eend[psb * DK + c0 + 1] = E1[7];
+    if (pact && rp == 7) *reinterpret_cast<float2*>(Eend + psb * DK + QW * qt + 2 * cpl) = make_float2(Tb[qt][0], Tb[qt][1]);
   }
   if (tid < C) Bet[tid] = rb;
-  __syncthreads();
-
-  // ---------------- Q.Gamma and K'^T to the record; prefix / suffix decays of the other sub-tiles
-  float eP0 = 1.f, eP1 = 1.f;
-  {
-    float eS0 = 1.f, eS1 = 1.f;
-#pragma unroll
-    for (int x = 0; x < NT; ++x) {
-      const float e0 = Eend[x * DK + c0], e1 = Eend[x * DK + c0 + 1];
-      if (x < psb) { eP0 *= e0; eP1 *= e1; }
-      if (x > psb) { eS0 *= e0; eS1 *= e1; }
-    }
-    if (pact && psb == 0 && half == 0) {
-      float g0 = 1.f, g1 = 1.f;
-#pragma unroll
-      for (int x = 0; x < NT; ++x) { g0 *= Eend[x * DK + c0]; g1 *= Eend[x * DK + c0 + 1]; }
-      *reinterpret_cast<float2*>(rgam + c0) = make_float2(g0, g1);
-    }
-    if (pact) {
-      float kp0[8], kp1[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float2 qq = rq[i].f(), kk = rk[i].f();
-        st2<F32>(rec + R::QG + (r0 + i) * DK + c0, qq.x * (E0[i] * eP0), qq.y * (E1[i] * eP1));
-        kp0[i] = kk.x * (F0[i] * eS0);
-        kp1[i] = kk.y * (F1[i] * eS1);
-      }
-      st8<F32>(rec + R::KPT + c0 * CP + r0, kp0);
-      st8<F32>(rec + R::KPT + (c0 + 1) * CP + r0, kp1);
-    }
-    if (pact) {  // (K . Gamma)^T for the W product
-      float kg0[8], kg1[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float2 kk = rk[i].f();
-        kg0[i] = kk.x * (E0[i] * eP0);
-        kg1[i] = kk.y * (E1[i] * eP1);
-      }
-      st8_a8<F32>(KGt + c0 * TS + r0, kg0);
-      st8_a8<F32>(KGt + (c0 + 1) * TS + r0, kg1);
-    }
-    if constexpr (CP > C) {  // token pads of K'^T and (K . Gamma)^T are zero
-      for (int e = tid; e < DK * (CP - C); e += 512) {
-        const int c = e / (CP - C), t = C + e % (CP - C);
-        rec[R::KPT + c * CP + t] = (E)0.f;
-        KGt[c * TS + t] = (E)0.f;
-      }
-    }
-  }
   if (vact) {  // V^T for the U~ product
     float x0[8], x1[8];
 #pragma unroll
@@ -355,44 +301,96 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
     st8_a8<F32>(Vt + (2 * vcp) * TS + 8 * vtg, x0);
     st8_a8<F32>(Vt + (2 * vcp + 1) * TS + 8 * vtg, x1);
   }
+  __syncthreads();
+
+  // ---------------- Q.Gamma and K'^T to the record, (K.Gamma)^T to LDS; prefix decay eP of the
+  // earlier sub-tiles (kept for nothing else) and suffix decay eS of the later ones
+  if (pact) {
+#pragma unroll
+    for (int qt = 0; qt < NQ; ++qt) {
+      const int c0 = QW * qt + 2 * cpl;
+      float eP[2] = {1.f, 1.f}, eS[2] = {1.f, 1.f}, ga[2] = {1.f, 1.f};
+#pragma unroll
+      for (int x = 0; x < NT; ++x) {
+        const float2 e = *reinterpret_cast<const float2*>(Eend + x * DK + c0);
+        if (x < psb) { eP[0] *= e.x; eP[1] *= e.y; }
+        if (x > psb) { eS[0] *= e.x; eS[1] *= e.y; }
+        ga[0] *= e.x;
+        ga[1] *= e.y;
+      }
+      if (psb == 0 && rp == 0) *reinterpret_cast<float2*>(rgam + c0) = make_float2(ga[0], ga[1]);
+      float qg[2][2], kg[2][2], kp[2][2];  // [row j][channel]
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float2 qq = rq[qt][j].f(), kk = rk[qt][j].f();
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+          const float e = Ef[qt][j][ch];
+          const float qv = ch ? qq.y : qq.x, kv = ch ? kk.y : kk.x;
+          qg[j][ch] = qv * (e * eP[ch]);
+          kg[j][ch] = kv * (e * eP[ch]);
+          kp[j][ch] = kv * (Tb[qt][ch] * __builtin_amdgcn_rcpf(e) * eS[ch]);
+        }
+        st2<F32>(rec + R::QG + (r0 + j) * DK + c0, qg[j][0], qg[j][1]);
+      }
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        st2<F32>(rec + R::KPT + (c0 + ch) * CP + r0, kp[0][ch], kp[1][ch]);
+        st2<F32>(KGt + (c0 + ch) * TS + r0, kg[0][ch], kg[1][ch]);
+      }
+    }
+  }
+  if constexpr (CP > C) {  // token pads of K'^T and (K . Gamma)^T are zero
+    for (int e = tid; e < DK * (CP - C); e += 512) {
+      const int c = e / (CP - C), t = C + e % (CP - C);
+      rec[R::KPT + c * CP + t] = (E)0.f;
+      KGt[c * TS + t] = (E)0.f;
+    }
+  }
 
   // ---------------- M_kk and M_qk, one quarter of the key dimension at a time
   f32x4 acc[NSLOT];
 #pragma unroll
   for (int sl = 0; sl < NSLOT; ++sl) acc[sl] = zero4();
-  for (int qt = 0; qt < Cf::NQ; ++qt) {
-    if (pact && pq == qt) {
-      factors(E0, E1, F0, F1);
-      // operands of this thread's rows and channels: Q and K rows scaled by e^{G_r - R_b}, K columns
-      // for the diagonal sub-tile (e^{R_b - G_i}), for earlier sub-tiles (e^{G_end - G_i}) and for
-      // each gap pair (times the decay of the sub-tiles in between); bf16 as hi + lo
+#pragma unroll
+  for (int qt = 0; qt < NQ; ++qt) {
+    if (pact) {
+      // operands of this thread's rows and channels: Q and K rows scaled by E = e^{G_r - R_b}, K
+      // columns for the diagonal sub-tile (1 / E = e^{R_b - G_i}), for earlier sub-tiles (Tb / E =
+      // e^{G_end - G_i}) and for each gap pair (times the decay of the sub-tiles in between);
+      // bf16 as hi + lo
       const int cl = 2 * cpl;
-      const float rT0 = 1.f / Eend[psb * DK + c0], rT1 = 1.f / Eend[psb * DK + c0 + 1];
       float gp[Cf::NGAP > 0 ? Cf::NGAP : 1][2];
       if constexpr (Cf::NGAP > 0) {  // gap pairs (2,0), (3,0), (3,1): decay of the sub-tiles strictly between
-        gp[0][0] = Eend[1 * DK + c0];
-        gp[0][1] = Eend[1 * DK + c0 + 1];
-        gp[1][0] = gp[0][0] * Eend[2 * DK + c0];
-        gp[1][1] = gp[0][1] * Eend[2 * DK + c0 + 1];
-        gp[2][0] = Eend[2 * DK + c0];
-        gp[2][1] = Eend[2 * DK + c0 + 1];
+        const float2 e1 = *reinterpret_cast<const float2*>(Eend + 1 * DK + QW * qt + cl);
+        const float2 e2 = *reinterpret_cast<const float2*>(Eend + 2 * DK + QW * qt + cl);
+        gp[0][0] = e1.x;
+        gp[0][1] = e1.y;
+        gp[1][0] = e1.x * e2.x;
+        gp[1][1] = e1.y * e2.y;
+        gp[2][0] = e2.x;
+        gp[2][1] = e2.y;
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = r0 + i;
-        const float2 qq = rq[i].f(), kk = rk[i].f();
+      for (int j = 0; j < 2; ++j) {
+        const int r = r0 + j;
+        const float2 qq = rq[qt][j].f(), kk = rk[qt][j].f();
+        const float e0 = Ef[qt][j][0], e1 = Ef[qt][j][1];
+        const float i0 = __builtin_amdgcn_rcpf(e0), i1 = __builtin_amdgcn_rcpf(e1);
+        const float kd0 = kk.x * i0, kd1 = kk.y * i1;              // diagonal columns
+        const float ko0 = kd0 * Tb[qt][0], ko1 = kd1 * Tb[qt][1];  // earlier columns
         const int o = r * QS + cl;
-        st2_split<F32>(opnd(0, 0) + o, opnd(0, SPLIT) + o, qq.x * E0[i], qq.y * E1[i]);
-        st2_split<F32>(opnd(1, 0) + o, opnd(1, SPLIT) + o, kk.x * E0[i], kk.y * E1[i]);
-        st2_split<F32>(opnd(2, 0) + o, opnd(2, SPLIT) + o, kk.x * (F0[i] * rT0), kk.y * (F1[i] * rT1));
-        st2_split<F32>(opnd(3, 0) + o, opnd(3, SPLIT) + o, kk.x * F0[i], kk.y * F1[i]);
+        st2_split<F32>(opnd(0, 0) + o, opnd(0, SPLIT) + o, qq.x * e0, qq.y * e1);
+        st2_split<F32>(opnd(1, 0) + o, opnd(1, SPLIT) + o, kk.x * e0, kk.y * e1);
+        st2_split<F32>(opnd(2, 0) + o, opnd(2, SPLIT) + o, kd0, kd1);
+        st2_split<F32>(opnd(3, 0) + o, opnd(3, SPLIT) + o, ko0, ko1);
         if constexpr (Cf::NGAP > 0) {
           const int og = (r - 16 * psb) * QS + cl;
 #pragma unroll
           for (int gi = 0; gi < Cf::NGAP; ++gi) {
             const int ga = gi == 2 ? 1 : 0;  // column sub-tile of gap pair gi
             if (psb == ga)
-              st2_split<F32>(gapt(gi, 0) + og, gapt(gi, SPLIT) + og, kk.x * F0[i] * gp[gi][0], kk.y * F1[i] * gp[gi][1]);
+              st2_split<F32>(gapt(gi, 0) + og, gapt(gi, SPLIT) + og, ko0 * gp[gi][0], ko1 * gp[gi][1]);
           }
         }
       }
