@@ -10,8 +10,7 @@
 // workgroup owns a WS-column slice of the state and the slices of one head run on different
 // CUs -- exact, and it spreads even one long sequence over several CUs.
 //
-// Workgroup of four waves: WS / 16 chain waves, each owning 16 value columns of the state, and
-// the others copy.
+// Workgroup: WS / 16 chain waves, each owning 16 value columns of the state, and four copy waves.
 // The fp32 state lives in MFMA accumulator registers and is fed back as the B operand of the
 // next chunk's products; U likewise.  The copy waves stream records from HBM into double-buffered
 // LDS two chunks ahead (two register staging sets): while the chain waves compute chunk n, the
@@ -39,10 +38,10 @@ struct ChainCfg {
   using R = Rec<F32, DK, DV, C>;
   static constexpr int NT = C / 16, CP = R::CP;
   static constexpr int NW = WS / 16;  // chain waves
-  static constexpr int NH = 4 - NW;   // copy waves
-  static constexpr int NTH = 256;
+  static constexpr int NH = 4;        // copy waves
+  static constexpr int NTH = 64 * (NW + NH);
   static constexpr int NC = 64 * NH;  // copy threads
-  static_assert(NW >= 1 && NH >= 2, "slice of 16 or 32 columns");
+  static_assert(NW == 1 || NW == 2, "slice of 16 or 32 columns");
   static constexpr int RS = DK + 8, TS = CP + 8, US = C + 8;  // US: stride of the U~^T slice [WS][C]
   static constexpr int ES = (int)sizeof(E);
   static constexpr int EPU = 16 / ES;  // elements per 16-byte copy unit
@@ -60,12 +59,11 @@ struct ChainCfg {
   static constexpr int U_NW = C * DK / EPU, U_QG = C * DK / EPU, U_P = C * CP / EPU, U_KPT = DK * CP / EPU;
   static constexpr int U_UT = WS * C / EPU, U_GAM = DK / 4;
   static constexpr int UNITS = U_NW + U_QG + U_P + U_KPT + U_UT + U_GAM;
-  static constexpr int UPT = (UNITS + NTH - 1) / NTH;  // units per thread
 };
 
 // One part of a record copied by the NC copy threads in 16-byte units: NU units, UPR units per
-// row.  Units past the end repeat the last one (same bytes to the same place), so the copy has no
-// branches and the compiler counts outstanding loads exactly across the pipeline.
+// row.  Loads of units past the end repeat the last one (in bounds, unconditional, so the
+// compiler counts outstanding loads exactly across the pipeline); their LDS stores are skipped.
 // SW: bf16 tiles read as 8-byte fragment pieces are stored with the two 8-byte halves of every
 // 16-byte unit swapped in rows whose bit 3 is set.  The fragment reads of 16 lanes (rows lo =
 // 0..15, one piece each) then fall on distinct LDS banks; unswizzled, rows lo and lo + 8 share
@@ -93,6 +91,7 @@ struct CopyPart {
   __device__ __forceinline__ void store(unsigned char* buf, int ht) const {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
+      if (NU % NC != 0 && ht + NC * k >= NU) continue;  // only the last slot can be partial
       const int u = unit(ht, k);
       const int row = u / UPR;
       const uint32_t a0 = st[4 * k], a1 = st[4 * k + 1], a2 = st[4 * k + 2], a3 = st[4 * k + 3];
@@ -112,7 +111,7 @@ struct CopyPart {
 };
 
 template <bool F32, int DK, int DV, int C, int WS>
-__global__ __launch_bounds__(256) void chain_kernel(const ChainParams p) {
+__global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainParams p) {
   using Cf = ChainCfg<F32, DK, DV, C, WS>;
   using O = typename Cf::O;
   using E = typename Cf::E;
@@ -343,7 +342,8 @@ static hipError_t launch_chain_impl(const ChainLaunch& L) {
   p.ws = L.records; p.h0 = L.h0; p.o = L.o; p.hT = L.hT; p.cu = L.cu; p.chunk0 = L.chunk0;
   p.units = L.units; p.H = L.H; p.T = L.T; p.nch = L.nch; p.dv = DV;
   const int grid = ((L.units + 7) / 8) * 8 * (DV / WS);
-  hipLaunchKernelGGL((chain_kernel<F32, DK, DV, C, WS>), dim3(grid), dim3(256), 0, (hipStream_t)L.stream, p);
+  hipLaunchKernelGGL((chain_kernel<F32, DK, DV, C, WS>), dim3(grid), dim3(ChainCfg<F32, DK, DV, C, WS>::NTH), 0,
+                     (hipStream_t)L.stream, p);
   return hipGetLastError();
 }
 
