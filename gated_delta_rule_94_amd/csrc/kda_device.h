@@ -114,6 +114,14 @@ struct Op<true> {
   static constexpr int nks(int n) { return n / 4; }
 };
 
+// two fp32 -> bf16 (round to nearest even) in one v_cvt_pk_bf16_f32; a in the low half
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // 16x16x16 product D += A B with A given as a[j] = A[lo][4 grp + j] and B as b[j] = B[4 grp + j][lo]
 // (accumulator order): one bf16 16x16x16 MFMA, or four fp32 16x16x4 MFMAs.
 template <bool F32>
@@ -123,25 +131,14 @@ __device__ __forceinline__ f32x4 mma16(const float (&a)[4], const float (&b)[4],
     for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
     return c;
   } else {
-    bf16x4 av, bv;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      av[j] = (__bf16)a[j];
-      bv[j] = (__bf16)b[j];
-    }
+    const bf16x4 av = __builtin_bit_cast(bf16x4, make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])));
+    const bf16x4 bv = __builtin_bit_cast(bf16x4, make_uint2(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])));
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, c, 0, 0, 0);
   }
 }
 
 // ---------------------------------------------------------------------------------------------
 // Packed element stores of operand type E (bf16 or fp32) to LDS or global memory.
-// two fp32 -> bf16 (round to nearest even) in one v_cvt_pk_bf16_f32; a in the low half
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
-  return __builtin_bit_cast(uint32_t, h);
-}
 // two adjacent elements (4-byte or 8-byte aligned)
 template <bool F32>
 __device__ __forceinline__ void st2(void* dst, float a, float b) {

@@ -216,8 +216,9 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   // in every quarter of the key dimension.  The 8 row pairs of a sub-tile are 8 consecutive lanes,
   // so prefix products over the sub-tile are an 8-lane scan; every quarter's operands are then
   // built by all threads.
-  const int rp = tid & 7, cpl = (tid >> 3) & 15, psb = tid >> 7;
-  const bool pact = tid < 128 * NT;
+  const int rp = tid & 7, cpl = (tid >> 3) & 15;
+  const int psb = __builtin_amdgcn_readfirstlane(tid >> 7);  // sub-tile: uniform over a wave
+  const bool pact = psb < NT;
   const int r0 = 16 * psb + 2 * rp;  // rows r0, r0 + 1; channels QW qt + 2 cpl (+1) of quarter qt
   // value unit of this thread
   const int vcp = tid % NVP, vtg = tid / NVP;
@@ -303,33 +304,47 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   }
   __syncthreads();
 
-  // ---------------- Q.Gamma and K'^T to the record, (K.Gamma)^T to LDS; prefix decay eP of the
-  // earlier sub-tiles (kept for nothing else) and suffix decay eS of the later ones
+  // q, k as fp32 and 1 / E, kept for the quarter builds
+  float qf[NQ][2][2], kf[NQ][2][2], iE[NQ][2][2];
+#pragma unroll
+  for (int qt = 0; qt < NQ; ++qt)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float2 qq = rq[qt][j].f(), kk = rk[qt][j].f();
+      qf[qt][j][0] = qq.x;
+      qf[qt][j][1] = qq.y;
+      kf[qt][j][0] = kk.x;
+      kf[qt][j][1] = kk.y;
+      iE[qt][j][0] = __builtin_amdgcn_rcpf(Ef[qt][j][0]);
+      iE[qt][j][1] = __builtin_amdgcn_rcpf(Ef[qt][j][1]);
+    }
+
+  // ---------------- Q.Gamma and K'^T to the record, (K.Gamma)^T to LDS: the prefix decay eP of the
+  // earlier sub-tiles and the suffix decay eS of the later ones (the sub-tile is wave-uniform)
   if (pact) {
 #pragma unroll
     for (int qt = 0; qt < NQ; ++qt) {
       const int c0 = QW * qt + 2 * cpl;
-      float eP[2] = {1.f, 1.f}, eS[2] = {1.f, 1.f}, ga[2] = {1.f, 1.f};
+      float eP[2] = {1.f, 1.f}, eS[2] = {1.f, 1.f};
 #pragma unroll
       for (int x = 0; x < NT; ++x) {
         const float2 e = *reinterpret_cast<const float2*>(Eend + x * DK + c0);
         if (x < psb) { eP[0] *= e.x; eP[1] *= e.y; }
         if (x > psb) { eS[0] *= e.x; eS[1] *= e.y; }
-        ga[0] *= e.x;
-        ga[1] *= e.y;
       }
-      if (psb == 0 && rp == 0) *reinterpret_cast<float2*>(rgam + c0) = make_float2(ga[0], ga[1]);
+      if (psb == 0 && rp == 0) {  // e^{G_last} = eS of sub-tile 0 times its own total
+        *reinterpret_cast<float2*>(rgam + c0) = make_float2(eS[0] * Tb[qt][0], eS[1] * Tb[qt][1]);
+      }
       float qg[2][2], kg[2][2], kp[2][2];  // [row j][channel]
+      const float tS[2] = {Tb[qt][0] * eS[0], Tb[qt][1] * eS[1]};
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float2 qq = rq[qt][j].f(), kk = rk[qt][j].f();
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-          const float e = Ef[qt][j][ch];
-          const float qv = ch ? qq.y : qq.x, kv = ch ? kk.y : kk.x;
-          qg[j][ch] = qv * (e * eP[ch]);
-          kg[j][ch] = kv * (e * eP[ch]);
-          kp[j][ch] = kv * (Tb[qt][ch] * __builtin_amdgcn_rcpf(e) * eS[ch]);
+          const float eg = Ef[qt][j][ch] * eP[ch];
+          qg[j][ch] = qf[qt][j][ch] * eg;
+          kg[j][ch] = kf[qt][j][ch] * eg;
+          kp[j][ch] = kf[qt][j][ch] * (iE[qt][j][ch] * tS[ch]);
         }
         st2<F32>(rec + R::QG + (r0 + j) * DK + c0, qg[j][0], qg[j][1]);
       }
@@ -374,14 +389,13 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int r = r0 + j;
-        const float2 qq = rq[qt][j].f(), kk = rk[qt][j].f();
         const float e0 = Ef[qt][j][0], e1 = Ef[qt][j][1];
-        const float i0 = __builtin_amdgcn_rcpf(e0), i1 = __builtin_amdgcn_rcpf(e1);
-        const float kd0 = kk.x * i0, kd1 = kk.y * i1;              // diagonal columns
-        const float ko0 = kd0 * Tb[qt][0], ko1 = kd1 * Tb[qt][1];  // earlier columns
+        const float k0 = kf[qt][j][0], k1 = kf[qt][j][1];
+        const float kd0 = k0 * iE[qt][j][0], kd1 = k1 * iE[qt][j][1];  // diagonal columns
+        const float ko0 = kd0 * Tb[qt][0], ko1 = kd1 * Tb[qt][1];      // earlier columns
         const int o = r * QS + cl;
-        st2_split<F32>(opnd(0, 0) + o, opnd(0, SPLIT) + o, qq.x * e0, qq.y * e1);
-        st2_split<F32>(opnd(1, 0) + o, opnd(1, SPLIT) + o, kk.x * e0, kk.y * e1);
+        st2_split<F32>(opnd(0, 0) + o, opnd(0, SPLIT) + o, qf[qt][j][0] * e0, qf[qt][j][1] * e1);
+        st2_split<F32>(opnd(1, 0) + o, opnd(1, SPLIT) + o, k0 * e0, k1 * e1);
         st2_split<F32>(opnd(2, 0) + o, opnd(2, SPLIT) + o, kd0, kd1);
         st2_split<F32>(opnd(3, 0) + o, opnd(3, SPLIT) + o, ko0, ko1);
         if constexpr (Cf::NGAP > 0) {
