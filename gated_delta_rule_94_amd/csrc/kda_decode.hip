@@ -10,35 +10,38 @@
 //   S  = S' + k u^T,   o = S^T q = r + (k . q) u
 // so the state is read once and written once, and o needs no second pass.
 //
-// This is pure HBM streaming (about 0.9 flop per byte): one workgroup of 256
-// threads owns one (sequence, head); each thread holds DK/RG rows x 4 columns
-// of the state in registers (float4 accesses, a wave covers whole 512-byte
-// rows), reduces its partial column sums across row groups with cross-lane
-// shuffles and one LDS exchange between the four waves, then writes back.
+// This is pure HBM streaming (about 0.9 flop per byte).  Value columns of the state evolve
+// independently (the gate acts on rows), so a (sequence, head) is split over NS workgroups by
+// value-column slices: more, smaller workgroups interleave their read and write phases better.
+// Each of the 256 threads holds RPT rows x 4 columns of its slice in registers (float4 accesses,
+// non-temporal: the state is read and written once per step), reduces its partial column sums
+// across row groups with cross-lane shuffles and one LDS exchange between the four waves, then
+// writes back.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
-template <bool F32, int DK, int DV>
+template <bool F32, int DK, int DV, int NS>
 __global__ __launch_bounds__(256) void decode_step_kernel(const void* __restrict__ q, const void* __restrict__ k,
                                                           const void* __restrict__ v, const void* __restrict__ g,
                                                           const void* __restrict__ beta, float* __restrict__ state,
                                                           void* __restrict__ o) {
-  constexpr int C4 = DV / 4;       // threads across one state row (float4 each)
+  constexpr int DW = DV / NS;      // value columns of this workgroup's slice
+  constexpr int C4 = DW / 4;       // threads across one slice row (float4 each)
   constexpr int RG = 256 / C4;     // row groups
   constexpr int RPT = DK / RG;     // rows per thread
-  constexpr int RG_WAVE = 64 / C4; // row groups inside one wave
-  static_assert(RG * C4 == 256 && RPT * RG == DK, "shape");
+  static_assert(RG * C4 == 256 && RPT * RG == DK && C4 <= 64, "shape");
 
   __shared__ float s_k[DK], s_q[DK], s_a[DK];
-  __shared__ float s_part[4][2][DV];  // per-wave partial p and r
+  __shared__ float s_part[4][2][DW];  // per-wave partial p and r
   __shared__ float s_kq[4];
 
-  const int unit = blockIdx.x;  // b * H + h
+  const int unit = blockIdx.x / NS;  // b * H + h
+  const int col0 = (blockIdx.x - unit * NS) * DW;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int64_t vec_k = (int64_t)unit * DK, vec_v = (int64_t)unit * DV;
+  const int64_t vec_k = (int64_t)unit * DK, vec_v = (int64_t)unit * DV + col0;
 
   // gate, key and query of this (sequence, head); k.q by a block reduction
   float kq = 0.f;
@@ -54,10 +57,11 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const void* __restrict
   if (lane == 0) s_kq[wave] = kq;
 
   const int c4 = tid % C4, rg = tid / C4;
-  float4* S4 = reinterpret_cast<float4*>(state + (int64_t)unit * DK * DV);
-  float4 s[RPT];
+  f32x4* S4 = reinterpret_cast<f32x4*>(state + (int64_t)unit * DK * DV + col0);
+  constexpr int RS4 = DV / 4;  // float4 per full state row
+  f32x4 s[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) s[i] = S4[(rg + RG * i) * C4 + c4];
+  for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(S4 + (rg + RG * i) * RS4 + c4);
   __syncthreads();
 
   float p[4] = {0.f, 0.f, 0.f, 0.f}, r[4] = {0.f, 0.f, 0.f, 0.f};
@@ -107,15 +111,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const void* __restrict
   for (int i = 0; i < RPT; ++i) {
     const float kr = s_k[rg + RG * i];
     s[i].x += kr * u[0]; s[i].y += kr * u[1]; s[i].z += kr * u[2]; s[i].w += kr * u[3];
-    S4[(rg + RG * i) * C4 + c4] = s[i];
+    __builtin_nontemporal_store(s[i], S4 + (rg + RG * i) * RS4 + c4);
   }
-  (void)RG_WAVE;
 }
 
 template <bool F32, int DK, int DV>
 static hipError_t launch_decode(const DecodeArgs& a) {
-  hipLaunchKernelGGL((decode_step_kernel<F32, DK, DV>), dim3(a.units), dim3(256), 0, (hipStream_t)a.stream, a.q, a.k,
-                     a.v, a.g, a.beta, a.state, a.o);
+  constexpr int NS = DV == 128 ? 2 : 1;  // value-column slices per (sequence, head)
+  hipLaunchKernelGGL((decode_step_kernel<F32, DK, DV, NS>), dim3(a.units * NS), dim3(256), 0, (hipStream_t)a.stream,
+                     a.q, a.k, a.v, a.g, a.beta, a.state, a.o);
   return hipGetLastError();
 }
 
