@@ -153,13 +153,9 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
   const int ccol = col0 + 16 * (chain ? wave : 0) + lo;  // value column of this lane
   const int64_t sbase = (int64_t)unit * DK * DVr;
 
-  // ---- state S in accumulator layout: Sacc[m][r] = S[16 m + 4 grp + r][ccol]
+  // ---- state S in accumulator layout: Sacc[m][r] = S[16 m + 4 grp + r][ccol]; set and used on the
+  // chain waves' path only, so it is not live across the copy waves' loop
   f32x4 Sacc[DK / 16];
-#pragma unroll
-  for (int m = 0; m < DK / 16; ++m)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      Sacc[m][r] = (chain && p.h0) ? p.h0[sbase + (int64_t)(16 * m + 4 * grp + r) * DVr + ccol] : 0.f;
 
   // ---- record streaming: 16-byte units, global -> registers -> LDS.  Two register staging sets
   // alternate, so a record's loads are issued two chunks before it is computed.
@@ -301,6 +297,10 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
   // free; the copy waves fill buffer (c+1)&1 while the chain waves read buffer c&1.
   const int last = nchunks - 1;
   if (chain) {
+#pragma unroll
+    for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Sacc[m][r] = p.h0 ? p.h0[sbase + (int64_t)(16 * m + 4 * grp + r) * DVr + ccol] : 0.f;
     __syncthreads();
     for (int c = 0; c < nchunks; c += 2) {
       chunk_step(c, 0);
@@ -308,6 +308,12 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
       if (c + 1 >= nchunks) break;
       chunk_step(c + 1, 1);
       __syncthreads();
+    }
+    if (p.hT) {
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p.hT[sbase + (int64_t)(16 * m + 4 * grp + r) * DVr + ccol] = Sacc[m][r];
     }
   } else {
     Stage s0, s1;
@@ -328,12 +334,6 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     }
   }
 
-  if (chain && p.hT) {
-#pragma unroll
-    for (int m = 0; m < DK / 16; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p.hT[sbase + (int64_t)(16 * m + 4 * grp + r) * DVr + ccol] = Sacc[m][r];
-  }
 }
 
 template <bool F32, int DK, int DV, int C, int WS>
