@@ -27,7 +27,8 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "K
 
 # exported symbols of libkda.so (the C ABI)
 EXPORTS = (
-    "kda_status_string", "kda_version", "kda_chunked_forward_workspace_bytes", "kda_chunked_forward",
+    "kda_status_string", "kda_version", "kda_chunked_forward_workspace_bytes", "kda_chunked_forward_plan",
+    "kda_chunked_forward",
     "kda_chunked_forward_profiled", "kda_chunked_forward_varlen", "kda_chunked_forward_varlen_workspace_bytes",
     "kda_decode_step",
 )
@@ -43,6 +44,8 @@ _lib.kda_version.argtypes = []
 _lib.kda_version.restype = _i32
 _lib.kda_chunked_forward_workspace_bytes.argtypes = [_i32] * 7
 _lib.kda_chunked_forward_workspace_bytes.restype = _sz
+_lib.kda_chunked_forward_plan.argtypes = [_i32] * 7 + [_vp] * 3
+_lib.kda_chunked_forward_plan.restype = _i32
 _lib.kda_chunked_forward_varlen_workspace_bytes.argtypes = [_i32] * 8
 _lib.kda_chunked_forward_varlen_workspace_bytes.restype = _sz
 _lib.kda_chunked_forward.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp, _sz, _vp]
@@ -107,6 +110,18 @@ def _nbytes(ws):
 def workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:
     """Device workspace kda_chunked_forward needs for this shape."""
     return int(_lib.kda_chunked_forward_workspace_bytes(B, T, H, dk, dv, chunk, _dtype_code(torch.empty(0, dtype=dtype))))
+
+
+def chain_plan(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16):
+    """(value_slice, segments, segment_chunks): how kda_chunked_forward lays out its state chain on
+    the current device for this shape."""
+    out = (ctypes.c_int * 3)()
+    addr = ctypes.addressof(out)
+    st = _lib.kda_chunked_forward_plan(B, T, H, dk, dv, chunk, _dtype_code(torch.empty(0, dtype=dtype)),
+                                       addr, addr + 4, addr + 8)
+    if st != 0:
+        raise KDAError("kda_chunked_forward_plan", st)
+    return int(out[0]), int(out[1]), int(out[2])
 
 
 def varlen_workspace_bytes(num_seqs, T_total, max_seqlen, H, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:

@@ -59,6 +59,19 @@ size_t kda_chunked_forward_varlen_workspace_bytes(int num_seqs, int T_total, int
   return kda::chunked_forward_workspace(dt == KDA_F32, d_k, d_v, chunk, max_chunks, H, num_seqs, true);
 }
 
+kda_status kda_chunked_forward_plan(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt,
+                                    int* value_slice, int* segments, int* segment_chunks) {
+  if (B <= 0 || T < 0 || H <= 0 || chunk <= 0 || (dt != KDA_F32 && dt != KDA_BF16)) return KDA_ERR_INVALID_ARG;
+  if (!dim_ok(d_k) || !dim_ok(d_v) || !chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+  if (!kda::chunked_forward_supported(dt == KDA_F32, d_k, d_v, chunk)) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
+  const kda::ChainPlan pl = kda::chain_plan(dt == KDA_F32, (int64_t)B * H, (T + chunk - 1) / chunk, d_v, false);
+  if (value_slice) *value_slice = pl.ws;
+  if (segments) *segments = pl.nseg;
+  if (segment_chunks) *segment_chunks = pl.nseg > 1 ? pl.seg_len : 0;
+  return KDA_OK;
+}
+
 namespace {
 bool workspace_ok(void* ws, size_t have, size_t need) {
   if (need == 0) return true;

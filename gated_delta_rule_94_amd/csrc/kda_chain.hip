@@ -10,6 +10,13 @@
 // workgroup owns a WS-column slice of the state and the slices of one head run on different
 // CUs -- exact, and it spreads even one long sequence over several CUs.
 //
+// Long sequences on few heads are further split into nseg segments of seg_len chunks.  The chain
+// is affine in its initial state: over segment g, S_end = M_g S_start + b_g.  A summary launch runs
+// segments 0..nseg-2 at once, from the zero state on the value columns (giving b_g) and from the
+// identity on d_k extra columns with U~ = 0 (giving M_g); segment_combine_kernel walks the segments
+// of each (sequence, head) in order, S_start(g + 1) = M_g S_start(g) + b_g in fp32; a second launch
+// then runs every segment from its start state, writing o and, from the last segment, hT.
+//
 // Workgroup: WS / 16 chain waves, each owning 16 value columns of the state, and four copy waves.
 // The fp32 state lives in MFMA accumulator registers and is fed back as the B operand of the
 // next chunk's products; U likewise.  The copy waves stream records from HBM into double-buffered
@@ -29,6 +36,9 @@ struct ChainParams {
   const int32_t* cu;      // packed offsets, or NULL
   const int32_t* chunk0;  // first chunk per packed sequence, or NULL
   int units, H, T, nch, dv;
+  int nseg, seg_len;      // segments per (sequence, head) and their length in chunks (1, 0: whole)
+  const float* sstart;    // nseg > 1: start state of every segment [units][nseg][DK][DV]
+  float* send;            // summary launch: [b_g | M_g] of segments 0..nseg-2 [units][nseg-1][DK][DV+DK]
 };
 
 template <bool F32, int DK, int DV, int C, int WS>
@@ -110,7 +120,7 @@ struct CopyPart {
   }
 };
 
-template <bool F32, int DK, int DV, int C, int WS>
+template <bool F32, int DK, int DV, int C, int WS, bool SUM>
 __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainParams p) {
   using Cf = ChainCfg<F32, DK, DV, C, WS>;
   using O = typename Cf::O;
@@ -121,18 +131,26 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
   constexpr int KSD = O::nks(DK), KSC = O::nks(CP);
   __shared__ __align__(16) unsigned char smem[Cf::TOTAL];
 
-  // ---- (unit, slice); the slices of one unit share an XCD (block id mod 8)
-  const int DVr = p.dv;
-  constexpr int nsl_c = DV / WS;
+  // ---- (unit, segment, slice); the slices of one (unit, segment) share an XCD (block id mod 8).
+  // A summary launch has DK more columns (the identity block) and no last segment.
+  constexpr int NCOL = SUM ? DV + DK : DV;
+  constexpr int nsl_c = NCOL / WS;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, idx = bid >> 3;
-  const int unit = (idx / nsl_c) * 8 + xcd;
+  const int segs = SUM ? p.nseg - 1 : p.nseg;
+  const int su = (idx / nsl_c) * 8 + xcd;
   const int slice = idx - (idx / nsl_c) * nsl_c;
-  if (unit >= p.units) return;
+  if (su >= p.units * segs) return;
+  const int unit = su / segs, seg = su - unit * segs;
   const int H = p.H;
   const int n = unit / H, h = unit - n * H;
   int64_t t_begin, t_end, first;
-  if (p.cu) {
+  if (p.nseg > 1) {  // equal-length sequences
+    const int64_t s0 = (int64_t)n * p.T, s1 = s0 + p.T;
+    t_begin = s0 + (int64_t)seg * p.seg_len * C;
+    t_end = t_begin + (int64_t)p.seg_len * C < s1 ? t_begin + (int64_t)p.seg_len * C : s1;
+    first = (int64_t)n * p.nch + (int64_t)seg * p.seg_len;
+  } else if (p.cu) {
     int x = p.cu[n], y = p.cu[n + 1];
     x = x < 0 ? 0 : (x > p.T ? p.T : x);
     y = y < x ? x : (y > p.T ? p.T : y);
@@ -151,7 +169,7 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
   const int gsw = F32 ? grp : (grp ^ ((lo >> 3) & 1));  // fragment piece of this lane in swizzled bf16 tiles
   const bool chain = wave < Cf::NW;
   const int ccol = col0 + 16 * (chain ? wave : 0) + lo;  // value column of this lane
-  const int64_t sbase = (int64_t)unit * DK * DVr;
+  const bool idsl = SUM && col0 >= DV;  // identity-column slice (U~ = 0)
 
   // ---- state S in accumulator layout: Sacc[m][r] = S[16 m + 4 grp + r][ccol]; set and used on the
   // chain waves' path only, so it is not live across the copy waves' loop
@@ -169,16 +187,18 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     CopyPart<Cf::NC, Cf::U_UT, C / EPU, (int)(R::UT * ES_), C * ES_, Cf::B_UT, US * ES_, !F32> ut;  // record pointer + col0 rows
     CopyPart<Cf::NC, Cf::U_GAM, Cf::U_GAM, (int)R::GAM_BYTE, 0, Cf::B_GAM, 0> gam;
     __device__ __forceinline__ void load(const unsigned char* rp, int ht, int col0b) {
-      nw.load(rp, ht); qg.load(rp, ht); pp.load(rp, ht); kpt.load(rp, ht); ut.load(rp + col0b, ht); gam.load(rp, ht);
+      nw.load(rp, ht); kpt.load(rp, ht); ut.load(rp + col0b, ht); gam.load(rp, ht);
+      if constexpr (!SUM) { qg.load(rp, ht); pp.load(rp, ht); }  // a summary writes no o
     }
     __device__ __forceinline__ void store(unsigned char* b, int ht) const {
-      nw.store(b, ht); qg.store(b, ht); pp.store(b, ht); kpt.store(b, ht); ut.store(b, ht); gam.store(b, ht);
+      nw.store(b, ht); kpt.store(b, ht); ut.store(b, ht); gam.store(b, ht);
+      if constexpr (!SUM) { qg.store(b, ht); pp.store(b, ht); }
     }
   };
   const int ht = tid - 64 * Cf::NW;  // copy-thread index (copy waves only)
-  const int ostride = H * DVr;                              // output elements between consecutive tokens
+  const int ostride = H * DV;                               // output elements between consecutive tokens
   const int ocol = col0 + 16 * (chain ? wave : 0) + 4 * grp;  // first of this lane's 4 output columns
-  const int col0b = col0 * C * ES_;  // first U~^T row of the slice
+  const int col0b = (idsl ? 0 : col0) * C * ES_;  // first U~^T row of the slice
 
   // one chunk of the chain from LDS buffer `buf`
   auto chunk_step = [&](int c, int buf) {
@@ -191,7 +211,7 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     const float* Gam = reinterpret_cast<const float*>(b + Cf::B_GAM);
     const int64_t t0 = t_begin + (int64_t)c * C;
     const int len = (int)((t_end - t0) < C ? (t_end - t0) : C);
-    const int64_t obase = (t0 * H + h) * DVr;  // output element of (token t0, head h, column 0): uniform
+    const int64_t obase = (t0 * H + h) * DV;  // output element of (token t0, head h, column 0): uniform
     if (!chain) return;
     // Phases, each issuing the LDS fragment loads of the next so that LDS latency hides behind
     // MFMAs; the state update (the chunk-to-chunk critical path) comes first:
@@ -212,7 +232,9 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     const E* ut = Ut + (16 * wave + lo) * US + 4 * gsw;  // U~^T: this lane's 4 tokens are contiguous
 #pragma unroll
     for (int bt = 0; bt < NT; ++bt) {
-      if constexpr (F32) {
+      if (idsl) {
+        U[bt] = zero4();
+      } else if constexpr (F32) {
         const float4 x = *reinterpret_cast<const float4*>(ut + 16 * bt);
         U[bt] = f32x4{x.x, x.y, x.z, x.w};
       } else {
@@ -254,6 +276,7 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
 #pragma unroll
       for (int sk = 0; sk < KSC; ++sk) Sacc[m] = O::mma(kf[m][sk], uf[sk], Sacc[m]);
     }
+    if constexpr (SUM) return;
 #pragma unroll
     for (int sk = 0; sk < KSD; ++sk)
 #pragma unroll
@@ -297,10 +320,19 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
   // free; the copy waves fill buffer (c+1)&1 while the chain waves read buffer c&1.
   const int last = nchunks - 1;
   if (chain) {
+    if constexpr (SUM) {  // zero on the value columns, the identity on the extra ones
 #pragma unroll
-    for (int m = 0; m < DK / 16; ++m)
+      for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Sacc[m][r] = p.h0 ? p.h0[sbase + (int64_t)(16 * m + 4 * grp + r) * DVr + ccol] : 0.f;
+        for (int r = 0; r < 4; ++r) Sacc[m][r] = (idsl && 16 * m + 4 * grp + r == ccol - DV) ? 1.f : 0.f;
+    } else {
+      const float* s0 = p.nseg > 1 ? p.sstart + ((int64_t)unit * p.nseg + seg) * DK * DV
+                                   : (p.h0 ? p.h0 + (int64_t)unit * DK * DV : nullptr);
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Sacc[m][r] = s0 ? s0[(16 * m + 4 * grp + r) * DV + ccol] : 0.f;
+    }
     __syncthreads();
     for (int c = 0; c < nchunks; c += 2) {
       chunk_step(c, 0);
@@ -309,11 +341,18 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
       chunk_step(c + 1, 1);
       __syncthreads();
     }
-    if (p.hT) {
+    if constexpr (SUM) {
+      float* se = p.send + ((int64_t)unit * (p.nseg - 1) + seg) * DK * (DV + DK);
 #pragma unroll
       for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p.hT[sbase + (int64_t)(16 * m + 4 * grp + r) * DVr + ccol] = Sacc[m][r];
+        for (int r = 0; r < 4; ++r) se[(16 * m + 4 * grp + r) * (DV + DK) + ccol] = Sacc[m][r];
+    } else if (p.hT && seg == p.nseg - 1) {
+      float* ht_ = p.hT + (int64_t)unit * DK * DV;
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ht_[(16 * m + 4 * grp + r) * DV + ccol] = Sacc[m][r];
     }
   } else {
     Stage s0, s1;
@@ -336,34 +375,122 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
 
 }
 
-template <bool F32, int DK, int DV, int C, int WS>
+template <bool F32, int DK, int DV, int C, int WS, bool SUM>
 static hipError_t launch_chain_impl(const ChainLaunch& L) {
   ChainParams p;
   p.ws = L.records; p.h0 = L.h0; p.o = L.o; p.hT = L.hT; p.cu = L.cu; p.chunk0 = L.chunk0;
   p.units = L.units; p.H = L.H; p.T = L.T; p.nch = L.nch; p.dv = DV;
-  const int grid = ((L.units + 7) / 8) * 8 * (DV / WS);
-  hipLaunchKernelGGL((chain_kernel<F32, DK, DV, C, WS>), dim3(grid), dim3(ChainCfg<F32, DK, DV, C, WS>::NTH), 0,
-                     (hipStream_t)L.stream, p);
+  p.nseg = L.nseg > 1 ? L.nseg : 1; p.seg_len = L.seg_len; p.sstart = L.sstart; p.send = L.send;
+  const int64_t su = (int64_t)L.units * (SUM ? p.nseg - 1 : p.nseg);
+  const int64_t grid = ((su + 7) / 8) * 8 * ((SUM ? DV + DK : DV) / WS);
+  if (su <= 0 || grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((chain_kernel<F32, DK, DV, C, WS, SUM>), dim3((unsigned)grid),
+                     dim3(ChainCfg<F32, DK, DV, C, WS>::NTH), 0, (hipStream_t)L.stream, p);
   return hipGetLastError();
 }
 
 // Slice width: bf16 picks 32 or 16 value columns per workgroup (16 -- more workgroups -- when there
-// are few (sequence, head) units); fp32 uses 16.
+// are few (sequence, head) units); fp32 uses 16.  Segment summaries use 32 (bf16) and 16 (fp32).
 #define KDA_CHAIN_BF16(X, D, V, CC) X(false, D, V, CC, 32) X(false, D, V, CC, 16)
 #define KDA_CHAIN_INSTANCES(X)                                                                                   \
   KDA_CHAIN_BF16(X, 64, 64, 16) KDA_CHAIN_BF16(X, 64, 64, 32) KDA_CHAIN_BF16(X, 64, 64, 64)                        \
   KDA_CHAIN_BF16(X, 64, 128, 16) KDA_CHAIN_BF16(X, 64, 128, 32) KDA_CHAIN_BF16(X, 64, 128, 64)                     \
   KDA_CHAIN_BF16(X, 128, 64, 16) KDA_CHAIN_BF16(X, 128, 64, 32) KDA_CHAIN_BF16(X, 128, 64, 64)                     \
   KDA_CHAIN_BF16(X, 128, 128, 16) KDA_CHAIN_BF16(X, 128, 128, 32) KDA_CHAIN_BF16(X, 128, 128, 64)                  \
+  KDA_CHAIN_F32(X)
+#define KDA_CHAIN_F32(X)                                                                                         \
   X(true, 64, 64, 16, 16) X(true, 64, 64, 32, 16) X(true, 64, 64, 64, 16)                                         \
   X(true, 64, 128, 16, 16) X(true, 64, 128, 32, 16) X(true, 64, 128, 64, 16)                                      \
   X(true, 128, 64, 16, 16) X(true, 128, 64, 32, 16) X(true, 128, 128, 16, 16) X(true, 128, 128, 32, 16)
+#define KDA_CHAIN_SUMMARY_INSTANCES(X)                                                                           \
+  X(false, 64, 64, 16, 32) X(false, 64, 64, 32, 32) X(false, 64, 64, 64, 32)                                      \
+  X(false, 64, 128, 16, 32) X(false, 64, 128, 32, 32) X(false, 64, 128, 64, 32)                                   \
+  X(false, 128, 64, 16, 32) X(false, 128, 64, 32, 32) X(false, 128, 64, 64, 32)                                   \
+  X(false, 128, 128, 16, 32) X(false, 128, 128, 32, 32) X(false, 128, 128, 64, 32)                                \
+  KDA_CHAIN_F32(X)
 
 hipError_t launch_chain(const ChainLaunch& L) {
+  if (L.summary) {
+#define KDA_LAUNCH(F, D, V, CC, W)                                                       \
+  if (L.f32 == F && L.dk == D && L.dv == V && L.chunk == CC && L.ws == W && L.nseg > 1) \
+    return launch_chain_impl<F, D, V, CC, W, true>(L);
+    KDA_CHAIN_SUMMARY_INSTANCES(KDA_LAUNCH)
+#undef KDA_LAUNCH
+    return hipErrorInvalidValue;
+  }
 #define KDA_LAUNCH(F, D, V, CC, W) \
-  if (L.f32 == F && L.dk == D && L.dv == V && L.chunk == CC && L.ws == W) return launch_chain_impl<F, D, V, CC, W>(L);
+  if (L.f32 == F && L.dk == D && L.dv == V && L.chunk == CC && L.ws == W) return launch_chain_impl<F, D, V, CC, W, false>(L);
   KDA_CHAIN_INSTANCES(KDA_LAUNCH)
 #undef KDA_LAUNCH
+  return hipErrorInvalidValue;
+}
+
+// Start states of the segments of one (sequence, head), 32 value columns per workgroup, in fp32:
+// S(0) = h0 (or 0), S(g + 1) = M_g S(g) + b_g, with [b_g | M_g] read from the summary launch's
+// output.  M_g and S(g) are staged in LDS; thread (c, rq) owns column c and rows rq + 8 i.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void segment_combine_kernel(const float* __restrict__ h0,
+                                                              const float* __restrict__ send,
+                                                              float* __restrict__ sstart, int units, int nseg) {
+  constexpr int CW = 32, MS = DK + 4, RPT = DK / 8, NSL = DV / CW, SE = DV + DK;
+  __shared__ __align__(16) float Ms[DK * MS];
+  __shared__ float Ss[DK * CW];
+  const int unit = blockIdx.x / NSL, col0 = (blockIdx.x % NSL) * CW;
+  if (unit >= units) return;
+  const int tid = threadIdx.x, c = tid & (CW - 1), rq = tid >> 5;
+  const float* hu = h0 ? h0 + (int64_t)unit * DK * DV : nullptr;
+  float* st = sstart + (int64_t)unit * nseg * DK * DV;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rq + 8 * i;
+    const float x = hu ? hu[r * DV + col0 + c] : 0.f;
+    st[r * DV + col0 + c] = x;
+    Ss[r * CW + c] = x;
+  }
+  for (int g = 0; g + 1 < nseg; ++g) {
+    const float* se = send + ((int64_t)unit * (nseg - 1) + g) * DK * SE;
+    for (int e = tid; e < DK * DK / 4; e += 256) {
+      const int r = e / (DK / 4), j4 = e - r * (DK / 4);
+      *reinterpret_cast<float4*>(Ms + r * MS + 4 * j4) = *reinterpret_cast<const float4*>(se + r * SE + DV + 4 * j4);
+    }
+    float acc[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) acc[i] = se[(rq + 8 * i) * SE + col0 + c];
+    __syncthreads();
+    for (int j = 0; j < DK; j += 4) {
+      const float s0 = Ss[j * CW + c], s1 = Ss[(j + 1) * CW + c], s2 = Ss[(j + 2) * CW + c], s3 = Ss[(j + 3) * CW + c];
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const float4 m = *reinterpret_cast<const float4*>(Ms + (rq + 8 * i) * MS + j);
+        acc[i] = fmaf(m.x, s0, acc[i]);
+        acc[i] = fmaf(m.y, s1, acc[i]);
+        acc[i] = fmaf(m.z, s2, acc[i]);
+        acc[i] = fmaf(m.w, s3, acc[i]);
+      }
+    }
+    __syncthreads();  // every read of S(g) and M_g is done
+    float* sn = st + (int64_t)(g + 1) * DK * DV;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rq + 8 * i;
+      Ss[r * CW + c] = acc[i];
+      sn[r * DV + col0 + c] = acc[i];
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_segment_combine(const float* h0, const float* send, float* sstart, int units, int nseg, int dk,
+                                  int dv, void* stream) {
+  if (units <= 0 || nseg < 2) return hipErrorInvalidValue;
+#define KDA_COMB(D, V)                                                                                      \
+  if (dk == D && dv == V) {                                                                                 \
+    hipLaunchKernelGGL((segment_combine_kernel<D, V>), dim3(units * (V / 32)), dim3(256), 0, (hipStream_t)stream, \
+                       h0, send, sstart, units, nseg);                                                      \
+    return hipGetLastError();                                                                               \
+  }
+  KDA_COMB(64, 64) KDA_COMB(64, 128) KDA_COMB(128, 64) KDA_COMB(128, 128)
+#undef KDA_COMB
   return hipErrorInvalidValue;
 }
 

@@ -56,8 +56,28 @@ struct ChainLaunch {
   int units, H, T, nch;
   int dk, dv, chunk, ws;
   bool f32;
+  // segments (equal-length sequences only): nseg > 1 splits every (sequence, head) into segments of
+  // seg_len chunks.  summary: run segments 0..nseg-2 from the zero state on the value columns and
+  // from the identity on d_k extra columns, writing [b_g | M_g] to send; otherwise segment g starts
+  // from sstart[unit][g] (all segments, the first included) and writes o, and the last writes hT.
+  int nseg = 1, seg_len = 0;
+  bool summary = false;
+  const float* sstart = nullptr;  // [units][nseg][dk][dv]
+  float* send = nullptr;          // [units][nseg - 1][dk][dv + dk]
   void* stream;
 };
+
+// How the chain is laid out over the GPU: value-slice width, and the segment split of long
+// sequences whose (sequence, head, slice) count alone would leave compute units idle.
+struct ChainPlan {
+  int ws, nseg, seg_len;
+};
+ChainPlan chain_plan(bool f32, int64_t units, int nch, int dv, bool varlen);
+
+// Segment start states: sstart[u][0] = h0 (or 0), sstart[u][g + 1] = M_g sstart[u][g] + b_g
+// (kda_chain.hip)
+hipError_t launch_segment_combine(const float* h0, const float* send, float* sstart, int units, int nseg, int dk,
+                                  int dv, void* stream);
 
 hipError_t launch_decode_step(const DecodeArgs& a);
 hipError_t launch_intra(const IntraLaunch& L);

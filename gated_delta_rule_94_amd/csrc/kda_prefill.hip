@@ -4,10 +4,14 @@
 //                          offsets -- no host synchronisation
 //   2. intra_chunk_kernel  gate cumulative sum + UT/WY transform of every (chunk, head), in parallel,
 //                          into per-chunk records in the workspace
-//   3. chain_kernel        the sequential state chain per (sequence, head, value slice)
+//   3. chain_kernel        the sequential state chain per (sequence, head, value slice); for long
+//                          sequences on few heads, per segment: a summary launch, the segment
+//                          start states (segment_combine_kernel), then the chain of every segment
 //
-// Workspace: [records: max_chunks * H * record bytes][chunk0: (num_seqs + 1) int32, packed only],
-// where max_chunks bounds the number of chunks: B * ceil(T / C) for equal-length sequences,
+// Workspace: [records: max_chunks * H * record bytes][chunk0: (num_seqs + 1) int32, packed only]
+// [segment start states: units * nseg * d_k * d_v fp32][segment summaries: units * (nseg - 1) *
+// d_k * (d_v + d_k) fp32], the last two only when the plan splits sequences into nseg > 1
+// segments.  max_chunks bounds the number of chunks: B * ceil(T / C) for equal-length sequences,
 // floor(T_total / C) + num_seqs for packed ones (each sequence adds at most one partial chunk).
 #include "kda_internal.h"
 #include "kda_record.h"
@@ -20,12 +24,47 @@ static int64_t max_chunks_of(int T, int chunk, int num_seqs, bool varlen) {
   return varlen ? (int64_t)T / chunk + num_seqs : (int64_t)num_seqs * ((T + chunk - 1) / chunk);
 }
 
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int compute_units();
+
+// Segments: at least kMinSegChunks chunks each, at most kMaxSeg per (sequence, head).
+static constexpr int kMinSegChunks = 32, kMaxSeg = 64;
+
+ChainPlan chain_plan(bool f32, int64_t units, int nch, int dv, bool varlen) {
+  const int cus = compute_units();
+  ChainPlan pl{16, 1, 0};
+  if (!f32 && units * (dv / 32) >= cus) pl.ws = 32;
+  // Long sequences on few heads: (sequence, head, slice) alone leave CUs idle, so split every
+  // sequence into segments.  That triples the chain's work (summaries over twice the columns, then
+  // the chain itself) but runs it on nseg times more workgroups.
+  const int wss = f32 ? 16 : 32;
+  const int64_t per = units * (dv / wss);
+  if (!varlen && per < cus && nch >= 2 * kMinSegChunks) {
+    int64_t nseg = (cus + per - 1) / per;
+    if (nseg > nch / kMinSegChunks) nseg = nch / kMinSegChunks;
+    if (nseg > kMaxSeg) nseg = kMaxSeg;
+    if (nseg >= 2) {
+      pl.ws = wss;
+      pl.seg_len = (int)((nch + nseg - 1) / nseg);
+      pl.nseg = (nch + pl.seg_len - 1) / pl.seg_len;
+    }
+  }
+  return pl;
+}
+
 size_t chunked_forward_workspace(bool f32, int dk, int dv, int chunk, int64_t max_chunks, int H, int num_seqs,
                                  bool varlen) {
   const int64_t rb = record_bytes(f32, dk, dv, chunk);
   if (rb == 0) return 0;
   size_t bytes = (size_t)(max_chunks * H * rb);
-  if (varlen) bytes += ((size_t)(num_seqs + 1) * 4 + 255) & ~(size_t)255;
+  if (varlen) bytes += al256((size_t)(num_seqs + 1) * 4);
+  const int nch = (!varlen && num_seqs > 0) ? (int)(max_chunks / num_seqs) : 0;
+  const ChainPlan pl = chain_plan(f32, (int64_t)num_seqs * H, nch, dv, varlen);
+  if (pl.nseg > 1) {
+    const size_t units = (size_t)num_seqs * H;
+    bytes += al256(units * pl.nseg * dk * dv * 4) + al256(units * (pl.nseg - 1) * dk * (dv + dk) * 4);
+  }
   return bytes;
 }
 
@@ -57,7 +96,6 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
     e = launch_chunk_map(a.cu_seqlens, a.num_seqs, a.T, C, chunk0, a.stream);
     if (e != hipSuccess) return e;
   }
-  const int cus = compute_units();
   const int64_t items = max_chunks * a.H;
   if (items > INT32_MAX) return hipErrorInvalidValue;
   if (items > 0) {
@@ -76,11 +114,19 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
   K.records = records; K.h0 = a.h0; K.o = a.o; K.hT = a.hT; K.cu = a.cu_seqlens; K.chunk0 = chunk0;
   K.units = a.num_seqs * a.H; K.H = a.H; K.T = a.T; K.nch = nch;
   K.dk = a.dk; K.dv = a.dv; K.chunk = C; K.f32 = a.f32;
-  // value-slice width: 32 columns when that still gives every CU a workgroup, else 16 (fp32: 16)
-  int ws = 16;
-  if (!a.f32 && (int64_t)K.units * (a.dv / 32) >= cus) ws = 32;
-  K.ws = ws;
+  const ChainPlan pl = chain_plan(a.f32, K.units, nch, a.dv, varlen);
+  K.ws = pl.ws;
   K.stream = a.stream;
+  if (pl.nseg > 1) {
+    unsigned char* seg = records + max_chunks * a.H * rb;
+    float* sstart = reinterpret_cast<float*>(seg);
+    float* send = reinterpret_cast<float*>(seg + al256((size_t)K.units * pl.nseg * a.dk * a.dv * 4));
+    K.nseg = pl.nseg; K.seg_len = pl.seg_len; K.sstart = sstart; K.send = send;
+    K.summary = true;
+    if ((e = launch_chain(K)) != hipSuccess) return e;
+    if ((e = launch_segment_combine(a.h0, send, sstart, K.units, pl.nseg, a.dk, a.dv, a.stream)) != hipSuccess) return e;
+    K.summary = false;
+  }
   if ((e = launch_chain(K)) != hipSuccess) return e;
   if (a.events) e = hipEventRecord(a.events[2], (hipStream_t)a.stream);
   return e;

@@ -75,6 +75,20 @@ int kda_version(void);
 size_t kda_chunked_forward_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt);
 
 /*
+ * How kda_chunked_forward lays out its state chain on the current device for
+ * this shape: *value_slice = value columns of the state per workgroup (16 or
+ * 32); *segments = the number of segments every sequence is split into (1 =
+ * none: the chain runs over whole sequences); *segment_chunks = chunks per
+ * segment (0 when *segments is 1).  Sequences are split only when (sequence,
+ * head, value slice) alone would leave compute units idle; the split costs a
+ * summary pass and a combine but runs the chain on more workgroups.  Any
+ * output pointer may be NULL.  The workspace size query accounts for the
+ * plan, so query, plan and call must use the same device.
+ */
+kda_status kda_chunked_forward_plan(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt,
+                                    int* value_slice, int* segments, int* segment_chunks);
+
+/*
  * Chunked prefill over B sequences of T tokens each.
  *   q, k, g [B,T,H,d_k], v [B,T,H,d_v], beta [B,T,H]   (dtype dt)   in
  *   h0 [B,H,d_k,d_v] fp32                               in, or NULL for a zero initial state
@@ -92,10 +106,11 @@ kda_status kda_chunked_forward(const void* q, const void* k, const void* v, cons
 /*
  * Profiling form of kda_chunked_forward: the same arguments, checks and
  * results, plus kernel_ms[2] (host memory, non-NULL), which receives the
- * durations in milliseconds of the two kernels of the call -- [0] the
+ * durations in milliseconds of the two stages of the call -- [0] the
  * intra-chunk kernel (gate cumulative sums, the UT/WY transform and the
  * chunk-local products; architecture blog, "Kimi Delta Attention: the linear
- * core"), [1] the chain kernel (the sequential state recurrence) -- measured
+ * core"), [1] the state chain (the sequential recurrence: one chain kernel, or
+ * for a segmented plan the summary pass, the combine and the chain) -- measured
  * with HIP events recorded on hip_stream around each.  It creates and destroys
  * its events and synchronises with the stream before returning, so it is for
  * measurement, not for a launch loop.  kernel_ms is zeroed when nothing runs.

@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
@@ -49,6 +50,30 @@ def test_workspace_queries():
     assert n == ((1 << 20) // 64 + 16) * 8 * rec + 256
     assert lib.kda_chunked_forward_workspace_bytes(0, 10, 2, 64, 64, 64, 1) == 0
     assert lib.kda_chunked_forward_workspace_bytes(1, 10, 2, 64, 64, 48, 1) == 0  # unsupported chunk
+
+
+def test_chain_plan_and_segment_workspace():
+    """The chain layout for 256 compute units (the count assumed without a device, and MI355X's):
+    whole sequences when (sequence, head, 32-column slice) fill the CUs; otherwise every sequence
+    split into segments of at least 32 chunks, and the workspace grows by the segment start states
+    and summaries."""
+    f32 = torch.float32
+    assert kda.chain_plan(4, 4096, 16, 128, 128) == (32, 1, 0)          # 256 workgroups already
+    assert kda.chain_plan(1, 2048, 8, 128, 128) == (16, 1, 0)           # 32 chunks: too short to split
+    assert kda.chain_plan(1, 4096, 8, 128, 128) == (32, 2, 32)
+    assert kda.chain_plan(1, 65536, 32, 128, 128) == (32, 2, 512)
+    assert kda.chain_plan(1, 1 << 20, 8, 128, 128) == (32, 8, 2048)     # 8 heads x 8 segments x 4 slices
+    assert kda.chain_plan(1, 8229, 2, 128, 128) == (32, 4, 33)          # ragged: 129 chunks, last segment 30
+    assert kda.chain_plan(1, 6400, 1, 64, 64, dtype=f32) == (16, 3, 34)
+    with pytest.raises(kda.KDAError):
+        kda.chain_plan(1, 6400, 1, 128, 128, dtype=f32)                 # fp32 at d_k 128 has no 64-token chunk
+    lib = kda.lib()
+    rec = 2 * (3 * 64 * 128 + 64 * 64 + 64 * 128) + 4 * 128
+    rec = (rec + 255) // 256 * 256
+    al = lambda x: (x + 255) // 256 * 256
+    units, nseg = 8, 8
+    want = 16384 * 8 * rec + al(units * nseg * 128 * 128 * 4) + al(units * (nseg - 1) * 128 * 256 * 4)
+    assert lib.kda_chunked_forward_workspace_bytes(1, 1 << 20, 8, 128, 128, 64, 1) == want
 
 
 FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced because validation fails first

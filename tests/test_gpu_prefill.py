@@ -125,6 +125,35 @@ def test_continuation_two_halves():
     assert state_err(host64(h2), h_ref) < TOL[BF16]
 
 
+@pytest.mark.parametrize("dt,B,T,H,dk,dv,h0", [
+    (BF16, 1, 8229, 2, 128, 128, True),   # 129 chunks: 4 segments, the last one shorter
+    (BF16, 2, 4113, 2, 128, 128, True),   # two sequences, 2 segments each, ragged tail
+    (BF16, 1, 4480, 1, 128, 64, True),    # the identity block is wider than the value columns
+    (BF16, 1, 4480, 1, 64, 128, False),
+    (F32, 1, 6400, 1, 64, 64, True),
+])
+def test_segmented_chain_against_oracle(dt, B, T, H, dk, dv, h0):
+    """Long sequences on few heads run the chain per segment (summaries, start states, chain):
+    o and hT still match the oracle element by element."""
+    plan = kda.chain_plan(B, T, H, dk, dv, 64, dtype=torch.float32 if dt == F32 else torch.bfloat16)
+    assert plan[1] > 1, plan
+    d = datagen.prefill_inputs(500 + T + dk, B, T, H, dk, dv, dt, 0.02 if h0 else None)
+    check(d, 64, dt, "segmented plan %s" % (plan,))
+
+
+def test_segmented_hT_aliases_h0():
+    """In a segmented call h0 is read (by the start-state combine) before any segment writes hT."""
+    assert kda.chain_plan(1, 4096, 8, 128, 128)[1] > 1
+    d = datagen.prefill_inputs(47, 1, 4096, 8, 128, 128, BF16, 0.02)
+    g = {key: dev_tensor(d[key]) for key in KEYS}
+    state = dev_tensor(d["h0"])
+    o, hT = kda.kda_chunked_forward(g["q"], g["k"], g["v"], g["g"], g["beta"], state, hT=state)
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"])
+    assert o_err(host64(o), o_ref) < TOL[BF16]
+    assert state_err(host64(state), h_ref) < TOL[BF16]
+
+
 def varlen_case(lens, H, dk, dv, dt, seed, h0=True):
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     Tt = int(cu[-1])
