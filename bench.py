@@ -25,8 +25,13 @@ The JSON line carries:
   roofline_call_hbm -- the whole call's algorithmic bytes (inputs, o, h0, hT)
   decode         -- 1000 sequential kda_decode_step calls on the 256-sequence x
                     32-head state (512 MiB fp32), bytes and fraction of HBM
-  cpu_baseline   -- the fp64 oracle on this host's cores over one of the four
-                    sequences of the same workload (a baseline, not a target)
+  workloads      -- the other seeded prefill workloads (fp32 2 x 256 tokens, 32
+                    heads x 65,536 tokens, one 1,048,576-token sequence x 8 heads,
+                    16 packed sequences), each timed over a few calls with the
+                    cache evicted before each: tokens/s, the chain's layout (value
+                    slice, segments) and the two stages' durations
+  cpu_baseline   -- the fp64 oracle on this host's cores, whole passes over the
+                    same workload for at least 10 s (a baseline, not a target)
 Algorithmic work per token and head (d_k = d_v = d, chunk C):
   flops 6 d^2 + (C-1) d + 2 (C+1) d + 2 (C+1) d + C^2/3 ; bytes (3 d_k + d_v) s_in + s_beta + d_v s_out,
   plus 2 * 4 d_k d_v per (sequence, head) for h0 and hT.
@@ -131,6 +136,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--no-flush", action="store_true", help="do not evict the Infinity Cache between steps")
     ap.add_argument("--copy-calibration", action="store_true", help="run one 1 GiB copy (counter scaling) and exit")
     args = ap.parse_args()
@@ -263,18 +269,78 @@ def main():
         }
         del state, pool
 
+    # ---------------- the other prefill workloads: tokens/s on one GPU
+    if not args.no_workloads:
+        out["workloads"] = {}
+        for name, reps in (("cfg0_f32_b1_h2_t256_d64", 20), ("cfg2_bf16_b1_h32_t65536_d128", 5),
+                           ("cfg4_bf16_b1_h8_t1048576_d128", 3), ("cfg4v_varlen_n16_h8_d128", 3)):
+            wl = datagen.WORKLOADS[name]
+            tdt = torch.float32 if wl.dtype == datagen.DT_F32 else torch.bfloat16
+            if wl.kind == "varlen":
+                lens = datagen.varlen_lengths(wl.seed, wl.num_seqs, wl.len_lo, wl.len_hi)
+                cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+                dl = datagen.prefill_inputs(wl.seed, 1, int(cu[-1]), wl.H, wl.dk, wl.dv, wl.dtype, None)
+            else:
+                dl = datagen.prefill_inputs(wl.seed, wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.dtype, wl.h0_std)
+            gl = {key: to_dev(val) for key, val in dl.items()}
+            del dl
+            ol = torch.empty(gl["v"].shape, dtype=tdt, device=dev)
+            entry = {}
+            if wl.kind == "varlen":
+                cud = to_dev(cu)
+                n_tok = int(cu[-1])
+                hTl = torch.empty((wl.num_seqs, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+                wsl = torch.empty(kda.varlen_workspace_bytes(wl.num_seqs, n_tok, int(max(lens)), wl.H, wl.dk, wl.dv,
+                                                             wl.chunk, tdt), dtype=torch.uint8, device=dev)
+
+                def lstep(_i):
+                    kda.kda_chunked_forward_varlen(gl["q"], gl["k"], gl["v"], gl["g"], gl["beta"], cud,
+                                                   int(max(lens)), None, chunk=wl.chunk, o=ol, hT=hTl, workspace=wsl)
+                entry["sequences"] = int(wl.num_seqs)
+            else:
+                n_tok = wl.B * wl.T
+                hTl = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+                wsl = torch.empty(kda.workspace_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.chunk, tdt),
+                                  dtype=torch.uint8, device=dev)
+
+                def lstep(_i):
+                    kda.kda_chunked_forward(gl["q"], gl["k"], gl["v"], gl["g"], gl["beta"], gl["h0"], chunk=wl.chunk,
+                                            o=ol, hT=hTl, workspace=wsl)
+                vs, nseg, segc = kda.chain_plan(wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.chunk, tdt)
+                entry["chain_plan"] = {"value_slice": vs, "segments": nseg, "segment_chunks": segc}
+            lstep(0)
+            torch.cuda.synchronize()
+            lms, _ = time_launches(lstep, reps, None if args.no_flush else flush)
+            entry.update({"ms_per_call": lms, "tokens_per_s": n_tok / (lms * 1e-3),
+                          "token_heads_per_s": n_tok * wl.H / (lms * 1e-3), "calls": reps,
+                          "dtype": "f32" if tdt == torch.float32 else "bf16"})
+            if wl.kind != "varlen":
+                if not args.no_flush:
+                    flush()
+                a_ms, b_ms = kda.kda_chunked_forward_profiled(gl["q"], gl["k"], gl["v"], gl["g"], gl["beta"], gl["h0"],
+                                                              ol, hTl, chunk=wl.chunk, workspace=wsl)
+                entry.update({"intra_ms": a_ms, "chain_ms": b_ms})
+            out["workloads"][name] = entry
+            print("workload %s: %.3f ms" % (name, lms), file=sys.stderr, flush=True)
+            del gl, ol, hTl, wsl
+            torch.cuda.empty_cache()
+
     # ---------------- CPU baseline: the fp64 oracle on this host's cores, one sequence of the workload
     if not args.no_cpu_baseline:
         import oracle
 
         threads = max(1, min(16, os.cpu_count() or 1))
-        one = {key: (val[:1] if val is not None else None) for key, val in d.items()}
-        t0 = time.perf_counter()
-        oracle.forward(one["q"], one["k"], one["v"], one["g"], one["beta"], one["h0"], nthreads=threads)
-        secs = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": w.T / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                               "sample": "sequence 0 of the prefill workload (%d tokens x %d heads, fp64, token by "
-                                         "token), %.1f s wall on %d threads" % (w.T, w.H, secs, threads)}
+        passes, t0 = 0, time.perf_counter()
+        while True:  # whole passes over the workload, for at least 10 s
+            oracle.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], nthreads=threads)
+            passes += 1
+            secs = time.perf_counter() - t0
+            if secs >= 10.0:
+                break
+        out["cpu_baseline"] = {"value": passes * tokens / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": "%d passes over the whole prefill workload (%d x %d tokens x %d heads, fp64, "
+                                         "token by token), %.1f s wall on %d threads"
+                                         % (passes, w.B, w.T, w.H, secs, threads)}
 
     print(json.dumps(out))
 
