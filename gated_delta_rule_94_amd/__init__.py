@@ -10,7 +10,7 @@ entry points' names:
 * ``kda_decode_step``            -- one token per sequence, state updated in place
 
 Importing this package fails loudly when ``libkda.so`` has not been built
-(``python gated_delta_rule_94_amd/build.py`` or ``__graft_entry__.build()``).
+(``python gated_delta_rule_94_amd/build.py``).
 """
 from __future__ import annotations
 
