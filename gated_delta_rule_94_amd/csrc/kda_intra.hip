@@ -269,13 +269,14 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   E* rec = reinterpret_cast<E*>(p.ws + (int64_t)item * R::BYTES);
   float* rgam = reinterpret_cast<float*>(p.ws + (int64_t)item * R::BYTES + R::GAM_BYTE);
 
-  // ---------------- prep: E = e^{G_r - R_b} (prefix products of e^g inside the 16-row sub-tile,
-  // R_b = G before it) for this thread's rows and channels; Tb = the sub-tile's total decay.
-  // Then e^{R_b - G_r} = 1 / E and the suffix product e^{G_end - G_r} = Tb / E.
-  float Ef[NQ][2][2], Tb[NQ][2];  // [quarter][row j][channel]
+  // ---------------- per quarter of the key dimension, pipelined so that the later quarters' loads
+  // arrive while the earlier ones compute:
+  //   scan(0) | sync | for qt: QG/K'/KG(qt) + operands(qt) | sync | scan(qt+1) + products(qt) | sync
+  // scan: E = e^{G_r - R_b} (prefix products of e^g inside the 16-row sub-tile, R_b = G before it)
+  // for this thread's rows and channels, Tb = the sub-tile's total decay (to LDS as Eend); then
+  // e^{R_b - G_r} = 1 / E and the suffix product e^{G_end - G_r} = Tb / E.
   const float m1 = rp >= 1 ? 1.f : 0.f, m2 = rp >= 2 ? 1.f : 0.f, m4 = rp >= 4 ? 1.f : 0.f;
-#pragma unroll
-  for (int qt = 0; qt < NQ; ++qt) {
+  auto scan = [&](int qt, float (&Ef)[2][2], float (&Tb)[2]) {
     const float2 g0 = rg[qt][0].f(), g1 = rg[qt][1].f();
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
@@ -284,47 +285,44 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
       x *= row_shr_or1<1>(x, m1);
       x *= row_shr_or1<2>(x, m2);
       x *= row_shr_or1<4>(x, m4);
-      Ef[qt][0][ch] = row_shr_or1<1>(x, m1) * a0;
-      Ef[qt][1][ch] = x;
-      Tb[qt][ch] = __shfl(x, (tid & 63) | 7);  // row pair 7 of this sub-tile
+      Ef[0][ch] = row_shr_or1<1>(x, m1) * a0;
+      Ef[1][ch] = x;
+      Tb[ch] = __shfl(x, (tid & 63) | 7);  // row pair 7 of this sub-tile
     }
-    if (pact && rp == 7) *reinterpret_cast<float2*>(Eend + psb * DK + QW * qt + 2 * cpl) = make_float2(Tb[qt][0], Tb[qt][1]);
+    if (pact && rp == 7) *reinterpret_cast<float2*>(Eend + psb * DK + QW * qt + 2 * cpl) = make_float2(Tb[0], Tb[1]);
+  };
+  float Ef[2][2], Tb[2];  // this quarter's: [row j][channel]
+  scan(0, Ef, Tb);
+  if constexpr (CP > C) {  // token pads of K'^T and (K . Gamma)^T are zero
+    for (int e = tid; e < DK * (CP - C); e += 512) {
+      const int c = e / (CP - C), t = C + e % (CP - C);
+      rec[R::KPT + c * CP + t] = (E)0.f;
+      KGt[c * TS + t] = (E)0.f;
+    }
   }
-  if (tid < C) Bet[tid] = rb;
-  if (vact) {  // V^T for the U~ product
-    float x0[8], x1[8];
+  f32x4 acc[NSLOT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float2 vv = rv[i].f();
-      x0[i] = vv.x;
-      x1[i] = vv.y;
-    }
-    st8_a8<F32>(Vt + (2 * vcp) * TS + 8 * vtg, x0);
-    st8_a8<F32>(Vt + (2 * vcp + 1) * TS + 8 * vtg, x1);
-  }
+  for (int sl = 0; sl < NSLOT; ++sl) acc[sl] = zero4();
   __syncthreads();
 
-  // q, k as fp32 and 1 / E, kept for the quarter builds
-  float qf[NQ][2][2], kf[NQ][2][2], iE[NQ][2][2];
 #pragma unroll
-  for (int qt = 0; qt < NQ; ++qt)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float2 qq = rq[qt][j].f(), kk = rk[qt][j].f();
-      qf[qt][j][0] = qq.x;
-      qf[qt][j][1] = qq.y;
-      kf[qt][j][0] = kk.x;
-      kf[qt][j][1] = kk.y;
-      iE[qt][j][0] = __builtin_amdgcn_rcpf(Ef[qt][j][0]);
-      iE[qt][j][1] = __builtin_amdgcn_rcpf(Ef[qt][j][1]);
-    }
-
-  // ---------------- Q.Gamma and K'^T to the record, (K.Gamma)^T to LDS: the prefix decay eP of the
-  // earlier sub-tiles and the suffix decay eS of the later ones (the sub-tile is wave-uniform)
-  if (pact) {
-#pragma unroll
-    for (int qt = 0; qt < NQ; ++qt) {
+  for (int qt = 0; qt < NQ; ++qt) {
+    if (pact) {
       const int c0 = QW * qt + 2 * cpl;
+      // q, k as fp32 and 1 / E
+      float qf[2][2], kf[2][2], iE[2][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float2 qq = rq[qt][j].f(), kk = rk[qt][j].f();
+        qf[j][0] = qq.x;
+        qf[j][1] = qq.y;
+        kf[j][0] = kk.x;
+        kf[j][1] = kk.y;
+        iE[j][0] = __builtin_amdgcn_rcpf(Ef[j][0]);
+        iE[j][1] = __builtin_amdgcn_rcpf(Ef[j][1]);
+      }
+      // Q.Gamma and K'^T to the record, (K.Gamma)^T to LDS: the prefix decay eP of the earlier
+      // sub-tiles and the suffix decay eS of the later ones (the sub-tile is wave-uniform)
       float eP[2] = {1.f, 1.f}, eS[2] = {1.f, 1.f};
 #pragma unroll
       for (int x = 0; x < NT; ++x) {
@@ -333,43 +331,28 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
         if (x > psb) { eS[0] *= e.x; eS[1] *= e.y; }
       }
       if (psb == 0 && rp == 0) {  // e^{G_last} = eS of sub-tile 0 times its own total
-        *reinterpret_cast<float2*>(rgam + c0) = make_float2(eS[0] * Tb[qt][0], eS[1] * Tb[qt][1]);
+        *reinterpret_cast<float2*>(rgam + c0) = make_float2(eS[0] * Tb[0], eS[1] * Tb[1]);
       }
-      float qg[2][2], kg[2][2], kp[2][2];  // [row j][channel]
-      const float tS[2] = {Tb[qt][0] * eS[0], Tb[qt][1] * eS[1]};
+      {
+        float qg[2][2], kg[2][2], kp[2][2];  // [row j][channel]
+        const float tS[2] = {Tb[0] * eS[0], Tb[1] * eS[1]};
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int ch = 0; ch < 2; ++ch) {
+            const float eg = Ef[j][ch] * eP[ch];
+            qg[j][ch] = qf[j][ch] * eg;
+            kg[j][ch] = kf[j][ch] * eg;
+            kp[j][ch] = kf[j][ch] * (iE[j][ch] * tS[ch]);
+          }
+          st2<F32>(rec + R::QG + (r0 + j) * DK + c0, qg[j][0], qg[j][1]);
+        }
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-          const float eg = Ef[qt][j][ch] * eP[ch];
-          qg[j][ch] = qf[qt][j][ch] * eg;
-          kg[j][ch] = kf[qt][j][ch] * eg;
-          kp[j][ch] = kf[qt][j][ch] * (iE[qt][j][ch] * tS[ch]);
+          st2<F32>(rec + R::KPT + (c0 + ch) * CP + r0, kp[0][ch], kp[1][ch]);
+          st2<F32>(KGt + (c0 + ch) * TS + r0, kg[0][ch], kg[1][ch]);
         }
-        st2<F32>(rec + R::QG + (r0 + j) * DK + c0, qg[j][0], qg[j][1]);
       }
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        st2<F32>(rec + R::KPT + (c0 + ch) * CP + r0, kp[0][ch], kp[1][ch]);
-        st2<F32>(KGt + (c0 + ch) * TS + r0, kg[0][ch], kg[1][ch]);
-      }
-    }
-  }
-  if constexpr (CP > C) {  // token pads of K'^T and (K . Gamma)^T are zero
-    for (int e = tid; e < DK * (CP - C); e += 512) {
-      const int c = e / (CP - C), t = C + e % (CP - C);
-      rec[R::KPT + c * CP + t] = (E)0.f;
-      KGt[c * TS + t] = (E)0.f;
-    }
-  }
-
-  // ---------------- M_kk and M_qk, one quarter of the key dimension at a time
-  f32x4 acc[NSLOT];
-#pragma unroll
-  for (int sl = 0; sl < NSLOT; ++sl) acc[sl] = zero4();
-#pragma unroll
-  for (int qt = 0; qt < NQ; ++qt) {
-    if (pact) {
       // operands of this thread's rows and channels: Q and K rows scaled by E = e^{G_r - R_b}, K
       // columns for the diagonal sub-tile (1 / E = e^{R_b - G_i}), for earlier sub-tiles (Tb / E =
       // e^{G_end - G_i}) and for each gap pair (times the decay of the sub-tiles in between);
@@ -389,12 +372,12 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int r = r0 + j;
-        const float e0 = Ef[qt][j][0], e1 = Ef[qt][j][1];
-        const float k0 = kf[qt][j][0], k1 = kf[qt][j][1];
-        const float kd0 = k0 * iE[qt][j][0], kd1 = k1 * iE[qt][j][1];  // diagonal columns
-        const float ko0 = kd0 * Tb[qt][0], ko1 = kd1 * Tb[qt][1];      // earlier columns
+        const float e0 = Ef[j][0], e1 = Ef[j][1];
+        const float k0 = kf[j][0], k1 = kf[j][1];
+        const float kd0 = k0 * iE[j][0], kd1 = k1 * iE[j][1];  // diagonal columns
+        const float ko0 = kd0 * Tb[0], ko1 = kd1 * Tb[1];      // earlier columns
         const int o = r * QS + cl;
-        st2_split<F32>(opnd(0, 0) + o, opnd(0, SPLIT) + o, qf[qt][j][0] * e0, qf[qt][j][1] * e1);
+        st2_split<F32>(opnd(0, 0) + o, opnd(0, SPLIT) + o, qf[j][0] * e0, qf[j][1] * e1);
         st2_split<F32>(opnd(1, 0) + o, opnd(1, SPLIT) + o, k0 * e0, k1 * e1);
         st2_split<F32>(opnd(2, 0) + o, opnd(2, SPLIT) + o, kd0, kd1);
         st2_split<F32>(opnd(3, 0) + o, opnd(3, SPLIT) + o, ko0, ko1);
@@ -410,6 +393,8 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
       }
     }
     __syncthreads();
+    // the next quarter's scan (Eend of other channels: no reader in this phase)
+    if (qt + 1 < NQ) scan(qt + 1 < NQ ? qt + 1 : qt, Ef, Tb);
     // tile pairs spread over the waves; each product M^T[a-cols][b-rows] holds, per lane, row
     // r = 16 b + lo and four consecutive columns i = 16 a + 4 grp + j
 #pragma unroll
@@ -437,6 +422,21 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
         }
       }
       acc[pi >> 3] = c;
+    }
+    if (qt == NQ - 1) {
+      // beta and V^T (for A, T and the U~ product) last: they were loaded last
+      if (tid < C) Bet[tid] = rb;
+      if (vact) {
+        float x0[8], x1[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float2 vv = rv[i].f();
+          x0[i] = vv.x;
+          x1[i] = vv.y;
+        }
+        st8_a8<F32>(Vt + (2 * vcp) * TS + 8 * vtg, x0);
+        st8_a8<F32>(Vt + (2 * vcp + 1) * TS + 8 * vtg, x1);
+      }
     }
     __syncthreads();
   }
