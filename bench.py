@@ -29,7 +29,8 @@ The JSON line carries:
                     heads x 65,536 tokens, one 1,048,576-token sequence x 8 heads,
                     16 packed sequences), each timed over a few calls with the
                     cache evicted before each: tokens/s, the chain's layout (value
-                    slice, segments) and the two stages' durations
+                    slice, segments), the two stages' durations, and the whole
+                    call's algorithmic bytes and (bf16) flops against HBM and MFMA
   cpu_baseline   -- the fp64 oracle on this host's cores, whole passes over the
                     same workload for at least 10 s (a baseline, not a target)
 Algorithmic work per token and head (d_k = d_v = d, chunk C):
@@ -311,9 +312,16 @@ def main():
             lstep(0)
             torch.cuda.synchronize()
             lms, _ = time_launches(lstep, reps, None if args.no_flush else flush)
+            s_io = 4 if tdt == torch.float32 else 2
+            n_seq = wl.num_seqs if wl.kind == "varlen" else wl.B
+            wbytes = prefill_bytes(1, n_tok, wl.H, wl.dk, wl.dv, s_io, s_io, with_h0=False, with_hT=False) \
+                + n_seq * wl.H * 4 * wl.dk * wl.dv * (int(wl.kind != "varlen" and wl.h0_std is not None) + 1)
+            wflops = n_tok * wl.H * prefill_flops_per_token_head(wl.dk, wl.dv, wl.chunk)
             entry.update({"ms_per_call": lms, "tokens_per_s": n_tok / (lms * 1e-3),
                           "token_heads_per_s": n_tok * wl.H / (lms * 1e-3), "calls": reps,
-                          "dtype": "f32" if tdt == torch.float32 else "bf16"})
+                          "dtype": "f32" if tdt == torch.float32 else "bf16",
+                          "hbm_frac": wbytes / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "mfma_frac": None if tdt == torch.float32 else wflops / (lms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS})
             if wl.kind != "varlen":
                 if not args.no_flush:
                     flush()
