@@ -138,6 +138,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the other prefill workloads")
+    ap.add_argument("--workloads", default="", help="comma-separated subset of the other prefill workloads")
     ap.add_argument("--no-flush", action="store_true", help="do not evict the Infinity Cache between steps")
     ap.add_argument("--copy-calibration", action="store_true", help="run one 1 GiB copy (counter scaling) and exit")
     args = ap.parse_args()
@@ -233,7 +234,7 @@ def main():
                      "alg_bytes_per_launch": intra_bytes},
         "roofline_chain": {"bound": "hbm", "achieved": gbs_chain, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": gbs_chain / HBM_PEAK_GBS, "traffic": measured_traffic("chain"),
-                           "kernel": "kda::chain_kernel<false, 128, 128, 64, 32>", "ms_per_launch": k_ms[1],
+                           "kernel": "kda::chain_kernel<false, 128, 128, 64, 32, false>", "ms_per_launch": k_ms[1],
                            "alg_bytes_per_launch": chain_bytes},
         "roofline_mfma": {"achieved": tfs, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                           "frac": tfs / MFMA_BF16_PEAK_TFS, "alg_flops_per_launch": alg_flops, "scope": "whole call"},
@@ -273,8 +274,11 @@ def main():
     # ---------------- the other prefill workloads: tokens/s on one GPU
     if not args.no_workloads:
         out["workloads"] = {}
+        chosen = set(x for x in args.workloads.split(",") if x)
         for name, reps in (("cfg0_f32_b1_h2_t256_d64", 20), ("cfg2_bf16_b1_h32_t65536_d128", 5),
                            ("cfg4_bf16_b1_h8_t1048576_d128", 3), ("cfg4v_varlen_n16_h8_d128", 3)):
+            if chosen and name not in chosen:
+                continue
             wl = datagen.WORKLOADS[name]
             tdt = torch.float32 if wl.dtype == datagen.DT_F32 else torch.bfloat16
             if wl.kind == "varlen":
