@@ -284,6 +284,30 @@ def test_p11_column_independence():
 
 
 # --------------------------------------------------------------------------------------------
+# P15: a segment is an affine map of its initial state.  Run from the identity on d_k columns
+# with zero values it gives M (and the per-token read-out of M); run from zero it gives b; then
+# from any S: hT = M S + b and o = o(0) + o_M S.  The segment-parallel chain rests on this.
+
+
+def test_p15_segment_affine_map():
+    d = inputs(151, 1, 70, 2, 16, 8)
+    B, T, H, dk = d["q"].shape
+    dv = d["v"].shape[-1]
+    eye = np.broadcast_to(np.eye(dk), (B, H, dk, dk)).copy()
+    di = dict(d)
+    di["v"] = np.zeros((B, T, H, dk), d["v"].dtype)
+    di["h0"] = eye
+    o_M, M = run(di)
+    o_0, b = run(d, h0=None)
+    S = np.random.default_rng(15).standard_normal((B, H, dk, dv))
+    dS = dict(d)
+    dS["h0"] = S
+    o_S, h_S = run(dS)
+    assert rel_err(np.einsum("bhij,bhjk->bhik", M, S) + b, h_S) < 1e-12
+    assert rel_err(o_0 + np.einsum("bthj,bhjk->bthk", o_M, S), o_S) < 1e-12
+
+
+# --------------------------------------------------------------------------------------------
 # P12: T single-token decode steps equal one prefill of T tokens
 
 
