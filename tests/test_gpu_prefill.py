@@ -125,20 +125,22 @@ def test_continuation_two_halves():
     assert state_err(host64(h2), h_ref) < TOL[BF16]
 
 
-@pytest.mark.parametrize("dt,B,T,H,dk,dv,h0", [
-    (BF16, 1, 8229, 2, 128, 128, True),   # 129 chunks: 4 segments, the last one shorter
-    (BF16, 2, 4113, 2, 128, 128, True),   # two sequences, 2 segments each, ragged tail
-    (BF16, 1, 4480, 1, 128, 64, True),    # the identity block is wider than the value columns
-    (BF16, 1, 4480, 1, 64, 128, False),
-    (F32, 1, 6400, 1, 64, 64, True),
+@pytest.mark.parametrize("dt,B,T,H,dk,dv,chunk,h0", [
+    (BF16, 1, 8229, 2, 128, 128, 64, True),   # 129 chunks: 4 segments, the last one shorter
+    (BF16, 2, 4113, 2, 128, 128, 64, True),   # two sequences, 2 segments each, ragged tail
+    (BF16, 1, 4480, 1, 128, 64, 64, True),    # the identity block is wider than the value columns
+    (BF16, 1, 4480, 1, 64, 128, 64, False),
+    (BF16, 1, 3000, 3, 64, 64, 32, True),     # 94 chunks of 32
+    (F32, 1, 6400, 1, 64, 64, 64, True),
+    (F32, 1, 2570, 1, 128, 128, 32, True),    # fp32 at d = 128 (16-column slices), ragged
 ])
-def test_segmented_chain_against_oracle(dt, B, T, H, dk, dv, h0):
+def test_segmented_chain_against_oracle(dt, B, T, H, dk, dv, chunk, h0):
     """Long sequences on few heads run the chain per segment (summaries, start states, chain):
     o and hT still match the oracle element by element."""
-    plan = kda.chain_plan(B, T, H, dk, dv, 64, dtype=torch.float32 if dt == F32 else torch.bfloat16)
+    plan = kda.chain_plan(B, T, H, dk, dv, chunk, dtype=torch.float32 if dt == F32 else torch.bfloat16)
     assert plan[1] > 1, plan
     d = datagen.prefill_inputs(500 + T + dk, B, T, H, dk, dv, dt, 0.02 if h0 else None)
-    check(d, 64, dt, "segmented plan %s" % (plan,))
+    check(d, chunk, dt, "segmented plan %s" % (plan,))
 
 
 def test_segmented_hT_aliases_h0():
