@@ -23,6 +23,8 @@ The JSON line carries:
   roofline_mfma  -- the whole call's algorithmic flops against dense bf16 MFMA
                     (the headline metric's "% of MFMA peak")
   roofline_call_hbm -- the whole call's algorithmic bytes (inputs, o, h0, hT)
+  states         -- the same call through kda_chunked_forward_with_states, keeping
+                    the state every 1024 tokens (prefix states for a serving cache)
   decode         -- 1000 sequential kda_decode_step calls on the 256-sequence x
                     32-head state (512 MiB fp32), bytes and fraction of HBM
   workloads      -- the other seeded prefill workloads (fp32 2 x 256 tokens, 32
@@ -138,6 +140,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the other prefill workloads")
+    ap.add_argument("--no-states", action="store_true", help="skip the state-snapshot leg")
     ap.add_argument("--workloads", default="", help="comma-separated subset of the other prefill workloads")
     ap.add_argument("--no-flush", action="store_true", help="do not evict the Infinity Cache between steps")
     ap.add_argument("--copy-calibration", action="store_true", help="run one 1 GiB copy (counter scaling) and exit")
@@ -242,6 +245,23 @@ def main():
                               "alg_bytes_per_launch": alg_bytes, "scope": "whole call"},
         "wall_s_timed_region": wall,
     }
+
+    # ---------------- the same call keeping the state every 1024 tokens (prefix states for a cache)
+    if not args.no_states:
+        every = 1024
+        st_buf = torch.empty((w.B, w.H, w.T // every, w.dk, w.dv), dtype=torch.float32, device=dev)
+
+        def sstep(_i):
+            kda.kda_chunked_forward_with_states(g["q"], g["k"], g["v"], g["g"], g["beta"], g["h0"], state_every=every,
+                                                chunk=w.chunk, o=o, hT=hT, states=st_buf)
+
+        sstep(0)
+        torch.cuda.synchronize()
+        sms, _ = time_launches(sstep, args.steps, None if args.no_flush else flush)
+        out["states"] = {"state_every": every, "states_per_call": w.B * w.H * (w.T // every),
+                         "state_bytes_per_call": st_buf.numel() * 4, "ms_per_call": sms,
+                         "tokens_per_s": tokens / (sms * 1e-3), "overhead_vs_plain": sms / ms - 1.0}
+        del st_buf
 
     # ---------------- decode
     if not args.no_decode:

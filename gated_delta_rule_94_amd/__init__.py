@@ -7,6 +7,8 @@ entry points' names:
 
 * ``kda_chunked_forward``        -- chunked prefill, B equal-length sequences
 * ``kda_chunked_forward_varlen`` -- chunked prefill, packed sequences (cu_seqlens)
+* ``kda_chunked_forward_with_states`` / ``kda_chunked_forward_varlen_with_states`` -- the same,
+  also keeping the state every N tokens (prefix states for a serving cache)
 * ``kda_decode_step``            -- one token per sequence, state updated in place
 
 Importing this package fails loudly when ``libkda.so`` has not been built
@@ -28,7 +30,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "K
 # exported symbols of libkda.so (the C ABI)
 EXPORTS = (
     "kda_status_string", "kda_version", "kda_chunked_forward_workspace_bytes", "kda_chunked_forward_plan",
-    "kda_chunked_forward",
+    "kda_chunked_forward", "kda_chunked_forward_with_states", "kda_chunked_forward_varlen_with_states",
     "kda_chunked_forward_profiled", "kda_chunked_forward_varlen", "kda_chunked_forward_varlen_workspace_bytes",
     "kda_decode_step",
 )
@@ -50,6 +52,10 @@ _lib.kda_chunked_forward_varlen_workspace_bytes.argtypes = [_i32] * 8
 _lib.kda_chunked_forward_varlen_workspace_bytes.restype = _sz
 _lib.kda_chunked_forward.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp, _sz, _vp]
 _lib.kda_chunked_forward.restype = _i32
+_lib.kda_chunked_forward_with_states.argtypes = [_vp] * 9 + [_i32] * 8 + [_vp, _sz, _vp]
+_lib.kda_chunked_forward_with_states.restype = _i32
+_lib.kda_chunked_forward_varlen_with_states.argtypes = [_vp] * 9 + [_i32, _vp] + [_i32] * 8 + [_vp, _sz, _vp]
+_lib.kda_chunked_forward_varlen_with_states.restype = _i32
 _lib.kda_chunked_forward_profiled.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp, _sz, _vp, _vp]
 _lib.kda_chunked_forward_profiled.restype = _i32
 _lib.kda_chunked_forward_varlen.argtypes = [_vp] * 8 + [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
@@ -171,6 +177,38 @@ def kda_chunked_forward(q, k, v, g, beta, h0=None, *, chunk: int = 64, o=None, h
     return o, hT
 
 
+def kda_chunked_forward_with_states(q, k, v, g, beta, h0=None, *, state_every: int, chunk: int = 64, o=None,
+                                    hT=None, states=None, want_hT: bool = True, workspace=None, stream=None):
+    """kda_chunked_forward that also returns the state after every state_every tokens (a positive
+    multiple of chunk): states [B,H,T//state_every,dk,dv] float32, entry j = the state after the
+    first (j+1)*state_every tokens.  Returns (o, hT, states)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("g", g, (B, T, H, dk)),
+                         ("v", v, (B, T, H, dv)), ("beta", beta, (B, T, H))):
+        _check(name, t, shp, dt, dev)
+    _check("h0", h0, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check("o", o, (B, T, H, dv), dt, dev)
+    if hT is None and want_hT:
+        hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check("hT", hT, (B, H, dk, dv), torch.float32, dev)
+    n_states = T // state_every if state_every > 0 else 0
+    if states is None:
+        states = torch.empty((B, H, n_states, dk, dv), dtype=torch.float32, device=dev)
+    _check("states", states, (B, H, n_states, dk, dv), torch.float32, dev)
+    ws_bytes = _lib.kda_chunked_forward_workspace_bytes(B, T, H, dk, dv, chunk, _dtype_code(q))
+    ws = _workspace(workspace, ws_bytes, dev)
+    st = _lib.kda_chunked_forward_with_states(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o),
+                                              _ptr(hT), _ptr(states), int(state_every), B, T, H, dk, dv, chunk,
+                                              _dtype_code(q), _ptr(ws), _nbytes(ws), _stream(stream))
+    if st:
+        raise KDAError("kda_chunked_forward_with_states", st)
+    return o, hT, states
+
+
 def kda_chunked_forward_profiled(q, k, v, g, beta, h0, o, hT, *, chunk: int = 64, workspace=None, stream=None):
     """kda_chunked_forward into preallocated o / hT (hT may be None), returning the two kernels'
     durations in ms (intra-chunk, chain) from HIP events on the stream; synchronises the stream."""
@@ -198,6 +236,11 @@ def kda_chunked_forward_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen: int, h0
     """Packed varlen prefill.  q, k, g [1,T_total,H,dk] (or [T_total,H,dk]); v [..,T_total,H,dv];
     beta [..,T_total,H]; cu_seqlens int32 [N+1] on the device; h0 [N,H,dk,dv] float32 or None.
     Returns (o shaped like v, hT [N,H,dk,dv] float32 or None)."""
+    return _varlen_call(q, k, v, g, beta, cu_seqlens, max_seqlen, h0, chunk, o, hT, want_hT, workspace, stream, None, 0)
+
+
+def _varlen_call(q, k, v, g, beta, cu_seqlens, max_seqlen, h0, chunk, o, hT, want_hT, workspace, stream, states,
+                 state_every):
     Tt, H, dk = q.shape[-3:]
     dv = v.shape[-1]
     N = cu_seqlens.numel() - 1
@@ -218,12 +261,39 @@ def kda_chunked_forward_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen: int, h0
     _check("hT", hT, (N, H, dk, dv), torch.float32, dev)
     ws_bytes = _lib.kda_chunked_forward_varlen_workspace_bytes(N, Tt, max_seqlen, H, dk, dv, chunk, _dtype_code(q))
     ws = _workspace(workspace, ws_bytes, dev)
-    st = _lib.kda_chunked_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
-                                         _ptr(cu_seqlens), N, Tt, int(max_seqlen), H, dk, dv, chunk, _dtype_code(q),
-                                         _ptr(ws), _nbytes(ws), _stream(stream))
-    if st:
-        raise KDAError("kda_chunked_forward_varlen", st)
+    if states is None:
+        st = _lib.kda_chunked_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o),
+                                             _ptr(hT), _ptr(cu_seqlens), N, Tt, int(max_seqlen), H, dk, dv, chunk,
+                                             _dtype_code(q), _ptr(ws), _nbytes(ws), _stream(stream))
+        if st:
+            raise KDAError("kda_chunked_forward_varlen", st)
+    else:
+        st = _lib.kda_chunked_forward_varlen_with_states(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT), _ptr(states), state_every,
+            _ptr(cu_seqlens), N, Tt, int(max_seqlen), H, dk, dv, chunk, _dtype_code(q), _ptr(ws), _nbytes(ws),
+            _stream(stream))
+        if st:
+            raise KDAError("kda_chunked_forward_varlen_with_states", st)
     return o, hT
+
+
+def kda_chunked_forward_varlen_with_states(q, k, v, g, beta, cu_seqlens, max_seqlen: int, h0=None, *,
+                                           state_every: int, chunk: int = 64, o=None, hT=None, states=None,
+                                           want_hT: bool = True, workspace=None, stream=None):
+    """kda_chunked_forward_varlen that also returns the state after every state_every tokens of each
+    sequence: states [N,H,max_seqlen//state_every,dk,dv] float32 (entries past a sequence's length
+    are left as allocated).  Returns (o, hT, states)."""
+    Tt, H, dk = q.shape[-3:]
+    dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    dev = q.device
+    n_states = int(max_seqlen) // state_every if state_every > 0 else 0
+    if states is None:
+        states = torch.zeros((N, H, n_states, dk, dv), dtype=torch.float32, device=dev)
+    _check("states", states, (N, H, n_states, dk, dv), torch.float32, dev)
+    o, hT = _varlen_call(q, k, v, g, beta, cu_seqlens, max_seqlen, h0, chunk, o, hT, want_hT, workspace, stream,
+                         states, int(state_every))
+    return o, hT, states
 
 
 def kda_decode_step(q, k, v, g, beta, state, *, o=None, stream=None):

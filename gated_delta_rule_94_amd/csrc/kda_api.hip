@@ -28,6 +28,11 @@ kda_status check_prefill(const void* q, const void* k, const void* v, const void
   return KDA_OK;
 }
 
+// Snapshot buffer and interval: a 16-byte-aligned buffer and a positive multiple of the chunk.
+bool states_ok(const float* states, int every, int chunk) {
+  return aligned16(states) && every > 0 && chunk > 0 && every % chunk == 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,13 +84,15 @@ bool workspace_ok(void* ws, size_t have, size_t need) {
 }
 }  // namespace
 
-kda_status kda_chunked_forward(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                               const float* h0, void* o, float* hT, int B, int T, int H, int d_k, int d_v, int chunk,
-                               kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
+kda_status kda_chunked_forward_with_states(const void* q, const void* k, const void* v, const void* g,
+                                           const void* beta, const float* h0, void* o, float* hT, float* states,
+                                           int state_every, int B, int T, int H, int d_k, int d_v, int chunk,
+                                           kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
   if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
   const kda_status st = check_prefill(q, k, v, g, beta, h0, o, hT, B * T, H, d_k, d_v, chunk, dt);
   if (st != KDA_OK) return st;
+  if (states && !states_ok(states, state_every, chunk)) return KDA_ERR_INVALID_ARG;
   if (B == 0) return KDA_OK;
   if (T == 0 && !hT) return KDA_OK;
   if (!workspace_ok(workspace, workspace_bytes, kda_chunked_forward_workspace_bytes(B, T, H, d_k, d_v, chunk, dt)))
@@ -101,7 +108,19 @@ kda_status kda_chunked_forward(const void* q, const void* k, const void* v, cons
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   a.stream = hip_stream;
+  if (states && T / state_every > 0) {
+    a.states = states;
+    a.state_every = state_every;
+    a.max_states = T / state_every;
+  }
   return kda::launch_chunked_forward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_chunked_forward(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                               const float* h0, void* o, float* hT, int B, int T, int H, int d_k, int d_v, int chunk,
+                               kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return kda_chunked_forward_with_states(q, k, v, g, beta, h0, o, hT, nullptr, 0, B, T, H, d_k, d_v, chunk, dt,
+                                         workspace, workspace_bytes, hip_stream);
 }
 
 kda_status kda_chunked_forward_profiled(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -142,15 +161,18 @@ kda_status kda_chunked_forward_profiled(const void* q, const void* k, const void
   return ok ? KDA_OK : KDA_ERR_HIP;
 }
 
-kda_status kda_chunked_forward_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                                      const float* h0, void* o, float* hT, const int32_t* cu_seqlens, int num_seqs,
-                                      int T_total, int max_seqlen, int H, int d_k, int d_v, int chunk, kda_dtype dt,
-                                      void* workspace, size_t workspace_bytes, void* hip_stream) {
+kda_status kda_chunked_forward_varlen_with_states(const void* q, const void* k, const void* v, const void* g,
+                                                  const void* beta, const float* h0, void* o, float* hT,
+                                                  float* states, int state_every, const int32_t* cu_seqlens,
+                                                  int num_seqs, int T_total, int max_seqlen, int H, int d_k, int d_v,
+                                                  int chunk, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                                                  void* hip_stream) {
   if (num_seqs < 0 || T_total < 0 || max_seqlen < 0) return KDA_ERR_INVALID_ARG;
   if (num_seqs > 0 && (!cu_seqlens || max_seqlen > T_total)) return KDA_ERR_INVALID_ARG;
   if ((int64_t)num_seqs * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
   const kda_status st = check_prefill(q, k, v, g, beta, h0, o, hT, T_total, H, d_k, d_v, chunk, dt);
   if (st != KDA_OK) return st;
+  if (states && !states_ok(states, state_every, chunk)) return KDA_ERR_INVALID_ARG;
   if (num_seqs == 0) return KDA_OK;
   if (!workspace_ok(workspace, workspace_bytes,
                     kda_chunked_forward_varlen_workspace_bytes(num_seqs, T_total, max_seqlen, H, d_k, d_v, chunk, dt)))
@@ -166,7 +188,21 @@ kda_status kda_chunked_forward_varlen(const void* q, const void* k, const void* 
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   a.stream = hip_stream;
+  if (states && max_seqlen / state_every > 0) {
+    a.states = states;
+    a.state_every = state_every;
+    a.max_states = max_seqlen / state_every;
+  }
   return kda::launch_chunked_forward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_chunked_forward_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                      const float* h0, void* o, float* hT, const int32_t* cu_seqlens, int num_seqs,
+                                      int T_total, int max_seqlen, int H, int d_k, int d_v, int chunk, kda_dtype dt,
+                                      void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return kda_chunked_forward_varlen_with_states(q, k, v, g, beta, h0, o, hT, nullptr, 0, cu_seqlens, num_seqs,
+                                                T_total, max_seqlen, H, d_k, d_v, chunk, dt, workspace,
+                                                workspace_bytes, hip_stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta, float* state,

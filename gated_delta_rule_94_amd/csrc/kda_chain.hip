@@ -39,6 +39,8 @@ struct ChainParams {
   int nseg, seg_len;      // segments per (sequence, head) and their length in chunks (1, 0: whole)
   const float* sstart;    // nseg > 1: start state of every segment [units][nseg][DK][DV]
   float* send;            // summary launch: [b_g | M_g] of segments 0..nseg-2 [units][nseg-1][DK][DV+DK]
+  float* states;          // or NULL: the state after every `every` tokens of a sequence,
+  int every, max_states;  // [units][max_states][DK][DV]
 };
 
 template <bool F32, int DK, int DV, int C, int WS>
@@ -144,9 +146,10 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
   const int unit = su / segs, seg = su - unit * segs;
   const int H = p.H;
   const int n = unit / H, h = unit - n * H;
-  int64_t t_begin, t_end, first;
+  int64_t t_begin, t_end, first, seq0;
   if (p.nseg > 1) {  // equal-length sequences
     const int64_t s0 = (int64_t)n * p.T, s1 = s0 + p.T;
+    seq0 = s0;
     t_begin = s0 + (int64_t)seg * p.seg_len * C;
     t_end = t_begin + (int64_t)p.seg_len * C < s1 ? t_begin + (int64_t)p.seg_len * C : s1;
     first = (int64_t)n * p.nch + (int64_t)seg * p.seg_len;
@@ -154,11 +157,11 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     int x = p.cu[n], y = p.cu[n + 1];
     x = x < 0 ? 0 : (x > p.T ? p.T : x);
     y = y < x ? x : (y > p.T ? p.T : y);
-    t_begin = x;
+    t_begin = seq0 = x;
     t_end = y;
     first = p.chunk0[n];
   } else {
-    t_begin = (int64_t)n * p.T;
+    t_begin = seq0 = (int64_t)n * p.T;
     t_end = t_begin + p.T;
     first = (int64_t)n * p.nch;
   }
@@ -311,6 +314,25 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
       }
     }
   };
+  // state snapshot after chunk c when it ends `every` tokens into the sequence (every is a multiple
+  // of C, so only a full chunk can): the prefix states a serving cache resumes from.  Wave-uniform.
+  const int rel0 = (int)(t_begin - seq0);  // tokens of the sequence before this range (a multiple of C)
+  auto snapshot = [&](int c) {
+    const int rel_end = rel0 + (c + 1) * C;
+    if (!p.states || rel_end % p.every != 0 || t_begin + (int64_t)(c + 1) * C > t_end) return;
+    const int j = rel_end / p.every - 1;
+    if (j >= p.max_states) return;
+    // a wave-uniform base and 32-bit lane offsets derived here from an opaque zero, so that the
+    // compiler keeps no store addresses live across the chunk loop
+    char* st = reinterpret_cast<char*>(p.states + ((int64_t)unit * p.max_states + j) * DK * DV);
+    uint32_t z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+    const uint32_t lane_off = 4u * ((4u * grp + z) * DV + ccol);
+#pragma unroll
+    for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) *reinterpret_cast<float*>(st + lane_off + 4u * (16 * m + r) * DV) = Sacc[m][r];
+  };
 
   // Chain waves compute; copy waves stream records.  The two roles run separate loops with the same
   // barriers, so each role's registers are live on its own path only.  Prologue: chunk 0 in buffer
@@ -336,9 +358,11 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     __syncthreads();
     for (int c = 0; c < nchunks; c += 2) {
       chunk_step(c, 0);
+      if constexpr (!SUM) snapshot(c);
       __syncthreads();
       if (c + 1 >= nchunks) break;
       chunk_step(c + 1, 1);
+      if constexpr (!SUM) snapshot(c + 1);
       __syncthreads();
     }
     if constexpr (SUM) {
@@ -381,6 +405,7 @@ static hipError_t launch_chain_impl(const ChainLaunch& L) {
   p.ws = L.records; p.h0 = L.h0; p.o = L.o; p.hT = L.hT; p.cu = L.cu; p.chunk0 = L.chunk0;
   p.units = L.units; p.H = L.H; p.T = L.T; p.nch = L.nch; p.dv = DV;
   p.nseg = L.nseg > 1 ? L.nseg : 1; p.seg_len = L.seg_len; p.sstart = L.sstart; p.send = L.send;
+  p.states = SUM ? nullptr : L.states; p.every = L.every; p.max_states = L.max_states;
   const int64_t su = (int64_t)L.units * (SUM ? p.nseg - 1 : p.nseg);
   const int64_t grid = ((su + 7) / 8) * 8 * ((SUM ? DV + DK : DV) / WS);
   if (su <= 0 || grid > INT32_MAX) return hipErrorInvalidValue;

@@ -30,6 +30,8 @@ struct PrefillArgs {
   size_t workspace_bytes;
   void* stream;
   hipEvent_t* events = nullptr;  // optional: [3] recorded before the intra kernel, between the kernels, after the chain
+  float* states = nullptr;       // optional state snapshots [num_seqs][H][max_states][dk][dv]
+  int state_every = 0, max_states = 0;
 };
 
 // intra-chunk kernel launch (kda_intra.hip)
@@ -64,6 +66,10 @@ struct ChainLaunch {
   bool summary = false;
   const float* sstart = nullptr;  // [units][nseg][dk][dv]
   float* send = nullptr;          // [units][nseg - 1][dk][dv + dk]
+  // optional state snapshots after every `every` tokens of each sequence (every: a multiple of
+  // chunk): [units][max_states][dk][dv]
+  float* states = nullptr;
+  int every = 0, max_states = 0;
   void* stream;
 };
 

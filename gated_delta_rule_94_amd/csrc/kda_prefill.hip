@@ -117,6 +117,7 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
   const ChainPlan pl = chain_plan(a.f32, K.units, nch, a.dv, varlen);
   K.ws = pl.ws;
   K.stream = a.stream;
+  K.states = a.states; K.every = a.state_every; K.max_states = a.max_states;
   if (pl.nseg > 1) {
     unsigned char* seg = records + max_chunks * a.H * rb;
     float* sstart = reinterpret_cast<float*>(seg);

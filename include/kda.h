@@ -104,6 +104,26 @@ kda_status kda_chunked_forward(const void* q, const void* k, const void* v, cons
                                kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * kda_chunked_forward that also keeps the recurrent state at fixed token
+ * intervals: the prefix states a serving cache stores so that a repeated
+ * prompt resumes from the state instead of being prefilled again (a recurrent
+ * state has no per-token KV slabs to replay: how-K3-works page, "KDA: a fixed
+ * memory instead of a growing bill"; architecture-explained page, "Kimi Delta
+ * Attention: Scaling Attention Beyond the Trillion-Parameter Regime").
+ *   states [B,H,T/state_every,d_k,d_v] fp32 out (16-byte aligned): entry j is the
+ *          state after the first (j+1)*state_every tokens of the sequence, i.e.
+ *          hT of a call on that prefix; passing it as h0 resumes from there.
+ *   state_every: a positive multiple of chunk.
+ * states may be NULL (then state_every is ignored and this is
+ * kda_chunked_forward).  Any overlap of states with another argument is
+ * undefined.  Other arguments, the workspace and errors as kda_chunked_forward.
+ */
+kda_status kda_chunked_forward_with_states(const void* q, const void* k, const void* v, const void* g,
+                                           const void* beta, const float* h0, void* o, float* hT, float* states,
+                                           int state_every, int B, int T, int H, int d_k, int d_v, int chunk,
+                                           kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
  * Profiling form of kda_chunked_forward: the same arguments, checks and
  * results, plus kernel_ms[2] (host memory, non-NULL), which receives the
  * durations in milliseconds of the two stages of the call -- [0] the
@@ -137,6 +157,19 @@ kda_status kda_chunked_forward_varlen(const void* q, const void* k, const void* 
                                       const float* h0, void* o, float* hT, const int32_t* cu_seqlens, int num_seqs,
                                       int T_total, int max_seqlen, int H, int d_k, int d_v, int chunk, kda_dtype dt,
                                       void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * kda_chunked_forward_varlen with state snapshots (see
+ * kda_chunked_forward_with_states): states [num_seqs,H,max_seqlen/state_every,
+ * d_k,d_v] fp32; entry j of sequence n is its state after (j+1)*state_every
+ * tokens; entries past a sequence's length are left untouched.
+ */
+kda_status kda_chunked_forward_varlen_with_states(const void* q, const void* k, const void* v, const void* g,
+                                                  const void* beta, const float* h0, void* o, float* hT,
+                                                  float* states, int state_every, const int32_t* cu_seqlens,
+                                                  int num_seqs, int T_total, int max_seqlen, int H, int d_k, int d_v,
+                                                  int chunk, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                                                  void* hip_stream);
 
 /* Workspace bytes kda_chunked_forward_varlen needs (0 = none). */
 size_t kda_chunked_forward_varlen_workspace_bytes(int num_seqs, int T_total, int max_seqlen, int H, int d_k, int d_v,

@@ -106,6 +106,29 @@ def test_prefill_validation():
     assert fwd(B=0, ptr=None, ws=None, ws_bytes=0) == OK
 
 
+def test_states_validation():
+    """Snapshot arguments are checked before anything would run: a 16-byte-aligned buffer and an
+    interval that is a positive multiple of the chunk; a NULL buffer ignores the interval."""
+    lib = kda.lib()
+
+    def fs(states=FAKE, every=128, chunk=64, ws=FAKE):
+        return lib.kda_chunked_forward_with_states(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, states, every,
+                                                   1, 256, 2, 64, 64, chunk, 1, ws, 1 << 40, None)
+
+    def fv(states=FAKE, every=128, chunk=64):
+        return lib.kda_chunked_forward_varlen_with_states(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, states,
+                                                          every, FAKE, 2, 256, 200, 2, 64, 64, chunk, 1, None, 0,
+                                                          None)
+
+    assert fs(every=96) == INVALID       # not a multiple of the chunk
+    assert fs(every=0) == INVALID
+    assert fs(every=-64) == INVALID
+    assert fs(states=FAKE + 4) == INVALID  # misaligned
+    assert fs(states=None, every=0, ws=None) == 3  # a NULL buffer ignores the interval (then: no workspace)
+    assert fv(every=96) == INVALID
+    assert fv(states=FAKE + 8) == INVALID
+
+
 def test_varlen_validation():
     lib = kda.lib()
     call = lambda cu, N, Tt, ms, ptr=FAKE: lib.kda_chunked_forward_varlen(ptr, ptr, ptr, ptr, ptr, None, ptr, None,
