@@ -36,7 +36,7 @@ _lock = threading.Lock()
 _lib = None
 
 # tensor ids of the streams
-TID_Q, TID_K, TID_V, TID_BETA, TID_G, TID_H0, TID_LEN = 0, 1, 2, 3, 4, 5, 6
+TID_Q, TID_K, TID_V, TID_BETA, TID_G, TID_H0, TID_LEN, TID_Z = 0, 1, 2, 3, 4, 5, 6, 7
 _KIND_NORMAL, _KIND_UNIT_ROWS, _KIND_SIGMOID = 0, 1, 2
 DT_F32, DT_BF16, DT_F64 = 0, 1, 2
 
@@ -126,6 +126,39 @@ def prefill_inputs(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: i
     }
     d["h0"] = None if h0_std is None else fill(seed, TID_H0, 0, _KIND_NORMAL, h0_std, DT_F32, (B, H, dk, dv), dv)
     return d
+
+
+def prefill_preactivations(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: int, h0_std=None,
+                           sub: int = 0):
+    """The same draws as prefill_inputs before their last transform, for the fused entry points:
+    q, k ~ N(0, 1) not normalised; x (the gate pre-activation, g = -5 sigmoid(x) in prefill_inputs)
+    ~ N(0, 1); plus z = sigmoid(N(0, 1)) [B,T,H,dv], an output gate.  v, beta, h0 as prefill_inputs."""
+    rows = (B, T, H)
+    d = {
+        "q": fill(seed, TID_Q, sub, _KIND_NORMAL, 1.0, dtype, rows + (dk,), dk),
+        "k": fill(seed, TID_K, sub, _KIND_NORMAL, 1.0, dtype, rows + (dk,), dk),
+        "v": fill(seed, TID_V, sub, _KIND_NORMAL, 1.0, dtype, rows + (dv,), dv),
+        "x": fill(seed, TID_G, sub, _KIND_NORMAL, 1.0, dtype, rows + (dk,), dk),
+        "beta": fill(seed, TID_BETA, sub, _KIND_SIGMOID, 1.0, dtype, rows, 1),
+        "z": fill(seed, TID_Z, sub, _KIND_SIGMOID, 1.0, dtype, rows + (dv,), dv),
+    }
+    d["h0"] = None if h0_std is None else fill(seed, TID_H0, 0, _KIND_NORMAL, h0_std, DT_F32, (B, H, dk, dv), dv)
+    return d
+
+
+def decode_preactivations(seed: int, step: int, B: int, H: int, dk: int, dv: int, dtype: int):
+    """decode_inputs before their last transform (see prefill_preactivations): q, k, x [B,H,dk],
+    v, z [B,H,dv], beta [B,H]."""
+    sub = step + 1
+    rows = (B, H)
+    return {
+        "q": fill(seed, TID_Q, sub, _KIND_NORMAL, 1.0, dtype, rows + (dk,), dk),
+        "k": fill(seed, TID_K, sub, _KIND_NORMAL, 1.0, dtype, rows + (dk,), dk),
+        "v": fill(seed, TID_V, sub, _KIND_NORMAL, 1.0, dtype, rows + (dv,), dv),
+        "x": fill(seed, TID_G, sub, _KIND_NORMAL, 1.0, dtype, rows + (dk,), dk),
+        "beta": fill(seed, TID_BETA, sub, _KIND_SIGMOID, 1.0, dtype, rows, 1),
+        "z": fill(seed, TID_Z, sub, _KIND_SIGMOID, 1.0, dtype, rows + (dv,), dv),
+    }
 
 
 def decode_inputs(seed: int, step: int, B: int, H: int, dk: int, dv: int, dtype: int):

@@ -71,7 +71,9 @@ def _dtype_code(*arrs) -> int:
         return 0
     if dts == {np.dtype(np.uint16)}:
         return 1
-    raise TypeError("oracle inputs must all be float32 or all bf16 bit patterns (uint16), got %s" % dts)
+    if dts == {np.dtype(np.float64)}:
+        return 2
+    raise TypeError("oracle inputs must all be float32, all bf16 bit patterns (uint16) or all float64, got %s" % dts)
 
 
 def _c(a):
@@ -171,3 +173,50 @@ def decode_step(q, k, v, g, beta, state, nthreads=None):
     if rc:
         raise RuntimeError("kda_oracle_decode_step: invalid arguments")
     return o
+
+
+# --------------------------------------------------------------------------------------------
+# Fused forms: the steps on either side of the recurrence, as plain fp64 definitions.
+#  - the log-decay from its gate pre-activation x through a scaled sigmoid, g = -A sigmoid(x)
+#    (technical-report page, "Architecture at a glance": the lower bound on the log-decay);
+#  - q and k L2-normalised over d_k per (token, head): q / sqrt(sum q^2 + 1e-12);
+#  - an output gate z multiplying o elementwise (same page: the input-dependent output gate; the
+#    gate tensor is taken as given -- its projection needs trained weights).
+
+
+def _dec(a):
+    """Exact fp64 value of a stored fp32 / bf16-bits / fp64 array."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return ((a.astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _fused_inputs(q, k, g, x, gate_scale, normalize_qk):
+    q, k = _dec(q), _dec(k)
+    if normalize_qk:
+        q = q / np.sqrt((q * q).sum(axis=-1, keepdims=True) + 1e-12)
+        k = k / np.sqrt((k * k).sum(axis=-1, keepdims=True) + 1e-12)
+    g = -float(gate_scale) / (1.0 + np.exp(-_dec(x))) if x is not None else _dec(g)
+    return np.ascontiguousarray(q), np.ascontiguousarray(k), np.ascontiguousarray(g)
+
+
+def forward_fused(q, k, v, g, beta, h0=None, *, x=None, gate_scale=5.0, normalize_qk=False, z=None,
+                  want_o=True, want_hT=True, nthreads=None):
+    """forward() with the fused steps: g = -gate_scale * sigmoid(x) when x is given (g unused),
+    q and k normalised when normalize_qk, o multiplied by z when given.  Returns fp64 (o, hT)."""
+    q64, k64, g64 = _fused_inputs(q, k, g, x, gate_scale, normalize_qk)
+    o, hT = forward(q64, k64, np.ascontiguousarray(_dec(v)), g64, np.ascontiguousarray(_dec(beta)), h0,
+                    want_o=want_o, want_hT=want_hT, nthreads=nthreads)
+    if o is not None and z is not None:
+        o = o * _dec(z)
+    return o, hT
+
+
+def decode_step_fused(q, k, v, g, beta, state, *, x=None, gate_scale=5.0, normalize_qk=False, z=None,
+                      nthreads=None):
+    """decode_step() with the fused steps (see forward_fused); state updated in place."""
+    q64, k64, g64 = _fused_inputs(q, k, g, x, gate_scale, normalize_qk)
+    o = decode_step(q64, k64, np.ascontiguousarray(_dec(v)), g64, np.ascontiguousarray(_dec(beta)), state,
+                    nthreads=nthreads)
+    return o * _dec(z) if z is not None else o

@@ -40,7 +40,9 @@
  *
  * Inputs are the stored values (fp32, or bf16 bit patterns) decoded exactly to
  * fp64, so the oracle measures the arithmetic of an implementation, not the
- * rounding of its inputs.  Layouts (row-major): q, k, g [.., T, H, d_k];
+ * rounding of its inputs; fp64 arrays are also accepted, for inputs that the
+ * caller has transformed in fp64 (gate from its pre-activation, normalised
+ * q and k).  Layouts (row-major): q, k, g [.., T, H, d_k];
  * v [.., T, H, d_v]; beta [.., T, H]; states [.., H, d_k, d_v].
  */
 #include <math.h>
@@ -49,9 +51,11 @@
 #include <stdlib.h>
 #include <string.h>
 
-/* exact decode of a stored element: dtype 0 = fp32, 1 = bf16 bits */
+/* exact decode of a stored element: dtype 0 = fp32, 1 = bf16 bits, 2 = fp64 (inputs already
+   transformed in fp64, e.g. from gate pre-activations) */
 static inline double ld(const void* p, int dtype, size_t i) {
   if (dtype == 0) return (double)((const float*)p)[i];
+  if (dtype == 2) return ((const double*)p)[i];
   uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
   float f;
   memcpy(&f, &u, 4);
@@ -157,7 +161,7 @@ static void run_all(const inputs_t* in, const unit_t* units, int n_units, int nt
   free(ok);
 }
 
-static int bad_dims(int H, int dk, int dv, int dtype) { return H <= 0 || dk <= 0 || dv <= 0 || dtype < 0 || dtype > 1; }
+static int bad_dims(int H, int dk, int dv, int dtype) { return H <= 0 || dk <= 0 || dv <= 0 || dtype < 0 || dtype > 2; }
 
 /*
  * Batched forward.  o: [B,T,H,dv] fp64 (or NULL); hT: [B,H,dk,dv] fp64 (or NULL);

@@ -308,6 +308,66 @@ def test_p15_segment_affine_map():
 
 
 # --------------------------------------------------------------------------------------------
+# P16: the fused forms (gate from its pre-activation, normalised q and k, output gate) reduce to
+# the plain recurrence where their definitions fix the values exactly, and agree with the input
+# generator's own transforms (independent code) up to the rounding of its stored inputs
+
+
+def test_p16_fused_gate_special_values():
+    d = inputs(161, 1, 60, 2, 16, 8)
+    B, T, H, dk = d["q"].shape
+    # sigmoid(0) = 1/2: g = -A/2 exactly
+    x0 = np.zeros((B, T, H, dk), np.float32)
+    o_f, h_f = oracle.forward_fused(d["q"], d["k"], d["v"], None, d["beta"], d["h0"], x=x0, gate_scale=5.0)
+    o_p, h_p = oracle.forward(d["q"], d["k"], d["v"], np.full((B, T, H, dk), -2.5, np.float32), d["beta"], d["h0"])
+    assert rel_err(o_f, o_p) == 0.0 and rel_err(h_f, h_p) == 0.0
+    # a very negative pre-activation: the decay is 1 in fp64
+    xm = np.full((B, T, H, dk), -60.0, np.float32)
+    o_f, _ = oracle.forward_fused(d["q"], d["k"], d["v"], None, d["beta"], d["h0"], x=xm, gate_scale=5.0)
+    o_p, _ = oracle.forward(d["q"], d["k"], d["v"], np.zeros((B, T, H, dk), np.float32), d["beta"], d["h0"])
+    assert rel_err(o_f, o_p) == 0.0
+
+
+def test_p16_fused_normalisation_and_output_gate():
+    d = inputs(162, 1, 50, 2, 16, 8)
+    raw = datagen.prefill_preactivations(162, 1, 50, 2, 16, 8, F32, 0.02)
+    # normalisation is scale-free
+    o1, h1 = oracle.forward_fused(raw["q"], raw["k"], d["v"], d["g"], d["beta"], d["h0"], normalize_qk=True)
+    o4, h4 = oracle.forward_fused(4 * raw["q"], 4 * raw["k"], d["v"], d["g"], d["beta"], d["h0"], normalize_qk=True)
+    assert rel_err(o4, o1) < 1e-12 and rel_err(h4, h1) < 1e-12
+    # the output gate multiplies o only
+    o_p, h_p = run(d)
+    o_z, h_z = oracle.forward_fused(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], z=2 * np.ones_like(d["v"]))
+    assert rel_err(o_z, 2 * o_p) == 0.0 and rel_err(h_z, h_p) == 0.0
+    o_z, _ = oracle.forward_fused(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], z=raw["z"])
+    assert rel_err(o_z, o_p * raw["z"].astype(np.float64)) == 0.0
+
+
+def test_p16_fused_matches_the_generators_transforms():
+    """prefill_inputs stores normalise(q), normalise(k) and -5 sigmoid(x) rounded to fp32; the fused
+    oracle applies the same definitions to the unrounded draws."""
+    raw = datagen.prefill_preactivations(163, 2, 40, 2, 16, 8, F32, 0.02)
+    plain = datagen.prefill_inputs(163, 2, 40, 2, 16, 8, F32, 0.02)
+    assert np.array_equal(raw["v"], plain["v"]) and np.array_equal(raw["beta"], plain["beta"])
+    o_f, h_f = oracle.forward_fused(raw["q"], raw["k"], raw["v"], None, raw["beta"], raw["h0"], x=raw["x"],
+                                    gate_scale=5.0, normalize_qk=True)
+    o_p, h_p = run(plain)
+    assert rel_err(o_f, o_p) < 1e-5 and rel_err(h_f, h_p) < 1e-5
+
+
+def test_p16_fused_decode_is_one_token_prefill():
+    raw = datagen.decode_preactivations(164, 0, 2, 3, 16, 8, F32)
+    state = datagen.decode_state0(164, 2, 3, 16, 8).astype(np.float64)
+    h0 = state.copy()
+    o_d = oracle.decode_step_fused(raw["q"], raw["k"], raw["v"], None, raw["beta"], state, x=raw["x"],
+                                   gate_scale=5.0, normalize_qk=True, z=raw["z"])
+    one = {key: raw[key][:, None] for key in ("q", "k", "v", "x", "beta", "z")}
+    o_p, h_p = oracle.forward_fused(one["q"], one["k"], one["v"], None, one["beta"], h0, x=one["x"], gate_scale=5.0,
+                                    normalize_qk=True, z=one["z"])
+    assert rel_err(o_d, o_p[:, 0]) < 1e-14 and rel_err(state, h_p) < 1e-14
+
+
+# --------------------------------------------------------------------------------------------
 # P12: T single-token decode steps equal one prefill of T tokens
 
 
