@@ -25,6 +25,8 @@ The JSON line carries:
   roofline_call_hbm -- the whole call's algorithmic bytes (inputs, o, h0, hT)
   states         -- the same call through kda_chunked_forward_with_states, keeping
                     the state every 1024 tokens (prefix states for a serving cache)
+  fused          -- the same workload through kda_chunked_forward_fused: gate from
+                    its pre-activation, q and k normalised, output gate
   decode         -- 1000 sequential kda_decode_step calls on the 256-sequence x
                     32-head state (512 MiB fp32), bytes and fraction of HBM
   workloads      -- the other seeded prefill workloads (fp32 2 x 256 tokens, 32
@@ -141,6 +143,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--no-states", action="store_true", help="skip the state-snapshot leg")
+    ap.add_argument("--no-fused", action="store_true", help="skip the fused-steps leg")
     ap.add_argument("--workloads", default="", help="comma-separated subset of the other prefill workloads")
     ap.add_argument("--no-flush", action="store_true", help="do not evict the Infinity Cache between steps")
     ap.add_argument("--copy-calibration", action="store_true", help="run one 1 GiB copy (counter scaling) and exit")
@@ -262,6 +265,25 @@ def main():
                          "state_bytes_per_call": st_buf.numel() * 4, "ms_per_call": sms,
                          "tokens_per_s": tokens / (sms * 1e-3), "overhead_vs_plain": sms / ms - 1.0}
         del st_buf
+
+    # ---------------- the same workload through the fused entry point: the log-decay from its gate
+    # pre-activation, q and k normalised in the kernel, an output gate on o
+    if not args.no_fused:
+        dr = datagen.prefill_preactivations(w.seed, w.B, w.T, w.H, w.dk, w.dv, w.dtype, w.h0_std)
+        gr = {key: to_dev(dr[key]) for key in ("q", "k", "v", "x", "beta", "z")}
+        del dr
+
+        def fstep(_i):
+            kda.kda_chunked_forward_fused(gr["q"], gr["k"], gr["v"], None, gr["beta"], g["h0"], gate_x=gr["x"],
+                                          gate_scale=5.0, normalize_qk=True, out_gate=gr["z"], chunk=w.chunk, o=o,
+                                          hT=hT)
+
+        fstep(0)
+        torch.cuda.synchronize()
+        fms, _ = time_launches(fstep, args.steps, None if args.no_flush else flush)
+        out["fused"] = {"gate": "-5 sigmoid(x) in the kernel", "normalize_qk": True, "out_gate": True,
+                        "ms_per_call": fms, "tokens_per_s": tokens / (fms * 1e-3), "overhead_vs_plain": fms / ms - 1.0}
+        del gr
 
     # ---------------- decode
     if not args.no_decode:

@@ -10,6 +10,8 @@ entry points' names:
 * ``kda_chunked_forward_with_states`` / ``kda_chunked_forward_varlen_with_states`` -- the same,
   also keeping the state every N tokens (prefix states for a serving cache)
 * ``kda_decode_step``            -- one token per sequence, state updated in place
+* ``kda_chunked_forward_fused`` / ``kda_decode_step_fused`` -- with the gate formed from its
+  pre-activation, q and k normalised, and an output gate, inside the kernels
 
 Importing this package fails loudly when ``libkda.so`` has not been built
 (``python gated_delta_rule_94_amd/build.py``).
@@ -31,6 +33,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "K
 EXPORTS = (
     "kda_status_string", "kda_version", "kda_chunked_forward_workspace_bytes", "kda_chunked_forward_plan",
     "kda_chunked_forward", "kda_chunked_forward_with_states", "kda_chunked_forward_varlen_with_states",
+    "kda_chunked_forward_fused", "kda_decode_step_fused",
     "kda_chunked_forward_profiled", "kda_chunked_forward_varlen", "kda_chunked_forward_varlen_workspace_bytes",
     "kda_decode_step",
 )
@@ -62,6 +65,17 @@ _lib.kda_chunked_forward_varlen.argtypes = [_vp] * 8 + [_vp, _i32, _i32, _i32, _
 _lib.kda_chunked_forward_varlen.restype = _i32
 _lib.kda_decode_step.argtypes = [_vp] * 7 + [_i32] * 4 + [_i32, _vp]
 _lib.kda_decode_step.restype = _i32
+
+
+class Fusion(ctypes.Structure):
+    """kda_fusion: gate pre-activation (g = -gate_scale * sigmoid(gate_x)), q/k normalisation, output gate."""
+    _fields_ = [("gate_x", _vp), ("gate_scale", ctypes.c_float), ("normalize_qk", _i32), ("out_gate", _vp)]
+
+
+_lib.kda_chunked_forward_fused.argtypes = [_vp] * 8 + [ctypes.POINTER(Fusion)] + [_i32] * 7 + [_vp, _sz, _vp]
+_lib.kda_chunked_forward_fused.restype = _i32
+_lib.kda_decode_step_fused.argtypes = [_vp] * 7 + [ctypes.POINTER(Fusion)] + [_i32] * 5 + [_vp]
+_lib.kda_decode_step_fused.restype = _i32
 
 
 class KDAError(RuntimeError):
@@ -209,6 +223,41 @@ def kda_chunked_forward_with_states(q, k, v, g, beta, h0=None, *, state_every: i
     return o, hT, states
 
 
+def _fusion(gate_x, gate_scale, normalize_qk, out_gate):
+    return Fusion(_ptr(gate_x), float(gate_scale), 1 if normalize_qk else 0, _ptr(out_gate))
+
+
+def kda_chunked_forward_fused(q, k, v, g, beta, h0=None, *, gate_x=None, gate_scale: float = 5.0,
+                              normalize_qk: bool = False, out_gate=None, chunk: int = 64, o=None, hT=None,
+                              want_hT: bool = True, workspace=None, stream=None):
+    """kda_chunked_forward with the fused steps: gate_x (like g) gives g = -gate_scale * sigmoid(gate_x)
+    and g is then not read (may be None); normalize_qk L2-normalises q and k over d_k; out_gate (like o)
+    multiplies o elementwise.  Returns (o, hT)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("g", g, (B, T, H, dk)),
+                         ("gate_x", gate_x, (B, T, H, dk)), ("v", v, (B, T, H, dv)), ("beta", beta, (B, T, H)),
+                         ("out_gate", out_gate, (B, T, H, dv))):
+        _check(name, t, shp, dt, dev)
+    _check("h0", h0, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check("o", o, (B, T, H, dv), dt, dev)
+    if hT is None and want_hT:
+        hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check("hT", hT, (B, H, dk, dv), torch.float32, dev)
+    ws_bytes = _lib.kda_chunked_forward_workspace_bytes(B, T, H, dk, dv, chunk, _dtype_code(q))
+    ws = _workspace(workspace, ws_bytes, dev)
+    fu = _fusion(gate_x, gate_scale, normalize_qk, out_gate)
+    st = _lib.kda_chunked_forward_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
+                                        ctypes.byref(fu), B, T, H, dk, dv, chunk, _dtype_code(q), _ptr(ws),
+                                        _nbytes(ws), _stream(stream))
+    if st:
+        raise KDAError("kda_chunked_forward_fused", st)
+    return o, hT
+
+
 def kda_chunked_forward_profiled(q, k, v, g, beta, h0, o, hT, *, chunk: int = 64, workspace=None, stream=None):
     """kda_chunked_forward into preallocated o / hT (hT may be None), returning the two kernels'
     durations in ms (intra-chunk, chain) from HIP events on the stream; synchronises the stream."""
@@ -313,4 +362,27 @@ def kda_decode_step(q, k, v, g, beta, state, *, o=None, stream=None):
                               _dtype_code(q), _stream(stream))
     if st:
         raise KDAError("kda_decode_step", st)
+    return o
+
+
+def kda_decode_step_fused(q, k, v, g, beta, state, *, gate_x=None, gate_scale: float = 5.0,
+                          normalize_qk: bool = False, out_gate=None, o=None, stream=None):
+    """kda_decode_step with the fused steps (see kda_chunked_forward_fused): gate_x [B,H,dk],
+    out_gate [B,H,dv].  Returns o [B,H,dv]."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, shp in (("q", q, (B, H, dk)), ("k", k, (B, H, dk)), ("g", g, (B, H, dk)),
+                         ("gate_x", gate_x, (B, H, dk)), ("v", v, (B, H, dv)), ("beta", beta, (B, H)),
+                         ("out_gate", out_gate, (B, H, dv))):
+        _check(name, t, shp, dt, dev)
+    _check("state", state, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+    _check("o", o, (B, H, dv), dt, dev)
+    fu = _fusion(gate_x, gate_scale, normalize_qk, out_gate)
+    st = _lib.kda_decode_step_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+                                    ctypes.byref(fu), B, H, dk, dv, _dtype_code(q), _stream(stream))
+    if st:
+        raise KDAError("kda_decode_step_fused", st)
     return o

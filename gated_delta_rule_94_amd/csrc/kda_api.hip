@@ -28,6 +28,23 @@ kda_status check_prefill(const void* q, const void* k, const void* v, const void
   return KDA_OK;
 }
 
+// Fused steps: a gate scale in (0, 5] with a gate pre-activation, aligned pointers.  Fills the
+// internal description and returns the pointer the kernels read as g.
+bool fusion_ok(const kda_fusion* f, const void* g, kda::Fusion& out, const void*& g_eff) {
+  out = kda::Fusion();
+  g_eff = g;
+  if (!f) return true;
+  if (f->gate_x) {
+    if (!(f->gate_scale > 0.f && f->gate_scale <= 5.f) || !aligned16(f->gate_x)) return false;
+    out.gate_scale = f->gate_scale;
+    g_eff = f->gate_x;
+  }
+  if (f->out_gate && !aligned16(f->out_gate)) return false;
+  out.normalize_qk = f->normalize_qk != 0;
+  out.out_gate = f->out_gate;
+  return true;
+}
+
 // Snapshot buffer and interval: a 16-byte-aligned buffer and a positive multiple of the chunk.
 bool states_ok(const float* states, int every, int chunk) {
   return aligned16(states) && every > 0 && chunk > 0 && every % chunk == 0;
@@ -84,13 +101,19 @@ bool workspace_ok(void* ws, size_t have, size_t need) {
 }
 }  // namespace
 
-kda_status kda_chunked_forward_with_states(const void* q, const void* k, const void* v, const void* g,
-                                           const void* beta, const float* h0, void* o, float* hT, float* states,
-                                           int state_every, int B, int T, int H, int d_k, int d_v, int chunk,
-                                           kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+kda_status chunked_forward_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                const float* h0, void* o, float* hT, float* states, int state_every,
+                                const kda_fusion* fusion, int B, int T, int H, int d_k, int d_v, int chunk,
+                                kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
   if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
-  const kda_status st = check_prefill(q, k, v, g, beta, h0, o, hT, B * T, H, d_k, d_v, chunk, dt);
+  kda::Fusion fu;
+  const void* g_eff = g;
+  if (!fusion_ok(fusion, g, fu, g_eff)) return KDA_ERR_INVALID_ARG;
+  const kda_status st = check_prefill(q, k, v, g_eff, beta, h0, o, hT, B * T, H, d_k, d_v, chunk, dt);
   if (st != KDA_OK) return st;
   if (states && !states_ok(states, state_every, chunk)) return KDA_ERR_INVALID_ARG;
   if (B == 0) return KDA_OK;
@@ -98,7 +121,7 @@ kda_status kda_chunked_forward_with_states(const void* q, const void* k, const v
   if (!workspace_ok(workspace, workspace_bytes, kda_chunked_forward_workspace_bytes(B, T, H, d_k, d_v, chunk, dt)))
     return KDA_ERR_WORKSPACE;
   kda::PrefillArgs a;
-  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.q = q; a.k = k; a.v = v; a.g = g_eff; a.beta = beta;
   a.h0 = h0; a.o = o; a.hT = hT;
   a.cu_seqlens = nullptr;
   a.num_seqs = B;
@@ -108,12 +131,32 @@ kda_status kda_chunked_forward_with_states(const void* q, const void* k, const v
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   a.stream = hip_stream;
+  a.fusion = fu;
   if (states && T / state_every > 0) {
     a.states = states;
     a.state_every = state_every;
     a.max_states = T / state_every;
   }
   return kda::launch_chunked_forward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunked_forward_with_states(const void* q, const void* k, const void* v, const void* g,
+                                           const void* beta, const float* h0, void* o, float* hT, float* states,
+                                           int state_every, int B, int T, int H, int d_k, int d_v, int chunk,
+                                           kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return chunked_forward_impl(q, k, v, g, beta, h0, o, hT, states, state_every, nullptr, B, T, H, d_k, d_v, chunk, dt,
+                              workspace, workspace_bytes, hip_stream);
+}
+
+kda_status kda_chunked_forward_fused(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                     const float* h0, void* o, float* hT, const kda_fusion* fusion, int B, int T,
+                                     int H, int d_k, int d_v, int chunk, kda_dtype dt, void* workspace,
+                                     size_t workspace_bytes, void* hip_stream) {
+  return chunked_forward_impl(q, k, v, g, beta, h0, o, hT, nullptr, 0, fusion, B, T, H, d_k, d_v, chunk, dt,
+                              workspace, workspace_bytes, hip_stream);
 }
 
 kda_status kda_chunked_forward(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -205,21 +248,25 @@ kda_status kda_chunked_forward_varlen(const void* q, const void* k, const void* 
                                                 workspace_bytes, hip_stream);
 }
 
-kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta, float* state,
-                           void* o, int B, int H, int d_k, int d_v, kda_dtype dt, void* hip_stream) {
+kda_status kda_decode_step_fused(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                 float* state, void* o, const kda_fusion* fusion, int B, int H, int d_k, int d_v,
+                                 kda_dtype dt, void* hip_stream) {
   if (B < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARG;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_INVALID_ARG;
   if ((int64_t)B * H > INT32_MAX / 2) return KDA_ERR_UNSUPPORTED;
+  kda::Fusion fu;
+  const void* g_eff = g;
+  if (!fusion_ok(fusion, g, fu, g_eff)) return KDA_ERR_INVALID_ARG;
   if (B > 0) {
-    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) || !aligned16(state) ||
-        !aligned16(o))
+    if (!q || !k || !v || !g_eff || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g_eff) || !aligned16(beta) ||
+        !aligned16(state) || !aligned16(o))
       return KDA_ERR_INVALID_ARG;
   }
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
   if (B == 0) return KDA_OK;
   kda::DecodeArgs a;
-  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.q = q; a.k = k; a.v = v; a.g = g_eff; a.beta = beta;
   a.state = state;
   a.o = o;
   a.units = B * H;
@@ -227,7 +274,13 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
   a.dv = d_v;
   a.f32 = dt == KDA_F32;
   a.stream = hip_stream;
+  a.fusion = fu;
   return kda::launch_decode_step(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta, float* state,
+                           void* o, int B, int H, int d_k, int d_v, kda_dtype dt, void* hip_stream) {
+  return kda_decode_step_fused(q, k, v, g, beta, state, o, nullptr, B, H, d_k, d_v, dt, hip_stream);
 }
 
 }  // extern "C"

@@ -22,6 +22,8 @@
 // next chunk's products; U likewise.  The copy waves stream records from HBM into double-buffered
 // LDS two chunks ahead (two register staging sets): while the chain waves compute chunk n, the
 // copy waves write chunk n+1 into the other buffer and load chunk n+2.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_record.h"
@@ -41,6 +43,7 @@ struct ChainParams {
   float* send;            // summary launch: [b_g | M_g] of segments 0..nseg-2 [units][nseg-1][DK][DV+DK]
   float* states;          // or NULL: the state after every `every` tokens of a sequence,
   int every, max_states;  // [units][max_states][DK][DV]
+  const void* z;          // or NULL: an output gate, laid out and typed like o, multiplying o
 };
 
 template <bool F32, int DK, int DV, int C, int WS>
@@ -216,6 +219,18 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     const int len = (int)((t_end - t0) < C ? (t_end - t0) : C);
     const int64_t obase = (t0 * H + h) * DV;  // output element of (token t0, head h, column 0): uniform
     if (!chain) return;
+    // output gate of this lane's outputs, loaded now and used at the stores (rows past the range
+    // re-read its last token, in bounds)
+    using ZV = std::conditional_t<F32, float4, uint2>;
+    ZV zv[NT];
+    const bool gz = !SUM && p.z != nullptr;
+    if (gz) {
+#pragma unroll
+      for (int bt = 0; bt < NT; ++bt) {
+        const int row = 16 * bt + lo < len ? 16 * bt + lo : len - 1;
+        zv[bt] = *reinterpret_cast<const ZV*>(static_cast<const E*>(p.z) + obase + (int64_t)row * ostride + ocol);
+      }
+    }
     // Phases, each issuing the LDS fragment loads of the next so that LDS latency hides behind
     // MFMAs; the state update (the chunk-to-chunk critical path) comes first:
     //   1  -W fragments, U~                   2  U = U~ - W S            | K'^T fragments, gamma
@@ -303,6 +318,17 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     for (int bt = 0; bt < NT; ++bt) {
 #pragma unroll
       for (int sk = 0; sk < O::nks(16 * (bt + 1)); ++sk) Ot[bt] = O::mma(uf[sk], pf[bt][sk], Ot[bt]);
+      if (gz) {
+        float zf[4];
+        if constexpr (F32) {
+          zf[0] = zv[bt].x; zf[1] = zv[bt].y; zf[2] = zv[bt].z; zf[3] = zv[bt].w;
+        } else {
+          zf[0] = __uint_as_float(zv[bt].x << 16); zf[1] = __uint_as_float(zv[bt].x & 0xffff0000u);
+          zf[2] = __uint_as_float(zv[bt].y << 16); zf[3] = __uint_as_float(zv[bt].y & 0xffff0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Ot[bt][i] *= zf[i];
+      }
       if (16 * bt + lo < len) {
         const int64_t oi = obase + (int64_t)(16 * bt + lo) * ostride + ocol;
         if constexpr (F32) {
@@ -406,6 +432,7 @@ static hipError_t launch_chain_impl(const ChainLaunch& L) {
   p.units = L.units; p.H = L.H; p.T = L.T; p.nch = L.nch; p.dv = DV;
   p.nseg = L.nseg > 1 ? L.nseg : 1; p.seg_len = L.seg_len; p.sstart = L.sstart; p.send = L.send;
   p.states = SUM ? nullptr : L.states; p.every = L.every; p.max_states = L.max_states;
+  p.z = SUM ? nullptr : L.out_gate;
   const int64_t su = (int64_t)L.units * (SUM ? p.nseg - 1 : p.nseg);
   const int64_t grid = ((su + 7) / 8) * 8 * ((SUM ? DV + DK : DV) / WS);
   if (su <= 0 || grid > INT32_MAX) return hipErrorInvalidValue;

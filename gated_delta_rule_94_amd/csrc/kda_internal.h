@@ -6,6 +6,16 @@
 
 namespace kda {
 
+// Optional steps fused on either side of the recurrence (all off by default):
+//   gate_scale > 0: the g pointer holds the gate pre-activation x, and g = -gate_scale sigmoid(x);
+//   normalize_qk:   q and k are L2-normalised over d_k per (token, head) in the kernel;
+//   out_gate:       o is multiplied elementwise by this tensor (laid out and typed like o).
+struct Fusion {
+  float gate_scale = 0.f;
+  bool normalize_qk = false;
+  const void* out_gate = nullptr;
+};
+
 struct DecodeArgs {
   const void *q, *k, *v, *g, *beta;
   float* state;
@@ -14,6 +24,7 @@ struct DecodeArgs {
   int dk, dv;
   bool f32;
   void* stream;
+  Fusion fusion;
 };
 
 struct PrefillArgs {
@@ -32,6 +43,7 @@ struct PrefillArgs {
   hipEvent_t* events = nullptr;  // optional: [3] recorded before the intra kernel, between the kernels, after the chain
   float* states = nullptr;       // optional state snapshots [num_seqs][H][max_states][dk][dv]
   int state_every = 0, max_states = 0;
+  Fusion fusion;
 };
 
 // intra-chunk kernel launch (kda_intra.hip)
@@ -45,6 +57,8 @@ struct IntraLaunch {
   bool f32;
   int grid;
   void* stream;
+  float gate_scale = 0.f;  // > 0: g holds the gate pre-activation (Fusion)
+  bool normalize_qk = false;
 };
 
 // chain kernel launch (kda_chain.hip)
@@ -70,6 +84,7 @@ struct ChainLaunch {
   // chunk): [units][max_states][dk][dv]
   float* states = nullptr;
   int every = 0, max_states = 0;
+  const void* out_gate = nullptr;  // o is multiplied by it elementwise (Fusion)
   void* stream;
 };
 

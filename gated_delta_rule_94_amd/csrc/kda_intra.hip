@@ -38,6 +38,8 @@
 // results go to memory are formed so that each lane holds four consecutive elements of a row.
 // LDS rows of 8-byte fragment pieces have strides that are odd multiples of 8 bytes (72, 136),
 // so the sixteen lanes of one fragment read fall on distinct banks.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_record.h"
@@ -50,6 +52,8 @@ struct IntraParams {
   const int32_t* chunk0;  // first chunk of each packed sequence [num_seqs + 1] (with cu), else NULL
   unsigned char* ws;      // records
   int num_seqs, H, T, nch;  // T: tokens per sequence (no cu) or T_total; nch: chunks per sequence (no cu)
+  float gate_scale;         // > 0: g holds the gate pre-activation x, and g = -gate_scale sigmoid(x)
+  int normalize_qk;         // nonzero: q and k are L2-normalised over d_k per (token, head)
 };
 
 template <bool F32, int DK, int DV, int C>
@@ -232,6 +236,7 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   constexpr int NQ = Cf::NQ;
   Raw2<F32> rg[NQ][2], rq[NQ][2], rk[NQ][2], rv[8];
   float rb;
+  bool rok[2];  // rows r0, r0 + 1 lie in the chunk (the others are zero padding)
   {
     const int chunk = item / H;
     const int h = item - chunk * H;
@@ -247,6 +252,8 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
     // loads are unconditional: rows past the chunk's end (len >= 1) and idle threads read a valid
     // element, then take zero
     const int last = cp.len - 1;
+    rok[0] = pact && r0 <= last;
+    rok[1] = pact && r0 + 1 <= last;
 #pragma unroll
     for (int qt = 0; qt < NQ; ++qt)
 #pragma unroll
@@ -276,11 +283,22 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   // for this thread's rows and channels, Tb = the sub-tile's total decay (to LDS as Eend); then
   // e^{R_b - G_r} = 1 / E and the suffix product e^{G_end - G_r} = Tb / E.
   const float m1 = rp >= 1 ? 1.f : 0.f, m2 = rp >= 2 ? 1.f : 0.f, m4 = rp >= 4 ? 1.f : 0.f;
-  auto scan = [&](int qt, float (&Ef)[2][2], float (&Tb)[2]) {
+  // the decay alpha = e^g of a row; with a gate pre-activation x, g = -A sigmoid(x) and padding
+  // rows (x loaded as 0) keep alpha = 1
+  const float gA = p.gate_scale;
+  auto decay = [&](auto gate_, float x, bool ok) -> float {
+    if constexpr (decltype(gate_)::value) {
+      const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-x));
+      return ok ? __expf(-gA * sg) : 1.f;
+    } else {
+      return __expf(x);
+    }
+  };
+  auto scan_ = [&](auto gate_, int qt, float (&Ef)[2][2], float (&Tb)[2]) {
     const float2 g0 = rg[qt][0].f(), g1 = rg[qt][1].f();
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
-      const float a0 = __expf(ch ? g0.y : g0.x), a1 = __expf(ch ? g1.y : g1.x);
+      const float a0 = decay(gate_, ch ? g0.y : g0.x, rok[0]), a1 = decay(gate_, ch ? g1.y : g1.x, rok[1]);
       float x = a0 * a1;  // this row pair's product; inclusive scan over the 8 row pairs
       x *= row_shr_or1<1>(x, m1);
       x *= row_shr_or1<2>(x, m2);
@@ -291,8 +309,40 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
     }
     if (pact && rp == 7) *reinterpret_cast<float2*>(Eend + psb * DK + QW * qt + 2 * cpl) = make_float2(Tb[0], Tb[1]);
   };
+  const bool gated = gA > 0.f;  // uniform: one scan or the other, by a scalar branch
+  auto scan = [&](int qt, float (&Ef)[2][2], float (&Tb)[2]) {
+    if (gated) scan_(std::true_type{}, qt, Ef, Tb);
+    else scan_(std::false_type{}, qt, Ef, Tb);
+  };
   float Ef[2][2], Tb[2];  // this quarter's: [row j][channel]
   scan(0, Ef, Tb);
+  // L2 norms of this thread's q and k rows over d_k: 8 channels here, the other 120 in the lanes
+  // with the same row pair (lane bits 3-5) and in the sibling wave (through LDS, in the V^T area,
+  // which is first written in the last quarter)
+  float qn[2] = {1.f, 1.f}, kn[2] = {1.f, 1.f};
+  float* Nrm = reinterpret_cast<float*>(Vt);  // [sub-tile][row pair][4][2 halves]
+  const bool norm = p.normalize_qk != 0;
+  if (norm) {
+    float ss[4] = {0.f, 0.f, 0.f, 0.f};  // q row 0, q row 1, k row 0, k row 1
+#pragma unroll
+    for (int qt = 0; qt < NQ; ++qt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float2 a = rq[qt][j].f(), b = rk[qt][j].f();
+        ss[j] += a.x * a.x + a.y * a.y;
+        ss[2 + j] += b.x * b.x + b.y * b.y;
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ss[i] += __shfl_xor(ss[i], 8);
+      ss[i] += __shfl_xor(ss[i], 16);
+      ss[i] += __shfl_xor(ss[i], 32);
+    }
+    if (pact && (lane >> 3) == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Nrm[((psb * 8 + rp) * 4 + i) * 2 + (wave & 1)] = ss[i];
+    }
+  }
   if constexpr (CP > C) {  // token pads of K'^T and (K . Gamma)^T are zero
     for (int e = tid; e < DK * (CP - C); e += 512) {
       const int c = e / (CP - C), t = C + e % (CP - C);
@@ -304,6 +354,15 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
 #pragma unroll
   for (int sl = 0; sl < NSLOT; ++sl) acc[sl] = zero4();
   __syncthreads();
+  if (norm && pact) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float2 a = *reinterpret_cast<const float2*>(Nrm + ((psb * 8 + rp) * 4 + j) * 2);
+      const float2 b = *reinterpret_cast<const float2*>(Nrm + ((psb * 8 + rp) * 4 + 2 + j) * 2);
+      qn[j] = __builtin_amdgcn_rsqf(a.x + a.y + 1e-12f);
+      kn[j] = __builtin_amdgcn_rsqf(b.x + b.y + 1e-12f);
+    }
+  }
 
 #pragma unroll
   for (int qt = 0; qt < NQ; ++qt) {
@@ -318,6 +377,12 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
         qf[j][1] = qq.y;
         kf[j][0] = kk.x;
         kf[j][1] = kk.y;
+        if (norm) {
+          qf[j][0] *= qn[j];
+          qf[j][1] *= qn[j];
+          kf[j][0] *= kn[j];
+          kf[j][1] *= kn[j];
+        }
         iE[j][0] = __builtin_amdgcn_rcpf(Ef[j][0]);
         iE[j][1] = __builtin_amdgcn_rcpf(Ef[j][1]);
       }
@@ -596,6 +661,7 @@ static hipError_t launch_intra_impl(const IntraLaunch& L) {
   p.q = L.q; p.k = L.k; p.v = L.v; p.g = L.g; p.beta = L.beta;
   p.cu = L.cu; p.chunk0 = L.chunk0; p.ws = L.records;
   p.num_seqs = L.num_seqs; p.H = L.H; p.T = L.T; p.nch = L.nch;
+  p.gate_scale = L.gate_scale; p.normalize_qk = L.normalize_qk ? 1 : 0;
   hipLaunchKernelGGL((intra_chunk_kernel<F32, DK, DV, C>), dim3(L.grid), dim3(512), 0, (hipStream_t)L.stream, p);
   return hipGetLastError();
 }

@@ -105,6 +105,8 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
     L.num_seqs = a.num_seqs; L.H = a.H; L.T = a.T; L.nch = nch;
     L.dk = a.dk; L.dv = a.dv; L.chunk = C; L.f32 = a.f32;
     L.grid = (int)items;  // one 8-wave workgroup per (chunk, head) record (bound; extra ones exit)
+    L.gate_scale = a.fusion.gate_scale;
+    L.normalize_qk = a.fusion.normalize_qk;
     L.stream = a.stream;
     e = launch_intra(L);
     if (e != hipSuccess) return e;
@@ -118,6 +120,7 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
   K.ws = pl.ws;
   K.stream = a.stream;
   K.states = a.states; K.every = a.state_every; K.max_states = a.max_states;
+  K.out_gate = a.fusion.out_gate;
   if (pl.nseg > 1) {
     unsigned char* seg = records + max_chunks * a.H * rb;
     float* sstart = reinterpret_cast<float*>(seg);

@@ -89,6 +89,28 @@ kda_status kda_chunked_forward_plan(int B, int T, int H, int d_k, int d_v, int c
                                     int* value_slice, int* segments, int* segment_chunks);
 
 /*
+ * Optional steps fused on either side of the recurrence, for the *_fused entry
+ * points (a NULL kda_fusion pointer, or all fields zero, means none):
+ *  - gate_x: the gate pre-activation, laid out and typed like g.  The kernel
+ *    then forms the log-decay through a scaled sigmoid, g = -gate_scale *
+ *    sigmoid(gate_x) (technical-report page, "Architecture at a glance": the
+ *    lower bound on the log-decay), and the g argument is not read (may be
+ *    NULL).  gate_scale must lie in (0, 5]: the kernels rely on g >= -5.
+ *  - normalize_qk: nonzero L2-normalises q and k over d_k per (token, head),
+ *    x / sqrt(sum x^2 + 1e-12), in fp32 in the kernel.
+ *  - out_gate: an output gate z laid out and typed like o; o is multiplied by
+ *    z elementwise before it is stored (same page: the input-dependent output
+ *    gate; z is taken as given -- its projection needs trained weights).
+ * All pointers are device memory, 16-byte aligned.
+ */
+typedef struct {
+  const void* gate_x;
+  float gate_scale;
+  int normalize_qk;
+  const void* out_gate;
+} kda_fusion;
+
+/*
  * Chunked prefill over B sequences of T tokens each.
  *   q, k, g [B,T,H,d_k], v [B,T,H,d_v], beta [B,T,H]   (dtype dt)   in
  *   h0 [B,H,d_k,d_v] fp32                               in, or NULL for a zero initial state
@@ -122,6 +144,17 @@ kda_status kda_chunked_forward_with_states(const void* q, const void* k, const v
                                            const void* beta, const float* h0, void* o, float* hT, float* states,
                                            int state_every, int B, int T, int H, int d_k, int d_v, int chunk,
                                            kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * kda_chunked_forward with the fused steps of *fusion (see kda_fusion); the
+ * arguments, workspace and errors are otherwise those of kda_chunked_forward.
+ * KDA_ERR_INVALID_ARG also for a gate_scale outside (0, 5] with gate_x, or a
+ * misaligned gate_x / out_gate.
+ */
+kda_status kda_chunked_forward_fused(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                     const float* h0, void* o, float* hT, const kda_fusion* fusion, int B, int T,
+                                     int H, int d_k, int d_v, int chunk, kda_dtype dt, void* workspace,
+                                     size_t workspace_bytes, void* hip_stream);
 
 /*
  * Profiling form of kda_chunked_forward: the same arguments, checks and
@@ -187,6 +220,14 @@ size_t kda_chunked_forward_varlen_workspace_bytes(int num_seqs, int T_total, int
  */
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta, float* state,
                            void* o, int B, int H, int d_k, int d_v, kda_dtype dt, void* hip_stream);
+
+/*
+ * kda_decode_step with the fused steps of *fusion (see kda_fusion): gate_x
+ * [B,H,d_k], out_gate [B,H,d_v].  Otherwise as kda_decode_step.
+ */
+kda_status kda_decode_step_fused(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                 float* state, void* o, const kda_fusion* fusion, int B, int H, int d_k, int d_v,
+                                 kda_dtype dt, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -129,6 +129,36 @@ def test_states_validation():
     assert fv(states=FAKE + 8) == INVALID
 
 
+def test_fused_validation():
+    """The fused steps are checked before anything would run: a gate scale in (0, 5] with a gate
+    pre-activation (g itself may then be NULL), aligned pointers."""
+    lib = kda.lib()
+
+    def ff(gate_x=FAKE, scale=5.0, norm=1, out_gate=FAKE, g=None, ws=FAKE):
+        fu = kda.Fusion(gate_x, scale, norm, out_gate)
+        return lib.kda_chunked_forward_fused(FAKE, FAKE, FAKE, g, FAKE, None, FAKE, None, ctypes.byref(fu),
+                                             1, 256, 2, 64, 64, 64, 1, ws, 1 << 40, None)
+
+    def fd(gate_x=FAKE, scale=5.0, out_gate=FAKE, g=None):
+        fu = kda.Fusion(gate_x, scale, 0, out_gate)
+        return lib.kda_decode_step_fused(FAKE, FAKE, FAKE, g, FAKE, FAKE, FAKE, ctypes.byref(fu), 0, 2, 64, 64, 1,
+                                         None)
+
+    assert ff(scale=0.0) == INVALID
+    assert ff(scale=5.5) == INVALID
+    assert ff(scale=-1.0) == INVALID
+    assert ff(gate_x=FAKE + 2) == INVALID
+    assert ff(out_gate=FAKE + 4) == INVALID
+    assert ff(gate_x=None, g=None) == INVALID      # no gate at all
+    assert ff(ws=None) == 3                        # valid arguments (g NULL with gate_x): then no workspace
+    assert ff(gate_x=None, g=FAKE, scale=0.0, ws=None) == 3  # no gate pre-activation: the scale is ignored
+    assert fd(scale=6.0) == INVALID
+    assert fd() == OK                              # B = 0: nothing to do
+    nofu = lib.kda_chunked_forward_fused(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, 1, 256, 2, 64, 64,
+                                         64, 1, None, 0, None)
+    assert nofu == 3                               # a NULL fusion is the plain call
+
+
 def test_varlen_validation():
     lib = kda.lib()
     call = lambda cu, N, Tt, ms, ptr=FAKE: lib.kda_chunked_forward_varlen(ptr, ptr, ptr, ptr, ptr, None, ptr, None,
