@@ -12,6 +12,7 @@ entry points' names:
 * ``kda_decode_step``            -- one token per sequence, state updated in place
 * ``kda_chunked_forward_fused`` / ``kda_decode_step_fused`` -- with the gate formed from its
   pre-activation, q and k normalised, and an output gate, inside the kernels
+* ``kda_chunked_forward_ex`` / ``kda_chunked_forward_varlen_ex`` -- snapshots and fused steps together
 
 Importing this package fails loudly when ``libkda.so`` has not been built
 (``python gated_delta_rule_94_amd/build.py``).
@@ -33,7 +34,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "K
 EXPORTS = (
     "kda_status_string", "kda_version", "kda_chunked_forward_workspace_bytes", "kda_chunked_forward_plan",
     "kda_chunked_forward", "kda_chunked_forward_with_states", "kda_chunked_forward_varlen_with_states",
-    "kda_chunked_forward_fused", "kda_decode_step_fused",
+    "kda_chunked_forward_fused", "kda_decode_step_fused", "kda_chunked_forward_ex", "kda_chunked_forward_varlen_ex",
     "kda_chunked_forward_profiled", "kda_chunked_forward_varlen", "kda_chunked_forward_varlen_workspace_bytes",
     "kda_decode_step",
 )
@@ -76,6 +77,11 @@ _lib.kda_chunked_forward_fused.argtypes = [_vp] * 8 + [ctypes.POINTER(Fusion)] +
 _lib.kda_chunked_forward_fused.restype = _i32
 _lib.kda_decode_step_fused.argtypes = [_vp] * 7 + [ctypes.POINTER(Fusion)] + [_i32] * 5 + [_vp]
 _lib.kda_decode_step_fused.restype = _i32
+_lib.kda_chunked_forward_ex.argtypes = [_vp] * 9 + [_i32, ctypes.POINTER(Fusion)] + [_i32] * 7 + [_vp, _sz, _vp]
+_lib.kda_chunked_forward_ex.restype = _i32
+_lib.kda_chunked_forward_varlen_ex.argtypes = ([_vp] * 9 + [_i32, ctypes.POINTER(Fusion), _vp] + [_i32] * 8 +
+                                               [_vp, _sz, _vp])
+_lib.kda_chunked_forward_varlen_ex.restype = _i32
 
 
 class KDAError(RuntimeError):
@@ -386,3 +392,78 @@ def kda_decode_step_fused(q, k, v, g, beta, state, *, gate_x=None, gate_scale: f
     if st:
         raise KDAError("kda_decode_step_fused", st)
     return o
+
+
+def kda_chunked_forward_ex(q, k, v, g, beta, h0=None, *, state_every: int = 0, states=None, gate_x=None,
+                           gate_scale: float = 5.0, normalize_qk: bool = False, out_gate=None, chunk: int = 64,
+                           o=None, hT=None, want_hT: bool = True, workspace=None, stream=None):
+    """kda_chunked_forward with state snapshots (state_every > 0) and the fused steps together.
+    Returns (o, hT, states or None)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("g", g, (B, T, H, dk)),
+                         ("gate_x", gate_x, (B, T, H, dk)), ("v", v, (B, T, H, dv)), ("beta", beta, (B, T, H)),
+                         ("out_gate", out_gate, (B, T, H, dv))):
+        _check(name, t, shp, dt, dev)
+    _check("h0", h0, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check("o", o, (B, T, H, dv), dt, dev)
+    if hT is None and want_hT:
+        hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check("hT", hT, (B, H, dk, dv), torch.float32, dev)
+    if state_every > 0 and states is None:
+        states = torch.empty((B, H, T // state_every, dk, dv), dtype=torch.float32, device=dev)
+    if states is not None:
+        _check("states", states, (B, H, T // state_every, dk, dv), torch.float32, dev)
+    ws = _workspace(workspace, _lib.kda_chunked_forward_workspace_bytes(B, T, H, dk, dv, chunk, _dtype_code(q)), dev)
+    fu = _fusion(gate_x, gate_scale, normalize_qk, out_gate)
+    st = _lib.kda_chunked_forward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
+                                     _ptr(states), int(state_every), ctypes.byref(fu), B, T, H, dk, dv, chunk,
+                                     _dtype_code(q), _ptr(ws), _nbytes(ws), _stream(stream))
+    if st:
+        raise KDAError("kda_chunked_forward_ex", st)
+    return o, hT, states
+
+
+def kda_chunked_forward_varlen_ex(q, k, v, g, beta, cu_seqlens, max_seqlen: int, h0=None, *, state_every: int = 0,
+                                  states=None, gate_x=None, gate_scale: float = 5.0, normalize_qk: bool = False,
+                                  out_gate=None, chunk: int = 64, o=None, hT=None, want_hT: bool = True,
+                                  workspace=None, stream=None):
+    """kda_chunked_forward_varlen with state snapshots and the fused steps together (gate_x shaped like
+    q, out_gate like v).  Returns (o, hT, states or None)."""
+    Tt, H, dk = q.shape[-3:]
+    dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    dt, dev = q.dtype, q.device
+    lead = tuple(q.shape[:-3])
+    if lead not in ((), (1,)):
+        raise ValueError("varlen inputs are packed along one token axis (batch 1)")
+    for name, t, shp in (("q", q, lead + (Tt, H, dk)), ("k", k, lead + (Tt, H, dk)), ("g", g, lead + (Tt, H, dk)),
+                         ("gate_x", gate_x, lead + (Tt, H, dk)), ("v", v, lead + (Tt, H, dv)),
+                         ("beta", beta, lead + (Tt, H)), ("out_gate", out_gate, lead + (Tt, H, dv))):
+        _check(name, t, shp, dt, dev)
+    _check("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
+    _check("h0", h0, (N, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty(lead + (Tt, H, dv), dtype=dt, device=dev)
+    _check("o", o, lead + (Tt, H, dv), dt, dev)
+    if hT is None and want_hT:
+        hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _check("hT", hT, (N, H, dk, dv), torch.float32, dev)
+    slots = int(max_seqlen) // state_every if state_every > 0 else 0
+    if state_every > 0 and states is None:
+        states = torch.zeros((N, H, slots, dk, dv), dtype=torch.float32, device=dev)
+    if states is not None:
+        _check("states", states, (N, H, slots, dk, dv), torch.float32, dev)
+    ws_bytes = _lib.kda_chunked_forward_varlen_workspace_bytes(N, Tt, max_seqlen, H, dk, dv, chunk, _dtype_code(q))
+    ws = _workspace(workspace, ws_bytes, dev)
+    fu = _fusion(gate_x, gate_scale, normalize_qk, out_gate)
+    st = _lib.kda_chunked_forward_varlen_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o),
+                                            _ptr(hT), _ptr(states), int(state_every), ctypes.byref(fu),
+                                            _ptr(cu_seqlens), N, Tt, int(max_seqlen), H, dk, dv, chunk,
+                                            _dtype_code(q), _ptr(ws), _nbytes(ws), _stream(stream))
+    if st:
+        raise KDAError("kda_chunked_forward_varlen_ex", st)
+    return o, hT, states

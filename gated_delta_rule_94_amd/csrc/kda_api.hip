@@ -143,6 +143,14 @@ kda_status chunked_forward_impl(const void* q, const void* k, const void* v, con
 
 extern "C" {
 
+kda_status kda_chunked_forward_ex(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                  const float* h0, void* o, float* hT, float* states, int state_every,
+                                  const kda_fusion* fusion, int B, int T, int H, int d_k, int d_v, int chunk,
+                                  kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return chunked_forward_impl(q, k, v, g, beta, h0, o, hT, states, state_every, fusion, B, T, H, d_k, d_v, chunk, dt,
+                              workspace, workspace_bytes, hip_stream);
+}
+
 kda_status kda_chunked_forward_with_states(const void* q, const void* k, const void* v, const void* g,
                                            const void* beta, const float* h0, void* o, float* hT, float* states,
                                            int state_every, int B, int T, int H, int d_k, int d_v, int chunk,
@@ -204,16 +212,18 @@ kda_status kda_chunked_forward_profiled(const void* q, const void* k, const void
   return ok ? KDA_OK : KDA_ERR_HIP;
 }
 
-kda_status kda_chunked_forward_varlen_with_states(const void* q, const void* k, const void* v, const void* g,
-                                                  const void* beta, const float* h0, void* o, float* hT,
-                                                  float* states, int state_every, const int32_t* cu_seqlens,
-                                                  int num_seqs, int T_total, int max_seqlen, int H, int d_k, int d_v,
-                                                  int chunk, kda_dtype dt, void* workspace, size_t workspace_bytes,
-                                                  void* hip_stream) {
+kda_status kda_chunked_forward_varlen_ex(const void* q, const void* k, const void* v, const void* g,
+                                         const void* beta, const float* h0, void* o, float* hT, float* states,
+                                         int state_every, const kda_fusion* fusion, const int32_t* cu_seqlens,
+                                         int num_seqs, int T_total, int max_seqlen, int H, int d_k, int d_v, int chunk,
+                                         kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (num_seqs < 0 || T_total < 0 || max_seqlen < 0) return KDA_ERR_INVALID_ARG;
   if (num_seqs > 0 && (!cu_seqlens || max_seqlen > T_total)) return KDA_ERR_INVALID_ARG;
   if ((int64_t)num_seqs * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
-  const kda_status st = check_prefill(q, k, v, g, beta, h0, o, hT, T_total, H, d_k, d_v, chunk, dt);
+  kda::Fusion fu;
+  const void* g_eff = g;
+  if (!fusion_ok(fusion, g, fu, g_eff)) return KDA_ERR_INVALID_ARG;
+  const kda_status st = check_prefill(q, k, v, g_eff, beta, h0, o, hT, T_total, H, d_k, d_v, chunk, dt);
   if (st != KDA_OK) return st;
   if (states && !states_ok(states, state_every, chunk)) return KDA_ERR_INVALID_ARG;
   if (num_seqs == 0) return KDA_OK;
@@ -221,7 +231,7 @@ kda_status kda_chunked_forward_varlen_with_states(const void* q, const void* k, 
                     kda_chunked_forward_varlen_workspace_bytes(num_seqs, T_total, max_seqlen, H, d_k, d_v, chunk, dt)))
     return KDA_ERR_WORKSPACE;
   kda::PrefillArgs a;
-  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.q = q; a.k = k; a.v = v; a.g = g_eff; a.beta = beta;
   a.h0 = h0; a.o = o; a.hT = hT;
   a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs;
@@ -231,12 +241,24 @@ kda_status kda_chunked_forward_varlen_with_states(const void* q, const void* k, 
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   a.stream = hip_stream;
+  a.fusion = fu;
   if (states && max_seqlen / state_every > 0) {
     a.states = states;
     a.state_every = state_every;
     a.max_states = max_seqlen / state_every;
   }
   return kda::launch_chunked_forward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_chunked_forward_varlen_with_states(const void* q, const void* k, const void* v, const void* g,
+                                                  const void* beta, const float* h0, void* o, float* hT,
+                                                  float* states, int state_every, const int32_t* cu_seqlens,
+                                                  int num_seqs, int T_total, int max_seqlen, int H, int d_k, int d_v,
+                                                  int chunk, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                                                  void* hip_stream) {
+  return kda_chunked_forward_varlen_ex(q, k, v, g, beta, h0, o, hT, states, state_every, nullptr, cu_seqlens,
+                                       num_seqs, T_total, max_seqlen, H, d_k, d_v, chunk, dt, workspace,
+                                       workspace_bytes, hip_stream);
 }
 
 kda_status kda_chunked_forward_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,

@@ -157,6 +157,16 @@ kda_status kda_chunked_forward_fused(const void* q, const void* k, const void* v
                                      size_t workspace_bytes, void* hip_stream);
 
 /*
+ * kda_chunked_forward with both state snapshots (states, state_every: see
+ * kda_chunked_forward_with_states; states may be NULL) and fused steps
+ * (fusion: see kda_fusion; may be NULL).
+ */
+kda_status kda_chunked_forward_ex(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                  const float* h0, void* o, float* hT, float* states, int state_every,
+                                  const kda_fusion* fusion, int B, int T, int H, int d_k, int d_v, int chunk,
+                                  kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
  * Profiling form of kda_chunked_forward: the same arguments, checks and
  * results, plus kernel_ms[2] (host memory, non-NULL), which receives the
  * durations in milliseconds of the two stages of the call -- [0] the
@@ -203,6 +213,17 @@ kda_status kda_chunked_forward_varlen_with_states(const void* q, const void* k, 
                                                   int num_seqs, int T_total, int max_seqlen, int H, int d_k, int d_v,
                                                   int chunk, kda_dtype dt, void* workspace, size_t workspace_bytes,
                                                   void* hip_stream);
+
+/*
+ * kda_chunked_forward_varlen with both state snapshots (see
+ * kda_chunked_forward_varlen_with_states; states may be NULL) and fused steps
+ * (see kda_fusion; gate_x laid out like g and out_gate like o; may be NULL).
+ */
+kda_status kda_chunked_forward_varlen_ex(const void* q, const void* k, const void* v, const void* g,
+                                         const void* beta, const float* h0, void* o, float* hT, float* states,
+                                         int state_every, const kda_fusion* fusion, const int32_t* cu_seqlens,
+                                         int num_seqs, int T_total, int max_seqlen, int H, int d_k, int d_v, int chunk,
+                                         kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Workspace bytes kda_chunked_forward_varlen needs (0 = none). */
 size_t kda_chunked_forward_varlen_workspace_bytes(int num_seqs, int T_total, int max_seqlen, int H, int d_k, int d_v,

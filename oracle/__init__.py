@@ -220,3 +220,14 @@ def decode_step_fused(q, k, v, g, beta, state, *, x=None, gate_scale=5.0, normal
     o = decode_step(q64, k64, np.ascontiguousarray(_dec(v)), g64, np.ascontiguousarray(_dec(beta)), state,
                     nthreads=nthreads)
     return o * _dec(z) if z is not None else o
+
+
+def forward_varlen_fused(q, k, v, g, beta, cu_seqlens, h0=None, *, x=None, gate_scale=5.0, normalize_qk=False,
+                         z=None, want_o=True, want_hT=True, nthreads=None):
+    """forward_varlen() with the fused steps (see forward_fused).  Returns fp64 (o, hT)."""
+    q64, k64, g64 = _fused_inputs(q, k, g, x, gate_scale, normalize_qk)
+    o, hT = forward_varlen(q64, k64, np.ascontiguousarray(_dec(v)), g64, np.ascontiguousarray(_dec(beta)),
+                           cu_seqlens, h0, want_o=want_o, want_hT=want_hT, nthreads=nthreads)
+    if o is not None and z is not None:
+        o = o * _dec(z).reshape(o.shape)
+    return o, hT

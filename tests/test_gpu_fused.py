@@ -104,3 +104,50 @@ def test_fused_decode(dt, dk, dv):
         eo = o_err(host64(o)[:, None], o_ref[:, None])
         assert eo < TOL[dt], (s, eo)
     assert state_err(host64(state), ref) < TOL[dt]
+
+
+def test_snapshots_and_fused_steps_together():
+    """kda_chunked_forward_ex: the fused steps and state snapshots in one call; each snapshot is the
+    oracle's final state of the fused forward on that prefix."""
+    d = raw_inputs(740, 2, 700, 2, 128, 128, BF16)
+    t = {key: dev_tensor(d[key]) for key in ("q", "k", "v", "x", "beta", "z")}
+    o, hT, states = kda.kda_chunked_forward_ex(t["q"], t["k"], t["v"], None, t["beta"], dev_tensor(d["h0"]),
+                                               state_every=128, gate_x=t["x"], gate_scale=5.0, normalize_qk=True,
+                                               out_gate=t["z"])
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle.forward_fused(d["q"], d["k"], d["v"], None, d["beta"], d["h0"], x=d["x"], gate_scale=5.0,
+                                        normalize_qk=True, z=d["z"])
+    assert o_err(host64(o), o_ref) < TOL[BF16] and state_err(host64(hT), h_ref) < TOL[BF16]
+    for j in range(700 // 128):
+        n = (j + 1) * 128
+        p = {key: np.ascontiguousarray(d[key][:, :n]) for key in ("q", "k", "v", "x", "beta")}
+        _, h_j = oracle.forward_fused(p["q"], p["k"], p["v"], None, p["beta"], d["h0"], x=p["x"], gate_scale=5.0,
+                                      normalize_qk=True, want_o=False)
+        assert state_err(host64(states[:, :, j]), h_j) < TOL[BF16], j
+
+
+def test_varlen_fused():
+    lens = [300, 1, 257, 0, 129]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    Tt, H = int(cu[-1]), 3
+    d = datagen.prefill_preactivations(750, 1, Tt, H, 128, 128, BF16, None)
+    h0 = datagen.fill(750, datagen.TID_H0, 0, 0, 0.02, F32, (len(lens), H, 128, 128), 128)
+    t = {key: dev_tensor(d[key]) for key in ("q", "k", "v", "x", "beta", "z")}
+    o, hT, states = kda.kda_chunked_forward_varlen_ex(t["q"], t["k"], t["v"], None, t["beta"], dev_tensor(cu),
+                                                      max(lens), dev_tensor(h0), state_every=64, gate_x=t["x"],
+                                                      gate_scale=5.0, normalize_qk=True, out_gate=t["z"])
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle.forward_varlen_fused(d["q"], d["k"], d["v"], None, d["beta"], cu, h0, x=d["x"],
+                                               gate_scale=5.0, normalize_qk=True, z=d["z"])
+    from tests.kda_testlib import slice_err
+    assert slice_err(host64(o)[0], o_ref, (1,)) < TOL[BF16]
+    assert state_err(host64(hT), h_ref) < TOL[BF16]
+    # one snapshot per sequence checked (the first full 64 tokens)
+    for n, L in enumerate(lens):
+        if L < 64:
+            continue
+        s = int(cu[n])
+        p = {key: np.ascontiguousarray(d[key][:, s:s + 64]) for key in ("q", "k", "v", "x", "beta")}
+        _, h_j = oracle.forward_fused(p["q"], p["k"], p["v"], None, p["beta"], h0[n:n + 1], x=p["x"], gate_scale=5.0,
+                                      normalize_qk=True, want_o=False)
+        assert state_err(host64(states[n:n + 1, :, 0]), h_j) < TOL[BF16], n

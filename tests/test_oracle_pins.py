@@ -367,6 +367,21 @@ def test_p16_fused_decode_is_one_token_prefill():
     assert rel_err(o_d, o_p[:, 0]) < 1e-14 and rel_err(state, h_p) < 1e-14
 
 
+def test_p16_fused_varlen_is_independent_fused_calls():
+    lens = [5, 0, 13, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    raw = datagen.prefill_preactivations(165, 1, int(cu[-1]), 2, 16, 8, F32, None)
+    h0 = datagen.fill(165, datagen.TID_H0, 0, 0, 0.02, F32, (len(lens), 2, 16, 8), 8)
+    o, hT = oracle.forward_varlen_fused(raw["q"], raw["k"], raw["v"], None, raw["beta"], cu, h0, x=raw["x"],
+                                        gate_scale=4.0, normalize_qk=True, z=raw["z"])
+    for n in range(len(lens)):
+        s, e = cu[n], cu[n + 1]
+        part = {key: np.ascontiguousarray(raw[key][:, s:e]) for key in ("q", "k", "v", "x", "beta", "z")}
+        o_n, h_n = oracle.forward_fused(part["q"], part["k"], part["v"], None, part["beta"], h0[n:n + 1],
+                                        x=part["x"], gate_scale=4.0, normalize_qk=True, z=part["z"])
+        assert rel_err(o[s:e], o_n[0]) < 1e-14 and rel_err(hT[n:n + 1], h_n) < 1e-14
+
+
 # --------------------------------------------------------------------------------------------
 # P12: T single-token decode steps equal one prefill of T tokens
 
