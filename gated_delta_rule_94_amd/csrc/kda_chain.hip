@@ -17,6 +17,9 @@
 // of each (sequence, head) in order, S_start(g + 1) = M_g S_start(g) + b_g in fp32; a second launch
 // then runs every segment from its start state, writing o and, from the last segment, hT.
 //
+// Optional per call: the state after every `every` tokens of a sequence (prefix states for a
+// serving cache), stored between chunk steps; and an output gate multiplying o at its stores.
+//
 // Workgroup: WS / 16 chain waves, each owning 16 value columns of the state, and four copy waves.
 // The fp32 state lives in MFMA accumulator registers and is fed back as the B operand of the
 // next chunk's products; U likewise.  The copy waves stream records from HBM into double-buffered

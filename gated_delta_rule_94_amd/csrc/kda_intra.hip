@@ -22,22 +22,32 @@
 // and running products inside each 16-row sub-tile.
 //
 // Workgroup: 8 waves, one (chunk, head) record; two workgroups share a CU (LDS <= 80 KB), so one
-// workgroup's input loads overlap the other's arithmetic.
-//   prep   one thread per (2 channels, 8 rows): e^g and running products once; Q.Gamma and K'^T
-//          straight to the record
-//   M      M_kk and M_qk accumulated over 32-channel quarters of the key dimension: the two
-//          waves owning a quarter write its scaled operand tiles to LDS, then all eight waves run
-//          the tile-pair MFMAs.  With bf16 operands each tile is carried as hi + lo (hi = bf16(x),
-//          lo = bf16(x - hi)) and a product takes three MFMAs (hi hi + hi lo + lo hi): q.k cancels
-//          strongly, and a single bf16 rounding of the scaled operands would leave P and A with
-//          errors of several percent of a short sequence's output
-//   T      16x16 diagonal blocks of (I + A)^{-1} by fp32 forward substitution; off-diagonal
-//          blocks by X_ba = -L_bb sum_c A_bc X_ca on 16x16x16 MFMA in registers
-//   W, U~  MFMA, straight to the record
-// After M, A and T reuse the LDS of the operand tiles; (K . Gamma)^T and V^T are staged during prep.  Products whose
+// workgroup's input loads overlap the other's arithmetic.  Thread (row pair rp, channel pair cpl,
+// sub-tile psb) owns 2 rows x 2 channels in each 32-channel quarter of the key dimension; the 8 row
+// pairs of a sub-tile are 8 consecutive lanes, so running products over it are an 8-lane scan.
+// Per quarter, pipelined so that the later quarters' loads arrive while the earlier ones compute:
+//   scan       e^g and the running products (E, the sub-tile totals Tb to LDS)
+//   outputs    Q.Gamma and K'^T straight to the record, (K.Gamma)^T to LDS
+//   operands   every thread writes its scaled Q / K rows, K columns and gap tiles to LDS; with
+//              bf16 each tile is carried as hi + lo (hi = bf16(x), lo = bf16(x - hi)) and a
+//              product takes three MFMAs (hi hi + hi lo + lo hi): q.k cancels strongly, and a
+//              single bf16 rounding of the scaled operands would leave P and A with errors of
+//              several percent of a short sequence's output
+//   products   all eight waves run the M_kk / M_qk tile-pair MFMAs (next quarter's scan beside)
+// then
+//   A, P       M_kk -> A (fp32, LDS), M_qk -> P (record)
+//   T          16x16 diagonal blocks of (I + A)^{-1} by fp32 forward substitution; off-diagonal
+//              blocks by X_ba = -L_bb sum_c A_bc X_ca on 16x16x16 MFMA in registers
+//   W, U~      MFMA, straight to the record
+// A and T reuse the LDS of the operand tiles; V^T is staged in the last quarter.  Products whose
 // results go to memory are formed so that each lane holds four consecutive elements of a row.
 // LDS rows of 8-byte fragment pieces have strides that are odd multiples of 8 bytes (72, 136),
 // so the sixteen lanes of one fragment read fall on distinct banks.
+//
+// Optional fused steps (IntraParams): the log-decay formed from its gate pre-activation in the
+// scan, g = -A sigmoid(x) (padding rows keep a decay of 1), and q, k L2-normalised per row from
+// per-thread partial sums (a lane shuffle over the row pair's lanes and one LDS exchange with
+// the sibling wave).
 #include <type_traits>
 
 #include "kda_device.h"
