@@ -9,11 +9,13 @@ kernels on the caller's stream: the intra-chunk kernel (gate cumsum, UT/WY
 transform and the chunk-local products of every (chunk, head), in parallel, to
 a workspace of per-chunk records) and the chain kernel (the sequential state
 recurrence and the outputs).  Inputs are resident in HBM before the timed
-region; before every timed step a 512 MiB buffer is written so the 256 MB
-Infinity Cache holds none of the step's inputs.  Each call is bracketed by HIP
-events on the stream it runs on; ms_per_step is their mean.  A second pass of
-the same steps through kda_chunked_forward_profiled gives each kernel's mean
-duration from events recorded between the kernels.
+region, and a 512 MiB write evicts the 256 MB Infinity Cache just before it;
+the timed region is exactly K back-to-back steps between two HIP events on the
+launch stream, bracketed by synchronisation (ms_per_step = event time / K; one
+step moves about 1 GB, so no step finds the previous one's inputs cached).
+cold_steps repeats the steps one at a time with the cache evicted before each.
+A pass through kda_chunked_forward_profiled, cache evicted before each call,
+gives each kernel's mean duration from events recorded between the kernels.
 
 The JSON line carries:
   roofline       -- the dominant kernel (intra-chunk) against HBM, its binding
@@ -191,7 +193,22 @@ def main():
     for _ in range(args.warmup):
         step(0)
     torch.cuda.synchronize()
-    ms, wall = time_launches(step, args.steps, None if args.no_flush else flush)
+    # the timed region: exactly K back-to-back steps, bracketed by synchronisation, after one write
+    # of 512 MiB has evicted the Infinity Cache (one step moves about 1 GB, more than the cache holds)
+    if not args.no_flush:
+        flush()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / args.steps
+    # the same steps one at a time with the cache evicted before each (each step timed alone)
+    ms_cold, _ = time_launches(step, args.steps, None if args.no_flush else flush)
 
     # per-kernel durations: the same steps through the profiling entry point
     k_ms = [0.0, 0.0]
@@ -233,7 +250,7 @@ def main():
         "data": "synthetic: seeded SplitMix64/Box-Muller inputs with the workload's distributions",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d_k": w.dk, "d_v": w.dv, "chunk": w.chunk,
                    "state": "fp32", "h0": "N(0, 0.02)", "tokens_per_step": tokens,
-                   "cache_flushed_between_steps": not args.no_flush},
+                   "timing": "K back-to-back steps between two HIP events, cache evicted once before"},
         "roofline": {"bound": "hbm", "achieved": gbs_intra, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs_intra / HBM_PEAK_GBS, "traffic": measured_traffic("intra"),
                      "kernel": "kda::intra_chunk_kernel<false, 128, 128, 64>", "ms_per_launch": k_ms[0],
@@ -247,6 +264,9 @@ def main():
         "roofline_call_hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                               "alg_bytes_per_launch": alg_bytes, "scope": "whole call"},
         "wall_s_timed_region": wall,
+        "ms_per_step_wall": 1e3 * wall / args.steps,
+        "cold_steps": {"ms_per_step": ms_cold, "tokens_per_s": tokens / (ms_cold * 1e-3),
+                       "note": "each step timed alone by HIP events, the Infinity Cache evicted before it"},
     }
 
     # ---------------- the same call keeping the state every 1024 tokens (prefix states for a cache)
