@@ -40,6 +40,7 @@ struct ChainParams {
   float* hT;
   const int32_t* cu;      // packed offsets, or NULL
   const int32_t* chunk0;  // first chunk per packed sequence, or NULL
+  const int32_t* order;   // packed sequences by decreasing length (the order workgroups take them), or NULL
   int units, H, T, nch, dv;
   int nseg, seg_len;      // segments per (sequence, head) and their length in chunks (1, 0: whole)
   const float* sstart;    // nseg > 1: start state of every segment [units][nseg][DK][DV]
@@ -149,9 +150,12 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
   const int su = (idx / nsl_c) * 8 + xcd;
   const int slice = idx - (idx / nsl_c) * nsl_c;
   if (su >= p.units * segs) return;
-  const int unit = su / segs, seg = su - unit * segs;
   const int H = p.H;
-  const int n = unit / H, h = unit - n * H;
+  // (sequence, head) of this workgroup: packed sequences are taken longest first, so that the
+  // long chains start in the first wave of workgroups and the short ones fill in behind them
+  const int ui = su / segs, seg = su - ui * segs;
+  const int n = p.order ? p.order[ui / H] : ui / H, h = ui - (ui / H) * H;
+  const int unit = n * H + h;
   int64_t t_begin, t_end, first, seq0;
   if (p.nseg > 1) {  // equal-length sequences
     const int64_t s0 = (int64_t)n * p.T, s1 = s0 + p.T;
@@ -431,7 +435,7 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
 template <bool F32, int DK, int DV, int C, int WS, bool SUM>
 static hipError_t launch_chain_impl(const ChainLaunch& L) {
   ChainParams p;
-  p.ws = L.records; p.h0 = L.h0; p.o = L.o; p.hT = L.hT; p.cu = L.cu; p.chunk0 = L.chunk0;
+  p.ws = L.records; p.h0 = L.h0; p.o = L.o; p.hT = L.hT; p.cu = L.cu; p.chunk0 = L.chunk0; p.order = L.order;
   p.units = L.units; p.H = L.H; p.T = L.T; p.nch = L.nch; p.dv = DV;
   p.nseg = L.nseg > 1 ? L.nseg : 1; p.seg_len = L.seg_len; p.sstart = L.sstart; p.send = L.send;
   p.states = SUM ? nullptr : L.states; p.every = L.every; p.max_states = L.max_states;

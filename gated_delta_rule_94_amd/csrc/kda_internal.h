@@ -69,6 +69,7 @@ struct ChainLaunch {
   float* hT;
   const int32_t* cu;
   const int32_t* chunk0;
+  const int32_t* order = nullptr;  // packed sequences longest first, or NULL
   int units, H, T, nch;
   int dk, dv, chunk, ws;
   bool f32;
@@ -103,7 +104,8 @@ hipError_t launch_segment_combine(const float* h0, const float* send, float* sst
 hipError_t launch_decode_step(const DecodeArgs& a);
 hipError_t launch_intra(const IntraLaunch& L);
 hipError_t launch_chain(const ChainLaunch& L);
-hipError_t launch_chunk_map(const int32_t* cu, int num_seqs, int T, int C, int32_t* chunk0, void* stream);
+hipError_t launch_chunk_map(const int32_t* cu, int num_seqs, int T, int C, int32_t* chunk0, int32_t* order,
+                            void* stream);
 
 // Prefill: supported shape?  workspace bytes?  launch (hipErrorInvalidValue: unsupported shape).
 bool chunked_forward_supported(bool f32, int dk, int dv, int chunk);

@@ -633,11 +633,15 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   }
 }
 
+// Sequences that the chunk map orders by length (LDS: 4 B each).
+constexpr int kOrderMax = 1024;
+
 // Chunk map of packed sequences: chunk0[s] = sum over earlier sequences of ceil(len / C), with the
 // lengths clamped to [0, T_total] as every kernel does.  One workgroup, no host synchronisation.
 __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restrict__ cu, int num_seqs, int T, int C,
-                                                        int32_t* __restrict__ chunk0) {
+                                                        int32_t* __restrict__ chunk0, int32_t* __restrict__ order) {
   __shared__ int32_t s_part[256];
+  __shared__ int32_t s_len[kOrderMax];
   const int tid = threadIdx.x;
   const int per = (num_seqs + 255) / 256;
   const int s_lo = tid * per, s_hi = min(num_seqs, s_lo + per);
@@ -663,6 +667,24 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
     run += (int32_t)((b - a + C - 1) / C);
   }
   if (tid == 255) chunk0[num_seqs] = s_part[255];
+  // order: the sequences by decreasing chunk count (ties by index), by ranking each against all
+  // others -- for up to kOrderMax sequences; beyond that, the given order
+  if (num_seqs > kOrderMax) {
+    for (int s = tid; s < num_seqs; s += 256) order[s] = s;
+    return;
+  }
+  for (int s = tid; s < num_seqs; s += 256) {
+    int64_t a, b;
+    seq_range(cu, s, T, a, b);
+    s_len[s] = (int32_t)((b - a + C - 1) / C);
+  }
+  __syncthreads();
+  for (int s = tid; s < num_seqs; s += 256) {
+    const int32_t ls = s_len[s];
+    int rank = 0;
+    for (int t = 0; t < num_seqs; ++t) rank += (s_len[t] > ls || (s_len[t] == ls && t < s)) ? 1 : 0;
+    order[rank] = s;
+  }
 }
 
 template <bool F32, int DK, int DV, int C>
@@ -676,8 +698,10 @@ static hipError_t launch_intra_impl(const IntraLaunch& L) {
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_map(const int32_t* cu, int num_seqs, int T, int C, int32_t* chunk0, void* stream) {
-  hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, cu, num_seqs, T, C, chunk0);
+hipError_t launch_chunk_map(const int32_t* cu, int num_seqs, int T, int C, int32_t* chunk0, int32_t* order,
+                            void* stream) {
+  hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, cu, num_seqs, T, C, chunk0,
+                     order);
   return hipGetLastError();
 }
 

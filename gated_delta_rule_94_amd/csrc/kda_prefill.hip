@@ -8,8 +8,8 @@
 //                          sequences on few heads, per segment: a summary launch, the segment
 //                          start states (segment_combine_kernel), then the chain of every segment
 //
-// Workspace: [records: max_chunks * H * record bytes][chunk0: (num_seqs + 1) int32, packed only]
-// [segment start states: units * nseg * d_k * d_v fp32][segment summaries: units * (nseg - 1) *
+// Workspace: [records: max_chunks * H * record bytes][chunk0: (num_seqs + 1) int32, and the
+// sequences longest first: num_seqs int32, packed only][segment start states: units * nseg * d_k * d_v fp32][segment summaries: units * (nseg - 1) *
 // d_k * (d_v + d_k) fp32], the last two only when the plan splits sequences into nseg > 1
 // segments.  max_chunks bounds the number of chunks: B * ceil(T / C) for equal-length sequences,
 // floor(T_total / C) + num_seqs for packed ones (each sequence adds at most one partial chunk).
@@ -58,7 +58,7 @@ size_t chunked_forward_workspace(bool f32, int dk, int dv, int chunk, int64_t ma
   const int64_t rb = record_bytes(f32, dk, dv, chunk);
   if (rb == 0) return 0;
   size_t bytes = (size_t)(max_chunks * H * rb);
-  if (varlen) bytes += al256((size_t)(num_seqs + 1) * 4);
+  if (varlen) bytes += al256((size_t)(num_seqs + 1) * 4) + al256((size_t)num_seqs * 4);  // chunk map, order
   const int nch = (!varlen && num_seqs > 0) ? (int)(max_chunks / num_seqs) : 0;
   const ChainPlan pl = chain_plan(f32, (int64_t)num_seqs * H, nch, dv, varlen);
   if (pl.nseg > 1) {
@@ -89,11 +89,13 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
   const int nch = varlen ? 0 : (a.T + C - 1) / C;
   unsigned char* records = static_cast<unsigned char*>(a.workspace);
   int32_t* chunk0 = nullptr;
+  int32_t* order = nullptr;
   hipError_t e = hipSuccess;
   if (a.events && (e = hipEventRecord(a.events[0], (hipStream_t)a.stream)) != hipSuccess) return e;
   if (varlen) {
     chunk0 = reinterpret_cast<int32_t*>(records + max_chunks * a.H * rb);
-    e = launch_chunk_map(a.cu_seqlens, a.num_seqs, a.T, C, chunk0, a.stream);
+    order = reinterpret_cast<int32_t*>(reinterpret_cast<unsigned char*>(chunk0) + al256((size_t)(a.num_seqs + 1) * 4));
+    e = launch_chunk_map(a.cu_seqlens, a.num_seqs, a.T, C, chunk0, order, a.stream);
     if (e != hipSuccess) return e;
   }
   const int64_t items = max_chunks * a.H;
@@ -113,7 +115,7 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
   }
   if (a.events && (e = hipEventRecord(a.events[1], (hipStream_t)a.stream)) != hipSuccess) return e;
   ChainLaunch K;
-  K.records = records; K.h0 = a.h0; K.o = a.o; K.hT = a.hT; K.cu = a.cu_seqlens; K.chunk0 = chunk0;
+  K.records = records; K.h0 = a.h0; K.o = a.o; K.hT = a.hT; K.cu = a.cu_seqlens; K.chunk0 = chunk0; K.order = order;
   K.units = a.num_seqs * a.H; K.H = a.H; K.T = a.T; K.nch = nch;
   K.dk = a.dk; K.dv = a.dv; K.chunk = C; K.f32 = a.f32;
   const ChainPlan pl = chain_plan(a.f32, K.units, nch, a.dv, varlen);

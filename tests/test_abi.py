@@ -45,9 +45,9 @@ def test_workspace_queries():
     rec = (rec + 255) // 256 * 256
     assert lib.kda_chunked_forward_workspace_bytes(4, 4096, 16, 128, 128, 64, 1) == 4 * 64 * 16 * rec
     assert lib.kda_chunked_forward_workspace_bytes(1, 100, 2, 128, 128, 64, 1) == 2 * 2 * rec  # ragged tail
-    # packed: at most floor(T_total / C) + N chunks, plus the chunk map
+    # packed: at most floor(T_total / C) + N chunks, plus the chunk map and the longest-first order
     n = lib.kda_chunked_forward_varlen_workspace_bytes(16, 1 << 20, 131072, 8, 128, 128, 64, 1)
-    assert n == ((1 << 20) // 64 + 16) * 8 * rec + 256
+    assert n == ((1 << 20) // 64 + 16) * 8 * rec + 256 + 256
     assert lib.kda_chunked_forward_workspace_bytes(0, 10, 2, 64, 64, 64, 1) == 0
     assert lib.kda_chunked_forward_workspace_bytes(1, 10, 2, 64, 64, 48, 1) == 0  # unsupported chunk
 

@@ -185,6 +185,21 @@ def test_varlen_against_oracle(dt):
             assert torch.equal(hT[n].cpu(), torch.from_numpy(d["h0"][n]))
 
 
+@pytest.mark.parametrize("n", [300, 1100])
+def test_varlen_many_sequences(n):
+    """Many short packed sequences: the chain takes them longest first (ordered on the device up
+    to 1024 sequences, in the given order beyond), with no effect on the results."""
+    lens = list(datagen.uniform_ints(800 + n, datagen.TID_LEN, n, 0, 70))
+    cu, d = varlen_case(lens, 1, 64, 64, BF16, 800 + n)
+    g = {key: dev_tensor(d[key]) for key in KEYS}
+    o, hT = kda.kda_chunked_forward_varlen(g["q"], g["k"], g["v"], g["g"], g["beta"], dev_tensor(cu), max(lens),
+                                           dev_tensor(d["h0"]), chunk=32)
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle.forward_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, d["h0"])
+    assert slice_err(host64(o)[0], o_ref, (1,)) < TOL[BF16]
+    assert state_err(host64(hT), h_ref) < TOL[BF16]
+
+
 def test_varlen_equals_batched():
     """Packed equal-length sequences give the same bits as the batched call."""
     B, T, H = 3, 200, 2
