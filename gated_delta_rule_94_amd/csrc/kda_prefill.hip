@@ -13,6 +13,8 @@
 // d_k * (d_v + d_k) fp32], the last two only when the plan splits sequences into nseg > 1
 // segments.  max_chunks bounds the number of chunks: B * ceil(T / C) for equal-length sequences,
 // floor(T_total / C) + num_seqs for packed ones (each sequence adds at most one partial chunk).
+#include <atomic>
+
 #include "kda_internal.h"
 #include "kda_record.h"
 
@@ -68,16 +70,18 @@ size_t chunked_forward_workspace(bool f32, int dk, int dv, int chunk, int64_t ma
   return bytes;
 }
 
+// CUs of the current device (256 when no device can be queried), cached per device; calls from
+// several host threads may query concurrently and store the same value.
 static int compute_units() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 hipError_t launch_chunked_forward(const PrefillArgs& a) {
