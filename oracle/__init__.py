@@ -16,6 +16,11 @@ sum of decay and erase, decay-only product), invariants (continuation,
 linearity, column independence, varlen = independent calls, decode = prefill,
 norm bound), a hand-computed worked example under tests/golden/, and an fp64
 chunked mirror of the chunkwise (UT/WY) algebra.
+
+The backward (``backward``: reverse-mode gradients through the same recurrence) is
+pinned in tests/test_oracle_backward_pins.py: finite differences of the forward,
+directional derivatives across its checkpoint blocks, the adjoint identity of the
+linear part, and closed forms at beta = 0.
 """
 from __future__ import annotations
 
@@ -57,6 +62,8 @@ def _load():
             lib.kda_oracle_forward_varlen.restype = i32
             lib.kda_oracle_decode_step.argtypes = [vp] * 5 + [i32, vp, vp, i32, i32, i32, i32, i32]
             lib.kda_oracle_decode_step.restype = i32
+            lib.kda_oracle_backward.argtypes = [vp] * 5 + [i32] + [vp] * 9 + [i32, i64, i32, i32, i32, i32]
+            lib.kda_oracle_backward.restype = i32
             _lib = lib
     return _lib
 
@@ -231,3 +238,38 @@ def forward_varlen_fused(q, k, v, g, beta, cu_seqlens, h0=None, *, x=None, gate_
     if o is not None and z is not None:
         o = o * _dec(z).reshape(o.shape)
     return o, hT
+
+
+# --------------------------------------------------------------------------------------------
+# Backward (reverse mode) of the plain recurrence, for training: the chain rule through the five
+# steps of each token, in reverse order (kda_oracle.c states each step's adjoint).
+
+
+def backward(q, k, v, g, beta, h0, do, dhT=None, nthreads=None):
+    """Gradients of L = <do, o> + <dhT, hT> with o, hT = forward(q, k, v, g, beta, h0).
+    q, k, g: [B,T,H,dk]; v, do: [B,T,H,dv]; beta: [B,T,H]; h0, dhT: [B,H,dk,dv] or None.
+    do and dhT may be fp32, bf16 bits or fp64 (decoded exactly).  Returns fp64
+    (dq, dk, dv, dg, dbeta, dh0) shaped like q, k, v, g, beta and [B,H,dk,dv]."""
+    q, k, v, g, beta = map(_c, (q, k, v, g, beta))
+    h0 = _state64(h0)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and g.shape == q.shape and v.shape == (B, T, H, dv) and beta.shape == (B, T, H)
+    dt = _dtype_code(q, k, v, g, beta)
+    do64 = np.ascontiguousarray(_dec(do))
+    assert do64.shape == (B, T, H, dv)
+    dhT64 = None if dhT is None else np.ascontiguousarray(_dec(dhT))
+    if dhT64 is not None:
+        assert dhT64.shape == (B, H, dk, dv)
+    if h0 is not None:
+        assert h0.shape == (B, H, dk, dv)
+    dq, dkk, dg = (np.empty((B, T, H, dk)) for _ in range(3))
+    dvv = np.empty((B, T, H, dv))
+    db = np.empty((B, T, H))
+    dh0 = np.empty((B, H, dk, dv))
+    rc = _load().kda_oracle_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), dt, _ptr(h0), _ptr(do64),
+                                     _ptr(dhT64), _ptr(dq), _ptr(dkk), _ptr(dg), _ptr(dvv), _ptr(db), _ptr(dh0),
+                                     B, T, H, dk, dv, nthreads or default_threads())
+    if rc:
+        raise RuntimeError("kda_oracle_backward: invalid arguments")
+    return dq, dkk, dvv, dg, db, dh0

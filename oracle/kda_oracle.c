@@ -324,3 +324,224 @@ int kda_oracle_decode_step(const void* q, const void* k, const void* v, const vo
   free(ok);
   return 0;
 }
+
+/*
+ * Backward (reverse mode) of the recurrence above, for training: given the
+ * adjoints do = dL/do [.., T, H, d_v] and dhT = dL/dhT [.., H, d_k, d_v] (or
+ * none), it returns dL/dq, dL/dk, dL/dg [.., T, H, d_k], dL/dv [.., T, H, d_v],
+ * dL/dbeta [.., T, H] and dL/dh0 [.., H, d_k, d_v], all fp64.  The pages give
+ * no backward (training with KDA is stated on the technical-report page,
+ * "Training"); this is the chain rule applied to the five steps of one token,
+ * taken in reverse order, with dS the adjoint of the state after the token:
+ *
+ *   5. o = S^T q            dq[c]  = sum_j S[c][j] do[j];      dS[c][j] += q[c] do[j]
+ *   4. S = S' + k u^T       dk[c] += sum_j dS[c][j] u[j];      du[j] = sum_c dS[c][j] k[c];  dS' = dS
+ *   3. u = beta (v - p)     dbeta  = sum_j du[j] (v[j] - p[j]); dv[j] = beta du[j];  dp[j] = -beta du[j]
+ *   2. p = S'^T k           dk[c] += sum_j S'[c][j] dp[j];     dS'[c][j] += k[c] dp[j]
+ *   1. S' = Diag(a) S_prev  dg[c]  = sum_j dS'[c][j] S'[c][j] (a = exp(g), da/dg = a);
+ *                           dS_prev[c][j] = a[c] dS'[c][j]
+ *
+ * and dh0 is dS once every token has been undone.  The forward states are
+ * recomputed from checkpoints kept every BWD_BLOCK tokens: one block's states
+ * at a time are held, so memory is (T / BWD_BLOCK + BWD_BLOCK) states per unit.
+ */
+#define BWD_BLOCK 64
+
+typedef struct {
+  size_t row0;
+  long T;
+  const double* h0;   /* or NULL */
+  const double* dO;   /* adjoint of o at token 0 (stride o_stride) */
+  size_t o_stride;
+  const double* dhT;  /* or NULL */
+  double *dq, *dk, *dg, *dv, *dbeta; /* token 0's rows; q/k/g rows advance by H dk, v rows by H dv, beta by H */
+  double* dh0;
+} bunit_t;
+
+/* one forward token step on S (in place); keeps S' (decayed state), p and u for the backward */
+static void fwd_token(const inputs_t* in, size_t row, double* S, double* Sd, double* p, double* u) {
+  const int dk = in->dk, dv = in->dv;
+  const double b = ld(in->beta, in->dtype, row);
+  for (int c = 0; c < dk; ++c) {
+    double a = exp(ld(in->g, in->dtype, row * dk + c));
+    for (int j = 0; j < dv; ++j) S[(size_t)c * dv + j] *= a;
+  }
+  if (Sd) memcpy(Sd, S, sizeof(double) * (size_t)dk * dv);
+  for (int j = 0; j < dv; ++j) p[j] = 0.0;
+  for (int c = 0; c < dk; ++c) {
+    double kc = ld(in->k, in->dtype, row * dk + c);
+    for (int j = 0; j < dv; ++j) p[j] += S[(size_t)c * dv + j] * kc;
+  }
+  for (int j = 0; j < dv; ++j) u[j] = b * (ld(in->v, in->dtype, row * dv + j) - p[j]);
+  for (int c = 0; c < dk; ++c) {
+    double kc = ld(in->k, in->dtype, row * dk + c);
+    for (int j = 0; j < dv; ++j) S[(size_t)c * dv + j] += kc * u[j];
+  }
+}
+
+static void backward_unit(const inputs_t* in, const bunit_t* u) {
+  const int dk = in->dk, dv = in->dv, H = in->H;
+  const size_t ss = (size_t)dk * dv;
+  const long T = u->T, nblk = (T + BWD_BLOCK - 1) / BWD_BLOCK;
+  double* ckpt = (double*)malloc(sizeof(double) * ss * (size_t)(nblk > 0 ? nblk : 1)); /* state before block */
+  double* blk = (double*)malloc(sizeof(double) * ss * (BWD_BLOCK + 1)); /* states before each token, + after */
+  double* Sd = (double*)malloc(sizeof(double) * ss);
+  double* dS = (double*)malloc(sizeof(double) * ss);
+  double* p = (double*)malloc(sizeof(double) * dv);
+  double* uu = (double*)malloc(sizeof(double) * dv);
+  double* du = (double*)malloc(sizeof(double) * dv);
+  double* S = (double*)calloc(ss, sizeof(double));
+  if (u->h0) memcpy(S, u->h0, sizeof(double) * ss);
+  for (long n = 0; n < nblk; ++n) {
+    memcpy(ckpt + (size_t)n * ss, S, sizeof(double) * ss);
+    for (long t = n * BWD_BLOCK; t < T && t < (n + 1) * BWD_BLOCK; ++t)
+      fwd_token(in, u->row0 + (size_t)t * H, S, NULL, p, uu);
+  }
+  if (u->dhT) memcpy(dS, u->dhT, sizeof(double) * ss);
+  else memset(dS, 0, sizeof(double) * ss);
+  for (long n = nblk - 1; n >= 0; --n) {
+    const long t0 = n * BWD_BLOCK, t1 = (t0 + BWD_BLOCK < T) ? t0 + BWD_BLOCK : T;
+    /* recompute the states before every token of the block */
+    memcpy(blk, ckpt + (size_t)n * ss, sizeof(double) * ss);
+    for (long t = t0; t < t1; ++t) {
+      memcpy(blk + (size_t)(t - t0 + 1) * ss, blk + (size_t)(t - t0) * ss, sizeof(double) * ss);
+      fwd_token(in, u->row0 + (size_t)t * H, blk + (size_t)(t - t0 + 1) * ss, NULL, p, uu);
+    }
+    for (long t = t1 - 1; t >= t0; --t) {
+      const size_t row = u->row0 + (size_t)t * H;
+      const double* Sprev = blk + (size_t)(t - t0) * ss;
+      const double* Snew = blk + (size_t)(t - t0 + 1) * ss;
+      const double b = ld(in->beta, in->dtype, row);
+      const double* dO = u->dO + (size_t)t * u->o_stride;
+      double* dq = u->dq + (size_t)t * H * dk;
+      double* dkk = u->dk + (size_t)t * H * dk;
+      double* dg = u->dg + (size_t)t * H * dk;
+      double* dvv = u->dv + (size_t)t * H * dv;
+      /* forward quantities of this token: S' (decayed state), p, u */
+      memcpy(S, Sprev, sizeof(double) * ss);
+      fwd_token(in, row, S, Sd, p, uu);
+      /* 5. readout */
+      for (int c = 0; c < dk; ++c) {
+        double acc = 0.0, qc = ld(in->q, in->dtype, row * dk + c);
+        for (int j = 0; j < dv; ++j) {
+          acc += Snew[(size_t)c * dv + j] * dO[j];
+          dS[(size_t)c * dv + j] += qc * dO[j];
+        }
+        dq[c] = acc;
+      }
+      /* 4. write k u^T */
+      for (int j = 0; j < dv; ++j) du[j] = 0.0;
+      for (int c = 0; c < dk; ++c) {
+        double acc = 0.0, kc = ld(in->k, in->dtype, row * dk + c);
+        for (int j = 0; j < dv; ++j) {
+          acc += dS[(size_t)c * dv + j] * uu[j];
+          du[j] += dS[(size_t)c * dv + j] * kc;
+        }
+        dkk[c] = acc;
+      }
+      /* 3. u = beta (v - p) */
+      double db = 0.0;
+      for (int j = 0; j < dv; ++j) {
+        double vj = ld(in->v, in->dtype, row * dv + j);
+        db += du[j] * (vj - p[j]);
+        dvv[j] = b * du[j];
+        du[j] = -b * du[j]; /* now dp */
+      }
+      u->dbeta[(size_t)t * H] = db;
+      /* 2. p = S'^T k */
+      for (int c = 0; c < dk; ++c) {
+        double acc = 0.0, kc = ld(in->k, in->dtype, row * dk + c);
+        for (int j = 0; j < dv; ++j) {
+          acc += Sd[(size_t)c * dv + j] * du[j];
+          dS[(size_t)c * dv + j] += kc * du[j];
+        }
+        dkk[c] += acc;
+      }
+      /* 1. decay */
+      for (int c = 0; c < dk; ++c) {
+        double acc = 0.0, a = exp(ld(in->g, in->dtype, row * dk + c));
+        for (int j = 0; j < dv; ++j) {
+          acc += dS[(size_t)c * dv + j] * Sd[(size_t)c * dv + j];
+          dS[(size_t)c * dv + j] *= a;
+        }
+        dg[c] = acc;
+      }
+    }
+  }
+  if (u->dh0) memcpy(u->dh0, dS, sizeof(double) * ss);
+  free(ckpt); free(blk); free(Sd); free(dS); free(p); free(uu); free(du); free(S);
+}
+
+typedef struct {
+  const inputs_t* in;
+  const bunit_t* units;
+  int n, next;
+  pthread_mutex_t mu;
+} bpool_t;
+
+static void* bworker(void* arg) {
+  bpool_t* P = (bpool_t*)arg;
+  for (;;) {
+    pthread_mutex_lock(&P->mu);
+    int i = P->next++;
+    pthread_mutex_unlock(&P->mu);
+    if (i >= P->n) break;
+    backward_unit(P->in, &P->units[i]);
+  }
+  return NULL;
+}
+
+static void bwd_run(const inputs_t* in, const bunit_t* units, int n, int nthreads) {
+  if (n <= 0) return;
+  bpool_t P;
+  P.in = in;
+  P.units = units;
+  P.n = n;
+  P.next = 0;
+  pthread_mutex_init(&P.mu, NULL);
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > n) nthreads = n;
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  int* ok = (int*)calloc((size_t)nthreads, sizeof(int));
+  for (int t = 0; t < nthreads; ++t) ok[t] = pthread_create(&th[t], NULL, bworker, &P) == 0;
+  bworker(&P);
+  for (int t = 0; t < nthreads; ++t)
+    if (ok[t]) pthread_join(th[t], NULL);
+  pthread_mutex_destroy(&P.mu);
+  free(th);
+  free(ok);
+}
+
+/*
+ * Batched backward.  dO: [B,T,H,dv] fp64; dhT: [B,H,dk,dv] fp64 or NULL (zero);
+ * h0 as in the forward.  Outputs (fp64, all required): dq, dk, dg [B,T,H,dk],
+ * dv [B,T,H,dv], dbeta [B,T,H], dh0 [B,H,dk,dv].  Returns 0 on success.
+ */
+int kda_oracle_backward(const void* q, const void* k, const void* v, const void* g, const void* beta, int dtype,
+                        const double* h0, const double* dO, const double* dhT, double* dq, double* dk, double* dg,
+                        double* dv, double* dbeta, double* dh0, int B, long T, int H, int dk_, int dv_, int nthreads) {
+  if (B < 0 || T < 0 || bad_dims(H, dk_, dv_, dtype) || !dO || !dq || !dk || !dg || !dv || !dbeta || !dh0) return 1;
+  inputs_t in = {q, k, v, g, beta, dtype, H, dk_, dv_};
+  int n = B * H;
+  bunit_t* units = (bunit_t*)calloc((size_t)(n > 0 ? n : 1), sizeof(bunit_t));
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+      bunit_t* u = &units[b * H + h];
+      size_t sidx = (size_t)(b * H + h) * dk_ * dv_, r0 = (size_t)b * (size_t)T * H + h;
+      u->row0 = r0;
+      u->T = T;
+      u->h0 = h0 ? h0 + sidx : NULL;
+      u->dO = dO + r0 * dv_;
+      u->o_stride = (size_t)H * dv_;
+      u->dhT = dhT ? dhT + sidx : NULL;
+      u->dq = dq + r0 * dk_;
+      u->dk = dk + r0 * dk_;
+      u->dg = dg + r0 * dk_;
+      u->dv = dv + r0 * dv_;
+      u->dbeta = dbeta + r0;
+      u->dh0 = dh0 + sidx;
+    }
+  bwd_run(&in, units, n, nthreads);
+  free(units);
+  return 0;
+}
