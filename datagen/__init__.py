@@ -36,7 +36,7 @@ _lock = threading.Lock()
 _lib = None
 
 # tensor ids of the streams
-TID_Q, TID_K, TID_V, TID_BETA, TID_G, TID_H0, TID_LEN, TID_Z = 0, 1, 2, 3, 4, 5, 6, 7
+TID_Q, TID_K, TID_V, TID_BETA, TID_G, TID_H0, TID_LEN, TID_Z, TID_DO, TID_DHT = 0, 1, 2, 3, 4, 5, 6, 7, 8, 9
 _KIND_NORMAL, _KIND_UNIT_ROWS, _KIND_SIGMOID = 0, 1, 2
 DT_F32, DT_BF16, DT_F64 = 0, 1, 2
 
@@ -126,6 +126,14 @@ def prefill_inputs(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: i
     }
     d["h0"] = None if h0_std is None else fill(seed, TID_H0, 0, _KIND_NORMAL, h0_std, DT_F32, (B, H, dk, dv), dv)
     return d
+
+
+def backward_adjoints(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: int, dhT_std=None, sub: int = 0):
+    """Adjoints for a backward call: do [B,T,H,dv] N(0,1) in the input dtype, dhT [B,H,dk,dv] fp32
+    N(0, dhT_std) (or None)."""
+    do = fill(seed, TID_DO, sub, _KIND_NORMAL, 1.0, dtype, (B, T, H, dv), dv)
+    dhT = None if dhT_std is None else fill(seed, TID_DHT, 0, _KIND_NORMAL, dhT_std, DT_F32, (B, H, dk, dv), dv)
+    return do, dhT
 
 
 def prefill_preactivations(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: int, h0_std=None,

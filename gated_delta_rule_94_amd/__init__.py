@@ -13,6 +13,7 @@ entry points' names:
 * ``kda_chunked_forward_fused`` / ``kda_decode_step_fused`` -- with the gate formed from its
   pre-activation, q and k normalised, and an output gate, inside the kernels
 * ``kda_chunked_forward_ex`` / ``kda_chunked_forward_varlen_ex`` -- snapshots and fused steps together
+* ``kda_chunked_backward``       -- gradients of the chunked prefill (training)
 
 Importing this package fails loudly when ``libkda.so`` has not been built
 (``python gated_delta_rule_94_amd/build.py``).
@@ -36,7 +37,7 @@ EXPORTS = (
     "kda_chunked_forward", "kda_chunked_forward_with_states", "kda_chunked_forward_varlen_with_states",
     "kda_chunked_forward_fused", "kda_decode_step_fused", "kda_chunked_forward_ex", "kda_chunked_forward_varlen_ex",
     "kda_chunked_forward_profiled", "kda_chunked_forward_varlen", "kda_chunked_forward_varlen_workspace_bytes",
-    "kda_decode_step",
+    "kda_decode_step", "kda_chunked_backward", "kda_chunked_backward_workspace_bytes",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -82,6 +83,10 @@ _lib.kda_chunked_forward_ex.restype = _i32
 _lib.kda_chunked_forward_varlen_ex.argtypes = ([_vp] * 9 + [_i32, ctypes.POINTER(Fusion), _vp] + [_i32] * 8 +
                                                [_vp, _sz, _vp])
 _lib.kda_chunked_forward_varlen_ex.restype = _i32
+_lib.kda_chunked_backward_workspace_bytes.argtypes = [_i32] * 7
+_lib.kda_chunked_backward_workspace_bytes.restype = _sz
+_lib.kda_chunked_backward.argtypes = [_vp] * 14 + [_i32] * 7 + [_vp, _sz, _vp]
+_lib.kda_chunked_backward.restype = _i32
 
 
 class KDAError(RuntimeError):
@@ -467,3 +472,41 @@ def kda_chunked_forward_varlen_ex(q, k, v, g, beta, cu_seqlens, max_seqlen: int,
     if st:
         raise KDAError("kda_chunked_forward_varlen_ex", st)
     return o, hT, states
+
+
+def backward_workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:
+    """Device workspace kda_chunked_backward needs for this shape (0: unsupported)."""
+    return int(_lib.kda_chunked_backward_workspace_bytes(B, T, H, dk, dv, chunk,
+                                                         _dtype_code(torch.empty(0, dtype=dtype))))
+
+
+def kda_chunked_backward(q, k, v, g, beta, h0, do, dhT=None, *, chunk: int = 64, want_dh0: bool = True,
+                         grads=None, workspace=None, stream=None):
+    """Gradients of <do, o> + <dhT, hT> for (o, hT) = kda_chunked_forward(q, k, v, g, beta, h0).
+    q, k, g [B,T,H,dk]; v, do [B,T,H,dv]; beta [B,T,H] (one dtype); h0, dhT [B,H,dk,dv] float32 or
+    None.  Returns (dq, dk, dv, dg, dbeta, dh0): the first five like q, k, v, g, beta, dh0 float32
+    [B,H,dk,dv] (None unless want_dh0).  grads: optional preallocated 6-tuple of outputs."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("g", g, (B, T, H, dk)),
+                         ("v", v, (B, T, H, dv)), ("beta", beta, (B, T, H)), ("do", do, (B, T, H, dv))):
+        _check(name, t, shp, dt, dev)
+    _check("h0", h0, (B, H, dk, dv), torch.float32, dev)
+    _check("dhT", dhT, (B, H, dk, dv), torch.float32, dev)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(g),
+                 torch.empty_like(beta),
+                 torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dh0 else None)
+    dq, dkk, dvv, dg, db, dh0 = grads
+    for name, t, ref in (("dq", dq, q), ("dk", dkk, k), ("dv", dvv, v), ("dg", dg, g), ("dbeta", db, beta)):
+        _check(name, t, ref.shape, dt, dev)
+    _check("dh0", dh0, (B, H, dk, dv), torch.float32, dev)
+    ws_bytes = _lib.kda_chunked_backward_workspace_bytes(B, T, H, dk, dv, chunk, _dtype_code(q))
+    ws = _workspace(workspace, ws_bytes, dev)
+    st = _lib.kda_chunked_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(do), _ptr(dhT),
+                                   _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg), _ptr(db), _ptr(dh0),
+                                   B, T, H, dk, dv, chunk, _dtype_code(q), _ptr(ws), _nbytes(ws), _stream(stream))
+    if st:
+        raise KDAError("kda_chunked_backward", st)
+    return dq, dkk, dvv, dg, db, dh0

@@ -270,6 +270,40 @@ kda_status kda_chunked_forward_varlen(const void* q, const void* k, const void* 
                                                 workspace_bytes, hip_stream);
 }
 
+size_t kda_chunked_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt) {
+  if (B <= 0 || T < 0 || H <= 0 || (dt != KDA_F32 && dt != KDA_BF16)) return 0;
+  if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return 0;
+  return kda::chunked_backward_workspace(dt == KDA_F32, d_k, d_v, chunk, B, T, H);
+}
+
+kda_status kda_chunked_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                const float* h0, const void* d_o, const float* dhT, void* dq, void* dk, void* dv,
+                                void* dg, void* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v, int chunk,
+                                kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
+  // the forward's checks (inputs, h0; d_o in place of o), then the gradient buffers
+  const kda_status st = check_prefill(q, k, v, g, beta, h0, d_o, dhT, B * T, H, d_k, d_v, chunk, dt);
+  if (st != KDA_OK) return st;
+  if (B * T > 0) {
+    if (!dq || !dk || !dv || !dg || !dbeta) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dg) || !aligned16(dbeta))
+      return KDA_ERR_INVALID_ARG;
+  }
+  if (dh0 && !aligned16(dh0)) return KDA_ERR_INVALID_ARG;
+  if (!kda::chunked_backward_supported(dt == KDA_F32, d_k, d_v, chunk)) return KDA_ERR_UNSUPPORTED;
+  if (B == 0 || (T == 0 && !dh0)) return KDA_OK;
+  if (!workspace_ok(workspace, workspace_bytes, kda_chunked_backward_workspace_bytes(B, T, H, d_k, d_v, chunk, dt)))
+    return KDA_ERR_WORKSPACE;
+  kda::BackwardArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dO = d_o; a.dhT = dhT;
+  a.dq = dq; a.dk_out = dk; a.dv_out = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+  a.B = B; a.T = T; a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk; a.f32 = dt == KDA_F32;
+  a.workspace = workspace;
+  a.stream = hip_stream;
+  return kda::launch_chunked_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_decode_step_fused(const void* q, const void* k, const void* v, const void* g, const void* beta,
                                  float* state, void* o, const kda_fusion* fusion, int B, int H, int d_k, int d_v,
                                  kda_dtype dt, void* hip_stream) {

@@ -107,6 +107,23 @@ hipError_t launch_chain(const ChainLaunch& L);
 hipError_t launch_chunk_map(const int32_t* cu, int num_seqs, int T, int C, int32_t* chunk0, int32_t* order,
                             void* stream);
 
+// Backward of the chunked prefill (kda_backward.hip): gradients of <dO, o> + <dhT, hT>.
+struct BackwardArgs {
+  const void *q, *k, *v, *g, *beta;
+  const float* h0;   // or NULL (zero)
+  const void* dO;    // like o
+  const float* dhT;  // or NULL (zero)
+  void *dq, *dk_out, *dv_out, *dg, *dbeta;  // like q, k, v, g, beta
+  float* dh0;        // or NULL (not written)
+  int B, T, H, dk, dv, chunk;
+  bool f32;
+  void* workspace;
+  void* stream;
+};
+bool chunked_backward_supported(bool f32, int dk, int dv, int chunk);
+size_t chunked_backward_workspace(bool f32, int dk, int dv, int chunk, int B, int T, int H);
+hipError_t launch_chunked_backward(const BackwardArgs& a);
+
 // Prefill: supported shape?  workspace bytes?  launch (hipErrorInvalidValue: unsupported shape).
 bool chunked_forward_supported(bool f32, int dk, int dv, int chunk);
 size_t chunked_forward_workspace(bool f32, int dk, int dv, int chunk, int64_t max_chunks, int H, int num_seqs,

@@ -250,6 +250,33 @@ kda_status kda_decode_step_fused(const void* q, const void* k, const void* v, co
                                  float* state, void* o, const kda_fusion* fusion, int B, int H, int d_k, int d_v,
                                  kda_dtype dt, void* hip_stream);
 
+/*
+ * Backward of kda_chunked_forward, for training with KDA (technical-report
+ * page, "Training"; the pages give no backward, so it is the chain rule through
+ * the chunkwise form the forward computes).  Given the adjoints d_o = dL/do
+ * and dhT = dL/dhT of a loss L, it returns
+ *   dq, dk, dg [B,T,H,d_k], dv [B,T,H,d_v], dbeta [B,T,H]   (dtype dt)   out
+ *   dh0 [B,H,d_k,d_v] fp32 (NULL: not written)                          out
+ * from the forward's inputs q, k, v, g, beta, h0 (as in kda_chunked_forward;
+ * h0 NULL = zero start) and
+ *   d_o [B,T,H,d_v] (dtype dt), dhT [B,H,d_k,d_v] fp32 (NULL = zero)    in
+ * The forward is recomputed inside the call (nothing is kept from an earlier
+ * forward call).  Supported: bf16 with d_k, d_v in {64, 128}; fp32 with
+ * d_k = d_v = 64; chunk in {16, 32, 64}; anything else returns
+ * KDA_ERR_UNSUPPORTED.  workspace: kda_chunked_backward_workspace_bytes(...)
+ * bytes, 256-byte aligned, caller-owned (it holds the recomputed per-chunk
+ * records and states and the adjoint states).  Every output is written, none
+ * is read; outputs must not overlap inputs.  Invalid calls return an error
+ * before anything is launched.
+ */
+kda_status kda_chunked_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                const float* h0, const void* d_o, const float* dhT, void* dq, void* dk, void* dv,
+                                void* dg, void* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v, int chunk,
+                                kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes kda_chunked_backward needs (0 = unsupported shape). */
+size_t kda_chunked_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt);
+
 #ifdef __cplusplus
 }
 #endif
