@@ -81,19 +81,68 @@ __device__ __forceinline__ void zero(float (&acc)[MI][NI]) {
     for (int j = 0; j < NI; ++j) acc[i][j] = 0.f;
 }
 
+// One 16x16 tile of D += A B over the contraction index k in [0, K) on MFMA: a(m, k) and b(k, n)
+// (m, n in [0, 16)) give the operand values, rounded to the operand type (bf16 with an fp32
+// accumulator, or fp32).  Contraction slots past K read as zero.  In lane (lo, grp) the result is
+// acc[r] = D[4 grp + r][lo].
+// SPLIT (bf16 only): each operand value x is carried as bf16(x) + bf16(x - bf16(x)) and three
+// products are accumulated (hi hi + hi lo + lo hi), for about 16 significant bits where a sum cancels.
+template <bool F32, int K, bool SPLIT = false, typename FA, typename FB>
+__device__ __forceinline__ f32x4 tile_mm(FA&& a, FB&& b, f32x4 acc) {
+  using O = Op<F32>;
+  const int lane = threadIdx.x & 63, lo = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < O::nks(K); ++s) {
+    typename O::Frag fa, fb, fal, fbl;
+    if constexpr (F32) {
+      const int k = O::kidx(s, grp, 0);
+      fa = a(lo, k);
+      fb = b(k, lo);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = O::kidx(s, grp, j);
+        const bool ok = (K % 32 == 0) || k < K;
+        const float x = ok ? a(lo, k) : 0.f, y = ok ? b(k, lo) : 0.f;
+        fa[j] = (__bf16)x;
+        fb[j] = (__bf16)y;
+        if constexpr (SPLIT) {
+          fal[j] = (__bf16)(x - (float)fa[j]);
+          fbl[j] = (__bf16)(y - (float)fb[j]);
+        }
+      }
+    }
+    acc = O::mma(fa, fb, acc);
+    if constexpr (!F32 && SPLIT) {
+      acc = O::mma(fa, fbl, acc);
+      acc = O::mma(fal, fb, acc);
+    }
+  }
+  return acc;
+}
+
+// slot j of a bf16 fragment pair: hi = bf16(x), lo = bf16(x - hi)
+__device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int j) {
+  hi[j] = (__bf16)x;
+  lo[j] = (__bf16)(x - (float)hi[j]);
+}
+
 // ------------------------------------------------------------------------------------------------
-// 2. adjoint chain.  One workgroup per (sequence, head, 32 value columns); the record's first four
-// fields (-W, Q Gamma, Kd^T, P) are copied to LDS as stored, dO's slice and dU in fp32.
+// 2. adjoint chain.  One 256-thread workgroup per (sequence, head, 32 value columns), products on
+// MFMA.  The record's first four fields (-W, Q Gamma, Kd^T, P) are copied to LDS as stored; dO's
+// slice and dU are held in the operand type, the adjoint state dS in fp32 (rounded to the operand
+// type only where it is an operand).
 template <bool F32, int DK, int DV, int C>
 struct BChainCfg {
   using R = Rec<F32, DK, DV, C>;
   using E = typename Op<F32>::E;
-  static constexpr int WS = 32, NSL = DV / WS, CP = R::CP, SS = WS + 1;
-  static constexpr int OFF_REC = 0;                          // E [R::UT]  (NW, QG, KPT, P)
-  static constexpr int OFF_GAM = (int)(R::UT * sizeof(E));   // f32 [DK]
-  static constexpr int OFF_DO = OFF_GAM + DK * 4;            // f32 [C][WS]
-  static constexpr int OFF_DU = OFF_DO + C * WS * 4;         // f32 [C][WS]
-  static constexpr int OFF_DS = OFF_DU + C * WS * 4;         // f32 [DK][SS]
+  static constexpr int ES = sizeof(E);
+  static constexpr int WS = 32, NSL = DV / WS, CP = R::CP, SE = WS + 16 / ES, SS = WS + 4;
+  static constexpr int OFF_REC = 0;                          // E [R::UT]  (-W, Q Gamma, Kd^T, P)
+  static constexpr int OFF_GAM = (int)(R::UT * ES);          // f32 [DK]
+  static constexpr int OFF_DO = OFF_GAM + DK * 4;            // E [C][SE]
+  static constexpr int OFF_DU = OFF_DO + ((C * SE * ES + 15) & ~15);  // E [C][SE]
+  static constexpr int OFF_DS = OFF_DU + ((C * SE * ES + 15) & ~15);  // f32 [DK][SS]
   static constexpr int TOTAL = OFF_DS + DK * SS * 4;
   static_assert(OFF_GAM % 16 == 0, "record prefix is a whole number of 16-byte vectors");
   static_assert(TOTAL <= 160 * 1024, "LDS");
@@ -104,15 +153,15 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
   using Cf = BChainCfg<F32, DK, DV, C>;
   using R = typename Cf::R;
   using E = typename Cf::E;
-  constexpr int WS = Cf::WS, CP = Cf::CP, SS = Cf::SS;
+  constexpr int WS = Cf::WS, CP = Cf::CP, SE = Cf::SE, SS = Cf::SS;
   __shared__ __align__(16) unsigned char smem[Cf::TOTAL];
   const E* sR = reinterpret_cast<const E*>(smem + Cf::OFF_REC);
   float* sGam = reinterpret_cast<float*>(smem + Cf::OFF_GAM);
-  float* sdO = reinterpret_cast<float*>(smem + Cf::OFF_DO);
-  float* sdU = reinterpret_cast<float*>(smem + Cf::OFF_DU);
+  E* sdO = reinterpret_cast<E*>(smem + Cf::OFF_DO);
+  E* sdU = reinterpret_cast<E*>(smem + Cf::OFF_DU);
   float* sdS = reinterpret_cast<float*>(smem + Cf::OFF_DS);
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lo = tid & 15, grp = (tid >> 4) & 3;
   const int unit = blockIdx.x / Cf::NSL, col0 = (blockIdx.x % Cf::NSL) * WS;
   const int H = p.H, b = unit / H, h = unit - b * H;
   for (int e = tid; e < DK * WS; e += 256) {
@@ -134,41 +183,34 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
     const int64_t orow = ((int64_t)b * p.T + (int64_t)ch * C) * H + h;
     for (int e = tid; e < C * WS; e += 256) {
       const int r = e / WS, j = e - r * WS;
-      sdO[e] = r < nr ? ldg<F32>(p.dO, (orow + (int64_t)r * H) * DV + col0 + j) : 0.f;
+      sdO[r * SE + j] = (E)(r < nr ? ldg<F32>(p.dO, (orow + (int64_t)r * H) * DV + col0 + j) : 0.f);
     }
     __syncthreads();
     // dU[i][j] = sum_{r >= i} P[r][i] dO[r][j] + sum_c Kd^T[c][i] dS[c][j]
-    for (int mt = tid; mt < (C / 4) * (WS / 2); mt += 256) {
-      const int i0 = 4 * (mt / (WS / 2)), j0 = 2 * (mt % (WS / 2));
-      float acc[4][2];
-      zero(acc);
-      // rows r >= i0 lie in P's written tiles; above the diagonal inside a 16-row tile P is zero
-      mac(acc, i0, C, [&](int i, int r) { return tf(sR[R::P + r * CP + i0 + i]); },
-          [&](int r, int j) { return sdO[r * WS + j0 + j]; });
-      mac(acc, 0, DK, [&](int i, int c) { return tf(sR[R::KPT + c * CP + i0 + i]); },
-          [&](int c, int j) { return sdS[c * SS + j0 + j]; });
+    // (P is read only where r >= i: its tiles above the diagonal are not all written)
+    for (int t = wave; t < (C / 16) * (WS / 16); t += 4) {
+      const int i0 = 16 * (t / (WS / 16)), j0 = 16 * (t % (WS / 16));
+      f32x4 acc = zero4();
+      acc = tile_mm<F32, C>([&](int m, int k) { return k >= i0 + m ? tf(sR[R::P + k * CP + i0 + m]) : 0.f; },
+                            [&](int k, int n) { return tf(sdO[k * SE + j0 + n]); }, acc);
+      acc = tile_mm<F32, DK>([&](int m, int k) { return tf(sR[R::KPT + k * CP + i0 + m]); },
+                             [&](int k, int n) { return sdS[k * SS + j0 + n]; }, acc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) sdU[(i0 + i) * WS + j0 + j] = acc[i][j];
+      for (int r = 0; r < 4; ++r) sdU[(i0 + 4 * grp + r) * SE + j0 + lo] = (E)acc[r];
     }
     __syncthreads();
     // dS[c][j] <- e^{gl_c} dS[c][j] + sum_r QG[r][c] dO[r][j] + sum_i (-W)[i][c] dU[i][j]
-    for (int mt = tid; mt < (DK / 4) * (WS / 4); mt += 256) {
-      const int c0 = 4 * (mt / (WS / 4)), j0 = 4 * (mt % (WS / 4));
-      float acc[4][4];
+    for (int t = wave; t < (DK / 16) * (WS / 16); t += 4) {
+      const int c0 = 16 * (t / (WS / 16)), j0 = 16 * (t % (WS / 16));
+      f32x4 acc;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int r = 0; r < 4; ++r) acc[r] = sGam[c0 + 4 * grp + r] * sdS[(c0 + 4 * grp + r) * SS + j0 + lo];
+      acc = tile_mm<F32, C>([&](int m, int k) { return tf(sR[R::QG + k * DK + c0 + m]); },
+                            [&](int k, int n) { return tf(sdO[k * SE + j0 + n]); }, acc);
+      acc = tile_mm<F32, C>([&](int m, int k) { return tf(sR[R::NW + k * DK + c0 + m]); },
+                            [&](int k, int n) { return tf(sdU[k * SE + j0 + n]); }, acc);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = sGam[c0 + i] * sdS[(c0 + i) * SS + j0 + j];
-      mac(acc, 0, C, [&](int i, int r) { return tf(sR[R::QG + r * DK + c0 + i]); },
-          [&](int r, int j) { return sdO[r * WS + j0 + j]; });
-      mac(acc, 0, C, [&](int i, int r) { return tf(sR[R::NW + r * DK + c0 + i]); },
-          [&](int r, int j) { return sdU[r * WS + j0 + j]; });
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sdS[(c0 + i) * SS + j0 + j] = acc[i][j];
+      for (int r = 0; r < 4; ++r) sdS[(c0 + 4 * grp + r) * SS + j0 + lo] = acc[r];
     }
   }
   __syncthreads();
@@ -180,40 +222,48 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// 3. products with the chunk's start state S0 and end adjoint dS1, one workgroup per (chunk, head).
-// S0, dS1 and dO are staged in LDS in the input type, U and dU in fp32; rows padded by 16 bytes.
+// 3. products with the chunk's start state S0 and end adjoint dS1, one 512-thread workgroup per
+// (chunk, head), on MFMA.  S0, dS1, dO, U and dU are staged in LDS in the operand type (rows padded
+// by 16 bytes); the record's -W, then P (masked to its lower triangle) and Kd^T, share one region.
 template <bool F32, int DK, int DV, int C>
 struct BStateCfg {
   using R = Rec<F32, DK, DV, C>;
   using E = typename Op<F32>::E;
   using GL = GradLayout<DK, DV, C>;
-  static constexpr int ES = sizeof(E), SE = DV + 16 / ES, SF = DV + 4;
-  static constexpr int OFF_S0 = 0;                       // E [DK][SE]
-  static constexpr int OFF_DS = OFF_S0 + DK * SE * ES;   // E [DK][SE]
-  static constexpr int OFF_DO = OFF_DS + DK * SE * ES;   // E [C][SE]
-  static constexpr int OFF_U = OFF_DO + C * SE * ES;     // f32 [C][SF]
-  static constexpr int OFF_DU = OFF_U + C * SF * 4;      // f32 [C][SF]
-  static constexpr int TOTAL = OFF_DU + C * SF * 4;
+  static constexpr int NTH = 512, ES = sizeof(E);
+  static constexpr int SV = DV + 16 / ES, SK = DK + 16 / ES, SC = C + 16 / ES;
+  static constexpr int OFF_S0 = 0;                                  // E [DK][SV]
+  static constexpr int OFF_DS = OFF_S0 + DK * SV * ES;              // E [DK][SV]
+  static constexpr int OFF_DO = OFF_DS + DK * SV * ES;              // E [C][SV]
+  static constexpr int OFF_U = OFF_DO + C * SV * ES;                // E [C][SV]
+  static constexpr int OFF_DU = OFF_U + C * SV * ES;                // E [C][SV]
+  static constexpr int OFF_X = OFF_DU + C * SV * ES;                // E: -W [C][SK], then P [C][SC] + Kd^T [DK][SC]
+  static constexpr int X_BYTES = (C * SK > (C + DK) * SC ? C * SK : (C + DK) * SC) * ES;
+  static constexpr int TOTAL = OFF_X + X_BYTES;
+  static_assert(OFF_X % 16 == 0, "alignment");
   static_assert(TOTAL <= 160 * 1024, "LDS");
 };
 
 template <bool F32, int DK, int DV, int C>
-__global__ __launch_bounds__(256) void bwd_state_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
   using Cf = BStateCfg<F32, DK, DV, C>;
   using R = typename Cf::R;
   using E = typename Cf::E;
   using GL = typename Cf::GL;
-  constexpr int SE = Cf::SE, SF = Cf::SF, CP = R::CP;
+  constexpr int SV = Cf::SV, SK = Cf::SK, SC = Cf::SC, CP = R::CP, NTH = Cf::NTH;
   __shared__ __align__(16) unsigned char smem[Cf::TOTAL];
   E* sS0 = reinterpret_cast<E*>(smem + Cf::OFF_S0);
   E* sdS = reinterpret_cast<E*>(smem + Cf::OFF_DS);
   E* sdO = reinterpret_cast<E*>(smem + Cf::OFF_DO);
-  float* sU = reinterpret_cast<float*>(smem + Cf::OFF_U);
-  float* sdU = reinterpret_cast<float*>(smem + Cf::OFF_DU);
+  E* sU = reinterpret_cast<E*>(smem + Cf::OFF_U);
+  E* sdU = reinterpret_cast<E*>(smem + Cf::OFF_DU);
+  E* sNW = reinterpret_cast<E*>(smem + Cf::OFF_X);
+  E* sP = reinterpret_cast<E*>(smem + Cf::OFF_X);
+  E* sKPT = sP + C * SC;
 
   const int64_t item = blockIdx.x;
   if (item >= p.items) return;
-  const int tid = threadIdx.x, H = p.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lo = tid & 15, grp = (tid >> 4) & 3, H = p.H;
   const int64_t cg = item / H;
   const int h = (int)(item - cg * H), b = (int)(cg / p.nch), ch = (int)(cg - (int64_t)b * p.nch);
   const int64_t unit = (int64_t)b * H + h;
@@ -225,147 +275,178 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(BwdParams p) {
   const float* ds1 = p.dstates + (unit * p.nch + ch) * DK * DV;
   float* gr = p.grads + item * GL::FLOATS;
 
-  for (int e = tid; e < DK * DV / 4; e += 256) {
+  for (int e = tid; e < DK * DV / 4; e += NTH) {
     const int c = (4 * e) / DV, j = 4 * e - c * DV;
     const float4 a = s0 ? reinterpret_cast<const float4*>(s0)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
     const float4 d = reinterpret_cast<const float4*>(ds1)[e];
-    E* pa = sS0 + c * SE + j;
-    E* pd = sdS + c * SE + j;
+    E* pa = sS0 + c * SV + j;
+    E* pd = sdS + c * SV + j;
     pa[0] = (E)a.x; pa[1] = (E)a.y; pa[2] = (E)a.z; pa[3] = (E)a.w;
     pd[0] = (E)d.x; pd[1] = (E)d.y; pd[2] = (E)d.z; pd[3] = (E)d.w;
   }
   const int64_t orow = ((int64_t)b * p.T + (int64_t)ch * C) * H + h;
-  for (int e = tid; e < C * DV; e += 256) {
+  for (int e = tid; e < C * DV; e += NTH) {
     const int r = e / DV, j = e - r * DV;
-    sdO[r * SE + j] = (E)(r < nr ? ldg<F32>(p.dO, (orow + (int64_t)r * H) * DV + j) : 0.f);
+    sdO[r * SV + j] = (E)(r < nr ? ldg<F32>(p.dO, (orow + (int64_t)r * H) * DV + j) : 0.f);
+  }
+  for (int e = tid; e < C * DK; e += NTH) {
+    const int r = e / DK, c = e - r * DK;
+    sNW[r * SK + c] = rec[R::NW + e];
   }
   __syncthreads();
-  // U[r][j] = U~[r][j] + sum_c (-W)[r][c] S0[c][j];  dU[r][j] = sum_{s >= r} P[s][r] dO[s][j] + sum_c Kd^T[c][r] dS1[c][j]
-  for (int mt = tid; mt < (C / 4) * (DV / 4); mt += 256) {
-    const int r0 = 4 * (mt / (DV / 4)), j0 = 4 * (mt % (DV / 4));
-    float acc[4][4];
+  // U = U~ + (-W) S0  (U~ from the record's U~^T)
+  for (int t = wave; t < (C / 16) * (DV / 16); t += NTH / 64) {
+    const int i0 = 16 * (t / (DV / 16)), j0 = 16 * (t % (DV / 16));
+    f32x4 acc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 4; ++r) acc[r] = tf(rec[R::UT + (j0 + lo) * C + i0 + 4 * grp + r]);
+    acc = tile_mm<F32, DK>([&](int m, int k) { return tf(sNW[(i0 + m) * SK + k]); },
+                           [&](int k, int n) { return tf(sS0[k * SV + j0 + n]); }, acc);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = tf(rec[R::UT + (j0 + j) * C + r0 + i]);
-    mac(acc, 0, DK, [&](int i, int c) { return tf(rec[R::NW + (r0 + i) * DK + c]); },
-        [&](int c, int j) { return tf(sS0[c * SE + j0 + j]); });
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sU[(r0 + i) * SF + j0 + j] = acc[i][j];
-    zero(acc);
-    mac(acc, r0, C, [&](int i, int s) { return tf(rec[R::P + s * CP + r0 + i]); },
-        [&](int s, int j) { return tf(sdO[s * SE + j0 + j]); });
-    mac(acc, 0, DK, [&](int i, int c) { return tf(rec[R::KPT + c * CP + r0 + i]); },
-        [&](int c, int j) { return tf(sdS[c * SE + j0 + j]); });
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sdU[(r0 + i) * SF + j0 + j] = acc[i][j];
-        gr[GL::DU + (r0 + i) * DV + j0 + j] = acc[i][j];
-      }
+    for (int r = 0; r < 4; ++r) sU[(i0 + 4 * grp + r) * SV + j0 + lo] = (E)acc[r];
+  }
+  // e^{gl} rowsum(S0 . dS1)
+  for (int c = tid; c < DK; c += NTH) {
+    float sum = 0.f;
+    for (int j = 0; j < DV; ++j) sum = fmaf(tf(sS0[c * SV + j]), tf(sdS[c * SV + j]), sum);
+    gr[GL::DGL + c] = gam[c] * sum;
   }
   __syncthreads();
-  // dP[r][i] = sum_j dO[r][j] U[i][j] for i <= r
-  for (int mt = tid; mt < (C / 4) * (C / 4); mt += 256) {
-    const int r0 = 4 * (mt / (C / 4)), i0 = 4 * (mt % (C / 4));
-    float acc[4][4];
-    zero(acc);
-    if (i0 <= r0 + 3)
-      mac(acc, 0, DV, [&](int i, int j) { return tf(sdO[(r0 + i) * SE + j]); },
-          [&](int j, int n) { return sU[(i0 + n) * SF + j]; });
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int n = 0; n < 4; ++n) gr[GL::DP + (r0 + i) * C + i0 + n] = (i0 + n <= r0 + i) ? acc[i][n] : 0.f;
+  for (int e = tid; e < C * C; e += NTH) {
+    const int s_ = e / C, r = e - s_ * C;
+    sP[s_ * SC + r] = r <= s_ ? rec[R::P + s_ * CP + r] : (E)0.f;
   }
-  // d(Q Gamma) = dO S0^T, dKd = U dS1^T, dW = -dU S0^T   ([C][DK] each)
-  for (int mt = tid; mt < (C / 4) * (DK / 4); mt += 256) {
-    const int r0 = 4 * (mt / (DK / 4)), c0 = 4 * (mt % (DK / 4));
-    float a1[4][4], a2[4][4], a3[4][4];
-    zero(a1);
-    zero(a2);
-    zero(a3);
-    for (int j = 0; j < DV; ++j) {
-      float o4[4], u4[4], du4[4], s4[4], d4[4];
+  for (int e = tid; e < DK * C; e += NTH) {
+    const int c = e / C, r = e - c * C;
+    sKPT[c * SC + r] = rec[R::KPT + c * CP + r];
+  }
+  __syncthreads();
+  // dU[r][j] = sum_{s >= r} P[s][r] dO[s][j] + sum_c Kd^T[c][r] dS1[c][j]
+  for (int t = wave; t < (C / 16) * (DV / 16); t += NTH / 64) {
+    const int i0 = 16 * (t / (DV / 16)), j0 = 16 * (t % (DV / 16));
+    f32x4 acc = zero4();
+    acc = tile_mm<F32, C>([&](int m, int k) { return tf(sP[k * SC + i0 + m]); },
+                          [&](int k, int n) { return tf(sdO[k * SV + j0 + n]); }, acc);
+    acc = tile_mm<F32, DK>([&](int m, int k) { return tf(sKPT[k * SC + i0 + m]); },
+                           [&](int k, int n) { return tf(sdS[k * SV + j0 + n]); }, acc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o4[i] = tf(sdO[(r0 + i) * SE + j]);
-        u4[i] = sU[(r0 + i) * SF + j];
-        du4[i] = sdU[(r0 + i) * SF + j];
-        s4[i] = tf(sS0[(c0 + i) * SE + j]);
-        d4[i] = tf(sdS[(c0 + i) * SE + j]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          a1[i][n] = fmaf(o4[i], s4[n], a1[i][n]);
-          a2[i][n] = fmaf(u4[i], d4[n], a2[i][n]);
-          a3[i][n] = fmaf(du4[i], s4[n], a3[i][n]);
-        }
+    for (int r = 0; r < 4; ++r) {
+      sdU[(i0 + 4 * grp + r) * SV + j0 + lo] = (E)acc[r];
+      gr[GL::DU + (i0 + 4 * grp + r) * DV + j0 + lo] = acc[r];
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int o = (r0 + i) * DK + c0 + n;
-        gr[GL::DQG + o] = a1[i][n];
-        gr[GL::DKD + o] = a2[i][n];
-        gr[GL::DW + o] = -a3[i][n];
-      }
   }
-  for (int c = tid; c < DK; c += 256) {
-    float s = 0.f;
-    for (int j = 0; j < DV; ++j) s = fmaf(tf(sS0[c * SE + j]), tf(sdS[c * SE + j]), s);
-    gr[GL::DGL + c] = gam[c] * s;
+  __syncthreads();
+  // dP = lowerIncl(dO U^T)
+  for (int t = wave; t < (C / 16) * (C / 16); t += NTH / 64) {
+    const int i0 = 16 * (t / (C / 16)), n0 = 16 * (t % (C / 16));
+    f32x4 acc = zero4();
+    if (n0 <= i0)
+      acc = tile_mm<F32, DV>([&](int m, int k) { return tf(sdO[(i0 + m) * SV + k]); },
+                             [&](int k, int n) { return tf(sU[(n0 + n) * SV + k]); }, acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = i0 + 4 * grp + r, col = n0 + lo;
+      gr[GL::DP + row * C + col] = col <= row ? acc[r] : 0.f;
+    }
+  }
+  // d(Q Gamma) = dO S0^T, dKd = U dS1^T, dW = -dU S0^T
+  for (int t = wave; t < 3 * (C / 16) * (DK / 16); t += NTH / 64) {
+    const int which = t / ((C / 16) * (DK / 16)), tt = t - which * ((C / 16) * (DK / 16));
+    const int i0 = 16 * (tt / (DK / 16)), c0 = 16 * (tt % (DK / 16));
+    const E* A = which == 0 ? sdO : which == 1 ? sU : sdU;
+    const E* Bt = which == 1 ? sdS : sS0;
+    f32x4 acc = tile_mm<F32, DV>([&](int m, int k) { return tf(A[(i0 + m) * SV + k]); },
+                                 [&](int k, int n) { return tf(Bt[(c0 + n) * SV + k]); }, zero4());
+    const int64_t off = which == 0 ? GL::DQG : which == 1 ? GL::DKD : GL::DW;
+    const float sg = which == 2 ? -1.f : 1.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) gr[off + (i0 + 4 * grp + r) * DK + c0 + lo] = sg * acc[r];
   }
 }
 
 // ------------------------------------------------------------------------------------------------
-// 4. through the UT transform, one 512-thread workgroup per (chunk, head).
-// Ownership for [C][DK] results: thread t owns channel t % DK and rows t / DK + NRG m.
+// 4. through the UT transform, one 512-thread workgroup per (chunk, head).  [C][DK] results live in
+// MFMA accumulator tiles: wave w owns tiles w + 8 q of the (C/16) x (DK/16) grid.  Exponent
+// differences are taken against a per-16-row-tile reference so that every factor is finite in fp32
+// at g >= -5: for a row tile, R = G just before it (row factors e^{G_r - R} in [e^{-80}, 1], column
+// factors e^{R - G_i} <= e^{80} for i in the tile and <= 1 before it); for a column tile, R' = G at
+// its last row (the mirror image).
 template <bool F32, int DK, int DV, int C>
 struct BIntraCfg {
   using E = typename Op<F32>::E;
   static constexpr int NTH = 512, ES = sizeof(E);
-  static constexpr int NRG = NTH / DK, RPT = C / NRG;            // row groups, rows per thread
-  static constexpr int NRGV = NTH / DV, RPTV = C / NRGV;
-  static constexpr int NCS = NTH / C, CPS = DK / NCS;            // channel slices per row (Ekk, dT)
-  static constexpr int NL = (NTH / C < C) ? NTH / C : C;         // lanes per column of the inverse
-  static constexpr int SK = DK + 4 / ES;                         // E row stride (one bank of skew)
-  static constexpr int SG = DK + 1, SV = DV + 4 / ES, SM = C + 1;
-  static constexpr int OFF_G = 0;                                // f32 [C][SG]  G, later dG
-  static constexpr int OFF_Q = OFF_G + C * SG * 4;               // E [C][SK]
-  static constexpr int OFF_K = OFF_Q + ((C * SK * ES + 15) & ~15);
-  static constexpr int OFF_V = OFF_K + ((C * SK * ES + 15) & ~15);
-  static constexpr int OFF_EKK = OFF_V + ((C * SV * ES + 15) & ~15);  // f32 [C][SM] Ekk (strict lower)
+  static constexpr int NTC = C / 16, NTK = DK / 16, NTV = DV / 16;
+  static constexpr int NTILE = NTC * NTK, MAXT = (NTILE + 7) / 8, NPAIR = NTC * (NTC + 1) / 2;
+  static constexpr int NPART = NTH / DK, RPP = C / NPART;       // scans: row parts per channel
+  static constexpr int NL = (NTH / C < C) ? NTH / C : C;        // lanes per column of the inverse
+  static constexpr int SG = DK + 4, SK = DK + 16 / ES, SV = DV + 16 / ES, SM = C + 4;
+  static constexpr int OFF_G = 0;                                // f32 [C][SG]  g, G, then dG
+  static constexpr int OFF_K = OFF_G + C * SG * 4;               // E [C][SK]
+  static constexpr int OFF_Q = OFF_K + C * SK * ES;              // E [C][SK]
+  static constexpr int OFF_V = OFF_Q + C * SK * ES;              // E [C][SV]
+  static constexpr int OFF_EKK = OFF_V + C * SV * ES;            // f32 [C][SM] Ekk (strict lower)
   static constexpr int OFF_L = OFF_EKK + C * SM * 4;             // f32 [C][SM] L = (I + A)^{-1}
   static constexpr int OFF_M3 = OFF_L + C * SM * 4;              // f32 [C][SM] dT -> dL -> dA -> dEkk
   static constexpr int OFF_M4 = OFF_M3 + C * SM * 4;             // f32 [C][SM] L^T dL, then dEqk
   static constexpr int OFF_BETA = OFF_M4 + C * SM * 4;           // f32 [C]
   static constexpr int OFF_DB = OFF_BETA + C * 4;                // f32 [C]
-  static constexpr int OFF_RED = OFF_DB + C * 4;                 // f32 [NRG][DK]
-  static constexpr int OFF_DGL = OFF_RED + NRG * DK * 4;         // f32 [DK]
+  static constexpr int OFF_RED = OFF_DB + C * 4;                 // f32 [NTC][DK]
+  static constexpr int OFF_SCAN = OFF_RED + NTC * DK * 4;        // f32 [NPART][DK]
+  static constexpr int OFF_DGL = OFF_SCAN + NPART * DK * 4;      // f32 [DK]
   static constexpr int TOTAL = OFF_DGL + DK * 4;
-  static_assert(NRG * DK == NTH && RPT * NRG == C && NCS * CPS == DK && NCS * C == NTH, "ownership");
-  static_assert(NRGV * DV == NTH && RPTV * NRGV == C, "ownership");
+  static_assert(NPART * DK == NTH && RPP * NPART == C && NL * C <= NTH, "thread layout");
+  static_assert((C * SK * ES) % 16 == 0 && (C * SV * ES) % 16 == 0, "alignment");
   static_assert(TOTAL <= 160 * 1024, "LDS");
 };
+
+// (b, a) of the a-th ... pair index t over the lower triangle of tiles, a <= b
+__device__ __forceinline__ void tri_pair(int t, int& b, int& a) {
+  b = 0;
+  while (t > b) {
+    t -= b + 1;
+    ++b;
+  }
+  a = t;
+}
+
+// Inclusive prefix sums down the rows of an LDS [C][ld] fp32 array, per channel, in place (reverse:
+// suffix sums).  Thread (channel tid % DK, part tid / DK) scans RPP rows; the parts' totals go
+// through `tot` [NPART][DK].
+template <int DK, int C, int NPART, int RPP, bool REV>
+__device__ __forceinline__ void scan_rows(float* a, int ld, float* tot, int tid) {
+  const int c = tid % DK, part = tid / DK;
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < RPP; ++u) {
+    const int r = REV ? C - 1 - (part * RPP + u) : part * RPP + u;
+    s += a[r * ld + c];
+    a[r * ld + c] = s;
+  }
+  tot[part * DK + c] = s;
+  __syncthreads();
+  float off = 0.f;
+  for (int q = 0; q < part; ++q) off += tot[q * DK + c];
+#pragma unroll
+  for (int u = 0; u < RPP; ++u) {
+    const int r = REV ? C - 1 - (part * RPP + u) : part * RPP + u;
+    a[r * ld + c] += off;
+  }
+  __syncthreads();
+}
 
 template <bool F32, int DK, int DV, int C>
 __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   using Cf = BIntraCfg<F32, DK, DV, C>;
   using E = typename Cf::E;
+  using O = Op<F32>;
+  using Frag = typename O::Frag;
   using GL = GradLayout<DK, DV, C>;
-  constexpr int NRG = Cf::NRG, RPT = Cf::RPT, NCS = Cf::NCS, CPS = Cf::CPS, NL = Cf::NL;
-  constexpr int SK = Cf::SK, SG = Cf::SG, SV = Cf::SV, SM = Cf::SM;
+  constexpr int NTK = Cf::NTK, NTV = Cf::NTV, NTILE = Cf::NTILE, MAXT = Cf::MAXT, NL = Cf::NL;
+  constexpr int SG = Cf::SG, SK = Cf::SK, SV = Cf::SV, SM = Cf::SM, NTH = Cf::NTH;
   __shared__ __align__(16) unsigned char smem[Cf::TOTAL];
   float* sG = reinterpret_cast<float*>(smem + Cf::OFF_G);
-  E* sQ = reinterpret_cast<E*>(smem + Cf::OFF_Q);
   E* sK = reinterpret_cast<E*>(smem + Cf::OFF_K);
+  E* sQ = reinterpret_cast<E*>(smem + Cf::OFF_Q);
   E* sV = reinterpret_cast<E*>(smem + Cf::OFF_V);
   float* sEkk = reinterpret_cast<float*>(smem + Cf::OFF_EKK);
   float* sL = reinterpret_cast<float*>(smem + Cf::OFF_L);
@@ -374,61 +455,54 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   float* sBeta = reinterpret_cast<float*>(smem + Cf::OFF_BETA);
   float* sDb = reinterpret_cast<float*>(smem + Cf::OFF_DB);
   float* sRed = reinterpret_cast<float*>(smem + Cf::OFF_RED);
+  float* sScan = reinterpret_cast<float*>(smem + Cf::OFF_SCAN);
   float* sDgl = reinterpret_cast<float*>(smem + Cf::OFF_DGL);
 
   const int64_t item = blockIdx.x;
   if (item >= p.items) return;
-  const int tid = threadIdx.x, H = p.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lo = tid & 15, grp = (tid >> 4) & 3, H = p.H;
   const int64_t cg = item / H;
   const int h = (int)(item - cg * H), b = (int)(cg / p.nch), ch = (int)(cg - (int64_t)b * p.nch);
   const int nr = min(C, p.T - ch * C);
   const int64_t row0 = ((int64_t)b * p.T + (int64_t)ch * C) * H + h;  // (token, head) row of the chunk's first token
   const float* gr = p.grads + item * GL::FLOATS;
 
-  // ---- stage q, k, v, beta (rows past the chunk's end are zero) and G = cumsum(g) per channel
-  for (int e = tid; e < C * DK; e += Cf::NTH) {
+  // ---- stage q, k, v, g, beta (rows past the chunk's end are zero), then G = cumsum(g)
+  for (int e = tid; e < C * DK; e += NTH) {
     const int r = e / DK, c = e - r * DK;
     const bool ok = r < nr;
-    sQ[r * SK + c] = (E)(ok ? ldg<F32>(p.q, (row0 + (int64_t)r * H) * DK + c) : 0.f);
-    sK[r * SK + c] = (E)(ok ? ldg<F32>(p.k, (row0 + (int64_t)r * H) * DK + c) : 0.f);
+    const int64_t gi = (row0 + (int64_t)r * H) * DK + c;
+    sQ[r * SK + c] = (E)(ok ? ldg<F32>(p.q, gi) : 0.f);
+    sK[r * SK + c] = (E)(ok ? ldg<F32>(p.k, gi) : 0.f);
+    sG[r * SG + c] = ok ? ldg<F32>(p.g, gi) : 0.f;
   }
-  for (int e = tid; e < C * DV; e += Cf::NTH) {
+  for (int e = tid; e < C * DV; e += NTH) {
     const int r = e / DV, j = e - r * DV;
     sV[r * SV + j] = (E)(r < nr ? ldg<F32>(p.v, (row0 + (int64_t)r * H) * DV + j) : 0.f);
   }
   if (tid < C) sBeta[tid] = tid < nr ? ldg<F32>(p.beta, row0 + (int64_t)tid * H) : 0.f;
-  if (tid < DK) {
-    float s = 0.f;
-    for (int r = 0; r < C; ++r) {
-      s += r < nr ? ldg<F32>(p.g, (row0 + (int64_t)r * H) * DK + tid) : 0.f;
-      sG[r * SG + tid] = s;
+  __syncthreads();
+  scan_rows<DK, C, Cf::NPART, Cf::RPP, false>(sG, SG, sScan, tid);
+
+  // ---- Ekk = strictLower(K e^{G - R_b}) (K e^{R_b - G})^T per tile pair (b, a), a <= b
+  for (int t = wave; t < Cf::NPAIR; t += 8) {
+    int tb, ta;
+    tri_pair(t, tb, ta);
+    const int r0 = 16 * tb, i0 = 16 * ta;
+    const float* Rb = tb > 0 ? sG + (r0 - 1) * SG : nullptr;
+    f32x4 acc = tile_mm<F32, DK, true>(
+        [&](int m, int k) { return tf(sK[(r0 + m) * SK + k]) * __expf(sG[(r0 + m) * SG + k] - (Rb ? Rb[k] : 0.f)); },
+        [&](int k, int n) { return tf(sK[(i0 + n) * SK + k]) * __expf((Rb ? Rb[k] : 0.f) - sG[(i0 + n) * SG + k]); },
+        zero4());
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = r0 + 4 * grp + r, col = i0 + lo;
+      sEkk[row * SM + col] = col < row ? acc[r] : 0.f;
     }
   }
-  __syncthreads();
-
-  // ---- Ekk[r][i] = sum_c k_r[c] k_i[c] e^{G_r[c] - G_i[c]} for i < r: thread (r, channel slice),
-  // slices reduced across NCS neighbouring lanes
-  {
-    const int r = tid / NCS, cs = tid - r * NCS;
-    float kr[CPS], gr_[CPS];
-#pragma unroll
-    for (int m = 0; m < CPS; ++m) {
-      kr[m] = tf(sK[r * SK + cs + NCS * m]);
-      gr_[m] = sG[r * SG + cs + NCS * m];
-    }
-    for (int i = 0; i < C; ++i) {
-      float s = 0.f;
-      if (i < r) {
-#pragma unroll
-        for (int m = 0; m < CPS; ++m) {
-          const int c = cs + NCS * m;
-          s = fmaf(kr[m] * tf(sK[i * SK + c]), __expf(gr_[m] - sG[i * SG + c]), s);
-        }
-      }
-#pragma unroll
-      for (int o = 1; o < NCS; o <<= 1) s += __shfl_xor(s, o, NCS);
-      if (cs == 0) sEkk[r * SM + i] = s;  // 0 on and above the diagonal
-    }
+  for (int e = tid; e < C * C; e += NTH) {
+    const int r = e / C, i = e - r * C;
+    if ((i >> 4) > (r >> 4)) sEkk[r * SM + i] = 0.f;
   }
   __syncthreads();
 
@@ -454,56 +528,57 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  // ---- dT[r][i] = sum_c dW[r][c] K[i][c] e^{G_i[c]} + sum_j dU[r][j] V[i][j] for i <= r
-  {
-    const int r = tid / NCS, cs = tid - r * NCS;
-    constexpr int VPS = DV / NCS;
-    float w[CPS], du[VPS];
+  // ---- dT = lowerIncl(dW (K Gamma)^T + dU V^T) into M3
+  for (int t = wave; t < Cf::NPAIR; t += 8) {
+    int tb, ta;
+    tri_pair(t, tb, ta);
+    const int r0 = 16 * tb, i0 = 16 * ta;
+    f32x4 acc = tile_mm<F32, DK, true>([&](int m, int k) { return gr[GL::DW + (r0 + m) * DK + k]; },
+                                 [&](int k, int n) { return tf(sK[(i0 + n) * SK + k]) * __expf(sG[(i0 + n) * SG + k]); },
+                                 zero4());
+    acc = tile_mm<F32, DV, true>([&](int m, int k) { return gr[GL::DU + (r0 + m) * DV + k]; },
+                           [&](int k, int n) { return tf(sV[(i0 + n) * SV + k]); }, acc);
 #pragma unroll
-    for (int m = 0; m < CPS; ++m) w[m] = gr[GL::DW + r * DK + cs + NCS * m];
-#pragma unroll
-    for (int m = 0; m < VPS; ++m) du[m] = gr[GL::DU + r * DV + cs + NCS * m];
-    for (int i = 0; i < C; ++i) {
-      float s = 0.f;
-      if (i <= r) {
-#pragma unroll
-        for (int m = 0; m < CPS; ++m) {
-          const int c = cs + NCS * m;
-          s = fmaf(w[m] * tf(sK[i * SK + c]), __expf(sG[i * SG + c]), s);
-        }
-#pragma unroll
-        for (int m = 0; m < VPS; ++m) s = fmaf(du[m], tf(sV[i * SV + cs + NCS * m]), s);
-      }
-#pragma unroll
-      for (int o = 1; o < NCS; o <<= 1) s += __shfl_xor(s, o, NCS);
-      if (cs == 0) sM3[r * SM + i] = s;
+    for (int r = 0; r < 4; ++r) {
+      const int row = r0 + 4 * grp + r, col = i0 + lo;
+      sM3[row * SM + col] = col <= row ? acc[r] : 0.f;
     }
   }
-
-  // ---- owned (row, channel) accumulators; dK and dG take dKG = T^T dW now:
-  // dKG[i][c] = beta_i sum_{r >= i} L[r][i] dW[r][c];  dK += dKG Gamma;  dG += dKG K Gamma
-  const int oc = tid % DK, org = tid / DK;
-  float aq[RPT], ak[RPT], ag[RPT];
-#pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int i = org + NRG * m;
-    float s = 0.f;
-    for (int r = i; r < C; ++r) s = fmaf(sL[r * SM + i], gr[GL::DW + r * DK + oc], s);
-    s *= sBeta[i];
-    const float gam = __expf(sG[i * SG + oc]);
-    aq[m] = 0.f;
-    ak[m] = s * gam;
-    ag[m] = s * tf(sK[i * SK + oc]) * gam;
+  for (int e = tid; e < C * C; e += NTH) {
+    const int r = e / C, i = e - r * C;
+    if ((i >> 4) > (r >> 4)) sM3[r * SM + i] = 0.f;
   }
-  // dV[i][j] = beta_i sum_{r >= i} L[r][i] dU[r][j]
-  {
-    const int jv = tid % DV, rgv = tid / DV;
+
+  // ---- owned tiles: dKG = T^T dW (T = L diag(beta)); dK += dKG Gamma, dG += dKG K Gamma
+  f32x4 aq[MAXT], ak[MAXT], ag[MAXT];
 #pragma unroll
-    for (int m = 0; m < Cf::RPTV; ++m) {
-      const int i = rgv + Cf::NRGV * m;
-      float s = 0.f;
-      for (int r = i; r < C; ++r) s = fmaf(sL[r * SM + i], gr[GL::DU + r * DV + jv], s);
-      if (i < nr) stg<F32>(p.dv, (row0 + (int64_t)i * H) * DV + jv, s * sBeta[i]);
+  for (int q = 0; q < MAXT; ++q) {
+    aq[q] = zero4();
+    ak[q] = zero4();
+    ag[q] = zero4();
+    const int t = wave + 8 * q;
+    if (t < NTILE) {
+      const int i0 = 16 * (t / NTK), c0 = 16 * (t % NTK);
+      const f32x4 d = tile_mm<F32, C, true>([&](int m, int k) { return sL[k * SM + i0 + m] * sBeta[i0 + m]; },
+                                      [&](int k, int n) { return gr[GL::DW + k * DK + c0 + n]; }, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 4 * grp + r, c = c0 + lo;
+        const float gam = __expf(sG[i * SG + c]);
+        ak[q][r] = d[r] * gam;
+        ag[q][r] = d[r] * tf(sK[i * SK + c]) * gam;
+      }
+    }
+  }
+  // dV = T^T dU, straight to the output
+  for (int t = wave; t < Cf::NTC * NTV; t += 8) {
+    const int i0 = 16 * (t / NTV), j0 = 16 * (t % NTV);
+    const f32x4 d = tile_mm<F32, C, true>([&](int m, int k) { return sL[k * SM + i0 + m] * sBeta[i0 + m]; },
+                                    [&](int k, int n) { return gr[GL::DU + k * DV + j0 + n]; }, zero4());
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + 4 * grp + r;
+      if (i < nr) stg<F32>(p.dv, (row0 + (int64_t)i * H) * DV + j0 + lo, d[r]);
     }
   }
   __syncthreads();
@@ -520,9 +595,8 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     sDb[i] = s;
   }
   __syncthreads();
-
   // ---- Y = L^T dL (into M4): Y[a][bb] = sum_{r >= max(a, bb)} L[r][a] dL[r][bb]
-  for (int e = tid; e < C * C; e += Cf::NTH) {
+  for (int e = tid; e < C * C; e += NTH) {
     const int a = e / C, bb = e - a * C;
     float s = 0.f;
     for (int r = max(a, bb); r < C; ++r) s = fmaf(sL[r * SM + a], sM3[r * SM + bb], s);
@@ -530,7 +604,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   }
   __syncthreads();
   // ---- dA = strictLower(-Y L^T) (into M3): dA[a][bb] = -sum_{s <= bb} Y[a][s] L[bb][s], a > bb
-  for (int e = tid; e < C * C; e += Cf::NTH) {
+  for (int e = tid; e < C * C; e += NTH) {
     const int a = e / C, bb = e - a * C;
     float s = 0.f;
     if (a > bb)
@@ -549,85 +623,146 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     }
     if (r < nr) stg<F32>(p.dbeta, row0 + (int64_t)r * H, sDb[r] + s);
   }
-  for (int e = tid; e < C * C; e += Cf::NTH) {
+  for (int e = tid; e < C * C; e += NTH) {
     const int r = e / C, i = e - r * C;
     sM4[r * SM + i] = gr[GL::DP + r * C + i];
   }
   __syncthreads();
 
-  // ---- through Ekk and Eqk: for every (r, i) with i <= r and channel c, e = e^{G_r[c] - G_i[c]} <= 1
-  //   row side:    dQ_r += dEqk[r][i] k_i e,  dK_r += dEkk[r][i] k_i e,  dG_r += (dEqk q_r + dEkk k_r) k_i e
-  //   column side: dK_i += (dEqk[r][i] q_r + dEkk[r][i] k_r) e,  dG_i -= the same times k_i
-  // (the diagonal i = r has e = 1 and no net dG)
+  // ---- through Ekk and Eqk, on the owned tiles (rows r0.., channels c0..):
+  //   row side (reference R = G before the row tile):
+  //     dQe = e^{G_r - R} sum_{i <= r} dEqk[r][i] (K e^{R - G})[i],   dKr = the same with dEkk
+  //     dQ += dQe, dK += dKr, dG += q dQe + k dKr
+  //   column side (reference R' = G at the tile's last row):
+  //     dKc = e^{R' - G_i} sum_{r >= i} (dEqk[r][i] q_r + dEkk[r][i] k_r) e^{G_r - R'}
+  //     dK += dKc, dG -= k dKc
+  // (dEqk is lower-inclusive, dEkk strictly lower: both zero elsewhere)
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int r = org + NRG * m;
-    const float Gr = sG[r * SG + oc], qr = tf(sQ[r * SK + oc]), kr = tf(sK[r * SK + oc]);
-    float dq = 0.f, dk = 0.f, dg = 0.f;
-    for (int i = 0; i < r; ++i) {
-      const float e = __expf(Gr - sG[i * SG + oc]);
-      const float ki = tf(sK[i * SK + oc]) * e;
-      const float wq = sM4[r * SM + i], wk = sM3[r * SM + i];
-      dq = fmaf(wq, ki, dq);
-      dk = fmaf(wk, ki, dk);
-      dg = fmaf(fmaf(wq, qr, wk * kr), ki, dg);
+  for (int q = 0; q < MAXT; ++q) {
+    const int t = wave + 8 * q;
+    if (t >= NTILE) continue;
+    const int r0 = 16 * (t / NTK), c = 16 * (t % NTK) + lo;
+    const float R = r0 > 0 ? sG[(r0 - 1) * SG + c] : 0.f, R2 = sG[(r0 + 15) * SG + c];
+    f32x4 d1 = zero4(), d2 = zero4(), d3 = zero4();
+    for (int s = 0; s < O::nks(r0 + 16); ++s) {
+      if constexpr (F32) {
+        const int k = O::kidx(s, grp, 0);
+        const Frag fb = tf(sK[k * SK + c]) * __expf(R - sG[k * SG + c]);
+        d1 = O::mma(sM4[(r0 + lo) * SM + k], fb, d1);
+        d2 = O::mma(sM3[(r0 + lo) * SM + k], fb, d2);
+      } else {
+        Frag fb, fbl, fa1, fa1l, fa2, fa2l;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int k = O::kidx(s, grp, j);
+          const bool ok = k < r0 + 16;
+          const int kc = ok ? k : 0;
+          split_bf16(ok ? tf(sK[kc * SK + c]) * __expf(R - sG[kc * SG + c]) : 0.f, fb, fbl, j);
+          split_bf16(ok ? sM4[(r0 + lo) * SM + kc] : 0.f, fa1, fa1l, j);
+          split_bf16(ok ? sM3[(r0 + lo) * SM + kc] : 0.f, fa2, fa2l, j);
+        }
+        d1 = O::mma(fa1, fb, d1);
+        d1 = O::mma(fa1, fbl, d1);
+        d1 = O::mma(fa1l, fb, d1);
+        d2 = O::mma(fa2, fb, d2);
+        d2 = O::mma(fa2, fbl, d2);
+        d2 = O::mma(fa2l, fb, d2);
+      }
     }
-    dq = fmaf(sM4[r * SM + r], kr, dq);
-    dk = fmaf(sM4[r * SM + r], qr, dk);
-    for (int s = r + 1; s < C; ++s) {
-      const float e = __expf(sG[s * SG + oc] - Gr);
-      const float u = fmaf(sM4[s * SM + r], tf(sQ[s * SK + oc]), sM3[s * SM + r] * tf(sK[s * SK + oc])) * e;
-      dk += u;
-      dg = fmaf(-u, kr, dg);
+    for (int s = 0; s < O::nks(C - r0); ++s) {
+      if constexpr (F32) {
+        const int r = r0 + O::kidx(s, grp, 0);
+        const float e = __expf(sG[r * SG + c] - R2);
+        d3 = O::mma(sM4[r * SM + r0 + lo], tf(sQ[r * SK + c]) * e, d3);
+        d3 = O::mma(sM3[r * SM + r0 + lo], tf(sK[r * SK + c]) * e, d3);
+      } else {
+        Frag fb1, fb1l, fb2, fb2l, fa1, fa1l, fa2, fa2l;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = r0 + O::kidx(s, grp, j);
+          const bool ok = r < C;
+          const int rc = ok ? r : 0;
+          const float e = ok ? __expf(sG[rc * SG + c] - R2) : 0.f;
+          split_bf16(tf(sQ[rc * SK + c]) * e, fb1, fb1l, j);
+          split_bf16(tf(sK[rc * SK + c]) * e, fb2, fb2l, j);
+          split_bf16(ok ? sM4[rc * SM + r0 + lo] : 0.f, fa1, fa1l, j);
+          split_bf16(ok ? sM3[rc * SM + r0 + lo] : 0.f, fa2, fa2l, j);
+        }
+        d3 = O::mma(fa1, fb1, d3);
+        d3 = O::mma(fa1, fb1l, d3);
+        d3 = O::mma(fa1l, fb1, d3);
+        d3 = O::mma(fa2, fb2, d3);
+        d3 = O::mma(fa2, fb2l, d3);
+        d3 = O::mma(fa2l, fb2, d3);
+      }
     }
-    aq[m] += dq;
-    ak[m] += dk;
-    ag[m] += dg;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = r0 + 4 * grp + r;
+      const float G = sG[i * SG + c], qv = tf(sQ[i * SK + c]), kv = tf(sK[i * SK + c]);
+      const float f = __expf(G - R), f2 = __expf(R2 - G);
+      const float dqe = d1[r] * f, dkr = d2[r] * f, dkc = d3[r] * f2;
+      aq[q][r] += dqe;
+      ak[q][r] += dkr + dkc;
+      ag[q][r] += qv * dqe + kv * (dkr - dkc);
+    }
   }
 
   // ---- elementwise: Q Gamma, Kd = K e^{gl - G}, and the chunk's total decay gl
-  float dglp = 0.f;
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int r = org + NRG * m;
-    const float G = sG[r * SG + oc], gl = sG[(C - 1) * SG + oc];
-    const float gam = __expf(G), dec = __expf(gl - G);
-    const float q = tf(sQ[r * SK + oc]), k = tf(sK[r * SK + oc]);
-    const float dqg = gr[GL::DQG + r * DK + oc], dkd = gr[GL::DKD + r * DK + oc];
-    aq[m] = fmaf(dqg, gam, aq[m]);
-    ag[m] = fmaf(dqg * q, gam, ag[m]);
-    ak[m] = fmaf(dkd, dec, ak[m]);
-    const float t = dkd * k * dec;
-    ag[m] -= t;
-    dglp += t;
+  for (int q = 0; q < MAXT; ++q) {
+    const int t = wave + 8 * q;
+    if (t >= NTILE) continue;
+    const int tm = t / NTK, r0 = 16 * tm, c = 16 * (t % NTK) + lo;
+    const float gl = sG[(C - 1) * SG + c];
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = r0 + 4 * grp + r;
+      const float G = sG[i * SG + c], gam = __expf(G), dec = __expf(gl - G);
+      const float qv = tf(sQ[i * SK + c]), kv = tf(sK[i * SK + c]);
+      const float dqg = gr[GL::DQG + i * DK + c], dkd = gr[GL::DKD + i * DK + c];
+      aq[q][r] = fmaf(dqg, gam, aq[q][r]);
+      ag[q][r] = fmaf(dqg * qv, gam, ag[q][r]);
+      ak[q][r] = fmaf(dkd, dec, ak[q][r]);
+      const float tt = dkd * kv * dec;
+      ag[q][r] -= tt;
+      part += tt;
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    if (grp == 0) sRed[tm * DK + c] = part;
   }
-  sRed[org * DK + oc] = dglp;
   __syncthreads();
   if (tid < DK) {
     float s = gr[GL::DGL + tid];
-    for (int o = 0; o < NRG; ++o) s += sRed[o * DK + tid];
+    for (int o = 0; o < Cf::NTC; ++o) s += sRed[o * DK + tid];
     sDgl[tid] = s;
   }
-  __syncthreads();
+  __syncthreads();  // sG (G) is read for the last time above
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int r = org + NRG * m;
-    if (r == C - 1) ag[m] += sDgl[oc];
-    if (r < nr) {
-      stg<F32>(p.dq, (row0 + (int64_t)r * H) * DK + oc, aq[m]);
-      stg<F32>(p.dk, (row0 + (int64_t)r * H) * DK + oc, ak[m]);
+  for (int q = 0; q < MAXT; ++q) {
+    const int t = wave + 8 * q;
+    if (t >= NTILE) continue;
+    const int r0 = 16 * (t / NTK), c = 16 * (t % NTK) + lo;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = r0 + 4 * grp + r;
+      float dg = ag[q][r];
+      if (i == C - 1) dg += sDgl[c];
+      sG[i * SG + c] = dg;
+      if (i < nr) {
+        stg<F32>(p.dq, (row0 + (int64_t)i * H) * DK + c, aq[q][r]);
+        stg<F32>(p.dk, (row0 + (int64_t)i * H) * DK + c, ak[q][r]);
+      }
     }
   }
-  // ---- dg = reverse cumulative sum of dG over the chunk's rows
-#pragma unroll
-  for (int m = 0; m < RPT; ++m) sG[(org + NRG * m) * SG + oc] = ag[m];
   __syncthreads();
-  if (tid < DK) {
-    float s = 0.f;
-    for (int r = C - 1; r >= 0; --r) {
-      s += sG[r * SG + tid];
-      if (r < nr) stg<F32>(p.dg, (row0 + (int64_t)r * H) * DK + tid, s);
-    }
+  // ---- dg = reverse cumulative sum of dG over the chunk's rows
+  scan_rows<DK, C, Cf::NPART, Cf::RPP, true>(sG, SG, sScan, tid);
+  for (int e = tid; e < C * DK; e += NTH) {
+    const int r = e / DK, c = e - r * DK;
+    if (r < nr) stg<F32>(p.dg, (row0 + (int64_t)r * H) * DK + c, sG[r * SG + c]);
   }
 }
 
@@ -675,7 +810,7 @@ static hipError_t launch_backward_kernels(const BwdParams& p, int64_t units, voi
                      (hipStream_t)stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.items == 0) return e;
-  hipLaunchKernelGGL((bwd_state_kernel<F32, DK, DV, C>), dim3((unsigned)p.items), dim3(256), 0, (hipStream_t)stream, p);
+  hipLaunchKernelGGL((bwd_state_kernel<F32, DK, DV, C>), dim3((unsigned)p.items), dim3(512), 0, (hipStream_t)stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_intra_kernel<F32, DK, DV, C>), dim3((unsigned)p.items), dim3(512), 0, (hipStream_t)stream, p);
   return hipGetLastError();
