@@ -69,6 +69,17 @@ def prefill_flops_per_token_head(dk, dv, C):
     return 6 * dk * dv + (C - 1) * dk + 2 * (C + 1) * dk + 2 * (C + 1) * dv + C * C / 3.0
 
 
+def backward_flops_per_token_head(dk, dv, C):
+    """Products the backward computes per (token, head), masked halves counted as half: the forward
+    recompute; the adjoint chain (P^T dO, Kd dS, (Q Gamma)^T dO, W^T dU); the state products (U, dU,
+    dP, d(Q Gamma), dKd, dW); the transform (Ekk, dT, T^T dW, T^T dU, L^T dL L^T, and the four
+    Ekk / Eqk products)."""
+    chain = C * dv + 6 * dk * dv
+    state = 2 * C * dv + 10 * dk * dv
+    transform = 7 * C * dk + 2 * C * dv + 2 * C * C // 3
+    return prefill_flops_per_token_head(dk, dv, C) + chain + state + transform
+
+
 def prefill_bytes(B, T, H, dk, dv, s_in, s_out, with_h0=True, with_hT=True):
     per_th = (3 * dk + dv) * s_in + s_in + dv * s_out
     return B * T * H * per_th + B * H * 4 * dk * dv * (int(with_h0) + int(with_hT))
@@ -146,6 +157,7 @@ def main():
     ap.add_argument("--no-workloads", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--no-states", action="store_true", help="skip the state-snapshot leg")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-steps leg")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward (training) leg")
     ap.add_argument("--workloads", default="", help="comma-separated subset of the other prefill workloads")
     ap.add_argument("--no-flush", action="store_true", help="do not evict the Infinity Cache between steps")
     ap.add_argument("--copy-calibration", action="store_true", help="run one 1 GiB copy (counter scaling) and exit")
@@ -304,6 +316,31 @@ def main():
         out["fused"] = {"gate": "-5 sigmoid(x) in the kernel", "normalize_qk": True, "out_gate": True,
                         "ms_per_call": fms, "tokens_per_s": tokens / (fms * 1e-3), "overhead_vs_plain": fms / ms - 1.0}
         del gr
+
+    # ---------------- backward of the same call (training): gradients of <do, o> + <dhT, hT>, the
+    # forward recomputed inside
+    if not args.no_backward:
+        do, dhT = datagen.backward_adjoints(w.seed, w.B, w.T, w.H, w.dk, w.dv, w.dtype, 0.5)
+        do, dhT = to_dev(do), to_dev(dhT)
+        bws = torch.empty(kda.backward_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.chunk, g["q"].dtype),
+                          dtype=torch.uint8, device=dev)
+        grads = kda.kda_chunked_backward(g["q"], g["k"], g["v"], g["g"], g["beta"], g["h0"], do, dhT, chunk=w.chunk,
+                                         workspace=bws)
+
+        def bstep(_i):
+            kda.kda_chunked_backward(g["q"], g["k"], g["v"], g["g"], g["beta"], g["h0"], do, dhT, chunk=w.chunk,
+                                     grads=grads, workspace=bws)
+
+        torch.cuda.synchronize()
+        bms, _ = time_launches(bstep, max(3, args.steps // 4), None if args.no_flush else flush)
+        bflops = backward_flops_per_token_head(w.dk, w.dv, w.chunk) * tokens * w.H
+        out["backward"] = {"ms_per_call": bms, "tokens_per_s": tokens / (bms * 1e-3), "ratio_to_forward": bms / ms,
+                           "flops_per_token_head": backward_flops_per_token_head(w.dk, w.dv, w.chunk),
+                           "tflops": bflops / (bms * 1e-3) / 1e12, "peak_tflops": MFMA_BF16_PEAK_TFS,
+                           "mfma_frac": bflops / (bms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+                           "workspace_bytes": bws.numel(),
+                           "note": "forward recompute + adjoint chain + state products + UT-transform backward"}
+        del bws, grads, do, dhT
 
     # ---------------- decode
     if not args.no_decode:

@@ -183,3 +183,42 @@ def test_decode_validation():
     assert call(dk=32) == UNSUPPORTED
     assert call(dt=3) == INVALID
     assert call(B=0, ptr=None) == OK
+
+
+def test_backward_workspace_and_validation():
+    lib = kda.lib()
+    rec = 2 * (3 * 64 * 128 + 64 * 64 + 64 * 128) + 4 * 128
+    rec = (rec + 255) // 256 * 256
+    al = lambda x: (x + 255) // 256 * 256
+    B, T, H, D, C = 4, 4096, 16, 128, 64
+    nch, units = T // C, B * H
+    grad = (C * D + C * C + 3 * C * D + D + 63) // 64 * 64  # dU, dP, d(Q Gamma), dKd, dW, dgl (fp32)
+    want = (al(B * nch * H * rec) + al(units * (nch - 1) * D * D * 4) + al(units * nch * D * D * 4)
+            + al(units * nch * grad * 4) + al(B * T * H * D * 2))
+    assert lib.kda_chunked_backward_workspace_bytes(B, T, H, D, D, C, 1) == want
+    assert lib.kda_chunked_backward_workspace_bytes(1, 100, 2, 128, 128, 48, 1) == 0  # unsupported chunk
+    assert lib.kda_chunked_backward_workspace_bytes(1, 100, 2, 128, 128, 64, 0) == 0  # fp32 only at d = 64
+    assert lib.kda_chunked_backward_workspace_bytes(1, 100, 2, 64, 64, 64, 0) > 0
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every call below fails validation
+    a = [fake] * 5 + [None, fake, None] + [fake] * 5 + [None]
+
+    def call(args, B=1, T=100, H=2, dk=128, dv=128, chunk=64, dt=1, ws=None, nbytes=0):
+        return lib.kda_chunked_backward(*args, B, T, H, dk, dv, chunk, dt, ws, nbytes, None)
+
+    assert call(a, chunk=48) == UNSUPPORTED
+    assert call(a, dk=96) == UNSUPPORTED
+    assert call(a, dt=0) == UNSUPPORTED                     # fp32 with d = 128
+    assert call(a, B=-1) == INVALID
+    assert call(a, dt=5) == INVALID
+    bad = list(a)
+    bad[8] = None                                           # dq missing
+    assert call(bad) == INVALID
+    bad = list(a)
+    bad[9] = ctypes.c_void_p((1 << 20) + 4)                 # dk misaligned
+    assert call(bad) == INVALID
+    bad = list(a)
+    bad[6] = None                                           # d_o missing
+    assert call(bad) == INVALID
+    assert call(a) == 3                                     # no workspace: KDA_ERR_WORKSPACE
+    assert call(a, B=0) == OK
+    assert call(a, T=0) == OK                               # nothing to do without dh0
