@@ -87,11 +87,12 @@ __device__ __forceinline__ void zero(float (&acc)[MI][NI]) {
 // acc[r] = D[4 grp + r][lo].
 // SPLIT (bf16 only): each operand value x is carried as bf16(x) + bf16(x - bf16(x)) and three
 // products are accumulated (hi hi + hi lo + lo hi), for about 16 significant bits where a sum cancels.
-template <bool F32, int K, bool SPLIT = false, typename FA, typename FB>
+// UNR: unroll factor of the contraction loop (fewer registers live at once when small).
+template <bool F32, int K, bool SPLIT = false, int UNR = 64, typename FA, typename FB>
 __device__ __forceinline__ f32x4 tile_mm(FA&& a, FB&& b, f32x4 acc) {
   using O = Op<F32>;
   const int lane = threadIdx.x & 63, lo = lane & 15, grp = lane >> 4;
-#pragma unroll
+#pragma unroll UNR
   for (int s = 0; s < O::nks(K); ++s) {
     typename O::Frag fa, fb, fal, fbl;
     if constexpr (F32) {
@@ -128,7 +129,7 @@ __device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int 
 }
 
 // ------------------------------------------------------------------------------------------------
-// 2. adjoint chain.  One 256-thread workgroup per (sequence, head, 32 value columns), products on
+// 2. adjoint chain.  One 512-thread workgroup per (sequence, head, 32 value columns), products on
 // MFMA.  The record's first four fields (-W, Q Gamma, Kd^T, P) are copied to LDS as stored; dO's
 // slice and dU are held in the operand type, the adjoint state dS in fp32 (rounded to the operand
 // type only where it is an operand).
@@ -138,84 +139,153 @@ struct BChainCfg {
   using E = typename Op<F32>::E;
   static constexpr int ES = sizeof(E);
   static constexpr int WS = 32, NSL = DV / WS, CP = R::CP, SE = WS + 16 / ES, SS = WS + 4;
-  static constexpr int OFF_REC = 0;                          // E [R::UT]  (-W, Q Gamma, Kd^T, P)
-  static constexpr int OFF_GAM = (int)(R::UT * ES);          // f32 [DK]
-  static constexpr int OFF_DO = OFF_GAM + DK * 4;            // E [C][SE]
-  static constexpr int OFF_DU = OFF_DO + ((C * SE * ES + 15) & ~15);  // E [C][SE]
-  static constexpr int OFF_DS = OFF_DU + ((C * SE * ES + 15) & ~15);  // f32 [DK][SS]
+  // per buffer: the record prefix (E [R::UT]: -W, Q Gamma, Kd^T, P), e^{gl} (f32 [DK]), dO (E [C][SE])
+  static constexpr int REC_BYTES = (int)(R::UT * ES);
+  static constexpr int OFF_GAM = REC_BYTES;
+  static constexpr int OFF_DO = OFF_GAM + DK * 4;
+  static constexpr int BUF = OFF_DO + ((C * SE * ES + 15) & ~15);
+  static constexpr int REST = ((C * SE * ES + 15) & ~15) + DK * SS * 4;  // dU (E [C][SE]), dS (f32 [DK][SS])
+  // two buffers (the next chunk's record arrives while this one computes) when they fit
+  static constexpr bool DBUF = 2 * BUF + REST <= 160 * 1024;
+  static constexpr int NBUF = DBUF ? 2 : 1;
+  static constexpr int OFF_DU = NBUF * BUF;
+  static constexpr int OFF_DS = OFF_DU + ((C * SE * ES + 15) & ~15);
   static constexpr int TOTAL = OFF_DS + DK * SS * 4;
-  static_assert(OFF_GAM % 16 == 0, "record prefix is a whole number of 16-byte vectors");
+  static constexpr int NTH = 512;
+  static constexpr int N16 = REC_BYTES / 16, NPF = (N16 + NTH - 1) / NTH, NDO = (C * WS + NTH - 1) / NTH;
+  static_assert(REC_BYTES % 16 == 0 && BUF % 16 == 0, "record prefix is a whole number of 16-byte vectors");
+  static_assert(DK <= NTH, "one e^{gl} entry per thread");
   static_assert(TOTAL <= 160 * 1024, "LDS");
 };
 
+// Registers holding one chunk's record prefix, e^{gl} and dO slice between its load and its store
+// into an LDS buffer.
 template <bool F32, int DK, int DV, int C>
-__global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
+struct ChainStage {
+  using Cf = BChainCfg<F32, DK, DV, C>;
+  using R = typename Cf::R;
+  using E = typename Cf::E;
+  // the slots in one vector each, so that they stay in registers
+  typedef uint32_t pf_t __attribute__((ext_vector_type(4 * Cf::NPF)));
+  typedef float do_t __attribute__((ext_vector_type(Cf::NDO)));
+  pf_t pf;
+  float pg;
+  do_t pdo;
+  __device__ __forceinline__ void fetch(const BwdParams& p, int b, int h, int ch, int col0, int tid) {
+    const unsigned char* rec = p.records + ((int64_t)(b * p.nch + ch) * p.H + h) * R::BYTES;
+#pragma unroll
+    for (int i = 0; i < Cf::NPF; ++i) {
+      const int e = tid + Cf::NTH * i;
+      const uint4 x = reinterpret_cast<const uint4*>(rec)[e < Cf::N16 ? e : 0];
+      pf[4 * i] = x.x;
+      pf[4 * i + 1] = x.y;
+      pf[4 * i + 2] = x.z;
+      pf[4 * i + 3] = x.w;
+    }
+    pg = reinterpret_cast<const float*>(rec + R::GAM_BYTE)[tid < DK ? tid : 0];
+    const int nr = min(C, p.T - ch * C);
+    const int64_t orow = ((int64_t)b * p.T + (int64_t)ch * C) * p.H + h;
+#pragma unroll
+    for (int i = 0; i < Cf::NDO; ++i) {
+      const int e = tid + Cf::NTH * i, r = e / Cf::WS, j = e - r * Cf::WS;
+      pdo[i] = (e < C * Cf::WS && r < nr) ? ldg<F32>(p.dO, (orow + (int64_t)r * p.H) * DV + col0 + j) : 0.f;
+    }
+  }
+  __device__ __forceinline__ void put(unsigned char* base, int tid) const {
+#pragma unroll
+    for (int i = 0; i < Cf::NPF; ++i) {
+      const int e = tid + Cf::NTH * i;
+      if (e < Cf::N16) reinterpret_cast<uint4*>(base)[e] = make_uint4(pf[4 * i], pf[4 * i + 1], pf[4 * i + 2], pf[4 * i + 3]);
+    }
+    if (tid < DK) reinterpret_cast<float*>(base + Cf::OFF_GAM)[tid] = pg;
+    E* d = reinterpret_cast<E*>(base + Cf::OFF_DO);
+#pragma unroll
+    for (int i = 0; i < Cf::NDO; ++i) {
+      const int e = tid + Cf::NTH * i, r = e / Cf::WS, j = e - r * Cf::WS;
+      if (e < C * Cf::WS) d[r * Cf::SE + j] = (E)pdo[i];
+    }
+  }
+};
+
+template <bool F32, int DK, int DV, int C>
+__global__ __launch_bounds__(512) void bwd_chain_kernel(BwdParams p) {
   using Cf = BChainCfg<F32, DK, DV, C>;
   using R = typename Cf::R;
   using E = typename Cf::E;
   constexpr int WS = Cf::WS, CP = Cf::CP, SE = Cf::SE, SS = Cf::SS;
   __shared__ __align__(16) unsigned char smem[Cf::TOTAL];
-  const E* sR = reinterpret_cast<const E*>(smem + Cf::OFF_REC);
-  float* sGam = reinterpret_cast<float*>(smem + Cf::OFF_GAM);
-  E* sdO = reinterpret_cast<E*>(smem + Cf::OFF_DO);
   E* sdU = reinterpret_cast<E*>(smem + Cf::OFF_DU);
   float* sdS = reinterpret_cast<float*>(smem + Cf::OFF_DS);
 
   const int tid = threadIdx.x, wave = tid >> 6, lo = tid & 15, grp = (tid >> 4) & 3;
   const int unit = blockIdx.x / Cf::NSL, col0 = (blockIdx.x % Cf::NSL) * WS;
   const int H = p.H, b = unit / H, h = unit - b * H;
-  for (int e = tid; e < DK * WS; e += 256) {
+
+  // one chunk's record prefix, e^{gl} and dO slice: into registers, then into an LDS buffer
+  ChainStage<F32, DK, DV, C> stage;
+  auto buf_of = [&](int ch) { return Cf::DBUF ? (ch & 1) : 0; };
+
+  for (int e = tid; e < DK * WS; e += Cf::NTH) {
     const int c = e / WS, j = e - c * WS;
     sdS[c * SS + j] = p.dhT ? p.dhT[((int64_t)unit * DK + c) * DV + col0 + j] : 0.f;
   }
+  if (p.nch > 0) {
+    stage.fetch(p, b, h, p.nch - 1, col0, tid);
+    stage.put(smem + buf_of(p.nch - 1) * Cf::BUF, tid);
+  }
   for (int ch = p.nch - 1; ch >= 0; --ch) {
-    const int nr = min(C, p.T - ch * C);
-    __syncthreads();  // dS of the previous step complete; the record buffers are free
+    __syncthreads();  // this chunk's buffer is filled; dS of the previous step is complete
     float* ds_out = p.dstates + ((int64_t)unit * p.nch + ch) * DK * DV + col0;
-    for (int e = tid; e < DK * WS; e += 256) {
+    for (int e = tid; e < DK * WS; e += Cf::NTH) {
       const int c = e / WS, j = e - c * WS;
       ds_out[(int64_t)c * DV + j] = sdS[c * SS + j];
     }
-    const unsigned char* rec = p.records + ((int64_t)(b * p.nch + ch) * H + h) * R::BYTES;
-    for (int e = tid; e < Cf::OFF_GAM / 16; e += 256)
-      reinterpret_cast<uint4*>(smem)[e] = reinterpret_cast<const uint4*>(rec)[e];
-    for (int e = tid; e < DK; e += 256) sGam[e] = reinterpret_cast<const float*>(rec + R::GAM_BYTE)[e];
-    const int64_t orow = ((int64_t)b * p.T + (int64_t)ch * C) * H + h;
-    for (int e = tid; e < C * WS; e += 256) {
-      const int r = e / WS, j = e - r * WS;
-      sdO[r * SE + j] = (E)(r < nr ? ldg<F32>(p.dO, (orow + (int64_t)r * H) * DV + col0 + j) : 0.f);
+    if constexpr (Cf::DBUF) {
+      if (ch > 0) stage.fetch(p, b, h, ch - 1, col0, tid);  // in flight while this chunk computes
     }
-    __syncthreads();
+    const unsigned char* base = smem + buf_of(ch) * Cf::BUF;
+    const E* sR = reinterpret_cast<const E*>(base);
+    const float* sGam = reinterpret_cast<const float*>(base + Cf::OFF_GAM);
+    const E* sdO = reinterpret_cast<const E*>(base + Cf::OFF_DO);
     // dU[i][j] = sum_{r >= i} P[r][i] dO[r][j] + sum_c Kd^T[c][i] dS[c][j]
     // (P is read only where r >= i: its tiles above the diagonal are not all written)
-    for (int t = wave; t < (C / 16) * (WS / 16); t += 4) {
+    for (int t = wave; t < (C / 16) * (WS / 16); t += Cf::NTH / 64) {
       const int i0 = 16 * (t / (WS / 16)), j0 = 16 * (t % (WS / 16));
       f32x4 acc = zero4();
-      acc = tile_mm<F32, C>([&](int m, int k) { return k >= i0 + m ? tf(sR[R::P + k * CP + i0 + m]) : 0.f; },
+      acc = tile_mm<F32, C, false, 1>([&](int m, int k) { return k >= i0 + m ? tf(sR[R::P + k * CP + i0 + m]) : 0.f; },
                             [&](int k, int n) { return tf(sdO[k * SE + j0 + n]); }, acc);
-      acc = tile_mm<F32, DK>([&](int m, int k) { return tf(sR[R::KPT + k * CP + i0 + m]); },
+      acc = tile_mm<F32, DK, false, 1>([&](int m, int k) { return tf(sR[R::KPT + k * CP + i0 + m]); },
                              [&](int k, int n) { return sdS[k * SS + j0 + n]; }, acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) sdU[(i0 + 4 * grp + r) * SE + j0 + lo] = (E)acc[r];
     }
     __syncthreads();
     // dS[c][j] <- e^{gl_c} dS[c][j] + sum_r QG[r][c] dO[r][j] + sum_i (-W)[i][c] dU[i][j]
-    for (int t = wave; t < (DK / 16) * (WS / 16); t += 4) {
+    for (int t = wave; t < (DK / 16) * (WS / 16); t += Cf::NTH / 64) {
       const int c0 = 16 * (t / (WS / 16)), j0 = 16 * (t % (WS / 16));
       f32x4 acc;
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = sGam[c0 + 4 * grp + r] * sdS[(c0 + 4 * grp + r) * SS + j0 + lo];
-      acc = tile_mm<F32, C>([&](int m, int k) { return tf(sR[R::QG + k * DK + c0 + m]); },
+      acc = tile_mm<F32, C, false, 1>([&](int m, int k) { return tf(sR[R::QG + k * DK + c0 + m]); },
                             [&](int k, int n) { return tf(sdO[k * SE + j0 + n]); }, acc);
-      acc = tile_mm<F32, C>([&](int m, int k) { return tf(sR[R::NW + k * DK + c0 + m]); },
+      acc = tile_mm<F32, C, false, 1>([&](int m, int k) { return tf(sR[R::NW + k * DK + c0 + m]); },
                             [&](int k, int n) { return tf(sdU[k * SE + j0 + n]); }, acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) sdS[(c0 + 4 * grp + r) * SS + j0 + lo] = acc[r];
     }
+    if (ch > 0) {
+      if constexpr (Cf::DBUF) {
+        stage.put(smem + buf_of(ch - 1) * Cf::BUF, tid);  // the other buffer: last read by the previous step
+      } else {
+        __syncthreads();  // every read of the one buffer is done
+        stage.fetch(p, b, h, ch - 1, col0, tid);
+        stage.put(smem, tid);
+      }
+    }
   }
   __syncthreads();
   if (p.dh0)
-    for (int e = tid; e < DK * WS; e += 256) {
+    for (int e = tid; e < DK * WS; e += Cf::NTH) {
       const int c = e / WS, j = e - c * WS;
       p.dh0[((int64_t)unit * DK + c) * DV + col0 + j] = sdS[c * SS + j];
     }
@@ -806,7 +876,7 @@ template <bool F32, int DK, int DV, int C>
 static hipError_t launch_backward_kernels(const BwdParams& p, int64_t units, void* stream) {
   static_assert(GradLayout<DK, DV, C>::FLOATS == (((int64_t)C * DV + C * C + 3 * C * DK + DK + 63) & ~(int64_t)63),
                 "grad layout");
-  hipLaunchKernelGGL((bwd_chain_kernel<F32, DK, DV, C>), dim3((unsigned)(units * (DV / 32))), dim3(256), 0,
+  hipLaunchKernelGGL((bwd_chain_kernel<F32, DK, DV, C>), dim3((unsigned)(units * (DV / 32))), dim3(512), 0,
                      (hipStream_t)stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.items == 0) return e;
