@@ -122,6 +122,20 @@ __device__ __forceinline__ f32x4 tile_mm(FA&& a, FB&& b, f32x4 acc) {
   return acc;
 }
 
+// One 16x16 tile of D += A B^T-stored operands read straight from LDS rows that run along the
+// contraction index: arow = &A[m0 + lo][0], brow = &Bt[n0 + lo][0] (operand type, 8-byte aligned
+// rows for bf16), K a multiple of the MFMA depth.
+template <bool F32, int K>
+__device__ __forceinline__ f32x4 tile_rows(const typename Op<F32>::E* arow, const typename Op<F32>::E* brow,
+                                           f32x4 acc) {
+  using O = Op<F32>;
+  static_assert(K % O::KS == 0 || F32, "whole MFMA steps");
+  const int grp = (threadIdx.x >> 4) & 3;
+#pragma unroll
+  for (int s = 0; s < O::nks(K); ++s) acc = O::mma(O::ld(arow, s, grp), O::ld(brow, s, grp), acc);
+  return acc;
+}
+
 // slot j of a bf16 fragment pair: hi = bf16(x), lo = bf16(x - hi)
 __device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int j) {
   hi[j] = (__bf16)x;
@@ -371,7 +385,7 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] = tf(rec[R::UT + (j0 + lo) * C + i0 + 4 * grp + r]);
     acc = tile_mm<F32, DK>([&](int m, int k) { return tf(sNW[(i0 + m) * SK + k]); },
-                           [&](int k, int n) { return tf(sS0[k * SV + j0 + n]); }, acc);
+                           [&](int k, int n) { return tf(sS0[k * SV + j0 + n]); }, acc);  // S0 runs along n
 #pragma unroll
     for (int r = 0; r < 4; ++r) sU[(i0 + 4 * grp + r) * SV + j0 + lo] = (E)acc[r];
   }
@@ -410,9 +424,7 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
   for (int t = wave; t < (C / 16) * (C / 16); t += NTH / 64) {
     const int i0 = 16 * (t / (C / 16)), n0 = 16 * (t % (C / 16));
     f32x4 acc = zero4();
-    if (n0 <= i0)
-      acc = tile_mm<F32, DV>([&](int m, int k) { return tf(sdO[(i0 + m) * SV + k]); },
-                             [&](int k, int n) { return tf(sU[(n0 + n) * SV + k]); }, acc);
+    if (n0 <= i0) acc = tile_rows<F32, DV>(sdO + (i0 + lo) * SV, sU + (n0 + lo) * SV, acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = i0 + 4 * grp + r, col = n0 + lo;
@@ -425,8 +437,7 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
     const int i0 = 16 * (tt / (DK / 16)), c0 = 16 * (tt % (DK / 16));
     const E* A = which == 0 ? sdO : which == 1 ? sU : sdU;
     const E* Bt = which == 1 ? sdS : sS0;
-    f32x4 acc = tile_mm<F32, DV>([&](int m, int k) { return tf(A[(i0 + m) * SV + k]); },
-                                 [&](int k, int n) { return tf(Bt[(c0 + n) * SV + k]); }, zero4());
+    f32x4 acc = tile_rows<F32, DV>(A + (i0 + lo) * SV, Bt + (c0 + lo) * SV, zero4());
     const int64_t off = which == 0 ? GL::DQG : which == 1 ? GL::DKD : GL::DW;
     const float sg = which == 2 ? -1.f : 1.f;
 #pragma unroll
@@ -560,7 +571,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     tri_pair(t, tb, ta);
     const int r0 = 16 * tb, i0 = 16 * ta;
     const float* Rb = tb > 0 ? sG + (r0 - 1) * SG : nullptr;
-    f32x4 acc = tile_mm<F32, DK, true>(
+    f32x4 acc = tile_mm<F32, DK>(
         [&](int m, int k) { return tf(sK[(r0 + m) * SK + k]) * __expf(sG[(r0 + m) * SG + k] - (Rb ? Rb[k] : 0.f)); },
         [&](int k, int n) { return tf(sK[(i0 + n) * SK + k]) * __expf((Rb ? Rb[k] : 0.f) - sG[(i0 + n) * SG + k]); },
         zero4());
@@ -630,7 +641,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     if (t < NTILE) {
       const int i0 = 16 * (t / NTK), c0 = 16 * (t % NTK);
       const f32x4 d = tile_mm<F32, C, true>([&](int m, int k) { return sL[k * SM + i0 + m] * sBeta[i0 + m]; },
-                                      [&](int k, int n) { return gr[GL::DW + k * DK + c0 + n]; }, zero4());
+                                            [&](int k, int n) { return gr[GL::DW + k * DK + c0 + n]; }, zero4());
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + 4 * grp + r, c = c0 + lo;
@@ -644,7 +655,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   for (int t = wave; t < Cf::NTC * NTV; t += 8) {
     const int i0 = 16 * (t / NTV), j0 = 16 * (t % NTV);
     const f32x4 d = tile_mm<F32, C, true>([&](int m, int k) { return sL[k * SM + i0 + m] * sBeta[i0 + m]; },
-                                    [&](int k, int n) { return gr[GL::DU + k * DV + j0 + n]; }, zero4());
+                                          [&](int k, int n) { return gr[GL::DU + k * DV + j0 + n]; }, zero4());
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = i0 + 4 * grp + r;
