@@ -38,6 +38,7 @@ struct BwdParams {
   void *dq, *dk, *dv, *dg, *dbeta;
   float* dh0;
   int T, H, nch;
+  int units;  // B H
   int64_t items;
 };
 
@@ -232,7 +233,12 @@ __global__ __launch_bounds__(512) void bwd_chain_kernel(BwdParams p) {
   float* sdS = reinterpret_cast<float*>(smem + Cf::OFF_DS);
 
   const int tid = threadIdx.x, wave = tid >> 6, lo = tid & 15, grp = (tid >> 4) & 3;
-  const int unit = blockIdx.x / Cf::NSL, col0 = (blockIdx.x % Cf::NSL) * WS;
+  // Workgroups go to the 8 XCDs round-robin (workgroup i to XCD i mod 8): the value slices of one
+  // (sequence, head) are given workgroups 8 apart, so they share one XCD's L2 and each record
+  // comes from HBM once.  The grid is padded to a multiple of 8 NSL; padding workgroups exit.
+  const int xcd = blockIdx.x & 7, q8 = blockIdx.x >> 3;
+  const int unit = (q8 / Cf::NSL) * 8 + xcd, col0 = (q8 % Cf::NSL) * WS;
+  if (unit >= p.units) return;
   const int H = p.H, b = unit / H, h = unit - b * H;
 
   // one chunk's record prefix, e^{gl} and dO slice: into registers, then into an LDS buffer
@@ -664,45 +670,57 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  // ---- column part of dbeta (T = L diag(beta)) and dL = dT diag(beta), column i per thread
-  if (tid < C) {
-    const int i = tid;
+  // ---- column part of dbeta (T = L diag(beta)) and dL = dT diag(beta): NPC lanes per column
+  constexpr int NPC = NTH / C;
+  {
+    const int i = tid / NPC, u = tid - i * NPC;
     float s = 0.f;
-    for (int r = i; r < C; ++r) {
+    for (int r = u; r < C; r += NPC) {
       const float t = sM3[r * SM + i];
       s = fmaf(t, sL[r * SM + i], s);
       sM3[r * SM + i] = t * sBeta[i];
     }
-    sDb[i] = s;
+#pragma unroll
+    for (int o = 1; o < NPC; o <<= 1) s += __shfl_xor(s, o, NPC);
+    if (u == 0) sDb[i] = s;
   }
   __syncthreads();
-  // ---- Y = L^T dL (into M4): Y[a][bb] = sum_{r >= max(a, bb)} L[r][a] dL[r][bb]
-  for (int e = tid; e < C * C; e += NTH) {
-    const int a = e / C, bb = e - a * C;
-    float s = 0.f;
-    for (int r = max(a, bb); r < C; ++r) s = fmaf(sL[r * SM + a], sM3[r * SM + bb], s);
-    sM4[a * SM + bb] = s;
+  // ---- Y = L^T dL (into M4), MFMA tiles: Y[a][bb] = sum_r L[r][a] dL[r][bb]
+  for (int t = wave; t < Cf::NTC * Cf::NTC; t += 8) {
+    const int a0 = 16 * (t / Cf::NTC), b0 = 16 * (t % Cf::NTC);
+    const f32x4 y = tile_mm<F32, C, true>([&](int m, int k) { return sL[k * SM + a0 + m]; },
+                                          [&](int k, int n) { return sM3[k * SM + b0 + n]; }, zero4());
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sM4[(a0 + 4 * grp + r) * SM + b0 + lo] = y[r];
   }
   __syncthreads();
-  // ---- dA = strictLower(-Y L^T) (into M3): dA[a][bb] = -sum_{s <= bb} Y[a][s] L[bb][s], a > bb
-  for (int e = tid; e < C * C; e += NTH) {
-    const int a = e / C, bb = e - a * C;
-    float s = 0.f;
-    if (a > bb)
-      for (int t = 0; t <= bb; ++t) s = fmaf(sM4[a * SM + t], sL[bb * SM + t], s);
-    sM3[a * SM + bb] = -s;
+  // ---- dA = strictLower(-Y L^T) (into M3): dA[a][bb] = -sum_s Y[a][s] L[bb][s], a > bb
+  for (int t = wave; t < Cf::NTC * Cf::NTC; t += 8) {
+    const int a0 = 16 * (t / Cf::NTC), b0 = 16 * (t % Cf::NTC);
+    f32x4 d = zero4();
+    if (b0 <= a0)
+      d = tile_mm<F32, C, true>([&](int m, int k) { return sM4[(a0 + m) * SM + k]; },
+                                [&](int k, int n) { return sL[(b0 + n) * SM + k]; }, d);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int a = a0 + 4 * grp + r, bb = b0 + lo;
+      sM3[a * SM + bb] = a > bb ? -d[r] : 0.f;
+    }
   }
   __syncthreads();
-  // ---- row part of dbeta (A = diag(beta) Ekk), dEkk = diag(beta) dA in place; dEqk = dP into M4
-  if (tid < C) {
-    const int r = tid;
+  // ---- row part of dbeta (A = diag(beta) Ekk), dEkk = diag(beta) dA in place: NPC lanes per row;
+  // dEqk = dP into M4
+  {
+    const int r = tid / NPC, u = tid - r * NPC;
     float s = 0.f;
-    for (int i = 0; i < r; ++i) {
+    for (int i = u; i < r; i += NPC) {
       const float da = sM3[r * SM + i];
       s = fmaf(da, sEkk[r * SM + i], s);
       sM3[r * SM + i] = sBeta[r] * da;
     }
-    if (r < nr) stg<F32>(p.dbeta, row0 + (int64_t)r * H, sDb[r] + s);
+#pragma unroll
+    for (int o = 1; o < NPC; o <<= 1) s += __shfl_xor(s, o, NPC);
+    if (u == 0 && r < nr) stg<F32>(p.dbeta, row0 + (int64_t)r * H, sDb[r] + s);
   }
   for (int e = tid; e < C * C; e += NTH) {
     const int r = e / C, i = e - r * C;
@@ -887,7 +905,7 @@ template <bool F32, int DK, int DV, int C>
 static hipError_t launch_backward_kernels(const BwdParams& p, int64_t units, void* stream) {
   static_assert(GradLayout<DK, DV, C>::FLOATS == (((int64_t)C * DV + C * C + 3 * C * DK + DK + 63) & ~(int64_t)63),
                 "grad layout");
-  hipLaunchKernelGGL((bwd_chain_kernel<F32, DK, DV, C>), dim3((unsigned)(units * (DV / 32))), dim3(512), 0,
+  hipLaunchKernelGGL((bwd_chain_kernel<F32, DK, DV, C>), dim3((unsigned)(((units + 7) / 8) * 8 * (DV / 32))), dim3(512), 0,
                      (hipStream_t)stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.items == 0) return e;
@@ -901,7 +919,7 @@ hipError_t launch_chunked_backward(const BackwardArgs& a) {
   if (!chunked_backward_supported(a.f32, a.dk, a.dv, a.chunk)) return hipErrorInvalidValue;
   const int C = a.chunk, nch = (a.T + C - 1) / C;
   const int64_t units = (int64_t)a.B * a.H, items = units * nch;
-  if (units <= 0 || units * (a.dv / 32) > INT32_MAX || items > INT32_MAX) return hipErrorInvalidValue;
+  if (units <= 0 || (units + 7) * (a.dv / 32) > INT32_MAX || items > INT32_MAX) return hipErrorInvalidValue;
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
   const size_t fwd = al256(chunked_forward_workspace(a.f32, a.dk, a.dv, C, (int64_t)a.B * nch, a.H, a.B, false));
   float* states = reinterpret_cast<float*>(ws + fwd);
@@ -931,7 +949,7 @@ hipError_t launch_chunked_backward(const BackwardArgs& a) {
   p.h0 = a.h0; p.dhT = a.dhT;
   p.records = ws; p.states = states; p.dstates = dstates; p.grads = grads;
   p.dq = a.dq; p.dk = a.dk_out; p.dv = a.dv_out; p.dg = a.dg; p.dbeta = a.dbeta; p.dh0 = a.dh0;
-  p.T = a.T; p.H = a.H; p.nch = nch; p.items = items;
+  p.T = a.T; p.H = a.H; p.nch = nch; p.units = (int)units; p.items = items;
 #define KDA_BWD_LAUNCH(F, D, V, CC) \
   if (a.f32 == F && a.dk == D && a.dv == V && C == CC) return launch_backward_kernels<F, D, V, CC>(p, units, a.stream);
   KDA_BWD_INSTANCES(KDA_BWD_LAUNCH)
