@@ -22,9 +22,12 @@
 // and running products inside each 16-row sub-tile.
 //
 // Workgroup: 8 waves, one (chunk, head) record; two workgroups share a CU (LDS <= 80 KB), so one
-// workgroup's input loads overlap the other's arithmetic.  Thread (row pair rp, channel pair cpl,
-// sub-tile psb) owns 2 rows x 2 channels in each 32-channel quarter of the key dimension; the 8 row
-// pairs of a sub-tile are 8 consecutive lanes, so running products over it are an 8-lane scan.
+// workgroup's input loads overlap the other's arithmetic.  Thread (row pair rp, channel group cpl,
+// sub-tile psb) owns 2 rows x 2 NQ consecutive key channels, loaded with one 8- or 16-byte access
+// per row; the 8 row pairs of a sub-tile are 8 consecutive lanes, so running products over it are
+// an 8-lane scan.  The contraction over the key dimension runs in NQ "quarters" of 32 channels
+// each, interleaved by channel pair: quarter qt holds pair qt of every thread's group (channels
+// 2 NQ cpl + 2 qt, + 1).  Which channels a quarter holds does not change the sum over all of them.
 // Per quarter, pipelined so that the later quarters' loads arrive while the earlier ones compute:
 //   scan       e^g and the running products (E, the sub-tile totals Tb to LDS)
 //   outputs    Q.Gamma and K'^T straight to the record, (K.Gamma)^T to LDS
@@ -153,6 +156,33 @@ __device__ __forceinline__ void st4(void* dst, float a, float b, float c, float 
   else *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 
+// The 2 NQ consecutive channels of one row at element offset i of a wave-uniform base (one 8- or
+// 16-byte load per 16 bytes), split into channel pairs: pair qt goes to x[qt][j].  The load is
+// unconditional (i must be in bounds, 2 NQ i element-aligned to the access); !ok only zeroes.
+template <bool F32, int NQ>
+__device__ __forceinline__ void load_group(const void* base, uint32_t i, bool ok, Raw2<F32> (&x)[NQ][2], int j) {
+  static_assert(NQ == 2 || NQ == 4, "64 or 128 key channels");
+  const char* b = static_cast<const char*>(base);
+  if constexpr (F32) {
+#pragma unroll
+    for (int h = 0; h < NQ / 2; ++h) {
+      const float4 w = *reinterpret_cast<const float4*>(b + 4u * i + 16u * h);
+      x[2 * h][j].v = ok ? make_float2(w.x, w.y) : make_float2(0.f, 0.f);
+      x[2 * h + 1][j].v = ok ? make_float2(w.z, w.w) : make_float2(0.f, 0.f);
+    }
+  } else if constexpr (NQ == 4) {
+    const uint4 w = *reinterpret_cast<const uint4*>(b + 2u * i);
+    x[0][j].w = ok ? w.x : 0u;
+    x[1][j].w = ok ? w.y : 0u;
+    x[2][j].w = ok ? w.z : 0u;
+    x[3][j].w = ok ? w.w : 0u;
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(b + 2u * i);
+    x[0][j].w = ok ? w.x : 0u;
+    x[1][j].w = ok ? w.y : 0u;
+  }
+}
+
 // (sequence start token, length) of one chunk, and the first chunk of every sequence;
 // packed offsets are clamped to [0, T_total] exactly as the chunk map does.
 struct ChunkPos {
@@ -226,14 +256,14 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   const int tid = threadIdx.x, lane = tid & 63, lo = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave work is a scalar branch
   const int H = p.H;
-  // prep unit of this thread: 2 consecutive rows (a row pair of one 16-row sub-tile) x 2 channels
-  // in every quarter of the key dimension.  The 8 row pairs of a sub-tile are 8 consecutive lanes,
-  // so prefix products over the sub-tile are an 8-lane scan; every quarter's operands are then
-  // built by all threads.
+  // prep unit of this thread: 2 consecutive rows (a row pair of one 16-row sub-tile) x 2 NQ
+  // consecutive channels, one channel pair in every quarter of the key dimension.  The 8 row pairs
+  // of a sub-tile are 8 consecutive lanes, so prefix products over the sub-tile are an 8-lane
+  // scan; every quarter's operands are then built by all threads.
   const int rp = tid & 7, cpl = (tid >> 3) & 15;
   const int psb = __builtin_amdgcn_readfirstlane(tid >> 7);  // sub-tile: uniform over a wave
   const bool pact = psb < NT;
-  const int r0 = 16 * psb + 2 * rp;  // rows r0, r0 + 1; channels QW qt + 2 cpl (+1) of quarter qt
+  const int r0 = 16 * psb + 2 * rp;  // rows r0, r0 + 1; channels chan(qt) (+1) in quarter qt
   // value unit of this thread
   const int vcp = tid % NVP, vtg = tid / NVP;
   const bool vact = tid < NVU;
@@ -265,15 +295,13 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
     rok[0] = pact && r0 <= last;
     rok[1] = pact && r0 + 1 <= last;
 #pragma unroll
-    for (int qt = 0; qt < NQ; ++qt)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bool ok = pact && (r0 + j) <= last;
-        const uint32_t off = (pact ? (uint32_t)(QW * qt + 2 * cpl) : 0u) + (uint32_t)min(r0 + j, last) * kstride;
-        rg[qt][j].load32(gb, off, ok);
-        rq[qt][j].load32(qb, off, ok);
-        rk[qt][j].load32(kb, off, ok);
-      }
+    for (int j = 0; j < 2; ++j) {
+      const bool ok = pact && (r0 + j) <= last;
+      const uint32_t off = (pact ? (uint32_t)(2 * NQ * cpl) : 0u) + (uint32_t)min(r0 + j, last) * kstride;
+      load_group<F32, NQ>(gb, off, ok, rg, j);
+      load_group<F32, NQ>(qb, off, ok, rq, j);
+      load_group<F32, NQ>(kb, off, ok, rk, j);
+    }
     const uint32_t vc = vact ? (uint32_t)(2 * vcp) : 0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -283,6 +311,8 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
     const float bx = ldg<F32>(p.beta, row0 + (int64_t)min(tid, last) * H);
     rb = tid <= last ? bx : 0.f;
   }
+  // first channel of this thread's pair in quarter qt
+  auto chan = [&](int qt) -> int { return 2 * NQ * cpl + 2 * qt; };
   E* rec = reinterpret_cast<E*>(p.ws + (int64_t)item * R::BYTES);
   float* rgam = reinterpret_cast<float*>(p.ws + (int64_t)item * R::BYTES + R::GAM_BYTE);
 
@@ -317,7 +347,7 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
       Ef[1][ch] = x;
       Tb[ch] = __shfl(x, (tid & 63) | 7);  // row pair 7 of this sub-tile
     }
-    if (pact && rp == 7) *reinterpret_cast<float2*>(Eend + psb * DK + QW * qt + 2 * cpl) = make_float2(Tb[0], Tb[1]);
+    if (pact && rp == 7) *reinterpret_cast<float2*>(Eend + psb * DK + chan(qt)) = make_float2(Tb[0], Tb[1]);
   };
   const bool gated = gA > 0.f;  // uniform: one scan or the other, by a scalar branch
   auto scan = [&](int qt, float (&Ef)[2][2], float (&Tb)[2]) {
@@ -377,7 +407,7 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
 #pragma unroll
   for (int qt = 0; qt < NQ; ++qt) {
     if (pact) {
-      const int c0 = QW * qt + 2 * cpl;
+      const int c0 = chan(qt);
       // q, k as fp32 and 1 / E
       float qf[2][2], kf[2][2], iE[2][2];
 #pragma unroll
@@ -435,8 +465,8 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
       const int cl = 2 * cpl;
       float gp[Cf::NGAP > 0 ? Cf::NGAP : 1][2];
       if constexpr (Cf::NGAP > 0) {  // gap pairs (2,0), (3,0), (3,1): decay of the sub-tiles strictly between
-        const float2 e1 = *reinterpret_cast<const float2*>(Eend + 1 * DK + QW * qt + cl);
-        const float2 e2 = *reinterpret_cast<const float2*>(Eend + 2 * DK + QW * qt + cl);
+        const float2 e1 = *reinterpret_cast<const float2*>(Eend + 1 * DK + c0);
+        const float2 e2 = *reinterpret_cast<const float2*>(Eend + 2 * DK + c0);
         gp[0][0] = e1.x;
         gp[0][1] = e1.y;
         gp[1][0] = e1.x * e2.x;
