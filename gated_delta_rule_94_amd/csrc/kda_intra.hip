@@ -183,6 +183,21 @@ __device__ __forceinline__ void load_group(const void* base, uint32_t i, bool ok
   }
 }
 
+// The inverse of load_group: channel pairs w (bf16) or f (fp32), pair qt at channels 2 qt, + 1 of
+// a 2 NQ-channel group, stored with one 8- or 16-byte access per 16 bytes.
+template <bool F32, int NQ>
+__device__ __forceinline__ void store_group(void* dst, const uint32_t (&w)[NQ], const float2 (&f)[NQ]) {
+  if constexpr (F32) {
+#pragma unroll
+    for (int h = 0; h < NQ / 2; ++h)
+      reinterpret_cast<float4*>(dst)[h] = make_float4(f[2 * h].x, f[2 * h].y, f[2 * h + 1].x, f[2 * h + 1].y);
+  } else if constexpr (NQ == 4) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  }
+}
+
 // (sequence start token, length) of one chunk, and the first chunk of every sequence;
 // packed offsets are clamped to [0, T_total] exactly as the chunk map does.
 struct ChunkPos {
@@ -393,6 +408,10 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   f32x4 acc[NSLOT];
 #pragma unroll
   for (int sl = 0; sl < NSLOT; ++sl) acc[sl] = zero4();
+  // Q.Gamma of this thread's rows, one channel pair per quarter, stored after the last quarter as
+  // one access per row (bf16 packed pairs, or fp32 pairs)
+  uint32_t qgw[2][NQ];
+  float2 qgf[2][NQ];
   __syncthreads();
   if (norm && pact) {
 #pragma unroll
@@ -450,7 +469,9 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
             kg[j][ch] = kf[j][ch] * eg;
             kp[j][ch] = kf[j][ch] * (iE[j][ch] * tS[ch]);
           }
-          st2<F32>(rec + R::QG + (r0 + j) * DK + c0, qg[j][0], qg[j][1]);
+          if constexpr (F32) qgf[j][qt] = make_float2(qg[j][0], qg[j][1]);
+          else qgw[j][qt] = pack_bf16x2(qg[j][0], qg[j][1]);
+          if (qt == NQ - 1) store_group<F32, NQ>(rec + R::QG + (r0 + j) * DK + 2 * NQ * cpl, qgw[j], qgf[j]);
         }
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
