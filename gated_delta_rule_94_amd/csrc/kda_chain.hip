@@ -60,7 +60,7 @@ struct ChainCfg {
   static constexpr int NH = 4;        // copy waves
   static constexpr int NTH = 64 * (NW + NH);
   static constexpr int NC = 64 * NH;  // copy threads
-  static_assert(NW == 1 || NW == 2, "slice of 16 or 32 columns");
+  static_assert(NW == 1 || NW == 2 || NW == 4, "slice of 16, 32 or 64 columns");
   static constexpr int RS = DK + 8, TS = CP + 8, US = C + 8;  // US: stride of the U~^T slice [WS][C]
   static constexpr int ES = (int)sizeof(E);
   static constexpr int EPU = 16 / ES;  // elements per 16-byte copy unit
@@ -449,7 +449,8 @@ static hipError_t launch_chain_impl(const ChainLaunch& L) {
 }
 
 // Slice width: bf16 picks 32 or 16 value columns per workgroup (16 -- more workgroups -- when there
-// are few (sequence, head) units); fp32 uses 16.  Segment summaries use 32 (bf16) and 16 (fp32).
+// are few (sequence, head) units); fp32 uses 16.  Segment summaries use 32 or 64 (bf16: 64 when
+// 32-column slices would need more than one workgroup per CU) and 16 (fp32).
 #define KDA_CHAIN_BF16(X, D, V, CC) X(false, D, V, CC, 32) X(false, D, V, CC, 16)
 #define KDA_CHAIN_INSTANCES(X)                                                                                   \
   KDA_CHAIN_BF16(X, 64, 64, 16) KDA_CHAIN_BF16(X, 64, 64, 32) KDA_CHAIN_BF16(X, 64, 64, 64)                        \
@@ -466,6 +467,10 @@ static hipError_t launch_chain_impl(const ChainLaunch& L) {
   X(false, 64, 128, 16, 32) X(false, 64, 128, 32, 32) X(false, 64, 128, 64, 32)                                   \
   X(false, 128, 64, 16, 32) X(false, 128, 64, 32, 32) X(false, 128, 64, 64, 32)                                   \
   X(false, 128, 128, 16, 32) X(false, 128, 128, 32, 32) X(false, 128, 128, 64, 32)                                \
+  X(false, 64, 64, 16, 64) X(false, 64, 64, 32, 64) X(false, 64, 64, 64, 64)                                      \
+  X(false, 64, 128, 16, 64) X(false, 64, 128, 32, 64) X(false, 64, 128, 64, 64)                                   \
+  X(false, 128, 64, 16, 64) X(false, 128, 64, 32, 64) X(false, 128, 64, 64, 64)                                   \
+  X(false, 128, 128, 16, 64) X(false, 128, 128, 32, 64) X(false, 128, 128, 64, 64)                                \
   KDA_CHAIN_F32(X)
 
 hipError_t launch_chain(const ChainLaunch& L) {

@@ -133,7 +133,12 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
     float* send = reinterpret_cast<float*>(seg + al256((size_t)K.units * pl.nseg * a.dk * a.dv * 4));
     K.nseg = pl.nseg; K.seg_len = pl.seg_len; K.sstart = sstart; K.send = send;
     K.summary = true;
+    // the summary has d_k more columns than the chain; where its 32-column slices would need more
+    // than one round of workgroups (one per CU: the record buffers fill the LDS), bf16 summaries
+    // take 64-column slices, one round at twice the work per workgroup
+    if (!a.f32 && K.units * (int64_t)(pl.nseg - 1) * ((a.dv + a.dk) / 32) > compute_units()) K.ws = 64;
     if ((e = launch_chain(K)) != hipSuccess) return e;
+    K.ws = pl.ws;
     if ((e = launch_segment_combine(a.h0, send, sstart, K.units, pl.nseg, a.dk, a.dv, a.stream)) != hipSuccess) return e;
     K.summary = false;
   }

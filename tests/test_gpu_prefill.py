@@ -143,6 +143,18 @@ def test_segmented_chain_against_oracle(dt, B, T, H, dk, dv, chunk, h0):
     check(d, chunk, dt, "segmented plan %s" % (plan,))
 
 
+def test_segmented_wide_summary_against_oracle():
+    """64 segments of one (sequence, head) pair: the summary launch (d_k more columns than the
+    chain) would need more than one workgroup per CU at 32 columns, so it runs 64-column slices;
+    o and hT still match the oracle element by element."""
+    B, T, H, dk, dv, chunk = 1, 32805, 2, 64, 64, 16
+    plan = kda.chain_plan(B, T, H, dk, dv, chunk)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert B * H * (plan[1] - 1) * (dk + dv) // 32 > cus, (plan, cus)
+    d = datagen.prefill_inputs(733, B, T, H, dk, dv, BF16, 0.02)
+    check(d, chunk, BF16, "segmented plan %s, wide summary" % (plan,))
+
+
 def test_segmented_hT_aliases_h0():
     """In a segmented call h0 is read (by the start-state combine) before any segment writes hT."""
     assert kda.chain_plan(1, 4096, 8, 128, 128)[1] > 1
