@@ -29,6 +29,8 @@ The JSON line carries:
                     the state every 1024 tokens (prefix states for a serving cache)
   fused          -- the same workload through kda_chunked_forward_fused: gate from
                     its pre-activation, q and k normalised, output gate
+  mxfp8          -- the same workload with q, k and v in MXFP8 (E4M3 codes, one E8M0
+                    scale per 32 channels) through kda_chunked_forward_mxfp8
   decode         -- 1000 sequential kda_decode_step calls on the 256-sequence x
                     32-head state (512 MiB fp32), bytes and fraction of HBM
   workloads      -- the other seeded prefill workloads (fp32 2 x 256 tokens, 32
@@ -157,6 +159,7 @@ def main():
     ap.add_argument("--no-workloads", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--no-states", action="store_true", help="skip the state-snapshot leg")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-steps leg")
+    ap.add_argument("--no-mxfp8", action="store_true", help="skip the MXFP8-input leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward (training) leg")
     ap.add_argument("--workloads", default="", help="comma-separated subset of the other prefill workloads")
     ap.add_argument("--no-flush", action="store_true", help="do not evict the Infinity Cache between steps")
@@ -316,6 +319,27 @@ def main():
         out["fused"] = {"gate": "-5 sigmoid(x) in the kernel", "normalize_qk": True, "out_gate": True,
                         "ms_per_call": fms, "tokens_per_s": tokens / (fms * 1e-3), "overhead_vs_plain": fms / ms - 1.0}
         del gr
+
+    # ---------------- the same workload with MXFP8 q, k, v (quantised from the bf16 inputs)
+    if not args.no_mxfp8:
+        dm = datagen.mxfp8_prefill_inputs(w.seed, w.B, w.T, w.H, w.dk, w.dv, w.h0_std)
+        gm = {key: to_dev(dm[key]) for key in ("q8", "qs", "k8", "ks", "v8", "vs")}
+        del dm
+
+        def mstep(_i):
+            kda.kda_chunked_forward_mxfp8(gm["q8"], gm["qs"], gm["k8"], gm["ks"], gm["v8"], gm["vs"], g["g"], g["beta"],
+                                          g["h0"], chunk=w.chunk, o=o, hT=hT)
+
+        mstep(0)
+        torch.cuda.synchronize()
+        mms, _ = time_launches(mstep, args.steps, None if args.no_flush else flush)
+        # q, k, v one byte per element plus a scale byte per 32; g, beta, o bf16; h0 and hT fp32
+        per_th = (2 * w.dk + w.dv) * (1 + 1 / 32) + 2 * w.dk + 2 + 2 * w.dv
+        mbytes = w.B * w.T * w.H * per_th + w.B * w.H * 4 * w.dk * w.dv * 2
+        out["mxfp8"] = {"format": "E4M3 elements, E8M0 scale per 32 channels (q, k, v)", "ms_per_call": mms,
+                        "tokens_per_s": tokens / (mms * 1e-3), "ratio_to_bf16_call": mms / ms,
+                        "alg_bytes_per_call": mbytes, "hbm_frac": mbytes / (mms * 1e-3) / 8e12}
+        del gm
 
     # ---------------- backward of the same call (training): gradients of <do, o> + <dhT, hT>, the
     # forward recomputed inside

@@ -128,6 +128,47 @@ def prefill_inputs(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: i
     return d
 
 
+def _e4m3_encode(y):
+    """FP8 E4M3 codes of fp64 values y, rounded to the nearest representable value (ties to the
+    even mantissa) and saturated to +-448.  Spacing of the E4M3 grid: 2^-9 below 2^-6
+    (subnormals), 2^(E-3) in [2^E, 2^(E+1))."""
+    y = np.asarray(y, np.float64)
+    neg = np.signbit(y)
+    a = np.minimum(np.abs(y), 448.0)
+    E = np.clip(np.floor(np.log2(np.maximum(a, 2.0 ** -6))), -6, 8)
+    step = np.exp2(E - 3)
+    r = np.minimum(np.round(a / step) * step, 448.0)  # np.round: ties to even
+    sub = r < 2.0 ** -6
+    Er = np.floor(np.log2(np.maximum(r, 2.0 ** -6)))
+    m = np.where(sub, r / 2.0 ** -9, r / np.exp2(Er) * 8.0 - 8.0)
+    code = np.where(sub, m, (Er + 7) * 8 + m).astype(np.int64)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def mxfp8_quantize(x, block=32):
+    """MXFP8 encoding of fp64 x [..., d]: per block of 32 channels the smallest shared scale 2^X
+    that keeps every x / 2^X within the largest E4M3 magnitude, X = ceil(log2(max |x| / 448))
+    (clamped to [-127, 127]; X = 0 for an all-zero block), then each x / 2^X as E4M3 (nearest).
+    Returns (codes uint8 [..., d], scale codes uint8 [..., d/block])."""
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    xb = x.reshape(x.shape[:-1] + (d // block, block))
+    amax = np.abs(xb).max(axis=-1)
+    X = np.where(amax > 0, np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / 448.0)), 0.0)
+    X = np.clip(X, -127, 127)
+    codes = _e4m3_encode(xb / np.exp2(X)[..., None]).reshape(x.shape)
+    return np.ascontiguousarray(codes), np.ascontiguousarray((X + 127).astype(np.uint8))
+
+
+def mxfp8_prefill_inputs(seed: int, B: int, T: int, H: int, dk: int, dv: int, h0_std=None, sub: int = 0):
+    """prefill_inputs (bf16) with q, k and v also in MXFP8: keys q8, qs, k8, ks, v8, vs (codes,
+    scale codes) quantised from the bf16 values; g and beta stay bf16."""
+    d = prefill_inputs(seed, B, T, H, dk, dv, DT_BF16, h0_std, sub)
+    for name in ("q", "k", "v"):
+        d[name + "8"], d[name[0] + "s"] = mxfp8_quantize(to_f64(d[name]))
+    return d
+
+
 def backward_adjoints(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: int, dhT_std=None, sub: int = 0):
     """Adjoints for a backward call: do [B,T,H,dv] N(0,1) in the input dtype, dhT [B,H,dk,dv] fp32
     N(0, dhT_std) (or None)."""

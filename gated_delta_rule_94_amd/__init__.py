@@ -37,7 +37,7 @@ EXPORTS = (
     "kda_chunked_forward", "kda_chunked_forward_with_states", "kda_chunked_forward_varlen_with_states",
     "kda_chunked_forward_fused", "kda_decode_step_fused", "kda_chunked_forward_ex", "kda_chunked_forward_varlen_ex",
     "kda_chunked_forward_profiled", "kda_chunked_forward_varlen", "kda_chunked_forward_varlen_workspace_bytes",
-    "kda_decode_step", "kda_chunked_backward", "kda_chunked_backward_workspace_bytes",
+    "kda_decode_step", "kda_chunked_backward", "kda_chunked_backward_workspace_bytes", "kda_chunked_forward_mxfp8",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -65,6 +65,8 @@ _lib.kda_chunked_forward_profiled.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp, _sz,
 _lib.kda_chunked_forward_profiled.restype = _i32
 _lib.kda_chunked_forward_varlen.argtypes = [_vp] * 8 + [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
 _lib.kda_chunked_forward_varlen.restype = _i32
+_lib.kda_chunked_forward_mxfp8.argtypes = [_vp] * 11 + [_i32] * 6 + [_vp, _sz, _vp]
+_lib.kda_chunked_forward_mxfp8.restype = _i32
 _lib.kda_decode_step.argtypes = [_vp] * 7 + [_i32] * 4 + [_i32, _vp]
 _lib.kda_decode_step.restype = _i32
 
@@ -199,6 +201,38 @@ def kda_chunked_forward(q, k, v, g, beta, h0=None, *, chunk: int = 64, o=None, h
                                   B, T, H, dk, dv, chunk, _dtype_code(q), _ptr(ws), _nbytes(ws), _stream(stream))
     if st:
         raise KDAError("kda_chunked_forward", st)
+    return o, hT
+
+
+def kda_chunked_forward_mxfp8(q, q_scale, k, k_scale, v, v_scale, g, beta, h0=None, *, chunk: int = 64, o=None,
+                              hT=None, want_hT: bool = True, workspace=None, stream=None):
+    """Chunked prefill with MXFP8 q, k, v: q, k [B,T,H,dk] and v [B,T,H,dv] uint8 E4M3 codes;
+    q_scale, k_scale [B,T,H,dk//32] and v_scale [B,T,H,dv//32] uint8 E8M0 scale codes (one per 32
+    channels); g [B,T,H,dk] and beta [B,T,H] bfloat16; h0 [B,H,dk,dv] float32 or None.  Returns
+    (o [B,T,H,dv] bfloat16, hT float32 or None)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    u8, bf = torch.uint8, torch.bfloat16
+    for name, t, shp, dt in (("q", q, (B, T, H, dk), u8), ("k", k, (B, T, H, dk), u8), ("v", v, (B, T, H, dv), u8),
+                             ("q_scale", q_scale, (B, T, H, dk // 32), u8), ("k_scale", k_scale, (B, T, H, dk // 32), u8),
+                             ("v_scale", v_scale, (B, T, H, dv // 32), u8), ("g", g, (B, T, H, dk), bf),
+                             ("beta", beta, (B, T, H), bf)):
+        _check(name, t, shp, dt, dev)
+    _check("h0", h0, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=bf, device=dev)
+    _check("o", o, (B, T, H, dv), bf, dev)
+    if hT is None and want_hT:
+        hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check("hT", hT, (B, H, dk, dv), torch.float32, dev)
+    ws_bytes = _lib.kda_chunked_forward_workspace_bytes(B, T, H, dk, dv, chunk, KDA_BF16)
+    ws = _workspace(workspace, ws_bytes, dev)
+    st = _lib.kda_chunked_forward_mxfp8(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(v), _ptr(v_scale),
+                                        _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT), B, T, H, dk, dv, chunk,
+                                        _ptr(ws), _nbytes(ws), _stream(stream))
+    if st:
+        raise KDAError("kda_chunked_forward_mxfp8", st)
     return o, hT
 
 

@@ -261,6 +261,36 @@ kda_status kda_chunked_forward_varlen_with_states(const void* q, const void* k, 
                                        workspace_bytes, hip_stream);
 }
 
+kda_status kda_chunked_forward_mxfp8(const void* q, const void* q_scale, const void* k, const void* k_scale,
+                                     const void* v, const void* v_scale, const void* g, const void* beta,
+                                     const float* h0, void* o, float* hT, int B, int T, int H, int d_k, int d_v,
+                                     int chunk, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
+  const kda_status st = check_prefill(q, k, v, g, beta, h0, o, hT, B * T, H, d_k, d_v, chunk, KDA_BF16);
+  if (st != KDA_OK) return st;
+  if ((int64_t)B * T > 0 && (!q_scale || !k_scale || !v_scale)) return KDA_ERR_INVALID_ARG;
+  if (B == 0) return KDA_OK;
+  if (T == 0 && !hT) return KDA_OK;
+  if (!workspace_ok(workspace, workspace_bytes, kda_chunked_forward_workspace_bytes(B, T, H, d_k, d_v, chunk, KDA_BF16)))
+    return KDA_ERR_WORKSPACE;
+  kda::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.q_scale = static_cast<const uint8_t*>(q_scale);
+  a.k_scale = static_cast<const uint8_t*>(k_scale);
+  a.v_scale = static_cast<const uint8_t*>(v_scale);
+  a.h0 = h0; a.o = o; a.hT = hT;
+  a.cu_seqlens = nullptr;
+  a.num_seqs = B;
+  a.T = T;
+  a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk;
+  a.f32 = false;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  a.stream = hip_stream;
+  return kda::launch_chunked_forward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_chunked_forward_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,
                                       const float* h0, void* o, float* hT, const int32_t* cu_seqlens, int num_seqs,
                                       int T_total, int max_seqlen, int H, int d_k, int d_v, int chunk, kda_dtype dt,

@@ -29,6 +29,7 @@ struct DecodeArgs {
 
 struct PrefillArgs {
   const void *q, *k, *v, *g, *beta;
+  const uint8_t *q_scale = nullptr, *k_scale = nullptr, *v_scale = nullptr;  // non-NULL: q, k, v are MXFP8
   const float* h0;
   void* o;
   float* hT;
@@ -49,6 +50,7 @@ struct PrefillArgs {
 // intra-chunk kernel launch (kda_intra.hip)
 struct IntraLaunch {
   const void *q, *k, *v, *g, *beta;
+  const uint8_t *qs = nullptr, *ks = nullptr, *vs = nullptr;  // non-NULL: q, k, v are MXFP8 (E4M3 codes)
   const int32_t* cu;
   const int32_t* chunk0;
   unsigned char* records;

@@ -61,6 +61,7 @@ namespace kda {
 
 struct IntraParams {
   const void *q, *k, *v, *g, *beta;
+  const uint8_t *qs, *ks, *vs;  // MXFP8 inputs: E8M0 scale codes of q, k, v (q, k, v hold E4M3 codes)
   const int32_t* cu;      // packed-sequence offsets [num_seqs + 1], or NULL for equal-length sequences
   const int32_t* chunk0;  // first chunk of each packed sequence [num_seqs + 1] (with cu), else NULL
   unsigned char* ws;      // records
@@ -198,6 +199,21 @@ __device__ __forceinline__ void store_group(void* dst, const uint32_t (&w)[NQ], 
   }
 }
 
+// OCP Microscaling (MX) inputs: a block of 32 consecutive channels shares one E8M0 scale code s,
+// worth 2^(s - 127) (code 255 is NaN); each element is an FP8 E4M3 code.  gfx950 converts a pair of
+// E4M3 codes and multiplies by a float scale in one instruction (checked against the E4M3
+// definition on all 256 codes, subnormals and NaN included).
+__device__ __forceinline__ float e8m0_scale(uint32_t s) {
+  return __uint_as_float(s == 0u ? 0x00400000u : (s == 255u ? 0x7fc00000u : s << 23));
+}
+// E4M3 codes in bytes 0-1 (hi: bytes 2-3) of w, times 2^(s - 127)
+__device__ __forceinline__ float2 mx_decode2(uint32_t w, uint32_t s, bool hi) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  const float sc = e8m0_scale(s);
+  const f2_t x = hi ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, sc, true) : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, sc, false);
+  return make_float2(x.x, x.y);
+}
+
 // (sequence start token, length) of one chunk, and the first chunk of every sequence;
 // packed offsets are clamped to [0, T_total] exactly as the chunk map does.
 struct ChunkPos {
@@ -238,8 +254,9 @@ __device__ __forceinline__ ChunkPos chunk_pos(const IntraParams& p, int chunk, i
   return cp;
 }
 
-template <bool F32, int DK, int DV, int C>
+template <bool F32, int DK, int DV, int C, bool MX>
 __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_chunk_kernel(const IntraParams p) {
+  static_assert(!(MX && F32), "MXFP8 inputs take the bf16 path");
   using Cf = IntraCfg<F32, DK, DV, C>;
   using O = typename Cf::O;
   using E = typename Cf::E;
@@ -290,6 +307,10 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
 
   constexpr int NQ = Cf::NQ;
   Raw2<F32> rg[NQ][2], rq[NQ][2], rk[NQ][2], rv[8];
+  // MXFP8 inputs: the E4M3 codes of this thread's q and k rows (2 NQ channels, one scale block) and
+  // of its 8 v pairs, with their scale codes; decoded where they are used, so the loads stay in
+  // flight until then
+  uint32_t mq[2][(NQ + 1) / 2], mk[2][(NQ + 1) / 2], sq[2], sk[2], mv[8], sv[8];
   float rb;
   bool rok[2];  // rows r0, r0 + 1 lie in the chunk (the others are zero padding)
   {
@@ -314,20 +335,64 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
       const bool ok = pact && (r0 + j) <= last;
       const uint32_t off = (pact ? (uint32_t)(2 * NQ * cpl) : 0u) + (uint32_t)min(r0 + j, last) * kstride;
       load_group<F32, NQ>(gb, off, ok, rg, j);
-      load_group<F32, NQ>(qb, off, ok, rq, j);
-      load_group<F32, NQ>(kb, off, ok, rk, j);
+      if constexpr (MX) {
+        // one byte per element: element offsets are byte offsets; padding rows take code 0 (= 0)
+        // with scale code 127 (= 1)
+        const uint8_t* qb8 = static_cast<const uint8_t*>(p.q) + row0 * DK;
+        const uint8_t* kb8 = static_cast<const uint8_t*>(p.k) + row0 * DK;
+        const uint32_t soff = (uint32_t)min(r0 + j, last) * (uint32_t)(H * (DK / 32)) + (pact ? (uint32_t)(2 * NQ * cpl / 32) : 0u);
+        if constexpr (NQ == 4) {
+          const uint2 a = *reinterpret_cast<const uint2*>(qb8 + off), b = *reinterpret_cast<const uint2*>(kb8 + off);
+          mq[j][0] = ok ? a.x : 0u;
+          mq[j][1] = ok ? a.y : 0u;
+          mk[j][0] = ok ? b.x : 0u;
+          mk[j][1] = ok ? b.y : 0u;
+        } else {
+          const uint32_t a = *reinterpret_cast<const uint32_t*>(qb8 + off), b = *reinterpret_cast<const uint32_t*>(kb8 + off);
+          mq[j][0] = ok ? a : 0u;
+          mk[j][0] = ok ? b : 0u;
+        }
+        const uint32_t a = p.qs[row0 * (DK / 32) + soff], b = p.ks[row0 * (DK / 32) + soff];
+        sq[j] = ok ? a : 127u;
+        sk[j] = ok ? b : 127u;
+      } else {
+        load_group<F32, NQ>(qb, off, ok, rq, j);
+        load_group<F32, NQ>(kb, off, ok, rk, j);
+      }
     }
     const uint32_t vc = vact ? (uint32_t)(2 * vcp) : 0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const bool okv = vact && (8 * vtg + i) <= last;
-      rv[i].load32(vb, vc + (uint32_t)min(8 * vtg + i, last) * vstride, okv);
+      const uint32_t vrow = (uint32_t)min(8 * vtg + i, last);
+      if constexpr (MX) {
+        const uint8_t* vb8 = static_cast<const uint8_t*>(p.v) + row0 * DV;
+        const uint32_t a = *reinterpret_cast<const uint16_t*>(vb8 + vc + vrow * vstride);
+        const uint32_t b = p.vs[row0 * (DV / 32) + vrow * (uint32_t)(H * (DV / 32)) + vc / 32];
+        mv[i] = okv ? a : 0u;
+        sv[i] = okv ? b : 127u;
+      } else {
+        rv[i].load32(vb, vc + vrow * vstride, okv);
+      }
     }
     const float bx = ldg<F32>(p.beta, row0 + (int64_t)min(tid, last) * H);
     rb = tid <= last ? bx : 0.f;
   }
   // first channel of this thread's pair in quarter qt
   auto chan = [&](int qt) -> int { return 2 * NQ * cpl + 2 * qt; };
+  // this thread's q, k pair of quarter qt in row j, and its v pair of token i, as fp32
+  auto qpair = [&](int qt, int j) -> float2 {
+    if constexpr (MX) return mx_decode2(mq[j][qt >> 1], sq[j], (qt & 1) != 0);
+    else return rq[qt][j].f();
+  };
+  auto kpair = [&](int qt, int j) -> float2 {
+    if constexpr (MX) return mx_decode2(mk[j][qt >> 1], sk[j], (qt & 1) != 0);
+    else return rk[qt][j].f();
+  };
+  auto vpair = [&](int i) -> float2 {
+    if constexpr (MX) return mx_decode2(mv[i], sv[i], false);
+    else return rv[i].f();
+  };
   E* rec = reinterpret_cast<E*>(p.ws + (int64_t)item * R::BYTES);
   float* rgam = reinterpret_cast<float*>(p.ws + (int64_t)item * R::BYTES + R::GAM_BYTE);
 
@@ -383,7 +448,7 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
     for (int qt = 0; qt < NQ; ++qt)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float2 a = rq[qt][j].f(), b = rk[qt][j].f();
+        const float2 a = qpair(qt, j), b = kpair(qt, j);
         ss[j] += a.x * a.x + a.y * a.y;
         ss[2 + j] += b.x * b.x + b.y * b.y;
       }
@@ -431,7 +496,7 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
       float qf[2][2], kf[2][2], iE[2][2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float2 qq = rq[qt][j].f(), kk = rk[qt][j].f();
+        const float2 qq = qpair(qt, j), kk = kpair(qt, j);
         qf[j][0] = qq.x;
         qf[j][1] = qq.y;
         kf[j][0] = kk.x;
@@ -556,7 +621,7 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
         float x0[8], x1[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float2 vv = rv[i].f();
+          const float2 vv = vpair(i);
           x0[i] = vv.x;
           x1[i] = vv.y;
         }
@@ -738,14 +803,15 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
   }
 }
 
-template <bool F32, int DK, int DV, int C>
+template <bool F32, int DK, int DV, int C, bool MX>
 static hipError_t launch_intra_impl(const IntraLaunch& L) {
   IntraParams p;
   p.q = L.q; p.k = L.k; p.v = L.v; p.g = L.g; p.beta = L.beta;
+  p.qs = L.qs; p.ks = L.ks; p.vs = L.vs;
   p.cu = L.cu; p.chunk0 = L.chunk0; p.ws = L.records;
   p.num_seqs = L.num_seqs; p.H = L.H; p.T = L.T; p.nch = L.nch;
   p.gate_scale = L.gate_scale; p.normalize_qk = L.normalize_qk ? 1 : 0;
-  hipLaunchKernelGGL((intra_chunk_kernel<F32, DK, DV, C>), dim3(L.grid), dim3(512), 0, (hipStream_t)L.stream, p);
+  hipLaunchKernelGGL((intra_chunk_kernel<F32, DK, DV, C, MX>), dim3(L.grid), dim3(512), 0, (hipStream_t)L.stream, p);
   return hipGetLastError();
 }
 
@@ -765,10 +831,22 @@ hipError_t launch_chunk_map(const int32_t* cu, int num_seqs, int T, int C, int32
   X(true, 64, 128, 16) X(true, 64, 128, 32) X(true, 64, 128, 64)                                        \
   X(true, 128, 64, 16) X(true, 128, 64, 32) X(true, 128, 128, 16) X(true, 128, 128, 32)
 
+// MXFP8 q, k, v: the bf16 shapes
+#define KDA_INTRA_MX_INSTANCES(X)                                                                       \
+  X(false, 64, 64, 16) X(false, 64, 64, 32) X(false, 64, 64, 64)                                        \
+  X(false, 64, 128, 16) X(false, 64, 128, 32) X(false, 64, 128, 64)                                     \
+  X(false, 128, 64, 16) X(false, 128, 64, 32) X(false, 128, 64, 64)                                     \
+  X(false, 128, 128, 16) X(false, 128, 128, 32) X(false, 128, 128, 64)
+
 hipError_t launch_intra(const IntraLaunch& L) {
+  const bool mx = L.qs != nullptr;
 #define KDA_LAUNCH(F, D, V, CC) \
-  if (L.f32 == F && L.dk == D && L.dv == V && L.chunk == CC) return launch_intra_impl<F, D, V, CC>(L);
+  if (!mx && L.f32 == F && L.dk == D && L.dv == V && L.chunk == CC) return launch_intra_impl<F, D, V, CC, false>(L);
   KDA_INTRA_INSTANCES(KDA_LAUNCH)
+#undef KDA_LAUNCH
+#define KDA_LAUNCH(F, D, V, CC) \
+  if (mx && L.f32 == F && L.dk == D && L.dv == V && L.chunk == CC) return launch_intra_impl<F, D, V, CC, true>(L);
+  KDA_INTRA_MX_INSTANCES(KDA_LAUNCH)
 #undef KDA_LAUNCH
   return hipErrorInvalidValue;
 }

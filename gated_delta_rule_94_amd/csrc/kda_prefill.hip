@@ -107,6 +107,7 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
   if (items > 0) {
     IntraLaunch L;
     L.q = a.q; L.k = a.k; L.v = a.v; L.g = a.g; L.beta = a.beta;
+    L.qs = a.q_scale; L.ks = a.k_scale; L.vs = a.v_scale;
     L.cu = a.cu_seqlens; L.chunk0 = chunk0; L.records = records;
     L.num_seqs = a.num_seqs; L.H = a.H; L.T = a.T; L.nch = nch;
     L.dk = a.dk; L.dv = a.dv; L.chunk = C; L.f32 = a.f32;

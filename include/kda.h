@@ -161,6 +161,32 @@ kda_status kda_chunked_forward_fused(const void* q, const void* k, const void* v
  * kda_chunked_forward_with_states; states may be NULL) and fused steps
  * (fusion: see kda_fusion; may be NULL).
  */
+/*
+ * kda_chunked_forward with q, k and v in the OCP Microscaling FP8 format
+ * (MXFP8): the pages train K3 with MXFP8 activations (how-K3-works page, "The
+ * systems layer": quantisation-aware training with MXFP4 weights and MXFP8
+ * activations), so the inputs of the recurrence may arrive in it.
+ *   q, k     [B,T,H,d_k] uint8: FP8 E4M3 codes (sign, 4 exponent bits with
+ *            bias 7, 3 mantissa bits; no infinities; 0x7F / 0xFF are NaN)
+ *   v        [B,T,H,d_v] uint8: FP8 E4M3 codes
+ *   q_scale, k_scale [B,T,H,d_k/32], v_scale [B,T,H,d_v/32] uint8: E8M0
+ *            scale codes, one per block of 32 consecutive channels of a
+ *            (token, head); code s stands for 2^(s-127), 255 is NaN
+ * Element x of a block with scale code s stands for E4M3(x) * 2^(s-127).
+ * g, beta and o are bf16, h0 / hT fp32, all as for kda_chunked_forward with
+ * KDA_BF16.  The kernels decode q, k and v as they load them; every decoded
+ * value of magnitude >= 2^-133 is a bf16 value, so the call computes what
+ * kda_chunked_forward (KDA_BF16) computes on the decoded q, k, v.  Workspace:
+ * kda_chunked_forward_workspace_bytes(..., KDA_BF16).  q, k, v 16-byte
+ * aligned; scales have no alignment requirement.  Same shapes, errors and
+ * stream semantics as kda_chunked_forward (KDA_ERR_INVALID_ARG also for a NULL
+ * scale pointer when B * T > 0).
+ */
+kda_status kda_chunked_forward_mxfp8(const void* q, const void* q_scale, const void* k, const void* k_scale,
+                                     const void* v, const void* v_scale, const void* g, const void* beta,
+                                     const float* h0, void* o, float* hT, int B, int T, int H, int d_k, int d_v,
+                                     int chunk, void* workspace, size_t workspace_bytes, void* hip_stream);
+
 kda_status kda_chunked_forward_ex(const void* q, const void* k, const void* v, const void* g, const void* beta,
                                   const float* h0, void* o, float* hT, float* states, int state_every,
                                   const kda_fusion* fusion, int B, int T, int H, int d_k, int d_v, int chunk,

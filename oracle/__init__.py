@@ -17,6 +17,11 @@ linearity, column independence, varlen = independent calls, decode = prefill,
 norm bound), a hand-computed worked example under tests/golden/, and an fp64
 chunked mirror of the chunkwise (UT/WY) algebra.
 
+MXFP8 inputs (``mxfp8_decode``, ``forward_mxfp8``) are decoded from the published OCP
+Microscaling definition (E4M3 elements, E8M0 block scales of 32) and then run through the same
+fp64 recurrence; the decoder is pinned in tests/test_oracle_mxfp8.py by the format's defining
+values (largest normal 448, smallest subnormal 2^-9, the NaN codes, the scale range).
+
 The backward (``backward``: reverse-mode gradients through the same recurrence) is
 pinned in tests/test_oracle_backward_pins.py: finite differences of the forward,
 directional derivatives across its checkpoint blocks, the adjoint identity of the
@@ -273,3 +278,50 @@ def backward(q, k, v, g, beta, h0, do, dhT=None, nthreads=None):
     if rc:
         raise RuntimeError("kda_oracle_backward: invalid arguments")
     return dq, dkk, dvv, dg, db, dh0
+
+
+# ---------------------------------------------------------------------------------------------
+# MXFP8 inputs.  The how-K3-works page ("The systems layer") says K3 trains with MXFP8
+# activations; the format itself is the OCP Microscaling (MX) one:
+#   - an element is FP8 E4M3: sign bit, 4 exponent bits e (bias 7), 3 mantissa bits m;
+#     e = 0 is subnormal, m * 2^-9; otherwise (1 + m/8) * 2^(e-7); e = 15 with m = 7 is NaN
+#     (no infinities), so the largest finite magnitude is 1.75 * 2^8 = 448;
+#   - a block of 32 consecutive elements shares an E8M0 scale: an unsigned exponent s worth
+#     2^(s-127), with s = 255 NaN;
+#   - the value of an element is its E4M3 value times its block's scale.
+
+
+def e4m3_value(codes):
+    """fp64 value of FP8 E4M3 codes (uint8 array), per the OCP definition."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where((c & 0x80) != 0, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def e8m0_value(codes):
+    """fp64 value of E8M0 scale codes (uint8 array): 2^(s-127), NaN for 255."""
+    s = np.asarray(codes).astype(np.int64)
+    return np.where(s == 255, np.nan, np.exp2((s - 127).astype(np.float64)))
+
+
+def mxfp8_decode(codes, scales, block=32):
+    """fp64 values of an MXFP8 tensor: codes [..., d] uint8 (E4M3), scales [..., d/block] uint8
+    (E8M0); element i of the last axis takes scale i // block."""
+    codes = np.asarray(codes)
+    scales = np.asarray(scales)
+    d = codes.shape[-1]
+    assert d % block == 0 and scales.shape == codes.shape[:-1] + (d // block,)
+    x = e4m3_value(codes).reshape(codes.shape[:-1] + (d // block, block))
+    return np.ascontiguousarray((x * e8m0_value(scales)[..., None]).reshape(codes.shape))
+
+
+def forward_mxfp8(q, q_scale, k, k_scale, v, v_scale, g, beta, h0=None, want_o=True, want_hT=True, nthreads=None):
+    """forward() on MXFP8 q, k, v (codes and scales as above), bf16 / fp32 / fp64 g and beta:
+    the inputs are decoded to their exact fp64 values first.  Returns fp64 (o, hT)."""
+    return forward(mxfp8_decode(q, q_scale), mxfp8_decode(k, k_scale), mxfp8_decode(v, v_scale),
+                   np.ascontiguousarray(_dec(g)), np.ascontiguousarray(_dec(beta)), h0,
+                   want_o=want_o, want_hT=want_hT, nthreads=nthreads)

@@ -106,6 +106,26 @@ def test_prefill_validation():
     assert fwd(B=0, ptr=None, ws=None, ws_bytes=0) == OK
 
 
+def fmx(B=1, T=64, H=2, dk=64, dv=64, chunk=64, ptr=FAKE, scale=FAKE + 1, h0=None, hT=None, ws=FAKE, ws_bytes=1 << 40):
+    return kda.lib().kda_chunked_forward_mxfp8(ptr, scale, ptr, scale, ptr, scale, ptr, ptr, h0, ptr, hT, B, T, H, dk,
+                                               dv, chunk, ws, ws_bytes, None)
+
+
+def test_mxfp8_validation():
+    """MXFP8 q, k, v: the bf16 shapes and checks, plus non-NULL scale pointers (any alignment)."""
+    assert fmx(scale=None) == INVALID
+    assert fmx(ptr=FAKE + 8) == INVALID  # misaligned codes
+    assert fmx(ptr=None) == INVALID
+    assert fmx(B=-1) == INVALID
+    assert fmx(dk=96) == UNSUPPORTED
+    assert fmx(chunk=128) == UNSUPPORTED
+    need = kda.lib().kda_chunked_forward_workspace_bytes(1, 64, 2, 64, 64, 64, 1)
+    assert fmx(ws=None) == 3
+    assert fmx(ws_bytes=need - 1) == 3
+    assert fmx(B=0, ptr=None, scale=None, ws=None, ws_bytes=0) == OK
+    assert fmx(T=0, ptr=None, scale=None, ws=None, ws_bytes=0) == OK  # nothing to read and no hT
+
+
 def test_states_validation():
     """Snapshot arguments are checked before anything would run: a 16-byte-aligned buffer and an
     interval that is a positive multiple of the chunk; a NULL buffer ignores the interval."""
