@@ -268,7 +268,7 @@ def main():
                    "timing": "K back-to-back steps between two HIP events, cache evicted once before"},
         "roofline": {"bound": "hbm", "achieved": gbs_intra, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs_intra / HBM_PEAK_GBS, "traffic": measured_traffic("intra"),
-                     "kernel": "kda::intra_chunk_kernel<false, 128, 128, 64>", "ms_per_launch": k_ms[0],
+                     "kernel": "kda::intra_chunk_kernel<false, 128, 128, 64, false>", "ms_per_launch": k_ms[0],
                      "alg_bytes_per_launch": intra_bytes},
         "roofline_chain": {"bound": "hbm", "achieved": gbs_chain, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": gbs_chain / HBM_PEAK_GBS, "traffic": measured_traffic("chain"),
