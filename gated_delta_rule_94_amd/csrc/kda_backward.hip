@@ -222,6 +222,40 @@ struct ChainStage {
   }
 };
 
+// Eight consecutive elements of an input tensor (element offset i, a multiple of 8) staged in LDS:
+// copy8 keeps the element type (bf16 bits or fp32 values unchanged), copy8f widens to fp32.  One
+// 16-byte global access per bf16 group (two for fp32); !ok stores zeros.
+template <bool F32>
+__device__ __forceinline__ void copy8(const void* src, int64_t i, void* dst, bool ok) {
+  if constexpr (F32) {
+    const float4* s4 = reinterpret_cast<const float4*>(static_cast<const float*>(src) + i);
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 a = s4[0], b = s4[1];
+    reinterpret_cast<float4*>(dst)[0] = ok ? a : z;
+    reinterpret_cast<float4*>(dst)[1] = ok ? b : z;
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + i);
+    *reinterpret_cast<uint4*>(dst) = ok ? w : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+template <bool F32>
+__device__ __forceinline__ void copy8f(const void* src, int64_t i, float* dst, bool ok) {
+  if constexpr (F32) {
+    copy8<true>(src, i, dst, ok);
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + i);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    float x[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      x[2 * m] = ok ? __uint_as_float(u[m] << 16) : 0.f;
+      x[2 * m + 1] = ok ? __uint_as_float(u[m] & 0xffff0000u) : 0.f;
+    }
+    reinterpret_cast<float4*>(dst)[0] = make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4*>(dst)[1] = make_float4(x[4], x[5], x[6], x[7]);
+  }
+}
+
 template <bool F32, int DK, int DV, int C>
 __global__ __launch_bounds__(512) void bwd_chain_kernel(BwdParams p) {
   using Cf = BChainCfg<F32, DK, DV, C>;
@@ -375,9 +409,10 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
     pd[0] = (E)d.x; pd[1] = (E)d.y; pd[2] = (E)d.z; pd[3] = (E)d.w;
   }
   const int64_t orow = ((int64_t)b * p.T + (int64_t)ch * C) * H + h;
-  for (int e = tid; e < C * DV; e += NTH) {
-    const int r = e / DV, j = e - r * DV;
-    sdO[r * SV + j] = (E)(r < nr ? ldg<F32>(p.dO, (orow + (int64_t)r * H) * DV + j) : 0.f);
+  for (int e = tid; e < C * DV / 8; e += NTH) {
+    const int r = (8 * e) / DV, j = 8 * e - r * DV;
+    const bool ok = r < nr;
+    copy8<F32>(p.dO, (orow + (int64_t)(ok ? r : 0) * H) * DV + j, sdO + r * SV + j, ok);
   }
   for (int e = tid; e < C * DK; e += NTH) {
     const int r = e / DK, c = e - r * DK;
@@ -554,18 +589,20 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   const int64_t row0 = ((int64_t)b * p.T + (int64_t)ch * C) * H + h;  // (token, head) row of the chunk's first token
   const float* gr = p.grads + item * GL::FLOATS;
 
-  // ---- stage q, k, v, g, beta (rows past the chunk's end are zero), then G = cumsum(g)
-  for (int e = tid; e < C * DK; e += NTH) {
-    const int r = e / DK, c = e - r * DK;
+  // ---- stage q, k, v, g, beta, 8 consecutive channels per access (rows past the chunk's end read
+  // row 0 and store zeros), then G = cumsum(g)
+  for (int e = tid; e < C * DK / 8; e += NTH) {
+    const int r = (8 * e) / DK, c = 8 * e - r * DK;
     const bool ok = r < nr;
-    const int64_t gi = (row0 + (int64_t)r * H) * DK + c;
-    sQ[r * SK + c] = (E)(ok ? ldg<F32>(p.q, gi) : 0.f);
-    sK[r * SK + c] = (E)(ok ? ldg<F32>(p.k, gi) : 0.f);
-    sG[r * SG + c] = ok ? ldg<F32>(p.g, gi) : 0.f;
+    const int64_t gi = (row0 + (int64_t)(ok ? r : 0) * H) * DK + c;
+    copy8<F32>(p.q, gi, sQ + r * SK + c, ok);
+    copy8<F32>(p.k, gi, sK + r * SK + c, ok);
+    copy8f<F32>(p.g, gi, sG + r * SG + c, ok);
   }
-  for (int e = tid; e < C * DV; e += NTH) {
-    const int r = e / DV, j = e - r * DV;
-    sV[r * SV + j] = (E)(r < nr ? ldg<F32>(p.v, (row0 + (int64_t)r * H) * DV + j) : 0.f);
+  for (int e = tid; e < C * DV / 8; e += NTH) {
+    const int r = (8 * e) / DV, j = 8 * e - r * DV;
+    const bool ok = r < nr;
+    copy8<F32>(p.v, (row0 + (int64_t)(ok ? r : 0) * H) * DV + j, sV + r * SV + j, ok);
   }
   if (tid < C) sBeta[tid] = tid < nr ? ldg<F32>(p.beta, row0 + (int64_t)tid * H) : 0.f;
   __syncthreads();
