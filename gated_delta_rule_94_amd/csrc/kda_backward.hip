@@ -238,6 +238,22 @@ __device__ __forceinline__ void copy8(const void* src, int64_t i, void* dst, boo
     *reinterpret_cast<uint4*>(dst) = ok ? w : make_uint4(0u, 0u, 0u, 0u);
   }
 }
+// copy8 keeping elements 0 .. keep-1 of the group and storing zeros for the rest
+template <bool F32>
+__device__ __forceinline__ void copy8_head(const void* src, int64_t i, void* dst, int keep) {
+  if constexpr (F32) {
+    const float4* s4 = reinterpret_cast<const float4*>(static_cast<const float*>(src) + i);
+    const float4 a = s4[0], b = s4[1];
+    reinterpret_cast<float4*>(dst)[0] = make_float4(keep > 0 ? a.x : 0.f, keep > 1 ? a.y : 0.f, keep > 2 ? a.z : 0.f,
+                                                    keep > 3 ? a.w : 0.f);
+    reinterpret_cast<float4*>(dst)[1] = make_float4(keep > 4 ? b.x : 0.f, keep > 5 ? b.y : 0.f, keep > 6 ? b.z : 0.f,
+                                                    keep > 7 ? b.w : 0.f);
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + i);
+    auto m = [&](int e) -> uint32_t { return (keep > e ? 0x0000ffffu : 0u) | (keep > e + 1 ? 0xffff0000u : 0u); };
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w.x & m(0), w.y & m(2), w.z & m(4), w.w & m(6));
+  }
+}
 template <bool F32>
 __device__ __forceinline__ void copy8f(const void* src, int64_t i, float* dst, bool ok) {
   if constexpr (F32) {
@@ -414,9 +430,9 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
     const bool ok = r < nr;
     copy8<F32>(p.dO, (orow + (int64_t)(ok ? r : 0) * H) * DV + j, sdO + r * SV + j, ok);
   }
-  for (int e = tid; e < C * DK; e += NTH) {
-    const int r = e / DK, c = e - r * DK;
-    sNW[r * SK + c] = rec[R::NW + e];
+  for (int e = tid; e < C * DK / 8; e += NTH) {
+    const int r = (8 * e) / DK, c = 8 * e - r * DK;
+    copy8<F32>(rec, R::NW + 8 * e, sNW + r * SK + c, true);
   }
   __syncthreads();
   // U = U~ + (-W) S0  (U~ from the record's U~^T)
@@ -437,13 +453,13 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
     gr[GL::DGL + c] = gam[c] * sum;
   }
   __syncthreads();
-  for (int e = tid; e < C * C; e += NTH) {
-    const int s_ = e / C, r = e - s_ * C;
-    sP[s_ * SC + r] = r <= s_ ? rec[R::P + s_ * CP + r] : (E)0.f;
+  for (int e = tid; e < C * C / 8; e += NTH) {  // P's lower triangle (record tiles above it are not all written)
+    const int s_ = (8 * e) / C, r = 8 * e - s_ * C;
+    copy8_head<F32>(rec, R::P + s_ * CP + r, sP + s_ * SC + r, s_ - r + 1);
   }
-  for (int e = tid; e < DK * C; e += NTH) {
-    const int c = e / C, r = e - c * C;
-    sKPT[c * SC + r] = rec[R::KPT + c * CP + r];
+  for (int e = tid; e < DK * C / 8; e += NTH) {
+    const int c = (8 * e) / C, r = 8 * e - c * C;
+    copy8<F32>(rec, R::KPT + c * CP + r, sKPT + c * SC + r, true);
   }
   __syncthreads();
   // dU[r][j] = sum_{s >= r} P[s][r] dO[s][j] + sum_c Kd^T[c][r] dS1[c][j]
