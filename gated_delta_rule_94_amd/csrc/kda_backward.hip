@@ -446,11 +446,16 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) sU[(i0 + 4 * grp + r) * SV + j0 + lo] = (E)acc[r];
   }
-  // e^{gl} rowsum(S0 . dS1)
-  for (int c = tid; c < DK; c += NTH) {
+  // e^{gl} rowsum(S0 . dS1): NTH / DK adjacent lanes per channel, each over every (NTH / DK)-th column
+  {
+    constexpr int NPCH = NTH / DK;
+    static_assert(NPCH * DK == NTH && (NPCH & (NPCH - 1)) == 0 && NPCH <= 64, "lanes per channel");
+    const int c = tid / NPCH, part = tid - c * NPCH;
     float sum = 0.f;
-    for (int j = 0; j < DV; ++j) sum = fmaf(tf(sS0[c * SV + j]), tf(sdS[c * SV + j]), sum);
-    gr[GL::DGL + c] = gam[c] * sum;
+    for (int j = part; j < DV; j += NPCH) sum = fmaf(tf(sS0[c * SV + j]), tf(sdS[c * SV + j]), sum);
+#pragma unroll
+    for (int off = 1; off < NPCH; off <<= 1) sum += __shfl_xor(sum, off);
+    if (part == 0) gr[GL::DGL + c] = gam[c] * sum;
   }
   __syncthreads();
   for (int e = tid; e < C * C / 8; e += NTH) {  // P's lower triangle (record tiles above it are not all written)
@@ -775,9 +780,9 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     for (int o = 1; o < NPC; o <<= 1) s += __shfl_xor(s, o, NPC);
     if (u == 0 && r < nr) stg<F32>(p.dbeta, row0 + (int64_t)r * H, sDb[r] + s);
   }
-  for (int e = tid; e < C * C; e += NTH) {
-    const int r = e / C, i = e - r * C;
-    sM4[r * SM + i] = gr[GL::DP + r * C + i];
+  for (int e = tid; e < C * C / 4; e += NTH) {  // 4 floats per access (records of grads are 256-byte aligned)
+    const int r = (4 * e) / C, i = 4 * e - r * C;
+    *reinterpret_cast<float4*>(sM4 + r * SM + i) = reinterpret_cast<const float4*>(gr + GL::DP)[e];
   }
   __syncthreads();
 
