@@ -213,6 +213,23 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
   const int ocol = col0 + 16 * (chain ? wave : 0) + 4 * grp;  // first of this lane's 4 output columns
   const int col0b = (idsl ? 0 : col0) * C * ES_;  // first U~^T row of the slice
 
+  // output gate of this lane's outputs of the chunk being computed (rows past the range re-read its
+  // last token, in bounds): the chain waves load chunk c + 1's once chunk c's outputs are stored, so
+  // the loads have a whole chunk step to arrive
+  using ZV = std::conditional_t<F32, float4, uint2>;
+  ZV zv[NT];
+  const bool gz = !SUM && p.z != nullptr;
+  auto load_z = [&](int c) {
+    const int64_t t0 = t_begin + (int64_t)c * C;
+    const int len = (int)((t_end - t0) < C ? (t_end - t0) : C);
+    const int64_t obase = (t0 * H + h) * DV;
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt) {
+      const int row = 16 * bt + lo < len ? 16 * bt + lo : len - 1;
+      zv[bt] = *reinterpret_cast<const ZV*>(static_cast<const E*>(p.z) + obase + (int64_t)row * ostride + ocol);
+    }
+  };
+
   // one chunk of the chain from LDS buffer `buf`
   auto chunk_step = [&](int c, int buf) {
     const unsigned char* b = smem + buf * Cf::BUF;
@@ -226,18 +243,6 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     const int len = (int)((t_end - t0) < C ? (t_end - t0) : C);
     const int64_t obase = (t0 * H + h) * DV;  // output element of (token t0, head h, column 0): uniform
     if (!chain) return;
-    // output gate of this lane's outputs, loaded now and used at the stores (rows past the range
-    // re-read its last token, in bounds)
-    using ZV = std::conditional_t<F32, float4, uint2>;
-    ZV zv[NT];
-    const bool gz = !SUM && p.z != nullptr;
-    if (gz) {
-#pragma unroll
-      for (int bt = 0; bt < NT; ++bt) {
-        const int row = 16 * bt + lo < len ? 16 * bt + lo : len - 1;
-        zv[bt] = *reinterpret_cast<const ZV*>(static_cast<const E*>(p.z) + obase + (int64_t)row * ostride + ocol);
-      }
-    }
     // Phases, each issuing the LDS fragment loads of the next so that LDS latency hides behind
     // MFMAs; the state update (the chunk-to-chunk critical path) comes first:
     //   1  -W fragments, U~                   2  U = U~ - W S            | K'^T fragments, gamma
@@ -346,6 +351,7 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
         }
       }
     }
+    if (gz && c + 1 < nchunks) load_z(c + 1);
   };
   // state snapshot after chunk c when it ends `every` tokens into the sequence (every is a multiple
   // of C, so only a full chunk can): the prefix states a serving cache resumes from.  Wave-uniform.
@@ -388,6 +394,7 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
 #pragma unroll
         for (int r = 0; r < 4; ++r) Sacc[m][r] = s0 ? s0[(16 * m + 4 * grp + r) * DV + ccol] : 0.f;
     }
+    if (gz && nchunks > 0) load_z(0);
     __syncthreads();
     for (int c = 0; c < nchunks; c += 2) {
       chunk_step(c, 0);
