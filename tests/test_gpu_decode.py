@@ -34,6 +34,15 @@ def test_decode_fp32(dk, dv):
     assert eo < 1e-4 and es < 1e-4
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+def test_decode_bf16_shapes(dk, dv):
+    B, H = 5, 3
+    s0 = datagen.decode_state0(3, B, H, dk, dv)
+    eo, es = run_steps(13, B, H, dk, dv, datagen.DT_BF16, 40, s0)
+    print("decode bf16 dk=%d dv=%d: o %.2e state %.2e" % (dk, dv, eo, es))
+    assert eo < TOL[datagen.DT_BF16] and es < TOL[datagen.DT_BF16]
+
+
 def test_decode_bf16_many_steps():
     B, H, d = 4, 8, 128
     s0 = datagen.decode_state0(2, B, H, d, d)
