@@ -213,20 +213,20 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
   const int ocol = col0 + 16 * (chain ? wave : 0) + 4 * grp;  // first of this lane's 4 output columns
   const int col0b = (idsl ? 0 : col0) * C * ES_;  // first U~^T row of the slice
 
-  // output gate of this lane's outputs of the chunk being computed (rows past the range re-read its
-  // last token, in bounds): the chain waves load chunk c + 1's once chunk c's outputs are stored, so
-  // the loads have a whole chunk step to arrive
+  // output gate of this lane's outputs (rows past the range re-read its last token, in bounds), in two
+  // register sets: chunk c's in set c & 1.  A chunk step first issues the next chunk's loads into the
+  // other set, so every set has a whole chunk step to arrive before its stores use it
   using ZV = std::conditional_t<F32, float4, uint2>;
-  ZV zv[NT];
+  ZV zv[2][NT];
   const bool gz = !SUM && p.z != nullptr;
-  auto load_z = [&](int c) {
+  auto load_z = [&](int c, ZV (&z)[NT]) {
     const int64_t t0 = t_begin + (int64_t)c * C;
     const int len = (int)((t_end - t0) < C ? (t_end - t0) : C);
     const int64_t obase = (t0 * H + h) * DV;
 #pragma unroll
     for (int bt = 0; bt < NT; ++bt) {
       const int row = 16 * bt + lo < len ? 16 * bt + lo : len - 1;
-      zv[bt] = *reinterpret_cast<const ZV*>(static_cast<const E*>(p.z) + obase + (int64_t)row * ostride + ocol);
+      z[bt] = *reinterpret_cast<const ZV*>(static_cast<const E*>(p.z) + obase + (int64_t)row * ostride + ocol);
     }
   };
 
@@ -243,6 +243,7 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     const int len = (int)((t_end - t0) < C ? (t_end - t0) : C);
     const int64_t obase = (t0 * H + h) * DV;  // output element of (token t0, head h, column 0): uniform
     if (!chain) return;
+    if (gz && c + 1 < nchunks) load_z(c + 1, zv[buf ^ 1]);
     // Phases, each issuing the LDS fragment loads of the next so that LDS latency hides behind
     // MFMAs; the state update (the chunk-to-chunk critical path) comes first:
     //   1  -W fragments, U~                   2  U = U~ - W S            | K'^T fragments, gamma
@@ -333,10 +334,10 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
       if (gz) {
         float zf[4];
         if constexpr (F32) {
-          zf[0] = zv[bt].x; zf[1] = zv[bt].y; zf[2] = zv[bt].z; zf[3] = zv[bt].w;
+          zf[0] = zv[buf][bt].x; zf[1] = zv[buf][bt].y; zf[2] = zv[buf][bt].z; zf[3] = zv[buf][bt].w;
         } else {
-          zf[0] = __uint_as_float(zv[bt].x << 16); zf[1] = __uint_as_float(zv[bt].x & 0xffff0000u);
-          zf[2] = __uint_as_float(zv[bt].y << 16); zf[3] = __uint_as_float(zv[bt].y & 0xffff0000u);
+          zf[0] = __uint_as_float(zv[buf][bt].x << 16); zf[1] = __uint_as_float(zv[buf][bt].x & 0xffff0000u);
+          zf[2] = __uint_as_float(zv[buf][bt].y << 16); zf[3] = __uint_as_float(zv[buf][bt].y & 0xffff0000u);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) Ot[bt][i] *= zf[i];
@@ -351,7 +352,6 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
         }
       }
     }
-    if (gz && c + 1 < nchunks) load_z(c + 1);
   };
   // state snapshot after chunk c when it ends `every` tokens into the sequence (every is a multiple
   // of C, so only a full chunk can): the prefix states a serving cache resumes from.  Wave-uniform.
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
 #pragma unroll
         for (int r = 0; r < 4; ++r) Sacc[m][r] = s0 ? s0[(16 * m + 4 * grp + r) * DV + ccol] : 0.f;
     }
-    if (gz && nchunks > 0) load_z(0);
+    if (gz && nchunks > 0) load_z(0, zv[0]);
     __syncthreads();
     for (int c = 0; c < nchunks; c += 2) {
       chunk_step(c, 0);
