@@ -50,7 +50,7 @@ struct ChainParams {
   const void* z;          // or NULL: an output gate, laid out and typed like o, multiplying o
 };
 
-template <bool F32, int DK, int DV, int C, int WS>
+template <bool F32, int DK, int DV, int C, int WS, bool ZG = false>
 struct ChainCfg {
   using O = Op<F32>;
   using E = typename O::E;
@@ -71,7 +71,13 @@ struct ChainCfg {
   static constexpr int B_KPT = al(B_P + C * TS * ES);
   static constexpr int B_UT = al(B_KPT + DK * TS * ES);
   static constexpr int B_GAM = al(B_UT + WS * US * ES);
-  static constexpr int BUF = al(B_GAM + DK * 4);
+  // the output gate of the slice's outputs, [C][ZROW bytes] (rows padded by 16 bytes), where the
+  // launch writes o (ZG) and two buffers still fit in LDS (HAS_Z; else the chain waves read it from
+  // global memory at the stores)
+  static constexpr int ZROW = WS * ES + 16, B_Z = al(B_GAM + DK * 4);
+  static constexpr int BUF0 = B_Z, BUFZ = al(B_Z + C * ZROW);
+  static constexpr bool HAS_Z = ZG && 2 * BUFZ <= 163840;
+  static constexpr int BUF = HAS_Z ? BUFZ : BUF0;
   static constexpr int TOTAL = 2 * BUF;
   static_assert(TOTAL <= 163840, "LDS budget of one gfx950 workgroup");
   // 16-byte copy units of one record slice: -W, Q.Gamma, P, K'^T, U~ slice, gamma
@@ -131,7 +137,7 @@ struct CopyPart {
 
 template <bool F32, int DK, int DV, int C, int WS, bool SUM>
 __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainParams p) {
-  using Cf = ChainCfg<F32, DK, DV, C, WS>;
+  using Cf = ChainCfg<F32, DK, DV, C, WS, !SUM>;
   using O = typename Cf::O;
   using E = typename Cf::E;
   using R = typename Cf::R;
@@ -199,6 +205,7 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     CopyPart<Cf::NC, Cf::U_KPT, CP / EPU, (int)(R::KPT * ES_), CP * ES_, Cf::B_KPT, TS * ES_, !F32> kpt;
     CopyPart<Cf::NC, Cf::U_UT, C / EPU, (int)(R::UT * ES_), C * ES_, Cf::B_UT, US * ES_, !F32> ut;  // record pointer + col0 rows
     CopyPart<Cf::NC, Cf::U_GAM, Cf::U_GAM, (int)R::GAM_BYTE, 0, Cf::B_GAM, 0> gam;
+    uint4 zg;  // output gate: one 16-byte unit of the chunk's [C][WS] slice per copy thread
     __device__ __forceinline__ void load(const unsigned char* rp, int ht, int col0b) {
       nw.load(rp, ht); kpt.load(rp, ht); ut.load(rp + col0b, ht); gam.load(rp, ht);
       if constexpr (!SUM) { qg.load(rp, ht); pp.load(rp, ht); }  // a summary writes no o
@@ -212,23 +219,24 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
   const int ostride = H * DV;                               // output elements between consecutive tokens
   const int ocol = col0 + 16 * (chain ? wave : 0) + 4 * grp;  // first of this lane's 4 output columns
   const int col0b = (idsl ? 0 : col0) * C * ES_;  // first U~^T row of the slice
-
-  // output gate of this lane's outputs (rows past the range re-read its last token, in bounds), in two
-  // register sets: chunk c's in set c & 1.  A chunk step first issues the next chunk's loads into the
-  // other set, so every set has a whole chunk step to arrive before its stores use it
-  using ZV = std::conditional_t<F32, float4, uint2>;
-  ZV zv[2][NT];
-  const bool gz = !SUM && p.z != nullptr;
-  auto load_z = [&](int c, ZV (&z)[NT]) {
+  // the output gate's units: ZU per row of the slice, C rows; rows past the chunk re-read its last
+  // token (in bounds, never stored to o)
+  constexpr int ZU = WS * ES_ / 16;
+  static_assert(!Cf::HAS_Z || C * ZU <= Cf::NC, "one output-gate unit per copy thread");
+  auto load_z = [&](Stage& st, int c) {
+    const int u = ht < C * ZU ? ht : C * ZU - 1, row = u / ZU;
     const int64_t t0 = t_begin + (int64_t)c * C;
     const int len = (int)((t_end - t0) < C ? (t_end - t0) : C);
-    const int64_t obase = (t0 * H + h) * DV;
-#pragma unroll
-    for (int bt = 0; bt < NT; ++bt) {
-      const int row = 16 * bt + lo < len ? 16 * bt + lo : len - 1;
-      z[bt] = *reinterpret_cast<const ZV*>(static_cast<const E*>(p.z) + obase + (int64_t)row * ostride + ocol);
-    }
+    const int64_t zi = ((t0 + (row < len ? row : len - 1)) * H + h) * DV + col0 + (u % ZU) * (16 / ES_);
+    st.zg = *reinterpret_cast<const uint4*>(static_cast<const E*>(p.z) + zi);
   };
+  auto store_z = [&](const Stage& st, unsigned char* b) {
+    if (ht < C * ZU) *reinterpret_cast<uint4*>(b + Cf::B_Z + (ht / ZU) * Cf::ZROW + 16 * (ht % ZU)) = st.zg;
+  };
+
+  // output gate: the copy waves stream each chunk's [C][WS] slice into the chunk's LDS buffer with
+  // its record, and the chain waves read it there at the stores
+  const bool gz = !SUM && p.z != nullptr;
 
   // one chunk of the chain from LDS buffer `buf`
   auto chunk_step = [&](int c, int buf) {
@@ -243,7 +251,6 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     const int len = (int)((t_end - t0) < C ? (t_end - t0) : C);
     const int64_t obase = (t0 * H + h) * DV;  // output element of (token t0, head h, column 0): uniform
     if (!chain) return;
-    if (gz && c + 1 < nchunks) load_z(c + 1, zv[buf ^ 1]);
     // Phases, each issuing the LDS fragment loads of the next so that LDS latency hides behind
     // MFMAs; the state update (the chunk-to-chunk critical path) comes first:
     //   1  -W fragments, U~                   2  U = U~ - W S            | K'^T fragments, gamma
@@ -333,11 +340,17 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
       for (int sk = 0; sk < O::nks(16 * (bt + 1)); ++sk) Ot[bt] = O::mma(uf[sk], pf[bt][sk], Ot[bt]);
       if (gz) {
         float zf[4];
+        const int zrow = 16 * bt + lo < len ? 16 * bt + lo : len - 1;
+        const unsigned char* zr =
+            Cf::HAS_Z ? b + Cf::B_Z + (16 * bt + lo) * Cf::ZROW + (ocol - col0) * ES_
+                      : reinterpret_cast<const unsigned char*>(static_cast<const E*>(p.z) + obase + (int64_t)zrow * ostride + ocol);
         if constexpr (F32) {
-          zf[0] = zv[buf][bt].x; zf[1] = zv[buf][bt].y; zf[2] = zv[buf][bt].z; zf[3] = zv[buf][bt].w;
+          const float4 zv = *reinterpret_cast<const float4*>(zr);
+          zf[0] = zv.x; zf[1] = zv.y; zf[2] = zv.z; zf[3] = zv.w;
         } else {
-          zf[0] = __uint_as_float(zv[buf][bt].x << 16); zf[1] = __uint_as_float(zv[buf][bt].x & 0xffff0000u);
-          zf[2] = __uint_as_float(zv[buf][bt].y << 16); zf[3] = __uint_as_float(zv[buf][bt].y & 0xffff0000u);
+          const uint2 zv = *reinterpret_cast<const uint2*>(zr);
+          zf[0] = __uint_as_float(zv.x << 16); zf[1] = __uint_as_float(zv.x & 0xffff0000u);
+          zf[2] = __uint_as_float(zv.y << 16); zf[3] = __uint_as_float(zv.y & 0xffff0000u);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) Ot[bt][i] *= zf[i];
@@ -394,7 +407,6 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
 #pragma unroll
         for (int r = 0; r < 4; ++r) Sacc[m][r] = s0 ? s0[(16 * m + 4 * grp + r) * DV + ccol] : 0.f;
     }
-    if (gz && nchunks > 0) load_z(0, zv[0]);
     __syncthreads();
     for (int c = 0; c < nchunks; c += 2) {
       chunk_step(c, 0);
@@ -422,17 +434,24 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     Stage s0, s1;
     if (nchunks > 0) {
       s0.load(rec_of(0), ht, col0b);
+      if (Cf::HAS_Z && gz) load_z(s0, 0);
       s0.store(smem, ht);
+      if (Cf::HAS_Z && gz) store_z(s0, smem);
       s1.load(rec_of(last < 1 ? last : 1), ht, col0b);
+      if (Cf::HAS_Z && gz) load_z(s1, last < 1 ? last : 1);
     }
     __syncthreads();
     for (int c = 0; c < nchunks; c += 2) {
       s0.load(rec_of(c + 2 < last ? c + 2 : last), ht, col0b);
+      if (Cf::HAS_Z && gz) load_z(s0, c + 2 < last ? c + 2 : last);
       s1.store(smem + Cf::BUF, ht);
+      if (Cf::HAS_Z && gz) store_z(s1, smem + Cf::BUF);
       __syncthreads();
       if (c + 1 >= nchunks) break;
       s1.load(rec_of(c + 3 < last ? c + 3 : last), ht, col0b);
+      if (Cf::HAS_Z && gz) load_z(s1, c + 3 < last ? c + 3 : last);
       s0.store(smem, ht);
+      if (Cf::HAS_Z && gz) store_z(s0, smem);
       __syncthreads();
     }
   }
@@ -451,7 +470,7 @@ static hipError_t launch_chain_impl(const ChainLaunch& L) {
   const int64_t grid = ((su + 7) / 8) * 8 * ((SUM ? DV + DK : DV) / WS);
   if (su <= 0 || grid > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL((chain_kernel<F32, DK, DV, C, WS, SUM>), dim3((unsigned)grid),
-                     dim3(ChainCfg<F32, DK, DV, C, WS>::NTH), 0, (hipStream_t)L.stream, p);
+                     dim3(ChainCfg<F32, DK, DV, C, WS, !SUM>::NTH), 0, (hipStream_t)L.stream, p);
   return hipGetLastError();
 }
 
