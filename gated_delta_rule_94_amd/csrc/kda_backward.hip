@@ -22,6 +22,8 @@
 //
 // Every product is fp32 arithmetic on operands staged in LDS (bf16 inputs and records stay bf16
 // there, which is exact for inputs and is the forward's own operand rounding for records).
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_record.h"
@@ -167,7 +169,8 @@ struct BChainCfg {
   static constexpr int OFF_DS = OFF_DU + ((C * SE * ES + 15) & ~15);
   static constexpr int TOTAL = OFF_DS + DK * SS * 4;
   static constexpr int NTH = 512;
-  static constexpr int N16 = REC_BYTES / 16, NPF = (N16 + NTH - 1) / NTH, NDO = (C * WS + NTH - 1) / NTH;
+  // dO slice in units of 4 consecutive columns of one row
+  static constexpr int N16 = REC_BYTES / 16, NPF = (N16 + NTH - 1) / NTH, NU4 = C * WS / 4, NDO = (NU4 + NTH - 1) / NTH;
   static_assert(REC_BYTES % 16 == 0 && BUF % 16 == 0, "record prefix is a whole number of 16-byte vectors");
   static_assert(DK <= NTH, "one e^{gl} entry per thread");
   static_assert(TOTAL <= 160 * 1024, "LDS");
@@ -182,10 +185,11 @@ struct ChainStage {
   using E = typename Cf::E;
   // the slots in one vector each, so that they stay in registers
   typedef uint32_t pf_t __attribute__((ext_vector_type(4 * Cf::NPF)));
-  typedef float do_t __attribute__((ext_vector_type(Cf::NDO)));
+  using DW = std::conditional_t<F32, float4, uint2>;  // 4 elements of dO
   pf_t pf;
   float pg;
-  do_t pdo;
+  DW pdo[Cf::NDO];   // raw dO units: loaded unconditionally (clamped rows), so that no wait for
+  bool pok[Cf::NDO];  // them is needed before put; pok: the unit lies in the chunk
   __device__ __forceinline__ void fetch(const BwdParams& p, int b, int h, int ch, int col0, int tid) {
     const unsigned char* rec = p.records + ((int64_t)(b * p.nch + ch) * p.H + h) * R::BYTES;
 #pragma unroll
@@ -202,8 +206,11 @@ struct ChainStage {
     const int64_t orow = ((int64_t)b * p.T + (int64_t)ch * C) * p.H + h;
 #pragma unroll
     for (int i = 0; i < Cf::NDO; ++i) {
-      const int e = tid + Cf::NTH * i, r = e / Cf::WS, j = e - r * Cf::WS;
-      pdo[i] = (e < C * Cf::WS && r < nr) ? ldg<F32>(p.dO, (orow + (int64_t)r * p.H) * DV + col0 + j) : 0.f;
+      const int e = tid + Cf::NTH * i, r = (4 * e) / Cf::WS, j = 4 * e - r * Cf::WS;
+      const bool ok = e < Cf::NU4 && r < nr;  // row 0 always lies in the chunk (nr >= 1)
+      pdo[i] = *reinterpret_cast<const DW*>(static_cast<const E*>(p.dO) + (orow + (int64_t)(ok ? r : 0) * p.H) * DV +
+                                            col0 + (ok ? j : 0));
+      pok[i] = ok;
     }
   }
   __device__ __forceinline__ void put(unsigned char* base, int tid) const {
@@ -216,8 +223,11 @@ struct ChainStage {
     E* d = reinterpret_cast<E*>(base + Cf::OFF_DO);
 #pragma unroll
     for (int i = 0; i < Cf::NDO; ++i) {
-      const int e = tid + Cf::NTH * i, r = e / Cf::WS, j = e - r * Cf::WS;
-      if (e < C * Cf::WS) d[r * Cf::SE + j] = (E)pdo[i];
+      const int e = tid + Cf::NTH * i, r = (4 * e) / Cf::WS, j = 4 * e - r * Cf::WS;
+      DW z;
+      if constexpr (F32) z = make_float4(0.f, 0.f, 0.f, 0.f);
+      else z = make_uint2(0u, 0u);
+      if (e < Cf::NU4) *reinterpret_cast<DW*>(d + r * Cf::SE + j) = pok[i] ? pdo[i] : z;
     }
   }
 };
