@@ -58,6 +58,15 @@ def test_fused_prefill_fp32(opt):
     fused_case(d, 32, F32, *OPTS[opt], "fused fp32 %s" % opt)
 
 
+@pytest.mark.parametrize("dv", [64, 128])
+def test_fused_fp32_chunk64_gate_read_at_stores(dv):
+    """fp32, d_k = 64, chunk 64: the chain kernel's two record buffers leave no LDS for the output
+    gate, so its chain waves read the gate from global memory at the stores (the other instances
+    stream it through LDS with the records)."""
+    d = raw_inputs(703 + dv, 2, 200, 2, 64, dv, F32)
+    fused_case(d, 64, F32, *OPTS["all"], "fused fp32 chunk 64 dv=%d" % dv)
+
+
 @pytest.mark.parametrize("T", [1, 17, 100])
 def test_fused_gate_ragged_chunks(T):
     """Rows past a partial chunk's end must keep a decay of 1 (their pre-activation loads as 0, and
