@@ -232,6 +232,18 @@ struct ChainStage {
   }
 };
 
+// f(e) for e = tid, tid + NTH, ... below N, unrolled with a compile-time trip count (a guarded tail
+// only when NTH does not divide N): the loads of every iteration can then be in flight together
+// instead of one wait per iteration
+template <int N, int NTH, typename F>
+__device__ __forceinline__ void for_units(int tid, F&& f) {
+#pragma unroll
+  for (int i = 0; i < N / NTH; ++i) f(tid + NTH * i);
+  if constexpr (N % NTH != 0) {
+    if (tid + NTH * (N / NTH) < N) f(tid + NTH * (N / NTH));
+  }
+}
+
 // Eight consecutive elements of an input tensor (element offset i, a multiple of 8) staged in LDS:
 // copy8 keeps the element type (bf16 bits or fp32 values unchanged), copy8f widens to fp32.  One
 // 16-byte global access per bf16 group (two for fp32); !ok stores zeros.
@@ -425,25 +437,28 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
   const float* ds1 = p.dstates + (unit * p.nch + ch) * DK * DV;
   float* gr = p.grads + item * GL::FLOATS;
 
-  for (int e = tid; e < DK * DV / 4; e += NTH) {
+  const bool has_s0 = s0 != nullptr;
+  const float4* s0v = reinterpret_cast<const float4*>(has_s0 ? s0 : ds1);  // loaded unconditionally, zeroed after
+  for_units<DK * DV / 4, NTH>(tid, [&](int e) {
     const int c = (4 * e) / DV, j = 4 * e - c * DV;
-    const float4 a = s0 ? reinterpret_cast<const float4*>(s0)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 a0 = s0v[e];
+    const float4 a = has_s0 ? a0 : make_float4(0.f, 0.f, 0.f, 0.f);
     const float4 d = reinterpret_cast<const float4*>(ds1)[e];
     E* pa = sS0 + c * SV + j;
     E* pd = sdS + c * SV + j;
     pa[0] = (E)a.x; pa[1] = (E)a.y; pa[2] = (E)a.z; pa[3] = (E)a.w;
     pd[0] = (E)d.x; pd[1] = (E)d.y; pd[2] = (E)d.z; pd[3] = (E)d.w;
-  }
+  });
   const int64_t orow = ((int64_t)b * p.T + (int64_t)ch * C) * H + h;
-  for (int e = tid; e < C * DV / 8; e += NTH) {
+  for_units<C * DV / 8, NTH>(tid, [&](int e) {
     const int r = (8 * e) / DV, j = 8 * e - r * DV;
     const bool ok = r < nr;
     copy8<F32>(p.dO, (orow + (int64_t)(ok ? r : 0) * H) * DV + j, sdO + r * SV + j, ok);
-  }
-  for (int e = tid; e < C * DK / 8; e += NTH) {
+  });
+  for_units<C * DK / 8, NTH>(tid, [&](int e) {
     const int r = (8 * e) / DK, c = 8 * e - r * DK;
     copy8<F32>(rec, R::NW + 8 * e, sNW + r * SK + c, true);
-  }
+  });
   __syncthreads();
   // U = U~ + (-W) S0  (U~ from the record's U~^T)
   for (int t = wave; t < (C / 16) * (DV / 16); t += NTH / 64) {
@@ -468,14 +483,14 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
     if (part == 0) gr[GL::DGL + c] = gam[c] * sum;
   }
   __syncthreads();
-  for (int e = tid; e < C * C / 8; e += NTH) {  // P's lower triangle (record tiles above it are not all written)
+  for_units<C * C / 8, NTH>(tid, [&](int e) {  // P's lower triangle (record tiles above it are not all written)
     const int s_ = (8 * e) / C, r = 8 * e - s_ * C;
     copy8_head<F32>(rec, R::P + s_ * CP + r, sP + s_ * SC + r, s_ - r + 1);
-  }
-  for (int e = tid; e < DK * C / 8; e += NTH) {
+  });
+  for_units<DK * C / 8, NTH>(tid, [&](int e) {
     const int c = (8 * e) / C, r = 8 * e - c * C;
     copy8<F32>(rec, R::KPT + c * CP + r, sKPT + c * SC + r, true);
-  }
+  });
   __syncthreads();
   // dU[r][j] = sum_{s >= r} P[s][r] dO[s][j] + sum_c Kd^T[c][r] dS1[c][j]
   for (int t = wave; t < (C / 16) * (DV / 16); t += NTH / 64) {
@@ -622,19 +637,19 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
 
   // ---- stage q, k, v, g, beta, 8 consecutive channels per access (rows past the chunk's end read
   // row 0 and store zeros), then G = cumsum(g)
-  for (int e = tid; e < C * DK / 8; e += NTH) {
+  for_units<C * DK / 8, NTH>(tid, [&](int e) {
     const int r = (8 * e) / DK, c = 8 * e - r * DK;
     const bool ok = r < nr;
     const int64_t gi = (row0 + (int64_t)(ok ? r : 0) * H) * DK + c;
     copy8<F32>(p.q, gi, sQ + r * SK + c, ok);
     copy8<F32>(p.k, gi, sK + r * SK + c, ok);
     copy8f<F32>(p.g, gi, sG + r * SG + c, ok);
-  }
-  for (int e = tid; e < C * DV / 8; e += NTH) {
+  });
+  for_units<C * DV / 8, NTH>(tid, [&](int e) {
     const int r = (8 * e) / DV, j = 8 * e - r * DV;
     const bool ok = r < nr;
     copy8<F32>(p.v, (row0 + (int64_t)(ok ? r : 0) * H) * DV + j, sV + r * SV + j, ok);
-  }
+  });
   if (tid < C) sBeta[tid] = tid < nr ? ldg<F32>(p.beta, row0 + (int64_t)tid * H) : 0.f;
   __syncthreads();
   scan_rows<DK, C, Cf::NPART, Cf::RPP, false>(sG, SG, sScan, tid);
@@ -790,10 +805,10 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     for (int o = 1; o < NPC; o <<= 1) s += __shfl_xor(s, o, NPC);
     if (u == 0 && r < nr) stg<F32>(p.dbeta, row0 + (int64_t)r * H, sDb[r] + s);
   }
-  for (int e = tid; e < C * C / 4; e += NTH) {  // 4 floats per access (records of grads are 256-byte aligned)
+  for_units<C * C / 4, NTH>(tid, [&](int e) {  // 4 floats per access (records of grads are 256-byte aligned)
     const int r = (4 * e) / C, i = 4 * e - r * C;
     *reinterpret_cast<float4*>(sM4 + r * SM + i) = reinterpret_cast<const float4*>(gr + GL::DP)[e];
-  }
+  });
   __syncthreads();
 
   // ---- through Ekk and Eqk, on the owned tiles (rows r0.., channels c0..):
