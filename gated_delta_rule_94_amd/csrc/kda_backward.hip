@@ -244,6 +244,26 @@ __device__ __forceinline__ void for_units(int tid, F&& f) {
   }
 }
 
+// Sum over aligned groups of N lanes (N a power of two up to 64), every lane of a group receiving
+// the total.  Within 16 lanes the partner values come through DPP (quad permutations for lane xor 1
+// and 2, then the mirrors that give lane i lanes 7 - i and 15 - i of its group) rather than through
+// an LDS permute; each addition pairs the same two partial sums as a butterfly over xor 1, 2, 4, 8.
+template <int CTRL>
+__device__ __forceinline__ float dpp_read(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float s) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "lane group");
+  if constexpr (N >= 2) s += dpp_read<0xB1>(s);   // quad_perm [1, 0, 3, 2]
+  if constexpr (N >= 4) s += dpp_read<0x4E>(s);   // quad_perm [2, 3, 0, 1]
+  if constexpr (N >= 8) s += dpp_read<0x141>(s);  // row_half_mirror
+  if constexpr (N >= 16) s += dpp_read<0x140>(s); // row_mirror
+  if constexpr (N >= 32) s += __shfl_xor(s, 16, N);
+  if constexpr (N >= 64) s += __shfl_xor(s, 32, N);
+  return s;
+}
+
 // Eight consecutive elements of an input tensor (element offset i, a multiple of 8) staged in LDS:
 // copy8 keeps the element type (bf16 bits or fp32 values unchanged), copy8f widens to fp32.  One
 // 16-byte global access per bf16 group (two for fp32); !ok stores zeros.
@@ -679,19 +699,31 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   // ---- L = (I + A)^{-1}, A = diag(beta) Ekk: column j by forward substitution, NL lanes per column,
   // lane u holding rows u + NL m
   if (tid < C * NL) {
+    // At step r only rows below r are known (x of every later row is still 0) and Ekk is strictly
+    // lower, so the sum runs over m <= r / NL; row r + 1 is read from LDS during step r.
+    constexpr int NM = C / NL;
     const int j = tid / NL, u = tid - j * NL;
-    float x[C / NL];
+    float x[NM], cur[NM], nxt[NM];
 #pragma unroll
-    for (int m = 0; m < C / NL; ++m) x[m] = 0.f;
+    for (int m = 0; m < NM; ++m) {
+      x[m] = 0.f;
+      cur[m] = sEkk[u + NL * m];
+      nxt[m] = 0.f;
+    }
 #pragma unroll
     for (int r = 0; r < C; ++r) {
+      if (r + 1 < C) {
+#pragma unroll
+        for (int m = 0; m <= (r + 1) / NL && m < NM; ++m) nxt[m] = sEkk[(r + 1) * SM + u + NL * m];
+      }
       float s = 0.f;
 #pragma unroll
-      for (int m = 0; m < C / NL; ++m) s = fmaf(sEkk[r * SM + u + NL * m], x[m], s);
-#pragma unroll
-      for (int o = 1; o < NL; o <<= 1) s += __shfl_xor(s, o, NL);
+      for (int m = 0; m <= r / NL; ++m) s = fmaf(cur[m], x[m], s);
+      s = group_sum<NL>(s);
       const float val = (r == j) ? 1.f : -sBeta[r] * s;
       if (u == (r % NL)) x[r / NL] = val;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) cur[m] = nxt[m];
     }
 #pragma unroll
     for (int m = 0; m < C / NL; ++m) sL[(u + NL * m) * SM + j] = x[m];
@@ -763,8 +795,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
       s = fmaf(t, sL[r * SM + i], s);
       sM3[r * SM + i] = t * sBeta[i];
     }
-#pragma unroll
-    for (int o = 1; o < NPC; o <<= 1) s += __shfl_xor(s, o, NPC);
+    s = group_sum<NPC>(s);
     if (u == 0) sDb[i] = s;
   }
   __syncthreads();
@@ -801,8 +832,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
       s = fmaf(da, sEkk[r * SM + i], s);
       sM3[r * SM + i] = sBeta[r] * da;
     }
-#pragma unroll
-    for (int o = 1; o < NPC; o <<= 1) s += __shfl_xor(s, o, NPC);
+    s = group_sum<NPC>(s);
     if (u == 0 && r < nr) stg<F32>(p.dbeta, row0 + (int64_t)r * H, sDb[r] + s);
   }
   for_units<C * C / 4, NTH>(tid, [&](int e) {  // 4 floats per access (records of grads are 256-byte aligned)
