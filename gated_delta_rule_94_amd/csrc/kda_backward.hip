@@ -266,7 +266,11 @@ __device__ __forceinline__ float group_sum(float s) {
 
 // Eight consecutive elements of an input tensor (element offset i, a multiple of 8) staged in LDS:
 // copy8 keeps the element type (bf16 bits or fp32 values unchanged), copy8f widens to fp32.  One
-// 16-byte global access per bf16 group (two for fp32); !ok stores zeros.
+// 16-byte global access per bf16 group (two for fp32); !ok stores zeros.  A select of a loaded
+// value on a per-thread condition is compiled into a branch around the load, which then waits on
+// its own; staging loops therefore copy every group unconditionally (rows past a sequence's end
+// read a valid row) and overwrite those rows with zero8 in a second pass taken only when the chunk
+// is short.
 template <bool F32>
 __device__ __forceinline__ void copy8(const void* src, int64_t i, void* dst, bool ok) {
   if constexpr (F32) {
@@ -294,6 +298,16 @@ __device__ __forceinline__ void copy8_head(const void* src, int64_t i, void* dst
     const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + i);
     auto m = [&](int e) -> uint32_t { return (keep > e ? 0x0000ffffu : 0u) | (keep > e + 1 ? 0xffff0000u : 0u); };
     *reinterpret_cast<uint4*>(dst) = make_uint4(w.x & m(0), w.y & m(2), w.z & m(4), w.w & m(6));
+  }
+}
+// zeros in place of a copy8 group
+template <bool F32>
+__device__ __forceinline__ void zero8(void* dst) {
+  if constexpr (F32) {
+    reinterpret_cast<float4*>(dst)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+    reinterpret_cast<float4*>(dst)[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(0u, 0u, 0u, 0u);
   }
 }
 template <bool F32>
@@ -457,28 +471,39 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
   const float* ds1 = p.dstates + (unit * p.nch + ch) * DK * DV;
   float* gr = p.grads + item * GL::FLOATS;
 
-  const bool has_s0 = s0 != nullptr;
-  const float4* s0v = reinterpret_cast<const float4*>(has_s0 ? s0 : ds1);  // loaded unconditionally, zeroed after
-  for_units<DK * DV / 4, NTH>(tid, [&](int e) {
-    const int c = (4 * e) / DV, j = 4 * e - c * DV;
-    const float4 a0 = s0v[e];
-    const float4 a = has_s0 ? a0 : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 d = reinterpret_cast<const float4*>(ds1)[e];
-    E* pa = sS0 + c * SV + j;
-    E* pd = sdS + c * SV + j;
-    pa[0] = (E)a.x; pa[1] = (E)a.y; pa[2] = (E)a.z; pa[3] = (E)a.w;
-    pd[0] = (E)d.x; pd[1] = (E)d.y; pd[2] = (E)d.z; pd[3] = (E)d.w;
-  });
+  // S0 (zeros without one) and dS1 to LDS; the branch on S0's presence is taken once for the
+  // workgroup, so no load sits under a per-element select
+  auto stage_states = [&](auto s0_present) {
+    for_units<DK * DV / 4, NTH>(tid, [&](int e) {
+      const int c = (4 * e) / DV, j = 4 * e - c * DV;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (decltype(s0_present)::value) a = reinterpret_cast<const float4*>(s0)[e];
+      const float4 d = reinterpret_cast<const float4*>(ds1)[e];
+      E* pa = sS0 + c * SV + j;
+      E* pd = sdS + c * SV + j;
+      pa[0] = (E)a.x; pa[1] = (E)a.y; pa[2] = (E)a.z; pa[3] = (E)a.w;
+      pd[0] = (E)d.x; pd[1] = (E)d.y; pd[2] = (E)d.z; pd[3] = (E)d.w;
+    });
+  };
+  if (s0)
+    stage_states(std::true_type{});
+  else
+    stage_states(std::false_type{});
   const int64_t orow = ((int64_t)b * p.T + (int64_t)ch * C) * H + h;
   for_units<C * DV / 8, NTH>(tid, [&](int e) {
     const int r = (8 * e) / DV, j = 8 * e - r * DV;
-    const bool ok = r < nr;
-    copy8<F32>(p.dO, (orow + (int64_t)(ok ? r : 0) * H) * DV + j, sdO + r * SV + j, ok);
+    copy8<F32>(p.dO, (orow + (int64_t)(r < nr ? r : 0) * H) * DV + j, sdO + r * SV + j, true);
   });
   for_units<C * DK / 8, NTH>(tid, [&](int e) {
     const int r = (8 * e) / DK, c = 8 * e - r * DK;
     copy8<F32>(rec, R::NW + 8 * e, sNW + r * SK + c, true);
   });
+  if (nr < C) {  // the same threads overwrite dO's rows past the end with zeros
+    for_units<C * DV / 8, NTH>(tid, [&](int e) {
+      const int r = (8 * e) / DV, j = 8 * e - r * DV;
+      if (r >= nr) zero8<F32>(sdO + r * SV + j);
+    });
+  }
   __syncthreads();
   // U = U~ + (-W) S0  (U~ from the record's U~^T)
   for (int t = wave; t < (C / 16) * (DV / 16); t += NTH / 64) {
@@ -661,15 +686,27 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     const int r = (8 * e) / DK, c = 8 * e - r * DK;
     const bool ok = r < nr;
     const int64_t gi = (row0 + (int64_t)(ok ? r : 0) * H) * DK + c;
-    copy8<F32>(p.q, gi, sQ + r * SK + c, ok);
-    copy8<F32>(p.k, gi, sK + r * SK + c, ok);
+    copy8<F32>(p.q, gi, sQ + r * SK + c, true);
+    copy8<F32>(p.k, gi, sK + r * SK + c, true);
     copy8f<F32>(p.g, gi, sG + r * SG + c, ok);
   });
   for_units<C * DV / 8, NTH>(tid, [&](int e) {
     const int r = (8 * e) / DV, j = 8 * e - r * DV;
-    const bool ok = r < nr;
-    copy8<F32>(p.v, (row0 + (int64_t)(ok ? r : 0) * H) * DV + j, sV + r * SV + j, ok);
+    copy8<F32>(p.v, (row0 + (int64_t)(r < nr ? r : 0) * H) * DV + j, sV + r * SV + j, true);
   });
+  if (nr < C) {  // the same threads overwrite the rows past the end with zeros
+    for_units<C * DK / 8, NTH>(tid, [&](int e) {
+      const int r = (8 * e) / DK, c = 8 * e - r * DK;
+      if (r >= nr) {
+        zero8<F32>(sQ + r * SK + c);
+        zero8<F32>(sK + r * SK + c);
+      }
+    });
+    for_units<C * DV / 8, NTH>(tid, [&](int e) {
+      const int r = (8 * e) / DV, j = 8 * e - r * DV;
+      if (r >= nr) zero8<F32>(sV + r * SV + j);
+    });
+  }
   if (tid < C) sBeta[tid] = tid < nr ? ldg<F32>(p.beta, row0 + (int64_t)tid * H) : 0.f;
   __syncthreads();
   scan_rows<DK, C, Cf::NPART, Cf::RPP, false>(sG, SG, sScan, tid);
