@@ -51,7 +51,7 @@ _lib.kda_version.argtypes = []
 _lib.kda_version.restype = _i32
 _lib.kda_chunked_forward_workspace_bytes.argtypes = [_i32] * 7
 _lib.kda_chunked_forward_workspace_bytes.restype = _sz
-_lib.kda_chunked_forward_plan.argtypes = [_i32] * 7 + [_vp] * 3
+_lib.kda_chunked_forward_plan.argtypes = [_i32] * 7 + [_vp] * 4
 _lib.kda_chunked_forward_plan.restype = _i32
 _lib.kda_chunked_forward_varlen_workspace_bytes.argtypes = [_i32] * 8
 _lib.kda_chunked_forward_varlen_workspace_bytes.restype = _sz
@@ -145,16 +145,25 @@ def workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:
     return int(_lib.kda_chunked_forward_workspace_bytes(B, T, H, dk, dv, chunk, _dtype_code(torch.empty(0, dtype=dtype))))
 
 
+def _plan(B, T, H, dk, dv, chunk, dtype):
+    out = (ctypes.c_int * 4)()
+    addr = ctypes.addressof(out)
+    st = _lib.kda_chunked_forward_plan(B, T, H, dk, dv, chunk, _dtype_code(torch.empty(0, dtype=dtype)),
+                                       addr, addr + 4, addr + 8, addr + 12)
+    if st != 0:
+        raise KDAError("kda_chunked_forward_plan", st)
+    return tuple(int(x) for x in out)
+
+
 def chain_plan(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16):
     """(value_slice, segments, segment_chunks): how kda_chunked_forward lays out its state chain on
     the current device for this shape."""
-    out = (ctypes.c_int * 3)()
-    addr = ctypes.addressof(out)
-    st = _lib.kda_chunked_forward_plan(B, T, H, dk, dv, chunk, _dtype_code(torch.empty(0, dtype=dtype)),
-                                       addr, addr + 4, addr + 8)
-    if st != 0:
-        raise KDAError("kda_chunked_forward_plan", st)
-    return int(out[0]), int(out[1]), int(out[2])
+    return _plan(B, T, H, dk, dv, chunk, dtype)[:3]
+
+
+def summary_slice(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16):
+    """State columns per workgroup of the segment summary pass for this shape (0: no segments)."""
+    return _plan(B, T, H, dk, dv, chunk, dtype)[3]
 
 
 def varlen_workspace_bytes(num_seqs, T_total, max_seqlen, H, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:

@@ -65,7 +65,7 @@ const char* kda_status_string(kda_status s) {
   return "unknown status";
 }
 
-int kda_version(void) { return 100; }
+int kda_version(void) { return 200; }
 
 size_t kda_chunked_forward_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt) {
   if (B <= 0 || T < 0 || H <= 0 || !chunk_ok(chunk) || (dt != KDA_F32 && dt != KDA_BF16)) return 0;
@@ -82,15 +82,16 @@ size_t kda_chunked_forward_varlen_workspace_bytes(int num_seqs, int T_total, int
 }
 
 kda_status kda_chunked_forward_plan(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt,
-                                    int* value_slice, int* segments, int* segment_chunks) {
+                                    int* value_slice, int* segments, int* segment_chunks, int* summary_slice) {
   if (B <= 0 || T < 0 || H <= 0 || chunk <= 0 || (dt != KDA_F32 && dt != KDA_BF16)) return KDA_ERR_INVALID_ARG;
   if (!dim_ok(d_k) || !dim_ok(d_v) || !chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
   if (!kda::chunked_forward_supported(dt == KDA_F32, d_k, d_v, chunk)) return KDA_ERR_UNSUPPORTED;
   if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
-  const kda::ChainPlan pl = kda::chain_plan(dt == KDA_F32, (int64_t)B * H, (T + chunk - 1) / chunk, d_v, false);
+  const kda::ChainPlan pl = kda::chain_plan(dt == KDA_F32, (int64_t)B * H, (T + chunk - 1) / chunk, d_k, d_v, false);
   if (value_slice) *value_slice = pl.ws;
   if (segments) *segments = pl.nseg;
   if (segment_chunks) *segment_chunks = pl.nseg > 1 ? pl.seg_len : 0;
+  if (summary_slice) *summary_slice = pl.nseg > 1 ? pl.sum_ws : 0;
   return KDA_OK;
 }
 

@@ -91,12 +91,13 @@ struct ChainLaunch {
   void* stream;
 };
 
-// How the chain is laid out over the GPU: value-slice width, and the segment split of long
-// sequences whose (sequence, head, slice) count alone would leave compute units idle.
+// How the chain is laid out over the GPU: value-slice width, the segment split of long sequences
+// whose (sequence, head, slice) count alone would leave compute units idle, and the column-slice
+// width of the segment summaries (0 when the plan has no segments).
 struct ChainPlan {
-  int ws, nseg, seg_len;
+  int ws, nseg, seg_len, sum_ws;
 };
-ChainPlan chain_plan(bool f32, int64_t units, int nch, int dv, bool varlen);
+ChainPlan chain_plan(bool f32, int64_t units, int nch, int dk, int dv, bool varlen);
 
 // Segment start states: sstart[u][0] = h0 (or 0), sstart[u][g + 1] = M_g sstart[u][g] + b_g
 // (kda_chain.hip)

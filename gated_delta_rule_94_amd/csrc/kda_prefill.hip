@@ -33,9 +33,9 @@ static int compute_units();
 // Segments: at least kMinSegChunks chunks each, at most kMaxSeg per (sequence, head).
 static constexpr int kMinSegChunks = 32, kMaxSeg = 64;
 
-ChainPlan chain_plan(bool f32, int64_t units, int nch, int dv, bool varlen) {
+ChainPlan chain_plan(bool f32, int64_t units, int nch, int dk, int dv, bool varlen) {
   const int cus = compute_units();
-  ChainPlan pl{16, 1, 0};
+  ChainPlan pl{16, 1, 0, 0};
   if (!f32 && units * (dv / 32) >= cus) pl.ws = 32;
   // Long sequences on few heads: (sequence, head, slice) alone leave CUs idle, so split every
   // sequence into segments.  That triples the chain's work (summaries over twice the columns, then
@@ -50,6 +50,11 @@ ChainPlan chain_plan(bool f32, int64_t units, int nch, int dv, bool varlen) {
       pl.ws = wss;
       pl.seg_len = (int)((nch + nseg - 1) / nseg);
       pl.nseg = (nch + pl.seg_len - 1) / pl.seg_len;
+      // the summary has d_k more columns than the chain; where its slices of wss columns would need
+      // more than one round of workgroups (one per CU: the record buffers fill the LDS), bf16
+      // summaries take 64-column slices, one round at twice the work per workgroup
+      pl.sum_ws = wss;
+      if (!f32 && units * (int64_t)(pl.nseg - 1) * ((dv + dk) / 32) > cus) pl.sum_ws = 64;
     }
   }
   return pl;
@@ -62,7 +67,7 @@ size_t chunked_forward_workspace(bool f32, int dk, int dv, int chunk, int64_t ma
   size_t bytes = (size_t)(max_chunks * H * rb);
   if (varlen) bytes += al256((size_t)(num_seqs + 1) * 4) + al256((size_t)num_seqs * 4);  // chunk map, order
   const int nch = (!varlen && num_seqs > 0) ? (int)(max_chunks / num_seqs) : 0;
-  const ChainPlan pl = chain_plan(f32, (int64_t)num_seqs * H, nch, dv, varlen);
+  const ChainPlan pl = chain_plan(f32, (int64_t)num_seqs * H, nch, dk, dv, varlen);
   if (pl.nseg > 1) {
     const size_t units = (size_t)num_seqs * H;
     bytes += al256(units * pl.nseg * dk * dv * 4) + al256(units * (pl.nseg - 1) * dk * (dv + dk) * 4);
@@ -123,7 +128,7 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
   K.records = records; K.h0 = a.h0; K.o = a.o; K.hT = a.hT; K.cu = a.cu_seqlens; K.chunk0 = chunk0; K.order = order;
   K.units = a.num_seqs * a.H; K.H = a.H; K.T = a.T; K.nch = nch;
   K.dk = a.dk; K.dv = a.dv; K.chunk = C; K.f32 = a.f32;
-  const ChainPlan pl = chain_plan(a.f32, K.units, nch, a.dv, varlen);
+  const ChainPlan pl = chain_plan(a.f32, K.units, nch, a.dk, a.dv, varlen);
   K.ws = pl.ws;
   K.stream = a.stream;
   K.states = a.states; K.every = a.state_every; K.max_states = a.max_states;
@@ -134,10 +139,7 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
     float* send = reinterpret_cast<float*>(seg + al256((size_t)K.units * pl.nseg * a.dk * a.dv * 4));
     K.nseg = pl.nseg; K.seg_len = pl.seg_len; K.sstart = sstart; K.send = send;
     K.summary = true;
-    // the summary has d_k more columns than the chain; where its 32-column slices would need more
-    // than one round of workgroups (one per CU: the record buffers fill the LDS), bf16 summaries
-    // take 64-column slices, one round at twice the work per workgroup
-    if (!a.f32 && K.units * (int64_t)(pl.nseg - 1) * ((a.dv + a.dk) / 32) > compute_units()) K.ws = 64;
+    K.ws = pl.sum_ws;
     if ((e = launch_chain(K)) != hipSuccess) return e;
     K.ws = pl.ws;
     if ((e = launch_segment_combine(a.h0, send, sstart, K.units, pl.nseg, a.dk, a.dv, a.stream)) != hipSuccess) return e;

@@ -79,14 +79,16 @@ size_t kda_chunked_forward_workspace_bytes(int B, int T, int H, int d_k, int d_v
  * this shape: *value_slice = value columns of the state per workgroup (16 or
  * 32); *segments = the number of segments every sequence is split into (1 =
  * none: the chain runs over whole sequences); *segment_chunks = chunks per
- * segment (0 when *segments is 1).  Sequences are split only when (sequence,
- * head, value slice) alone would leave compute units idle; the split costs a
- * summary pass and a combine but runs the chain on more workgroups.  Any
- * output pointer may be NULL.  The workspace size query accounts for the
- * plan, so query, plan and call must use the same device.
+ * segment (0 when *segments is 1); *summary_slice = state columns per
+ * workgroup of the segment summary pass (0 when *segments is 1).  Sequences
+ * are split only when (sequence, head, value slice) alone would leave compute
+ * units idle; the split costs a summary pass and a combine but runs the chain
+ * on more workgroups.  Any output pointer may be NULL.  The workspace size
+ * query accounts for the plan, so query, plan and call must use the same
+ * device.
  */
 kda_status kda_chunked_forward_plan(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt,
-                                    int* value_slice, int* segments, int* segment_chunks);
+                                    int* value_slice, int* segments, int* segment_chunks, int* summary_slice);
 
 /*
  * Optional steps fused on either side of the recurrence, for the *_fused entry

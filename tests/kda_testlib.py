@@ -54,3 +54,15 @@ def state_err(s_gpu, s_ref):
 
 def gpu_inputs(d):
     return {key: dev_tensor(val) for key, val in d.items()}
+
+
+def bf16_bits(x):
+    """fp64 / fp32 values -> bf16 bit patterns (uint16), rounded fp64 -> fp32 -> bf16, both to nearest
+    even, as the input generator rounds (finite values only)."""
+    f = np.ascontiguousarray(np.asarray(x, np.float64).astype(np.float32)).view(np.uint32)
+    return ((f + (((f >> 16) & 1) + 0x7FFF)) >> 16).astype(np.uint16)
+
+
+def stored(x, dt):
+    """fp64 values in the storage type of dtype code dt (fp32, or bf16 bit patterns)."""
+    return bf16_bits(x) if dt == datagen.DT_BF16 else np.ascontiguousarray(np.asarray(x, np.float64), np.float32)

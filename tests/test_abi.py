@@ -35,7 +35,7 @@ def test_status_strings_and_version():
     assert "invalid" in kda.kda_status_string(1)
     assert "unsupported" in kda.kda_status_string(2)
     assert kda.kda_status_string(99) == "unknown status"
-    assert kda.kda_version() >= 100
+    assert kda.kda_version() >= 200
 
 
 def test_workspace_queries():

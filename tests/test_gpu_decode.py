@@ -51,25 +51,29 @@ def test_decode_bf16_many_steps():
     assert eo < TOL[datagen.DT_BF16] and es < TOL[datagen.DT_BF16]
 
 
-def test_decode_full_size_sampled():
-    """The 256-sequence x 32-head workload (512 MiB state), three steps, checked on sampled units."""
+def test_decode_full_size_1000_steps_sampled():
+    """The 256-sequence x 32-head workload (512 MiB fp32 state) for all of its 1000 sequential
+    steps: o of 48 sampled (sequence, head) units against the oracle at every step, and their
+    states every 100 steps and at the end (the oracle carries only the sampled units' states)."""
     w = datagen.WORKLOADS["cfg3_decode_b256_h32_d128"]
     B, H, d = w.B, w.H, w.dk
     s0 = datagen.decode_state0(w.seed, B, H, d, d)
     st_gpu = dev_tensor(s0)
     units = np.random.default_rng(3).choice(B * H, size=48, replace=False)
     ub, uh = units // H, units % H
+    ub_d, uh_d = torch.from_numpy(ub).cuda(), torch.from_numpy(uh).cuda()
     st_ref = s0[ub, uh].astype(np.float64)[:, None]  # [n, 1, dk, dv]
-    for s in range(3):
+    worst_o = worst_s = 0.0
+    for s in range(w.steps):
         dd = datagen.decode_inputs(w.seed, s, B, H, d, d, w.dtype)
         o = kda.kda_decode_step(*(dev_tensor(dd[key]) for key in ("q", "k", "v", "g", "beta")), st_gpu)
         sub = {key: np.ascontiguousarray(dd[key][ub, uh][:, None]) for key in ("q", "k", "v", "g", "beta")}
         o_ref = oracle.decode_step(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], st_ref)
-        e = slice_err(host64(o)[ub, uh][:, None], o_ref, (0, 1))
-        assert e < TOL[w.dtype], e
-    es = state_err(host64(st_gpu)[ub, uh][:, None], st_ref)
-    print("decode full size sampled: state %.2e" % es)
-    assert es < TOL[w.dtype]
+        worst_o = max(worst_o, slice_err(host64(o[ub_d, uh_d])[:, None], o_ref, (0, 1)))
+        if (s + 1) % 100 == 0:
+            worst_s = max(worst_s, state_err(host64(st_gpu[ub_d, uh_d])[:, None], st_ref))
+            print("decode step %d: o %.2e state %.2e" % (s + 1, worst_o, worst_s), flush=True)
+    assert worst_o < TOL[w.dtype] and worst_s < TOL[w.dtype], (worst_o, worst_s)
 
 
 def test_decode_steps_equal_prefill():

@@ -1,0 +1,129 @@
+"""The method's edge cases on the HIP chunked prefill, element by element against the fp64 oracle and
+against their closed forms, for every chunk size, d in {64, 128}, fp32 and bf16 inputs:
+
+* the log-decay at its lower bound, g = -5 on every channel and token (technical-report page,
+  "Architecture at a glance": the scaled sigmoid bounds the log-decay below, which is what keeps the
+  16-row sub-tile factors of the intra-chunk products within [e^-80, e^80]); and half the channels
+  at -5, half at 0 (no decay), so that neighbouring channels differ by the full range;
+* the delta rule's exact overwrite: g = 0, beta = 1, one-hot keys with repeats and q = k, so every
+  token replaces the value stored under its key and reads it back: o_t = v_t, and each row of hT is
+  the last value written under that key, or the row of h0 (architecture blog, "Kimi Delta Attention:
+  the linear core": the delta rule removes what a key held before writing);
+* beta = 0: nothing is written, so the state only decays: with g = 0, hT = h0 and o_t = h0^T q_t;
+  with a decay, o_t = h0^T (e^{G_t} q_t) and hT = Diag(e^{G_T}) h0, G the running sum of g (g is
+  the workload's draw divided by 25, so that e^{G_T} stays within fp32's range over these lengths:
+  at the workload's g, h0 decays by about e^-150 over 60 tokens and hT underflows);
+* orthogonal (Hadamard) keys with g = 0 and h0 = 0: no write disturbs another, so
+  o_t = sum_{j <= t} beta_j (q_t . k_j) v_j, beta-weighted cumulative linear attention.
+
+Closed forms are evaluated in fp64 from the stored (rounded) inputs.  Bars: 1e-4 for fp32 inputs,
+2e-2 for bf16 inputs with the fp32 state, per (sequence, head) slice: max |x - y| / max |y|."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from tests.kda_testlib import TOL, dev_tensor, host64, o_err, state_err, stored
+
+pytestmark = pytest.mark.gpu
+kda = pytest.importorskip("gated_delta_rule_94_amd")
+
+F32, BF16 = datagen.DT_F32, datagen.DT_BF16
+KEYS = ("q", "k", "v", "g", "beta")
+CASES = ("g_min", "g_mixed", "overwrite", "frozen", "decay_only", "orthogonal")
+
+
+def hadamard(n):
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def make_case(case, dt, d, chunk):
+    """Stored inputs (dict as datagen.prefill_inputs) and the fp64 closed form (o, hT) or None."""
+    B, H = 2, 2
+    T = d - 3 if case == "orthogonal" else 3 * chunk + 11  # several chunks and a ragged tail
+    seed = 7000 + 100 * CASES.index(case) + d + chunk + 7 * dt
+    base = datagen.prefill_inputs(seed, B, T, H, d, d, dt, 0.02)
+    f = {key: datagen.to_f64(base[key]) for key in KEYS}
+    h0 = base["h0"].astype(np.float64)
+    rng = np.random.default_rng(seed)
+    closed = None
+    if case == "g_min":
+        f["g"] = np.full_like(f["g"], -5.0)
+    elif case == "g_mixed":
+        f["g"] = np.where(np.arange(d) % 2 == 0, -5.0, 0.0) * np.ones_like(f["g"])
+    elif case == "overwrite":
+        f["g"] = np.zeros_like(f["g"])
+        f["beta"] = np.ones_like(f["beta"])
+        keys = rng.integers(0, 12, size=(B, T, H))  # 12 keys over 3 chunks and more: many repeats
+        f["k"] = np.zeros_like(f["k"])
+        np.put_along_axis(f["k"], keys[..., None], 1.0, axis=-1)
+        f["q"] = f["k"].copy()
+    elif case == "frozen":
+        f["g"] = np.zeros_like(f["g"])
+        f["beta"] = np.zeros_like(f["beta"])
+    elif case == "decay_only":
+        f["beta"] = np.zeros_like(f["beta"])
+        f["g"] = f["g"] / 25.0
+    elif case == "orthogonal":
+        f["g"] = np.zeros_like(f["g"])
+        h0 = None
+        had = hadamard(d) / np.sqrt(d)
+        for b in range(B):
+            for h in range(H):
+                f["k"][b, :, h] = had[rng.permutation(d)[:T]]
+    d_st = {key: stored(f[key], dt) for key in KEYS}
+    d_st["h0"] = None if h0 is None else h0.astype(np.float32)
+    x = {key: datagen.to_f64(d_st[key]) for key in KEYS}  # what the kernels see
+    s0 = np.zeros((B, H, d, d)) if h0 is None else d_st["h0"].astype(np.float64)
+    if case == "overwrite":
+        o = x["v"].copy()
+        hT = s0.copy()
+        for b in range(B):
+            for h in range(H):
+                for t in range(T):
+                    hT[b, h, keys[b, t, h]] = x["v"][b, t, h]
+        closed = (o, hT)
+    elif case == "frozen":
+        closed = (np.einsum("bthc,bhcj->bthj", x["q"], s0), s0)
+    elif case == "decay_only":
+        G = np.cumsum(x["g"], axis=1)
+        closed = (np.einsum("bthc,bhcj->bthj", x["q"] * np.exp(G), s0), np.exp(G[:, -1])[..., None] * s0)
+    elif case == "orthogonal":
+        qk = np.einsum("bthc,bshc->bhts", x["q"], x["k"]) * np.tril(np.ones((T, T)))
+        o = np.einsum("bhts,bsh,bshj->bthj", qk, x["beta"], x["v"])
+        hT = np.einsum("bthc,bth,bthj->bhcj", x["k"], x["beta"], x["v"])
+        closed = (o, hT)
+    return d_st, closed
+
+
+@pytest.mark.parametrize("dt", [F32, BF16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("case", CASES)
+def test_edge_case(case, chunk, d, dt):
+    if dt == F32 and d == 128 and chunk == 64:
+        pytest.skip("fp32 inputs with d_k = 128 take chunks of at most 32 tokens")
+    ds, closed = make_case(case, dt, d, chunk)
+    g = {key: dev_tensor(ds[key]) for key in KEYS}
+    print("case %s chunk=%d d=%d dt=%d" % (case, chunk, d, dt), flush=True)
+    o, hT = kda.kda_chunked_forward(g["q"], g["k"], g["v"], g["g"], g["beta"], dev_tensor(ds["h0"]), chunk=chunk)
+    torch.cuda.synchronize()
+    og, hg = host64(o), host64(hT)
+    o_ref, h_ref = oracle.forward(ds["q"], ds["k"], ds["v"], ds["g"], ds["beta"], ds["h0"])
+    eo, eh = o_err(og, o_ref), state_err(hg, h_ref)
+    print("  against the oracle: o %.2e hT %.2e" % (eo, eh))
+    assert eo < TOL[dt] and eh < TOL[dt], (eo, eh)
+    if closed is not None:
+        co, ch = closed
+        # the oracle itself meets the closed form to fp64 rounding
+        assert o_err(o_ref, co) < 1e-12 and state_err(h_ref, ch) < 1e-12
+        ec, ehc = o_err(og, co), state_err(hg, ch)
+        print("  against the closed form: o %.2e hT %.2e" % (ec, ehc))
+        assert ec < TOL[dt] and ehc < TOL[dt], (ec, ehc)
+    if case == "frozen":
+        # nothing is written and nothing decays: the state passes through the chain unchanged
+        assert np.array_equal(hg, ds["h0"].astype(np.float64))

@@ -274,52 +274,6 @@ def test_workload_b1_h32_t65536_continuation():
     assert state_err(host64(h2), h_ref) < TOL[w.dtype]
 
 
-def test_workload_single_1m_sequence_sampled():
-    """One 1,048,576-token sequence x 8 heads: outputs of the first 32768 tokens against the oracle
-    (they depend on those tokens only), and the whole run against a call split in two."""
-    w = datagen.WORKLOADS["cfg4_bf16_b1_h8_t1048576_d128"]
-    d = datagen.prefill_inputs(w.seed, w.B, w.T, w.H, w.dk, w.dv, w.dtype, w.h0_std)
-    o, hT = gpu_forward(d, w.chunk)
-    P = 32768
-    pre = {key: np.ascontiguousarray(d[key][:, :P]) for key in KEYS}
-    o_ref, _ = oracle.forward(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], None, want_hT=False)
-    eo = o_err(host64(o[:, :P]), o_ref)
-    print("%s prefix: o %.2e" % (w.name, eo))
-    assert eo < TOL[w.dtype]
-    cut = 600_000 + 17  # not a chunk multiple
-    first = {key: np.ascontiguousarray(d[key][:, :cut]) for key in KEYS}
-    second = {key: np.ascontiguousarray(d[key][:, cut:]) for key in KEYS}
-    first["h0"] = second["h0"] = None
-    o1, h1 = gpu_forward(first, w.chunk)
-    o2, h2 = gpu_forward(second, w.chunk, h0=h1)
-    assert o_err(host64(o2), host64(o[:, cut:])) < TOL[w.dtype]
-    assert state_err(host64(h2), host64(hT)) < TOL[w.dtype]
-    assert np.isfinite(host64(hT)).all()
-
-
-def test_workload_varlen_16_sequences():
-    """16 packed sequences of seeded lengths in [1024, 131072], 8 heads: every output of the
-    four shortest sequences and the first 8192 tokens of every other against the oracle."""
-    w = datagen.WORKLOADS["cfg4v_varlen_n16_h8_d128"]
-    lens = datagen.varlen_lengths(w.seed, w.num_seqs, w.len_lo, w.len_hi)
-    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    Tt = int(cu[-1])
-    d = datagen.prefill_inputs(w.seed, 1, Tt, w.H, w.dk, w.dv, w.dtype, None)
-    g = {key: dev_tensor(d[key]) for key in KEYS}
-    o, hT = kda.kda_chunked_forward_varlen(g["q"], g["k"], g["v"], g["g"], g["beta"], dev_tensor(cu),
-                                           int(lens.max()), None, chunk=w.chunk)
-    torch.cuda.synchronize()
-    short = set(np.argsort(lens)[:4].tolist())
-    for n in range(w.num_seqs):
-        s = int(cu[n])
-        e = int(cu[n + 1]) if n in short else s + 8192
-        sub = {key: np.ascontiguousarray(d[key][:, s:e]) for key in KEYS}
-        o_ref, h_ref = oracle.forward(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], None)
-        assert o_err(host64(o[:, s:e]), o_ref) < TOL[w.dtype]
-        if n in short:
-            assert state_err(host64(hT[n:n + 1]), h_ref) < TOL[w.dtype]
-
-
 def test_short_sequences_precision():
     """Sequences of 1-4 tokens from a zero state: the output is P U alone, so the intra-chunk products
     carry the whole result, including slices where q . k nearly cancels."""

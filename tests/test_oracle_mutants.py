@@ -5,6 +5,8 @@ Mistakes planted: a sign flip in the delta correction, a dropped beta, a
 dropped or inverted decay, the gate read from the wrong channel, the write
 term subtracted, the read-out taken with the key instead of the query, the
 decay applied after the write, and the decayed state not used for the erase.
+For the sampled-unit forward (forward_units): b and h swapped in the unit id,
+the initial state taken by output slot instead of unit, a wrong output stride.
 """
 import os
 import subprocess
@@ -71,3 +73,29 @@ def test_mutant_is_caught(name, tmp_path, monkeypatch):
     print(name, "caught by", failed)
     # the decode-vs-prefill pin alone would not prove the recurrence wrong: require a pin of the math itself
     assert set(failed) - {"test_p12_decode_equals_prefill"}, "no pin caught the planted mistake %r" % name
+
+
+# Slips in the unit selection of forward_units (the sampled-unit oracle): each must fail its pin.
+UNIT_MUTANTS = {
+    "unit_b_h_swapped": ("int b = id / H, h = id % H;", "int h = id / B, b = id % B;"),
+    "unit_h0_of_slot": ("u->h0 = h0 ? h0 + (size_t)id * dk * dv : NULL;",
+                        "u->h0 = h0 ? h0 + (size_t)i * dk * dv : NULL;"),
+    "unit_o_stride": ("u->o = o ? o + (size_t)i * (size_t)T * dv : NULL;", "u->o = o ? o + (size_t)i * dv : NULL;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(UNIT_MUTANTS))
+def test_unit_mutant_is_caught(name, tmp_path, monkeypatch):
+    old, new = UNIT_MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) == 1, "mutation anchor not found: %s" % name
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", str(src), "-o", str(so), "-lm"])
+    monkeypatch.setattr(oracle, "_LIB_PATH", str(so))
+    monkeypatch.setattr(oracle, "_SRC", str(src))
+    monkeypatch.setattr(oracle, "_lib", None)
+    with pytest.raises(AssertionError):
+        pins.test_forward_units_equals_batched_slices()
+    monkeypatch.setattr(oracle, "_lib", None)

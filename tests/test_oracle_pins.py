@@ -453,3 +453,32 @@ def test_bf16_inputs_decode_exactly():
     o1, h1 = run(d32)
     o2, h2 = run(dd)
     assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
+
+
+# --------------------------------------------------------------------------------------------
+# forward_units: the batched forward restricted to chosen (b, h) units, unit id = b * H + h.  Every
+# unit runs the same token-by-token code as forward(), so a selected unit's o and hT must equal the
+# batched call's slice bit for bit; a slip in the unit index (b and h swapped, id taken as h * B + b)
+# or in the output stride fails this, because every unit sees different inputs and a different h0.
+
+
+def test_forward_units_equals_batched_slices():
+    B, T, H, dk, dv = 3, 37, 5, 16, 8
+    d = inputs(171, B, T, H, dk, dv)
+    o, hT = run(d)
+    ids = [14, 0, 7, 7, 3, 11, 5]  # permuted, repeated, first and last unit, b and h both vary
+    ou, hu = oracle.forward_units(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], ids)
+    assert ou.shape == (len(ids), T, dv) and hu.shape == (len(ids), dk, dv)
+    for i, uid in enumerate(ids):
+        b, h = divmod(uid, H)
+        assert np.array_equal(ou[i], o[b, :, h]), uid
+        assert np.array_equal(hu[i], hT[b, h]), uid
+    # without h0, and with only one of the outputs wanted
+    o0, h00 = run(d, h0=None)
+    _, hu0 = oracle.forward_units(d["q"], d["k"], d["v"], d["g"], d["beta"], None, ids, want_o=False)
+    ou0, _ = oracle.forward_units(d["q"], d["k"], d["v"], d["g"], d["beta"], None, ids, want_hT=False)
+    for i, uid in enumerate(ids):
+        b, h = divmod(uid, H)
+        assert np.array_equal(hu0[i], h00[b, h]) and np.array_equal(ou0[i], o0[b, :, h])
+    with pytest.raises(RuntimeError):
+        oracle.forward_units(d["q"], d["k"], d["v"], d["g"], d["beta"], None, [B * H])
