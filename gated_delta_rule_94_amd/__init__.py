@@ -38,7 +38,11 @@ EXPORTS = (
     "kda_chunked_forward_fused", "kda_decode_step_fused", "kda_chunked_forward_ex", "kda_chunked_forward_varlen_ex",
     "kda_chunked_forward_profiled", "kda_chunked_forward_varlen", "kda_chunked_forward_varlen_workspace_bytes",
     "kda_decode_step", "kda_chunked_backward", "kda_chunked_backward_workspace_bytes", "kda_chunked_forward_mxfp8",
+    "kda_chunked_forward_noalloc",
 )
+
+# bytes of the library's fixed device scratch used by kda_chunked_forward_noalloc (KDA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libkda.so is not built (%s): run `python gated_delta_rule_94_amd/build.py`" % LIB_PATH)
@@ -57,6 +61,8 @@ _lib.kda_chunked_forward_varlen_workspace_bytes.argtypes = [_i32] * 8
 _lib.kda_chunked_forward_varlen_workspace_bytes.restype = _sz
 _lib.kda_chunked_forward.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp, _sz, _vp]
 _lib.kda_chunked_forward.restype = _i32
+_lib.kda_chunked_forward_noalloc.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp]
+_lib.kda_chunked_forward_noalloc.restype = _i32
 _lib.kda_chunked_forward_with_states.argtypes = [_vp] * 9 + [_i32] * 8 + [_vp, _sz, _vp]
 _lib.kda_chunked_forward_with_states.restype = _i32
 _lib.kda_chunked_forward_varlen_with_states.argtypes = [_vp] * 9 + [_i32, _vp] + [_i32] * 8 + [_vp, _sz, _vp]
@@ -210,6 +216,31 @@ def kda_chunked_forward(q, k, v, g, beta, h0=None, *, chunk: int = 64, o=None, h
                                   B, T, H, dk, dv, chunk, _dtype_code(q), _ptr(ws), _nbytes(ws), _stream(stream))
     if st:
         raise KDAError("kda_chunked_forward", st)
+    return o, hT
+
+
+def kda_chunked_forward_noalloc(q, k, v, g, beta, h0=None, *, chunk: int = 64, o=None, hT=None, want_hT: bool = True,
+                                stream=None):
+    """kda_chunked_forward with no workspace: the library's fixed device scratch (NOALLOC_SCRATCH_BYTES,
+    one per GPU) holds the per-chunk records, and the C call allocates nothing.  Pass o (and hT) to
+    make the whole call allocation-free; calls that overlap on one GPU race on the scratch."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("g", g, (B, T, H, dk)),
+                         ("v", v, (B, T, H, dv)), ("beta", beta, (B, T, H))):
+        _check(name, t, shp, dt, dev)
+    _check("h0", h0, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check("o", o, (B, T, H, dv), dt, dev)
+    if hT is None and want_hT:
+        hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check("hT", hT, (B, H, dk, dv), torch.float32, dev)
+    st = _lib.kda_chunked_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
+                                          B, T, H, dk, dv, chunk, _dtype_code(q), _stream(stream))
+    if st:
+        raise KDAError("kda_chunked_forward_noalloc", st)
     return o, hT
 
 

@@ -2,10 +2,36 @@
 // Declarations and the contract of every entry point are in include/kda.h.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/kda.h"
 #include "kda_internal.h"
 
+// Fixed device scratch of kda_chunked_forward_noalloc: the per-chunk records and segment states that
+// kda_chunked_forward keeps in the caller's workspace.  One copy lives on every GPU the library runs
+// on, from the library's first use there until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is looked up once per device
+// (scratch_address) and only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch` on each device (NULL: not looked up yet)
+
+// Device address of `scratch` on the current device, or NULL if the runtime cannot give it.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool dim_ok(int d) { return d == 64 || d == 128; }
@@ -105,10 +131,12 @@ bool workspace_ok(void* ws, size_t have, size_t need) {
 }  // extern "C"
 
 namespace {
+// noalloc: the fixed device scratch stands in for the caller's workspace (workspace is ignored).
 kda_status chunked_forward_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
                                 const float* h0, void* o, float* hT, float* states, int state_every,
                                 const kda_fusion* fusion, int B, int T, int H, int d_k, int d_v, int chunk,
-                                kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
+                                kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream,
+                                bool noalloc = false) {
   if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
   if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
   kda::Fusion fu;
@@ -119,8 +147,17 @@ kda_status chunked_forward_impl(const void* q, const void* k, const void* v, con
   if (states && !states_ok(states, state_every, chunk)) return KDA_ERR_INVALID_ARG;
   if (B == 0) return KDA_OK;
   if (T == 0 && !hT) return KDA_OK;
-  if (!workspace_ok(workspace, workspace_bytes, kda_chunked_forward_workspace_bytes(B, T, H, d_k, d_v, chunk, dt)))
-    return KDA_ERR_WORKSPACE;
+  const size_t need = kda_chunked_forward_workspace_bytes(B, T, H, d_k, d_v, chunk, dt);
+  if (noalloc) {
+    if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      if (!(workspace = scratch_address())) return KDA_ERR_HIP;
+      workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+    }
+  }
+  if (!workspace_ok(workspace, workspace_bytes, need)) return KDA_ERR_WORKSPACE;
   kda::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g_eff; a.beta = beta;
   a.h0 = h0; a.o = o; a.hT = hT;
@@ -173,6 +210,13 @@ kda_status kda_chunked_forward(const void* q, const void* k, const void* v, cons
                                kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
   return kda_chunked_forward_with_states(q, k, v, g, beta, h0, o, hT, nullptr, 0, B, T, H, d_k, d_v, chunk, dt,
                                          workspace, workspace_bytes, hip_stream);
+}
+
+kda_status kda_chunked_forward_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                       const float* h0, void* o, float* hT, int B, int T, int H, int d_k, int d_v,
+                                       int chunk, kda_dtype dt, void* hip_stream) {
+  return chunked_forward_impl(q, k, v, g, beta, h0, o, hT, nullptr, 0, nullptr, B, T, H, d_k, d_v, chunk, dt, nullptr,
+                              0, hip_stream, true);
 }
 
 kda_status kda_chunked_forward_profiled(const void* q, const void* k, const void* v, const void* g, const void* beta,

@@ -128,6 +128,29 @@ kda_status kda_chunked_forward(const void* q, const void* k, const void* v, cons
                                kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * kda_chunked_forward for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, layouts, results and errors as
+ * kda_chunked_forward, without the workspace: the scratch it needs (the
+ * per-chunk records and segment states; kda_chunked_forward_workspace_bytes
+ * gives its size) lives in a fixed device buffer of KDA_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per GPU, held from the first use of the library on
+ * that GPU until the process ends.  The call allocates nothing.
+ *   KDA_ERR_WORKSPACE: the shape needs more than KDA_NOALLOC_SCRATCH_BYTES of
+ *   scratch (use kda_chunked_forward with a workspace, or split the call).
+ *   KDA_ERR_HIP also if the runtime cannot give the buffer's device address.
+ * Every call on one GPU uses that GPU's single buffer: calls on one stream are
+ * ordered, but calls whose executions overlap on one GPU (different streams,
+ * host threads) race on it and give unspecified results.  The kernels write
+ * every scratch byte they read before reading it, so the contents a previous
+ * call left behind are never used and nothing is cleared.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_chunked_forward_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                       const float* h0, void* o, float* hT, int B, int T, int H, int d_k, int d_v,
+                                       int chunk, kda_dtype dt, void* hip_stream);
+
+/*
  * kda_chunked_forward that also keeps the recurrent state at fixed token
  * intervals: the prefix states a serving cache stores so that a repeated
  * prompt resumes from the state instead of being prefilled again (a recurrent

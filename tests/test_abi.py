@@ -106,6 +106,28 @@ def test_prefill_validation():
     assert fwd(B=0, ptr=None, ws=None, ws_bytes=0) == OK
 
 
+def fna(B=1, T=64, H=2, dk=64, dv=64, chunk=64, dt=1, ptr=FAKE, h0=None, hT=None):
+    return kda.lib().kda_chunked_forward_noalloc(ptr, ptr, ptr, ptr, ptr, h0, ptr, hT, B, T, H, dk, dv, chunk, dt, None)
+
+
+def test_noalloc_validation():
+    """The no-allocation prefill checks its arguments as kda_chunked_forward does, and refuses, before
+    anything runs, a shape whose scratch exceeds the library's fixed buffer."""
+    assert fna(ptr=None) == INVALID
+    assert fna(ptr=FAKE + 4) == INVALID
+    assert fna(B=-1) == INVALID
+    assert fna(dk=96) == UNSUPPORTED
+    assert fna(chunk=48) == UNSUPPORTED
+    assert fna(h0=FAKE + 8) == INVALID
+    assert fna(B=0, ptr=None) == OK
+    big = kda.lib().kda_chunked_forward_workspace_bytes(4, 4096, 16, 128, 128, 64, 1)
+    assert big > kda.NOALLOC_SCRATCH_BYTES
+    assert fna(B=4, T=4096, H=16, dk=128, dv=128) == 3
+    header = open(os.path.join(ROOT, "include", "kda.h")).read()
+    assert "#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in header
+    assert kda.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
 def fmx(B=1, T=64, H=2, dk=64, dv=64, chunk=64, ptr=FAKE, scale=FAKE + 1, h0=None, hT=None, ws=FAKE, ws_bytes=1 << 40):
     return kda.lib().kda_chunked_forward_mxfp8(ptr, scale, ptr, scale, ptr, scale, ptr, ptr, h0, ptr, hT, B, T, H, dk,
                                                dv, chunk, ws, ws_bytes, None)
