@@ -3,47 +3,47 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-A step is one kda_chunked_forward call over the 4-sequence x 16-head x
-4096-token bf16 workload (fp32 state, random h0, chunk 64).  The call runs two
-kernels on the caller's stream: the intra-chunk kernel (gate cumsum, UT/WY
-transform and the chunk-local products of every (chunk, head), in parallel, to
-a workspace of per-chunk records) and the chain kernel (the sequential state
-recurrence and the outputs).  Inputs are resident in HBM before the timed
-region, and a 512 MiB write evicts the 256 MB Infinity Cache just before it;
-the timed region is exactly K back-to-back steps between two HIP events on the
-launch stream, bracketed by synchronisation (ms_per_step = event time / K; one
-step moves about 1 GB, so no step finds the previous one's inputs cached).
-cold_steps repeats the steps one at a time with the cache evicted before each.
-A pass through kda_chunked_forward_profiled, cache evicted before each call,
-gives each kernel's mean duration from events recorded between the kernels.
+A step is one kda_chunked_forward call over the largest single-GPU prefill
+workload: one sequence of 1,048,576 tokens x 8 heads, bf16 q/k/v/g/beta,
+d_k = d_v = 128, chunk 64, fp32 state from zero.  The call runs, on the
+caller's stream, the intra-chunk kernel (gate cumsum, UT/WY transform and the
+chunk-local products of every (chunk, head), in parallel, into per-chunk
+records) and the state chain (for this shape: a summary pass over 8 segments
+per head, the fp32 combine of segment start states, then the chain of every
+segment, writing o and hT).  Inputs are resident in HBM before the timed
+region; the timed region is exactly K back-to-back steps between two HIP events
+on the launch stream, bracketed by synchronisation (ms_per_step = event time /
+K; a step moves tens of GB, far beyond the 256 MB Infinity Cache).  A pass
+through kda_chunked_forward_profiled gives the two stages' durations.
 
 The JSON line carries:
-  roofline       -- the dominant kernel (intra-chunk) against HBM, its binding
-                    roof: achieved = its algorithmic bytes per launch (inputs
-                    read + records written) / its mean duration
-  roofline_chain -- the chain kernel likewise (records read once, h0, hT, o)
-  roofline_mfma  -- the whole call's algorithmic flops against dense bf16 MFMA
-                    (the headline metric's "% of MFMA peak")
-  roofline_call_hbm -- the whole call's algorithmic bytes (inputs, o, h0, hT)
-  states         -- the same call through kda_chunked_forward_with_states, keeping
-                    the state every 1024 tokens (prefix states for a serving cache)
-  fused          -- the same workload through kda_chunked_forward_fused: gate from
-                    its pre-activation, q and k normalised, output gate
-  mxfp8          -- the same workload with q, k and v in MXFP8 (E4M3 codes, one E8M0
-                    scale per 32 channels) through kda_chunked_forward_mxfp8
+  roofline       -- the whole call against HBM, its binding roof: achieved = the
+                    call's algorithmic bytes (q, k, v, g, beta in, o out: 1,282 B
+                    per token-head at bf16, d = 128; plus the hT write) / ms_per_step;
+                    traffic = the call's HBM bytes from the rocprofv3 FETCH_SIZE /
+                    WRITE_SIZE counters (summed over its kernels, scaled by a plain
+                    copy's reading; profiles/hbm_traffic.json), null unless taken on
+                    the current kernel sources; traffic_ratio = traffic / algorithmic
+  roofline_mfma  -- the call's algorithmic flops against dense bf16 MFMA (the
+                    headline metric's "% of MFMA peak")
+  stages         -- intra-chunk kernel and state-chain durations (profiled entry point)
+  workloads      -- the other seeded prefill workloads (fp32 2 x 256 tokens; 4 x 16
+                    heads x 4096 tokens; 32 heads x 65,536 tokens; 16 packed
+                    sequences), each timed over a few calls with the cache evicted
+                    before each: tokens/s, the chain layout, the two stages'
+                    durations, and the call's algorithmic bytes / flops against
+                    HBM / MFMA
+  states, fused, mxfp8, backward -- on the 4 x 16 x 4096 workload: the call keeping
+                    the state every 1024 tokens; the fused gate / q-k norm / output
+                    gate; MXFP8 q, k, v; the backward (training) call
   decode         -- 1000 sequential kda_decode_step calls on the 256-sequence x
                     32-head state (512 MiB fp32), bytes and fraction of HBM
-  workloads      -- the other seeded prefill workloads (fp32 2 x 256 tokens, 32
-                    heads x 65,536 tokens, one 1,048,576-token sequence x 8 heads,
-                    16 packed sequences), each timed over a few calls with the
-                    cache evicted before each: tokens/s, the chain's layout (value
-                    slice, segments), the two stages' durations, and the whole
-                    call's algorithmic bytes and (bf16) flops against HBM and MFMA
-  cpu_baseline   -- the fp64 oracle on this host's cores, whole passes over the
-                    same workload for at least 10 s (a baseline, not a target)
+  cpu_baseline   -- the fp64 oracle on this host's cores, whole passes over the first
+                    65,536 tokens x 8 heads of the headline workload for at least 10 s
+                    (a baseline, not a target); cores = the threads it used
 Algorithmic work per token and head (d_k = d_v = d, chunk C):
   flops 6 d^2 + (C-1) d + 2 (C+1) d + 2 (C+1) d + C^2/3 ; bytes (3 d_k + d_v) s_in + s_beta + d_v s_out,
-  plus 2 * 4 d_k d_v per (sequence, head) for h0 and hT.
+  plus 4 d_k d_v per (sequence, head) for each of h0 (when given) and hT.
 """
 import argparse
 import hashlib
@@ -58,13 +58,14 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2516.6  # MI355X dense bf16 MFMA
 CSRC = os.path.join(ROOT, "gated_delta_rule_94_amd", "csrc")
-# the sources each kernel is built from (a counter reading is valid for these exact sources only)
+# the sources each measured launch group is built from (a counter reading is valid for these exact
+# sources only)
 KERNEL_SOURCES = {
-    "intra": ("kda_intra.hip", "kda_device.h", "kda_record.h"),
-    "chain": ("kda_chain.hip", "kda_device.h", "kda_record.h"),
+    "prefill": ("kda_intra.hip", "kda_chain.hip", "kda_prefill.hip", "kda_device.h", "kda_record.h", "kda_internal.h"),
     "decode": ("kda_decode.hip", "kda_device.h"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+HEADLINE = "cfg4_bf16_b1_h8_t1048576_d128"
 
 
 def prefill_flops_per_token_head(dk, dv, C):
@@ -99,16 +100,17 @@ def sources_sha256(kernel_key):
     return h.hexdigest()
 
 
-def measured_traffic(kernel_key):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if taken on these sources."""
+def measured_traffic(entry, kernel_key):
+    """HBM bytes per call from the committed rocprofv3 counter summary (entry: a workload name or
+    "decode"), if taken on the current sources of kernel_key."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)[kernel_key]
+            t = json.load(f)[entry]
     except (OSError, KeyError, ValueError):
         return None
     if t.get("source_sha256") != sources_sha256(kernel_key):
         return None
-    return t["bytes_per_launch"]
+    return t["bytes_per_call"]
 
 
 def world_size():
@@ -191,28 +193,69 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    # ---------------- prefill (headline)
-    w = datagen.WORKLOADS["cfg1_bf16_b4_h16_t4096_d128"]
-    d = datagen.prefill_inputs(w.seed, w.B, w.T, w.H, w.dk, w.dv, w.dtype, w.h0_std)
-    g = {key: to_dev(val) for key, val in d.items()}
-    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16, device=dev)
-    hT = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
     scratch = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-
-    def step(_i):
-        kda.kda_chunked_forward(g["q"], g["k"], g["v"], g["g"], g["beta"], g["h0"], chunk=w.chunk, o=o, hT=hT)
 
     def flush():
         scratch.fill_(1)
 
+    def prefill_case(wl):
+        """Device inputs, outputs and workspace of a seeded prefill workload, and its call."""
+        tdt = torch.float32 if wl.dtype == datagen.DT_F32 else torch.bfloat16
+        c = {"wl": wl, "tdt": tdt, "s_io": 4 if tdt == torch.float32 else 2}
+        if wl.kind == "varlen":
+            lens = datagen.varlen_lengths(wl.seed, wl.num_seqs, wl.len_lo, wl.len_hi)
+            cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+            dl = datagen.prefill_inputs(wl.seed, 1, int(cu[-1]), wl.H, wl.dk, wl.dv, wl.dtype, None)
+            c.update(n_tok=int(cu[-1]), n_seq=wl.num_seqs, maxlen=int(lens.max()), cu=to_dev(cu), with_h0=False)
+        else:
+            dl = datagen.prefill_inputs(wl.seed, wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.dtype, wl.h0_std)
+            c.update(n_tok=wl.B * wl.T, n_seq=wl.B, with_h0=wl.h0_std is not None)
+        c["host"] = dl
+        c["g"] = {key: to_dev(val) for key, val in dl.items()}
+        c["o"] = torch.empty(c["g"]["v"].shape, dtype=tdt, device=dev)
+        c["hT"] = torch.empty((c["n_seq"], wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+        gg = c["g"]
+        if wl.kind == "varlen":
+            c["ws"] = torch.empty(kda.varlen_workspace_bytes(wl.num_seqs, c["n_tok"], c["maxlen"], wl.H, wl.dk, wl.dv,
+                                                             wl.chunk, tdt), dtype=torch.uint8, device=dev)
+
+            def call(_i):
+                kda.kda_chunked_forward_varlen(gg["q"], gg["k"], gg["v"], gg["g"], gg["beta"], c["cu"], c["maxlen"],
+                                               None, chunk=wl.chunk, o=c["o"], hT=c["hT"], workspace=c["ws"])
+        else:
+            c["ws"] = torch.empty(kda.workspace_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.chunk, tdt),
+                                  dtype=torch.uint8, device=dev)
+
+            def call(_i):
+                kda.kda_chunked_forward(gg["q"], gg["k"], gg["v"], gg["g"], gg["beta"], gg["h0"], chunk=wl.chunk,
+                                        o=c["o"], hT=c["hT"], workspace=c["ws"])
+        c["call"] = call
+        c["alg_bytes"] = prefill_bytes(1, c["n_tok"], wl.H, wl.dk, wl.dv, c["s_io"], c["s_io"], with_h0=False,
+                                       with_hT=False) + c["n_seq"] * wl.H * 4 * wl.dk * wl.dv * (int(c["with_h0"]) + 1)
+        c["alg_flops"] = c["n_tok"] * wl.H * prefill_flops_per_token_head(wl.dk, wl.dv, wl.chunk)
+        return c
+
+    def stages(c):
+        """(intra-chunk kernel ms, state chain ms) of one call, cache evicted before it."""
+        wl, gg = c["wl"], c["g"]
+        if not args.no_flush:
+            flush()
+        return kda.kda_chunked_forward_profiled(gg["q"], gg["k"], gg["v"], gg["g"], gg["beta"], gg["h0"], c["o"],
+                                                c["hT"], chunk=wl.chunk, workspace=c["ws"])
+
+    def plan_of(wl, tdt):
+        vs, nseg, segc = kda.chain_plan(wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.chunk, tdt)
+        return {"value_slice": vs, "segments": nseg, "segment_chunks": segc,
+                "summary_slice": kda.summary_slice(wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.chunk, tdt)}
+
+    # ---------------- prefill (headline): one 1,048,576-token sequence x 8 heads
+    w = datagen.WORKLOADS[HEADLINE]
+    hc = prefill_case(w)
+    step = hc["call"]
     for _ in range(args.warmup):
         step(0)
     torch.cuda.synchronize()
-    # the timed region: exactly K back-to-back steps, bracketed by synchronisation, after one write
-    # of 512 MiB has evicted the Infinity Cache (one step moves about 1 GB, more than the cache holds)
-    if not args.no_flush:
-        flush()
-    torch.cuda.synchronize()
+    # the timed region: exactly K back-to-back steps, bracketed by synchronisation
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     ev0.record()
@@ -222,34 +265,19 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms = ev0.elapsed_time(ev1) / args.steps
-    # the same steps one at a time with the cache evicted before each (each step timed alone)
-    ms_cold, _ = time_launches(step, args.steps, None if args.no_flush else flush)
+    # the two stages of the call, through the profiling entry point
+    st_ms = [0.0, 0.0]
+    n_prof = max(1, min(args.steps, 5))
+    for _ in range(n_prof):
+        a_ms, b_ms = stages(hc)
+        st_ms[0] += a_ms / n_prof
+        st_ms[1] += b_ms / n_prof
 
-    # per-kernel durations: the same steps through the profiling entry point
-    k_ms = [0.0, 0.0]
-    for _ in range(args.steps):
-        if not args.no_flush:
-            flush()
-        a_ms, b_ms = kda.kda_chunked_forward_profiled(g["q"], g["k"], g["v"], g["g"], g["beta"], g["h0"], o, hT,
-                                                      chunk=w.chunk)
-        k_ms[0] += a_ms / args.steps
-        k_ms[1] += b_ms / args.steps
-
-    s_in = 2
-    tokens = w.B * w.T
-    n_in = w.B * w.T * w.H * ((3 * w.dk + w.dv) * s_in + s_in)  # q, k, g, v, beta
-    n_out = w.B * w.T * w.H * w.dv * s_in
-    n_state = w.B * w.H * w.dk * w.dv * 4
-    rec_bytes = kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.chunk, torch.bfloat16)  # the per-chunk records
-    intra_bytes = n_in + rec_bytes
-    chain_bytes = rec_bytes + 2 * n_state + n_out
-    alg_bytes = prefill_bytes(w.B, w.T, w.H, w.dk, w.dv, s_in, s_in)
-    alg_flops = w.B * w.T * w.H * prefill_flops_per_token_head(w.dk, w.dv, w.chunk)
-    gbs_intra = intra_bytes / (k_ms[0] * 1e-3) / 1e9
-    gbs_chain = chain_bytes / (k_ms[1] * 1e-3) / 1e9
+    tokens = hc["n_tok"]
+    alg_bytes, alg_flops = hc["alg_bytes"], hc["alg_flops"]
     gbs = alg_bytes / (ms * 1e-3) / 1e9
     tfs = alg_flops / (ms * 1e-3) / 1e12
-
+    traffic = measured_traffic(HEADLINE, "prefill")
     out = {
         "metric": "KDA prefill tokens/s (% bf16 MFMA peak); decode GB/s (% HBM peak)",
         "value": tokens / (ms * 1e-3),
@@ -264,26 +292,39 @@ def main():
         "dtype": "bf16",
         "data": "synthetic: seeded SplitMix64/Box-Muller inputs with the workload's distributions",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d_k": w.dk, "d_v": w.dv, "chunk": w.chunk,
-                   "state": "fp32", "h0": "N(0, 0.02)", "tokens_per_step": tokens,
-                   "timing": "K back-to-back steps between two HIP events, cache evicted once before"},
-        "roofline": {"bound": "hbm", "achieved": gbs_intra, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs_intra / HBM_PEAK_GBS, "traffic": measured_traffic("intra"),
-                     "kernel": "kda::intra_chunk_kernel<false, 128, 128, 64, false>", "ms_per_launch": k_ms[0],
-                     "alg_bytes_per_launch": intra_bytes},
-        "roofline_chain": {"bound": "hbm", "achieved": gbs_chain, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": gbs_chain / HBM_PEAK_GBS, "traffic": measured_traffic("chain"),
-                           "kernel": "kda::chain_kernel<false, 128, 128, 64, 32, false>", "ms_per_launch": k_ms[1],
-                           "alg_bytes_per_launch": chain_bytes},
+                   "state": "fp32", "h0": "zero", "tokens_per_step": tokens,
+                   "chain_plan": plan_of(w, hc["tdt"]),
+                   "timing": "K back-to-back steps between two HIP events on the launch stream"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_ratio": None if traffic is None else traffic / alg_bytes,
+                     "scope": "whole call (intra-chunk kernel, segment summaries, combine, chain)",
+                     "alg_bytes_per_call": alg_bytes, "ms_per_call": ms},
         "roofline_mfma": {"achieved": tfs, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                          "frac": tfs / MFMA_BF16_PEAK_TFS, "alg_flops_per_launch": alg_flops, "scope": "whole call"},
-        "roofline_call_hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                              "alg_bytes_per_launch": alg_bytes, "scope": "whole call"},
+                          "frac": tfs / MFMA_BF16_PEAK_TFS, "alg_flops_per_call": alg_flops, "scope": "whole call"},
+        "stages": {"intra_ms": st_ms[0], "chain_ms": st_ms[1],
+                   "note": "mean of %d calls through kda_chunked_forward_profiled (events between the stages)"
+                           % n_prof},
         "wall_s_timed_region": wall,
         "ms_per_step_wall": 1e3 * wall / args.steps,
-        "cold_steps": {"ms_per_step": ms_cold, "tokens_per_s": tokens / (ms_cold * 1e-3),
-                       "note": "each step timed alone by HIP events, the Infinity Cache evicted before it"},
     }
+    cpu_sample = {key: np.ascontiguousarray(hc["host"][key][:, :65536]) for key in ("q", "k", "v", "g", "beta")}
+    del hc, step
+    torch.cuda.empty_cache()
 
+    # ---------------- the 4 x 16 x 4096 workload: its own line in `workloads`, and the legs below
+    # (skipped when none of them runs, so that a profile of the headline holds the headline only)
+    if args.no_workloads and args.no_states and args.no_fused and args.no_mxfp8 and args.no_backward:
+        args.no_states = args.no_fused = args.no_mxfp8 = args.no_backward = True
+        c1 = None
+    else:
+        w = datagen.WORKLOADS["cfg1_bf16_b4_h16_t4096_d128"]
+        c1 = prefill_case(w)
+        g, o, hT = c1["g"], c1["o"], c1["hT"]
+        tokens = c1["n_tok"]
+        c1["call"](0)
+        torch.cuda.synchronize()
+        ms, _ = time_launches(c1["call"], args.steps, None if args.no_flush else flush)
     # ---------------- the same call keeping the state every 1024 tokens (prefix states for a cache)
     if not args.no_states:
         every = 1024
@@ -389,93 +430,67 @@ def main():
             "workload": wd.name, "steps": args.decode_steps, "us_per_step": dms * 1e3,
             "tokens_per_s": wd.B / (dms * 1e-3), "wall_s": dwall,
             "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dgbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode"),
+                         "frac": dgbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode", "decode"),
                          "kernel": "decode_step_kernel<bf16, 128, 128>", "alg_bytes_per_launch": dbytes},
         }
         del state, pool
 
     # ---------------- the other prefill workloads: tokens/s on one GPU
+    def workload_entry(c, lms, reps):
+        wl = c["wl"]
+        entry = {"ms_per_call": lms, "tokens_per_s": c["n_tok"] / (lms * 1e-3),
+                 "token_heads_per_s": c["n_tok"] * wl.H / (lms * 1e-3), "calls": reps,
+                 "dtype": "f32" if c["tdt"] == torch.float32 else "bf16",
+                 "alg_bytes_per_call": c["alg_bytes"],
+                 "hbm_frac": c["alg_bytes"] / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "mfma_frac": None if c["tdt"] == torch.float32
+                 else c["alg_flops"] / (lms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS}
+        if wl.kind == "varlen":
+            entry["sequences"] = int(wl.num_seqs)
+        else:
+            entry["chain_plan"] = plan_of(wl, c["tdt"])
+            a_ms, b_ms = stages(c)
+            entry.update({"intra_ms": a_ms, "chain_ms": b_ms})
+        return entry
+
     if not args.no_workloads:
         out["workloads"] = {}
         chosen = set(x for x in args.workloads.split(",") if x)
+        out["workloads"]["cfg1_bf16_b4_h16_t4096_d128"] = workload_entry(c1, ms, args.steps)
         for name, reps in (("cfg0_f32_b1_h2_t256_d64", 20), ("cfg2_bf16_b1_h32_t65536_d128", 5),
-                           ("cfg4_bf16_b1_h8_t1048576_d128", 3), ("cfg4v_varlen_n16_h8_d128", 3)):
+                           ("cfg4v_varlen_n16_h8_d128", 3)):
             if chosen and name not in chosen:
                 continue
-            wl = datagen.WORKLOADS[name]
-            tdt = torch.float32 if wl.dtype == datagen.DT_F32 else torch.bfloat16
-            if wl.kind == "varlen":
-                lens = datagen.varlen_lengths(wl.seed, wl.num_seqs, wl.len_lo, wl.len_hi)
-                cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-                dl = datagen.prefill_inputs(wl.seed, 1, int(cu[-1]), wl.H, wl.dk, wl.dv, wl.dtype, None)
-            else:
-                dl = datagen.prefill_inputs(wl.seed, wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.dtype, wl.h0_std)
-            gl = {key: to_dev(val) for key, val in dl.items()}
-            del dl
-            ol = torch.empty(gl["v"].shape, dtype=tdt, device=dev)
-            entry = {}
-            if wl.kind == "varlen":
-                cud = to_dev(cu)
-                n_tok = int(cu[-1])
-                hTl = torch.empty((wl.num_seqs, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
-                wsl = torch.empty(kda.varlen_workspace_bytes(wl.num_seqs, n_tok, int(max(lens)), wl.H, wl.dk, wl.dv,
-                                                             wl.chunk, tdt), dtype=torch.uint8, device=dev)
-
-                def lstep(_i):
-                    kda.kda_chunked_forward_varlen(gl["q"], gl["k"], gl["v"], gl["g"], gl["beta"], cud,
-                                                   int(max(lens)), None, chunk=wl.chunk, o=ol, hT=hTl, workspace=wsl)
-                entry["sequences"] = int(wl.num_seqs)
-            else:
-                n_tok = wl.B * wl.T
-                hTl = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
-                wsl = torch.empty(kda.workspace_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.chunk, tdt),
-                                  dtype=torch.uint8, device=dev)
-
-                def lstep(_i):
-                    kda.kda_chunked_forward(gl["q"], gl["k"], gl["v"], gl["g"], gl["beta"], gl["h0"], chunk=wl.chunk,
-                                            o=ol, hT=hTl, workspace=wsl)
-                vs, nseg, segc = kda.chain_plan(wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.chunk, tdt)
-                entry["chain_plan"] = {"value_slice": vs, "segments": nseg, "segment_chunks": segc}
-            lstep(0)
+            cl = prefill_case(datagen.WORKLOADS[name])
+            cl["call"](0)
             torch.cuda.synchronize()
-            lms, _ = time_launches(lstep, reps, None if args.no_flush else flush)
-            s_io = 4 if tdt == torch.float32 else 2
-            n_seq = wl.num_seqs if wl.kind == "varlen" else wl.B
-            wbytes = prefill_bytes(1, n_tok, wl.H, wl.dk, wl.dv, s_io, s_io, with_h0=False, with_hT=False) \
-                + n_seq * wl.H * 4 * wl.dk * wl.dv * (int(wl.kind != "varlen" and wl.h0_std is not None) + 1)
-            wflops = n_tok * wl.H * prefill_flops_per_token_head(wl.dk, wl.dv, wl.chunk)
-            entry.update({"ms_per_call": lms, "tokens_per_s": n_tok / (lms * 1e-3),
-                          "token_heads_per_s": n_tok * wl.H / (lms * 1e-3), "calls": reps,
-                          "dtype": "f32" if tdt == torch.float32 else "bf16",
-                          "hbm_frac": wbytes / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                          "mfma_frac": None if tdt == torch.float32 else wflops / (lms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS})
-            if wl.kind != "varlen":
-                if not args.no_flush:
-                    flush()
-                a_ms, b_ms = kda.kda_chunked_forward_profiled(gl["q"], gl["k"], gl["v"], gl["g"], gl["beta"], gl["h0"],
-                                                              ol, hTl, chunk=wl.chunk, workspace=wsl)
-                entry.update({"intra_ms": a_ms, "chain_ms": b_ms})
-            out["workloads"][name] = entry
+            lms, _ = time_launches(cl["call"], reps, None if args.no_flush else flush)
+            out["workloads"][name] = workload_entry(cl, lms, reps)
             print("workload %s: %.3f ms" % (name, lms), file=sys.stderr, flush=True)
-            del gl, ol, hTl, wsl
+            del cl
             torch.cuda.empty_cache()
 
-    # ---------------- CPU baseline: the fp64 oracle on this host's cores, one sequence of the workload
+    # ---------------- CPU baseline: the fp64 oracle on this host's cores, on a bounded sample of the
+    # headline workload (its first 65,536 tokens, all 8 heads; the oracle runs one thread per head)
     if not args.no_cpu_baseline:
         import oracle
 
-        threads = max(1, min(16, os.cpu_count() or 1))
+        wh = datagen.WORKLOADS[HEADLINE]
+        threads = max(1, min(16, os.cpu_count() or 1, wh.H))  # the oracle's work units are the 8 heads
+        n_tok = cpu_sample["q"].shape[1]
         passes, t0 = 0, time.perf_counter()
-        while True:  # whole passes over the workload, for at least 10 s
-            oracle.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], nthreads=threads)
+        while True:  # whole passes over the sample, for at least 10 s
+            oracle.forward(cpu_sample["q"], cpu_sample["k"], cpu_sample["v"], cpu_sample["g"], cpu_sample["beta"],
+                           None, nthreads=threads)
             passes += 1
             secs = time.perf_counter() - t0
             if secs >= 10.0:
                 break
-        out["cpu_baseline"] = {"value": passes * tokens / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                               "sample": "%d passes over the whole prefill workload (%d x %d tokens x %d heads, fp64, "
-                                         "token by token), %.1f s wall on %d threads"
-                                         % (passes, w.B, w.T, w.H, secs, threads)}
+        out["cpu_baseline"] = {"value": passes * n_tok / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "host_cpu_count": os.cpu_count(),
+                               "sample": "%d passes over the first %d tokens x %d heads of the %s workload (fp64, "
+                                         "token by token, one thread per head), %.1f s wall on %d threads"
+                                         % (passes, n_tok, wh.H, wh.name, secs, threads)}
 
     print(json.dumps(out))
 

@@ -24,7 +24,10 @@
 // The fp32 state lives in MFMA accumulator registers and is fed back as the B operand of the
 // next chunk's products; U likewise.  The copy waves stream records from HBM into double-buffered
 // LDS two chunks ahead (two register staging sets): while the chain waves compute chunk n, the
-// copy waves write chunk n+1 into the other buffer and load chunk n+2.
+// copy waves write chunk n+1 into the other buffer and load chunk n+2.  Where two record buffers
+// do not fit in LDS (fp32 records at d_k = 128, chunk 64), one buffer and one register set: the
+// copy waves load chunk n+1 while the chain waves compute chunk n, then refill the buffer between
+// two barriers.
 #include <type_traits>
 
 #include "kda_device.h"
@@ -76,9 +79,12 @@ struct ChainCfg {
   // global memory at the stores)
   static constexpr int ZROW = WS * ES + 16, B_Z = al(B_GAM + DK * 4);
   static constexpr int BUF0 = B_Z, BUFZ = al(B_Z + C * ZROW);
-  static constexpr bool HAS_Z = ZG && 2 * BUFZ <= 163840;
+  // record buffers in LDS: two (the copy waves fill one while the chain waves read the other), or
+  // one where two do not fit (fp32 records with d_k = 128 and 64-token chunks)
+  static constexpr int NBUF = 2 * BUF0 <= 163840 ? 2 : 1;
+  static constexpr bool HAS_Z = ZG && NBUF * BUFZ <= 163840;
   static constexpr int BUF = HAS_Z ? BUFZ : BUF0;
-  static constexpr int TOTAL = 2 * BUF;
+  static constexpr int TOTAL = NBUF * BUF;
   static_assert(TOTAL <= 163840, "LDS budget of one gfx950 workgroup");
   // 16-byte copy units of one record slice: -W, Q.Gamma, P, K'^T, U~ slice, gamma
   static constexpr int U_NW = C * DK / EPU, U_QG = C * DK / EPU, U_P = C * CP / EPU, U_KPT = DK * CP / EPU;
@@ -393,6 +399,7 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
   // Invariant at chunk c: buffer c&1 holds chunk c, stage (c+1)&1 holds chunk c+1, stage c&1 is
   // free; the copy waves fill buffer (c+1)&1 while the chain waves read buffer c&1.
   const int last = nchunks - 1;
+  constexpr bool ONEBUF = Cf::NBUF == 1;
   if (chain) {
     if constexpr (SUM) {  // zero on the value columns, the identity on the extra ones
 #pragma unroll
@@ -408,14 +415,24 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
         for (int r = 0; r < 4; ++r) Sacc[m][r] = s0 ? s0[(16 * m + 4 * grp + r) * DV + ccol] : 0.f;
     }
     __syncthreads();
-    for (int c = 0; c < nchunks; c += 2) {
-      chunk_step(c, 0);
-      if constexpr (!SUM) snapshot(c);
-      __syncthreads();
-      if (c + 1 >= nchunks) break;
-      chunk_step(c + 1, 1);
-      if constexpr (!SUM) snapshot(c + 1);
-      __syncthreads();
+    if constexpr (ONEBUF) {
+      for (int c = 0; c < nchunks; ++c) {
+        chunk_step(c, 0);
+        if constexpr (!SUM) snapshot(c);
+        __syncthreads();  // the buffer is free
+        if (c + 1 >= nchunks) break;
+        __syncthreads();  // the buffer holds chunk c + 1
+      }
+    } else {
+      for (int c = 0; c < nchunks; c += 2) {
+        chunk_step(c, 0);
+        if constexpr (!SUM) snapshot(c);
+        __syncthreads();
+        if (c + 1 >= nchunks) break;
+        chunk_step(c + 1, 1);
+        if constexpr (!SUM) snapshot(c + 1);
+        __syncthreads();
+      }
     }
     if constexpr (SUM) {
       float* se = p.send + ((int64_t)unit * (p.nseg - 1) + seg) * DK * (DV + DK);
@@ -429,6 +446,27 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
       for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) ht_[(16 * m + 4 * grp + r) * DV + ccol] = Sacc[m][r];
+    }
+  } else if constexpr (ONEBUF) {
+    // one buffer: chunk c + 1 waits in registers while the chain waves compute chunk c
+    Stage s0;
+    if (nchunks > 0) {
+      s0.load(rec_of(0), ht, col0b);
+      if (Cf::HAS_Z && gz) load_z(s0, 0);
+      s0.store(smem, ht);
+      if (Cf::HAS_Z && gz) store_z(s0, smem);
+      s0.load(rec_of(last < 1 ? last : 1), ht, col0b);
+      if (Cf::HAS_Z && gz) load_z(s0, last < 1 ? last : 1);
+    }
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+      __syncthreads();  // the chain waves are done with chunk c
+      if (c + 1 >= nchunks) break;
+      s0.store(smem, ht);
+      if (Cf::HAS_Z && gz) store_z(s0, smem);
+      __syncthreads();  // the buffer holds chunk c + 1
+      s0.load(rec_of(c + 2 < last ? c + 2 : last), ht, col0b);
+      if (Cf::HAS_Z && gz) load_z(s0, c + 2 < last ? c + 2 : last);
     }
   } else {
     Stage s0, s1;
@@ -487,7 +525,8 @@ static hipError_t launch_chain_impl(const ChainLaunch& L) {
 #define KDA_CHAIN_F32(X)                                                                                         \
   X(true, 64, 64, 16, 16) X(true, 64, 64, 32, 16) X(true, 64, 64, 64, 16)                                         \
   X(true, 64, 128, 16, 16) X(true, 64, 128, 32, 16) X(true, 64, 128, 64, 16)                                      \
-  X(true, 128, 64, 16, 16) X(true, 128, 64, 32, 16) X(true, 128, 128, 16, 16) X(true, 128, 128, 32, 16)
+  X(true, 128, 64, 16, 16) X(true, 128, 64, 32, 16) X(true, 128, 64, 64, 16)                                      \
+  X(true, 128, 128, 16, 16) X(true, 128, 128, 32, 16) X(true, 128, 128, 64, 16)
 #define KDA_CHAIN_SUMMARY_INSTANCES(X)                                                                           \
   X(false, 64, 64, 16, 32) X(false, 64, 64, 32, 32) X(false, 64, 64, 64, 32)                                      \
   X(false, 64, 128, 16, 32) X(false, 64, 128, 32, 32) X(false, 64, 128, 64, 32)                                   \

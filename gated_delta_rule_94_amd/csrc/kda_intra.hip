@@ -829,7 +829,8 @@ hipError_t launch_chunk_map(const int32_t* cu, int num_seqs, int T, int C, int32
   X(false, 128, 128, 16) X(false, 128, 128, 32) X(false, 128, 128, 64)                                  \
   X(true, 64, 64, 16) X(true, 64, 64, 32) X(true, 64, 64, 64)                                           \
   X(true, 64, 128, 16) X(true, 64, 128, 32) X(true, 64, 128, 64)                                        \
-  X(true, 128, 64, 16) X(true, 128, 64, 32) X(true, 128, 128, 16) X(true, 128, 128, 32)
+  X(true, 128, 64, 16) X(true, 128, 64, 32) X(true, 128, 64, 64)                                        \
+  X(true, 128, 128, 16) X(true, 128, 128, 32) X(true, 128, 128, 64)
 
 // MXFP8 q, k, v: the bf16 shapes
 #define KDA_INTRA_MX_INSTANCES(X)                                                                       \

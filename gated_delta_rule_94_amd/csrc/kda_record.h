@@ -42,8 +42,8 @@ inline int64_t record_bytes(bool f32, int dk, int dv, int chunk) {
   KDA_REC(false, 128, 128, 16) KDA_REC(false, 128, 128, 32) KDA_REC(false, 128, 128, 64)
   KDA_REC(true, 64, 64, 16) KDA_REC(true, 64, 64, 32) KDA_REC(true, 64, 64, 64)
   KDA_REC(true, 64, 128, 16) KDA_REC(true, 64, 128, 32) KDA_REC(true, 64, 128, 64)
-  KDA_REC(true, 128, 64, 16) KDA_REC(true, 128, 64, 32)
-  KDA_REC(true, 128, 128, 16) KDA_REC(true, 128, 128, 32)
+  KDA_REC(true, 128, 64, 16) KDA_REC(true, 128, 64, 32) KDA_REC(true, 128, 64, 64)
+  KDA_REC(true, 128, 128, 16) KDA_REC(true, 128, 128, 32) KDA_REC(true, 128, 128, 64)
 #undef KDA_REC
   return 0;
 }

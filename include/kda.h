@@ -32,9 +32,9 @@
  *      q, k, g   [B, T, H, d_k]      v, o   [B, T, H, d_v]      beta [B, T, H]
  *      h0, hT, state   [B, H, d_k, d_v] fp32
  *    q, k, v, g, beta and o share one dtype (kda_dtype); states are fp32.
- *  - Supported: d_k, d_v in {64, 128}; chunk in {16, 32, 64}; any T >= 0;
- *    pointers 16-byte aligned.  fp32 inputs with d_k = 128 need chunk <= 32.
- *    Anything else returns KDA_ERR_UNSUPPORTED.
+ *  - Supported: d_k, d_v in {64, 128}; chunk in {16, 32, 64}; fp32 or bf16;
+ *    any T >= 0; pointers 16-byte aligned.  Anything else returns
+ *    KDA_ERR_UNSUPPORTED.
  *  - Deterministic: no atomics; repeated calls give bitwise-identical results.
  *  - Thread-safe: calls share no mutable state.
  *  - Inputs are expected in the documented envelope (-5 <= g <= 0,

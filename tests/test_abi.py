@@ -65,8 +65,7 @@ def test_chain_plan_and_segment_workspace():
     assert kda.chain_plan(1, 1 << 20, 8, 128, 128) == (32, 8, 2048)     # 8 heads x 8 segments x 4 slices
     assert kda.chain_plan(1, 8229, 2, 128, 128) == (32, 4, 33)          # ragged: 129 chunks, last segment 30
     assert kda.chain_plan(1, 6400, 1, 64, 64, dtype=f32) == (16, 3, 34)
-    with pytest.raises(kda.KDAError):
-        kda.chain_plan(1, 6400, 1, 128, 128, dtype=f32)                 # fp32 at d_k 128 has no 64-token chunk
+    assert kda.chain_plan(1, 6400, 1, 128, 128, dtype=f32) == (16, 3, 34)  # fp32 records at d_k 128, chunk 64
     lib = kda.lib()
     rec = 2 * (3 * 64 * 128 + 64 * 64 + 64 * 128) + 4 * 128
     rec = (rec + 255) // 256 * 256
@@ -95,7 +94,6 @@ def test_prefill_validation():
     assert fwd(dv=32) == UNSUPPORTED
     assert fwd(chunk=48) == UNSUPPORTED
     assert fwd(chunk=128) == UNSUPPORTED
-    assert fwd(dt=0, dk=128, chunk=64) == UNSUPPORTED  # fp32 with d_k = 128 needs chunk <= 32
     assert fwd(h0=FAKE + 8) == INVALID
     # workspace missing, too small or misaligned
     need = kda.lib().kda_chunked_forward_workspace_bytes(1, 64, 2, 64, 64, 64, 1)

@@ -67,6 +67,14 @@ def test_fused_fp32_chunk64_gate_read_at_stores(dv):
     fused_case(d, 64, F32, *OPTS["all"], "fused fp32 chunk 64 dv=%d" % dv)
 
 
+@pytest.mark.parametrize("dv", [64, 128])
+def test_fused_fp32_dk128_chunk64(dv):
+    """fp32, d_k = 128, chunk 64: one LDS record buffer in the chain kernel, the output gate
+    streamed with it."""
+    d = raw_inputs(705 + dv, 2, 150, 2, 128, dv, F32)
+    fused_case(d, 64, F32, *OPTS["all"], "fused fp32 d_k 128 chunk 64 dv=%d" % dv)
+
+
 @pytest.mark.parametrize("T", [1, 17, 100])
 def test_fused_gate_ragged_chunks(T):
     """Rows past a partial chunk's end must keep a decay of 1 (their pre-activation loads as 0, and

@@ -46,7 +46,7 @@ def test_fp32_ragged(chunk, T):
     check(d, chunk, F32, "fp32 T=%d" % T)
 
 
-@pytest.mark.parametrize("dk,dv,chunk", [(128, 64, 16), (128, 128, 32), (64, 128, 64)])
+@pytest.mark.parametrize("dk,dv,chunk", [(128, 64, 16), (128, 128, 32), (64, 128, 64), (128, 128, 64), (128, 64, 64)])
 def test_fp32_shapes(dk, dv, chunk):
     d = datagen.prefill_inputs(7, 1, 150, 3, dk, dv, F32, 0.02)
     check(d, chunk, F32, "fp32 dk=%d dv=%d" % (dk, dv))
@@ -133,6 +133,7 @@ def test_continuation_two_halves():
     (BF16, 1, 3000, 3, 64, 64, 32, True),     # 94 chunks of 32
     (F32, 1, 6400, 1, 64, 64, 64, True),
     (F32, 1, 2570, 1, 128, 128, 32, True),    # fp32 at d = 128 (16-column slices), ragged
+    (F32, 1, 4480, 1, 128, 128, 64, True),    # fp32 records at d = 128, chunk 64: one LDS record buffer
 ])
 def test_segmented_chain_against_oracle(dt, B, T, H, dk, dv, chunk, h0):
     """Long sequences on few heads run the chain per segment (summaries, start states, chain):

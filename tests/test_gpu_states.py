@@ -45,6 +45,7 @@ def check_states(d, chunk, every, dt, label):
     (BF16, 2, 1000, 3, 128, 128, 64, 128),
     (BF16, 1, 777, 2, 64, 128, 32, 96),
     (F32, 2, 300, 2, 64, 64, 32, 64),
+    (F32, 1, 300, 2, 128, 128, 64, 128),  # one LDS record buffer in the chain
 ])
 def test_states_are_prefix_states(dt, B, T, H, dk, dv, chunk, every):
     d = datagen.prefill_inputs(600 + T, B, T, H, dk, dv, dt, 0.02)
