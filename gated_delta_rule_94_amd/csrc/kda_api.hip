@@ -113,7 +113,7 @@ kda_status kda_chunked_forward_plan(int B, int T, int H, int d_k, int d_v, int c
   if (!dim_ok(d_k) || !dim_ok(d_v) || !chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
   if (!kda::chunked_forward_supported(dt == KDA_F32, d_k, d_v, chunk)) return KDA_ERR_UNSUPPORTED;
   if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
-  const kda::ChainPlan pl = kda::chain_plan(dt == KDA_F32, (int64_t)B * H, (T + chunk - 1) / chunk, d_k, d_v, false);
+  const kda::ChainPlan pl = kda::chain_plan(dt == KDA_F32, (int64_t)B * H, (T + chunk - 1) / chunk, d_k, d_v, chunk, false);
   if (value_slice) *value_slice = pl.ws;
   if (segments) *segments = pl.nseg;
   if (segment_chunks) *segment_chunks = pl.nseg > 1 ? pl.seg_len : 0;

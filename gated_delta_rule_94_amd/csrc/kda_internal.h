@@ -81,6 +81,7 @@ struct ChainLaunch {
   // from sstart[unit][g] (all segments, the first included) and writes o, and the last writes hT.
   int nseg = 1, seg_len = 0;
   bool summary = false;
+  bool wide = false;  // the wide kernel (bf16, chunk 64: 32-column chain waves, ws up to 128)
   const float* sstart = nullptr;  // [units][nseg][dk][dv]
   float* send = nullptr;          // [units][nseg - 1][dk][dv + dk]
   // optional state snapshots after every `every` tokens of each sequence (every: a multiple of
@@ -96,8 +97,9 @@ struct ChainLaunch {
 // width of the segment summaries (0 when the plan has no segments).
 struct ChainPlan {
   int ws, nseg, seg_len, sum_ws;
+  bool wide;  // chain_wide_kernel (bf16 records of 64-token chunks), else chain_kernel
 };
-ChainPlan chain_plan(bool f32, int64_t units, int nch, int dk, int dv, bool varlen);
+ChainPlan chain_plan(bool f32, int64_t units, int nch, int dk, int dv, int chunk, bool varlen);
 
 // Segment start states: sstart[u][0] = h0 (or 0), sstart[u][g + 1] = M_g sstart[u][g] + b_g
 // (kda_chain.hip)

@@ -33,9 +33,32 @@ static int compute_units();
 // Segments: at least kMinSegChunks chunks each, at most kMaxSeg per (sequence, head).
 static constexpr int kMinSegChunks = 32, kMaxSeg = 64;
 
-ChainPlan chain_plan(bool f32, int64_t units, int nch, int dk, int dv, bool varlen) {
+ChainPlan chain_plan(bool f32, int64_t units, int nch, int dk, int dv, int chunk, bool varlen) {
   const int cus = compute_units();
-  ChainPlan pl{16, 1, 0, 0};
+  ChainPlan pl{16, 1, 0, 0, false};
+  if (!f32 && chunk == 64) {
+    // the wide kernel: chain waves of 32 columns, a workgroup of ws / 32 of them
+    pl.wide = true;
+    pl.ws = 32;
+    if (!varlen && units * (dv / 32) < cus && nch >= 2 * kMinSegChunks) {
+      // long sequences on few heads: the widest slice (each record then streamed from HBM by fewer
+      // workgroups) whose segments, enough of them to fill the CUs, still hold kMinSegChunks chunks
+      for (int ws = dv; ws >= 32; ws /= 2) {
+        const int64_t per = units * (dv / ws);
+        int64_t nseg = (cus + per - 1) / per;
+        if (nseg > kMaxSeg) nseg = kMaxSeg;
+        if (ws > 32 && nseg * kMinSegChunks > nch) continue;
+        if (nseg > nch / kMinSegChunks) nseg = nch / kMinSegChunks;
+        if (nseg < 2) break;
+        pl.ws = ws;
+        pl.seg_len = (int)((nch + nseg - 1) / nseg);
+        pl.nseg = (nch + pl.seg_len - 1) / pl.seg_len;
+        pl.sum_ws = (dk + dv) % 128 == 0 ? 128 : 64;
+        break;
+      }
+    }
+    return pl;
+  }
   if (!f32 && units * (dv / 32) >= cus) pl.ws = 32;
   // Long sequences on few heads: (sequence, head, slice) alone leave CUs idle, so split every
   // sequence into segments.  That triples the chain's work (summaries over twice the columns, then
@@ -67,7 +90,7 @@ size_t chunked_forward_workspace(bool f32, int dk, int dv, int chunk, int64_t ma
   size_t bytes = (size_t)(max_chunks * H * rb);
   if (varlen) bytes += al256((size_t)(num_seqs + 1) * 4) + al256((size_t)num_seqs * 4);  // chunk map, order
   const int nch = (!varlen && num_seqs > 0) ? (int)(max_chunks / num_seqs) : 0;
-  const ChainPlan pl = chain_plan(f32, (int64_t)num_seqs * H, nch, dk, dv, varlen);
+  const ChainPlan pl = chain_plan(f32, (int64_t)num_seqs * H, nch, dk, dv, chunk, varlen);
   if (pl.nseg > 1) {
     const size_t units = (size_t)num_seqs * H;
     bytes += al256(units * pl.nseg * dk * dv * 4) + al256(units * (pl.nseg - 1) * dk * (dv + dk) * 4);
@@ -128,7 +151,8 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
   K.records = records; K.h0 = a.h0; K.o = a.o; K.hT = a.hT; K.cu = a.cu_seqlens; K.chunk0 = chunk0; K.order = order;
   K.units = a.num_seqs * a.H; K.H = a.H; K.T = a.T; K.nch = nch;
   K.dk = a.dk; K.dv = a.dv; K.chunk = C; K.f32 = a.f32;
-  const ChainPlan pl = chain_plan(a.f32, K.units, nch, a.dk, a.dv, varlen);
+  const ChainPlan pl = chain_plan(a.f32, K.units, nch, a.dk, a.dv, C, varlen);
+  K.wide = pl.wide;
   K.ws = pl.ws;
   K.stream = a.stream;
   K.states = a.states; K.every = a.state_every; K.max_states = a.max_states;

@@ -53,24 +53,29 @@ def test_workspace_queries():
 
 
 def test_chain_plan_and_segment_workspace():
-    """The chain layout for 256 compute units (the count assumed without a device, and MI355X's):
-    whole sequences when (sequence, head, 32-column slice) fill the CUs; otherwise every sequence
-    split into segments of at least 32 chunks, and the workspace grows by the segment start states
-    and summaries."""
+    """The chain layout for 256 compute units (the count assumed without a device, and MI355X's).
+    bf16 with 64-token chunks (the wide chain kernel): whole sequences in 32-column slices when
+    (sequence, head, slice) fill the CUs; otherwise every sequence split into enough segments of at
+    least 32 chunks to fill them, in the widest slice (up to d_v) that allows it.  Other shapes
+    (the narrow chain kernel): 16- or 32-column slices, segments of at least 32 chunks.  The
+    workspace grows by the segment start states and summaries."""
     f32 = torch.float32
     assert kda.chain_plan(4, 4096, 16, 128, 128) == (32, 1, 0)          # 256 workgroups already
-    assert kda.chain_plan(1, 2048, 8, 128, 128) == (16, 1, 0)           # 32 chunks: too short to split
+    assert kda.chain_plan(1, 2048, 8, 128, 128) == (32, 1, 0)           # 32 chunks: too short to split
+    assert kda.chain_plan(1, 1024, 8, 128, 128, chunk=32) == (16, 1, 0)  # narrow kernel, 32 chunks
     assert kda.chain_plan(1, 4096, 8, 128, 128) == (32, 2, 32)
-    assert kda.chain_plan(1, 65536, 32, 128, 128) == (32, 2, 512)
-    assert kda.chain_plan(1, 1 << 20, 8, 128, 128) == (32, 8, 2048)     # 8 heads x 8 segments x 4 slices
+    assert kda.chain_plan(1, 65536, 32, 128, 128) == (128, 8, 128)      # 32 heads x 8 segments, whole states
+    assert kda.chain_plan(1, 1 << 20, 8, 128, 128) == (128, 32, 512)    # 8 heads x 32 segments
+    assert kda.summary_slice(1, 1 << 20, 8, 128, 128) == 128            # value and identity halves
     assert kda.chain_plan(1, 8229, 2, 128, 128) == (32, 4, 33)          # ragged: 129 chunks, last segment 30
+    assert kda.chain_plan(1, 8229, 2, 128, 128, chunk=32) == (32, 8, 33)
     assert kda.chain_plan(1, 6400, 1, 64, 64, dtype=f32) == (16, 3, 34)
     assert kda.chain_plan(1, 6400, 1, 128, 128, dtype=f32) == (16, 3, 34)  # fp32 records at d_k 128, chunk 64
     lib = kda.lib()
     rec = 2 * (3 * 64 * 128 + 64 * 64 + 64 * 128) + 4 * 128
     rec = (rec + 255) // 256 * 256
     al = lambda x: (x + 255) // 256 * 256
-    units, nseg = 8, 8
+    units, nseg = 8, 32
     want = 16384 * 8 * rec + al(units * nseg * 128 * 128 * 4) + al(units * (nseg - 1) * 128 * 256 * 4)
     assert lib.kda_chunked_forward_workspace_bytes(1, 1 << 20, 8, 128, 128, 64, 1) == want
 

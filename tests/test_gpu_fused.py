@@ -83,6 +83,15 @@ def test_fused_gate_ragged_chunks(T):
     fused_case(d, 64, BF16, True, False, False, "fused ragged T=%d" % T, scale=3.0)
 
 
+def test_fused_with_whole_state_slices():
+    """A plan with whole 128-column states per workgroup (32 segments): two buffers of the output
+    gate do not fit beside the records, so the chain waves read the gate from global memory."""
+    assert kda.chain_plan(1, 65601, 4, 128, 128) == (64, 32, 33)
+    assert kda.chain_plan(2, 65601, 4, 128, 128) == (128, 32, 33)
+    d = raw_inputs(711, 2, 65601, 4, 128, 128, BF16)
+    fused_case(d, 64, BF16, True, True, True, "fused, whole-state slices")
+
+
 def test_fused_with_segmented_chain():
     assert kda.chain_plan(1, 8229, 2, 128, 128)[1] == 4
     d = raw_inputs(710, 1, 8229, 2, 128, 128, BF16)

@@ -1,11 +1,13 @@
 """Long single sequences on few heads: the segmented chain (segment summaries, the fp32 combine of
 segment start states, the chain per segment) against the fp64 oracle.
 
-* The plan shape of the 1,048,576-token workload (8 heads, d = 128, chunk 64: 8 segments and
-  64-column summaries) at 16,401 tokens, every element of o and hT against the oracle.
+* The plan shape of the 1,048,576-token workload (8 heads, d = 128, chunk 64: whole 128-column
+  states per workgroup, 32 segments, summaries in two 128-column halves) at 65,601 tokens, and
+  every other layout of the wide chain kernel, every element of o and hT against the oracle.
 * The 1,048,576-token workload itself, in the launch configuration the benchmark times: hT against
-  the oracle (the recurrence run over all tokens), o in a window inside segment 5 (the oracle's
-  state carried to the window start), o of the first 32,768 tokens, and a call split in two.
+  the oracle (the recurrence run over all tokens), o in a window starting mid-chunk 700,001 tokens
+  in (segment 21 of 32; the oracle's state carried to the window start), o of the first 32,768
+  tokens, and a call split in two.
 * The packed 16-sequence workload (lengths in [1024, 131072]): every sequence's hT against the
   oracle and o in a window in the middle of every sequence (past 8,192 tokens for all but the
   shortest), the oracle's state carried to each window.
@@ -40,21 +42,50 @@ def oracle_run(d, s, e, h0, want_o):
 
 @pytest.mark.parametrize("h0", [False, True])
 def test_1m_plan_shape_against_oracle(h0):
-    """8 heads, d = 128, chunk 64 and 257 chunks give the 1M-token workload's plan: 32-column
-    chain slices, 8 segments (of 33 chunks; the last is ragged), 64-column summaries."""
-    B, T, H, d, chunk = 1, 16401, 8, 128, 64
-    assert kda.chain_plan(B, T, H, d, d, chunk) == (32, 8, 33)
-    assert kda.summary_slice(B, T, H, d, d, chunk) == 64
+    """8 heads, d = 128, chunk 64 and 1026 chunks give the 1M-token workload's plan: whole 128-column
+    states per workgroup, 32 segments (of 33 chunks; the last is ragged), summaries in two
+    128-column halves (value columns, identity columns)."""
+    B, T, H, d, chunk = 1, 65601, 8, 128, 64
+    assert kda.chain_plan(B, T, H, d, d, chunk) == (128, 32, 33)
+    assert kda.summary_slice(B, T, H, d, d, chunk) == 128
     w = datagen.WORKLOADS["cfg4_bf16_b1_h8_t1048576_d128"]
-    assert kda.chain_plan(w.B, w.T, w.H, w.dk, w.dv, w.chunk)[1] == 8
-    assert kda.summary_slice(w.B, w.T, w.H, w.dk, w.dv, w.chunk) == 64
+    assert kda.chain_plan(w.B, w.T, w.H, w.dk, w.dv, w.chunk) == (128, 32, 512)
+    assert kda.summary_slice(w.B, w.T, w.H, w.dk, w.dv, w.chunk) == 128
     dd = datagen.prefill_inputs(911, B, T, H, d, d, BF16, 0.02 if h0 else None)
     g = {key: dev_tensor(dd[key]) for key in KEYS}
     o, hT = kda.kda_chunked_forward(g["q"], g["k"], g["v"], g["g"], g["beta"], dev_tensor(dd["h0"]), chunk=chunk)
     torch.cuda.synchronize()
     o_ref, h_ref = oracle.forward(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["h0"])
     eo, eh = o_err(host64(o), o_ref), state_err(host64(hT), h_ref)
-    print("16401 tokens x 8 heads, 8 segments: o %.2e hT %.2e" % (eo, eh))
+    print("65601 tokens x 8 heads, 32 segments: o %.2e hT %.2e" % (eo, eh))
+    assert eo < TOL[BF16] and eh < TOL[BF16]
+
+
+@pytest.mark.parametrize("dk,dv,B,T,H,plan,summary", [
+    (64, 64, 1, 4160, 1, (32, 2, 33), 128),
+    (64, 128, 1, 4160, 1, (32, 2, 33), 64),
+    (128, 64, 1, 4160, 1, (32, 2, 33), 64),
+    (128, 128, 1, 4160, 1, (32, 2, 33), 128),
+    (64, 64, 2, 65601, 4, (64, 32, 33), 128),
+    (64, 128, 1, 65601, 4, (64, 32, 33), 64),
+    (64, 128, 2, 65601, 4, (128, 32, 33), 64),
+    (128, 64, 2, 65601, 4, (64, 32, 33), 64),
+    (128, 128, 1, 65601, 4, (64, 32, 33), 128),
+])
+def test_wide_chain_layouts_against_oracle(dk, dv, B, T, H, plan, summary):
+    """Every layout of the wide chain kernel (bf16, chunk 64) a segmented plan takes: value slices
+    of 32, 64 and 128 columns, summaries of 64 (d_v + d_k not a multiple of 128) and 128 columns,
+    every (d_k, d_v); every element of o and hT against the oracle."""
+    assert kda.chain_plan(B, T, H, dk, dv, 64) == plan
+    assert kda.summary_slice(B, T, H, dk, dv, 64) == summary
+    dd = datagen.prefill_inputs(920 + dk + dv + B, B, T, H, dk, dv, BF16, 0.02)
+    g = {key: dev_tensor(dd[key]) for key in KEYS}
+    print("dk=%d dv=%d B=%d T=%d H=%d plan %s summary %d" % (dk, dv, B, T, H, plan, summary), flush=True)
+    o, hT = kda.kda_chunked_forward(g["q"], g["k"], g["v"], g["g"], g["beta"], dev_tensor(dd["h0"]), chunk=64)
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle.forward(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["h0"])
+    eo, eh = o_err(host64(o), o_ref), state_err(host64(hT), h_ref)
+    print("  o %.2e hT %.2e" % (eo, eh))
     assert eo < TOL[BF16] and eh < TOL[BF16]
 
 
@@ -71,8 +102,8 @@ def one_million():
 
 
 def test_1m_sequence_against_oracle(one_million):
-    """hT after all 1,048,576 tokens, o in a 4096-token window inside segment 5 (segments are 2048
-    chunks = 131,072 tokens; the window starts mid-chunk) and o of the first 32,768 tokens."""
+    """hT after all 1,048,576 tokens, o in a 4096-token window starting mid-chunk 700,001 tokens in
+    (segments are 512 chunks = 32,768 tokens) and o of the first 32,768 tokens (segment 0)."""
     w, d, o, hT = one_million
     cut, win = 700_001, 4096
     _, h_cut = oracle_run(d, 0, cut, None, want_o=False)
