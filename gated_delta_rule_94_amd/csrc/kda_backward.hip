@@ -42,6 +42,15 @@ struct BwdParams {
   int T, H, nch;
   int units;  // B H
   int64_t items;
+  // segments of the adjoint chain (long sequences on few heads): nseg > 1 splits every (sequence,
+  // head) into segments of seg_len chunks.  The adjoint chain is affine in the adjoint state at a
+  // segment's end, dS_start = N_g dS_end + c_g.  A summary launch writes [c_g | N_g] of segments
+  // 1..nseg-1 to bsend slot nseg - 1 - g ([units][nseg - 1][DK][DV + DK]); the combine turns them,
+  // from dhT at the last segment's end, into every segment's end adjoint, slot nseg - 1 - g of
+  // bstart ([units][nseg][DK][DV]); the main launch then runs every segment from there.
+  int nseg, seg_len;
+  const float* bstart;
+  float* bsend;
 };
 
 template <int DK, int DV, int C>
@@ -190,7 +199,8 @@ struct ChainStage {
   float pg;
   DW pdo[Cf::NDO];   // raw dO units: loaded unconditionally (clamped rows), so that no wait for
   bool pok[Cf::NDO];  // them is needed before put; pok: the unit lies in the chunk
-  __device__ __forceinline__ void fetch(const BwdParams& p, int b, int h, int ch, int col0, int tid) {
+  // nodo: the slice is identity columns of a segment summary, whose adjoint has no dO term
+  __device__ __forceinline__ void fetch(const BwdParams& p, int b, int h, int ch, int col0, int tid, bool nodo = false) {
     const unsigned char* rec = p.records + ((int64_t)(b * p.nch + ch) * p.H + h) * R::BYTES;
 #pragma unroll
     for (int i = 0; i < Cf::NPF; ++i) {
@@ -207,9 +217,9 @@ struct ChainStage {
 #pragma unroll
     for (int i = 0; i < Cf::NDO; ++i) {
       const int e = tid + Cf::NTH * i, r = (4 * e) / Cf::WS, j = 4 * e - r * Cf::WS;
-      const bool ok = e < Cf::NU4 && r < nr;  // row 0 always lies in the chunk (nr >= 1)
+      const bool ok = !nodo && e < Cf::NU4 && r < nr;  // row 0 always lies in the chunk (nr >= 1)
       pdo[i] = *reinterpret_cast<const DW*>(static_cast<const E*>(p.dO) + (orow + (int64_t)(ok ? r : 0) * p.H) * DV +
-                                            col0 + (ok ? j : 0));
+                                            (ok ? col0 + j : 0));
       pok[i] = ok;
     }
   }
@@ -328,46 +338,61 @@ __device__ __forceinline__ void copy8f(const void* src, int64_t i, float* dst, b
   }
 }
 
-template <bool F32, int DK, int DV, int C>
+// SUM: the summary launch of a segmented adjoint chain (segments 1..nseg-1, d_k more columns that
+// start from the identity and see no dO; see BwdParams).
+template <bool F32, int DK, int DV, int C, bool SUM>
 __global__ __launch_bounds__(512) void bwd_chain_kernel(BwdParams p) {
   using Cf = BChainCfg<F32, DK, DV, C>;
   using R = typename Cf::R;
   using E = typename Cf::E;
   constexpr int WS = Cf::WS, CP = Cf::CP, SE = Cf::SE, SS = Cf::SS;
+  constexpr int NSL = (SUM ? DV + DK : DV) / WS;
   __shared__ __align__(16) unsigned char smem[Cf::TOTAL];
   E* sdU = reinterpret_cast<E*>(smem + Cf::OFF_DU);
   float* sdS = reinterpret_cast<float*>(smem + Cf::OFF_DS);
 
   const int tid = threadIdx.x, wave = tid >> 6, lo = tid & 15, grp = (tid >> 4) & 3;
   // Workgroups go to the 8 XCDs round-robin (workgroup i to XCD i mod 8): the value slices of one
-  // (sequence, head) are given workgroups 8 apart, so they share one XCD's L2 and each record
-  // comes from HBM once.  The grid is padded to a multiple of 8 NSL; padding workgroups exit.
+  // (sequence, head, segment) are given workgroups 8 apart, so they share one XCD's L2 and each
+  // record comes from HBM once.  The grid is padded to a multiple of 8 NSL; padding workgroups exit.
+  const int segs = SUM ? p.nseg - 1 : p.nseg;
   const int xcd = blockIdx.x & 7, q8 = blockIdx.x >> 3;
-  const int unit = (q8 / Cf::NSL) * 8 + xcd, col0 = (q8 % Cf::NSL) * WS;
-  if (unit >= p.units) return;
+  const int su = (q8 / NSL) * 8 + xcd, col0 = (q8 % NSL) * WS;
+  if (su >= p.units * segs) return;
+  const int unit = su / segs, g = su - (su / segs) * segs + (SUM ? 1 : 0);  // g: the segment
   const int H = p.H, b = unit / H, h = unit - b * H;
+  const int ch_lo = p.nseg > 1 ? g * p.seg_len : 0;
+  const int ch_hi = p.nseg > 1 ? min(p.nch, (g + 1) * p.seg_len) : p.nch;  // chunks [ch_lo, ch_hi), in reverse
+  const bool idsl = SUM && col0 >= DV;  // identity columns: no dO term
 
   // one chunk's record prefix, e^{gl} and dO slice: into registers, then into an LDS buffer
   ChainStage<F32, DK, DV, C> stage;
   auto buf_of = [&](int ch) { return Cf::DBUF ? (ch & 1) : 0; };
 
+  // the adjoint state at the range's end: dhT (or the combine's end adjoint of this segment); a
+  // summary starts from zero on the value columns and from the identity on the extra ones
+  const float* d_end = p.nseg > 1 ? p.bstart + ((int64_t)unit * p.nseg + (p.nseg - 1 - g)) * DK * DV
+                                  : (p.dhT ? p.dhT + (int64_t)unit * DK * DV : nullptr);
   for (int e = tid; e < DK * WS; e += Cf::NTH) {
     const int c = e / WS, j = e - c * WS;
-    sdS[c * SS + j] = p.dhT ? p.dhT[((int64_t)unit * DK + c) * DV + col0 + j] : 0.f;
+    if constexpr (SUM) sdS[c * SS + j] = (idsl && c == col0 + j - DV) ? 1.f : 0.f;
+    else sdS[c * SS + j] = d_end ? d_end[(int64_t)c * DV + col0 + j] : 0.f;
   }
-  if (p.nch > 0) {
-    stage.fetch(p, b, h, p.nch - 1, col0, tid);
-    stage.put(smem + buf_of(p.nch - 1) * Cf::BUF, tid);
+  if (ch_hi > ch_lo) {
+    stage.fetch(p, b, h, ch_hi - 1, col0, tid, idsl);
+    stage.put(smem + buf_of(ch_hi - 1) * Cf::BUF, tid);
   }
-  for (int ch = p.nch - 1; ch >= 0; --ch) {
+  for (int ch = ch_hi - 1; ch >= ch_lo; --ch) {
     __syncthreads();  // this chunk's buffer is filled; dS of the previous step is complete
-    float* ds_out = p.dstates + ((int64_t)unit * p.nch + ch) * DK * DV + col0;
-    for (int e = tid; e < DK * WS; e += Cf::NTH) {
-      const int c = e / WS, j = e - c * WS;
-      ds_out[(int64_t)c * DV + j] = sdS[c * SS + j];
+    if constexpr (!SUM) {
+      float* ds_out = p.dstates + ((int64_t)unit * p.nch + ch) * DK * DV + col0;
+      for (int e = tid; e < DK * WS; e += Cf::NTH) {
+        const int c = e / WS, j = e - c * WS;
+        ds_out[(int64_t)c * DV + j] = sdS[c * SS + j];
+      }
     }
     if constexpr (Cf::DBUF) {
-      if (ch > 0) stage.fetch(p, b, h, ch - 1, col0, tid);  // in flight while this chunk computes
+      if (ch > ch_lo) stage.fetch(p, b, h, ch - 1, col0, tid, idsl);  // in flight while this chunk computes
     }
     const unsigned char* base = smem + buf_of(ch) * Cf::BUF;
     const E* sR = reinterpret_cast<const E*>(base);
@@ -399,22 +424,29 @@ __global__ __launch_bounds__(512) void bwd_chain_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) sdS[(c0 + 4 * grp + r) * SS + j0 + lo] = acc[r];
     }
-    if (ch > 0) {
+    if (ch > ch_lo) {
       if constexpr (Cf::DBUF) {
         stage.put(smem + buf_of(ch - 1) * Cf::BUF, tid);  // the other buffer: last read by the previous step
       } else {
         __syncthreads();  // every read of the one buffer is done
-        stage.fetch(p, b, h, ch - 1, col0, tid);
+        stage.fetch(p, b, h, ch - 1, col0, tid, idsl);
         stage.put(smem, tid);
       }
     }
   }
   __syncthreads();
-  if (p.dh0)
+  if constexpr (SUM) {
+    float* se = p.bsend + ((int64_t)unit * (p.nseg - 1) + (p.nseg - 1 - g)) * DK * (DV + DK);
+    for (int e = tid; e < DK * WS; e += Cf::NTH) {
+      const int c = e / WS, j = e - c * WS;
+      se[(int64_t)c * (DV + DK) + col0 + j] = sdS[c * SS + j];
+    }
+  } else if (p.dh0 && g == 0) {
     for (int e = tid; e < DK * WS; e += Cf::NTH) {
       const int c = e / WS, j = e - c * WS;
       p.dh0[((int64_t)unit * DK + c) * DV + col0 + j] = sdS[c * SS + j];
     }
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1038,8 +1070,32 @@ static size_t grad_floats(int dk, int dv, int chunk) {
   return (size_t)((f + 63) & ~(int64_t)63);
 }
 
+// Segments of the adjoint chain, as the forward chain's: when (sequence, head, 32-column slice)
+// alone would leave compute units idle, every sequence is split into nseg segments of at least 32
+// chunks (at most 64 segments); one workgroup per (sequence, head, segment, slice).
+struct BwdPlan {
+  int nseg, seg_len;
+};
+static BwdPlan bwd_plan(int64_t units, int nch, int dv) {
+  BwdPlan pl{1, 0};
+  const int64_t per = units * (dv / 32);
+  const int cus = compute_units();
+  if (per < cus && nch >= 64) {
+    int64_t nseg = (cus + per - 1) / per;
+    if (nseg > nch / 32) nseg = nch / 32;
+    if (nseg > 64) nseg = 64;
+    if (nseg >= 2) {
+      pl.seg_len = (int)((nch + nseg - 1) / nseg);
+      pl.nseg = (nch + pl.seg_len - 1) / pl.seg_len;
+    }
+  }
+  return pl;
+}
+
 // [forward workspace][states: units (nch - 1) dk dv fp32][dstates: units nch dk dv fp32]
-// [grads: items GradLayout floats][o scratch: B T H dv elements], each 256-byte aligned
+// [grads: items GradLayout floats][o scratch: B T H dv elements], and for a segmented adjoint chain
+// [segment end adjoints: units nseg dk dv fp32][summaries: units (nseg - 1) dk (dv + dk) fp32], each
+// 256-byte aligned
 size_t chunked_backward_workspace(bool f32, int dk, int dv, int chunk, int B, int T, int H) {
   if (!chunked_backward_supported(f32, dk, dv, chunk)) return 0;
   const int64_t nch = (T + chunk - 1) / chunk, units = (int64_t)B * H, items = units * nch;
@@ -1048,6 +1104,9 @@ size_t chunked_backward_workspace(bool f32, int dk, int dv, int chunk, int B, in
   bytes += al256((size_t)(units * nch) * dk * dv * 4);
   bytes += al256((size_t)items * grad_floats(dk, dv, chunk) * 4);
   bytes += al256((size_t)B * T * H * dv * (f32 ? 4 : 2));
+  const BwdPlan pl = bwd_plan(units, (int)nch, dv);
+  if (pl.nseg > 1)
+    bytes += al256((size_t)(units * pl.nseg) * dk * dv * 4) + al256((size_t)(units * (pl.nseg - 1)) * dk * (dv + dk) * 4);
   return bytes;
 }
 
@@ -1055,9 +1114,20 @@ template <bool F32, int DK, int DV, int C>
 static hipError_t launch_backward_kernels(const BwdParams& p, int64_t units, void* stream) {
   static_assert(GradLayout<DK, DV, C>::FLOATS == (((int64_t)C * DV + C * C + 3 * C * DK + DK + 63) & ~(int64_t)63),
                 "grad layout");
-  hipLaunchKernelGGL((bwd_chain_kernel<F32, DK, DV, C>), dim3((unsigned)(((units + 7) / 8) * 8 * (DV / 32))), dim3(512), 0,
-                     (hipStream_t)stream, p);
-  hipError_t e = hipGetLastError();
+  hipError_t e = hipSuccess;
+  if (p.nseg > 1) {  // segment summaries, then every segment's end adjoint from dhT
+    const int64_t su = units * (p.nseg - 1);
+    hipLaunchKernelGGL((bwd_chain_kernel<F32, DK, DV, C, true>), dim3((unsigned)(((su + 7) / 8) * 8 * ((DV + DK) / 32))),
+                       dim3(512), 0, (hipStream_t)stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_segment_combine(p.dhT, p.bsend, const_cast<float*>(p.bstart), (int)units, p.nseg, DK, DV, stream)) !=
+        hipSuccess)
+      return e;
+  }
+  const int64_t su = units * p.nseg;
+  hipLaunchKernelGGL((bwd_chain_kernel<F32, DK, DV, C, false>), dim3((unsigned)(((su + 7) / 8) * 8 * (DV / 32))), dim3(512),
+                     0, (hipStream_t)stream, p);
+  e = hipGetLastError();
   if (e != hipSuccess || p.items == 0) return e;
   hipLaunchKernelGGL((bwd_state_kernel<F32, DK, DV, C>), dim3((unsigned)p.items), dim3(512), 0, (hipStream_t)stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1069,7 +1139,9 @@ hipError_t launch_chunked_backward(const BackwardArgs& a) {
   if (!chunked_backward_supported(a.f32, a.dk, a.dv, a.chunk)) return hipErrorInvalidValue;
   const int C = a.chunk, nch = (a.T + C - 1) / C;
   const int64_t units = (int64_t)a.B * a.H, items = units * nch;
-  if (units <= 0 || (units + 7) * (a.dv / 32) > INT32_MAX || items > INT32_MAX) return hipErrorInvalidValue;
+  const BwdPlan pl = bwd_plan(units, nch, a.dv);
+  if (units <= 0 || (units * pl.nseg + 7) * ((a.dv + a.dk) / 32) > INT32_MAX || items > INT32_MAX)
+    return hipErrorInvalidValue;
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
   const size_t fwd = al256(chunked_forward_workspace(a.f32, a.dk, a.dv, C, (int64_t)a.B * nch, a.H, a.B, false));
   float* states = reinterpret_cast<float*>(ws + fwd);
@@ -1079,6 +1151,7 @@ hipError_t launch_chunked_backward(const BackwardArgs& a) {
   float* grads = reinterpret_cast<float*>(ws + fwd + st_bytes + ds_bytes);
   const size_t gr_bytes = al256((size_t)items * grad_floats(a.dk, a.dv, C) * 4);
   void* o_scratch = ws + fwd + st_bytes + ds_bytes + gr_bytes;
+  unsigned char* seg = static_cast<unsigned char*>(o_scratch) + al256((size_t)a.B * a.T * a.H * a.dv * (a.f32 ? 4 : 2));
   hipError_t e = hipSuccess;
   if (a.T > 0) {
     PrefillArgs f;
@@ -1100,6 +1173,9 @@ hipError_t launch_chunked_backward(const BackwardArgs& a) {
   p.records = ws; p.states = states; p.dstates = dstates; p.grads = grads;
   p.dq = a.dq; p.dk = a.dk_out; p.dv = a.dv_out; p.dg = a.dg; p.dbeta = a.dbeta; p.dh0 = a.dh0;
   p.T = a.T; p.H = a.H; p.nch = nch; p.units = (int)units; p.items = items;
+  p.nseg = pl.nseg; p.seg_len = pl.seg_len;
+  p.bstart = reinterpret_cast<const float*>(seg);
+  p.bsend = reinterpret_cast<float*>(seg + al256((size_t)(units * pl.nseg) * a.dk * a.dv * 4));
 #define KDA_BWD_LAUNCH(F, D, V, CC) \
   if (a.f32 == F && a.dk == D && a.dv == V && C == CC) return launch_backward_kernels<F, D, V, CC>(p, units, a.stream);
   KDA_BWD_INSTANCES(KDA_BWD_LAUNCH)

@@ -101,6 +101,9 @@ struct ChainPlan {
 };
 ChainPlan chain_plan(bool f32, int64_t units, int nch, int dk, int dv, int chunk, bool varlen);
 
+// Compute units of the current device (256 when none can be queried), cached per device.
+int compute_units();
+
 // Segment start states: sstart[u][0] = h0 (or 0), sstart[u][g + 1] = M_g sstart[u][g] + b_g
 // (kda_chain.hip)
 hipError_t launch_segment_combine(const float* h0, const float* send, float* sstart, int units, int nseg, int dk,

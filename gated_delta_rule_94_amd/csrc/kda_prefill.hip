@@ -28,36 +28,32 @@ static int64_t max_chunks_of(int T, int chunk, int num_seqs, bool varlen) {
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static int compute_units();
-
 // Segments: at least kMinSegChunks chunks each, at most kMaxSeg per (sequence, head).
 static constexpr int kMinSegChunks = 32, kMaxSeg = 64;
 
 ChainPlan chain_plan(bool f32, int64_t units, int nch, int dk, int dv, int chunk, bool varlen) {
   const int cus = compute_units();
   ChainPlan pl{16, 1, 0, 0, false};
-  if (!f32 && chunk == 64) {
-    // the wide kernel: chain waves of 32 columns, a workgroup of ws / 32 of them
-    pl.wide = true;
-    pl.ws = 32;
-    if (!varlen && units * (dv / 32) < cus && nch >= 2 * kMinSegChunks) {
-      // long sequences on few heads: the widest slice (each record then streamed from HBM by fewer
-      // workgroups) whose segments, enough of them to fill the CUs, still hold kMinSegChunks chunks
-      for (int ws = dv; ws >= 32; ws /= 2) {
-        const int64_t per = units * (dv / ws);
-        int64_t nseg = (cus + per - 1) / per;
-        if (nseg > kMaxSeg) nseg = kMaxSeg;
-        if (ws > 32 && nseg * kMinSegChunks > nch) continue;
-        if (nseg > nch / kMinSegChunks) nseg = nch / kMinSegChunks;
-        if (nseg < 2) break;
-        pl.ws = ws;
-        pl.seg_len = (int)((nch + nseg - 1) / nseg);
-        pl.nseg = (nch + pl.seg_len - 1) / pl.seg_len;
-        pl.sum_ws = (dk + dv) % 128 == 0 ? 128 : 64;
-        break;
-      }
+  if (!f32 && chunk == 64 && !varlen && units * (dv / 32) < cus && nch >= 2 * kMinSegChunks) {
+    // segments on the wide kernel (chain waves of 32 columns, a workgroup of ws / 32 of them).
+    // Unsegmented plans stay on chain_kernel: two 16-column chain waves per workgroup finish a
+    // chunk sooner than one 32-column wave, and there the chunk time is the whole chain's pace.
+    // Long sequences on few heads: the widest slice (each record then streamed from HBM by fewer
+    // workgroups) whose segments, enough of them to fill the CUs, still hold kMinSegChunks chunks.
+    for (int ws = dv; ws >= 32; ws /= 2) {
+      const int64_t per = units * (dv / ws);
+      int64_t nseg = (cus + per - 1) / per;
+      if (nseg > kMaxSeg) nseg = kMaxSeg;
+      if (ws > 32 && nseg * kMinSegChunks > nch) continue;
+      if (nseg > nch / kMinSegChunks) nseg = nch / kMinSegChunks;
+      if (nseg < 2) break;
+      pl.ws = ws;
+      pl.seg_len = (int)((nch + nseg - 1) / nseg);
+      pl.nseg = (nch + pl.seg_len - 1) / pl.seg_len;
+      pl.sum_ws = (dk + dv) % 128 == 0 ? 128 : 64;
+      pl.wide = true;
+      return pl;
     }
-    return pl;
   }
   if (!f32 && units * (dv / 32) >= cus) pl.ws = 32;
   // Long sequences on few heads: (sequence, head, slice) alone leave CUs idle, so split every
@@ -100,7 +96,7 @@ size_t chunked_forward_workspace(bool f32, int dk, int dv, int chunk, int64_t ma
 
 // CUs of the current device (256 when no device can be queried), cached per device; calls from
 // several host threads may query concurrently and store the same value.
-static int compute_units() {
+int compute_units() {
   static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

@@ -53,16 +53,16 @@ def test_workspace_queries():
 
 
 def test_chain_plan_and_segment_workspace():
-    """The chain layout for 256 compute units (the count assumed without a device, and MI355X's).
-    bf16 with 64-token chunks (the wide chain kernel): whole sequences in 32-column slices when
-    (sequence, head, slice) fill the CUs; otherwise every sequence split into enough segments of at
-    least 32 chunks to fill them, in the widest slice (up to d_v) that allows it.  Other shapes
-    (the narrow chain kernel): 16- or 32-column slices, segments of at least 32 chunks.  The
-    workspace grows by the segment start states and summaries."""
+    """The chain layout for 256 compute units (the count assumed without a device, and MI355X's):
+    whole sequences in 16- or 32-column slices when (sequence, head, 32-column slice) fill the CUs
+    or the sequences are too short to split; otherwise every sequence split into enough segments of
+    at least 32 chunks to fill them -- for bf16 with 64-token chunks (the wide chain kernel) in the
+    widest slice, up to d_v, that allows it.  The workspace grows by the segment start states and
+    summaries."""
     f32 = torch.float32
     assert kda.chain_plan(4, 4096, 16, 128, 128) == (32, 1, 0)          # 256 workgroups already
-    assert kda.chain_plan(1, 2048, 8, 128, 128) == (32, 1, 0)           # 32 chunks: too short to split
-    assert kda.chain_plan(1, 1024, 8, 128, 128, chunk=32) == (16, 1, 0)  # narrow kernel, 32 chunks
+    assert kda.chain_plan(1, 2048, 8, 128, 128) == (16, 1, 0)           # 32 chunks: too short to split
+    assert kda.chain_plan(1, 1024, 8, 128, 128, chunk=32) == (16, 1, 0)
     assert kda.chain_plan(1, 4096, 8, 128, 128) == (32, 2, 32)
     assert kda.chain_plan(1, 65536, 32, 128, 128) == (128, 8, 128)      # 32 heads x 8 segments, whole states
     assert kda.chain_plan(1, 1 << 20, 8, 128, 128) == (128, 32, 512)    # 8 heads x 32 segments
@@ -228,6 +228,29 @@ def test_decode_validation():
     assert call(dk=32) == UNSUPPORTED
     assert call(dt=3) == INVALID
     assert call(B=0, ptr=None) == OK
+
+
+def test_backward_segment_workspace():
+    """Long sequences on few heads segment the adjoint chain (as the forward chain): the backward
+    workspace then also holds every segment's end adjoint and the segment summaries."""
+    lib = kda.lib()
+    al = lambda x: (x + 255) // 256 * 256
+    B, T, H, d, C = 1, 16401, 8, 128, 64
+    nch, units = (T + C - 1) // C, B * H
+    fwd = al(lib.kda_chunked_forward_workspace_bytes(B, T, H, d, d, C, 1))
+    grad = ((C * d + C * C + 3 * C * d + d + 63) // 64) * 64
+    base = fwd + al(units * (nch - 1) * d * d * 4) + al(units * nch * d * d * 4) + al(units * nch * grad * 4) \
+        + al(B * T * H * d * 2)
+    nseg = 8  # 8 heads x 4 slices of 32 columns: 32 workgroups, 257 chunks -> 8 segments of 33
+    seg = al(units * nseg * d * d * 4) + al(units * (nseg - 1) * d * 2 * d * 4)
+    assert lib.kda_chunked_backward_workspace_bytes(B, T, H, d, d, C, 1) == base + seg
+    # 16 heads x 4 sequences fill the CUs: no segments
+    B, T, H = 4, 4096, 16
+    nch, units = T // C, B * H
+    fwd = al(lib.kda_chunked_forward_workspace_bytes(B, T, H, d, d, C, 1))
+    base = fwd + al(units * (nch - 1) * d * d * 4) + al(units * nch * d * d * 4) + al(units * nch * grad * 4) \
+        + al(B * T * H * d * 2)
+    assert lib.kda_chunked_backward_workspace_bytes(B, T, H, d, d, C, 1) == base
 
 
 def test_backward_workspace_and_validation():

@@ -84,6 +84,22 @@ def test_backward_with_segmented_forward():
     run_case(950, 1, 8229, 2, 128, 128, BF16, 64, label="segmented")
 
 
+@pytest.mark.parametrize("dhT_std", [0.5, None])
+def test_backward_segmented_adjoint_chain(dhT_std):
+    """8 heads x 16,401 tokens (257 chunks of 64): (sequence, head, 32-column slice) would give 32
+    workgroups, so the adjoint chain runs in 8 segments -- summaries of segments 1..7 over d_k extra
+    identity columns, the combine of their end adjoints from dhT, then every segment -- and the
+    forward recompute is segmented too.  Every gradient element against the oracle."""
+    assert kda.chain_plan(1, 16401, 8, 128, 128)[1] > 1
+    run_case(970, 1, 16401, 8, 128, 128, BF16, 64, dhT_std=dhT_std, label="segmented adjoint chain")
+
+
+@pytest.mark.parametrize("chunk,T", [(64, 4160), (32, 2101)])
+def test_backward_segmented_adjoint_chain_fp32(chunk, T):
+    """One head, fp32, d = 64: 2 adjoint segments (ragged last chunk)."""
+    run_case(975 + chunk, 1, T, 1, 64, 64, F32, chunk, label="segmented adjoint chain fp32")
+
+
 def test_backward_is_deterministic():
     d = datagen.prefill_inputs(960, 2, 300, 4, 128, 128, BF16, 0.02)
     do, dhT = datagen.backward_adjoints(960, 2, 300, 4, 128, 128, BF16, 0.5)
