@@ -985,12 +985,12 @@ static hipError_t launch_chain_wide_impl(const ChainLaunch& L) {
 }
 
 // Wide instances (bf16, chunk 64): value slices of 32, 64 or 128 columns (up to d_v); summaries of
-// 128 columns where they divide d_v + d_k, else 64.
+// all d_v + d_k columns in one workgroup (one round of workgroups; the record streamed once).
 #define KDA_WIDE_INSTANCES(X)                                                                         \
   X(64, 64, 32, false) X(64, 64, 64, false) X(64, 128, 32, false) X(64, 128, 64, false)              \
   X(64, 128, 128, false) X(128, 64, 32, false) X(128, 64, 64, false) X(128, 128, 32, false)          \
   X(128, 128, 64, false) X(128, 128, 128, false)                                                     \
-  X(64, 64, 128, true) X(64, 128, 64, true) X(128, 64, 64, true) X(128, 128, 128, true)
+  X(64, 64, 128, true) X(64, 128, 192, true) X(128, 64, 192, true) X(128, 128, 256, true)
 
 bool chain_wide_supported(bool f32, int dk, int dv, int chunk, int ws, bool summary) {
 #define KDA_HAS(D, V, W, S) \

@@ -50,7 +50,7 @@ ChainPlan chain_plan(bool f32, int64_t units, int nch, int dk, int dv, int chunk
       pl.ws = ws;
       pl.seg_len = (int)((nch + nseg - 1) / nseg);
       pl.nseg = (nch + pl.seg_len - 1) / pl.seg_len;
-      pl.sum_ws = (dk + dv) % 128 == 0 ? 128 : 64;
+      pl.sum_ws = dk + dv;  // a summary workgroup holds the value and identity columns together
       pl.wide = true;
       return pl;
     }

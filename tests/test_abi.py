@@ -66,7 +66,7 @@ def test_chain_plan_and_segment_workspace():
     assert kda.chain_plan(1, 4096, 8, 128, 128) == (32, 2, 32)
     assert kda.chain_plan(1, 65536, 32, 128, 128) == (128, 8, 128)      # 32 heads x 8 segments, whole states
     assert kda.chain_plan(1, 1 << 20, 8, 128, 128) == (128, 32, 512)    # 8 heads x 32 segments
-    assert kda.summary_slice(1, 1 << 20, 8, 128, 128) == 128            # value and identity halves
+    assert kda.summary_slice(1, 1 << 20, 8, 128, 128) == 256            # value and identity columns together
     assert kda.chain_plan(1, 8229, 2, 128, 128) == (32, 4, 33)          # ragged: 129 chunks, last segment 30
     assert kda.chain_plan(1, 8229, 2, 128, 128, chunk=32) == (32, 8, 33)
     assert kda.chain_plan(1, 6400, 1, 64, 64, dtype=f32) == (16, 3, 34)

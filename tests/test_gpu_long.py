@@ -43,14 +43,14 @@ def oracle_run(d, s, e, h0, want_o):
 @pytest.mark.parametrize("h0", [False, True])
 def test_1m_plan_shape_against_oracle(h0):
     """8 heads, d = 128, chunk 64 and 1026 chunks give the 1M-token workload's plan: whole 128-column
-    states per workgroup, 32 segments (of 33 chunks; the last is ragged), summaries in two
-    128-column halves (value columns, identity columns)."""
+    states per workgroup, 32 segments (of 33 chunks; the last is ragged), summaries of all 256
+    columns (value and identity) in one workgroup."""
     B, T, H, d, chunk = 1, 65601, 8, 128, 64
     assert kda.chain_plan(B, T, H, d, d, chunk) == (128, 32, 33)
-    assert kda.summary_slice(B, T, H, d, d, chunk) == 128
+    assert kda.summary_slice(B, T, H, d, d, chunk) == 256
     w = datagen.WORKLOADS["cfg4_bf16_b1_h8_t1048576_d128"]
     assert kda.chain_plan(w.B, w.T, w.H, w.dk, w.dv, w.chunk) == (128, 32, 512)
-    assert kda.summary_slice(w.B, w.T, w.H, w.dk, w.dv, w.chunk) == 128
+    assert kda.summary_slice(w.B, w.T, w.H, w.dk, w.dv, w.chunk) == 256
     dd = datagen.prefill_inputs(911, B, T, H, d, d, BF16, 0.02 if h0 else None)
     g = {key: dev_tensor(dd[key]) for key in KEYS}
     o, hT = kda.kda_chunked_forward(g["q"], g["k"], g["v"], g["g"], g["beta"], dev_tensor(dd["h0"]), chunk=chunk)
@@ -63,19 +63,19 @@ def test_1m_plan_shape_against_oracle(h0):
 
 @pytest.mark.parametrize("dk,dv,B,T,H,plan,summary", [
     (64, 64, 1, 4160, 1, (32, 2, 33), 128),
-    (64, 128, 1, 4160, 1, (32, 2, 33), 64),
-    (128, 64, 1, 4160, 1, (32, 2, 33), 64),
-    (128, 128, 1, 4160, 1, (32, 2, 33), 128),
+    (64, 128, 1, 4160, 1, (32, 2, 33), 192),
+    (128, 64, 1, 4160, 1, (32, 2, 33), 192),
+    (128, 128, 1, 4160, 1, (32, 2, 33), 256),
     (64, 64, 2, 65601, 4, (64, 32, 33), 128),
-    (64, 128, 1, 65601, 4, (64, 32, 33), 64),
-    (64, 128, 2, 65601, 4, (128, 32, 33), 64),
-    (128, 64, 2, 65601, 4, (64, 32, 33), 64),
-    (128, 128, 1, 65601, 4, (64, 32, 33), 128),
+    (64, 128, 1, 65601, 4, (64, 32, 33), 192),
+    (64, 128, 2, 65601, 4, (128, 32, 33), 192),
+    (128, 64, 2, 65601, 4, (64, 32, 33), 192),
+    (128, 128, 1, 65601, 4, (64, 32, 33), 256),
 ])
 def test_wide_chain_layouts_against_oracle(dk, dv, B, T, H, plan, summary):
     """Every layout of the wide chain kernel (bf16, chunk 64) a segmented plan takes: value slices
-    of 32, 64 and 128 columns, summaries of 64 (d_v + d_k not a multiple of 128) and 128 columns,
-    every (d_k, d_v); every element of o and hT against the oracle."""
+    of 32, 64 and 128 columns, summaries of all d_v + d_k columns (128, 192, 256), every (d_k, d_v);
+    every element of o and hT against the oracle."""
     assert kda.chain_plan(B, T, H, dk, dv, 64) == plan
     assert kda.summary_slice(B, T, H, dk, dv, 64) == summary
     dd = datagen.prefill_inputs(920 + dk + dv + B, B, T, H, dk, dv, BF16, 0.02)
