@@ -8,9 +8,10 @@ workload: one sequence of 1,048,576 tokens x 8 heads, bf16 q/k/v/g/beta,
 d_k = d_v = 128, chunk 64, fp32 state from zero.  The call runs, on the
 caller's stream, the intra-chunk kernel (gate cumsum, UT/WY transform and the
 chunk-local products of every (chunk, head), in parallel, into per-chunk
-records) and the state chain (for this shape: a summary pass over 8 segments
-per head, the fp32 combine of segment start states, then the chain of every
-segment, writing o and hT).  Inputs are resident in HBM before the timed
+records) and the state chain (for this shape: 32 segments of 512 chunks per
+head; a summary pass over each segment's value and identity columns, the fp32
+combine of segment start states, then the chain of every segment on whole
+128-column states, writing o and hT).  Inputs are resident in HBM before the timed
 region; the timed region is exactly K back-to-back steps between two HIP events
 on the launch stream, bracketed by synchronisation (ms_per_step = event time /
 K; a step moves tens of GB, far beyond the 256 MB Infinity Cache).  A pass
@@ -27,6 +28,9 @@ The JSON line carries:
   roofline_mfma  -- the call's algorithmic flops against dense bf16 MFMA (the
                     headline metric's "% of MFMA peak")
   stages         -- intra-chunk kernel and state-chain durations (profiled entry point)
+  stream         -- plain device copy / fill / read rates on this GPU, and the call's
+                    counter-measured HBM bytes (whole call and per kernel) at the copy
+                    rate: the least time any kernel moving those bytes could take
   workloads      -- the other seeded prefill workloads (fp32 2 x 256 tokens; 4 x 16
                     heads x 4096 tokens; 32 heads x 65,536 tokens; 16 packed
                     sequences), each timed over a few calls with the cache evicted
@@ -100,9 +104,9 @@ def sources_sha256(kernel_key):
     return h.hexdigest()
 
 
-def measured_traffic(entry, kernel_key):
-    """HBM bytes per call from the committed rocprofv3 counter summary (entry: a workload name or
-    "decode"), if taken on the current sources of kernel_key."""
+def traffic_entry(entry, kernel_key):
+    """The committed rocprofv3 counter summary of a workload (or "decode"): HBM bytes per call and
+    per kernel, if taken on the current sources of kernel_key, else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)[entry]
@@ -110,7 +114,38 @@ def measured_traffic(entry, kernel_key):
         return None
     if t.get("source_sha256") != sources_sha256(kernel_key):
         return None
-    return t["bytes_per_call"]
+    return t
+
+
+def measured_traffic(entry, kernel_key):
+    t = traffic_entry(entry, kernel_key)
+    return None if t is None else t["bytes_per_call"]
+
+
+def stream_rates(reps=5):
+    """Rates of plain device streams on this GPU (torch's own copy, fill and max-reduction over 4 GiB,
+    far beyond the 256 MB Infinity Cache): what a kernel that only moves bytes reaches here, the
+    practical ceiling the kernels' HBM traffic is held against."""
+    import torch
+
+    n = 1 << 30  # 4 GiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    rates = {}
+    for name, fn, moved in (("copy_GBps", lambda: b.copy_(a), 8 * n), ("fill_GBps", lambda: b.fill_(2.0), 4 * n),
+                            ("read_GBps", lambda: torch.amax(a), 4 * n)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        rates[name] = moved / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return rates
 
 
 def world_size():
@@ -166,6 +201,7 @@ def main():
     ap.add_argument("--workloads", default="", help="comma-separated subset of the other prefill workloads")
     ap.add_argument("--no-flush", action="store_true", help="do not evict the Infinity Cache between steps")
     ap.add_argument("--copy-calibration", action="store_true", help="run one 1 GiB copy (counter scaling) and exit")
+    ap.add_argument("--no-stream", action="store_true", help="skip the plain-stream rates")
     args = ap.parse_args()
 
     if args.gpus != 1 or world_size() != 1:
@@ -311,6 +347,20 @@ def main():
     cpu_sample = {key: np.ascontiguousarray(hc["host"][key][:, :65536]) for key in ("q", "k", "v", "g", "beta")}
     del hc, step
     torch.cuda.empty_cache()
+
+    # ---------------- plain streams: the call's measured HBM traffic at a plain device copy's rate is
+    # the least time any kernel moving those bytes could take on this GPU
+    if not args.no_stream:
+        rates = stream_rates()
+        tr = traffic_entry(HEADLINE, "prefill")
+        floor = {"rates": rates, "call_floor_ms": None, "kernel_floor_ms": None, "call_frac_of_floor": None}
+        if tr is not None:
+            floor["call_floor_ms"] = tr["bytes_per_call"] / (rates["copy_GBps"] * 1e6)
+            floor["call_frac_of_floor"] = floor["call_floor_ms"] / ms
+            floor["kernel_floor_ms"] = {k: v["bytes"] / (rates["copy_GBps"] * 1e6) for k, v in tr["kernels"].items()}
+        floor["note"] = ("floor = the call's HBM bytes (rocprofv3 counters, profiles/hbm_traffic.json) at the rate of "
+                         "a plain device copy (read + write) on this GPU")
+        out["stream"] = floor
 
     # ---------------- the 4 x 16 x 4096 workload: its own line in `workloads`, and the legs below
     # (skipped when none of them runs, so that a profile of the headline holds the headline only)
