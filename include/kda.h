@@ -182,11 +182,6 @@ kda_status kda_chunked_forward_fused(const void* q, const void* k, const void* v
                                      size_t workspace_bytes, void* hip_stream);
 
 /*
- * kda_chunked_forward with both state snapshots (states, state_every: see
- * kda_chunked_forward_with_states; states may be NULL) and fused steps
- * (fusion: see kda_fusion; may be NULL).
- */
-/*
  * kda_chunked_forward with q, k and v in the OCP Microscaling FP8 format
  * (MXFP8): the pages train K3 with MXFP8 activations (how-K3-works page, "The
  * systems layer": quantisation-aware training with MXFP4 weights and MXFP8
@@ -212,6 +207,11 @@ kda_status kda_chunked_forward_mxfp8(const void* q, const void* q_scale, const v
                                      const float* h0, void* o, float* hT, int B, int T, int H, int d_k, int d_v,
                                      int chunk, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/*
+ * kda_chunked_forward with both state snapshots (states, state_every: see
+ * kda_chunked_forward_with_states; states may be NULL) and fused steps
+ * (fusion: see kda_fusion; may be NULL).
+ */
 kda_status kda_chunked_forward_ex(const void* q, const void* k, const void* v, const void* g, const void* beta,
                                   const float* h0, void* o, float* hT, float* states, int state_every,
                                   const kda_fusion* fusion, int B, int T, int H, int d_k, int d_v, int chunk,
