@@ -13,7 +13,8 @@ entry points' names:
 * ``kda_chunked_forward_fused`` / ``kda_decode_step_fused`` -- with the gate formed from its
   pre-activation, q and k normalised, and an output gate, inside the kernels
 * ``kda_chunked_forward_ex`` / ``kda_chunked_forward_varlen_ex`` -- snapshots and fused steps together
-* ``kda_chunked_backward``       -- gradients of the chunked prefill (training)
+* ``kda_chunked_backward`` / ``kda_chunked_backward_varlen`` -- gradients of the chunked prefill
+  (training), equal-length or packed sequences
 
 Importing this package fails loudly when ``libkda.so`` has not been built
 (``python gated_delta_rule_94_amd/build.py``).
@@ -38,7 +39,7 @@ EXPORTS = (
     "kda_chunked_forward_fused", "kda_decode_step_fused", "kda_chunked_forward_ex", "kda_chunked_forward_varlen_ex",
     "kda_chunked_forward_profiled", "kda_chunked_forward_varlen", "kda_chunked_forward_varlen_workspace_bytes",
     "kda_decode_step", "kda_chunked_backward", "kda_chunked_backward_workspace_bytes", "kda_chunked_forward_mxfp8",
-    "kda_chunked_forward_noalloc",
+    "kda_chunked_forward_noalloc", "kda_chunked_backward_varlen", "kda_chunked_backward_varlen_workspace_bytes",
 )
 
 # bytes of the library's fixed device scratch used by kda_chunked_forward_noalloc (KDA_NOALLOC_SCRATCH_BYTES)
@@ -95,6 +96,10 @@ _lib.kda_chunked_backward_workspace_bytes.argtypes = [_i32] * 7
 _lib.kda_chunked_backward_workspace_bytes.restype = _sz
 _lib.kda_chunked_backward.argtypes = [_vp] * 14 + [_i32] * 7 + [_vp, _sz, _vp]
 _lib.kda_chunked_backward.restype = _i32
+_lib.kda_chunked_backward_varlen_workspace_bytes.argtypes = [_i32] * 8
+_lib.kda_chunked_backward_varlen_workspace_bytes.restype = _sz
+_lib.kda_chunked_backward_varlen.argtypes = [_vp] * 15 + [_i32] * 8 + [_vp, _sz, _vp]
+_lib.kda_chunked_backward_varlen.restype = _i32
 
 
 class KDAError(RuntimeError):
@@ -583,4 +588,49 @@ def kda_chunked_backward(q, k, v, g, beta, h0, do, dhT=None, *, chunk: int = 64,
                                    B, T, H, dk, dv, chunk, _dtype_code(q), _ptr(ws), _nbytes(ws), _stream(stream))
     if st:
         raise KDAError("kda_chunked_backward", st)
+    return dq, dkk, dvv, dg, db, dh0
+
+
+def backward_varlen_workspace_bytes(num_seqs, T_total, max_seqlen, H, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:
+    """Device workspace kda_chunked_backward_varlen needs for this shape (0: unsupported)."""
+    return int(_lib.kda_chunked_backward_varlen_workspace_bytes(num_seqs, T_total, max_seqlen, H, dk, dv, chunk,
+                                                                _dtype_code(torch.empty(0, dtype=dtype))))
+
+
+def kda_chunked_backward_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen: int, h0, do, dhT=None, *, chunk: int = 64,
+                                want_dh0: bool = True, grads=None, workspace=None, stream=None):
+    """Gradients of <do, o> + <dhT, hT> for (o, hT) = kda_chunked_forward_varlen(q, k, v, g, beta, cu_seqlens,
+    max_seqlen, h0): packed inputs as for the varlen forward ([1,T_total,...] or [T_total,...]), h0 and dhT
+    [N,H,dk,dv] float32 or None.  Returns (dq, dk, dv, dg, dbeta, dh0) shaped like q, k, v, g, beta and
+    [N,H,dk,dv] float32 (None unless want_dh0)."""
+    Tt, H, dk = q.shape[-3:]
+    dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    dt, dev = q.dtype, q.device
+    lead = tuple(q.shape[:-3])
+    if lead not in ((), (1,)):
+        raise ValueError("varlen inputs are packed along one token axis (batch 1)")
+    for name, t, shp in (("q", q, lead + (Tt, H, dk)), ("k", k, lead + (Tt, H, dk)), ("g", g, lead + (Tt, H, dk)),
+                         ("v", v, lead + (Tt, H, dv)), ("beta", beta, lead + (Tt, H)), ("do", do, lead + (Tt, H, dv))):
+        _check(name, t, shp, dt, dev)
+    _check("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
+    _check("h0", h0, (N, H, dk, dv), torch.float32, dev)
+    _check("dhT", dhT, (N, H, dk, dv), torch.float32, dev)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(g),
+                 torch.empty_like(beta),
+                 torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_dh0 else None)
+    dq, dkk, dvv, dg, db, dh0 = grads
+    for name, t, ref in (("dq", dq, q), ("dk", dkk, k), ("dv", dvv, v), ("dg", dg, g), ("dbeta", db, beta)):
+        _check(name, t, ref.shape, dt, dev)
+    _check("dh0", dh0, (N, H, dk, dv), torch.float32, dev)
+    ws_bytes = _lib.kda_chunked_backward_varlen_workspace_bytes(N, Tt, int(max_seqlen), H, dk, dv, chunk,
+                                                               _dtype_code(q))
+    ws = _workspace(workspace, ws_bytes, dev)
+    st = _lib.kda_chunked_backward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(do),
+                                          _ptr(dhT), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg), _ptr(db), _ptr(dh0),
+                                          _ptr(cu_seqlens), N, Tt, int(max_seqlen), H, dk, dv, chunk, _dtype_code(q),
+                                          _ptr(ws), _nbytes(ws), _stream(stream))
+    if st:
+        raise KDAError("kda_chunked_backward_varlen", st)
     return dq, dkk, dvv, dg, db, dh0

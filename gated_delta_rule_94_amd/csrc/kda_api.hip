@@ -348,8 +348,27 @@ kda_status kda_chunked_forward_varlen(const void* q, const void* k, const void* 
 size_t kda_chunked_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt) {
   if (B <= 0 || T < 0 || H <= 0 || (dt != KDA_F32 && dt != KDA_BF16)) return 0;
   if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return 0;
-  return kda::chunked_backward_workspace(dt == KDA_F32, d_k, d_v, chunk, B, T, H);
+  return kda::chunked_backward_workspace(dt == KDA_F32, d_k, d_v, chunk, B, T, H, false);
 }
+
+namespace {
+// Checks shared by the two backward entry points (everything except the batch geometry).
+kda_status check_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                          const float* h0, const void* d_o, const float* dhT, void* dq, void* dk, void* dv, void* dg,
+                          void* dbeta, float* dh0, int tokens, int H, int d_k, int d_v, int chunk, kda_dtype dt) {
+  // the forward's checks (inputs, h0; d_o in place of o), then the gradient buffers
+  const kda_status st = check_prefill(q, k, v, g, beta, h0, d_o, dhT, tokens, H, d_k, d_v, chunk, dt);
+  if (st != KDA_OK) return st;
+  if (tokens > 0) {
+    if (!dq || !dk || !dv || !dg || !dbeta) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dg) || !aligned16(dbeta))
+      return KDA_ERR_INVALID_ARG;
+  }
+  if (dh0 && !aligned16(dh0)) return KDA_ERR_INVALID_ARG;
+  if (!kda::chunked_backward_supported(dt == KDA_F32, d_k, d_v, chunk)) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+}  // namespace
 
 kda_status kda_chunked_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
                                 const float* h0, const void* d_o, const float* dhT, void* dq, void* dk, void* dv,
@@ -357,16 +376,9 @@ kda_status kda_chunked_backward(const void* q, const void* k, const void* v, con
                                 kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
   if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
-  // the forward's checks (inputs, h0; d_o in place of o), then the gradient buffers
-  const kda_status st = check_prefill(q, k, v, g, beta, h0, d_o, dhT, B * T, H, d_k, d_v, chunk, dt);
+  const kda_status st = check_backward(q, k, v, g, beta, h0, d_o, dhT, dq, dk, dv, dg, dbeta, dh0, B * T, H, d_k,
+                                       d_v, chunk, dt);
   if (st != KDA_OK) return st;
-  if (B * T > 0) {
-    if (!dq || !dk || !dv || !dg || !dbeta) return KDA_ERR_INVALID_ARG;
-    if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dg) || !aligned16(dbeta))
-      return KDA_ERR_INVALID_ARG;
-  }
-  if (dh0 && !aligned16(dh0)) return KDA_ERR_INVALID_ARG;
-  if (!kda::chunked_backward_supported(dt == KDA_F32, d_k, d_v, chunk)) return KDA_ERR_UNSUPPORTED;
   if (B == 0 || (T == 0 && !dh0)) return KDA_OK;
   if (!workspace_ok(workspace, workspace_bytes, kda_chunked_backward_workspace_bytes(B, T, H, d_k, d_v, chunk, dt)))
     return KDA_ERR_WORKSPACE;
@@ -374,6 +386,39 @@ kda_status kda_chunked_backward(const void* q, const void* k, const void* v, con
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dO = d_o; a.dhT = dhT;
   a.dq = dq; a.dk_out = dk; a.dv_out = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
   a.B = B; a.T = T; a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk; a.f32 = dt == KDA_F32;
+  a.workspace = workspace;
+  a.stream = hip_stream;
+  return kda::launch_chunked_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_chunked_backward_varlen_workspace_bytes(int num_seqs, int T_total, int max_seqlen, int H, int d_k,
+                                                   int d_v, int chunk, kda_dtype dt) {
+  (void)max_seqlen;
+  if (num_seqs <= 0 || T_total < 0 || H <= 0 || !chunk_ok(chunk) || (dt != KDA_F32 && dt != KDA_BF16)) return 0;
+  if ((int64_t)num_seqs * H > INT32_MAX / 8) return 0;
+  return kda::chunked_backward_workspace(dt == KDA_F32, d_k, d_v, chunk, num_seqs, T_total, H, true);
+}
+
+kda_status kda_chunked_backward_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                       const float* h0, const void* d_o, const float* dhT, void* dq, void* dk,
+                                       void* dv, void* dg, void* dbeta, float* dh0, const int32_t* cu_seqlens,
+                                       int num_seqs, int T_total, int max_seqlen, int H, int d_k, int d_v, int chunk,
+                                       kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (num_seqs < 0 || T_total < 0 || max_seqlen < 0) return KDA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!cu_seqlens || max_seqlen > T_total)) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)num_seqs * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
+  const kda_status st = check_backward(q, k, v, g, beta, h0, d_o, dhT, dq, dk, dv, dg, dbeta, dh0, T_total, H, d_k,
+                                       d_v, chunk, dt);
+  if (st != KDA_OK) return st;
+  if (num_seqs == 0 || (T_total == 0 && !dh0)) return KDA_OK;
+  if (!workspace_ok(workspace, workspace_bytes,
+                    kda_chunked_backward_varlen_workspace_bytes(num_seqs, T_total, max_seqlen, H, d_k, d_v, chunk, dt)))
+    return KDA_ERR_WORKSPACE;
+  kda::BackwardArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dO = d_o; a.dhT = dhT;
+  a.dq = dq; a.dk_out = dk; a.dv_out = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+  a.cu_seqlens = cu_seqlens;
+  a.B = num_seqs; a.T = T_total; a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk; a.f32 = dt == KDA_F32;
   a.workspace = workspace;
   a.stream = hip_stream;
   return kda::launch_chunked_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;

@@ -33,15 +33,19 @@ namespace kda {
 struct BwdParams {
   const void *q, *k, *v, *g, *beta, *dO;
   const float *h0, *dhT;
-  const unsigned char* records;
-  const float* states;  // start state of chunk c >= 1 of unit u at (u (nch - 1) + c - 1) DK DV
-  float* dstates;       // adjoint of the state at the end of chunk c of unit u at (u nch + c) DK DV
+  const unsigned char* records;  // one per (chunk, head) item, item = chunk H + head
+  const float* states;  // the state after chunk c of head h (full chunks) at item (c H + h): DK DV each
+  float* dstates;       // the adjoint of the state at the end of chunk c of head h, at item (c H + h)
   float* grads;         // per (chunk, head) item: GradLayout::FLOATS
   void *dq, *dk, *dv, *dg, *dbeta;
   float* dh0;
-  int T, H, nch;
-  int units;  // B H
-  int64_t items;
+  int T, H, nch;  // tokens per sequence and chunks per sequence (equal lengths), or T_total and 0
+  int units;      // (sequence, head) units: num_seqs H
+  int64_t items;  // (chunk, head) items: exact for equal lengths, a bound for packed sequences
+  // packed sequences: offsets [num_seqs + 1] and the chunk map of the forward recompute (first chunk
+  // of every sequence [num_seqs + 1], the sequences longest first), or NULL
+  const int32_t *cu, *chunk0, *order;
+  int num_seqs;
   // segments of the adjoint chain (long sequences on few heads): nseg > 1 splits every (sequence,
   // head) into segments of seg_len chunks.  The adjoint chain is affine in the adjoint state at a
   // segment's end, dS_start = N_g dS_end + c_g.  A summary launch writes [c_g | N_g] of segments
@@ -67,6 +71,60 @@ struct GradLayout {
 template <typename E>
 __device__ __forceinline__ float tf(E x) {
   return (float)x;
+}
+
+// Token span [a, b) of (sequence, head) unit's sequence n, and its first chunk: equal lengths, or a
+// packed sequence with its offsets clamped to [0, T_total] as the forward's chunk map clamps them.
+__device__ __forceinline__ void seq_span(const BwdParams& p, int n, int64_t& a, int64_t& b, int64_t& first) {
+  if (p.cu) {
+    int x = p.cu[n], y = p.cu[n + 1];
+    x = x < 0 ? 0 : (x > p.T ? p.T : x);
+    y = y < x ? x : (y > p.T ? p.T : y);
+    a = x;
+    b = y;
+    first = p.chunk0[n];
+  } else {
+    a = (int64_t)n * p.T;
+    b = a + p.T;
+    first = (int64_t)n * p.nch;
+  }
+}
+
+// A (chunk, head) item: its head, sequence, first token, length (>= 1), and whether it is the first
+// chunk of its sequence
+struct BItem {
+  int h, seq, len;
+  int64_t tok0;
+  bool first;
+};
+template <int C>
+__device__ __forceinline__ BItem locate(const BwdParams& p, int64_t item) {
+  BItem it;
+  const int64_t c = item / p.H;
+  it.h = (int)(item - c * p.H);
+  int n;
+  if (p.cu) {
+    int lo = 0, hi = p.num_seqs - 1;  // the last sequence whose first chunk is <= c
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.chunk0[mid] <= c) lo = mid;
+      else hi = mid - 1;
+    }
+    n = lo;
+  } else {
+    n = (int)(c / p.nch);
+  }
+  int64_t a, b, first;
+  seq_span(p, n, a, b, first);
+  it.seq = n;
+  it.first = c == first;
+  it.tok0 = a + (c - first) * C;
+  it.len = (int)min((int64_t)C, b - it.tok0);
+  return it;
+}
+// (chunk, head) items that exist: for packed sequences, counted by the chunk map
+__device__ __forceinline__ int64_t item_count(const BwdParams& p) {
+  return p.cu ? (int64_t)p.chunk0[p.num_seqs] * p.H : p.items;
 }
 
 // acc[i][j] += sum_{k in [k0, k1)} a(i, k) b(k, j)
@@ -200,8 +258,10 @@ struct ChainStage {
   DW pdo[Cf::NDO];   // raw dO units: loaded unconditionally (clamped rows), so that no wait for
   bool pok[Cf::NDO];  // them is needed before put; pok: the unit lies in the chunk
   // nodo: the slice is identity columns of a segment summary, whose adjoint has no dO term
-  __device__ __forceinline__ void fetch(const BwdParams& p, int b, int h, int ch, int col0, int tid, bool nodo = false) {
-    const unsigned char* rec = p.records + ((int64_t)(b * p.nch + ch) * p.H + h) * R::BYTES;
+  // chunk c (global index) of head h, tokens [tok0, tok0 + nr), nr >= 1
+  __device__ __forceinline__ void fetch(const BwdParams& p, int64_t c, int h, int64_t tok0, int nr, int col0, int tid,
+                                        bool nodo = false) {
+    const unsigned char* rec = p.records + (c * p.H + h) * R::BYTES;
 #pragma unroll
     for (int i = 0; i < Cf::NPF; ++i) {
       const int e = tid + Cf::NTH * i;
@@ -212,8 +272,7 @@ struct ChainStage {
       pf[4 * i + 3] = x.w;
     }
     pg = reinterpret_cast<const float*>(rec + R::GAM_BYTE)[tid < DK ? tid : 0];
-    const int nr = min(C, p.T - ch * C);
-    const int64_t orow = ((int64_t)b * p.T + (int64_t)ch * C) * p.H + h;
+    const int64_t orow = tok0 * p.H + h;
 #pragma unroll
     for (int i = 0; i < Cf::NDO; ++i) {
       const int e = tid + Cf::NTH * i, r = (4 * e) / Cf::WS, j = 4 * e - r * Cf::WS;
@@ -359,15 +418,26 @@ __global__ __launch_bounds__(512) void bwd_chain_kernel(BwdParams p) {
   const int xcd = blockIdx.x & 7, q8 = blockIdx.x >> 3;
   const int su = (q8 / NSL) * 8 + xcd, col0 = (q8 % NSL) * WS;
   if (su >= p.units * segs) return;
-  const int unit = su / segs, g = su - (su / segs) * segs + (SUM ? 1 : 0);  // g: the segment
-  const int H = p.H, b = unit / H, h = unit - b * H;
+  const int ui = su / segs, g = su - ui * segs + (SUM ? 1 : 0);  // g: the segment
+  const int H = p.H;
+  // packed sequences are taken longest first (the chunk map's order), so that the long chains start
+  // in the first wave of workgroups and the short ones fill in behind them
+  const int n = p.order ? p.order[ui / H] : ui / H, h = ui - (ui / H) * H;
+  const int unit = n * H + h;
+  int64_t t_begin, t_end, first;
+  seq_span(p, n, t_begin, t_end, first);
+  const int nchu = (int)((t_end - t_begin + C - 1) / C);  // chunks of the sequence
   const int ch_lo = p.nseg > 1 ? g * p.seg_len : 0;
-  const int ch_hi = p.nseg > 1 ? min(p.nch, (g + 1) * p.seg_len) : p.nch;  // chunks [ch_lo, ch_hi), in reverse
+  const int ch_hi = p.nseg > 1 ? min(nchu, (g + 1) * p.seg_len) : nchu;  // chunks [ch_lo, ch_hi), in reverse
   const bool idsl = SUM && col0 >= DV;  // identity columns: no dO term
 
   // one chunk's record prefix, e^{gl} and dO slice: into registers, then into an LDS buffer
   ChainStage<F32, DK, DV, C> stage;
   auto buf_of = [&](int ch) { return Cf::DBUF ? (ch & 1) : 0; };
+  auto fetch_ch = [&](int ch) {  // chunk ch of the sequence
+    const int64_t t0 = t_begin + (int64_t)ch * C;
+    stage.fetch(p, first + ch, h, t0, (int)min((int64_t)C, t_end - t0), col0, tid, idsl);
+  };
 
   // the adjoint state at the range's end: dhT (or the combine's end adjoint of this segment); a
   // summary starts from zero on the value columns and from the identity on the extra ones
@@ -379,20 +449,20 @@ __global__ __launch_bounds__(512) void bwd_chain_kernel(BwdParams p) {
     else sdS[c * SS + j] = d_end ? d_end[(int64_t)c * DV + col0 + j] : 0.f;
   }
   if (ch_hi > ch_lo) {
-    stage.fetch(p, b, h, ch_hi - 1, col0, tid, idsl);
+    fetch_ch(ch_hi - 1);
     stage.put(smem + buf_of(ch_hi - 1) * Cf::BUF, tid);
   }
   for (int ch = ch_hi - 1; ch >= ch_lo; --ch) {
     __syncthreads();  // this chunk's buffer is filled; dS of the previous step is complete
     if constexpr (!SUM) {
-      float* ds_out = p.dstates + ((int64_t)unit * p.nch + ch) * DK * DV + col0;
+      float* ds_out = p.dstates + ((first + ch) * H + h) * DK * DV + col0;
       for (int e = tid; e < DK * WS; e += Cf::NTH) {
         const int c = e / WS, j = e - c * WS;
         ds_out[(int64_t)c * DV + j] = sdS[c * SS + j];
       }
     }
     if constexpr (Cf::DBUF) {
-      if (ch > ch_lo) stage.fetch(p, b, h, ch - 1, col0, tid, idsl);  // in flight while this chunk computes
+      if (ch > ch_lo) fetch_ch(ch - 1);  // in flight while this chunk computes
     }
     const unsigned char* base = smem + buf_of(ch) * Cf::BUF;
     const E* sR = reinterpret_cast<const E*>(base);
@@ -429,7 +499,7 @@ __global__ __launch_bounds__(512) void bwd_chain_kernel(BwdParams p) {
         stage.put(smem + buf_of(ch - 1) * Cf::BUF, tid);  // the other buffer: last read by the previous step
       } else {
         __syncthreads();  // every read of the one buffer is done
-        stage.fetch(p, b, h, ch - 1, col0, tid, idsl);
+        fetch_ch(ch - 1);
         stage.put(smem, tid);
       }
     }
@@ -490,17 +560,17 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
   E* sKPT = sP + C * SC;
 
   const int64_t item = blockIdx.x;
-  if (item >= p.items) return;
+  if (item >= item_count(p)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lo = tid & 15, grp = (tid >> 4) & 3, H = p.H;
-  const int64_t cg = item / H;
-  const int h = (int)(item - cg * H), b = (int)(cg / p.nch), ch = (int)(cg - (int64_t)b * p.nch);
-  const int64_t unit = (int64_t)b * H + h;
-  const int nr = min(C, p.T - ch * C);
+  const BItem it = locate<C>(p, item);
+  const int h = it.h, nr = it.len;
+  const int64_t unit = (int64_t)it.seq * H + h;
   const E* rec = reinterpret_cast<const E*>(p.records + item * R::BYTES);
   const float* gam = reinterpret_cast<const float*>(p.records + item * R::BYTES + R::GAM_BYTE);
-  const float* s0 = ch > 0 ? p.states + (unit * (p.nch - 1) + ch - 1) * DK * DV
-                           : (p.h0 ? p.h0 + unit * DK * DV : nullptr);  // nullptr: zero start state
-  const float* ds1 = p.dstates + (unit * p.nch + ch) * DK * DV;
+  // the chunk's start state: the state after the sequence's previous chunk, item - H
+  const float* s0 = !it.first ? p.states + (item - H) * DK * DV
+                              : (p.h0 ? p.h0 + unit * DK * DV : nullptr);  // nullptr: zero start state
+  const float* ds1 = p.dstates + item * DK * DV;
   float* gr = p.grads + item * GL::FLOATS;
 
   // S0 (zeros without one) and dS1 to LDS; the branch on S0's presence is taken once for the
@@ -521,7 +591,7 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
     stage_states(std::true_type{});
   else
     stage_states(std::false_type{});
-  const int64_t orow = ((int64_t)b * p.T + (int64_t)ch * C) * H + h;
+  const int64_t orow = it.tok0 * H + h;
   for_units<C * DV / 8, NTH>(tid, [&](int e) {
     const int r = (8 * e) / DV, j = 8 * e - r * DV;
     copy8<F32>(p.dO, (orow + (int64_t)(r < nr ? r : 0) * H) * DV + j, sdO + r * SV + j, true);
@@ -704,12 +774,11 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   float* sDgl = reinterpret_cast<float*>(smem + Cf::OFF_DGL);
 
   const int64_t item = blockIdx.x;
-  if (item >= p.items) return;
+  if (item >= item_count(p)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lo = tid & 15, grp = (tid >> 4) & 3, H = p.H;
-  const int64_t cg = item / H;
-  const int h = (int)(item - cg * H), b = (int)(cg / p.nch), ch = (int)(cg - (int64_t)b * p.nch);
-  const int nr = min(C, p.T - ch * C);
-  const int64_t row0 = ((int64_t)b * p.T + (int64_t)ch * C) * H + h;  // (token, head) row of the chunk's first token
+  const BItem it = locate<C>(p, item);
+  const int h = it.h, nr = it.len;
+  const int64_t row0 = it.tok0 * H + h;  // (token, head) row of the chunk's first token
   const float* gr = p.grads + item * GL::FLOATS;
 
   // ---- stage q, k, v, g, beta, 8 consecutive channels per access (rows past the chunk's end read
@@ -1092,21 +1161,29 @@ static BwdPlan bwd_plan(int64_t units, int nch, int dv) {
   return pl;
 }
 
-// [forward workspace][states: units (nch - 1) dk dv fp32][dstates: units nch dk dv fp32]
-// [grads: items GradLayout floats][o scratch: B T H dv elements], and for a segmented adjoint chain
-// [segment end adjoints: units nseg dk dv fp32][summaries: units (nseg - 1) dk (dv + dk) fp32], each
-// 256-byte aligned
-size_t chunked_backward_workspace(bool f32, int dk, int dv, int chunk, int B, int T, int H) {
+// The chunks of B equal-length sequences, or a bound on those of num_seqs packed ones (each sequence
+// adds at most one partial chunk), as the forward counts them.
+static int64_t bwd_max_chunks(int C, int num_seqs, int T, bool varlen) {
+  return varlen ? (int64_t)T / C + num_seqs : (int64_t)num_seqs * ((T + C - 1) / C);
+}
+
+// [forward workspace][states: chunks H dk dv fp32][dstates: chunks H dk dv fp32]
+// [grads: chunks H GradLayout floats][o scratch: tokens H dv elements], and for a segmented adjoint
+// chain [segment end adjoints: units nseg dk dv fp32][summaries: units (nseg - 1) dk (dv + dk) fp32],
+// each 256-byte aligned.  tokens: B T, or T_total for packed sequences.
+size_t chunked_backward_workspace(bool f32, int dk, int dv, int chunk, int num_seqs, int T, int H, bool varlen) {
   if (!chunked_backward_supported(f32, dk, dv, chunk)) return 0;
-  const int64_t nch = (T + chunk - 1) / chunk, units = (int64_t)B * H, items = units * nch;
-  size_t bytes = al256(chunked_forward_workspace(f32, dk, dv, chunk, (int64_t)B * nch, H, B, false));
-  bytes += al256((size_t)(units * (nch > 0 ? nch - 1 : 0)) * dk * dv * 4);
-  bytes += al256((size_t)(units * nch) * dk * dv * 4);
+  const int64_t mc = bwd_max_chunks(chunk, num_seqs, T, varlen), units = (int64_t)num_seqs * H, items = mc * H;
+  const int64_t tokens = varlen ? (int64_t)T : (int64_t)num_seqs * T;
+  size_t bytes = al256(chunked_forward_workspace(f32, dk, dv, chunk, mc, H, num_seqs, varlen));
+  bytes += 2 * al256((size_t)items * dk * dv * 4);
   bytes += al256((size_t)items * grad_floats(dk, dv, chunk) * 4);
-  bytes += al256((size_t)B * T * H * dv * (f32 ? 4 : 2));
-  const BwdPlan pl = bwd_plan(units, (int)nch, dv);
-  if (pl.nseg > 1)
-    bytes += al256((size_t)(units * pl.nseg) * dk * dv * 4) + al256((size_t)(units * (pl.nseg - 1)) * dk * (dv + dk) * 4);
+  bytes += al256((size_t)tokens * H * dv * (f32 ? 4 : 2));
+  if (!varlen) {
+    const BwdPlan pl = bwd_plan(units, (T + chunk - 1) / chunk, dv);
+    if (pl.nseg > 1)
+      bytes += al256((size_t)(units * pl.nseg) * dk * dv * 4) + al256((size_t)(units * (pl.nseg - 1)) * dk * (dv + dk) * 4);
+  }
   return bytes;
 }
 
@@ -1137,34 +1214,35 @@ static hipError_t launch_backward_kernels(const BwdParams& p, int64_t units, voi
 
 hipError_t launch_chunked_backward(const BackwardArgs& a) {
   if (!chunked_backward_supported(a.f32, a.dk, a.dv, a.chunk)) return hipErrorInvalidValue;
-  const int C = a.chunk, nch = (a.T + C - 1) / C;
-  const int64_t units = (int64_t)a.B * a.H, items = units * nch;
-  const BwdPlan pl = bwd_plan(units, nch, a.dv);
+  const bool varlen = a.cu_seqlens != nullptr;
+  const int C = a.chunk, nch = varlen ? 0 : (a.T + C - 1) / C;
+  const int64_t mc = bwd_max_chunks(C, a.B, a.T, varlen), units = (int64_t)a.B * a.H, items = mc * a.H;
+  const int64_t tokens = varlen ? (int64_t)a.T : (int64_t)a.B * a.T;
+  const BwdPlan pl = varlen ? BwdPlan{1, 0} : bwd_plan(units, nch, a.dv);
   if (units <= 0 || (units * pl.nseg + 7) * ((a.dv + a.dk) / 32) > INT32_MAX || items > INT32_MAX)
     return hipErrorInvalidValue;
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  const size_t fwd = al256(chunked_forward_workspace(a.f32, a.dk, a.dv, C, (int64_t)a.B * nch, a.H, a.B, false));
+  const size_t fwd = al256(chunked_forward_workspace(a.f32, a.dk, a.dv, C, mc, a.H, a.B, varlen));
+  const size_t st_bytes = al256((size_t)items * a.dk * a.dv * 4);
   float* states = reinterpret_cast<float*>(ws + fwd);
-  const size_t st_bytes = al256((size_t)(units * (nch > 0 ? nch - 1 : 0)) * a.dk * a.dv * 4);
   float* dstates = reinterpret_cast<float*>(ws + fwd + st_bytes);
-  const size_t ds_bytes = al256((size_t)(units * nch) * a.dk * a.dv * 4);
-  float* grads = reinterpret_cast<float*>(ws + fwd + st_bytes + ds_bytes);
+  float* grads = reinterpret_cast<float*>(ws + fwd + 2 * st_bytes);
   const size_t gr_bytes = al256((size_t)items * grad_floats(a.dk, a.dv, C) * 4);
-  void* o_scratch = ws + fwd + st_bytes + ds_bytes + gr_bytes;
-  unsigned char* seg = static_cast<unsigned char*>(o_scratch) + al256((size_t)a.B * a.T * a.H * a.dv * (a.f32 ? 4 : 2));
+  void* o_scratch = ws + fwd + 2 * st_bytes + gr_bytes;
+  unsigned char* seg = static_cast<unsigned char*>(o_scratch) + al256((size_t)tokens * a.H * a.dv * (a.f32 ? 4 : 2));
   hipError_t e = hipSuccess;
-  if (a.T > 0) {
+  if (tokens > 0) {
+    // the forward, keeping the state after every full chunk at that chunk's item slot (the start
+    // state of the sequence's next chunk)
     PrefillArgs f;
     f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta;
     f.h0 = a.h0; f.o = o_scratch; f.hT = nullptr;
-    f.cu_seqlens = nullptr; f.num_seqs = a.B; f.T = a.T;
+    f.cu_seqlens = a.cu_seqlens; f.num_seqs = a.B; f.T = a.T;
     f.H = a.H; f.dk = a.dk; f.dv = a.dv; f.chunk = C; f.f32 = a.f32;
     f.workspace = ws; f.workspace_bytes = fwd; f.stream = a.stream;
-    if (nch >= 2) {
-      f.states = states;
-      f.state_every = C;
-      f.max_states = nch - 1;
-    }
+    f.states = states;
+    f.state_every = C;
+    f.states_by_chunk = true;
     if ((e = launch_chunked_forward(f)) != hipSuccess) return e;
   }
   BwdParams p;
@@ -1173,6 +1251,16 @@ hipError_t launch_chunked_backward(const BackwardArgs& a) {
   p.records = ws; p.states = states; p.dstates = dstates; p.grads = grads;
   p.dq = a.dq; p.dk = a.dk_out; p.dv = a.dv_out; p.dg = a.dg; p.dbeta = a.dbeta; p.dh0 = a.dh0;
   p.T = a.T; p.H = a.H; p.nch = nch; p.units = (int)units; p.items = items;
+  p.cu = a.cu_seqlens; p.num_seqs = a.B;
+  p.chunk0 = p.order = nullptr;
+  if (varlen) {
+    int32_t *c0, *ord;
+    chunk_map_of(ws, a.f32, a.dk, a.dv, C, mc, a.H, a.B, &c0, &ord);
+    // built by the forward recompute; with no tokens every sequence is empty and only the map is needed
+    if (tokens == 0 && (e = launch_chunk_map(a.cu_seqlens, a.B, a.T, C, c0, ord, a.stream)) != hipSuccess) return e;
+    p.chunk0 = c0;
+    p.order = ord;
+  }
   p.nseg = pl.nseg; p.seg_len = pl.seg_len;
   p.bstart = reinterpret_cast<const float*>(seg);
   p.bsend = reinterpret_cast<float*>(seg + al256((size_t)(units * pl.nseg) * a.dk * a.dv * 4));

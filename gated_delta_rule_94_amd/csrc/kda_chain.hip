@@ -49,7 +49,8 @@ struct ChainParams {
   const float* sstart;    // nseg > 1: start state of every segment [units][nseg][DK][DV]
   float* send;            // summary launch: [b_g | M_g] of segments 0..nseg-2 [units][nseg-1][DK][DV+DK]
   float* states;          // or NULL: the state after every `every` tokens of a sequence,
-  int every, max_states;  // [units][max_states][DK][DV]
+  int every, max_states;  // [units][max_states][DK][DV]; with states_by_chunk (every = C), the state
+  int states_by_chunk;    // after every full chunk at its record's slot: [(chunk) H + head][DK][DV]
   const void* z;          // or NULL: an output gate, laid out and typed like o, multiplying o
 };
 
@@ -379,10 +380,11 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     const int rel_end = rel0 + (c + 1) * C;
     if (!p.states || rel_end % p.every != 0 || t_begin + (int64_t)(c + 1) * C > t_end) return;
     const int j = rel_end / p.every - 1;
-    if (j >= p.max_states) return;
+    if (!p.states_by_chunk && j >= p.max_states) return;
+    const int64_t slot = p.states_by_chunk ? (first + c) * H + h : (int64_t)unit * p.max_states + j;
     // a wave-uniform base and 32-bit lane offsets derived here from an opaque zero, so that the
     // compiler keeps no store addresses live across the chunk loop
-    char* st = reinterpret_cast<char*>(p.states + ((int64_t)unit * p.max_states + j) * DK * DV);
+    char* st = reinterpret_cast<char*>(p.states + slot * DK * DV);
     uint32_t z;
     asm volatile("s_mov_b32 %0, 0" : "=s"(z));
     const uint32_t lane_off = 4u * ((4u * grp + z) * DV + ccol);
@@ -876,10 +878,11 @@ __global__ __launch_bounds__(64 * (WS / 32 + 4)) void chain_wide_kernel(const Ch
     const int rel_end = rel0 + (c + 1) * C;
     if (!p.states || rel_end % p.every != 0 || t_begin + (int64_t)(c + 1) * C > t_end) return;
     const int j = rel_end / p.every - 1;
-    if (j >= p.max_states) return;
+    if (!p.states_by_chunk && j >= p.max_states) return;
+    const int64_t slot = p.states_by_chunk ? (first + c) * H + h : (int64_t)unit * p.max_states + j;
     // a wave-uniform base and 32-bit lane offsets derived here from an opaque zero, so that the
     // compiler keeps no store addresses live across the chunk loop
-    char* st = reinterpret_cast<char*>(p.states + ((int64_t)unit * p.max_states + j) * DK * DV);
+    char* st = reinterpret_cast<char*>(p.states + slot * DK * DV);
     uint32_t z;
     asm volatile("s_mov_b32 %0, 0" : "=s"(z));
     const uint32_t lane_off = 4u * ((4u * grp + z) * DV + ccol0 + lo);
@@ -975,6 +978,7 @@ static hipError_t launch_chain_wide_impl(const ChainLaunch& L) {
   p.units = L.units; p.H = L.H; p.T = L.T; p.nch = L.nch; p.dv = DV;
   p.nseg = L.nseg > 1 ? L.nseg : 1; p.seg_len = L.seg_len; p.sstart = L.sstart; p.send = L.send;
   p.states = SUM ? nullptr : L.states; p.every = L.every; p.max_states = L.max_states;
+  p.states_by_chunk = L.states_by_chunk ? 1 : 0;
   p.z = SUM ? nullptr : L.out_gate;
   const int64_t su = (int64_t)L.units * (SUM ? p.nseg - 1 : p.nseg);
   const int64_t grid = ((su + 7) / 8) * 8 * ((SUM ? DV + DK : DV) / WS);
@@ -1016,6 +1020,7 @@ static hipError_t launch_chain_impl(const ChainLaunch& L) {
   p.units = L.units; p.H = L.H; p.T = L.T; p.nch = L.nch; p.dv = DV;
   p.nseg = L.nseg > 1 ? L.nseg : 1; p.seg_len = L.seg_len; p.sstart = L.sstart; p.send = L.send;
   p.states = SUM ? nullptr : L.states; p.every = L.every; p.max_states = L.max_states;
+  p.states_by_chunk = L.states_by_chunk ? 1 : 0;
   p.z = SUM ? nullptr : L.out_gate;
   const int64_t su = (int64_t)L.units * (SUM ? p.nseg - 1 : p.nseg);
   const int64_t grid = ((su + 7) / 8) * 8 * ((SUM ? DV + DK : DV) / WS);

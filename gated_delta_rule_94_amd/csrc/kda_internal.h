@@ -44,6 +44,8 @@ struct PrefillArgs {
   hipEvent_t* events = nullptr;  // optional: [3] recorded before the intra kernel, between the kernels, after the chain
   float* states = nullptr;       // optional state snapshots [num_seqs][H][max_states][dk][dv]
   int state_every = 0, max_states = 0;
+  bool states_by_chunk = false;  // instead: state_every = chunk, the state after every full chunk at
+                                 // its record's slot [(chunk) H + head][dk][dv] (the backward's layout)
   Fusion fusion;
 };
 
@@ -88,6 +90,7 @@ struct ChainLaunch {
   // chunk): [units][max_states][dk][dv]
   float* states = nullptr;
   int every = 0, max_states = 0;
+  bool states_by_chunk = false;  // every = chunk, the state after each full chunk at [(chunk) H + head]
   const void* out_gate = nullptr;  // o is multiplied by it elementwise (Fusion)
   void* stream;
 };
@@ -118,6 +121,7 @@ hipError_t launch_chunk_map(const int32_t* cu, int num_seqs, int T, int C, int32
 // Backward of the chunked prefill (kda_backward.hip): gradients of <dO, o> + <dhT, hT>.
 struct BackwardArgs {
   const void *q, *k, *v, *g, *beta;
+  const int32_t* cu_seqlens = nullptr;  // packed sequences (B = num_seqs, T = T_total), or NULL
   const float* h0;   // or NULL (zero)
   const void* dO;    // like o
   const float* dhT;  // or NULL (zero)
@@ -129,7 +133,7 @@ struct BackwardArgs {
   void* stream;
 };
 bool chunked_backward_supported(bool f32, int dk, int dv, int chunk);
-size_t chunked_backward_workspace(bool f32, int dk, int dv, int chunk, int B, int T, int H);
+size_t chunked_backward_workspace(bool f32, int dk, int dv, int chunk, int num_seqs, int T, int H, bool varlen);
 hipError_t launch_chunked_backward(const BackwardArgs& a);
 
 // Prefill: supported shape?  workspace bytes?  launch (hipErrorInvalidValue: unsupported shape).
@@ -137,5 +141,8 @@ bool chunked_forward_supported(bool f32, int dk, int dv, int chunk);
 size_t chunked_forward_workspace(bool f32, int dk, int dv, int chunk, int64_t max_chunks, int H, int num_seqs,
                                  bool varlen);
 hipError_t launch_chunked_forward(const PrefillArgs& a);
+// the chunk map of a packed call inside its workspace (built by launch_chunked_forward)
+void chunk_map_of(void* workspace, bool f32, int dk, int dv, int chunk, int64_t max_chunks, int H, int num_seqs,
+                  int32_t** chunk0, int32_t** order);
 
 }  // namespace kda

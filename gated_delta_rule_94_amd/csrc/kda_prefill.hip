@@ -108,6 +108,15 @@ int compute_units() {
   return n;
 }
 
+// Where a packed call's chunk map sits in its workspace (after the records): the first chunk of every
+// sequence [num_seqs + 1] and the sequences longest first [num_seqs].
+void chunk_map_of(void* workspace, bool f32, int dk, int dv, int chunk, int64_t max_chunks, int H, int num_seqs,
+                  int32_t** chunk0, int32_t** order) {
+  unsigned char* c0 = static_cast<unsigned char*>(workspace) + max_chunks * H * record_bytes(f32, dk, dv, chunk);
+  *chunk0 = reinterpret_cast<int32_t*>(c0);
+  *order = reinterpret_cast<int32_t*>(c0 + al256((size_t)(num_seqs + 1) * 4));
+}
+
 hipError_t launch_chunked_forward(const PrefillArgs& a) {
   const bool varlen = a.cu_seqlens != nullptr;
   const int C = a.chunk;
@@ -121,8 +130,7 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
   hipError_t e = hipSuccess;
   if (a.events && (e = hipEventRecord(a.events[0], (hipStream_t)a.stream)) != hipSuccess) return e;
   if (varlen) {
-    chunk0 = reinterpret_cast<int32_t*>(records + max_chunks * a.H * rb);
-    order = reinterpret_cast<int32_t*>(reinterpret_cast<unsigned char*>(chunk0) + al256((size_t)(a.num_seqs + 1) * 4));
+    chunk_map_of(a.workspace, a.f32, a.dk, a.dv, C, max_chunks, a.H, a.num_seqs, &chunk0, &order);
     e = launch_chunk_map(a.cu_seqlens, a.num_seqs, a.T, C, chunk0, order, a.stream);
     if (e != hipSuccess) return e;
   }
@@ -151,7 +159,7 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
   K.wide = pl.wide;
   K.ws = pl.ws;
   K.stream = a.stream;
-  K.states = a.states; K.every = a.state_every; K.max_states = a.max_states;
+  K.states = a.states; K.every = a.state_every; K.max_states = a.max_states; K.states_by_chunk = a.states_by_chunk;
   K.out_gate = a.fusion.out_gate;
   if (pl.nseg > 1) {
     unsigned char* seg = records + max_chunks * a.H * rb;

@@ -328,6 +328,27 @@ kda_status kda_chunked_backward(const void* q, const void* k, const void* v, con
 /* Workspace bytes kda_chunked_backward needs (0 = unsupported shape). */
 size_t kda_chunked_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt);
 
+/*
+ * Backward of kda_chunked_forward_varlen: the packed sequences of
+ * kda_chunked_forward_varlen (tensors as in kda_chunked_backward with B = 1
+ * and T = T_total; cu_seqlens, num_seqs, T_total and max_seqlen as in
+ * kda_chunked_forward_varlen), with h0, dhT and dh0 per sequence
+ * [num_seqs,H,d_k,d_v] fp32.  Every sequence's gradients are those of its own
+ * <d_o, o> + <dhT, hT>; no adjoint crosses a sequence boundary, and an empty
+ * sequence gets dh0 = dhT.  Same domain, errors, ownership and stream
+ * semantics as kda_chunked_backward.  workspace:
+ * kda_chunked_backward_varlen_workspace_bytes(...) bytes, 256-byte aligned.
+ */
+kda_status kda_chunked_backward_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                       const float* h0, const void* d_o, const float* dhT, void* dq, void* dk,
+                                       void* dv, void* dg, void* dbeta, float* dh0, const int32_t* cu_seqlens,
+                                       int num_seqs, int T_total, int max_seqlen, int H, int d_k, int d_v, int chunk,
+                                       kda_dtype dt, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes kda_chunked_backward_varlen needs (0 = unsupported shape). */
+size_t kda_chunked_backward_varlen_workspace_bytes(int num_seqs, int T_total, int max_seqlen, int H, int d_k,
+                                                   int d_v, int chunk, kda_dtype dt);
+
 #ifdef __cplusplus
 }
 #endif

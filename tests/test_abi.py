@@ -239,8 +239,7 @@ def test_backward_segment_workspace():
     nch, units = (T + C - 1) // C, B * H
     fwd = al(lib.kda_chunked_forward_workspace_bytes(B, T, H, d, d, C, 1))
     grad = ((C * d + C * C + 3 * C * d + d + 63) // 64) * 64
-    base = fwd + al(units * (nch - 1) * d * d * 4) + al(units * nch * d * d * 4) + al(units * nch * grad * 4) \
-        + al(B * T * H * d * 2)
+    base = fwd + 2 * al(units * nch * d * d * 4) + al(units * nch * grad * 4) + al(B * T * H * d * 2)
     nseg = 8  # 8 heads x 4 slices of 32 columns: 32 workgroups, 257 chunks -> 8 segments of 33
     seg = al(units * nseg * d * d * 4) + al(units * (nseg - 1) * d * 2 * d * 4)
     assert lib.kda_chunked_backward_workspace_bytes(B, T, H, d, d, C, 1) == base + seg
@@ -248,8 +247,7 @@ def test_backward_segment_workspace():
     B, T, H = 4, 4096, 16
     nch, units = T // C, B * H
     fwd = al(lib.kda_chunked_forward_workspace_bytes(B, T, H, d, d, C, 1))
-    base = fwd + al(units * (nch - 1) * d * d * 4) + al(units * nch * d * d * 4) + al(units * nch * grad * 4) \
-        + al(B * T * H * d * 2)
+    base = fwd + 2 * al(units * nch * d * d * 4) + al(units * nch * grad * 4) + al(B * T * H * d * 2)
     assert lib.kda_chunked_backward_workspace_bytes(B, T, H, d, d, C, 1) == base
 
 
@@ -261,8 +259,10 @@ def test_backward_workspace_and_validation():
     B, T, H, D, C = 4, 4096, 16, 128, 64
     nch, units = T // C, B * H
     grad = (C * D + C * C + 3 * C * D + D + 63) // 64 * 64  # dU, dP, d(Q Gamma), dKd, dW, dgl (fp32)
-    want = (al(B * nch * H * rec) + al(units * (nch - 1) * D * D * 4) + al(units * nch * D * D * 4)
-            + al(units * nch * grad * 4) + al(B * T * H * D * 2))
+    # records, the state after every chunk and the adjoint at every chunk end (both per (chunk, head)
+    # record slot), the state products, an o scratch
+    want = (al(B * nch * H * rec) + 2 * al(units * nch * D * D * 4) + al(units * nch * grad * 4)
+            + al(B * T * H * D * 2))
     assert lib.kda_chunked_backward_workspace_bytes(B, T, H, D, D, C, 1) == want
     assert lib.kda_chunked_backward_workspace_bytes(1, 100, 2, 128, 128, 48, 1) == 0  # unsupported chunk
     assert lib.kda_chunked_backward_workspace_bytes(1, 100, 2, 128, 128, 64, 0) == 0  # fp32 only at d = 64
@@ -290,3 +290,42 @@ def test_backward_workspace_and_validation():
     assert call(a) == 3                                     # no workspace: KDA_ERR_WORKSPACE
     assert call(a, B=0) == OK
     assert call(a, T=0) == OK                               # nothing to do without dh0
+
+
+def test_backward_varlen_workspace_and_validation():
+    """The packed backward: workspace for a bound on the chunks (T_total / C + num_seqs) after the
+    varlen forward's own (records and chunk map), and the varlen forward's argument checks plus the
+    gradient buffers'."""
+    lib = kda.lib()
+    al = lambda x: (x + 255) // 256 * 256
+    N, Tt, maxlen, H, D, C = 3, 1000, 600, 4, 128, 64
+    mc = Tt // C + N
+    grad = (C * D + C * C + 3 * C * D + D + 63) // 64 * 64
+    fwd = al(lib.kda_chunked_forward_varlen_workspace_bytes(N, Tt, maxlen, H, D, D, C, 1))
+    want = fwd + 2 * al(mc * H * D * D * 4) + al(mc * H * grad * 4) + al(Tt * H * D * 2)
+    assert lib.kda_chunked_backward_varlen_workspace_bytes(N, Tt, maxlen, H, D, D, C, 1) == want
+    assert lib.kda_chunked_backward_varlen_workspace_bytes(N, Tt, maxlen, H, D, D, 48, 1) == 0
+    assert lib.kda_chunked_backward_varlen_workspace_bytes(N, Tt, maxlen, H, D, D, C, 0) == 0  # fp32 only at d = 64
+    assert lib.kda_chunked_backward_varlen_workspace_bytes(N, Tt, maxlen, H, 64, 64, C, 0) > 0
+    assert lib.kda_chunked_backward_varlen_workspace_bytes(0, Tt, maxlen, H, D, D, C, 1) == 0
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every call below fails validation
+    a = [fake] * 5 + [None, fake, None] + [fake] * 5 + [None, fake]
+
+    def call(args, N=3, Tt=1000, maxlen=600, H=4, dk=128, dv=128, chunk=64, dt=1, ws=None, nbytes=0):
+        return lib.kda_chunked_backward_varlen(*args, N, Tt, maxlen, H, dk, dv, chunk, dt, ws, nbytes, None)
+
+    assert call(a, chunk=48) == UNSUPPORTED
+    assert call(a, dk=96) == UNSUPPORTED
+    assert call(a, dt=0) == UNSUPPORTED                     # fp32 with d = 128
+    assert call(a, N=-1) == INVALID
+    assert call(a, maxlen=1001) == INVALID                  # longer than T_total
+    assert call(a, dt=5) == INVALID
+    bad = list(a)
+    bad[14] = None                                          # cu_seqlens missing
+    assert call(bad) == INVALID
+    bad = list(a)
+    bad[8] = None                                           # dq missing
+    assert call(bad) == INVALID
+    assert call(a) == 3                                     # no workspace: KDA_ERR_WORKSPACE
+    assert call(a, N=0) == OK
+    assert call(a, Tt=0, maxlen=0) == OK                    # nothing to do without dh0
