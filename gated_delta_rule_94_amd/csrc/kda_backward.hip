@@ -523,13 +523,11 @@ __global__ __launch_bounds__(512) void bwd_chain_kernel(BwdParams p) {
 // 3. products with the chunk's start state S0 and end adjoint dS1, one 512-thread workgroup per
 // (chunk, head), on MFMA.  S0, dS1, dO, U and dU are staged in LDS in the operand type (rows padded
 // by 16 bytes); the record's -W, then P (masked to its lower triangle) and Kd^T, share one region.
-template <bool F32, int DK, int DV, int C>
-struct BStateCfg {
-  using R = Rec<F32, DK, DV, C>;
+template <bool F32, int DK, int DV, int C, int VP_>
+struct BStateLayout {
   using E = typename Op<F32>::E;
-  using GL = GradLayout<DK, DV, C>;
-  static constexpr int NTH = 512, ES = sizeof(E);
-  static constexpr int SV = DV + 16 / ES, SK = DK + 16 / ES, SC = C + 16 / ES;
+  static constexpr int ES = sizeof(E);
+  static constexpr int SV = VP_ + 16 / ES, SK = DK + 16 / ES, SC = C + 16 / ES;
   static constexpr int OFF_S0 = 0;                                  // E [DK][SV]
   static constexpr int OFF_DS = OFF_S0 + DK * SV * ES;              // E [DK][SV]
   static constexpr int OFF_DO = OFF_DS + DK * SV * ES;              // E [C][SV]
@@ -538,8 +536,26 @@ struct BStateCfg {
   static constexpr int OFF_X = OFF_DU + C * SV * ES;                // E: -W [C][SK], then P [C][SC] + Kd^T [DK][SC]
   static constexpr int X_BYTES = (C * SK > (C + DK) * SC ? C * SK : (C + DK) * SC) * ES;
   static constexpr int TOTAL = OFF_X + X_BYTES;
+};
+// The value columns are taken VP at a time (all of them where the LDS holds them, else halves or
+// quarters): U and dU are per column, and the other products sum over the columns, so a pass adds
+// its share to them.
+template <bool F32, int DK, int DV, int C>
+struct BStateCfg {
+  using R = Rec<F32, DK, DV, C>;
+  using E = typename Op<F32>::E;
+  using GL = GradLayout<DK, DV, C>;
+  static constexpr int NTH = 512;
+  static constexpr int VP = BStateLayout<F32, DK, DV, C, DV>::TOTAL <= 160 * 1024       ? DV
+                            : BStateLayout<F32, DK, DV, C, DV / 2>::TOTAL <= 160 * 1024 ? DV / 2
+                                                                                          : DV / 4;
+  using L = BStateLayout<F32, DK, DV, C, VP>;
+  static constexpr int SV = L::SV, SK = L::SK, SC = L::SC;
+  static constexpr int OFF_S0 = L::OFF_S0, OFF_DS = L::OFF_DS, OFF_DO = L::OFF_DO, OFF_U = L::OFF_U,
+                       OFF_DU = L::OFF_DU, OFF_X = L::OFF_X, TOTAL = L::TOTAL;
   static_assert(OFF_X % 16 == 0, "alignment");
   static_assert(TOTAL <= 160 * 1024, "LDS");
+  static_assert(VP % 16 == 0, "whole 16-column tiles per pass");
 };
 
 template <bool F32, int DK, int DV, int C>
@@ -548,7 +564,7 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
   using R = typename Cf::R;
   using E = typename Cf::E;
   using GL = typename Cf::GL;
-  constexpr int SV = Cf::SV, SK = Cf::SK, SC = Cf::SC, CP = R::CP, NTH = Cf::NTH;
+  constexpr int SV = Cf::SV, SK = Cf::SK, SC = Cf::SC, CP = R::CP, NTH = Cf::NTH, VP = Cf::VP;
   __shared__ __align__(16) unsigned char smem[Cf::TOTAL];
   E* sS0 = reinterpret_cast<E*>(smem + Cf::OFF_S0);
   E* sdS = reinterpret_cast<E*>(smem + Cf::OFF_DS);
@@ -572,110 +588,118 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
                               : (p.h0 ? p.h0 + unit * DK * DV : nullptr);  // nullptr: zero start state
   const float* ds1 = p.dstates + item * DK * DV;
   float* gr = p.grads + item * GL::FLOATS;
-
-  // S0 (zeros without one) and dS1 to LDS; the branch on S0's presence is taken once for the
-  // workgroup, so no load sits under a per-element select
-  auto stage_states = [&](auto s0_present) {
-    for_units<DK * DV / 4, NTH>(tid, [&](int e) {
-      const int c = (4 * e) / DV, j = 4 * e - c * DV;
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-      if constexpr (decltype(s0_present)::value) a = reinterpret_cast<const float4*>(s0)[e];
-      const float4 d = reinterpret_cast<const float4*>(ds1)[e];
-      E* pa = sS0 + c * SV + j;
-      E* pd = sdS + c * SV + j;
-      pa[0] = (E)a.x; pa[1] = (E)a.y; pa[2] = (E)a.z; pa[3] = (E)a.w;
-      pd[0] = (E)d.x; pd[1] = (E)d.y; pd[2] = (E)d.z; pd[3] = (E)d.w;
-    });
-  };
-  if (s0)
-    stage_states(std::true_type{});
-  else
-    stage_states(std::false_type{});
   const int64_t orow = it.tok0 * H + h;
-  for_units<C * DV / 8, NTH>(tid, [&](int e) {
-    const int r = (8 * e) / DV, j = 8 * e - r * DV;
-    copy8<F32>(p.dO, (orow + (int64_t)(r < nr ? r : 0) * H) * DV + j, sdO + r * SV + j, true);
-  });
-  for_units<C * DK / 8, NTH>(tid, [&](int e) {
-    const int r = (8 * e) / DK, c = 8 * e - r * DK;
-    copy8<F32>(rec, R::NW + 8 * e, sNW + r * SK + c, true);
-  });
-  if (nr < C) {  // the same threads overwrite dO's rows past the end with zeros
-    for_units<C * DV / 8, NTH>(tid, [&](int e) {
-      const int r = (8 * e) / DV, j = 8 * e - r * DV;
-      if (r >= nr) zero8<F32>(sdO + r * SV + j);
+
+#pragma unroll
+  for (int vp0 = 0; vp0 < DV; vp0 += VP) {
+    // a sum over the value columns: the first pass writes it, later ones add their share (each
+    // element has one owner thread in every pass)
+    auto put = [&](int64_t i, float x) { gr[i] = vp0 == 0 ? x : gr[i] + x; };
+    if (vp0 > 0) __syncthreads();  // the previous pass's reads of every LDS region are done
+    // columns [vp0, vp0 + VP) of S0 (zeros without one) and dS1 to LDS; the branch on S0's presence
+    // is taken once for the workgroup, so no load sits under a per-element select
+    auto stage_states = [&](auto s0_present) {
+      for_units<DK * VP / 4, NTH>(tid, [&](int e) {
+        const int c = (4 * e) / VP, j = 4 * e - c * VP;
+        const int64_t gi = (int64_t)c * DV + vp0 + j;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (decltype(s0_present)::value) a = *reinterpret_cast<const float4*>(s0 + gi);
+        const float4 d = *reinterpret_cast<const float4*>(ds1 + gi);
+        E* pa = sS0 + c * SV + j;
+        E* pd = sdS + c * SV + j;
+        pa[0] = (E)a.x; pa[1] = (E)a.y; pa[2] = (E)a.z; pa[3] = (E)a.w;
+        pd[0] = (E)d.x; pd[1] = (E)d.y; pd[2] = (E)d.z; pd[3] = (E)d.w;
+      });
+    };
+    if (s0)
+      stage_states(std::true_type{});
+    else
+      stage_states(std::false_type{});
+    for_units<C * VP / 8, NTH>(tid, [&](int e) {
+      const int r = (8 * e) / VP, j = 8 * e - r * VP;
+      copy8<F32>(p.dO, (orow + (int64_t)(r < nr ? r : 0) * H) * DV + vp0 + j, sdO + r * SV + j, true);
     });
-  }
-  __syncthreads();
-  // U = U~ + (-W) S0  (U~ from the record's U~^T)
-  for (int t = wave; t < (C / 16) * (DV / 16); t += NTH / 64) {
-    const int i0 = 16 * (t / (DV / 16)), j0 = 16 * (t % (DV / 16));
-    f32x4 acc;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = tf(rec[R::UT + (j0 + lo) * C + i0 + 4 * grp + r]);
-    acc = tile_mm<F32, DK>([&](int m, int k) { return tf(sNW[(i0 + m) * SK + k]); },
-                           [&](int k, int n) { return tf(sS0[k * SV + j0 + n]); }, acc);  // S0 runs along n
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sU[(i0 + 4 * grp + r) * SV + j0 + lo] = (E)acc[r];
-  }
-  // e^{gl} rowsum(S0 . dS1): NTH / DK adjacent lanes per channel, each over every (NTH / DK)-th column
-  {
-    constexpr int NPCH = NTH / DK;
-    static_assert(NPCH * DK == NTH && (NPCH & (NPCH - 1)) == 0 && NPCH <= 64, "lanes per channel");
-    const int c = tid / NPCH, part = tid - c * NPCH;
-    float sum = 0.f;
-    for (int j = part; j < DV; j += NPCH) sum = fmaf(tf(sS0[c * SV + j]), tf(sdS[c * SV + j]), sum);
-#pragma unroll
-    for (int off = 1; off < NPCH; off <<= 1) sum += __shfl_xor(sum, off);
-    if (part == 0) gr[GL::DGL + c] = gam[c] * sum;
-  }
-  __syncthreads();
-  for_units<C * C / 8, NTH>(tid, [&](int e) {  // P's lower triangle (record tiles above it are not all written)
-    const int s_ = (8 * e) / C, r = 8 * e - s_ * C;
-    copy8_head<F32>(rec, R::P + s_ * CP + r, sP + s_ * SC + r, s_ - r + 1);
-  });
-  for_units<DK * C / 8, NTH>(tid, [&](int e) {
-    const int c = (8 * e) / C, r = 8 * e - c * C;
-    copy8<F32>(rec, R::KPT + c * CP + r, sKPT + c * SC + r, true);
-  });
-  __syncthreads();
-  // dU[r][j] = sum_{s >= r} P[s][r] dO[s][j] + sum_c Kd^T[c][r] dS1[c][j]
-  for (int t = wave; t < (C / 16) * (DV / 16); t += NTH / 64) {
-    const int i0 = 16 * (t / (DV / 16)), j0 = 16 * (t % (DV / 16));
-    f32x4 acc = zero4();
-    acc = tile_mm<F32, C>([&](int m, int k) { return tf(sP[k * SC + i0 + m]); },
-                          [&](int k, int n) { return tf(sdO[k * SV + j0 + n]); }, acc);
-    acc = tile_mm<F32, DK>([&](int m, int k) { return tf(sKPT[k * SC + i0 + m]); },
-                           [&](int k, int n) { return tf(sdS[k * SV + j0 + n]); }, acc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sdU[(i0 + 4 * grp + r) * SV + j0 + lo] = (E)acc[r];
-      gr[GL::DU + (i0 + 4 * grp + r) * DV + j0 + lo] = acc[r];
+    for_units<C * DK / 8, NTH>(tid, [&](int e) {
+      const int r = (8 * e) / DK, c = 8 * e - r * DK;
+      copy8<F32>(rec, R::NW + 8 * e, sNW + r * SK + c, true);
+    });
+    if (nr < C) {  // the same threads overwrite dO's rows past the end with zeros
+      for_units<C * VP / 8, NTH>(tid, [&](int e) {
+        const int r = (8 * e) / VP, j = 8 * e - r * VP;
+        if (r >= nr) zero8<F32>(sdO + r * SV + j);
+      });
     }
-  }
-  __syncthreads();
-  // dP = lowerIncl(dO U^T)
-  for (int t = wave; t < (C / 16) * (C / 16); t += NTH / 64) {
-    const int i0 = 16 * (t / (C / 16)), n0 = 16 * (t % (C / 16));
-    f32x4 acc = zero4();
-    if (n0 <= i0) acc = tile_rows<F32, DV>(sdO + (i0 + lo) * SV, sU + (n0 + lo) * SV, acc);
+    __syncthreads();
+    // U = U~ + (-W) S0  (U~ from the record's U~^T)
+    for (int t = wave; t < (C / 16) * (VP / 16); t += NTH / 64) {
+      const int i0 = 16 * (t / (VP / 16)), j0 = 16 * (t % (VP / 16));
+      f32x4 acc;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = i0 + 4 * grp + r, col = n0 + lo;
-      gr[GL::DP + row * C + col] = col <= row ? acc[r] : 0.f;
+      for (int r = 0; r < 4; ++r) acc[r] = tf(rec[R::UT + (vp0 + j0 + lo) * C + i0 + 4 * grp + r]);
+      acc = tile_mm<F32, DK>([&](int m, int k) { return tf(sNW[(i0 + m) * SK + k]); },
+                             [&](int k, int n) { return tf(sS0[k * SV + j0 + n]); }, acc);  // S0 runs along n
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sU[(i0 + 4 * grp + r) * SV + j0 + lo] = (E)acc[r];
     }
-  }
-  // d(Q Gamma) = dO S0^T, dKd = U dS1^T, dW = -dU S0^T
-  for (int t = wave; t < 3 * (C / 16) * (DK / 16); t += NTH / 64) {
-    const int which = t / ((C / 16) * (DK / 16)), tt = t - which * ((C / 16) * (DK / 16));
-    const int i0 = 16 * (tt / (DK / 16)), c0 = 16 * (tt % (DK / 16));
-    const E* A = which == 0 ? sdO : which == 1 ? sU : sdU;
-    const E* Bt = which == 1 ? sdS : sS0;
-    f32x4 acc = tile_rows<F32, DV>(A + (i0 + lo) * SV, Bt + (c0 + lo) * SV, zero4());
-    const int64_t off = which == 0 ? GL::DQG : which == 1 ? GL::DKD : GL::DW;
-    const float sg = which == 2 ? -1.f : 1.f;
+    // e^{gl} rowsum(S0 . dS1): NTH / DK adjacent lanes per channel, each over every (NTH / DK)-th column
+    {
+      constexpr int NPCH = NTH / DK;
+      static_assert(NPCH * DK == NTH && (NPCH & (NPCH - 1)) == 0 && NPCH <= 64, "lanes per channel");
+      const int c = tid / NPCH, part = tid - c * NPCH;
+      float sum = 0.f;
+      for (int j = part; j < VP; j += NPCH) sum = fmaf(tf(sS0[c * SV + j]), tf(sdS[c * SV + j]), sum);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) gr[off + (i0 + 4 * grp + r) * DK + c0 + lo] = sg * acc[r];
+      for (int off = 1; off < NPCH; off <<= 1) sum += __shfl_xor(sum, off);
+      if (part == 0) put(GL::DGL + c, gam[c] * sum);
+    }
+    __syncthreads();
+    for_units<C * C / 8, NTH>(tid, [&](int e) {  // P's lower triangle (record tiles above it are not all written)
+      const int s_ = (8 * e) / C, r = 8 * e - s_ * C;
+      copy8_head<F32>(rec, R::P + s_ * CP + r, sP + s_ * SC + r, s_ - r + 1);
+    });
+    for_units<DK * C / 8, NTH>(tid, [&](int e) {
+      const int c = (8 * e) / C, r = 8 * e - c * C;
+      copy8<F32>(rec, R::KPT + c * CP + r, sKPT + c * SC + r, true);
+    });
+    __syncthreads();
+    // dU[r][j] = sum_{s >= r} P[s][r] dO[s][j] + sum_c Kd^T[c][r] dS1[c][j]
+    for (int t = wave; t < (C / 16) * (VP / 16); t += NTH / 64) {
+      const int i0 = 16 * (t / (VP / 16)), j0 = 16 * (t % (VP / 16));
+      f32x4 acc = zero4();
+      acc = tile_mm<F32, C>([&](int m, int k) { return tf(sP[k * SC + i0 + m]); },
+                            [&](int k, int n) { return tf(sdO[k * SV + j0 + n]); }, acc);
+      acc = tile_mm<F32, DK>([&](int m, int k) { return tf(sKPT[k * SC + i0 + m]); },
+                             [&](int k, int n) { return tf(sdS[k * SV + j0 + n]); }, acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sdU[(i0 + 4 * grp + r) * SV + j0 + lo] = (E)acc[r];
+        gr[GL::DU + (i0 + 4 * grp + r) * DV + vp0 + j0 + lo] = acc[r];
+      }
+    }
+    __syncthreads();
+    // dP = lowerIncl(dO U^T)
+    for (int t = wave; t < (C / 16) * (C / 16); t += NTH / 64) {
+      const int i0 = 16 * (t / (C / 16)), n0 = 16 * (t % (C / 16));
+      f32x4 acc = zero4();
+      if (n0 <= i0) acc = tile_rows<F32, VP>(sdO + (i0 + lo) * SV, sU + (n0 + lo) * SV, acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = i0 + 4 * grp + r, col = n0 + lo;
+        put(GL::DP + row * C + col, col <= row ? acc[r] : 0.f);
+      }
+    }
+    // d(Q Gamma) = dO S0^T, dKd = U dS1^T, dW = -dU S0^T
+    for (int t = wave; t < 3 * (C / 16) * (DK / 16); t += NTH / 64) {
+      const int which = t / ((C / 16) * (DK / 16)), tt = t - which * ((C / 16) * (DK / 16));
+      const int i0 = 16 * (tt / (DK / 16)), c0 = 16 * (tt % (DK / 16));
+      const E* A = which == 0 ? sdO : which == 1 ? sU : sdU;
+      const E* Bt = which == 1 ? sdS : sS0;
+      f32x4 acc = tile_rows<F32, VP>(A + (i0 + lo) * SV, Bt + (c0 + lo) * SV, zero4());
+      const int64_t off = which == 0 ? GL::DQG : which == 1 ? GL::DKD : GL::DW;
+      const float sg = which == 2 ? -1.f : 1.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) put(off + (i0 + 4 * grp + r) * DK + c0 + lo, sg * acc[r]);
+    }
   }
 }
 
@@ -695,11 +719,15 @@ struct BIntraCfg {
   static constexpr int NPART = NTH / DK, RPP = C / NPART;       // scans: row parts per channel
   static constexpr int NL = (NTH / C < C) ? NTH / C : C;        // lanes per column of the inverse
   static constexpr int SG = DK + 4, SK = DK + 16 / ES, SV = DV + 16 / ES, SM = C + 4;
+  // q and v staged in LDS where they fit beside the rest (fp32 at d_k = 128, chunk 64: read from
+  // global memory where they are used instead)
+  static constexpr int REST = C * SG * 4 + C * SK * ES + 4 * C * SM * 4 + 2 * C * 4 + (C / 16 + NPART + 1) * DK * 4;
+  static constexpr bool QV_LDS = REST + C * SK * ES + C * SV * ES <= 160 * 1024;
   static constexpr int OFF_G = 0;                                // f32 [C][SG]  g, G, then dG
   static constexpr int OFF_K = OFF_G + C * SG * 4;               // E [C][SK]
-  static constexpr int OFF_Q = OFF_K + C * SK * ES;              // E [C][SK]
-  static constexpr int OFF_V = OFF_Q + C * SK * ES;              // E [C][SV]
-  static constexpr int OFF_EKK = OFF_V + C * SV * ES;            // f32 [C][SM] Ekk (strict lower)
+  static constexpr int OFF_Q = OFF_K + C * SK * ES;              // E [C][SK] (QV_LDS)
+  static constexpr int OFF_V = OFF_Q + (QV_LDS ? C * SK * ES : 0);       // E [C][SV] (QV_LDS)
+  static constexpr int OFF_EKK = OFF_V + (QV_LDS ? C * SV * ES : 0);     // f32 [C][SM] Ekk (strict lower)
   static constexpr int OFF_L = OFF_EKK + C * SM * 4;             // f32 [C][SM] L = (I + A)^{-1}
   static constexpr int OFF_M3 = OFF_L + C * SM * 4;              // f32 [C][SM] dT -> dL -> dA -> dEkk
   static constexpr int OFF_M4 = OFF_M3 + C * SM * 4;             // f32 [C][SM] L^T dL, then dEqk
@@ -712,6 +740,7 @@ struct BIntraCfg {
   static_assert(NPART * DK == NTH && RPP * NPART == C && NL * C <= NTH, "thread layout");
   static_assert((C * SK * ES) % 16 == 0 && (C * SV * ES) % 16 == 0, "alignment");
   static_assert(TOTAL <= 160 * 1024, "LDS");
+  static_assert(TOTAL == REST + (QV_LDS ? C * SK * ES + C * SV * ES : 0), "layout");
 };
 
 // (b, a) of the a-th ... pair index t over the lower triangle of tiles, a <= b
@@ -787,27 +816,40 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     const int r = (8 * e) / DK, c = 8 * e - r * DK;
     const bool ok = r < nr;
     const int64_t gi = (row0 + (int64_t)(ok ? r : 0) * H) * DK + c;
-    copy8<F32>(p.q, gi, sQ + r * SK + c, true);
+    if constexpr (Cf::QV_LDS) copy8<F32>(p.q, gi, sQ + r * SK + c, true);
     copy8<F32>(p.k, gi, sK + r * SK + c, true);
     copy8f<F32>(p.g, gi, sG + r * SG + c, ok);
   });
-  for_units<C * DV / 8, NTH>(tid, [&](int e) {
-    const int r = (8 * e) / DV, j = 8 * e - r * DV;
-    copy8<F32>(p.v, (row0 + (int64_t)(r < nr ? r : 0) * H) * DV + j, sV + r * SV + j, true);
-  });
+  if constexpr (Cf::QV_LDS) {
+    for_units<C * DV / 8, NTH>(tid, [&](int e) {
+      const int r = (8 * e) / DV, j = 8 * e - r * DV;
+      copy8<F32>(p.v, (row0 + (int64_t)(r < nr ? r : 0) * H) * DV + j, sV + r * SV + j, true);
+    });
+  }
   if (nr < C) {  // the same threads overwrite the rows past the end with zeros
     for_units<C * DK / 8, NTH>(tid, [&](int e) {
       const int r = (8 * e) / DK, c = 8 * e - r * DK;
       if (r >= nr) {
-        zero8<F32>(sQ + r * SK + c);
+        if constexpr (Cf::QV_LDS) zero8<F32>(sQ + r * SK + c);
         zero8<F32>(sK + r * SK + c);
       }
     });
-    for_units<C * DV / 8, NTH>(tid, [&](int e) {
-      const int r = (8 * e) / DV, j = 8 * e - r * DV;
-      if (r >= nr) zero8<F32>(sV + r * SV + j);
-    });
+    if constexpr (Cf::QV_LDS) {
+      for_units<C * DV / 8, NTH>(tid, [&](int e) {
+        const int r = (8 * e) / DV, j = 8 * e - r * DV;
+        if (r >= nr) zero8<F32>(sV + r * SV + j);
+      });
+    }
   }
+  // q[r][c] and v[r][j] of the chunk (zero past its end): from LDS, or from global memory
+  auto q_at = [&](int r, int c) -> float {
+    if constexpr (Cf::QV_LDS) return tf(sQ[r * SK + c]);
+    else return r < nr ? ldg<F32>(p.q, (row0 + (int64_t)r * H) * DK + c) : 0.f;
+  };
+  auto v_at = [&](int r, int j) -> float {
+    if constexpr (Cf::QV_LDS) return tf(sV[r * SV + j]);
+    else return r < nr ? ldg<F32>(p.v, (row0 + (int64_t)r * H) * DV + j) : 0.f;
+  };
   if (tid < C) sBeta[tid] = tid < nr ? ldg<F32>(p.beta, row0 + (int64_t)tid * H) : 0.f;
   __syncthreads();
   scan_rows<DK, C, Cf::NPART, Cf::RPP, false>(sG, SG, sScan, tid);
@@ -877,7 +919,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
                                  [&](int k, int n) { return tf(sK[(i0 + n) * SK + k]) * __expf(sG[(i0 + n) * SG + k]); },
                                  zero4());
     acc = tile_mm<F32, DV, true>([&](int m, int k) { return gr[GL::DU + (r0 + m) * DV + k]; },
-                           [&](int k, int n) { return tf(sV[(i0 + n) * SV + k]); }, acc);
+                           [&](int k, int n) { return v_at(i0 + n, k); }, acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = r0 + 4 * grp + r, col = i0 + lo;
@@ -1023,7 +1065,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
       if constexpr (F32) {
         const int r = r0 + O::kidx(s, grp, 0);
         const float e = __expf(sG[r * SG + c] - R2);
-        d3 = O::mma(sM4[r * SM + r0 + lo], tf(sQ[r * SK + c]) * e, d3);
+        d3 = O::mma(sM4[r * SM + r0 + lo], q_at(r, c) * e, d3);
         d3 = O::mma(sM3[r * SM + r0 + lo], tf(sK[r * SK + c]) * e, d3);
       } else {
         Frag fb1, fb1l, fb2, fb2l, fa1, fa1l, fa2, fa2l;
@@ -1049,7 +1091,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = r0 + 4 * grp + r;
-      const float G = sG[i * SG + c], qv = tf(sQ[i * SK + c]), kv = tf(sK[i * SK + c]);
+      const float G = sG[i * SG + c], qv = q_at(i, c), kv = tf(sK[i * SK + c]);
       const float f = __expf(G - R), f2 = __expf(R2 - G);
       const float dqe = d1[r] * f, dkr = d2[r] * f, dkc = d3[r] * f2;
       aq[q][r] += dqe;
@@ -1070,7 +1112,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     for (int r = 0; r < 4; ++r) {
       const int i = r0 + 4 * grp + r;
       const float G = sG[i * SG + c], gam = __expf(G), dec = __expf(gl - G);
-      const float qv = tf(sQ[i * SK + c]), kv = tf(sK[i * SK + c]);
+      const float qv = q_at(i, c), kv = tf(sK[i * SK + c]);
       const float dqg = gr[GL::DQG + i * DK + c], dkd = gr[GL::DKD + i * DK + c];
       aq[q][r] = fmaf(dqg, gam, aq[q][r]);
       ag[q][r] = fmaf(dqg * qv, gam, ag[q][r]);
@@ -1122,7 +1164,10 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   X(false, 64, 128, 16) X(false, 64, 128, 32) X(false, 64, 128, 64)                             \
   X(false, 128, 64, 16) X(false, 128, 64, 32) X(false, 128, 64, 64)                             \
   X(false, 128, 128, 16) X(false, 128, 128, 32) X(false, 128, 128, 64)                          \
-  X(true, 64, 64, 16) X(true, 64, 64, 32) X(true, 64, 64, 64)
+  X(true, 64, 64, 16) X(true, 64, 64, 32) X(true, 64, 64, 64)                                   \
+  X(true, 64, 128, 16) X(true, 64, 128, 32) X(true, 64, 128, 64)                                \
+  X(true, 128, 64, 16) X(true, 128, 64, 32) X(true, 128, 64, 64)                                \
+  X(true, 128, 128, 16) X(true, 128, 128, 32) X(true, 128, 128, 64)
 
 bool chunked_backward_supported(bool f32, int dk, int dv, int chunk) {
 #define KDA_SUP(F, D, V, CC) \

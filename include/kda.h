@@ -312,9 +312,8 @@ kda_status kda_decode_step_fused(const void* q, const void* k, const void* v, co
  * h0 NULL = zero start) and
  *   d_o [B,T,H,d_v] (dtype dt), dhT [B,H,d_k,d_v] fp32 (NULL = zero)    in
  * The forward is recomputed inside the call (nothing is kept from an earlier
- * forward call).  Supported: bf16 with d_k, d_v in {64, 128}; fp32 with
- * d_k = d_v = 64; chunk in {16, 32, 64}; anything else returns
- * KDA_ERR_UNSUPPORTED.  workspace: kda_chunked_backward_workspace_bytes(...)
+ * forward call).  Supported: bf16 or fp32 with d_k, d_v in {64, 128}; chunk
+ * in {16, 32, 64}; anything else returns KDA_ERR_UNSUPPORTED.  workspace: kda_chunked_backward_workspace_bytes(...)
  * bytes, 256-byte aligned, caller-owned (it holds the recomputed per-chunk
  * records and states and the adjoint states).  Every output is written, none
  * is read; outputs must not overlap inputs.  Invalid calls return an error

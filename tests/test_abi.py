@@ -265,7 +265,7 @@ def test_backward_workspace_and_validation():
             + al(B * T * H * D * 2))
     assert lib.kda_chunked_backward_workspace_bytes(B, T, H, D, D, C, 1) == want
     assert lib.kda_chunked_backward_workspace_bytes(1, 100, 2, 128, 128, 48, 1) == 0  # unsupported chunk
-    assert lib.kda_chunked_backward_workspace_bytes(1, 100, 2, 128, 128, 64, 0) == 0  # fp32 only at d = 64
+    assert lib.kda_chunked_backward_workspace_bytes(1, 100, 2, 128, 128, 64, 0) > 0  # fp32 at every d
     assert lib.kda_chunked_backward_workspace_bytes(1, 100, 2, 64, 64, 64, 0) > 0
     fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every call below fails validation
     a = [fake] * 5 + [None, fake, None] + [fake] * 5 + [None]
@@ -275,7 +275,7 @@ def test_backward_workspace_and_validation():
 
     assert call(a, chunk=48) == UNSUPPORTED
     assert call(a, dk=96) == UNSUPPORTED
-    assert call(a, dt=0) == UNSUPPORTED                     # fp32 with d = 128
+    assert call(a, dt=0) == 3                               # fp32 with d = 128: supported, no workspace
     assert call(a, B=-1) == INVALID
     assert call(a, dt=5) == INVALID
     bad = list(a)
@@ -305,7 +305,7 @@ def test_backward_varlen_workspace_and_validation():
     want = fwd + 2 * al(mc * H * D * D * 4) + al(mc * H * grad * 4) + al(Tt * H * D * 2)
     assert lib.kda_chunked_backward_varlen_workspace_bytes(N, Tt, maxlen, H, D, D, C, 1) == want
     assert lib.kda_chunked_backward_varlen_workspace_bytes(N, Tt, maxlen, H, D, D, 48, 1) == 0
-    assert lib.kda_chunked_backward_varlen_workspace_bytes(N, Tt, maxlen, H, D, D, C, 0) == 0  # fp32 only at d = 64
+    assert lib.kda_chunked_backward_varlen_workspace_bytes(N, Tt, maxlen, H, D, D, C, 0) > 0
     assert lib.kda_chunked_backward_varlen_workspace_bytes(N, Tt, maxlen, H, 64, 64, C, 0) > 0
     assert lib.kda_chunked_backward_varlen_workspace_bytes(0, Tt, maxlen, H, D, D, C, 1) == 0
     fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every call below fails validation
@@ -316,7 +316,7 @@ def test_backward_varlen_workspace_and_validation():
 
     assert call(a, chunk=48) == UNSUPPORTED
     assert call(a, dk=96) == UNSUPPORTED
-    assert call(a, dt=0) == UNSUPPORTED                     # fp32 with d = 128
+    assert call(a, dt=0) == 3                               # fp32 with d = 128: supported, no workspace
     assert call(a, N=-1) == INVALID
     assert call(a, maxlen=1001) == INVALID                  # longer than T_total
     assert call(a, dt=5) == INVALID

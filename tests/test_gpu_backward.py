@@ -57,6 +57,15 @@ def test_backward_fp32(chunk, T):
     run_case(920 + chunk + T, 1, T, 2, 64, 64, F32, chunk, label="fp32")
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 64), (64, 128)])
+@pytest.mark.parametrize("chunk", [64, 32, 16])
+def test_backward_fp32_d128(dk, dv, chunk):
+    """fp32 with a 128-wide dimension: the state products take the value columns in passes (the
+    LDS holds half or a quarter of them), and at d_k = 128, chunk 64, the transform reads q and v
+    from global memory where it uses them."""
+    run_case(985 + dk + dv + chunk, 2, 3 * chunk + 11, 2, dk, dv, F32, chunk, label="fp32 d128")
+
+
 def test_backward_without_h0_and_dhT():
     run_case(930, 2, 130, 2, 128, 128, BF16, 64, h0_std=None, dhT_std=None, label="no h0/dhT")
 

@@ -84,7 +84,8 @@ def check_sequences(d, do, h0, dhT, cu, got, dt, seqs=None):
 
 
 @pytest.mark.parametrize("dt,dk,dv,chunk", [(BF16, 128, 128, 64), (BF16, 128, 128, 16), (BF16, 64, 128, 32),
-                                            (F32, 64, 64, 64), (F32, 64, 64, 16)])
+                                            (F32, 64, 64, 64), (F32, 64, 64, 16), (F32, 128, 128, 64),
+                                            (F32, 128, 64, 32)])
 def test_backward_varlen_against_oracle(dt, dk, dv, chunk):
     """Ten sequences: empty; 1, 2, 3, 5 and 8 tokens (19 pooled short tokens per head with bf16);
     one short of a chunk; one chunk; several chunks with a ragged tail; another empty one."""
