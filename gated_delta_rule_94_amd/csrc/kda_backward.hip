@@ -717,7 +717,6 @@ struct BIntraCfg {
   static constexpr int NTC = C / 16, NTK = DK / 16, NTV = DV / 16;
   static constexpr int NTILE = NTC * NTK, MAXT = (NTILE + 7) / 8, NPAIR = NTC * (NTC + 1) / 2;
   static constexpr int NPART = NTH / DK, RPP = C / NPART;       // scans: row parts per channel
-  static constexpr int NL = (NTH / C < C) ? NTH / C : C;        // lanes per column of the inverse
   static constexpr int SG = DK + 4, SK = DK + 16 / ES, SV = DV + 16 / ES, SM = C + 4;
   // q and v staged in LDS where they fit beside the rest (fp32 at d_k = 128, chunk 64: read from
   // global memory where they are used instead)
@@ -737,7 +736,7 @@ struct BIntraCfg {
   static constexpr int OFF_SCAN = OFF_RED + NTC * DK * 4;        // f32 [NPART][DK]
   static constexpr int OFF_DGL = OFF_SCAN + NPART * DK * 4;      // f32 [DK]
   static constexpr int TOTAL = OFF_DGL + DK * 4;
-  static_assert(NPART * DK == NTH && RPP * NPART == C && NL * C <= NTH, "thread layout");
+  static_assert(NPART * DK == NTH && RPP * NPART == C && 64 * NTC <= NTH, "thread layout");
   static_assert((C * SK * ES) % 16 == 0 && (C * SV * ES) % 16 == 0, "alignment");
   static_assert(TOTAL <= 160 * 1024, "LDS");
   static_assert(TOTAL == REST + (QV_LDS ? C * SK * ES + C * SV * ES : 0), "layout");
@@ -785,7 +784,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   using O = Op<F32>;
   using Frag = typename O::Frag;
   using GL = GradLayout<DK, DV, C>;
-  constexpr int NTK = Cf::NTK, NTV = Cf::NTV, NTILE = Cf::NTILE, MAXT = Cf::MAXT, NL = Cf::NL;
+  constexpr int NTK = Cf::NTK, NTV = Cf::NTV, NTILE = Cf::NTILE, MAXT = Cf::MAXT;
   constexpr int SG = Cf::SG, SK = Cf::SK, SV = Cf::SV, SM = Cf::SM, NTH = Cf::NTH;
   __shared__ __align__(16) unsigned char smem[Cf::TOTAL];
   float* sG = reinterpret_cast<float*>(smem + Cf::OFF_G);
@@ -876,37 +875,62 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  // ---- L = (I + A)^{-1}, A = diag(beta) Ekk: column j by forward substitution, NL lanes per column,
-  // lane u holding rows u + NL m
-  if (tid < C * NL) {
-    // At step r only rows below r are known (x of every later row is still 0) and Ekk is strictly
-    // lower, so the sum runs over m <= r / NL; row r + 1 is read from LDS during step r.
-    constexpr int NM = C / NL;
-    const int j = tid / NL, u = tid - j * NL;
-    float x[NM], cur[NM], nxt[NM];
+  // ---- L = (I + A)^{-1}, A = diag(beta) Ekk (strictly lower), in 16x16 blocks: the diagonal blocks
+  // by forward substitution, one wave each (one column per lane); then, one wave per column block a,
+  // the blocks below it in order, L_ba = -L_bb sum_{c=a}^{b-1} A_bc L_ca, on fp32 MFMA -- 16
+  // dependent substitution steps instead of C.  Blocks above the diagonal are zero.
+  constexpr int NTC = Cf::NTC;
+  if (wave < NTC) {
+    const int b = wave, j = lo;
+    float x[16];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      x[m] = 0.f;
-      cur[m] = sEkk[u + NL * m];
-      nxt[m] = 0.f;
-    }
-#pragma unroll
-    for (int r = 0; r < C; ++r) {
-      if (r + 1 < C) {
-#pragma unroll
-        for (int m = 0; m <= (r + 1) / NL && m < NM; ++m) nxt[m] = sEkk[(r + 1) * SM + u + NL * m];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float* arow = sEkk + (16 * b + r) * SM + 16 * b;
       float s = 0.f;
 #pragma unroll
-      for (int m = 0; m <= r / NL; ++m) s = fmaf(cur[m], x[m], s);
-      s = group_sum<NL>(s);
-      const float val = (r == j) ? 1.f : -sBeta[r] * s;
-      if (u == (r % NL)) x[r / NL] = val;
-#pragma unroll
-      for (int m = 0; m < NM; ++m) cur[m] = nxt[m];
+      for (int i = 0; i < r; ++i) s = fmaf(arow[i], x[i], s);
+      x[r] = (r == j ? 1.f : 0.f) - sBeta[16 * b + r] * s;
     }
+    if (grp == 0) {
 #pragma unroll
-    for (int m = 0; m < C / NL; ++m) sL[(u + NL * m) * SM + j] = x[m];
+      for (int r = 0; r < 16; ++r) sL[(16 * b + r) * SM + 16 * b + j] = x[r];
+    }
+  } else {
+    for (int e = tid - 64 * NTC; e < C * C; e += NTH - 64 * NTC) {
+      const int r = e / C, i = e - r * C;
+      if ((i >> 4) > (r >> 4)) sL[r * SM + i] = 0.f;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a + 1 < NTC; ++a) {
+    if (wave != a) continue;
+    float Xb[NTC][4];  // Xb[c][r] = L_ca[4 grp + r][lo] (accumulator order)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Xb[a][r] = sL[(16 * a + 4 * grp + r) * SM + 16 * a + lo];
+#pragma unroll
+    for (int b = a + 1; b < NTC; ++b) {
+      f32x4 z = zero4();
+      const float bb = sBeta[16 * b + lo];
+#pragma unroll
+      for (int c = a; c < b; ++c) {
+        const float4 e4 = *reinterpret_cast<const float4*>(sEkk + (16 * b + lo) * SM + 16 * c + 4 * grp);
+        const float av[4] = {bb * e4.x, bb * e4.y, bb * e4.z, bb * e4.w};
+        z = mma16<true>(av, Xb[c], z);
+      }
+      float lv[4], zb[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        lv[r] = -sL[(16 * b + lo) * SM + 16 * b + 4 * grp + r];
+        zb[r] = z[r];
+      }
+      const f32x4 xv = mma16<true>(lv, zb, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        Xb[b][r] = xv[r];
+        sL[(16 * b + 4 * grp + r) * SM + 16 * a + lo] = xv[r];
+      }
+    }
   }
   __syncthreads();
 
