@@ -113,6 +113,28 @@ struct IntraCfg {
 // index of sub-tile pair (b, a), b >= a + 2 (chunks of 64 only): (2,0) -> 0, (3,0) -> 1, (3,1) -> 2
 __device__ __forceinline__ constexpr int gap_index(int b, int a) { return (b == 2) ? 0 : (a == 0 ? 1 : 2); }
 
+// sub-tile pair q of the lower triangle, pairs ordered by row b then column a <= b: (0,0), (1,0),
+// (1,1), (2,0), ...
+__host__ __device__ constexpr int pair_row(int q) {
+  int b = 0;
+  while (q > b) {
+    q -= b + 1;
+    ++b;
+  }
+  return b;
+}
+__host__ __device__ constexpr int pair_col(int q) { return q - pair_row(q) * (pair_row(q) + 1) / 2; }
+
+// f(integral_constant<int, I>) for I = 0 .. N-1: a loop whose index is a compile-time constant in
+// the body (the tile pairs' sub-tiles and LDS offsets then fold into immediates)
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // x as bf16 hi + lo (hi = bf16(x), lo = bf16(x - hi)), or x itself for fp32 operands
 template <bool F32>
 __device__ __forceinline__ void st2_split(void* hi, void* lo, float a, float b) {
@@ -286,14 +308,14 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   float* Bet = reinterpret_cast<float*>(smem + Cf::OFF_BETA);
 
   const int tid = threadIdx.x, lane = tid & 63, lo = lane & 15, grp = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave work is a scalar branch
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 7;  // wave-uniform: per-wave work is a scalar branch
   const int H = p.H;
   // prep unit of this thread: 2 consecutive rows (a row pair of one 16-row sub-tile) x 2 NQ
   // consecutive channels, one channel pair in every quarter of the key dimension.  The 8 row pairs
   // of a sub-tile are 8 consecutive lanes, so prefix products over the sub-tile are an 8-lane
   // scan; every quarter's operands are then built by all threads.
   const int rp = tid & 7, cpl = (tid >> 3) & 15;
-  const int psb = __builtin_amdgcn_readfirstlane(tid >> 7);  // sub-tile: uniform over a wave
+  const int psb = __builtin_amdgcn_readfirstlane(tid >> 7) & 3;  // sub-tile: uniform over a wave
   const bool pact = psb < NT;
   const int r0 = 16 * psb + 2 * rp;  // rows r0, r0 + 1; channels chan(qt) (+1) in quarter qt
   // value unit of this thread
@@ -393,8 +415,11 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
     if constexpr (MX) return mx_decode2(mv[i], sv[i], false);
     else return rv[i].f();
   };
-  E* rec = reinterpret_cast<E*>(p.ws + (int64_t)item * R::BYTES);
-  float* rgam = reinterpret_cast<float*>(p.ws + (int64_t)item * R::BYTES + R::GAM_BYTE);
+  unsigned char* rec0 = p.ws + (int64_t)item * R::BYTES;  // wave-uniform
+  float* rgam = reinterpret_cast<float*>(rec0 + R::GAM_BYTE);
+  // element e of the record: the wave-uniform base plus a 32-bit per-lane offset, so that the stores
+  // address from a scalar base instead of forming 64-bit lane addresses
+  auto recp = [&](uint32_t e) -> E* { return reinterpret_cast<E*>(rec0 + e * (uint32_t)sizeof(E)); };
 
   // ---------------- per quarter of the key dimension, pipelined so that the later quarters' loads
   // arrive while the earlier ones compute:
@@ -466,7 +491,7 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   if constexpr (CP > C) {  // token pads of K'^T and (K . Gamma)^T are zero
     for (int e = tid; e < DK * (CP - C); e += 512) {
       const int c = e / (CP - C), t = C + e % (CP - C);
-      rec[R::KPT + c * CP + t] = (E)0.f;
+      *recp(R::KPT + c * CP + t) = (E)0.f;
       KGt[c * TS + t] = (E)0.f;
     }
   }
@@ -536,11 +561,11 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
           }
           if constexpr (F32) qgf[j][qt] = make_float2(qg[j][0], qg[j][1]);
           else qgw[j][qt] = pack_bf16x2(qg[j][0], qg[j][1]);
-          if (qt == NQ - 1) store_group<F32, NQ>(rec + R::QG + (r0 + j) * DK + 2 * NQ * cpl, qgw[j], qgf[j]);
+          if (qt == NQ - 1) store_group<F32, NQ>(recp(R::QG + (r0 + j) * DK + 2 * NQ * cpl), qgw[j], qgf[j]);
         }
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-          st2<F32>(rec + R::KPT + (c0 + ch) * CP + r0, kp[0][ch], kp[1][ch]);
+          st2<F32>(recp(R::KPT + (c0 + ch) * CP + r0), kp[0][ch], kp[1][ch]);
           st2<F32>(KGt + (c0 + ch) * TS + r0, kg[0][ch], kg[1][ch]);
         }
       }
@@ -588,16 +613,13 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
     if (qt + 1 < NQ) scan(qt + 1 < NQ ? qt + 1 : qt, Ef, Tb);
     // tile pairs spread over the waves; each product M^T[a-cols][b-rows] holds, per lane, row
     // r = 16 b + lo and four consecutive columns i = 16 a + 4 grp + j
-#pragma unroll
-    for (int pi = 0; pi < 2 * NPAIR; ++pi) {
-      if ((pi & 7) != wave) continue;
-      const bool qk = pi >= NPAIR;
-      int qq = qk ? pi - NPAIR : pi;
-      int b = 0;
-      while (qq > b) { qq -= b + 1; ++b; }
-      const int a = qq;
+    static_for<0, 2 * NPAIR>([&](auto pic) {
+      constexpr int pi = decltype(pic)::value;
+      if ((pi & 7) != wave) return;
+      constexpr bool qk = pi >= NPAIR;
+      constexpr int b = pair_row(qk ? pi - NPAIR : pi), a = pair_col(qk ? pi - NPAIR : pi);
       const int rr = (16 * b + lo) * QS;
-      const bool gap = b >= a + 2;
+      constexpr bool gap = b >= a + 2;
       const E* ch = gap ? gapt(gap_index(b, a), 0) + lo * QS : opnd(a == b ? 2 : 3, 0) + (16 * a + lo) * QS;
       const E* cl_ = gap ? gapt(gap_index(b, a), SPLIT) + lo * QS : opnd(a == b ? 2 : 3, SPLIT) + (16 * a + lo) * QS;
       const E* rh = opnd(qk ? 0 : 1, 0) + rr;
@@ -613,7 +635,7 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
         }
       }
       acc[pi >> 3] = c;
-    }
+    });
     if (qt == NQ - 1) {
       // beta and V^T (for A, T and the U~ product) last: they were loaded last
       if (tid < C) Bet[tid] = rb;
@@ -633,31 +655,28 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   }
 
   // ---------------- M_kk -> A (fp32, LDS, strictly lower, rows scaled by beta); M_qk -> P (record)
-#pragma unroll
-  for (int pi = 0; pi < 2 * NPAIR; ++pi) {
-    if ((pi & 7) != wave) continue;
-    const bool qk = pi >= NPAIR;
-    int qq = qk ? pi - NPAIR : pi;
-    int b = 0;
-    while (qq > b) { qq -= b + 1; ++b; }
-    const int a = qq;
+  static_for<0, 2 * NPAIR>([&](auto pic) {
+    constexpr int pi = decltype(pic)::value;
+    if ((pi & 7) != wave) return;
+    constexpr bool qk = pi >= NPAIR;
+    constexpr int b = pair_row(qk ? pi - NPAIR : pi), a = pair_col(qk ? pi - NPAIR : pi);
     const int row = 16 * b + lo, col = 16 * a + 4 * grp;
     const f32x4 m = acc[pi >> 3];
-    if (!qk) {
+    if constexpr (!qk) {
       const float bt = Bet[row];
       *reinterpret_cast<float4*>(As + row * AS + col) =
           make_float4(row > col ? bt * m[0] : 0.f, row > col + 1 ? bt * m[1] : 0.f, row > col + 2 ? bt * m[2] : 0.f,
                       row > col + 3 ? bt * m[3] : 0.f);
     } else {
-      st4<F32>(rec + R::P + row * CP + col, row >= col ? m[0] : 0.f, row >= col + 1 ? m[1] : 0.f,
+      st4<F32>(recp(R::P + row * CP + col), row >= col ? m[0] : 0.f, row >= col + 1 ? m[1] : 0.f,
                row >= col + 2 ? m[2] : 0.f, row >= col + 3 ? m[3] : 0.f);
     }
-  }
+  });
   // tiles above the diagonal that the chain's 32-deep token steps read: zero
   if constexpr (!F32) {
     for (int e = tid; e < C * 16; e += 512) {
       const int row = e >> 4, b = row >> 4;
-      if ((b & 1) == 0 && 16 * (b + 1) < CP) rec[R::P + row * CP + 16 * (b + 1) + (e & 15)] = (E)0.f;
+      if ((b & 1) == 0 && 16 * (b + 1) < CP) *recp(R::P + row * CP + 16 * (b + 1) + (e & 15)) = (E)0.f;
     }
   }
   __syncthreads();
@@ -738,11 +757,11 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
         if (isw) {
 #pragma unroll
           for (int s = 0; s < O::nks(16 * (b + 1)); ++s) acc2 = O::mma(O::ld(brow, s, grp), O::ld(trow, s, grp), acc2);
-          st4<F32>(rec + R::NW + (16 * b + lo) * DK + 16 * n16 + 4 * grp, -acc2[0], -acc2[1], -acc2[2], -acc2[3]);
+          st4<F32>(recp(R::NW + (16 * b + lo) * DK + 16 * n16 + 4 * grp), -acc2[0], -acc2[1], -acc2[2], -acc2[3]);
         } else {
 #pragma unroll
           for (int s = 0; s < O::nks(16 * (b + 1)); ++s) acc2 = O::mma(O::ld(trow, s, grp), O::ld(brow, s, grp), acc2);
-          st4<F32>(rec + R::UT + (16 * n16 + lo) * C + 16 * b + 4 * grp, acc2[0], acc2[1], acc2[2], acc2[3]);
+          st4<F32>(recp(R::UT + (16 * n16 + lo) * C + 16 * b + 4 * grp), acc2[0], acc2[1], acc2[2], acc2[3]);
         }
       }
     }
