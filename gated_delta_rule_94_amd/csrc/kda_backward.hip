@@ -73,6 +73,23 @@ __device__ __forceinline__ float tf(E x) {
   return (float)x;
 }
 
+// Element i of a wave-uniform base with a 32-bit offset: the access addresses from a scalar base
+// plus a 32-bit lane offset instead of forming a 64-bit address in every lane.
+template <typename T>
+__device__ __forceinline__ T& at(T* base, uint32_t i) {
+  return *reinterpret_cast<T*>(reinterpret_cast<unsigned char*>(base) + (uint32_t)sizeof(T) * i);
+}
+template <typename T>
+__device__ __forceinline__ const T& at(const T* base, uint32_t i) {
+  return *reinterpret_cast<const T*>(reinterpret_cast<const unsigned char*>(base) + (uint32_t)sizeof(T) * i);
+}
+// an output element (operand type) at element offset i of a wave-uniform base
+template <bool F32>
+__device__ __forceinline__ void stg_at(void* base, uint32_t i, float x) {
+  if constexpr (F32) at(static_cast<float*>(base), i) = x;
+  else at(static_cast<uint16_t*>(base), i) = f32_to_bf16_bits(x);
+}
+
 // Token span [a, b) of (sequence, head) unit's sequence n, and its first chunk: equal lengths, or a
 // packed sequence with its offsets clamped to [0, T_total] as the forward's chunk map clamps them.
 __device__ __forceinline__ void seq_span(const BwdParams& p, int n, int64_t& a, int64_t& b, int64_t& first) {
@@ -594,7 +611,7 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
   for (int vp0 = 0; vp0 < DV; vp0 += VP) {
     // a sum over the value columns: the first pass writes it, later ones add their share (each
     // element has one owner thread in every pass)
-    auto put = [&](int64_t i, float x) { gr[i] = vp0 == 0 ? x : gr[i] + x; };
+    auto put = [&](uint32_t i, float x) { at(gr, i) = vp0 == 0 ? x : at(gr, i) + x; };
     if (vp0 > 0) __syncthreads();  // the previous pass's reads of every LDS region are done
     // columns [vp0, vp0 + VP) of S0 (zeros without one) and dS1 to LDS; the branch on S0's presence
     // is taken once for the workgroup, so no load sits under a per-element select
@@ -673,7 +690,7 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         sdU[(i0 + 4 * grp + r) * SV + j0 + lo] = (E)acc[r];
-        gr[GL::DU + (i0 + 4 * grp + r) * DV + vp0 + j0 + lo] = acc[r];
+        at(gr, GL::DU + (i0 + 4 * grp + r) * DV + vp0 + j0 + lo) = acc[r];
       }
     }
     __syncthreads();
@@ -807,6 +824,13 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   const BItem it = locate<C>(p, item);
   const int h = it.h, nr = it.len;
   const int64_t row0 = it.tok0 * H + h;  // (token, head) row of the chunk's first token
+  // wave-uniform bases of the chunk's rows in the outputs (32-bit element offsets from them)
+  constexpr int ES_ = F32 ? 4 : 2;
+  void* dqb = static_cast<unsigned char*>(p.dq) + row0 * DK * ES_;
+  void* dkb = static_cast<unsigned char*>(p.dk) + row0 * DK * ES_;
+  void* dgb = static_cast<unsigned char*>(p.dg) + row0 * DK * ES_;
+  void* dvb = static_cast<unsigned char*>(p.dv) + row0 * DV * ES_;
+  void* dbb = static_cast<unsigned char*>(p.dbeta) + row0 * ES_;
   const float* gr = p.grads + item * GL::FLOATS;
 
   // ---- stage q, k, v, g, beta, 8 consecutive channels per access (rows past the chunk's end read
@@ -939,10 +963,10 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     int tb, ta;
     tri_pair(t, tb, ta);
     const int r0 = 16 * tb, i0 = 16 * ta;
-    f32x4 acc = tile_mm<F32, DK, true>([&](int m, int k) { return gr[GL::DW + (r0 + m) * DK + k]; },
+    f32x4 acc = tile_mm<F32, DK, true>([&](int m, int k) { return at(gr, GL::DW + (r0 + m) * DK + k); },
                                  [&](int k, int n) { return tf(sK[(i0 + n) * SK + k]) * __expf(sG[(i0 + n) * SG + k]); },
                                  zero4());
-    acc = tile_mm<F32, DV, true>([&](int m, int k) { return gr[GL::DU + (r0 + m) * DV + k]; },
+    acc = tile_mm<F32, DV, true>([&](int m, int k) { return at(gr, GL::DU + (r0 + m) * DV + k); },
                            [&](int k, int n) { return v_at(i0 + n, k); }, acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -966,7 +990,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     if (t < NTILE) {
       const int i0 = 16 * (t / NTK), c0 = 16 * (t % NTK);
       const f32x4 d = tile_mm<F32, C, true>([&](int m, int k) { return sL[k * SM + i0 + m] * sBeta[i0 + m]; },
-                                            [&](int k, int n) { return gr[GL::DW + k * DK + c0 + n]; }, zero4());
+                                            [&](int k, int n) { return at(gr, GL::DW + k * DK + c0 + n); }, zero4());
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + 4 * grp + r, c = c0 + lo;
@@ -980,11 +1004,11 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   for (int t = wave; t < Cf::NTC * NTV; t += 8) {
     const int i0 = 16 * (t / NTV), j0 = 16 * (t % NTV);
     const f32x4 d = tile_mm<F32, C, true>([&](int m, int k) { return sL[k * SM + i0 + m] * sBeta[i0 + m]; },
-                                          [&](int k, int n) { return gr[GL::DU + k * DV + j0 + n]; }, zero4());
+                                          [&](int k, int n) { return at(gr, GL::DU + k * DV + j0 + n); }, zero4());
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = i0 + 4 * grp + r;
-      if (i < nr) stg<F32>(p.dv, (row0 + (int64_t)i * H) * DV + j0 + lo, d[r]);
+      if (i < nr) stg_at<F32>(dvb, (uint32_t)(i * H * DV + j0 + lo), d[r]);
     }
   }
   __syncthreads();
@@ -1037,7 +1061,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
       sM3[r * SM + i] = sBeta[r] * da;
     }
     s = group_sum<NPC>(s);
-    if (u == 0 && r < nr) stg<F32>(p.dbeta, row0 + (int64_t)r * H, sDb[r] + s);
+    if (u == 0 && r < nr) stg_at<F32>(dbb, (uint32_t)(r * H), sDb[r] + s);
   }
   for_units<C * C / 4, NTH>(tid, [&](int e) {  // 4 floats per access (records of grads are 256-byte aligned)
     const int r = (4 * e) / C, i = 4 * e - r * C;
@@ -1137,7 +1161,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
       const int i = r0 + 4 * grp + r;
       const float G = sG[i * SG + c], gam = __expf(G), dec = __expf(gl - G);
       const float qv = q_at(i, c), kv = tf(sK[i * SK + c]);
-      const float dqg = gr[GL::DQG + i * DK + c], dkd = gr[GL::DKD + i * DK + c];
+      const float dqg = at(gr, GL::DQG + i * DK + c), dkd = at(gr, GL::DKD + i * DK + c);
       aq[q][r] = fmaf(dqg, gam, aq[q][r]);
       ag[q][r] = fmaf(dqg * qv, gam, ag[q][r]);
       ak[q][r] = fmaf(dkd, dec, ak[q][r]);
@@ -1151,7 +1175,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   }
   __syncthreads();
   if (tid < DK) {
-    float s = gr[GL::DGL + tid];
+    float s = at(gr, GL::DGL + tid);
     for (int o = 0; o < Cf::NTC; ++o) s += sRed[o * DK + tid];
     sDgl[tid] = s;
   }
@@ -1168,8 +1192,8 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
       if (i == C - 1) dg += sDgl[c];
       sG[i * SG + c] = dg;
       if (i < nr) {
-        stg<F32>(p.dq, (row0 + (int64_t)i * H) * DK + c, aq[q][r]);
-        stg<F32>(p.dk, (row0 + (int64_t)i * H) * DK + c, ak[q][r]);
+        stg_at<F32>(dqb, (uint32_t)(i * H * DK + c), aq[q][r]);
+        stg_at<F32>(dkb, (uint32_t)(i * H * DK + c), ak[q][r]);
       }
     }
   }
@@ -1178,7 +1202,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   scan_rows<DK, C, Cf::NPART, Cf::RPP, true>(sG, SG, sScan, tid);
   for (int e = tid; e < C * DK; e += NTH) {
     const int r = e / DK, c = e - r * DK;
-    if (r < nr) stg<F32>(p.dg, (row0 + (int64_t)r * H) * DK + c, sG[r * SG + c]);
+    if (r < nr) stg_at<F32>(dgb, (uint32_t)(r * H * DK + c), sG[r * SG + c]);
   }
 }
 
