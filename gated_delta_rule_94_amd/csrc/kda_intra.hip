@@ -99,12 +99,21 @@ struct IntraCfg {
   static constexpr int OFF_L = al(OFF_A + C * AS * 4);          // fp32 [NT][16][17]
   static constexpr int OFF_T = al(OFF_L + NT * 16 * 17 * 4);    // E [C][TS]
   static constexpr int X_END = OFF_T + C * TS * ES;
+  // Record fields written through LDS as whole rows (16-byte accesses over full cache lines)
+  // instead of 4- or 8-byte pieces straight from the registers: K'^T staged in the V^T area during
+  // the quarters (V^T is written after them) where it fits; U~^T in place over the rows of V^T
+  // that its own wave alone reads; -W over A and the diagonal inverses, dead once T is formed.
+  static constexpr bool KPT_LDS = !F32 && DK <= DV;
+  static constexpr bool UT_LDS = !F32;
+  static constexpr int SW = DK + 4;  // -W rows in LDS
+  static constexpr bool NW_LDS = !F32 && C * SW * ES <= OFF_T;
   // written during prep, read by the W / U~ products
   static constexpr int OFF_KGT = al(mx(M_END, X_END));          // E [DK][TS]  (K . Gamma)^T
   static constexpr int OFF_VT = al(OFF_KGT + DK * TS * ES);     // E [DV][TS]  V^T
   static constexpr int OFF_EEND = al(OFF_VT + DV * TS * ES);    // fp32 [NT][DK] e^{sub-tile total}
   static constexpr int OFF_BETA = al(OFF_EEND + NT * DK * 4);   // fp32 [C]
-  static constexpr int TOTAL = al(OFF_BETA + C * 4);
+  static constexpr int OFF_NRM = al(OFF_BETA + C * 4);           // fp32 [NT][8][4][2] row norms (KPT_LDS)
+  static constexpr int TOTAL = al(OFF_NRM + (KPT_LDS ? NT * 8 * 4 * 2 * 4 : 0));
   static_assert(TOTAL <= 163840, "LDS budget of one gfx950 workgroup");
   // minimum waves per SIMD: two 8-wave workgroups per CU (4 waves per SIMD) where their LDS fits
   static constexpr int MINW = (2 * TOTAL <= 163840) ? 4 : 2;
@@ -221,6 +230,25 @@ __device__ __forceinline__ void store_group(void* dst, const uint32_t (&w)[NQ], 
   }
 }
 
+// ROWS rows of RB bytes each, at a stride of SB bytes in LDS (8-byte aligned), to the contiguous
+// array at dst (16-byte aligned, wave-uniform), 16 bytes per access: consecutive lanes write
+// consecutive 16-byte pieces, so every store covers whole cache lines.
+template <int ROWS, int RB, int SB>
+__device__ __forceinline__ void rows_out(const unsigned char* lds, unsigned char* dst, int tid) {
+  static_assert(RB % 16 == 0 && SB % 8 == 0, "16-byte pieces of 8-byte aligned rows");
+  constexpr int U = RB / 16, N = ROWS * U;
+#pragma unroll
+  for (int k = 0; k < (N + 511) / 512; ++k) {
+    const int u = tid + 512 * k;
+    if (N % 512 == 0 || u < N) {
+      const int r = u / U, pc = u - r * U;
+      const uint2 a = *reinterpret_cast<const uint2*>(lds + r * SB + 16 * pc);
+      const uint2 b = *reinterpret_cast<const uint2*>(lds + r * SB + 16 * pc + 8);
+      *reinterpret_cast<uint4*>(dst + 16u * (uint32_t)u) = make_uint4(a.x, a.y, b.x, b.y);
+    }
+  }
+}
+
 // OCP Microscaling (MX) inputs: a block of 32 consecutive channels shares one E8M0 scale code s,
 // worth 2^(s - 127) (code 255 is NaN); each element is an FP8 E4M3 code.  gfx950 converts a pair of
 // E4M3 codes and multiplies by a float scale in one instruction (checked against the E4M3
@@ -300,6 +328,7 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
     return reinterpret_cast<E*>(smem + Cf::OFF_GAP + (gi * Cf::NPART + part) * Cf::GPB);
   };
   float* As = reinterpret_cast<float*>(smem + Cf::OFF_A);
+  E* Ws = reinterpret_cast<E*>(smem + Cf::OFF_A);  // -W [C][SW] once T is formed (NW_LDS)
   float* Ls = reinterpret_cast<float*>(smem + Cf::OFF_L);
   E* Ts = reinterpret_cast<E*>(smem + Cf::OFF_T);
   E* KGt = reinterpret_cast<E*>(smem + Cf::OFF_KGT);
@@ -465,7 +494,9 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   // with the same row pair (lane bits 3-5) and in the sibling wave (through LDS, in the V^T area,
   // which is first written in the last quarter)
   float qn[2] = {1.f, 1.f}, kn[2] = {1.f, 1.f};
-  float* Nrm = reinterpret_cast<float*>(Vt);  // [sub-tile][row pair][4][2 halves]
+  // [sub-tile][row pair][4][2 halves]; in the V^T area unless K'^T is staged there
+  float* Nrm = reinterpret_cast<float*>(Cf::KPT_LDS ? smem + Cf::OFF_NRM : reinterpret_cast<unsigned char*>(Vt));
+  E* KPs = Vt;  // K'^T [DK][TS] during the quarters (KPT_LDS)
   const bool norm = p.normalize_qk != 0;
   if (norm) {
     float ss[4] = {0.f, 0.f, 0.f, 0.f};  // q row 0, q row 1, k row 0, k row 1
@@ -491,13 +522,28 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
   if constexpr (CP > C) {  // token pads of K'^T and (K . Gamma)^T are zero
     for (int e = tid; e < DK * (CP - C); e += 512) {
       const int c = e / (CP - C), t = C + e % (CP - C);
-      *recp(R::KPT + c * CP + t) = (E)0.f;
+      if constexpr (Cf::KPT_LDS) KPs[c * TS + t] = (E)0.f;
+      else *recp(R::KPT + c * CP + t) = (E)0.f;
       KGt[c * TS + t] = (E)0.f;
     }
   }
   f32x4 acc[NSLOT];
 #pragma unroll
   for (int sl = 0; sl < NSLOT; ++sl) acc[sl] = zero4();
+  // V^T (value unit of this thread: column pair vcp, 8 tokens from 8 vtg) to LDS
+  auto write_vt = [&]() {
+    if (vact) {
+      float x0[8], x1[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float2 vv = vpair(i);
+        x0[i] = vv.x;
+        x1[i] = vv.y;
+      }
+      st8_a8<F32>(Vt + (2 * vcp) * TS + 8 * vtg, x0);
+      st8_a8<F32>(Vt + (2 * vcp + 1) * TS + 8 * vtg, x1);
+    }
+  };
   // Q.Gamma of this thread's rows, one channel pair per quarter, stored after the last quarter as
   // one access per row (bf16 packed pairs, or fp32 pairs)
   uint32_t qgw[2][NQ];
@@ -565,7 +611,7 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
         }
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-          st2<F32>(recp(R::KPT + (c0 + ch) * CP + r0), kp[0][ch], kp[1][ch]);
+          st2<F32>(Cf::KPT_LDS ? KPs + (c0 + ch) * TS + r0 : recp(R::KPT + (c0 + ch) * CP + r0), kp[0][ch], kp[1][ch]);
           st2<F32>(KGt + (c0 + ch) * TS + r0, kg[0][ch], kg[1][ch]);
         }
       }
@@ -637,22 +683,15 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
       acc[pi >> 3] = c;
     });
     if (qt == NQ - 1) {
-      // beta and V^T (for A, T and the U~ product) last: they were loaded last
+      // beta and V^T (for A, T and the U~ product) last: they were loaded last; with K'^T staged
+      // in the V^T area, K'^T goes to the record here and V^T follows after the barrier
       if (tid < C) Bet[tid] = rb;
-      if (vact) {
-        float x0[8], x1[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float2 vv = vpair(i);
-          x0[i] = vv.x;
-          x1[i] = vv.y;
-        }
-        st8_a8<F32>(Vt + (2 * vcp) * TS + 8 * vtg, x0);
-        st8_a8<F32>(Vt + (2 * vcp + 1) * TS + 8 * vtg, x1);
-      }
+      if constexpr (Cf::KPT_LDS) rows_out<DK, CP * sizeof(E), TS * sizeof(E)>(reinterpret_cast<const unsigned char*>(KPs), rec0 + R::KPT * sizeof(E), tid);
+      else write_vt();
     }
     __syncthreads();
   }
+  if constexpr (Cf::KPT_LDS) write_vt();  // read first by the U~ product, three barriers on
 
   // ---------------- M_kk -> A (fp32, LDS, strictly lower, rows scaled by beta); M_qk -> P (record)
   static_for<0, 2 * NPAIR>([&](auto pic) {
@@ -749,7 +788,8 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
       if ((ct & 7) != wave) continue;
       const bool isw = ct < DK / 16;
       const int n16 = isw ? ct : ct - DK / 16;
-      const E* brow = (isw ? KGt : Vt) + (16 * n16 + lo) * TS;
+      E* brow = (isw ? KGt : Vt) + (16 * n16 + lo) * TS;
+      f32x4 u[NT];  // U~^T tiles, held until this wave's last read of its V^T rows
 #pragma unroll
       for (int b = 0; b < NT; ++b) {
         const E* trow = Ts + (16 * b + lo) * TS;
@@ -757,14 +797,27 @@ __global__ __launch_bounds__(512, (IntraCfg<F32, DK, DV, C>::MINW)) void intra_c
         if (isw) {
 #pragma unroll
           for (int s = 0; s < O::nks(16 * (b + 1)); ++s) acc2 = O::mma(O::ld(brow, s, grp), O::ld(trow, s, grp), acc2);
-          st4<F32>(recp(R::NW + (16 * b + lo) * DK + 16 * n16 + 4 * grp), -acc2[0], -acc2[1], -acc2[2], -acc2[3]);
+          E* dst = Cf::NW_LDS ? Ws + (16 * b + lo) * Cf::SW + 16 * n16 + 4 * grp : recp(R::NW + (16 * b + lo) * DK + 16 * n16 + 4 * grp);
+          st4<F32>(dst, -acc2[0], -acc2[1], -acc2[2], -acc2[3]);
         } else {
 #pragma unroll
           for (int s = 0; s < O::nks(16 * (b + 1)); ++s) acc2 = O::mma(O::ld(trow, s, grp), O::ld(brow, s, grp), acc2);
-          st4<F32>(recp(R::UT + (16 * n16 + lo) * C + 16 * b + 4 * grp), acc2[0], acc2[1], acc2[2], acc2[3]);
+          if constexpr (Cf::UT_LDS) u[b] = acc2;
+          else st4<F32>(recp(R::UT + (16 * n16 + lo) * C + 16 * b + 4 * grp), acc2[0], acc2[1], acc2[2], acc2[3]);
         }
       }
+      if (!isw && Cf::UT_LDS) {
+#pragma unroll
+        for (int b = 0; b < NT; ++b) st4<F32>(brow + 16 * b + 4 * grp, u[b][0], u[b][1], u[b][2], u[b][3]);
+      }
     }
+  }
+  if constexpr (Cf::NW_LDS || Cf::UT_LDS) {
+    __syncthreads();
+    if constexpr (Cf::NW_LDS)
+      rows_out<C, DK * sizeof(E), Cf::SW * sizeof(E)>(reinterpret_cast<const unsigned char*>(Ws), rec0 + R::NW * sizeof(E), tid);
+    if constexpr (Cf::UT_LDS)
+      rows_out<DV, C * sizeof(E), TS * sizeof(E)>(reinterpret_cast<const unsigned char*>(Vt), rec0 + R::UT * sizeof(E), tid);
   }
 }
 
