@@ -841,16 +841,22 @@ __global__ __launch_bounds__(64 * (WS / 32 + 4)) void chain_wide_kernel(const Ch
         Ot[1][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uf[1][sk], fp[bt][sk], Ot[1][bt], 0, 0, 0);
       }
     }
-    // output gate, stores: four consecutive value columns of one token per lane (8 bytes), at a
-    // wave-uniform base (the chunk's first token) plus 32-bit lane offsets rebuilt here from an
-    // opaque zero, so that no per-lane 64-bit address stays live across the chunk loop
+    // output gate, stores at a wave-uniform base (the chunk's first token) plus 32-bit lane offsets
+    // rebuilt here from an opaque zero, so that no per-lane 64-bit address stays live across the
+    // chunk loop.  A lane holds four consecutive columns of one token in each of the two column
+    // tiles; one exchange with the lane of the neighbouring column group (lane ^ 16) gives every
+    // lane eight consecutive columns, so each store writes 16 bytes per lane and the four column
+    // groups of a token row cover 64 contiguous bytes (two stores of 8-byte pieces covered 32).
     uint32_t zero;
     asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
     char* ob = reinterpret_cast<char*>(static_cast<__bf16*>(p.o) + obase);
     const char* zb = gz ? reinterpret_cast<const char*>(static_cast<const __bf16*>(p.z) + obase) : nullptr;
+    const bool odd = (grp & 1) != 0;
+    const int ocol = ccol0 + (odd ? 16 + 4 * (grp - 1) : 4 * grp);  // first of this lane's 8 columns
 #pragma unroll
     for (int bt = 0; bt < NT; ++bt) {
       const int row = 16 * bt + lo;
+      uint2 pk[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const int col = ccol0 + 16 * ct + 4 * grp;
@@ -865,11 +871,13 @@ __global__ __launch_bounds__(64 * (WS / 32 + 4)) void chain_wide_kernel(const Ch
           ov[2] *= __uint_as_float(zv.y << 16);
           ov[3] *= __uint_as_float(zv.y & 0xffff0000u);
         }
-        if (row < len) {
-          *reinterpret_cast<uint2*>(ob + 2u * ((uint32_t)row * (uint32_t)ostride + (uint32_t)col + zero)) =
-              make_uint2(pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]));
-        }
+        pk[ct] = make_uint2(pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]));
       }
+      // even groups keep tile 0 and take the odd neighbour's tile-0 columns; odd groups the reverse
+      const uint2 give = odd ? pk[0] : pk[1];
+      const uint2 got = make_uint2((uint32_t)__shfl_xor((int)give.x, 16), (uint32_t)__shfl_xor((int)give.y, 16));
+      const uint4 w = odd ? make_uint4(got.x, got.y, pk[1].x, pk[1].y) : make_uint4(pk[0].x, pk[0].y, got.x, got.y);
+      if (row < len) *reinterpret_cast<uint4*>(ob + 2u * ((uint32_t)row * (uint32_t)ostride + (uint32_t)ocol + zero)) = w;
     }
   };
   // state snapshot after chunk c when it ends `every` tokens into the sequence (wave-uniform)
