@@ -28,9 +28,11 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libkda_debug.so")  # the debug build: input envelope checked
 
 KDA_F32, KDA_BF16 = 0, 1
-STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_HIP"}
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_HIP",
+          5: "KDA_ERR_ENVELOPE"}
 
 # exported symbols of libkda.so (the C ABI)
 EXPORTS = (
@@ -40,6 +42,7 @@ EXPORTS = (
     "kda_chunked_forward_profiled", "kda_chunked_forward_varlen", "kda_chunked_forward_varlen_workspace_bytes",
     "kda_decode_step", "kda_chunked_backward", "kda_chunked_backward_workspace_bytes", "kda_chunked_forward_mxfp8",
     "kda_chunked_forward_noalloc", "kda_chunked_backward_varlen", "kda_chunked_backward_varlen_workspace_bytes",
+    "kda_debug_checks",
 )
 
 # bytes of the library's fixed device scratch used by kda_chunked_forward_noalloc (KDA_NOALLOC_SCRATCH_BYTES)
@@ -50,32 +53,6 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
-_lib.kda_status_string.argtypes = [_i32]
-_lib.kda_status_string.restype = ctypes.c_char_p
-_lib.kda_version.argtypes = []
-_lib.kda_version.restype = _i32
-_lib.kda_chunked_forward_workspace_bytes.argtypes = [_i32] * 7
-_lib.kda_chunked_forward_workspace_bytes.restype = _sz
-_lib.kda_chunked_forward_plan.argtypes = [_i32] * 7 + [_vp] * 4
-_lib.kda_chunked_forward_plan.restype = _i32
-_lib.kda_chunked_forward_varlen_workspace_bytes.argtypes = [_i32] * 8
-_lib.kda_chunked_forward_varlen_workspace_bytes.restype = _sz
-_lib.kda_chunked_forward.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp, _sz, _vp]
-_lib.kda_chunked_forward.restype = _i32
-_lib.kda_chunked_forward_noalloc.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp]
-_lib.kda_chunked_forward_noalloc.restype = _i32
-_lib.kda_chunked_forward_with_states.argtypes = [_vp] * 9 + [_i32] * 8 + [_vp, _sz, _vp]
-_lib.kda_chunked_forward_with_states.restype = _i32
-_lib.kda_chunked_forward_varlen_with_states.argtypes = [_vp] * 9 + [_i32, _vp] + [_i32] * 8 + [_vp, _sz, _vp]
-_lib.kda_chunked_forward_varlen_with_states.restype = _i32
-_lib.kda_chunked_forward_profiled.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp, _sz, _vp, _vp]
-_lib.kda_chunked_forward_profiled.restype = _i32
-_lib.kda_chunked_forward_varlen.argtypes = [_vp] * 8 + [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
-_lib.kda_chunked_forward_varlen.restype = _i32
-_lib.kda_chunked_forward_mxfp8.argtypes = [_vp] * 11 + [_i32] * 6 + [_vp, _sz, _vp]
-_lib.kda_chunked_forward_mxfp8.restype = _i32
-_lib.kda_decode_step.argtypes = [_vp] * 7 + [_i32] * 4 + [_i32, _vp]
-_lib.kda_decode_step.restype = _i32
 
 
 class Fusion(ctypes.Structure):
@@ -83,23 +60,58 @@ class Fusion(ctypes.Structure):
     _fields_ = [("gate_x", _vp), ("gate_scale", ctypes.c_float), ("normalize_qk", _i32), ("out_gate", _vp)]
 
 
-_lib.kda_chunked_forward_fused.argtypes = [_vp] * 8 + [ctypes.POINTER(Fusion)] + [_i32] * 7 + [_vp, _sz, _vp]
-_lib.kda_chunked_forward_fused.restype = _i32
-_lib.kda_decode_step_fused.argtypes = [_vp] * 7 + [ctypes.POINTER(Fusion)] + [_i32] * 5 + [_vp]
-_lib.kda_decode_step_fused.restype = _i32
-_lib.kda_chunked_forward_ex.argtypes = [_vp] * 9 + [_i32, ctypes.POINTER(Fusion)] + [_i32] * 7 + [_vp, _sz, _vp]
-_lib.kda_chunked_forward_ex.restype = _i32
-_lib.kda_chunked_forward_varlen_ex.argtypes = ([_vp] * 9 + [_i32, ctypes.POINTER(Fusion), _vp] + [_i32] * 8 +
-                                               [_vp, _sz, _vp])
-_lib.kda_chunked_forward_varlen_ex.restype = _i32
-_lib.kda_chunked_backward_workspace_bytes.argtypes = [_i32] * 7
-_lib.kda_chunked_backward_workspace_bytes.restype = _sz
-_lib.kda_chunked_backward.argtypes = [_vp] * 14 + [_i32] * 7 + [_vp, _sz, _vp]
-_lib.kda_chunked_backward.restype = _i32
-_lib.kda_chunked_backward_varlen_workspace_bytes.argtypes = [_i32] * 8
-_lib.kda_chunked_backward_varlen_workspace_bytes.restype = _sz
-_lib.kda_chunked_backward_varlen.argtypes = [_vp] * 15 + [_i32] * 8 + [_vp, _sz, _vp]
-_lib.kda_chunked_backward_varlen.restype = _i32
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Argument and result types of every entry point (the same for the release and debug builds)."""
+    lib.kda_status_string.argtypes = [_i32]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = _i32
+    lib.kda_chunked_forward_workspace_bytes.argtypes = [_i32] * 7
+    lib.kda_chunked_forward_workspace_bytes.restype = _sz
+    lib.kda_chunked_forward_plan.argtypes = [_i32] * 7 + [_vp] * 4
+    lib.kda_chunked_forward_plan.restype = _i32
+    lib.kda_chunked_forward_varlen_workspace_bytes.argtypes = [_i32] * 8
+    lib.kda_chunked_forward_varlen_workspace_bytes.restype = _sz
+    lib.kda_chunked_forward.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp, _sz, _vp]
+    lib.kda_chunked_forward.restype = _i32
+    lib.kda_chunked_forward_noalloc.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp]
+    lib.kda_chunked_forward_noalloc.restype = _i32
+    lib.kda_chunked_forward_with_states.argtypes = [_vp] * 9 + [_i32] * 8 + [_vp, _sz, _vp]
+    lib.kda_chunked_forward_with_states.restype = _i32
+    lib.kda_chunked_forward_varlen_with_states.argtypes = [_vp] * 9 + [_i32, _vp] + [_i32] * 8 + [_vp, _sz, _vp]
+    lib.kda_chunked_forward_varlen_with_states.restype = _i32
+    lib.kda_chunked_forward_profiled.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp, _sz, _vp, _vp]
+    lib.kda_chunked_forward_profiled.restype = _i32
+    lib.kda_chunked_forward_varlen.argtypes = [_vp] * 8 + [_vp] + [_i32] * 8 + [_vp, _sz, _vp]
+    lib.kda_chunked_forward_varlen.restype = _i32
+    lib.kda_chunked_forward_mxfp8.argtypes = [_vp] * 11 + [_i32] * 6 + [_vp, _sz, _vp]
+    lib.kda_chunked_forward_mxfp8.restype = _i32
+    lib.kda_decode_step.argtypes = [_vp] * 7 + [_i32] * 4 + [_i32, _vp]
+    lib.kda_decode_step.restype = _i32
+    lib.kda_chunked_forward_fused.argtypes = [_vp] * 8 + [ctypes.POINTER(Fusion)] + [_i32] * 7 + [_vp, _sz, _vp]
+    lib.kda_chunked_forward_fused.restype = _i32
+    lib.kda_decode_step_fused.argtypes = [_vp] * 7 + [ctypes.POINTER(Fusion)] + [_i32] * 5 + [_vp]
+    lib.kda_decode_step_fused.restype = _i32
+    lib.kda_chunked_forward_ex.argtypes = [_vp] * 9 + [_i32, ctypes.POINTER(Fusion)] + [_i32] * 7 + [_vp, _sz, _vp]
+    lib.kda_chunked_forward_ex.restype = _i32
+    lib.kda_chunked_forward_varlen_ex.argtypes = ([_vp] * 9 + [_i32, ctypes.POINTER(Fusion), _vp] + [_i32] * 8 +
+                                                   [_vp, _sz, _vp])
+    lib.kda_chunked_forward_varlen_ex.restype = _i32
+    lib.kda_chunked_backward_workspace_bytes.argtypes = [_i32] * 7
+    lib.kda_chunked_backward_workspace_bytes.restype = _sz
+    lib.kda_chunked_backward.argtypes = [_vp] * 14 + [_i32] * 7 + [_vp, _sz, _vp]
+    lib.kda_chunked_backward.restype = _i32
+    lib.kda_chunked_backward_varlen_workspace_bytes.argtypes = [_i32] * 8
+    lib.kda_chunked_backward_varlen_workspace_bytes.restype = _sz
+    lib.kda_chunked_backward_varlen.argtypes = [_vp] * 15 + [_i32] * 8 + [_vp, _sz, _vp]
+    lib.kda_chunked_backward_varlen.restype = _i32
+    lib.kda_debug_checks.argtypes = []
+    lib.kda_debug_checks.restype = _i32
+    return lib
+
+
+_declare(_lib)
+_debug_lib = None
 
 
 class KDAError(RuntimeError):
@@ -119,6 +131,19 @@ def kda_version() -> int:
 def lib() -> ctypes.CDLL:
     """The loaded libkda.so (for callers that marshal arguments themselves)."""
     return _lib
+
+
+def debug_lib() -> ctypes.CDLL:
+    """The debug build, libkda_debug.so, loaded on first use: the same C ABI with every entry point
+    first checking g and beta against the input envelope (KDA_ERR_ENVELOPE on a violation; one
+    stream synchronisation per call).  Callers marshal arguments themselves, as with lib()."""
+    global _debug_lib
+    if _debug_lib is None:
+        if not os.path.exists(DEBUG_LIB_PATH):
+            raise ImportError("libkda_debug.so is not built (%s): run `python gated_delta_rule_94_amd/build.py`"
+                              % DEBUG_LIB_PATH)
+        _debug_lib = _declare(ctypes.CDLL(DEBUG_LIB_PATH))
+    return _debug_lib
 
 
 def _dtype_code(t: torch.Tensor) -> int:

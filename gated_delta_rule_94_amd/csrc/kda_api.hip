@@ -34,6 +34,78 @@ void* scratch_address() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#ifdef KDA_DEBUG_CHECKS
+}  // namespace
+
+// Debug build: the input envelope (-5 <= g <= 0, 0 <= beta <= 1, finite) checked on the GPU before a
+// call enqueues its work.  `envelope_flag` is raised by any thread that finds a violation (plain
+// stores of the same value; no atomics), cleared by a one-thread kernel before each check.
+static __device__ int envelope_flag;
+
+__global__ void envelope_clear_kernel(int* flag) {
+  if (threadIdx.x == 0) flag[threadIdx.x] = 0;
+}
+
+// g [n_g] (log-decays; n_g = 0 skips them) then beta [n_b]: bf16 bits or fp32
+__global__ void envelope_kernel(const void* g, const void* beta, int64_t n_g, int64_t n_b, int f32, int* flag) {
+  bool bad = false;
+  const int64_t n = n_g + n_b, step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += step) {
+    const bool isg = i < n_g;
+    const int64_t j = isg ? i : i - n_g;
+    const void* base = isg ? g : beta;
+    const float x = f32 ? static_cast<const float*>(base)[j]
+                        : __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[j] << 16);
+    const bool ok = isg ? (x >= -5.f && x <= 0.f) : (x >= 0.f && x <= 1.f);  // false for NaN
+    bad = bad || !ok;
+  }
+  if (bad) flag[0] = 1;
+}
+
+namespace {
+std::mutex g_flag_mu;
+void* g_flag[kMaxDevices];  // device address of `envelope_flag` on each device
+
+int* flag_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_flag_mu);
+  if (!g_flag[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(envelope_flag)) != hipSuccess || !p) return nullptr;
+    g_flag[dev] = p;
+  }
+  return static_cast<int*>(g_flag[dev]);
+}
+#endif
+
+// The debug build's envelope check of g (when it holds log-decays: not a fused gate's
+// pre-activation) and beta over `tokens` token-heads x H; the release build checks nothing.
+// KDA_OK, KDA_ERR_ENVELOPE, or KDA_ERR_HIP.
+kda_status envelope_check(const void* g, const void* beta, int64_t tokens, int H, int d_k, bool f32,
+                          bool g_is_log_decay, void* hip_stream) {
+#ifdef KDA_DEBUG_CHECKS
+  if (tokens <= 0) return KDA_OK;
+  int* flag = flag_address();
+  if (!flag) return KDA_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const int64_t n_g = g_is_log_decay ? tokens * H * d_k : 0, n_b = tokens * H;
+  const int64_t blocks = (n_g + n_b + 255) / 256;
+  hipLaunchKernelGGL(envelope_clear_kernel, dim3(1), dim3(64), 0, s, flag);
+  hipLaunchKernelGGL(envelope_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, s, g, beta, n_g,
+                     n_b, f32 ? 1 : 0, flag);
+  int raised = 0;
+  if (hipGetLastError() != hipSuccess ||
+      hipMemcpyAsync(&raised, flag, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return KDA_ERR_HIP;
+  return raised ? KDA_ERR_ENVELOPE : KDA_OK;
+#else
+  (void)g; (void)beta; (void)tokens; (void)H; (void)d_k; (void)f32; (void)g_is_log_decay; (void)hip_stream;
+  return KDA_OK;
+#endif
+}
 bool dim_ok(int d) { return d == 64 || d == 128; }
 bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
 
@@ -87,11 +159,20 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case KDA_ERR_WORKSPACE: return "workspace too small";
     case KDA_ERR_HIP: return "HIP runtime error";
+    case KDA_ERR_ENVELOPE: return "g or beta outside the documented envelope (debug build)";
   }
   return "unknown status";
 }
 
 int kda_version(void) { return 200; }
+
+int kda_debug_checks(void) {
+#ifdef KDA_DEBUG_CHECKS
+  return 1;
+#else
+  return 0;
+#endif
+}
 
 size_t kda_chunked_forward_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt) {
   if (B <= 0 || T < 0 || H <= 0 || !chunk_ok(chunk) || (dt != KDA_F32 && dt != KDA_BF16)) return 0;
@@ -158,6 +239,9 @@ kda_status chunked_forward_impl(const void* q, const void* k, const void* v, con
     }
   }
   if (!workspace_ok(workspace, workspace_bytes, need)) return KDA_ERR_WORKSPACE;
+  if (const kda_status e =
+          envelope_check(g_eff, beta, (int64_t)B * T, H, d_k, dt == KDA_F32, fu.gate_scale == 0.f, hip_stream))
+    return e;
   kda::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g_eff; a.beta = beta;
   a.h0 = h0; a.o = o; a.hT = hT;
@@ -232,6 +316,7 @@ kda_status kda_chunked_forward_profiled(const void* q, const void* k, const void
   if (B == 0 || (T == 0 && !hT)) return KDA_OK;
   if (!workspace_ok(workspace, workspace_bytes, kda_chunked_forward_workspace_bytes(B, T, H, d_k, d_v, chunk, dt)))
     return KDA_ERR_WORKSPACE;
+  if (const kda_status e = envelope_check(g, beta, (int64_t)B * T, H, d_k, dt == KDA_F32, true, hip_stream)) return e;
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
   for (int i = 0; i < 3; ++i)
     if (hipEventCreate(&ev[i]) != hipSuccess) {
@@ -275,6 +360,9 @@ kda_status kda_chunked_forward_varlen_ex(const void* q, const void* k, const voi
   if (!workspace_ok(workspace, workspace_bytes,
                     kda_chunked_forward_varlen_workspace_bytes(num_seqs, T_total, max_seqlen, H, d_k, d_v, chunk, dt)))
     return KDA_ERR_WORKSPACE;
+  if (const kda_status e =
+          envelope_check(g_eff, beta, T_total, H, d_k, dt == KDA_F32, fu.gate_scale == 0.f, hip_stream))
+    return e;
   kda::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g_eff; a.beta = beta;
   a.h0 = h0; a.o = o; a.hT = hT;
@@ -319,6 +407,7 @@ kda_status kda_chunked_forward_mxfp8(const void* q, const void* q_scale, const v
   if (T == 0 && !hT) return KDA_OK;
   if (!workspace_ok(workspace, workspace_bytes, kda_chunked_forward_workspace_bytes(B, T, H, d_k, d_v, chunk, KDA_BF16)))
     return KDA_ERR_WORKSPACE;
+  if (const kda_status e = envelope_check(g, beta, (int64_t)B * T, H, d_k, false, true, hip_stream)) return e;
   kda::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.q_scale = static_cast<const uint8_t*>(q_scale);
@@ -382,6 +471,7 @@ kda_status kda_chunked_backward(const void* q, const void* k, const void* v, con
   if (B == 0 || (T == 0 && !dh0)) return KDA_OK;
   if (!workspace_ok(workspace, workspace_bytes, kda_chunked_backward_workspace_bytes(B, T, H, d_k, d_v, chunk, dt)))
     return KDA_ERR_WORKSPACE;
+  if (const kda_status e = envelope_check(g, beta, (int64_t)B * T, H, d_k, dt == KDA_F32, true, hip_stream)) return e;
   kda::BackwardArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dO = d_o; a.dhT = dhT;
   a.dq = dq; a.dk_out = dk; a.dv_out = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
@@ -414,6 +504,7 @@ kda_status kda_chunked_backward_varlen(const void* q, const void* k, const void*
   if (!workspace_ok(workspace, workspace_bytes,
                     kda_chunked_backward_varlen_workspace_bytes(num_seqs, T_total, max_seqlen, H, d_k, d_v, chunk, dt)))
     return KDA_ERR_WORKSPACE;
+  if (const kda_status e = envelope_check(g, beta, T_total, H, d_k, dt == KDA_F32, true, hip_stream)) return e;
   kda::BackwardArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dO = d_o; a.dhT = dhT;
   a.dq = dq; a.dk_out = dk; a.dv_out = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
@@ -441,6 +532,8 @@ kda_status kda_decode_step_fused(const void* q, const void* k, const void* v, co
   }
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
   if (B == 0) return KDA_OK;
+  if (const kda_status e = envelope_check(g_eff, beta, B, H, d_k, dt == KDA_F32, fu.gate_scale == 0.f, hip_stream))
+    return e;
   kda::DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g_eff; a.beta = beta;
   a.state = state;

@@ -40,6 +40,17 @@
  *  - Inputs are expected in the documented envelope (-5 <= g <= 0,
  *    0 <= beta <= 1, |q|, |k| of order 1).  Outside it the result is
  *    unspecified; NaN or Inf in an input propagates to o and hT.
+ *
+ * Debug build (libkda_debug.so: the same sources, kda_api.hip compiled with
+ * KDA_DEBUG_CHECKS; kda_debug_checks() returns 1)
+ *  - Every entry point that takes g and beta first checks them against the
+ *    envelope on the GPU: each element of g in [-5, 0] (skipped where the
+ *    fused gate forms g from a pre-activation, which keeps it there by
+ *    construction) and each element of beta in [0, 1]; NaN and Inf fail.  A
+ *    violation returns KDA_ERR_ENVELOPE and nothing else is enqueued.
+ *  - To read the check's result the debug build synchronises `hip_stream`
+ *    once per call (unlike the release build, which never synchronises), so it
+ *    is for diagnosis, not for graph capture or timing.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -59,7 +70,8 @@ typedef enum {
   KDA_ERR_INVALID_ARG = 1, /* null pointer, negative size, misaligned pointer, bad cu_seqlens bound */
   KDA_ERR_UNSUPPORTED = 2, /* valid but outside the supported shapes */
   KDA_ERR_WORKSPACE = 3,   /* workspace smaller than the size query returned */
-  KDA_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+  KDA_ERR_HIP = 4,         /* a HIP launch or runtime call failed */
+  KDA_ERR_ENVELOPE = 5     /* debug build only: g or beta outside the documented envelope */
 } kda_status;
 
 /* Static description of a status code (never NULL). */
@@ -67,6 +79,9 @@ const char* kda_status_string(kda_status s);
 
 /* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
 int kda_version(void);
+
+/* 1 in the debug build (the envelope checks above), 0 in the release build. */
+int kda_debug_checks(void);
 
 /*
  * Bytes of device workspace kda_chunked_forward needs for this shape

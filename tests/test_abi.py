@@ -30,6 +30,18 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(kda.EXPORTS)
 
 
+def test_debug_build_exports_and_flag():
+    """libkda_debug.so (the debug build: envelope checks) exports the same entry points; only it
+    reports debug checks."""
+    dbg = ctypes.CDLL(kda.DEBUG_LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(dbg, name), name
+    assert kda.lib().kda_debug_checks() == 0
+    assert kda.debug_lib().kda_debug_checks() == 1
+    assert "envelope" in kda.kda_status_string(5)
+    assert kda.STATUS[5] == "KDA_ERR_ENVELOPE"
+
+
 def test_status_strings_and_version():
     assert kda.kda_status_string(0) == "ok"
     assert "invalid" in kda.kda_status_string(1)
