@@ -34,8 +34,11 @@ struct BwdParams {
   const void *q, *k, *v, *g, *beta, *dO;
   const float *h0, *dhT;
   const unsigned char* records;  // one per (chunk, head) item, item = chunk H + head
-  const float* states;  // the state after chunk c of head h (full chunks) at item (c H + h): DK DV each
-  float* dstates;       // the adjoint of the state at the end of chunk c of head h, at item (c H + h)
+  // the state after chunk c of head h (full chunks) at item (c H + h), DK DV each, and the adjoint of
+  // the state at the end of chunk c of head h at the same item: elements of the operand type (fp32,
+  // or bf16 rounded to nearest even -- what the state products round them to anyway)
+  const void* states;
+  void* dstates;
   float* grads;         // per (chunk, head) item: GradLayout::FLOATS
   void *dq, *dk, *dv, *dg, *dbeta;
   float* dh0;
@@ -472,10 +475,10 @@ __global__ __launch_bounds__(512) void bwd_chain_kernel(BwdParams p) {
   for (int ch = ch_hi - 1; ch >= ch_lo; --ch) {
     __syncthreads();  // this chunk's buffer is filled; dS of the previous step is complete
     if constexpr (!SUM) {
-      float* ds_out = p.dstates + ((first + ch) * H + h) * DK * DV + col0;
+      E* ds_out = static_cast<E*>(p.dstates) + ((first + ch) * H + h) * DK * DV + col0;
       for (int e = tid; e < DK * WS; e += Cf::NTH) {
         const int c = e / WS, j = e - c * WS;
-        ds_out[(int64_t)c * DV + j] = sdS[c * SS + j];
+        ds_out[(int64_t)c * DV + j] = (E)sdS[c * SS + j];
       }
     }
     if constexpr (Cf::DBUF) {
@@ -600,10 +603,11 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
   const int64_t unit = (int64_t)it.seq * H + h;
   const E* rec = reinterpret_cast<const E*>(p.records + item * R::BYTES);
   const float* gam = reinterpret_cast<const float*>(p.records + item * R::BYTES + R::GAM_BYTE);
-  // the chunk's start state: the state after the sequence's previous chunk, item - H
-  const float* s0 = !it.first ? p.states + (item - H) * DK * DV
-                              : (p.h0 ? p.h0 + unit * DK * DV : nullptr);  // nullptr: zero start state
-  const float* ds1 = p.dstates + item * DK * DV;
+  // the chunk's start state: the state after the sequence's previous chunk (item - H, operand type),
+  // or h0 (fp32) for a sequence's first chunk, or zero
+  const E* s0c = !it.first ? static_cast<const E*>(p.states) + (item - H) * DK * DV : nullptr;
+  const float* s0h = it.first && p.h0 ? p.h0 + unit * DK * DV : nullptr;
+  const E* ds1 = static_cast<const E*>(p.dstates) + item * DK * DV;
   float* gr = p.grads + item * GL::FLOATS;
   const int64_t orow = it.tok0 * H + h;
 
@@ -613,25 +617,42 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
     // element has one owner thread in every pass)
     auto put = [&](uint32_t i, float x) { at(gr, i) = vp0 == 0 ? x : at(gr, i) + x; };
     if (vp0 > 0) __syncthreads();  // the previous pass's reads of every LDS region are done
-    // columns [vp0, vp0 + VP) of S0 (zeros without one) and dS1 to LDS; the branch on S0's presence
-    // is taken once for the workgroup, so no load sits under a per-element select
-    auto stage_states = [&](auto s0_present) {
+    // columns [vp0, vp0 + VP) of S0 and dS1 to LDS, 4 elements per access; the source of S0 (a kept
+    // state, h0, or none: zeros) is chosen once for the workgroup, so no load sits under a
+    // per-element select
+    auto stage_states = [&](auto s0_kind) {
+      constexpr int K = decltype(s0_kind)::value;  // 0 none, 1 kept state, 2 h0
       for_units<DK * VP / 4, NTH>(tid, [&](int e) {
         const int c = (4 * e) / VP, j = 4 * e - c * VP;
         const int64_t gi = (int64_t)c * DV + vp0 + j;
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-        if constexpr (decltype(s0_present)::value) a = *reinterpret_cast<const float4*>(s0 + gi);
-        const float4 d = *reinterpret_cast<const float4*>(ds1 + gi);
         E* pa = sS0 + c * SV + j;
         E* pd = sdS + c * SV + j;
-        pa[0] = (E)a.x; pa[1] = (E)a.y; pa[2] = (E)a.z; pa[3] = (E)a.w;
-        pd[0] = (E)d.x; pd[1] = (E)d.y; pd[2] = (E)d.z; pd[3] = (E)d.w;
+        if constexpr (F32) {
+          float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+          if constexpr (K == 1) a = *reinterpret_cast<const float4*>(s0c + gi);
+          if constexpr (K == 2) a = *reinterpret_cast<const float4*>(s0h + gi);
+          const float4 d = *reinterpret_cast<const float4*>(ds1 + gi);
+          pa[0] = a.x; pa[1] = a.y; pa[2] = a.z; pa[3] = a.w;
+          pd[0] = d.x; pd[1] = d.y; pd[2] = d.z; pd[3] = d.w;
+        } else {
+          bf16x4 a = {(E)0.f, (E)0.f, (E)0.f, (E)0.f};
+          if constexpr (K == 1) a = *reinterpret_cast<const bf16x4*>(s0c + gi);
+          if constexpr (K == 2) {
+            const float4 x = *reinterpret_cast<const float4*>(s0h + gi);
+            a = bf16x4{(E)x.x, (E)x.y, (E)x.z, (E)x.w};
+          }
+          const bf16x4 d = *reinterpret_cast<const bf16x4*>(ds1 + gi);
+          pa[0] = a[0]; pa[1] = a[1]; pa[2] = a[2]; pa[3] = a[3];
+          pd[0] = d[0]; pd[1] = d[1]; pd[2] = d[2]; pd[3] = d[3];
+        }
       });
     };
-    if (s0)
-      stage_states(std::true_type{});
+    if (s0c)
+      stage_states(std::integral_constant<int, 1>{});
+    else if (s0h)
+      stage_states(std::integral_constant<int, 2>{});
     else
-      stage_states(std::false_type{});
+      stage_states(std::integral_constant<int, 0>{});
     for_units<C * VP / 8, NTH>(tid, [&](int e) {
       const int r = (8 * e) / VP, j = 8 * e - r * VP;
       copy8<F32>(p.dO, (orow + (int64_t)(r < nr ? r : 0) * H) * DV + vp0 + j, sdO + r * SV + j, true);
@@ -1260,7 +1281,7 @@ static int64_t bwd_max_chunks(int C, int num_seqs, int T, bool varlen) {
   return varlen ? (int64_t)T / C + num_seqs : (int64_t)num_seqs * ((T + C - 1) / C);
 }
 
-// [forward workspace][states: chunks H dk dv fp32][dstates: chunks H dk dv fp32]
+// [forward workspace][states: chunks H dk dv][dstates: chunks H dk dv] (operand type: fp32 or bf16)
 // [grads: chunks H GradLayout floats][o scratch: tokens H dv elements], and for a segmented adjoint
 // chain [segment end adjoints: units nseg dk dv fp32][summaries: units (nseg - 1) dk (dv + dk) fp32],
 // each 256-byte aligned.  tokens: B T, or T_total for packed sequences.
@@ -1269,7 +1290,7 @@ size_t chunked_backward_workspace(bool f32, int dk, int dv, int chunk, int num_s
   const int64_t mc = bwd_max_chunks(chunk, num_seqs, T, varlen), units = (int64_t)num_seqs * H, items = mc * H;
   const int64_t tokens = varlen ? (int64_t)T : (int64_t)num_seqs * T;
   size_t bytes = al256(chunked_forward_workspace(f32, dk, dv, chunk, mc, H, num_seqs, varlen));
-  bytes += 2 * al256((size_t)items * dk * dv * 4);
+  bytes += 2 * al256((size_t)items * dk * dv * (f32 ? 4 : 2));
   bytes += al256((size_t)items * grad_floats(dk, dv, chunk) * 4);
   bytes += al256((size_t)tokens * H * dv * (f32 ? 4 : 2));
   if (!varlen) {
@@ -1316,9 +1337,9 @@ hipError_t launch_chunked_backward(const BackwardArgs& a) {
     return hipErrorInvalidValue;
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
   const size_t fwd = al256(chunked_forward_workspace(a.f32, a.dk, a.dv, C, mc, a.H, a.B, varlen));
-  const size_t st_bytes = al256((size_t)items * a.dk * a.dv * 4);
-  float* states = reinterpret_cast<float*>(ws + fwd);
-  float* dstates = reinterpret_cast<float*>(ws + fwd + st_bytes);
+  const size_t st_bytes = al256((size_t)items * a.dk * a.dv * (a.f32 ? 4 : 2));
+  float* states = reinterpret_cast<float*>(ws + fwd);  // fp32 or bf16 elements (f.states_bf16)
+  void* dstates = ws + fwd + st_bytes;
   float* grads = reinterpret_cast<float*>(ws + fwd + 2 * st_bytes);
   const size_t gr_bytes = al256((size_t)items * grad_floats(a.dk, a.dv, C) * 4);
   void* o_scratch = ws + fwd + 2 * st_bytes + gr_bytes;
@@ -1336,6 +1357,7 @@ hipError_t launch_chunked_backward(const BackwardArgs& a) {
     f.states = states;
     f.state_every = C;
     f.states_by_chunk = true;
+    f.states_bf16 = !a.f32;
     if ((e = launch_chunked_forward(f)) != hipSuccess) return e;
   }
   BwdParams p;

@@ -51,6 +51,7 @@ struct ChainParams {
   float* states;          // or NULL: the state after every `every` tokens of a sequence,
   int every, max_states;  // [units][max_states][DK][DV]; with states_by_chunk (every = C), the state
   int states_by_chunk;    // after every full chunk at its record's slot: [(chunk) H + head][DK][DV]
+  int states_bf16;        // states stored as bf16 (round to nearest even) instead of fp32
   const void* z;          // or NULL: an output gate, laid out and typed like o, multiplying o
 };
 
@@ -384,14 +385,23 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     const int64_t slot = p.states_by_chunk ? (first + c) * H + h : (int64_t)unit * p.max_states + j;
     // a wave-uniform base and 32-bit lane offsets derived here from an opaque zero, so that the
     // compiler keeps no store addresses live across the chunk loop
-    char* st = reinterpret_cast<char*>(p.states + slot * DK * DV);
     uint32_t z;
     asm volatile("s_mov_b32 %0, 0" : "=s"(z));
-    const uint32_t lane_off = 4u * ((4u * grp + z) * DV + ccol);
+    const uint32_t lane_el = (4u * grp + z) * DV + ccol;  // element offset of this lane's first value
+    if (p.states_bf16) {
+      char* st = reinterpret_cast<char*>(p.states) + slot * DK * DV * 2;
 #pragma unroll
-    for (int m = 0; m < DK / 16; ++m)
+      for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) *reinterpret_cast<float*>(st + lane_off + 4u * (16 * m + r) * DV) = Sacc[m][r];
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<__bf16*>(st + 2u * (lane_el + (uint32_t)(16 * m + r) * DV)) = (__bf16)Sacc[m][r];
+    } else {
+      char* st = reinterpret_cast<char*>(p.states + slot * DK * DV);
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) *reinterpret_cast<float*>(st + 4u * (lane_el + (uint32_t)(16 * m + r) * DV)) = Sacc[m][r];
+    }
   };
 
   // Chain waves compute; copy waves stream records.  The two roles run separate loops with the same
@@ -890,17 +900,28 @@ __global__ __launch_bounds__(64 * (WS / 32 + 4)) void chain_wide_kernel(const Ch
     const int64_t slot = p.states_by_chunk ? (first + c) * H + h : (int64_t)unit * p.max_states + j;
     // a wave-uniform base and 32-bit lane offsets derived here from an opaque zero, so that the
     // compiler keeps no store addresses live across the chunk loop
-    char* st = reinterpret_cast<char*>(p.states + slot * DK * DV);
     uint32_t z;
     asm volatile("s_mov_b32 %0, 0" : "=s"(z));
-    const uint32_t lane_off = 4u * ((4u * grp + z) * DV + ccol0 + lo);
+    const uint32_t lane_el = (4u * grp + z) * DV + ccol0 + lo;  // element offset of this lane's first value
+    if (p.states_bf16) {
+      char* st = reinterpret_cast<char*>(p.states) + slot * DK * DV * 2;
 #pragma unroll
-    for (int m = 0; m < DK / 16; ++m)
+      for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          *reinterpret_cast<float*>(st + lane_off + 4u * ((16 * m + r) * DV + 16 * ct)) = Sacc[m][ct][r];
+          for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<__bf16*>(st + 2u * (lane_el + (uint32_t)((16 * m + r) * DV + 16 * ct))) = (__bf16)Sacc[m][ct][r];
+    } else {
+      char* st = reinterpret_cast<char*>(p.states + slot * DK * DV);
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<float*>(st + 4u * (lane_el + (uint32_t)((16 * m + r) * DV + 16 * ct))) = Sacc[m][ct][r];
+    }
   };
 
   // Chain waves compute; copy waves stream records (the loops and barriers of chain_kernel).
@@ -987,6 +1008,7 @@ static hipError_t launch_chain_wide_impl(const ChainLaunch& L) {
   p.nseg = L.nseg > 1 ? L.nseg : 1; p.seg_len = L.seg_len; p.sstart = L.sstart; p.send = L.send;
   p.states = SUM ? nullptr : L.states; p.every = L.every; p.max_states = L.max_states;
   p.states_by_chunk = L.states_by_chunk ? 1 : 0;
+  p.states_bf16 = L.states_bf16 ? 1 : 0;
   p.z = SUM ? nullptr : L.out_gate;
   const int64_t su = (int64_t)L.units * (SUM ? p.nseg - 1 : p.nseg);
   const int64_t grid = ((su + 7) / 8) * 8 * ((SUM ? DV + DK : DV) / WS);
@@ -1029,6 +1051,7 @@ static hipError_t launch_chain_impl(const ChainLaunch& L) {
   p.nseg = L.nseg > 1 ? L.nseg : 1; p.seg_len = L.seg_len; p.sstart = L.sstart; p.send = L.send;
   p.states = SUM ? nullptr : L.states; p.every = L.every; p.max_states = L.max_states;
   p.states_by_chunk = L.states_by_chunk ? 1 : 0;
+  p.states_bf16 = L.states_bf16 ? 1 : 0;
   p.z = SUM ? nullptr : L.out_gate;
   const int64_t su = (int64_t)L.units * (SUM ? p.nseg - 1 : p.nseg);
   const int64_t grid = ((su + 7) / 8) * 8 * ((SUM ? DV + DK : DV) / WS);

@@ -44,6 +44,7 @@ struct PrefillArgs {
   hipEvent_t* events = nullptr;  // optional: [3] recorded before the intra kernel, between the kernels, after the chain
   float* states = nullptr;       // optional state snapshots [num_seqs][H][max_states][dk][dv]
   int state_every = 0, max_states = 0;
+  bool states_bf16 = false;      // with states_by_chunk: the states stored as bf16 (the bf16 backward)
   bool states_by_chunk = false;  // instead: state_every = chunk, the state after every full chunk at
                                  // its record's slot [(chunk) H + head][dk][dv] (the backward's layout)
   Fusion fusion;
@@ -91,6 +92,7 @@ struct ChainLaunch {
   float* states = nullptr;
   int every = 0, max_states = 0;
   bool states_by_chunk = false;  // every = chunk, the state after each full chunk at [(chunk) H + head]
+  bool states_bf16 = false;      // the states stored as bf16 (the bf16 backward's chunk-start states)
   const void* out_gate = nullptr;  // o is multiplied by it elementwise (Fusion)
   void* stream;
 };

@@ -160,6 +160,7 @@ hipError_t launch_chunked_forward(const PrefillArgs& a) {
   K.ws = pl.ws;
   K.stream = a.stream;
   K.states = a.states; K.every = a.state_every; K.max_states = a.max_states; K.states_by_chunk = a.states_by_chunk;
+  K.states_bf16 = a.states_bf16;
   K.out_gate = a.fusion.out_gate;
   if (pl.nseg > 1) {
     unsigned char* seg = records + max_chunks * a.H * rb;

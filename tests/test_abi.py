@@ -244,14 +244,15 @@ def test_decode_validation():
 
 def test_backward_segment_workspace():
     """Long sequences on few heads segment the adjoint chain (as the forward chain): the backward
-    workspace then also holds every segment's end adjoint and the segment summaries."""
+    workspace then also holds every segment's end adjoint and the segment summaries.  The per-chunk
+    states and adjoints are kept in the operand type (bf16 here); the segment adjoints in fp32."""
     lib = kda.lib()
     al = lambda x: (x + 255) // 256 * 256
     B, T, H, d, C = 1, 16401, 8, 128, 64
     nch, units = (T + C - 1) // C, B * H
     fwd = al(lib.kda_chunked_forward_workspace_bytes(B, T, H, d, d, C, 1))
     grad = ((C * d + C * C + 3 * C * d + d + 63) // 64) * 64
-    base = fwd + 2 * al(units * nch * d * d * 4) + al(units * nch * grad * 4) + al(B * T * H * d * 2)
+    base = fwd + 2 * al(units * nch * d * d * 2) + al(units * nch * grad * 4) + al(B * T * H * d * 2)
     nseg = 8  # 8 heads x 4 slices of 32 columns: 32 workgroups, 257 chunks -> 8 segments of 33
     seg = al(units * nseg * d * d * 4) + al(units * (nseg - 1) * d * 2 * d * 4)
     assert lib.kda_chunked_backward_workspace_bytes(B, T, H, d, d, C, 1) == base + seg
@@ -259,7 +260,7 @@ def test_backward_segment_workspace():
     B, T, H = 4, 4096, 16
     nch, units = T // C, B * H
     fwd = al(lib.kda_chunked_forward_workspace_bytes(B, T, H, d, d, C, 1))
-    base = fwd + 2 * al(units * nch * d * d * 4) + al(units * nch * grad * 4) + al(B * T * H * d * 2)
+    base = fwd + 2 * al(units * nch * d * d * 2) + al(units * nch * grad * 4) + al(B * T * H * d * 2)
     assert lib.kda_chunked_backward_workspace_bytes(B, T, H, d, d, C, 1) == base
 
 
@@ -272,8 +273,8 @@ def test_backward_workspace_and_validation():
     nch, units = T // C, B * H
     grad = (C * D + C * C + 3 * C * D + D + 63) // 64 * 64  # dU, dP, d(Q Gamma), dKd, dW, dgl (fp32)
     # records, the state after every chunk and the adjoint at every chunk end (both per (chunk, head)
-    # record slot), the state products, an o scratch
-    want = (al(B * nch * H * rec) + 2 * al(units * nch * D * D * 4) + al(units * nch * grad * 4)
+    # record slot, in the operand type: bf16 here), the state products, an o scratch
+    want = (al(B * nch * H * rec) + 2 * al(units * nch * D * D * 2) + al(units * nch * grad * 4)
             + al(B * T * H * D * 2))
     assert lib.kda_chunked_backward_workspace_bytes(B, T, H, D, D, C, 1) == want
     assert lib.kda_chunked_backward_workspace_bytes(1, 100, 2, 128, 128, 48, 1) == 0  # unsupported chunk
@@ -314,7 +315,7 @@ def test_backward_varlen_workspace_and_validation():
     mc = Tt // C + N
     grad = (C * D + C * C + 3 * C * D + D + 63) // 64 * 64
     fwd = al(lib.kda_chunked_forward_varlen_workspace_bytes(N, Tt, maxlen, H, D, D, C, 1))
-    want = fwd + 2 * al(mc * H * D * D * 4) + al(mc * H * grad * 4) + al(Tt * H * D * 2)
+    want = fwd + 2 * al(mc * H * D * D * 2) + al(mc * H * grad * 4) + al(Tt * H * D * 2)
     assert lib.kda_chunked_backward_varlen_workspace_bytes(N, Tt, maxlen, H, D, D, C, 1) == want
     assert lib.kda_chunked_backward_varlen_workspace_bytes(N, Tt, maxlen, H, D, D, 48, 1) == 0
     assert lib.kda_chunked_backward_varlen_workspace_bytes(N, Tt, maxlen, H, D, D, C, 0) > 0
