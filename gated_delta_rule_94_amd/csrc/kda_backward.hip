@@ -226,12 +226,6 @@ __device__ __forceinline__ f32x4 tile_rows(const typename Op<F32>::E* arow, cons
   return acc;
 }
 
-// slot j of a bf16 fragment pair: hi = bf16(x), lo = bf16(x - hi)
-__device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int j) {
-  hi[j] = (__bf16)x;
-  lo[j] = (__bf16)(x - (float)hi[j]);
-}
-
 // ------------------------------------------------------------------------------------------------
 // 2. adjoint chain.  One 512-thread workgroup per (sequence, head, 32 value columns), products on
 // MFMA.  The record's first four fields (-W, Q Gamma, Kd^T, P) are copied to LDS as stored; dO's
@@ -819,8 +813,6 @@ template <bool F32, int DK, int DV, int C>
 __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   using Cf = BIntraCfg<F32, DK, DV, C>;
   using E = typename Cf::E;
-  using O = Op<F32>;
-  using Frag = typename O::Frag;
   using GL = GradLayout<DK, DV, C>;
   constexpr int NTK = Cf::NTK, NTV = Cf::NTV, NTILE = Cf::NTILE, MAXT = Cf::MAXT;
   constexpr int SG = Cf::SG, SK = Cf::SK, SV = Cf::SV, SM = Cf::SM, NTH = Cf::NTH;
@@ -1104,58 +1096,23 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     if (t >= NTILE) continue;
     const int r0 = 16 * (t / NTK), c = 16 * (t % NTK) + lo;
     const float R = r0 > 0 ? sG[(r0 - 1) * SG + c] : 0.f, R2 = sG[(r0 + 15) * SG + c];
+    // fp32 MFMA (16x16x4) for both input types: with bf16 inputs the operands built here (an exponent
+    // factor per element) would otherwise be split into bf16 hi + lo parts element by element for
+    // three bf16 products; the fp32 products are exact in the operands and took this phase from
+    // 0.20 to 0.16 ms per 4 x 16 x 4096 backward call
+    using OF = Op<true>;
     f32x4 d1 = zero4(), d2 = zero4(), d3 = zero4();
-    for (int s = 0; s < O::nks(r0 + 16); ++s) {
-      if constexpr (F32) {
-        const int k = O::kidx(s, grp, 0);
-        const Frag fb = tf(sK[k * SK + c]) * __expf(R - sG[k * SG + c]);
-        d1 = O::mma(sM4[(r0 + lo) * SM + k], fb, d1);
-        d2 = O::mma(sM3[(r0 + lo) * SM + k], fb, d2);
-      } else {
-        Frag fb, fbl, fa1, fa1l, fa2, fa2l;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int k = O::kidx(s, grp, j);
-          const bool ok = k < r0 + 16;
-          const int kc = ok ? k : 0;
-          split_bf16(ok ? tf(sK[kc * SK + c]) * __expf(R - sG[kc * SG + c]) : 0.f, fb, fbl, j);
-          split_bf16(ok ? sM4[(r0 + lo) * SM + kc] : 0.f, fa1, fa1l, j);
-          split_bf16(ok ? sM3[(r0 + lo) * SM + kc] : 0.f, fa2, fa2l, j);
-        }
-        d1 = O::mma(fa1, fb, d1);
-        d1 = O::mma(fa1, fbl, d1);
-        d1 = O::mma(fa1l, fb, d1);
-        d2 = O::mma(fa2, fb, d2);
-        d2 = O::mma(fa2, fbl, d2);
-        d2 = O::mma(fa2l, fb, d2);
-      }
+    for (int s = 0; s < OF::nks(r0 + 16); ++s) {
+      const int k = OF::kidx(s, grp, 0);
+      const float fb = tf(sK[k * SK + c]) * __expf(R - sG[k * SG + c]);
+      d1 = OF::mma(sM4[(r0 + lo) * SM + k], fb, d1);
+      d2 = OF::mma(sM3[(r0 + lo) * SM + k], fb, d2);
     }
-    for (int s = 0; s < O::nks(C - r0); ++s) {
-      if constexpr (F32) {
-        const int r = r0 + O::kidx(s, grp, 0);
-        const float e = __expf(sG[r * SG + c] - R2);
-        d3 = O::mma(sM4[r * SM + r0 + lo], q_at(r, c) * e, d3);
-        d3 = O::mma(sM3[r * SM + r0 + lo], tf(sK[r * SK + c]) * e, d3);
-      } else {
-        Frag fb1, fb1l, fb2, fb2l, fa1, fa1l, fa2, fa2l;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = r0 + O::kidx(s, grp, j);
-          const bool ok = r < C;
-          const int rc = ok ? r : 0;
-          const float e = ok ? __expf(sG[rc * SG + c] - R2) : 0.f;
-          split_bf16(tf(sQ[rc * SK + c]) * e, fb1, fb1l, j);
-          split_bf16(tf(sK[rc * SK + c]) * e, fb2, fb2l, j);
-          split_bf16(ok ? sM4[rc * SM + r0 + lo] : 0.f, fa1, fa1l, j);
-          split_bf16(ok ? sM3[rc * SM + r0 + lo] : 0.f, fa2, fa2l, j);
-        }
-        d3 = O::mma(fa1, fb1, d3);
-        d3 = O::mma(fa1, fb1l, d3);
-        d3 = O::mma(fa1l, fb1, d3);
-        d3 = O::mma(fa2, fb2, d3);
-        d3 = O::mma(fa2, fb2l, d3);
-        d3 = O::mma(fa2l, fb2, d3);
-      }
+    for (int s = 0; s < OF::nks(C - r0); ++s) {
+      const int r = r0 + OF::kidx(s, grp, 0);
+      const float e = __expf(sG[r * SG + c] - R2);
+      d3 = OF::mma(sM4[r * SM + r0 + lo], q_at(r, c) * e, d3);
+      d3 = OF::mma(sM3[r * SM + r0 + lo], tf(sK[r * SK + c]) * e, d3);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
