@@ -39,7 +39,9 @@ The JSON line carries:
                     HBM / MFMA
   states, fused, mxfp8, backward -- on the 4 x 16 x 4096 workload: the call keeping
                     the state every 1024 tokens; the fused gate / q-k norm / output
-                    gate; MXFP8 q, k, v; the backward (training) call
+                    gate; MXFP8 q, k, v; the backward (training) call, and a
+                    training step (forward + backward) with and without the
+                    forward's records and states saved for the backward
   decode         -- 1000 sequential kda_decode_step calls on the 256-sequence x
                     32-head state (512 MiB fp32), bytes and fraction of HBM
   cpu_baseline   -- the fp64 oracle on this host's cores, whole passes over the first
@@ -455,7 +457,33 @@ def main():
                            "mfma_frac": bflops / (bms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
                            "workspace_bytes": bws.numel(),
                            "note": "forward recompute + adjoint chain + state products + UT-transform backward"}
-        del bws, grads, do, dhT
+        # a training step: forward + backward, the backward recomputing the forward, or using what
+        # kda_chunked_forward_train saved (the same gradients bitwise)
+        saved = torch.empty(kda.train_saved_bytes(w.B, w.T, w.H, w.dk, w.dv, w.chunk, g["q"].dtype), dtype=torch.uint8,
+                            device=dev)
+        sws = torch.empty(kda.backward_saved_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.chunk, g["q"].dtype),
+                          dtype=torch.uint8, device=dev)
+
+        def step_recompute(_i):
+            c1["call"](0)
+            bstep(0)
+
+        def step_saved(_i):
+            kda.kda_chunked_forward_train(g["q"], g["k"], g["v"], g["g"], g["beta"], g["h0"], chunk=w.chunk, o=o, hT=hT,
+                                          saved=saved)
+            kda.kda_chunked_backward_saved(g["q"], g["k"], g["v"], g["g"], g["beta"], g["h0"], do, dhT, saved,
+                                           chunk=w.chunk, grads=grads, workspace=sws)
+
+        step_saved(0)
+        torch.cuda.synchronize()
+        rms, _ = time_launches(step_recompute, max(3, args.steps // 4), None if args.no_flush else flush)
+        tms, _ = time_launches(step_saved, max(3, args.steps // 4), None if args.no_flush else flush)
+        out["train_step"] = {"ms_recompute": rms, "ms_saved": tms, "saved_bytes": saved.numel(),
+                             "workspace_bytes_saved_backward": sws.numel(),
+                             "tokens_per_s_saved": tokens / (tms * 1e-3),
+                             "note": "forward + backward per step; 'saved': kda_chunked_forward_train + "
+                                     "kda_chunked_backward_saved (no forward recompute)"}
+        del bws, grads, do, dhT, saved, sws
 
     # ---------------- decode
     if not args.no_decode:

@@ -15,6 +15,8 @@ entry points' names:
 * ``kda_chunked_forward_ex`` / ``kda_chunked_forward_varlen_ex`` -- snapshots and fused steps together
 * ``kda_chunked_backward`` / ``kda_chunked_backward_varlen`` -- gradients of the chunked prefill
   (training), equal-length or packed sequences
+* ``kda_chunked_forward_train`` / ``kda_chunked_backward_saved`` -- a training step whose backward
+  uses what the forward saved instead of recomputing it
 
 Importing this package fails loudly when ``libkda.so`` has not been built
 (``python gated_delta_rule_94_amd/build.py``).
@@ -42,7 +44,8 @@ EXPORTS = (
     "kda_chunked_forward_profiled", "kda_chunked_forward_varlen", "kda_chunked_forward_varlen_workspace_bytes",
     "kda_decode_step", "kda_chunked_backward", "kda_chunked_backward_workspace_bytes", "kda_chunked_forward_mxfp8",
     "kda_chunked_forward_noalloc", "kda_chunked_backward_varlen", "kda_chunked_backward_varlen_workspace_bytes",
-    "kda_debug_checks",
+    "kda_debug_checks", "kda_chunked_forward_train", "kda_chunked_forward_train_saved_bytes",
+    "kda_chunked_backward_saved", "kda_chunked_backward_saved_workspace_bytes",
 )
 
 # bytes of the library's fixed device scratch used by kda_chunked_forward_noalloc (KDA_NOALLOC_SCRATCH_BYTES)
@@ -107,6 +110,14 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.kda_chunked_backward_varlen.restype = _i32
     lib.kda_debug_checks.argtypes = []
     lib.kda_debug_checks.restype = _i32
+    lib.kda_chunked_forward_train_saved_bytes.argtypes = [_i32] * 7
+    lib.kda_chunked_forward_train_saved_bytes.restype = _sz
+    lib.kda_chunked_forward_train.argtypes = [_vp] * 8 + [_i32] * 7 + [_vp, _sz, _vp]
+    lib.kda_chunked_forward_train.restype = _i32
+    lib.kda_chunked_backward_saved_workspace_bytes.argtypes = [_i32] * 7
+    lib.kda_chunked_backward_saved_workspace_bytes.restype = _sz
+    lib.kda_chunked_backward_saved.argtypes = [_vp] * 14 + [_i32] * 7 + [_vp, _sz, _vp, _sz, _vp]
+    lib.kda_chunked_backward_saved.restype = _i32
     return lib
 
 
@@ -613,6 +624,76 @@ def kda_chunked_backward(q, k, v, g, beta, h0, do, dhT=None, *, chunk: int = 64,
                                    B, T, H, dk, dv, chunk, _dtype_code(q), _ptr(ws), _nbytes(ws), _stream(stream))
     if st:
         raise KDAError("kda_chunked_backward", st)
+    return dq, dkk, dvv, dg, db, dh0
+
+
+def train_saved_bytes(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:
+    """Bytes of the buffer kda_chunked_forward_train fills for kda_chunked_backward_saved (0: unsupported)."""
+    return int(_lib.kda_chunked_forward_train_saved_bytes(B, T, H, dk, dv, chunk,
+                                                          _dtype_code(torch.empty(0, dtype=dtype))))
+
+
+def backward_saved_workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:
+    """Device workspace kda_chunked_backward_saved needs besides the saved buffer (0: unsupported)."""
+    return int(_lib.kda_chunked_backward_saved_workspace_bytes(B, T, H, dk, dv, chunk,
+                                                               _dtype_code(torch.empty(0, dtype=dtype))))
+
+
+def kda_chunked_forward_train(q, k, v, g, beta, h0=None, *, chunk: int = 64, o=None, hT=None, want_hT: bool = True,
+                              saved=None, stream=None):
+    """The forward of a training step: (o, hT) as kda_chunked_forward, plus `saved`, a uint8 device
+    tensor holding what kda_chunked_backward_saved needs (the per-chunk records and chunk-start
+    states).  Returns (o, hT, saved); keep saved and the inputs unchanged until the backward."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("g", g, (B, T, H, dk)),
+                         ("v", v, (B, T, H, dv)), ("beta", beta, (B, T, H))):
+        _check(name, t, shp, dt, dev)
+    _check("h0", h0, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check("o", o, (B, T, H, dv), dt, dev)
+    if hT is None and want_hT:
+        hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check("hT", hT, (B, H, dk, dv), torch.float32, dev)
+    sv = _workspace(saved, _lib.kda_chunked_forward_train_saved_bytes(B, T, H, dk, dv, chunk, _dtype_code(q)), dev)
+    st = _lib.kda_chunked_forward_train(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
+                                        B, T, H, dk, dv, chunk, _dtype_code(q), _ptr(sv), _nbytes(sv), _stream(stream))
+    if st:
+        raise KDAError("kda_chunked_forward_train", st)
+    return o, hT, sv
+
+
+def kda_chunked_backward_saved(q, k, v, g, beta, h0, do, dhT, saved, *, chunk: int = 64, want_dh0: bool = True,
+                               grads=None, workspace=None, stream=None):
+    """kda_chunked_backward for a forward run by kda_chunked_forward_train on the same inputs: the
+    same gradients, from `saved` instead of a recomputed forward."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("g", g, (B, T, H, dk)),
+                         ("v", v, (B, T, H, dv)), ("beta", beta, (B, T, H)), ("do", do, (B, T, H, dv))):
+        _check(name, t, shp, dt, dev)
+    _check("h0", h0, (B, H, dk, dv), torch.float32, dev)
+    _check("dhT", dhT, (B, H, dk, dv), torch.float32, dev)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(g),
+                 torch.empty_like(beta),
+                 torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dh0 else None)
+    dq, dkk, dvv, dg, db, dh0 = grads
+    for name, t, ref in (("dq", dq, q), ("dk", dkk, k), ("dv", dvv, v), ("dg", dg, g), ("dbeta", db, beta)):
+        _check(name, t, ref.shape, dt, dev)
+    _check("dh0", dh0, (B, H, dk, dv), torch.float32, dev)
+    sv = _workspace(saved, 0, dev)
+    ws = _workspace(workspace, _lib.kda_chunked_backward_saved_workspace_bytes(B, T, H, dk, dv, chunk, _dtype_code(q)),
+                    dev)
+    st = _lib.kda_chunked_backward_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(do),
+                                         _ptr(dhT), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg), _ptr(db), _ptr(dh0),
+                                         B, T, H, dk, dv, chunk, _dtype_code(q), _ptr(sv), _nbytes(sv), _ptr(ws),
+                                         _nbytes(ws), _stream(stream))
+    if st:
+        raise KDAError("kda_chunked_backward_saved", st)
     return dq, dkk, dvv, dg, db, dh0
 
 

@@ -481,6 +481,66 @@ kda_status kda_chunked_backward(const void* q, const void* k, const void* v, con
   return kda::launch_chunked_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+size_t kda_chunked_forward_train_saved_bytes(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt) {
+  if (B <= 0 || T < 0 || H <= 0 || (dt != KDA_F32 && dt != KDA_BF16)) return 0;
+  if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return 0;
+  return kda::chunked_backward_saved_bytes(dt == KDA_F32, d_k, d_v, chunk, B, T, H, false);
+}
+
+size_t kda_chunked_backward_saved_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt) {
+  if (B <= 0 || T < 0 || H <= 0 || (dt != KDA_F32 && dt != KDA_BF16)) return 0;
+  if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return 0;
+  return kda::chunked_backward_own_bytes(dt == KDA_F32, d_k, d_v, chunk, B, T, H, false);
+}
+
+kda_status kda_chunked_forward_train(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                     const float* h0, void* o, float* hT, int B, int T, int H, int d_k, int d_v,
+                                     int chunk, kda_dtype dt, void* saved, size_t saved_bytes, void* hip_stream) {
+  if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
+  const kda_status st = check_prefill(q, k, v, g, beta, h0, o, hT, B * T, H, d_k, d_v, chunk, dt);
+  if (st != KDA_OK) return st;
+  if (!kda::chunked_backward_supported(dt == KDA_F32, d_k, d_v, chunk)) return KDA_ERR_UNSUPPORTED;
+  if (B == 0 || (T == 0 && !hT)) return KDA_OK;
+  if (!workspace_ok(saved, saved_bytes, kda_chunked_forward_train_saved_bytes(B, T, H, d_k, d_v, chunk, dt)))
+    return KDA_ERR_WORKSPACE;
+  if (const kda_status e = envelope_check(g, beta, (int64_t)B * T, H, d_k, dt == KDA_F32, true, hip_stream)) return e;
+  kda::BackwardArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0;
+  a.dO = nullptr; a.dhT = nullptr;
+  a.dq = a.dk_out = a.dv_out = a.dg = a.dbeta = nullptr; a.dh0 = nullptr;
+  a.B = B; a.T = T; a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk; a.f32 = dt == KDA_F32;
+  a.workspace = nullptr;
+  a.stream = hip_stream;
+  return kda::launch_forward_train(a, saved, o, hT) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_chunked_backward_saved(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                      const float* h0, const void* d_o, const float* dhT, void* dq, void* dk,
+                                      void* dv, void* dg, void* dbeta, float* dh0, int B, int T, int H, int d_k,
+                                      int d_v, int chunk, kda_dtype dt, const void* saved, size_t saved_bytes,
+                                      void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (B < 0 || T < 0) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)B * T > INT32_MAX || (int64_t)B * H > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
+  const kda_status st = check_backward(q, k, v, g, beta, h0, d_o, dhT, dq, dk, dv, dg, dbeta, dh0, B * T, H, d_k,
+                                       d_v, chunk, dt);
+  if (st != KDA_OK) return st;
+  if (B == 0 || (T == 0 && !dh0)) return KDA_OK;
+  if (!workspace_ok(const_cast<void*>(saved), saved_bytes,
+                    kda_chunked_forward_train_saved_bytes(B, T, H, d_k, d_v, chunk, dt)) ||
+      !workspace_ok(workspace, workspace_bytes, kda_chunked_backward_saved_workspace_bytes(B, T, H, d_k, d_v, chunk, dt)))
+    return KDA_ERR_WORKSPACE;
+  if (const kda_status e = envelope_check(g, beta, (int64_t)B * T, H, d_k, dt == KDA_F32, true, hip_stream)) return e;
+  kda::BackwardArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.dO = d_o; a.dhT = dhT;
+  a.dq = dq; a.dk_out = dk; a.dv_out = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+  a.B = B; a.T = T; a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk; a.f32 = dt == KDA_F32;
+  a.workspace = workspace;
+  a.saved = saved;
+  a.stream = hip_stream;
+  return kda::launch_chunked_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 size_t kda_chunked_backward_varlen_workspace_bytes(int num_seqs, int T_total, int max_seqlen, int H, int d_k,
                                                    int d_v, int chunk, kda_dtype dt) {
   (void)max_seqlen;

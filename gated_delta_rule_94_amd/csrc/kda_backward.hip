@@ -1238,24 +1238,49 @@ static int64_t bwd_max_chunks(int C, int num_seqs, int T, bool varlen) {
   return varlen ? (int64_t)T / C + num_seqs : (int64_t)num_seqs * ((T + C - 1) / C);
 }
 
-// [forward workspace][states: chunks H dk dv][dstates: chunks H dk dv] (operand type: fp32 or bf16)
-// [grads: chunks H GradLayout floats][o scratch: tokens H dv elements], and for a segmented adjoint
-// chain [segment end adjoints: units nseg dk dv fp32][summaries: units (nseg - 1) dk (dv + dk) fp32],
-// each 256-byte aligned.  tokens: B T, or T_total for packed sequences.
-size_t chunked_backward_workspace(bool f32, int dk, int dv, int chunk, int num_seqs, int T, int H, bool varlen) {
-  if (!chunked_backward_supported(f32, dk, dv, chunk)) return 0;
+// The backward's buffers, each 256-byte aligned.  The part a forward leaves for it: [forward
+// workspace: records (and, packed, the chunk map)][states: chunks H dk dv].  The backward's own:
+// [dstates: chunks H dk dv][grads: chunks H GradLayout floats][o scratch: tokens H dv elements,
+// only where the forward is recomputed], and for a segmented adjoint chain [segment end adjoints:
+// units nseg dk dv fp32][summaries: units (nseg - 1) dk (dv + dk) fp32].  States and adjoints are
+// in the operand type (fp32 or bf16).  tokens: B T, or T_total for packed sequences.
+struct BwdSizes {
+  size_t fwd = 0, st = 0, gr = 0, os = 0, seg_end = 0, seg_sum = 0;
+};
+static BwdSizes bwd_sizes(bool f32, int dk, int dv, int chunk, int num_seqs, int T, int H, bool varlen) {
+  BwdSizes z;
   const int64_t mc = bwd_max_chunks(chunk, num_seqs, T, varlen), units = (int64_t)num_seqs * H, items = mc * H;
   const int64_t tokens = varlen ? (int64_t)T : (int64_t)num_seqs * T;
-  size_t bytes = al256(chunked_forward_workspace(f32, dk, dv, chunk, mc, H, num_seqs, varlen));
-  bytes += 2 * al256((size_t)items * dk * dv * (f32 ? 4 : 2));
-  bytes += al256((size_t)items * grad_floats(dk, dv, chunk) * 4);
-  bytes += al256((size_t)tokens * H * dv * (f32 ? 4 : 2));
+  z.fwd = al256(chunked_forward_workspace(f32, dk, dv, chunk, mc, H, num_seqs, varlen));
+  z.st = al256((size_t)items * dk * dv * (f32 ? 4 : 2));
+  z.gr = al256((size_t)items * grad_floats(dk, dv, chunk) * 4);
+  z.os = al256((size_t)tokens * H * dv * (f32 ? 4 : 2));
   if (!varlen) {
     const BwdPlan pl = bwd_plan(units, (T + chunk - 1) / chunk, dv);
-    if (pl.nseg > 1)
-      bytes += al256((size_t)(units * pl.nseg) * dk * dv * 4) + al256((size_t)(units * (pl.nseg - 1)) * dk * (dv + dk) * 4);
+    if (pl.nseg > 1) {
+      z.seg_end = al256((size_t)(units * pl.nseg) * dk * dv * 4);
+      z.seg_sum = al256((size_t)(units * (pl.nseg - 1)) * dk * (dv + dk) * 4);
+    }
   }
-  return bytes;
+  return z;
+}
+
+size_t chunked_backward_workspace(bool f32, int dk, int dv, int chunk, int num_seqs, int T, int H, bool varlen) {
+  if (!chunked_backward_supported(f32, dk, dv, chunk)) return 0;
+  const BwdSizes z = bwd_sizes(f32, dk, dv, chunk, num_seqs, T, H, varlen);
+  return z.fwd + 2 * z.st + z.gr + z.os + z.seg_end + z.seg_sum;
+}
+
+size_t chunked_backward_saved_bytes(bool f32, int dk, int dv, int chunk, int num_seqs, int T, int H, bool varlen) {
+  if (!chunked_backward_supported(f32, dk, dv, chunk)) return 0;
+  const BwdSizes z = bwd_sizes(f32, dk, dv, chunk, num_seqs, T, H, varlen);
+  return z.fwd + z.st;
+}
+
+size_t chunked_backward_own_bytes(bool f32, int dk, int dv, int chunk, int num_seqs, int T, int H, bool varlen) {
+  if (!chunked_backward_supported(f32, dk, dv, chunk)) return 0;
+  const BwdSizes z = bwd_sizes(f32, dk, dv, chunk, num_seqs, T, H, varlen);
+  return z.st + z.gr + z.seg_end + z.seg_sum;
 }
 
 template <bool F32, int DK, int DV, int C>
@@ -1283,6 +1308,30 @@ static hipError_t launch_backward_kernels(const BwdParams& p, int64_t units, voi
   return hipGetLastError();
 }
 
+// The forward as the backward needs it: the state after every full chunk kept at that chunk's
+// record slot (the start state of the sequence's next chunk), in the operand type.
+static hipError_t forward_for_backward(const BackwardArgs& a, unsigned char* ws, size_t fwd_bytes, void* states,
+                                       void* o, float* hT) {
+  PrefillArgs f;
+  f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta;
+  f.h0 = a.h0; f.o = o; f.hT = hT;
+  f.cu_seqlens = a.cu_seqlens; f.num_seqs = a.B; f.T = a.T;
+  f.H = a.H; f.dk = a.dk; f.dv = a.dv; f.chunk = a.chunk; f.f32 = a.f32;
+  f.workspace = ws; f.workspace_bytes = fwd_bytes; f.stream = a.stream;
+  f.states = static_cast<float*>(states);  // fp32 or bf16 elements (f.states_bf16)
+  f.state_every = a.chunk;
+  f.states_by_chunk = true;
+  f.states_bf16 = !a.f32;
+  return launch_chunked_forward(f);
+}
+
+hipError_t launch_forward_train(const BackwardArgs& a, void* saved, void* o, float* hT) {
+  if (!chunked_backward_supported(a.f32, a.dk, a.dv, a.chunk)) return hipErrorInvalidValue;
+  const BwdSizes z = bwd_sizes(a.f32, a.dk, a.dv, a.chunk, a.B, a.T, a.H, a.cu_seqlens != nullptr);
+  unsigned char* sv = static_cast<unsigned char*>(saved);
+  return forward_for_backward(a, sv, z.fwd, sv + z.fwd, o, hT);
+}
+
 hipError_t launch_chunked_backward(const BackwardArgs& a) {
   if (!chunked_backward_supported(a.f32, a.dk, a.dv, a.chunk)) return hipErrorInvalidValue;
   const bool varlen = a.cu_seqlens != nullptr;
@@ -1292,42 +1341,30 @@ hipError_t launch_chunked_backward(const BackwardArgs& a) {
   const BwdPlan pl = varlen ? BwdPlan{1, 0} : bwd_plan(units, nch, a.dv);
   if (units <= 0 || (units * pl.nseg + 7) * ((a.dv + a.dk) / 32) > INT32_MAX || items > INT32_MAX)
     return hipErrorInvalidValue;
+  const BwdSizes z = bwd_sizes(a.f32, a.dk, a.dv, C, a.B, a.T, a.H, varlen);
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  const size_t fwd = al256(chunked_forward_workspace(a.f32, a.dk, a.dv, C, mc, a.H, a.B, varlen));
-  const size_t st_bytes = al256((size_t)items * a.dk * a.dv * (a.f32 ? 4 : 2));
-  float* states = reinterpret_cast<float*>(ws + fwd);  // fp32 or bf16 elements (f.states_bf16)
-  void* dstates = ws + fwd + st_bytes;
-  float* grads = reinterpret_cast<float*>(ws + fwd + 2 * st_bytes);
-  const size_t gr_bytes = al256((size_t)items * grad_floats(a.dk, a.dv, C) * 4);
-  void* o_scratch = ws + fwd + 2 * st_bytes + gr_bytes;
-  unsigned char* seg = static_cast<unsigned char*>(o_scratch) + al256((size_t)tokens * a.H * a.dv * (a.f32 ? 4 : 2));
+  // the forward's part: from a forward-train call, or recomputed at the start of the workspace
+  unsigned char* saved = a.saved ? static_cast<unsigned char*>(const_cast<void*>(a.saved)) : ws;
+  unsigned char* own = a.saved ? ws : ws + z.fwd + z.st;
+  void* states = saved + z.fwd;
+  void* dstates = own;
+  float* grads = reinterpret_cast<float*>(own + z.st);
+  unsigned char* seg = own + z.st + z.gr + (a.saved ? 0 : z.os);
   hipError_t e = hipSuccess;
-  if (tokens > 0) {
-    // the forward, keeping the state after every full chunk at that chunk's item slot (the start
-    // state of the sequence's next chunk)
-    PrefillArgs f;
-    f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta;
-    f.h0 = a.h0; f.o = o_scratch; f.hT = nullptr;
-    f.cu_seqlens = a.cu_seqlens; f.num_seqs = a.B; f.T = a.T;
-    f.H = a.H; f.dk = a.dk; f.dv = a.dv; f.chunk = C; f.f32 = a.f32;
-    f.workspace = ws; f.workspace_bytes = fwd; f.stream = a.stream;
-    f.states = states;
-    f.state_every = C;
-    f.states_by_chunk = true;
-    f.states_bf16 = !a.f32;
-    if ((e = launch_chunked_forward(f)) != hipSuccess) return e;
+  if (!a.saved && tokens > 0) {
+    if ((e = forward_for_backward(a, ws, z.fwd, states, own + z.st + z.gr, nullptr)) != hipSuccess) return e;
   }
   BwdParams p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta; p.dO = a.dO;
   p.h0 = a.h0; p.dhT = a.dhT;
-  p.records = ws; p.states = states; p.dstates = dstates; p.grads = grads;
+  p.records = saved; p.states = states; p.dstates = dstates; p.grads = grads;
   p.dq = a.dq; p.dk = a.dk_out; p.dv = a.dv_out; p.dg = a.dg; p.dbeta = a.dbeta; p.dh0 = a.dh0;
   p.T = a.T; p.H = a.H; p.nch = nch; p.units = (int)units; p.items = items;
   p.cu = a.cu_seqlens; p.num_seqs = a.B;
   p.chunk0 = p.order = nullptr;
   if (varlen) {
     int32_t *c0, *ord;
-    chunk_map_of(ws, a.f32, a.dk, a.dv, C, mc, a.H, a.B, &c0, &ord);
+    chunk_map_of(saved, a.f32, a.dk, a.dv, C, mc, a.H, a.B, &c0, &ord);
     // built by the forward recompute; with no tokens every sequence is empty and only the map is needed
     if (tokens == 0 && (e = launch_chunk_map(a.cu_seqlens, a.B, a.T, C, c0, ord, a.stream)) != hipSuccess) return e;
     p.chunk0 = c0;

@@ -133,10 +133,21 @@ struct BackwardArgs {
   bool f32;
   void* workspace;
   void* stream;
+  // training: what a forward-train call left (records, chunk map, chunk-start states), or NULL to
+  // recompute the forward into the workspace
+  const void* saved = nullptr;
 };
 bool chunked_backward_supported(bool f32, int dk, int dv, int chunk);
+// the whole workspace of a backward that recomputes the forward
 size_t chunked_backward_workspace(bool f32, int dk, int dv, int chunk, int num_seqs, int T, int H, bool varlen);
+// the part of it a forward-train call fills (records, chunk map, chunk-start states), and the rest
+// a backward from that saved part needs as its workspace
+size_t chunked_backward_saved_bytes(bool f32, int dk, int dv, int chunk, int num_seqs, int T, int H, bool varlen);
+size_t chunked_backward_own_bytes(bool f32, int dk, int dv, int chunk, int num_seqs, int T, int H, bool varlen);
 hipError_t launch_chunked_backward(const BackwardArgs& a);
+// the forward of a training step: o and hT as kda_chunked_forward, and the backward's saved part in
+// `saved` (a.workspace is ignored; a.dO, the gradient pointers and a.dhT are not used)
+hipError_t launch_forward_train(const BackwardArgs& a, void* saved, void* o, float* hT);
 
 // Prefill: supported shape?  workspace bytes?  launch (hipErrorInvalidValue: unsupported shape).
 bool chunked_forward_supported(bool f32, int dk, int dv, int chunk);

@@ -363,6 +363,40 @@ kda_status kda_chunked_backward_varlen(const void* q, const void* k, const void*
 size_t kda_chunked_backward_varlen_workspace_bytes(int num_seqs, int T_total, int max_seqlen, int H, int d_k,
                                                    int d_v, int chunk, kda_dtype dt);
 
+/*
+ * A training step without the recompute: the forward keeps what the backward
+ * needs, the backward uses it.  kda_chunked_forward_train computes o and hT
+ * exactly as kda_chunked_forward (the same kernels; bitwise the same results)
+ * and also leaves, in the caller-owned `saved` buffer, every (chunk, head)
+ * record of the chunkwise form and the state at every chunk start (in the
+ * dtype dt).  kda_chunked_backward_saved then returns the gradients
+ * kda_chunked_backward returns for the same inputs (bitwise the same) without
+ * running the forward again.  The caller keeps `saved` unchanged, and passes
+ * the same q, k, v, g, beta, h0 and shapes, between the two calls; the
+ * library cannot check that.  Equal-length sequences; same domain, errors,
+ * ownership and stream semantics as kda_chunked_backward.
+ *   saved: kda_chunked_forward_train_saved_bytes(...) bytes, 256-byte aligned
+ *   workspace (backward): kda_chunked_backward_saved_workspace_bytes(...)
+ *     bytes, 256-byte aligned (the adjoint states and the state products)
+ * The two together hold what kda_chunked_backward's own workspace holds, less
+ * its recomputed o.
+ */
+kda_status kda_chunked_forward_train(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                     const float* h0, void* o, float* hT, int B, int T, int H, int d_k, int d_v,
+                                     int chunk, kda_dtype dt, void* saved, size_t saved_bytes, void* hip_stream);
+
+/* Bytes of the `saved` buffer kda_chunked_forward_train fills (0 = unsupported shape). */
+size_t kda_chunked_forward_train_saved_bytes(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt);
+
+kda_status kda_chunked_backward_saved(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                      const float* h0, const void* d_o, const float* dhT, void* dq, void* dk,
+                                      void* dv, void* dg, void* dbeta, float* dh0, int B, int T, int H, int d_k,
+                                      int d_v, int chunk, kda_dtype dt, const void* saved, size_t saved_bytes,
+                                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes kda_chunked_backward_saved needs (0 = unsupported shape). */
+size_t kda_chunked_backward_saved_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, kda_dtype dt);
+
 #ifdef __cplusplus
 }
 #endif

@@ -342,3 +342,48 @@ def test_backward_varlen_workspace_and_validation():
     assert call(a) == 3                                     # no workspace: KDA_ERR_WORKSPACE
     assert call(a, N=0) == OK
     assert call(a, Tt=0, maxlen=0) == OK                    # nothing to do without dh0
+
+
+def test_training_step_buffers_and_validation():
+    """kda_chunked_forward_train's saved buffer plus kda_chunked_backward_saved's workspace hold what
+    kda_chunked_backward's workspace holds, less its recomputed o; invalid calls fail before launch."""
+    lib = kda.lib()
+    al = lambda x: (x + 255) // 256 * 256
+    for (B, T, H, d, C, dt) in [(4, 4096, 16, 128, 64, 1), (1, 16401, 8, 128, 64, 1), (2, 300, 2, 64, 32, 0)]:
+        saved = lib.kda_chunked_forward_train_saved_bytes(B, T, H, d, d, C, dt)
+        own = lib.kda_chunked_backward_saved_workspace_bytes(B, T, H, d, d, C, dt)
+        full = lib.kda_chunked_backward_workspace_bytes(B, T, H, d, d, C, dt)
+        assert saved > 0 and own > 0
+        assert saved + own + al(B * T * H * d * (4 if dt == 0 else 2)) == full
+    assert lib.kda_chunked_forward_train_saved_bytes(1, 100, 2, 128, 128, 48, 1) == 0
+    assert lib.kda_chunked_backward_saved_workspace_bytes(1, 100, 2, 96, 128, 64, 1) == 0
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every call below fails validation
+    fwd = [fake] * 5 + [None, fake, fake]
+
+    def train(args=fwd, B=1, T=100, H=2, dk=128, chunk=64, dt=1, saved=None, nbytes=0):
+        return lib.kda_chunked_forward_train(*args, B, T, H, dk, dk, chunk, dt, saved, nbytes, None)
+
+    assert train() == 3                            # no saved buffer: KDA_ERR_WORKSPACE
+    assert train(chunk=48) == UNSUPPORTED
+    assert train(B=-1) == INVALID
+    assert train(B=0) == OK
+    bad = list(fwd)
+    bad[6] = None                                  # o missing
+    assert train(bad) == INVALID
+    need = lib.kda_chunked_forward_train_saved_bytes(1, 100, 2, 128, 128, 64, 1)
+    assert train(saved=ctypes.c_void_p((1 << 20) + 16), nbytes=need) == 3  # misaligned saved buffer
+    bwd = [fake] * 5 + [None, fake, None] + [fake] * 5 + [None]
+
+    def back(args=bwd, B=1, T=100, H=2, dk=128, chunk=64, dt=1, saved=None, sbytes=0, ws=None, wbytes=0):
+        return lib.kda_chunked_backward_saved(*args, B, T, H, dk, dk, chunk, dt, saved, sbytes, ws, wbytes, None)
+
+    own = lib.kda_chunked_backward_saved_workspace_bytes(1, 100, 2, 128, 128, 64, 1)
+    assert back() == 3                                                  # neither buffer
+    assert back(saved=fake, sbytes=need) == 3                           # no workspace
+    assert back(ws=fake, wbytes=own) == 3                               # no saved buffer
+    assert back(saved=fake, sbytes=need - 256, ws=fake, wbytes=own) == 3
+    assert back(chunk=48) == UNSUPPORTED
+    bad = list(bwd)
+    bad[8] = None                                                       # dq missing
+    assert back(bad, saved=fake, sbytes=need, ws=fake, wbytes=own) == INVALID
+    assert back(B=0) == OK
