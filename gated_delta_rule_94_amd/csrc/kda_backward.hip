@@ -534,6 +534,257 @@ __global__ __launch_bounds__(512) void bwd_chain_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// 2'. adjoint chain for bf16 records of 32- and 64-token chunks, in the form of the forward chain:
+// per (sequence, head, 32 value columns) two chain waves, each holding its 16 columns of dS (fp32)
+// in MFMA accumulators across chunks, and four copy waves streaming the next chunk's record prefix
+// and dO slice into the other of two LDS buffers.  Every product of the step contracts a record
+// field (and dO) over its row index -- dU = P^T dO + K' dS, dS <- e^{gl} dS + (Q Gamma)^T dO +
+// (-W)^T dU -- so the fields are staged as stored and their fragments read with the transposing LDS
+// load: lane L of a 16-lane group points at row k0 + L / 4, columns n0 + 4 (L mod 4), and receives
+// column n0 + L at rows k0 .. k0 + 3.  dS and dU serve as B operands straight from the
+// accumulators (no LDS).  Rows are padded by 16 elements, which keeps each half-wave of a
+// transposing load on distinct banks.
+template <int DK, int DV, int C>
+struct BChainTCfg {
+  using R = Rec<false, DK, DV, C>;
+  static_assert(R::CP == C && C % 32 == 0, "32- or 64-token chunks");
+  static constexpr int WS = 32, NCW = 2, NH = 4, NTH = 64 * (NCW + NH), NC = 64 * NH;
+  static constexpr int NT = C / 16, KSD = DK / 32, KSC = C / 32;
+  static constexpr int RK = DK + 16, RC = C + 16, RW = WS + 16;  // LDS row lengths (elements)
+  static constexpr int B_NW = 0;                         // -W       [C][RK]
+  static constexpr int B_QG = B_NW + C * RK * 2;         // Q.Gamma  [C][RK]
+  static constexpr int B_KPT = B_QG + C * RK * 2;        // K'^T     [DK][RC]
+  static constexpr int B_P = B_KPT + DK * RC * 2;        // P        [C][RC]
+  static constexpr int B_DO = B_P + C * RC * 2;          // dO slice [C][RW]
+  static constexpr int B_GAM = B_DO + C * RW * 2;        // e^{gl}   fp32 [DK]
+  static constexpr int BUF = (B_GAM + DK * 4 + 15) & ~15;
+  static constexpr int TOTAL = 2 * BUF;
+  static_assert(TOTAL <= 163840, "LDS budget of one gfx950 workgroup");
+  static_assert(C * WS / 8 <= NC, "one dO unit per copy thread");
+};
+
+// one part of a record: NU 16-byte units, UPR per row, from global row stride GROW bytes to LDS row
+// stride LROW bytes; loads of units past the end repeat the last one (in bounds), their stores are
+// skipped
+template <int NC, int NU, int UPR, int GBASE, int GROW, int LBASE, int LROW>
+struct TCopy {
+  static constexpr int K = (NU + NC - 1) / NC;
+  typedef uint32_t vec_t __attribute__((ext_vector_type(4 * K)));
+  vec_t st;
+  __device__ __forceinline__ void load(const unsigned char* rec, int ht) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int u = ht + NC * k < NU ? ht + NC * k : NU - 1;
+      const uint4 x = *reinterpret_cast<const uint4*>(rec + GBASE + (u / UPR) * GROW + 16 * (u % UPR));
+      st[4 * k] = x.x;
+      st[4 * k + 1] = x.y;
+      st[4 * k + 2] = x.z;
+      st[4 * k + 3] = x.w;
+    }
+  }
+  __device__ __forceinline__ void store(unsigned char* buf, int ht) const {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int u = ht + NC * k;
+      if (NU % NC != 0 && u >= NU) continue;
+      *reinterpret_cast<uint4*>(buf + LBASE + (u / UPR) * LROW + 16 * (u % UPR)) =
+          make_uint4(st[4 * k], st[4 * k + 1], st[4 * k + 2], st[4 * k + 3]);
+    }
+  }
+};
+
+// four bf16 of one column from the transposing LDS load (see above)
+__device__ __forceinline__ bf16x4 lds_tr4(const unsigned char* a) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(a));
+  return __builtin_bit_cast(bf16x4, x);
+}
+
+template <int DK, int DV, int C, bool SUM>
+__global__ __launch_bounds__(384) void bwd_chain_t_kernel(BwdParams p) {
+  using Cf = BChainTCfg<DK, DV, C>;
+  using R = typename Cf::R;
+  using O = Op<false>;
+  using Frag = typename O::Frag;
+  constexpr int WS = Cf::WS, NT = Cf::NT, KSD = Cf::KSD, KSC = Cf::KSC;
+  constexpr int NSL = (SUM ? DV + DK : DV) / WS;
+  __shared__ __align__(16) unsigned char smem[Cf::TOTAL];
+
+  // (sequence, head, segment, slice) as in bwd_chain_kernel: the slices of one (sequence, head,
+  // segment) are workgroups 8 apart, on one XCD
+  const int segs = SUM ? p.nseg - 1 : p.nseg;
+  const int xcd = blockIdx.x & 7, q8 = blockIdx.x >> 3;
+  const int su = (q8 / NSL) * 8 + xcd, col0 = (q8 % NSL) * WS;
+  if (su >= p.units * segs) return;
+  const int ui = su / segs, g = su - ui * segs + (SUM ? 1 : 0);
+  const int H = p.H;
+  const int n = p.order ? p.order[ui / H] : ui / H, h = ui - (ui / H) * H;
+  const int unit = n * H + h;
+  int64_t t_begin, t_end, first;
+  seq_span(p, n, t_begin, t_end, first);
+  const int nchu = (int)((t_end - t_begin + C - 1) / C);
+  const int ch_lo = p.nseg > 1 ? g * p.seg_len : 0;
+  const int ch_hi = p.nseg > 1 ? min(nchu, (g + 1) * p.seg_len) : nchu;  // chunks [ch_lo, ch_hi), in reverse
+  const int nq = ch_hi > ch_lo ? ch_hi - ch_lo : 0;                      // steps
+  const bool idsl = SUM && col0 >= DV;  // identity columns: no dO term
+
+  const int tid = threadIdx.x, lane = tid & 63, lo = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool chain = wave < Cf::NCW;
+  const int wcol = 16 * (chain ? wave : 0);  // this wave's columns within the slice
+  const int jc = col0 + wcol + lo;           // this lane's column
+
+  // ---- copy waves: a step's record prefix, e^{gl} and dO slice, global -> registers -> LDS
+  auto rec_of = [&](int q) -> const unsigned char* { return p.records + ((first + ch_hi - 1 - q) * H + h) * R::BYTES; };
+  struct Stage {
+    TCopy<Cf::NC, C * DK / 8, DK / 8, (int)(R::NW * 2), DK * 2, Cf::B_NW, Cf::RK * 2> nw;
+    TCopy<Cf::NC, C * DK / 8, DK / 8, (int)(R::QG * 2), DK * 2, Cf::B_QG, Cf::RK * 2> qg;
+    TCopy<Cf::NC, DK * C / 8, C / 8, (int)(R::KPT * 2), C * 2, Cf::B_KPT, Cf::RC * 2> kpt;
+    TCopy<Cf::NC, C * C / 8, C / 8, (int)(R::P * 2), C * 2, Cf::B_P, Cf::RC * 2> pp;
+    TCopy<Cf::NC, DK / 4, DK / 4, (int)R::GAM_BYTE, 0, Cf::B_GAM, 0> gam;
+    uint4 dov;
+    bool dook;  // the dO unit lies in the chunk (rows past its end, and summary identity columns: zeros)
+  };
+  const int ht = tid - 64 * Cf::NCW;  // copy-thread index (copy waves only)
+  auto stage_load = [&](Stage& st, int q) {
+    const unsigned char* rp = rec_of(q);
+    st.nw.load(rp, ht); st.qg.load(rp, ht); st.kpt.load(rp, ht); st.pp.load(rp, ht); st.gam.load(rp, ht);
+    // dO: unit ht = (row ht / 4, 8 columns); rows past the chunk's end read its last row (in bounds)
+    const int64_t t0 = t_begin + (int64_t)(ch_hi - 1 - q) * C;
+    const int len = (int)min((int64_t)C, t_end - t0);
+    const int u = ht < C * WS / 8 ? ht : 0, r = u / (WS / 8);
+    st.dov = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(p.dO) +
+                                             ((t0 + (r < len ? r : len - 1)) * H + h) * DV + col0 + 8 * (u % (WS / 8)));
+    st.dook = !idsl && r < len;
+  };
+  auto stage_store = [&](const Stage& st, unsigned char* b) {
+    st.nw.store(b, ht); st.qg.store(b, ht); st.kpt.store(b, ht); st.pp.store(b, ht); st.gam.store(b, ht);
+    if (ht < C * WS / 8)
+      *reinterpret_cast<uint4*>(b + Cf::B_DO + (ht / (WS / 8)) * Cf::RW * 2 + 16 * (ht % (WS / 8))) =
+          st.dook ? st.dov : make_uint4(0u, 0u, 0u, 0u);
+  };
+
+  // ---- chain waves: dS[m][r] = dS[16 m + 4 grp + r][jc]
+  f32x4 dS[DK / 16];
+  // fragment of k-step s (contraction rows kidx(s, grp, .)) of an LDS matrix [rows: contraction]
+  // [cols: n0 + 0..15] with row length RL elements
+  auto frag = [&](const unsigned char* base, int RL, int s, int n0) -> Frag {
+    const unsigned char* a = base + (32 * s + 4 * grp + (lo >> 2)) * RL * 2 + 2 * (n0 + 4 * (lo & 3));
+    const bf16x4 x = lds_tr4(a), y = lds_tr4(a + 16 * RL * 2);
+    return Frag{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  };
+  auto step = [&](int q, int buf) {
+    const unsigned char* b = smem + buf * Cf::BUF;
+    const int ch = ch_hi - 1 - q;
+    if (!chain) return;
+    if constexpr (!SUM) {  // the adjoint at this chunk's end, as bf16 at the chunk's item slot
+      char* ds_out = reinterpret_cast<char*>(static_cast<__bf16*>(p.dstates) + ((first + ch) * H + h) * DK * DV);
+      uint32_t z;
+      asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+      const uint32_t lane_el = (4u * grp + z) * DV + jc;
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<__bf16*>(ds_out + 2u * (lane_el + (uint32_t)(16 * m + r) * DV)) = (__bf16)dS[m][r];
+    }
+    // dU = K' dS + P^T dO (P^T's k-steps start at the tile's diagonal: the record's P tiles above
+    // the diagonal that no step reads are not all written)
+    f32x4 dU[NT];
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt) dU[bt] = zero4();
+#pragma unroll
+    for (int sk = 0; sk < KSD; ++sk) {
+      const Frag sf = O::from_acc(dS, sk);
+#pragma unroll
+      for (int bt = 0; bt < NT; ++bt) dU[bt] = O::mma(frag(b + Cf::B_KPT, Cf::RC, sk, 16 * bt), sf, dU[bt]);
+    }
+    Frag df[KSC];
+    if (!idsl) {
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) df[s] = frag(b + Cf::B_DO, Cf::RW, s, wcol);
+#pragma unroll
+      for (int bt = 0; bt < NT; ++bt)
+#pragma unroll
+        for (int s = bt / 2; s < KSC; ++s) dU[bt] = O::mma(frag(b + Cf::B_P, Cf::RC, s, 16 * bt), df[s], dU[bt]);
+    }
+    // dS <- e^{gl} dS + (Q Gamma)^T dO + (-W)^T dU
+    Frag uf[KSC];
+#pragma unroll
+    for (int s = 0; s < KSC; ++s) uf[s] = O::from_acc(dU, s);
+    const float* gam = reinterpret_cast<const float*>(b + Cf::B_GAM);
+#pragma unroll
+    for (int m = 0; m < DK / 16; ++m) {
+      const float4 gm = *reinterpret_cast<const float4*>(gam + 16 * m + 4 * grp);
+      dS[m][0] *= gm.x;
+      dS[m][1] *= gm.y;
+      dS[m][2] *= gm.z;
+      dS[m][3] *= gm.w;
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+        if (!idsl) dS[m] = O::mma(frag(b + Cf::B_QG, Cf::RK, s, 16 * m), df[s], dS[m]);
+        dS[m] = O::mma(frag(b + Cf::B_NW, Cf::RK, s, 16 * m), uf[s], dS[m]);
+      }
+    }
+  };
+
+  if (chain) {
+    // the adjoint at the range's end: dhT (or the combine's end adjoint of this segment); a summary
+    // starts from zero on the value columns and from the identity on the extra ones
+    const float* d_end = p.nseg > 1 ? p.bstart + ((int64_t)unit * p.nseg + (p.nseg - 1 - g)) * DK * DV
+                                    : (p.dhT ? p.dhT + (int64_t)unit * DK * DV : nullptr);
+#pragma unroll
+    for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = 16 * m + 4 * grp + r;
+        if constexpr (SUM) dS[m][r] = (idsl && c == jc - DV) ? 1.f : 0.f;
+        else dS[m][r] = d_end ? d_end[(int64_t)c * DV + jc] : 0.f;
+      }
+    __syncthreads();
+    for (int q = 0; q < nq; q += 2) {
+      step(q, 0);
+      __syncthreads();
+      if (q + 1 >= nq) break;
+      step(q + 1, 1);
+      __syncthreads();
+    }
+    if constexpr (SUM) {
+      float* se = p.bsend + ((int64_t)unit * (p.nseg - 1) + (p.nseg - 1 - g)) * DK * (DV + DK);
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) se[(int64_t)(16 * m + 4 * grp + r) * (DV + DK) + jc] = dS[m][r];
+    } else if (p.dh0 && g == 0) {
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p.dh0[((int64_t)unit * DK + 16 * m + 4 * grp + r) * DV + jc] = dS[m][r];
+    }
+  } else {
+    // invariant at step q: buffer q & 1 holds step q, stage (q + 1) & 1 holds step q + 1; steps past
+    // the last are clamped to it (copies into a buffer nobody reads)
+    Stage s0, s1;
+    const int last = nq - 1;
+    if (nq > 0) {
+      stage_load(s0, 0);
+      stage_store(s0, smem);
+      stage_load(s1, last < 1 ? last : 1);
+    }
+    __syncthreads();
+    for (int q = 0; q < nq; q += 2) {
+      stage_load(s0, q + 2 < last ? q + 2 : last);
+      stage_store(s1, smem + Cf::BUF);
+      __syncthreads();
+      if (q + 1 >= nq) break;
+      stage_load(s1, q + 3 < last ? q + 3 : last);
+      stage_store(s0, smem);
+      __syncthreads();
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // 3. products with the chunk's start state S0 and end adjoint dS1, one 512-thread workgroup per
 // (chunk, head), on MFMA.  S0, dS1, dO, U and dU are staged in LDS in the operand type (rows padded
 // by 16 bytes); the record's -W, then P (masked to its lower triangle) and Kd^T, share one region.
@@ -1288,18 +1539,22 @@ static hipError_t launch_backward_kernels(const BwdParams& p, int64_t units, voi
   static_assert(GradLayout<DK, DV, C>::FLOATS == (((int64_t)C * DV + C * C + 3 * C * DK + DK + 63) & ~(int64_t)63),
                 "grad layout");
   hipError_t e = hipSuccess;
+  // bf16 records of 32- or 64-token chunks: the accumulator-resident adjoint chain
+  constexpr bool TR = !F32 && C >= 32;
   if (p.nseg > 1) {  // segment summaries, then every segment's end adjoint from dhT
     const int64_t su = units * (p.nseg - 1);
-    hipLaunchKernelGGL((bwd_chain_kernel<F32, DK, DV, C, true>), dim3((unsigned)(((su + 7) / 8) * 8 * ((DV + DK) / 32))),
-                       dim3(512), 0, (hipStream_t)stream, p);
+    const dim3 grid((unsigned)(((su + 7) / 8) * 8 * ((DV + DK) / 32)));
+    if constexpr (TR) hipLaunchKernelGGL((bwd_chain_t_kernel<DK, DV, C, true>), grid, dim3(384), 0, (hipStream_t)stream, p);
+    else hipLaunchKernelGGL((bwd_chain_kernel<F32, DK, DV, C, true>), grid, dim3(512), 0, (hipStream_t)stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_segment_combine(p.dhT, p.bsend, const_cast<float*>(p.bstart), (int)units, p.nseg, DK, DV, stream)) !=
         hipSuccess)
       return e;
   }
   const int64_t su = units * p.nseg;
-  hipLaunchKernelGGL((bwd_chain_kernel<F32, DK, DV, C, false>), dim3((unsigned)(((su + 7) / 8) * 8 * (DV / 32))), dim3(512),
-                     0, (hipStream_t)stream, p);
+  const dim3 grid((unsigned)(((su + 7) / 8) * 8 * (DV / 32)));
+  if constexpr (TR) hipLaunchKernelGGL((bwd_chain_t_kernel<DK, DV, C, false>), grid, dim3(384), 0, (hipStream_t)stream, p);
+  else hipLaunchKernelGGL((bwd_chain_kernel<F32, DK, DV, C, false>), grid, dim3(512), 0, (hipStream_t)stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || p.items == 0) return e;
   hipLaunchKernelGGL((bwd_state_kernel<F32, DK, DV, C>), dim3((unsigned)p.items), dim3(512), 0, (hipStream_t)stream, p);
