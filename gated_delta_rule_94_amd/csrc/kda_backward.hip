@@ -226,6 +226,24 @@ __device__ __forceinline__ f32x4 tile_rows(const typename Op<F32>::E* arow, cons
   return acc;
 }
 
+// gfx950's transposing LDS load of 16-bit data: lane L of a 16-lane group points at row k0 + L / 4,
+// columns n0 + 4 (L mod 4) of a row-major matrix, and receives column n0 + L at rows k0 .. k0 + 3
+// (the lane layout was probed on the GPU).  The address must be 8-byte aligned.
+__device__ __forceinline__ bf16x4 lds_tr4(const unsigned char* a) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(a));
+  return __builtin_bit_cast(bf16x4, x);
+}
+// bf16 MFMA fragment (A or B) of k-step s for this lane, from an LDS matrix stored with the
+// contraction index as its row (row length RL elements, 32 (s + 1) rows at least): column n0 + lo at
+// the contraction rows kidx(s, grp, .) = 32 s + 4 grp + 0..3 and 32 s + 16 + 4 grp + 0..3
+__device__ __forceinline__ bf16x8 frag_tr(const __bf16* m, int RL, int s, int n0) {
+  const int lane = threadIdx.x & 63, lo = lane & 15, grp = lane >> 4;
+  const unsigned char* a = reinterpret_cast<const unsigned char*>(m + (32 * s + 4 * grp + (lo >> 2)) * RL + n0 + 4 * (lo & 3));
+  const bf16x4 x = lds_tr4(a), y = lds_tr4(a + 32 * RL);
+  return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+
 // ------------------------------------------------------------------------------------------------
 // 2. adjoint chain.  One 512-thread workgroup per (sequence, head, 32 value columns), products on
 // MFMA.  The record's first four fields (-W, Q Gamma, Kd^T, P) are copied to LDS as stored; dO's
@@ -593,13 +611,6 @@ struct TCopy {
   }
 };
 
-// four bf16 of one column from the transposing LDS load (see above)
-__device__ __forceinline__ bf16x4 lds_tr4(const unsigned char* a) {
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
-  const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(a));
-  return __builtin_bit_cast(bf16x4, x);
-}
-
 template <int DK, int DV, int C, bool SUM>
 __global__ __launch_bounds__(384) void bwd_chain_t_kernel(BwdParams p) {
   using Cf = BChainTCfg<DK, DV, C>;
@@ -666,12 +677,9 @@ __global__ __launch_bounds__(384) void bwd_chain_t_kernel(BwdParams p) {
 
   // ---- chain waves: dS[m][r] = dS[16 m + 4 grp + r][jc]
   f32x4 dS[DK / 16];
-  // fragment of k-step s (contraction rows kidx(s, grp, .)) of an LDS matrix [rows: contraction]
-  // [cols: n0 + 0..15] with row length RL elements
+  // fragment of k-step s of an LDS matrix [rows: contraction][cols: n0 + 0..15], row length RL
   auto frag = [&](const unsigned char* base, int RL, int s, int n0) -> Frag {
-    const unsigned char* a = base + (32 * s + 4 * grp + (lo >> 2)) * RL * 2 + 2 * (n0 + 4 * (lo & 3));
-    const bf16x4 x = lds_tr4(a), y = lds_tr4(a + 16 * RL * 2);
-    return Frag{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    return frag_tr(reinterpret_cast<const __bf16*>(base), RL, s, n0);
   };
   auto step = [&](int q, int buf) {
     const unsigned char* b = smem + buf * Cf::BUF;
@@ -830,6 +838,9 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
   using E = typename Cf::E;
   using GL = typename Cf::GL;
   constexpr int SV = Cf::SV, SK = Cf::SK, SC = Cf::SC, CP = R::CP, NTH = Cf::NTH, VP = Cf::VP;
+  // bf16 with 32- or 64-token chunks: the products read whole MFMA fragments (the transposing LDS
+  // load where the contraction runs along a matrix's rows) instead of building them element by element
+  constexpr bool TRF = !F32 && C % 32 == 0;
   __shared__ __align__(16) unsigned char smem[Cf::TOTAL];
   E* sS0 = reinterpret_cast<E*>(smem + Cf::OFF_S0);
   E* sdS = reinterpret_cast<E*>(smem + Cf::OFF_DS);
@@ -919,8 +930,14 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
       f32x4 acc;
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = tf(rec[R::UT + (vp0 + j0 + lo) * C + i0 + 4 * grp + r]);
-      acc = tile_mm<F32, DK>([&](int m, int k) { return tf(sNW[(i0 + m) * SK + k]); },
-                             [&](int k, int n) { return tf(sS0[k * SV + j0 + n]); }, acc);  // S0 runs along n
+      if constexpr (TRF) {  // -W rows run along the contraction; S0 is read with the transposing load
+#pragma unroll
+        for (int sk = 0; sk < DK / 32; ++sk)
+          acc = Op<false>::mma(Op<false>::ld(sNW + (i0 + lo) * SK, sk, grp), frag_tr(sS0, SV, sk, j0), acc);
+      } else {
+        acc = tile_mm<F32, DK>([&](int m, int k) { return tf(sNW[(i0 + m) * SK + k]); },
+                               [&](int k, int n) { return tf(sS0[k * SV + j0 + n]); }, acc);  // S0 runs along n
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) sU[(i0 + 4 * grp + r) * SV + j0 + lo] = (E)acc[r];
     }
@@ -949,10 +966,18 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
     for (int t = wave; t < (C / 16) * (VP / 16); t += NTH / 64) {
       const int i0 = 16 * (t / (VP / 16)), j0 = 16 * (t % (VP / 16));
       f32x4 acc = zero4();
-      acc = tile_mm<F32, C>([&](int m, int k) { return tf(sP[k * SC + i0 + m]); },
-                            [&](int k, int n) { return tf(sdO[k * SV + j0 + n]); }, acc);
-      acc = tile_mm<F32, DK>([&](int m, int k) { return tf(sKPT[k * SC + i0 + m]); },
-                             [&](int k, int n) { return tf(sdS[k * SV + j0 + n]); }, acc);
+      if constexpr (TRF) {  // P^T, dO, Kd and dS1 all contract over their rows: transposing loads
+#pragma unroll
+        for (int sk = 0; sk < C / 32; ++sk) acc = Op<false>::mma(frag_tr(sP, SC, sk, i0), frag_tr(sdO, SV, sk, j0), acc);
+#pragma unroll
+        for (int sk = 0; sk < DK / 32; ++sk)
+          acc = Op<false>::mma(frag_tr(sKPT, SC, sk, i0), frag_tr(sdS, SV, sk, j0), acc);
+      } else {
+        acc = tile_mm<F32, C>([&](int m, int k) { return tf(sP[k * SC + i0 + m]); },
+                              [&](int k, int n) { return tf(sdO[k * SV + j0 + n]); }, acc);
+        acc = tile_mm<F32, DK>([&](int m, int k) { return tf(sKPT[k * SC + i0 + m]); },
+                               [&](int k, int n) { return tf(sdS[k * SV + j0 + n]); }, acc);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         sdU[(i0 + 4 * grp + r) * SV + j0 + lo] = (E)acc[r];
