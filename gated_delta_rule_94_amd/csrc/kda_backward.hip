@@ -1091,6 +1091,12 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   using E = typename Cf::E;
   using GL = GradLayout<DK, DV, C>;
   constexpr int NTK = Cf::NTK, NTV = Cf::NTV, NTILE = Cf::NTILE, MAXT = Cf::MAXT;
+  // owned tile q of this wave, t = wave + 8 q of the (C/16) x (DK/16) grid: its row tile and channel
+  // tile.  At d_k = 128 (8 channel tiles) the row tile is q itself, known at compile time in the
+  // unrolled loops over q, so the loops over its rows get constant trip counts and offsets.
+  auto tile_row = [&](int q, int t) { return NTK == 8 ? q : t / NTK; };
+  auto tile_col = [&](int t) { return NTK == 8 ? (t & 7) : t % NTK; };
+  constexpr int EEU = NTK == 8 ? C / 4 : 1;  // unrolling of the loops over a row tile's rows (constant counts at d_k = 128)
   constexpr int SG = Cf::SG, SK = Cf::SK, SV = Cf::SV, SM = Cf::SM, NTH = Cf::NTH;
   __shared__ __align__(16) unsigned char smem[Cf::TOTAL];
   float* sG = reinterpret_cast<float*>(smem + Cf::OFF_G);
@@ -1277,7 +1283,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     ag[q] = zero4();
     const int t = wave + 8 * q;
     if (t < NTILE) {
-      const int i0 = 16 * (t / NTK), c0 = 16 * (t % NTK);
+      const int i0 = 16 * tile_row(q, t), c0 = 16 * tile_col(t);
       const f32x4 d = tile_mm<F32, C, true>([&](int m, int k) { return sL[k * SM + i0 + m] * sBeta[i0 + m]; },
                                             [&](int k, int n) { return at(gr, GL::DW + k * DK + c0 + n); }, zero4());
 #pragma unroll
@@ -1370,7 +1376,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   for (int q = 0; q < MAXT; ++q) {
     const int t = wave + 8 * q;
     if (t >= NTILE) continue;
-    const int r0 = 16 * (t / NTK), c = 16 * (t % NTK) + lo;
+    const int r0 = 16 * tile_row(q, t), c = 16 * tile_col(t) + lo;
     const float R = r0 > 0 ? sG[(r0 - 1) * SG + c] : 0.f, R2 = sG[(r0 + 15) * SG + c];
     // fp32 MFMA (16x16x4) for both input types: with bf16 inputs the operands built here (an exponent
     // factor per element) would otherwise be split into bf16 hi + lo parts element by element for
@@ -1378,12 +1384,14 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     // 0.20 to 0.16 ms per 4 x 16 x 4096 backward call
     using OF = Op<true>;
     f32x4 d1 = zero4(), d2 = zero4(), d3 = zero4();
+#pragma unroll EEU
     for (int s = 0; s < OF::nks(r0 + 16); ++s) {
       const int k = OF::kidx(s, grp, 0);
       const float fb = tf(sK[k * SK + c]) * __expf(R - sG[k * SG + c]);
       d1 = OF::mma(sM4[(r0 + lo) * SM + k], fb, d1);
       d2 = OF::mma(sM3[(r0 + lo) * SM + k], fb, d2);
     }
+#pragma unroll EEU
     for (int s = 0; s < OF::nks(C - r0); ++s) {
       const int r = r0 + OF::kidx(s, grp, 0);
       const float e = __expf(sG[r * SG + c] - R2);
@@ -1407,7 +1415,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   for (int q = 0; q < MAXT; ++q) {
     const int t = wave + 8 * q;
     if (t >= NTILE) continue;
-    const int tm = t / NTK, r0 = 16 * tm, c = 16 * (t % NTK) + lo;
+    const int tm = tile_row(q, t), r0 = 16 * tm, c = 16 * tile_col(t) + lo;
     const float gl = sG[(C - 1) * SG + c];
     float part = 0.f;
 #pragma unroll
@@ -1438,7 +1446,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   for (int q = 0; q < MAXT; ++q) {
     const int t = wave + 8 * q;
     if (t >= NTILE) continue;
-    const int r0 = 16 * (t / NTK), c = 16 * (t % NTK) + lo;
+    const int r0 = 16 * tile_row(q, t), c = 16 * tile_col(t) + lo;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = r0 + 4 * grp + r;
