@@ -226,6 +226,69 @@ __device__ __forceinline__ f32x4 tile_rows(const typename Op<F32>::E* arow, cons
   return acc;
 }
 
+// Four consecutive elements (operand type) as fp32, from LDS or global memory: one 8-byte (bf16) or
+// 16-byte (fp32) access at an aligned address.
+template <typename E>
+__device__ __forceinline__ float4 ld4f(const E* p) {
+  if constexpr (std::is_same<E, float>::value) {
+    return *reinterpret_cast<const float4*>(p);
+  } else {
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+    return make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+  }
+}
+__device__ __forceinline__ float4 ld4f(const float4* p) { return *p; }
+__device__ __forceinline__ float4 mul4(float4 a, float4 b) { return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w); }
+__device__ __forceinline__ float4 exp4(float4 a, float4 b) {  // e^{a - b}
+  return make_float4(__expf(a.x - b.x), __expf(a.y - b.y), __expf(a.z - b.z), __expf(a.w - b.w));
+}
+
+// tile_mm for operands that run along the contraction index in memory: a4(m, k) returns A[m][k ..
+// k + 3] and b4(k, n) returns B[k .. k + 3][n] (k a multiple of 4), so each fragment takes two
+// 4-element accesses per operand instead of eight single ones.  K: a multiple of 32 (bf16) or 16 (fp32).
+template <bool F32, int K, bool SPLIT = false, typename FA4, typename FB4>
+__device__ __forceinline__ f32x4 tile_mm4(FA4&& a4, FB4&& b4, f32x4 acc) {
+  const int lane = threadIdx.x & 63, lo = lane & 15, grp = lane >> 4;
+  if constexpr (F32) {
+    static_assert(K % 16 == 0, "whole fp32 k-step groups");
+    using O = Op<true>;
+#pragma unroll
+    for (int t = 0; t < K / 16; ++t) {  // k-steps 4 t .. 4 t + 3 take k = 16 t + 4 grp + 0..3
+      const float4 x = a4(lo, 16 * t + 4 * grp), y = b4(16 * t + 4 * grp, lo);
+      acc = O::mma(x.x, y.x, acc);
+      acc = O::mma(x.y, y.y, acc);
+      acc = O::mma(x.z, y.z, acc);
+      acc = O::mma(x.w, y.w, acc);
+    }
+  } else {
+    static_assert(K % 32 == 0, "whole bf16 k-steps");
+    using O = Op<false>;
+#pragma unroll
+    for (int s = 0; s < K / 32; ++s) {  // slots 0..3: k = 32 s + 4 grp + j, slots 4..7: + 16
+      const float4 xa = a4(lo, 32 * s + 4 * grp), xb = a4(lo, 32 * s + 16 + 4 * grp);
+      const float4 ya = b4(32 * s + 4 * grp, lo), yb = b4(32 * s + 16 + 4 * grp, lo);
+      const float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+      const float y[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};
+      typename O::Frag fa, fb, fal, fbl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        fa[j] = (__bf16)x[j];
+        fb[j] = (__bf16)y[j];
+        if constexpr (SPLIT) {
+          fal[j] = (__bf16)(x[j] - (float)fa[j]);
+          fbl[j] = (__bf16)(y[j] - (float)fb[j]);
+        }
+      }
+      acc = O::mma(fa, fb, acc);
+      if constexpr (SPLIT) {
+        acc = O::mma(fa, fbl, acc);
+        acc = O::mma(fal, fb, acc);
+      }
+    }
+  }
+  return acc;
+}
+
 // gfx950's transposing LDS load of 16-bit data: lane L of a 16-lane group points at row k0 + L / 4,
 // columns n0 + 4 (L mod 4) of a row-major matrix, and receives column n0 + L at rows k0 .. k0 + 3
 // (the lane layout was probed on the GPU).  The address must be 8-byte aligned.
@@ -1159,14 +1222,18 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
       });
     }
   }
-  // q[r][c] and v[r][j] of the chunk (zero past its end): from LDS, or from global memory
+  // q[r][c] and v[r][j .. j + 3] of the chunk (zero past its end): from LDS, or from global memory
   auto q_at = [&](int r, int c) -> float {
     if constexpr (Cf::QV_LDS) return tf(sQ[r * SK + c]);
     else return r < nr ? ldg<F32>(p.q, (row0 + (int64_t)r * H) * DK + c) : 0.f;
   };
-  auto v_at = [&](int r, int j) -> float {
-    if constexpr (Cf::QV_LDS) return tf(sV[r * SV + j]);
-    else return r < nr ? ldg<F32>(p.v, (row0 + (int64_t)r * H) * DV + j) : 0.f;
+  auto v4_at = [&](int r, int j) -> float4 {  // v[r][j .. j + 3], j a multiple of 4
+    if constexpr (Cf::QV_LDS) {
+      return ld4f(sV + r * SV + j);
+    } else {
+      const float4 x = ld4f(static_cast<const E*>(p.v) + (row0 + (int64_t)(r < nr ? r : 0) * H) * DV + j);
+      return r < nr ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   };
   if (tid < C) sBeta[tid] = tid < nr ? ldg<F32>(p.beta, row0 + (int64_t)tid * H) : 0.f;
   __syncthreads();
@@ -1178,10 +1245,11 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     tri_pair(t, tb, ta);
     const int r0 = 16 * tb, i0 = 16 * ta;
     const float* Rb = tb > 0 ? sG + (r0 - 1) * SG : nullptr;
-    f32x4 acc = tile_mm<F32, DK>(
-        [&](int m, int k) { return tf(sK[(r0 + m) * SK + k]) * __expf(sG[(r0 + m) * SG + k] - (Rb ? Rb[k] : 0.f)); },
-        [&](int k, int n) { return tf(sK[(i0 + n) * SK + k]) * __expf((Rb ? Rb[k] : 0.f) - sG[(i0 + n) * SG + k]); },
-        zero4());
+    auto rb4 = [&](int k) { return Rb ? *reinterpret_cast<const float4*>(Rb + k) : make_float4(0.f, 0.f, 0.f, 0.f); };
+    auto g4 = [&](int r, int k) { return *reinterpret_cast<const float4*>(sG + r * SG + k); };
+    f32x4 acc = tile_mm4<F32, DK>(
+        [&](int m, int k) { return mul4(ld4f(sK + (r0 + m) * SK + k), exp4(g4(r0 + m, k), rb4(k))); },
+        [&](int k, int n) { return mul4(ld4f(sK + (i0 + n) * SK + k), exp4(rb4(k), g4(i0 + n, k))); }, zero4());
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = r0 + 4 * grp + r, col = i0 + lo;
@@ -1258,11 +1326,16 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     int tb, ta;
     tri_pair(t, tb, ta);
     const int r0 = 16 * tb, i0 = 16 * ta;
-    f32x4 acc = tile_mm<F32, DK, true>([&](int m, int k) { return at(gr, GL::DW + (r0 + m) * DK + k); },
-                                 [&](int k, int n) { return tf(sK[(i0 + n) * SK + k]) * __expf(sG[(i0 + n) * SG + k]); },
-                                 zero4());
-    acc = tile_mm<F32, DV, true>([&](int m, int k) { return at(gr, GL::DU + (r0 + m) * DV + k); },
-                           [&](int k, int n) { return v_at(i0 + n, k); }, acc);
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    f32x4 acc = tile_mm4<F32, DK, true>(
+        [&](int m, int k) { return ld4f(reinterpret_cast<const float4*>(&at(gr, GL::DW + (r0 + m) * DK + k))); },
+        [&](int k, int n) {
+          return mul4(ld4f(sK + (i0 + n) * SK + k), exp4(*reinterpret_cast<const float4*>(sG + (i0 + n) * SG + k), z4));
+        },
+        zero4());
+    acc = tile_mm4<F32, DV, true>(
+        [&](int m, int k) { return ld4f(reinterpret_cast<const float4*>(&at(gr, GL::DU + (r0 + m) * DV + k))); },
+        [&](int k, int n) { return v4_at(i0 + n, k); }, acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = r0 + 4 * grp + r, col = i0 + lo;
@@ -1335,9 +1408,14 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   for (int t = wave; t < Cf::NTC * Cf::NTC; t += 8) {
     const int a0 = 16 * (t / Cf::NTC), b0 = 16 * (t % Cf::NTC);
     f32x4 d = zero4();
-    if (b0 <= a0)
-      d = tile_mm<F32, C, true>([&](int m, int k) { return sM4[(a0 + m) * SM + k]; },
-                                [&](int k, int n) { return sL[(b0 + n) * SM + k]; }, d);
+    if (b0 <= a0) {
+      if constexpr (F32 || C % 32 == 0)
+        d = tile_mm4<F32, C, true>([&](int m, int k) { return *reinterpret_cast<const float4*>(sM4 + (a0 + m) * SM + k); },
+                                   [&](int k, int n) { return *reinterpret_cast<const float4*>(sL + (b0 + n) * SM + k); }, d);
+      else
+        d = tile_mm<F32, C, true>([&](int m, int k) { return sM4[(a0 + m) * SM + k]; },
+                                  [&](int k, int n) { return sL[(b0 + n) * SM + k]; }, d);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int a = a0 + 4 * grp + r, bb = b0 + lo;
