@@ -474,15 +474,24 @@ def main():
             kda.kda_chunked_backward_saved(g["q"], g["k"], g["v"], g["g"], g["beta"], g["h0"], do, dhT, saved,
                                            chunk=w.chunk, grads=grads, workspace=sws)
 
+        def bstep_saved(_i):  # the backward alone, from the buffer the last training forward filled
+            kda.kda_chunked_backward_saved(g["q"], g["k"], g["v"], g["g"], g["beta"], g["h0"], do, dhT, saved,
+                                           chunk=w.chunk, grads=grads, workspace=sws)
+
         step_saved(0)
         torch.cuda.synchronize()
         rms, _ = time_launches(step_recompute, max(3, args.steps // 4), None if args.no_flush else flush)
         tms, _ = time_launches(step_saved, max(3, args.steps // 4), None if args.no_flush else flush)
+        step_saved(0)
+        torch.cuda.synchronize()
+        bsms, _ = time_launches(bstep_saved, max(3, args.steps // 4), None if args.no_flush else flush)
         out["train_step"] = {"ms_recompute": rms, "ms_saved": tms, "saved_bytes": saved.numel(),
                              "workspace_bytes_saved_backward": sws.numel(),
                              "tokens_per_s_saved": tokens / (tms * 1e-3),
+                             "ms_backward_saved": bsms,
                              "note": "forward + backward per step; 'saved': kda_chunked_forward_train + "
-                                     "kda_chunked_backward_saved (no forward recompute)"}
+                                     "kda_chunked_backward_saved (no forward recompute); ms_backward_saved: "
+                                     "kda_chunked_backward_saved alone"}
         del bws, grads, do, dhT, saved, sws
 
     # ---------------- decode

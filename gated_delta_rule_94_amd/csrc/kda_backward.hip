@@ -212,6 +212,47 @@ __device__ __forceinline__ f32x4 tile_mm(FA&& a, FB&& b, f32x4 acc) {
   return acc;
 }
 
+// Two tiles sharing their A operand, D1 += A B1 and D2 += A B2, as tile_mm: A's fragments (and
+// their hi + lo split) are formed once for both products.
+template <bool F32, int K, bool SPLIT, typename FA, typename FB1, typename FB2>
+__device__ __forceinline__ void tile_mm2(FA&& a, FB1&& b1, FB2&& b2, f32x4& d1, f32x4& d2) {
+  using O = Op<F32>;
+  const int lane = threadIdx.x & 63, lo = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < O::nks(K); ++s) {
+    if constexpr (F32) {
+      const int k = O::kidx(s, grp, 0);
+      const float fa = a(lo, k);
+      d1 = O::mma(fa, b1(k, lo), d1);
+      d2 = O::mma(fa, b2(k, lo), d2);
+    } else {
+      typename O::Frag fa, fal, fb, fbl, fc, fcl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = O::kidx(s, grp, j);
+        const bool ok = (K % 32 == 0) || k < K;
+        const float x = ok ? a(lo, k) : 0.f, y = ok ? b1(k, lo) : 0.f, z = ok ? b2(k, lo) : 0.f;
+        fa[j] = (__bf16)x;
+        fb[j] = (__bf16)y;
+        fc[j] = (__bf16)z;
+        if constexpr (SPLIT) {
+          fal[j] = (__bf16)(x - (float)fa[j]);
+          fbl[j] = (__bf16)(y - (float)fb[j]);
+          fcl[j] = (__bf16)(z - (float)fc[j]);
+        }
+      }
+      d1 = O::mma(fa, fb, d1);
+      d2 = O::mma(fa, fc, d2);
+      if constexpr (SPLIT) {
+        d1 = O::mma(fa, fbl, d1);
+        d2 = O::mma(fa, fcl, d2);
+        d1 = O::mma(fal, fb, d1);
+        d2 = O::mma(fal, fc, d2);
+      }
+    }
+  }
+}
+
 // One 16x16 tile of D += A B^T-stored operands read straight from LDS rows that run along the
 // contraction index: arow = &A[m0 + lo][0], brow = &Bt[n0 + lo][0] (operand type, 8-byte aligned
 // rows for bf16), K a multiple of the MFMA depth.
@@ -246,7 +287,9 @@ __device__ __forceinline__ float4 exp4(float4 a, float4 b) {  // e^{a - b}
 // tile_mm for operands that run along the contraction index in memory: a4(m, k) returns A[m][k ..
 // k + 3] and b4(k, n) returns B[k .. k + 3][n] (k a multiple of 4), so each fragment takes two
 // 4-element accesses per operand instead of eight single ones.  K: a multiple of 32 (bf16) or 16 (fp32).
-template <bool F32, int K, bool SPLIT = false, typename FA4, typename FB4>
+// SPLITB = false with SPLIT: B is exact in bf16 (an input read as it is), so only A is carried as
+// hi + lo parts and the hi x lo(B) product, zero, is left out.
+template <bool F32, int K, bool SPLIT = false, bool SPLITB = SPLIT, typename FA4, typename FB4>
 __device__ __forceinline__ f32x4 tile_mm4(FA4&& a4, FB4&& b4, f32x4 acc) {
   const int lane = threadIdx.x & 63, lo = lane & 15, grp = lane >> 4;
   if constexpr (F32) {
@@ -274,16 +317,12 @@ __device__ __forceinline__ f32x4 tile_mm4(FA4&& a4, FB4&& b4, f32x4 acc) {
       for (int j = 0; j < 8; ++j) {
         fa[j] = (__bf16)x[j];
         fb[j] = (__bf16)y[j];
-        if constexpr (SPLIT) {
-          fal[j] = (__bf16)(x[j] - (float)fa[j]);
-          fbl[j] = (__bf16)(y[j] - (float)fb[j]);
-        }
+        if constexpr (SPLIT) fal[j] = (__bf16)(x[j] - (float)fa[j]);
+        if constexpr (SPLIT && SPLITB) fbl[j] = (__bf16)(y[j] - (float)fb[j]);
       }
       acc = O::mma(fa, fb, acc);
-      if constexpr (SPLIT) {
-        acc = O::mma(fa, fbl, acc);
-        acc = O::mma(fal, fb, acc);
-      }
+      if constexpr (SPLIT && SPLITB) acc = O::mma(fa, fbl, acc);
+      if constexpr (SPLIT) acc = O::mma(fal, fb, acc);
     }
   }
   return acc;
@@ -1333,7 +1372,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
           return mul4(ld4f(sK + (i0 + n) * SK + k), exp4(*reinterpret_cast<const float4*>(sG + (i0 + n) * SG + k), z4));
         },
         zero4());
-    acc = tile_mm4<F32, DV, true>(
+    acc = tile_mm4<F32, DV, true, false>(  // v is exact in the operand type: only dU is split
         [&](int m, int k) { return ld4f(reinterpret_cast<const float4*>(&at(gr, GL::DU + (r0 + m) * DV + k))); },
         [&](int k, int n) { return v4_at(i0 + n, k); }, acc);
 #pragma unroll
@@ -1347,7 +1386,10 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     if ((i >> 4) > (r >> 4)) sM3[r * SM + i] = 0.f;
   }
 
-  // ---- owned tiles: dKG = T^T dW (T = L diag(beta)); dK += dKG Gamma, dG += dKG K Gamma
+  // ---- owned tiles: dKG = T^T dW (T = L diag(beta)); dK += dKG Gamma, dG += dKG K Gamma; and
+  // dV = T^T dU, straight to the output.  With d_k = d_v the dV tile of the same row tile and column
+  // tile index is formed beside each owned tile, the T^T fragments shared by the two products.
+  constexpr bool DKV = NTK == NTV;
   f32x4 aq[MAXT], ak[MAXT], ag[MAXT];
 #pragma unroll
   for (int q = 0; q < MAXT; ++q) {
@@ -1357,8 +1399,20 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
     const int t = wave + 8 * q;
     if (t < NTILE) {
       const int i0 = 16 * tile_row(q, t), c0 = 16 * tile_col(t);
-      const f32x4 d = tile_mm<F32, C, true>([&](int m, int k) { return sL[k * SM + i0 + m] * sBeta[i0 + m]; },
-                                            [&](int k, int n) { return at(gr, GL::DW + k * DK + c0 + n); }, zero4());
+      auto ta = [&](int m, int k) { return sL[k * SM + i0 + m] * sBeta[i0 + m]; };
+      auto bw = [&](int k, int n) { return at(gr, GL::DW + k * DK + c0 + n); };
+      f32x4 d = zero4();
+      if constexpr (DKV) {
+        f32x4 v = zero4();
+        tile_mm2<F32, C, true>(ta, bw, [&](int k, int n) { return at(gr, GL::DU + k * DV + c0 + n); }, d, v);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = i0 + 4 * grp + r;
+          if (i < nr) stg_at<F32>(dvb, (uint32_t)(i * H * DV + c0 + lo), v[r]);
+        }
+      } else {
+        d = tile_mm<F32, C, true>(ta, bw, zero4());
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + 4 * grp + r, c = c0 + lo;
@@ -1368,15 +1422,16 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
       }
     }
   }
-  // dV = T^T dU, straight to the output
-  for (int t = wave; t < Cf::NTC * NTV; t += 8) {
-    const int i0 = 16 * (t / NTV), j0 = 16 * (t % NTV);
-    const f32x4 d = tile_mm<F32, C, true>([&](int m, int k) { return sL[k * SM + i0 + m] * sBeta[i0 + m]; },
-                                          [&](int k, int n) { return at(gr, GL::DU + k * DV + j0 + n); }, zero4());
+  if constexpr (!DKV) {
+    for (int t = wave; t < Cf::NTC * NTV; t += 8) {
+      const int i0 = 16 * (t / NTV), j0 = 16 * (t % NTV);
+      const f32x4 d = tile_mm<F32, C, true>([&](int m, int k) { return sL[k * SM + i0 + m] * sBeta[i0 + m]; },
+                                            [&](int k, int n) { return at(gr, GL::DU + k * DV + j0 + n); }, zero4());
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + 4 * grp + r;
-      if (i < nr) stg_at<F32>(dvb, (uint32_t)(i * H * DV + j0 + lo), d[r]);
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 4 * grp + r;
+        if (i < nr) stg_at<F32>(dvb, (uint32_t)(i * H * DV + j0 + lo), d[r]);
+      }
     }
   }
   __syncthreads();
