@@ -902,7 +902,10 @@ template <bool F32, int DK, int DV, int C, int VP_>
 struct BStateLayout {
   using E = typename Op<F32>::E;
   static constexpr int ES = sizeof(E);
-  static constexpr int SV = VP_ + 16 / ES, SK = DK + 16 / ES, SC = C + 16 / ES;
+  // row padding: 16 bytes where the rows are also read straight along a row (16 rows of one 8-byte
+  // access each then fall on distinct banks), 32 bytes for P and Kd^T, read only with the transposing
+  // load (whose half-wave covers 8 consecutive rows)
+  static constexpr int SV = VP_ + 16 / ES, SK = DK + 16 / ES, SC = C + 32 / ES;
   static constexpr int OFF_S0 = 0;                                  // E [DK][SV]
   static constexpr int OFF_DS = OFF_S0 + DK * SV * ES;              // E [DK][SV]
   static constexpr int OFF_DO = OFF_DS + DK * SV * ES;              // E [C][SV]
@@ -1000,8 +1003,8 @@ __global__ __launch_bounds__(512) void bwd_state_kernel(BwdParams p) {
             a = bf16x4{(E)x.x, (E)x.y, (E)x.z, (E)x.w};
           }
           const bf16x4 d = *reinterpret_cast<const bf16x4*>(ds1 + gi);
-          pa[0] = a[0]; pa[1] = a[1]; pa[2] = a[2]; pa[3] = a[3];
-          pd[0] = d[0]; pd[1] = d[1]; pd[2] = d[2]; pd[3] = d[3];
+          *reinterpret_cast<bf16x4*>(pa) = a;
+          *reinterpret_cast<bf16x4*>(pd) = d;
         }
       });
     };
@@ -1187,6 +1190,19 @@ __device__ __forceinline__ void scan_rows(float* a, int ld, float* tot, int tid)
   __syncthreads();
 }
 
+// Rows 0 .. nr-1 of a bf16 [C][D + 8] LDS tile to an output whose row r starts D * H * r elements
+// after `base`: 16-byte accesses, 8 elements each, so every row of the output (D * 2 contiguous
+// bytes) is written as whole 64-byte pieces rather than 2-byte elements.
+template <int C, int D, int NTH>
+__device__ __forceinline__ void rows_out_bf16(const __bf16* src, void* base, int H, int nr, int tid) {
+  for_units<C * D / 8, NTH>(tid, [&](int e) {
+    const int r = (8 * e) / D, c = 8 * e - r * D;
+    if (r < nr)
+      at(static_cast<uint4*>(base), (uint32_t)((r * H * D + c) / 8)) =
+          *reinterpret_cast<const uint4*>(src + r * (D + 8) + c);
+  });
+}
+
 template <bool F32, int DK, int DV, int C>
 __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   using Cf = BIntraCfg<F32, DK, DV, C>;
@@ -1200,6 +1216,10 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   auto tile_col = [&](int t) { return NTK == 8 ? (t & 7) : t % NTK; };
   constexpr int EEU = NTK == 8 ? C / 4 : 1;  // unrolling of the loops over a row tile's rows (constant counts at d_k = 128)
   constexpr int SG = Cf::SG, SK = Cf::SK, SV = Cf::SV, SM = Cf::SM, NTH = Cf::NTH;
+  // bf16 gradients staged in LDS regions that are dead by then and written out as whole rows: dv in
+  // M4 (free until Y), dq and dk over Ekk and L (free after dA), where a [C][d + 8] tile fits
+  constexpr bool STG_V = !F32 && C * (DV + 8) * 2 <= C * SM * 4;
+  constexpr bool STG_QK = !F32 && C * (DK + 8) * 2 <= C * SM * 4;
   __shared__ __align__(16) unsigned char smem[Cf::TOTAL];
   float* sG = reinterpret_cast<float*>(smem + Cf::OFF_G);
   E* sK = reinterpret_cast<E*>(smem + Cf::OFF_K);
@@ -1408,7 +1428,10 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = i0 + 4 * grp + r;
-          if (i < nr) stg_at<F32>(dvb, (uint32_t)(i * H * DV + c0 + lo), v[r]);
+          if constexpr (STG_V)
+            reinterpret_cast<__bf16*>(sM4)[i * (DV + 8) + c0 + lo] = (__bf16)v[r];
+          else if (i < nr)
+            stg_at<F32>(dvb, (uint32_t)(i * H * DV + c0 + lo), v[r]);
         }
       } else {
         d = tile_mm<F32, C, true>(ta, bw, zero4());
@@ -1430,11 +1453,15 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + 4 * grp + r;
-        if (i < nr) stg_at<F32>(dvb, (uint32_t)(i * H * DV + j0 + lo), d[r]);
+        if constexpr (STG_V)
+          reinterpret_cast<__bf16*>(sM4)[i * (DV + 8) + j0 + lo] = (__bf16)d[r];
+        else if (i < nr)
+          stg_at<F32>(dvb, (uint32_t)(i * H * DV + j0 + lo), d[r]);
       }
     }
   }
   __syncthreads();
+  if constexpr (STG_V) rows_out_bf16<C, DV, NTH>(reinterpret_cast<const __bf16*>(sM4), dvb, H, nr, tid);
 
   // ---- column part of dbeta (T = L diag(beta)) and dL = dT diag(beta): NPC lanes per column
   constexpr int NPC = NTH / C;
@@ -1586,18 +1613,36 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
       float dg = ag[q][r];
       if (i == C - 1) dg += sDgl[c];
       sG[i * SG + c] = dg;
-      if (i < nr) {
+      if constexpr (STG_QK) {
+        reinterpret_cast<__bf16*>(sEkk)[i * (DK + 8) + c] = (__bf16)aq[q][r];
+        reinterpret_cast<__bf16*>(sL)[i * (DK + 8) + c] = (__bf16)ak[q][r];
+      } else if (i < nr) {
         stg_at<F32>(dqb, (uint32_t)(i * H * DK + c), aq[q][r]);
         stg_at<F32>(dkb, (uint32_t)(i * H * DK + c), ak[q][r]);
       }
     }
   }
   __syncthreads();
-  // ---- dg = reverse cumulative sum of dG over the chunk's rows
+  if constexpr (STG_QK) {
+    rows_out_bf16<C, DK, NTH>(reinterpret_cast<const __bf16*>(sEkk), dqb, H, nr, tid);
+    rows_out_bf16<C, DK, NTH>(reinterpret_cast<const __bf16*>(sL), dkb, H, nr, tid);
+  }
+  // ---- dg = reverse cumulative sum of dG over the chunk's rows, written 8 channels per access
   scan_rows<DK, C, Cf::NPART, Cf::RPP, true>(sG, SG, sScan, tid);
-  for (int e = tid; e < C * DK; e += NTH) {
-    const int r = e / DK, c = e - r * DK;
-    if (r < nr) stg_at<F32>(dgb, (uint32_t)(r * H * DK + c), sG[r * SG + c]);
+  if constexpr (F32) {
+    for (int e = tid; e < C * DK; e += NTH) {
+      const int r = e / DK, c = e - r * DK;
+      if (r < nr) stg_at<F32>(dgb, (uint32_t)(r * H * DK + c), sG[r * SG + c]);
+    }
+  } else {
+    for_units<C * DK / 8, NTH>(tid, [&](int e) {
+      const int r = (8 * e) / DK, c = 8 * e - r * DK;
+      if (r < nr) {
+        const float4 a = *reinterpret_cast<const float4*>(sG + r * SG + c), b = *reinterpret_cast<const float4*>(sG + r * SG + c + 4);
+        at(static_cast<uint4*>(dgb), (uint32_t)((r * H * DK + c) / 8)) =
+            make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
+      }
+    });
   }
 }
 
