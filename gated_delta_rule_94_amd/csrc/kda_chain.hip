@@ -110,11 +110,29 @@ struct CopyPart {
     const int u = ht + NC * k;
     return u < NU ? u : NU - 1;
   }
-  __device__ __forceinline__ void load(const unsigned char* rec, int ht) {
+  // The byte offsets of this thread's units in a record, formed once: each load addresses from the
+  // wave-uniform record base (scalar registers) plus one of these 32-bit offsets, with no address
+  // temporaries.  The empty asm in load() marks the offset as redefined there, so that it is not
+  // hoisted out of the chunk loop as a 64-bit value, and keeps it in the same register for the
+  // whole loop: no offset register is ever reused as a load destination, which would make the
+  // next chunk's loads wait for every load of this one.
+  struct Off {
+    uint32_t o[K];
+  };
+  __device__ static __forceinline__ Off offsets(int ht) {
+    Off f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int u = unit(ht, k);
-      const uint4 x = *reinterpret_cast<const uint4*>(rec + GBASE + (u / UPR) * GROW + 16 * (u % UPR));
+      f.o[k] = (uint32_t)(GBASE + (u / UPR) * GROW + 16 * (u % UPR));
+    }
+    return f;
+  }
+  __device__ __forceinline__ void load(const unsigned char* rec, Off& f) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      asm volatile("" : "+v"(f.o[k]));
+      const uint4 x = *reinterpret_cast<const uint4*>(rec + f.o[k]);
       st[4 * k] = x.x;
       st[4 * k + 1] = x.y;
       st[4 * k + 2] = x.z;
@@ -214,9 +232,21 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     CopyPart<Cf::NC, Cf::U_UT, C / EPU, (int)(R::UT * ES_), C * ES_, Cf::B_UT, US * ES_, !F32> ut;  // record pointer + col0 rows
     CopyPart<Cf::NC, Cf::U_GAM, Cf::U_GAM, (int)R::GAM_BYTE, 0, Cf::B_GAM, 0> gam;
     uint4 zg;  // output gate: one 16-byte unit of the chunk's [C][WS] slice per copy thread
-    __device__ __forceinline__ void load(const unsigned char* rp, int ht, int col0b) {
-      nw.load(rp, ht); kpt.load(rp, ht); ut.load(rp + col0b, ht); gam.load(rp, ht);
-      if constexpr (!SUM) { qg.load(rp, ht); pp.load(rp, ht); }  // a summary writes no o
+    struct Offs {
+      typename decltype(nw)::Off nw;
+      typename decltype(qg)::Off qg;
+      typename decltype(pp)::Off pp;
+      typename decltype(kpt)::Off kpt;
+      typename decltype(ut)::Off ut;
+      typename decltype(gam)::Off gam;
+    };
+    __device__ static __forceinline__ Offs offsets(int ht) {
+      return Offs{decltype(nw)::offsets(ht), decltype(qg)::offsets(ht), decltype(pp)::offsets(ht),
+                  decltype(kpt)::offsets(ht), decltype(ut)::offsets(ht), decltype(gam)::offsets(ht)};
+    }
+    __device__ __forceinline__ void load(const unsigned char* rp, Offs& f, int col0b) {
+      nw.load(rp, f.nw); kpt.load(rp, f.kpt); ut.load(rp + col0b, f.ut); gam.load(rp, f.gam);
+      if constexpr (!SUM) { qg.load(rp, f.qg); pp.load(rp, f.pp); }  // a summary writes no o
     }
     __device__ __forceinline__ void store(unsigned char* b, int ht) const {
       nw.store(b, ht); kpt.store(b, ht); ut.store(b, ht); gam.store(b, ht);
@@ -236,7 +266,11 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
     const int64_t t0 = t_begin + (int64_t)c * C;
     const int len = (int)((t_end - t0) < C ? (t_end - t0) : C);
     const int64_t zi = ((t0 + (row < len ? row : len - 1)) * H + h) * DV + col0 + (u % ZU) * (16 / ES_);
-    st.zg = *reinterpret_cast<const uint4*>(static_cast<const E*>(p.z) + zi);
+    // without an output gate the unit is read from the record buffer and never stored: the copy
+    // waves then issue the same loads on every call, so the compiler counts the loads in flight
+    // exactly across the pipeline (a load under a runtime branch makes it wait for all of them)
+    const void* zp = p.z != nullptr ? static_cast<const void*>(static_cast<const E*>(p.z) + zi) : static_cast<const void*>(p.ws);
+    st.zg = *reinterpret_cast<const uint4*>(zp);
   };
   auto store_z = [&](const Stage& st, unsigned char* b) {
     if (ht < C * ZU) *reinterpret_cast<uint4*>(b + Cf::B_Z + (ht / ZU) * Cf::ZROW + 16 * (ht % ZU)) = st.zg;
@@ -462,13 +496,14 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
   } else if constexpr (ONEBUF) {
     // one buffer: chunk c + 1 waits in registers while the chain waves compute chunk c
     Stage s0;
+    typename Stage::Offs offs = Stage::offsets(ht);
     if (nchunks > 0) {
-      s0.load(rec_of(0), ht, col0b);
-      if (Cf::HAS_Z && gz) load_z(s0, 0);
+      s0.load(rec_of(0), offs, col0b);
+      if (Cf::HAS_Z) load_z(s0, 0);
       s0.store(smem, ht);
       if (Cf::HAS_Z && gz) store_z(s0, smem);
-      s0.load(rec_of(last < 1 ? last : 1), ht, col0b);
-      if (Cf::HAS_Z && gz) load_z(s0, last < 1 ? last : 1);
+      s0.load(rec_of(last < 1 ? last : 1), offs, col0b);
+      if (Cf::HAS_Z) load_z(s0, last < 1 ? last : 1);
     }
     __syncthreads();
     for (int c = 0; c < nchunks; ++c) {
@@ -477,29 +512,30 @@ __global__ __launch_bounds__(64 * (WS / 16 + 4)) void chain_kernel(const ChainPa
       s0.store(smem, ht);
       if (Cf::HAS_Z && gz) store_z(s0, smem);
       __syncthreads();  // the buffer holds chunk c + 1
-      s0.load(rec_of(c + 2 < last ? c + 2 : last), ht, col0b);
-      if (Cf::HAS_Z && gz) load_z(s0, c + 2 < last ? c + 2 : last);
+      s0.load(rec_of(c + 2 < last ? c + 2 : last), offs, col0b);
+      if (Cf::HAS_Z) load_z(s0, c + 2 < last ? c + 2 : last);
     }
   } else {
     Stage s0, s1;
+    typename Stage::Offs offs = Stage::offsets(ht);
     if (nchunks > 0) {
-      s0.load(rec_of(0), ht, col0b);
-      if (Cf::HAS_Z && gz) load_z(s0, 0);
+      s0.load(rec_of(0), offs, col0b);
+      if (Cf::HAS_Z) load_z(s0, 0);
       s0.store(smem, ht);
       if (Cf::HAS_Z && gz) store_z(s0, smem);
-      s1.load(rec_of(last < 1 ? last : 1), ht, col0b);
-      if (Cf::HAS_Z && gz) load_z(s1, last < 1 ? last : 1);
+      s1.load(rec_of(last < 1 ? last : 1), offs, col0b);
+      if (Cf::HAS_Z) load_z(s1, last < 1 ? last : 1);
     }
     __syncthreads();
     for (int c = 0; c < nchunks; c += 2) {
-      s0.load(rec_of(c + 2 < last ? c + 2 : last), ht, col0b);
-      if (Cf::HAS_Z && gz) load_z(s0, c + 2 < last ? c + 2 : last);
+      s0.load(rec_of(c + 2 < last ? c + 2 : last), offs, col0b);
+      if (Cf::HAS_Z) load_z(s0, c + 2 < last ? c + 2 : last);
       s1.store(smem + Cf::BUF, ht);
       if (Cf::HAS_Z && gz) store_z(s1, smem + Cf::BUF);
       __syncthreads();
       if (c + 1 >= nchunks) break;
-      s1.load(rec_of(c + 3 < last ? c + 3 : last), ht, col0b);
-      if (Cf::HAS_Z && gz) load_z(s1, c + 3 < last ? c + 3 : last);
+      s1.load(rec_of(c + 3 < last ? c + 3 : last), offs, col0b);
+      if (Cf::HAS_Z) load_z(s1, c + 3 < last ? c + 3 : last);
       s0.store(smem, ht);
       if (Cf::HAS_Z && gz) store_z(s0, smem);
       __syncthreads();
@@ -571,12 +607,25 @@ struct WideCopy {
     const int u = ht + NC * k;
     return u < NU ? u : NU - 1;
   }
-  __device__ __forceinline__ void load(const unsigned char* rec, int ht) {
+  // 32-bit unit offsets formed once, as CopyPart's
+  struct Off {
+    uint32_t o[K];
+  };
+  __device__ static __forceinline__ Off offsets(int ht) {
+    Off f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int u = unit(ht, k);
+      f.o[k] = NU > 0 ? (uint32_t)(GBASE + (u / UPR) * GROW + 16 * (u % UPR)) : 0u;
+    }
+    return f;
+  }
+  __device__ __forceinline__ void load(const unsigned char* rec, Off& f) {
     if constexpr (NU > 0) {
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const int u = unit(ht, k);
-        const uint4 x = *reinterpret_cast<const uint4*>(rec + GBASE + (u / UPR) * GROW + 16 * (u % UPR));
+        asm volatile("" : "+v"(f.o[k]));
+        const uint4 x = *reinterpret_cast<const uint4*>(rec + f.o[k]);
         st[4 * k] = x.x;
         st[4 * k + 1] = x.y;
         st[4 * k + 2] = x.z;
@@ -695,14 +744,27 @@ __global__ __launch_bounds__(64 * (WS / 32 + 4)) void chain_wide_kernel(const Ch
     WideCopy<Cf::NC, Cf::U_UT, C / 8, (int)(R::UT * 2), C * 2, Cf::B_UT, 1> ut;  // record pointer + col0 rows
     WideCopy<Cf::NC, Cf::U_GAM, Cf::U_GAM, (int)R::GAM_BYTE, 0, Cf::B_GAM, 0> gam;
     uint4 zg[Cf::ZK];
+    struct Offs {
+      typename decltype(nw)::Off nw;
+      typename decltype(qg)::Off qg;
+      typename decltype(pp)::Off pp;
+      typename decltype(kpt)::Off kpt;
+      typename decltype(ut)::Off ut;
+      typename decltype(gam)::Off gam;
+    };
   };
   // gam: one row of U_GAM units; the swizzle key of row 0 is 0, so it is stored in order
   const int ht = tid - 64 * Cf::NWV;  // copy-thread index (copy waves only)
   const int64_t col0b = (int64_t)(no_ut ? 0 : col0) * C * 2;  // first U~^T row of the slice
+  // identity-column slices load a U~ slice too (col0b is then 0) and do not store it: the same loads
+  // on every path keep the compiler's count of loads in flight exact
+  typename Stage::Offs offs{decltype(Stage::nw)::offsets(ht), decltype(Stage::qg)::offsets(ht),
+                            decltype(Stage::pp)::offsets(ht), decltype(Stage::kpt)::offsets(ht),
+                            decltype(Stage::ut)::offsets(ht), decltype(Stage::gam)::offsets(ht)};
   auto stage_load = [&](Stage& st, const unsigned char* rp) {
-    st.nw.load(rp, ht); st.kpt.load(rp, ht); st.gam.load(rp, ht);
-    if (!no_ut) st.ut.load(rp + col0b, ht);
-    if constexpr (!SUM) { st.qg.load(rp, ht); st.pp.load(rp, ht); }
+    st.nw.load(rp, offs.nw); st.kpt.load(rp, offs.kpt); st.gam.load(rp, offs.gam);
+    st.ut.load(rp + col0b, offs.ut);
+    if constexpr (!SUM) { st.qg.load(rp, offs.qg); st.pp.load(rp, offs.pp); }
   };
   auto stage_store = [&](const Stage& st, unsigned char* b) {
     st.nw.store(b, ht); st.kpt.store(b, ht); st.gam.store(b, ht);
@@ -721,7 +783,9 @@ __global__ __launch_bounds__(64 * (WS / 32 + 4)) void chain_wide_kernel(const Ch
       u = u < C * Cf::ZU ? u : C * Cf::ZU - 1;
       const int row = u / Cf::ZU;
       const int64_t zi = ((t0 + (row < len ? row : len - 1)) * H + h) * DV + col0 + (u % Cf::ZU) * 8;
-      st.zg[k] = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(p.z) + zi);
+      // unconditional, as in chain_kernel: the record buffer stands in without an output gate
+      const void* zp = p.z != nullptr ? static_cast<const void*>(static_cast<const __bf16*>(p.z) + zi) : static_cast<const void*>(p.ws);
+      st.zg[k] = *reinterpret_cast<const uint4*>(zp);
     }
   };
   auto store_z = [&](const Stage& st, unsigned char* b) {
@@ -977,22 +1041,22 @@ __global__ __launch_bounds__(64 * (WS / 32 + 4)) void chain_wide_kernel(const Ch
     Stage s0, s1;
     if (nchunks > 0) {
       stage_load(s0, rec_of(0));
-      if (Cf::HAS_Z && gz) load_z(s0, 0);
+      if (Cf::HAS_Z) load_z(s0, 0);
       stage_store(s0, smem);
       if (Cf::HAS_Z && gz) store_z(s0, smem);
       stage_load(s1, rec_of(last < 1 ? last : 1));
-      if (Cf::HAS_Z && gz) load_z(s1, last < 1 ? last : 1);
+      if (Cf::HAS_Z) load_z(s1, last < 1 ? last : 1);
     }
     __syncthreads();
     for (int c = 0; c < nchunks; c += 2) {
       stage_load(s0, rec_of(c + 2 < last ? c + 2 : last));
-      if (Cf::HAS_Z && gz) load_z(s0, c + 2 < last ? c + 2 : last);
+      if (Cf::HAS_Z) load_z(s0, c + 2 < last ? c + 2 : last);
       stage_store(s1, smem + Cf::BUF);
       if (Cf::HAS_Z && gz) store_z(s1, smem + Cf::BUF);
       __syncthreads();
       if (c + 1 >= nchunks) break;
       stage_load(s1, rec_of(c + 3 < last ? c + 3 : last));
-      if (Cf::HAS_Z && gz) load_z(s1, c + 3 < last ? c + 3 : last);
+      if (Cf::HAS_Z) load_z(s1, c + 3 < last ? c + 3 : last);
       stage_store(s0, smem);
       if (Cf::HAS_Z && gz) store_z(s0, smem);
       __syncthreads();
