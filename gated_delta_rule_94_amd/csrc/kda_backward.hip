@@ -691,11 +691,27 @@ struct TCopy {
   static constexpr int K = (NU + NC - 1) / NC;
   typedef uint32_t vec_t __attribute__((ext_vector_type(4 * K)));
   vec_t st;
-  __device__ __forceinline__ void load(const unsigned char* rec, int ht) {
+  // 32-bit unit offsets formed once and kept in their registers across the chunk loop (the empty
+  // asm in load() stops the compiler hoisting them as 64-bit values): each load addresses from the
+  // scalar record base, and no offset register is reused as a load destination, which would make
+  // the next chunk's loads wait for all of this chunk's
+  struct Off {
+    uint32_t o[K];
+  };
+  __device__ static __forceinline__ Off offsets(int ht) {
+    Off f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int u = ht + NC * k < NU ? ht + NC * k : NU - 1;
-      const uint4 x = *reinterpret_cast<const uint4*>(rec + GBASE + (u / UPR) * GROW + 16 * (u % UPR));
+      f.o[k] = (uint32_t)(GBASE + (u / UPR) * GROW + 16 * (u % UPR));
+    }
+    return f;
+  }
+  __device__ __forceinline__ void load(const unsigned char* rec, Off& f) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      asm volatile("" : "+v"(f.o[k]));
+      const uint4 x = *reinterpret_cast<const uint4*>(rec + f.o[k]);
       st[4 * k] = x.x;
       st[4 * k + 1] = x.y;
       st[4 * k + 2] = x.z;
@@ -759,9 +775,18 @@ __global__ __launch_bounds__(384) void bwd_chain_t_kernel(BwdParams p) {
     bool dook;  // the dO unit lies in the chunk (rows past its end, and summary identity columns: zeros)
   };
   const int ht = tid - 64 * Cf::NCW;  // copy-thread index (copy waves only)
+  struct Offs {
+    typename decltype(Stage::nw)::Off nw;
+    typename decltype(Stage::qg)::Off qg;
+    typename decltype(Stage::kpt)::Off kpt;
+    typename decltype(Stage::pp)::Off pp;
+    typename decltype(Stage::gam)::Off gam;
+  } offs{decltype(Stage::nw)::offsets(ht), decltype(Stage::qg)::offsets(ht), decltype(Stage::kpt)::offsets(ht),
+         decltype(Stage::pp)::offsets(ht), decltype(Stage::gam)::offsets(ht)};
   auto stage_load = [&](Stage& st, int q) {
     const unsigned char* rp = rec_of(q);
-    st.nw.load(rp, ht); st.qg.load(rp, ht); st.kpt.load(rp, ht); st.pp.load(rp, ht); st.gam.load(rp, ht);
+    st.nw.load(rp, offs.nw); st.qg.load(rp, offs.qg); st.kpt.load(rp, offs.kpt); st.pp.load(rp, offs.pp);
+    st.gam.load(rp, offs.gam);
     // dO: unit ht = (row ht / 4, 8 columns); rows past the chunk's end read its last row (in bounds)
     const int64_t t0 = t_begin + (int64_t)(ch_hi - 1 - q) * C;
     const int len = (int)min((int64_t)C, t_end - t0);
