@@ -1172,8 +1172,9 @@ hipError_t launch_chain(const ChainLaunch& L) {
 // S(g + 1) = M_g S(g) + b_g, with [b_g | M_g] read from the summary launch's output.  One workgroup
 // per (sequence, head, 16 value columns): four waves, each owning 32 rows of S(g + 1) as two
 // 16x16 fp32 MFMA accumulator tiles, A = M_g (staged in LDS), B = S(g) (in LDS).  While the waves
-// multiply, every thread already loads its share of M_{g+1} into registers and stores it into the
-// other M buffer after the step, so a step waits on no global load.
+// multiply, every thread already loads its share of M_{g+1} and its b_{g+1} elements into
+// registers (M_{g+1} stored into the other M buffer after the step), so a step waits on no global
+// load.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void segment_combine_kernel(const float* __restrict__ h0,
                                                               const float* __restrict__ send,
@@ -1205,20 +1206,27 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(const float* __res
   for (int i = 0; i < MV; ++i) mv[i] = *reinterpret_cast<const f32x4*>(se0 + (mr + MRS * i) * SE + DV + mj);
 #pragma unroll
   for (int i = 0; i < MV; ++i) *reinterpret_cast<f32x4*>(&Ms[0][(mr + MRS * i) * MS + mj]) = mv[i];
-  __syncthreads();
-  for (int g = 0; g + 1 < nseg; ++g) {
-    const float* se = se0 + (int64_t)g * DK * SE;
-    {  // M_{g+1} (the last step reloads M_g: in bounds, never stored), stored after this step
-      const float* sn1 = se0 + (int64_t)(g + 2 < nseg ? g + 1 : g) * DK * SE;
-#pragma unroll
-      for (int i = 0; i < MV; ++i) mv[i] = *reinterpret_cast<const f32x4*>(sn1 + (mr + MRS * i) * SE + DV + mj);
-    }
-    // acc[t] = b_g rows 16 (RT wave + t) + 4 grp + r, column lo, then += M_g S(g)
-    f32x4 acc[RT];
+  // b_g rows 16 (RT wave + t) + 4 grp + r, column lo: this thread's accumulator elements
+  f32x4 bv[RT];
+  auto load_b = [&](const float* se) {
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[t][r] = se[(16 * (RT * wave + t) + 4 * grp + r) * SE + col0 + lo];
+      for (int r = 0; r < 4; ++r) bv[t][r] = se[(16 * (RT * wave + t) + 4 * grp + r) * SE + col0 + lo];
+  };
+  load_b(se0);
+  __syncthreads();
+  for (int g = 0; g + 1 < nseg; ++g) {
+    // acc = b_g (loaded during the previous step), then += M_g S(g)
+    f32x4 acc[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[t] = bv[t];
+    {  // M_{g+1} and b_{g+1} (the last step reloads segment g: in bounds, never used)
+      const float* sn1 = se0 + (int64_t)(g + 2 < nseg ? g + 1 : g) * DK * SE;
+      load_b(sn1);
+#pragma unroll
+      for (int i = 0; i < MV; ++i) mv[i] = *reinterpret_cast<const f32x4*>(sn1 + (mr + MRS * i) * SE + DV + mj);
+    }
     const float* m = Ms[g & 1];
 #pragma unroll 8
     for (int ks = 0; ks < DK / 4; ++ks) {
