@@ -1170,18 +1170,19 @@ hipError_t launch_chain(const ChainLaunch& L) {
 
 // Start states of the segments of one (sequence, head), in fp32: S(0) = h0 (or 0),
 // S(g + 1) = M_g S(g) + b_g, with [b_g | M_g] read from the summary launch's output.  One workgroup
-// per (sequence, head, 16 value columns): four waves, each owning 32 rows of S(g + 1) as two
-// 16x16 fp32 MFMA accumulator tiles, A = M_g (staged in LDS), B = S(g) (in LDS).  While the waves
+// per (sequence, head, 16 value columns): d_k / 16 waves, each owning 16 rows of S(g + 1) as one
+// 16x16 fp32 MFMA accumulator tile, A = M_g (staged in LDS), B = S(g) (in LDS).  While the waves
 // multiply, every thread already loads its share of M_{g+1} and its b_{g+1} elements into
 // registers (M_{g+1} stored into the other M buffer after the step), so a step waits on no global
 // load.
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void segment_combine_kernel(const float* __restrict__ h0,
+__global__ __launch_bounds__(64 * (DK / 16)) void segment_combine_kernel(const float* __restrict__ h0,
                                                               const float* __restrict__ send,
                                                               float* __restrict__ sstart, int units, int nseg) {
   constexpr int CW = 16, MS = DK + 4, SE = DV + DK, NSL = DV / CW;
-  constexpr int MV = DK * DK / 4 / 256;  // float4 of M_g per thread
-  constexpr int RT = DK / 64;            // 16-row tiles per wave (DK / 16 tiles over 4 waves)
+  constexpr int NTHC = 64 * (DK / 16);   // one wave per 16-row tile of S(g + 1)
+  constexpr int MV = DK * DK / 4 / NTHC; // float4 of M_g per thread
+  constexpr int RT = 1;                  // 16-row tiles per wave
   __shared__ __align__(16) float Ms[2][DK * MS];
   __shared__ __align__(16) float Ss[DK * CW];
   const int unit = blockIdx.x / NSL, col0 = (blockIdx.x % NSL) * CW;
@@ -1190,12 +1191,12 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(const float* __res
   const float* hu = h0 ? h0 + (int64_t)unit * DK * DV : nullptr;
   float* st = sstart + (int64_t)unit * nseg * DK * DV;
   const float* se0 = send + (int64_t)unit * (nseg - 1) * DK * SE;
-  // M_g, one float4 per (row, 4 columns): thread tid takes units tid + 256 i, i.e. row
+  // M_g, one float4 per (row, 4 columns): thread tid takes units tid + NTHC i, i.e. row
   // tid / (DK / 4) + 1024 i / DK, columns 4 (tid % (DK / 4)) ..
   const int mr = tid / (DK / 4), mj = 4 * (tid % (DK / 4));
-  constexpr int MRS = 256 / (DK / 4);  // rows between a thread's units
+  constexpr int MRS = NTHC / (DK / 4);  // rows between a thread's units
   // S(0) = h0 (or 0) into Ss and sstart[0]
-  for (int e = tid; e < DK * CW; e += 256) {
+  for (int e = tid; e < DK * CW; e += NTHC) {
     const int r = e / CW, c = e % CW;
     const float x = hu ? hu[r * DV + col0 + c] : 0.f;
     Ss[e] = x;
@@ -1261,7 +1262,7 @@ hipError_t launch_segment_combine(const float* h0, const float* send, float* sst
   if (units <= 0 || nseg < 2) return hipErrorInvalidValue;
 #define KDA_COMB(D, V)                                                                                      \
   if (dk == D && dv == V) {                                                                                 \
-    hipLaunchKernelGGL((segment_combine_kernel<D, V>), dim3(units * (V / 16)), dim3(256), 0, (hipStream_t)stream, \
+    hipLaunchKernelGGL((segment_combine_kernel<D, V>), dim3(units * (V / 16)), dim3(64 * (D / 16)), 0, (hipStream_t)stream, \
                        h0, send, sstart, units, nseg);                                                      \
     return hipGetLastError();                                                                               \
   }
