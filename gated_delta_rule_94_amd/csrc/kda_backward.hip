@@ -1549,6 +1549,21 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
   });
   __syncthreads();
 
+  // d(Q Gamma) and dKd of the owned elements, loaded here so that their latency passes behind the
+  // Ekk/Eqk backward (they are used in the elementwise phase after it)
+  float pfq[MAXT][4], pfk[MAXT][4];
+#pragma unroll
+  for (int q = 0; q < MAXT; ++q) {
+    const int t = wave + 8 * q;
+    if (t >= NTILE) continue;
+    const int r0 = 16 * tile_row(q, t), c = 16 * tile_col(t) + lo;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = r0 + 4 * grp + r;
+      pfq[q][r] = at(gr, GL::DQG + i * DK + c);
+      pfk[q][r] = at(gr, GL::DKD + i * DK + c);
+    }
+  }
   // ---- through Ekk and Eqk, on the owned tiles (rows r0.., channels c0..):
   //   row side (reference R = G before the row tile):
   //     dQe = e^{G_r - R} sum_{i <= r} dEqk[r][i] (K e^{R - G})[i],   dKr = the same with dEkk
@@ -1608,7 +1623,7 @@ __global__ __launch_bounds__(512) void bwd_intra_kernel(BwdParams p) {
       const int i = r0 + 4 * grp + r;
       const float G = sG[i * SG + c], gam = __expf(G), dec = __expf(gl - G);
       const float qv = q_at(i, c), kv = tf(sK[i * SK + c]);
-      const float dqg = at(gr, GL::DQG + i * DK + c), dkd = at(gr, GL::DKD + i * DK + c);
+      const float dqg = pfq[q][r], dkd = pfk[q][r];
       aq[q][r] = fmaf(dqg, gam, aq[q][r]);
       ag[q][r] = fmaf(dqg * qv, gam, ag[q][r]);
       ak[q][r] = fmaf(dkd, dec, ak[q][r]);
